@@ -1,0 +1,182 @@
+/*
+ * pmk.h -- C ABI of the persistent decode megakernel library (libpmk.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call runs one memory-bound LLM decode step of a whole decoder stack as a
+ * single persistent kernel whose tile tasks synchronise through per-tile event
+ * counters held in device memory instead of kernel boundaries ("Event Tensor: A
+ * Unified Abstraction for Compiling Dynamic Megakernel", summary page, Core
+ * method: an event marks that a group of tile tasks finished; notify() is an
+ * atomic decrement and wait() spins until the count reaches zero; under static
+ * scheduling each compute unit walks a precomputed task queue inside one
+ * persistent main loop). Event counts and task queues are rebuilt on the device
+ * from (batch, seq_lens) at every call, so batch size and per-request lengths
+ * may change between calls with no recompilation or capture (same page, Core
+ * method, two kinds of dynamism: shape dynamism).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor arguments are device pointers (hipMalloc'd or equivalent) and
+ *    stay owned by the caller. The library never copies or frees them.
+ *  - Weights are row-major [out][in] in the model dtype (float32 or bfloat16
+ *    as raw 16-bit patterns); RMSNorm gains are always float32.
+ *  - Calls are stream-ordered and asynchronous; `stream` is a hipStream_t
+ *    passed as void* (NULL = the null stream). One handle serves one stream at a
+ *    time: calls on one handle must not overlap.
+ *  - Return value: 0 (PMK_OK) or a PMK_ERR_* code; no exception crosses the ABI.
+ *    Errors the device detects (a request length out of range, an event wait
+ *    that exceeded the watchdog) are recorded in a device error word, returned
+ *    by pmk_get_device_error() and by the next call on the handle.
+ */
+#ifndef PMK_H
+#define PMK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PMK_ABI_VERSION 1
+
+enum pmk_status {
+  PMK_OK = 0,
+  PMK_ERR_ARG = 1,          /* invalid argument (dims, null pointer, batch out of range) */
+  PMK_ERR_OOM = 2,          /* device allocation failed */
+  PMK_ERR_DEVICE = 3,       /* a HIP call failed (launch, copy, event) */
+  PMK_ERR_TIMEOUT = 4,      /* device: an event wait exceeded the watchdog; the step was abandoned */
+  PMK_ERR_SEQ = 5,          /* device: seq_lens[b] < 0 or >= max_seq; the step did not run */
+  PMK_ERR_UNSUPPORTED = 6   /* a shape this build does not implement (see pmk_strerror) */
+};
+
+enum pmk_dtype { PMK_F32 = 0, PMK_BF16 = 1 };
+
+/* Model description. Dense stack when n_experts == 0, MoE layers otherwise. */
+typedef struct pmk_model_desc {
+  int32_t abi_version;       /* must be PMK_ABI_VERSION */
+  int32_t dtype;             /* pmk_dtype: weights and KV cache */
+  int32_t n_layers;
+  int32_t hidden;            /* H, multiple of 8 */
+  int32_t n_q_heads;         /* Hq, multiple of n_kv_heads */
+  int32_t n_kv_heads;        /* Hkv */
+  int32_t head_dim;          /* d; d * sizeof(dtype) must be 256 bytes (d = 128 bf16, d = 64 f32) */
+  int32_t ffn_dim;           /* F (dense), multiple of 8 */
+  int32_t n_experts;         /* E (0 = dense) */
+  int32_t top_k;             /* k <= 8 */
+  int32_t expert_ffn_dim;    /* Fe, multiple of 8 */
+  int32_t max_batch;         /* largest batch (or MoE token count) a call may pass */
+  int32_t max_seq;           /* KV cache slots per request; seq_lens[b] < max_seq */
+  float rms_eps;             /* e.g. 1e-5 */
+  float rope_theta;          /* e.g. 10000 */
+  int32_t watchdog_ms;       /* event-wait limit before the step is abandoned; 0 = 2000 */
+  int32_t reserved[6];       /* zero */
+} pmk_model_desc;
+
+/* One layer's weights (device pointers, caller-owned). Dense layers use
+ * w_gate/w_up/w_down; MoE layers use w_router and the w_exp_* tensors. */
+typedef struct pmk_layer_weights {
+  const float* attn_norm;    /* [H] */
+  const void* w_qkv;         /* [(Hq + 2 Hkv) d][H]: the q rows, then k, then v */
+  const void* w_o;           /* [H][Hq d] */
+  const float* ffn_norm;     /* [H] */
+  const void* w_gate;        /* [F][H] */
+  const void* w_up;          /* [F][H] */
+  const void* w_down;        /* [H][F] */
+  const void* w_router;      /* [E][H] */
+  const void* w_exp_gate;    /* [E][Fe][H] */
+  const void* w_exp_up;      /* [E][Fe][H] */
+  const void* w_exp_down;    /* [E][H][Fe] */
+} pmk_layer_weights;
+
+typedef struct pmk_weights {
+  int32_t n_layers;                  /* must equal desc->n_layers */
+  const pmk_layer_weights* layers;   /* host array of n_layers entries (copied at init) */
+} pmk_weights;
+
+/* Optional routing outputs of moe_layer_step (device pointers, caller-owned;
+ * each may be NULL). All describe the last MoE layer of the call. */
+typedef struct pmk_routing {
+  int32_t* topk_idx;        /* [T][k]   experts by (logit desc, index asc) */
+  float* topk_w;            /* [T][k]   softmax over the k selected logits */
+  float* router_logits;     /* [T][E]   float32 logits the selection was taken on */
+  int32_t* exp_indptr;      /* [E+1]    prefix sum of per-expert routed rows; last = T k */
+  int32_t* tile_indptr;     /* [E+1]    prefix sum of ceil(count_e / moe_bm) row tiles */
+  int32_t* sorted_tok;      /* [T k]    routed (token) ordered by expert, then token */
+  int32_t* sorted_slot;     /* [T k]    the matching top-k slot j */
+} pmk_routing;
+
+typedef struct pmk_info {
+  int32_t grid;              /* persistent workgroups (one per compute unit) */
+  int32_t block;             /* threads per workgroup */
+  int32_t lds_bytes;         /* dynamic LDS per workgroup */
+  int32_t moe_bm;            /* row-tile size of the grouped GEMM (tile_indptr granularity) */
+  int32_t attn_chunk;        /* KV positions per attention tile task */
+  int32_t max_queue;         /* task-queue capacity per workgroup per layer */
+  int64_t workspace_bytes;   /* device memory owned by the handle */
+  int32_t arch;              /* 950 for gfx950 */
+  int32_t reserved[7];
+} pmk_info;
+
+typedef struct pmk_handle pmk_handle;
+
+/* Create a handle: validates desc and every weight pointer, keeps the weight
+ * pointers (no copy), builds the RoPE cos/sin table on the host in double and
+ * uploads it as float32, allocates the workspace (activations, attention
+ * partials, event counters, task queues, MoE routing arrays, error word) for
+ * max_batch and max_seq, and sizes the persistent grid to the device's compute
+ * units. Errors: PMK_ERR_ARG, PMK_ERR_UNSUPPORTED, PMK_ERR_OOM, PMK_ERR_DEVICE. */
+int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* weights, pmk_handle** out);
+
+/* One decode step of the whole stack for `batch` requests (Event Tensor
+ * summary, Experiments: the end-to-end decode step covers attention, RoPE, KV
+ * cache, norm and MLP; Core method, ETC compiler and scheduling: static
+ * scheduling with a per-compute-unit queue and a persistent main loop).
+ *   hidden    float32 [batch][H], in/out: each request's input hidden state in,
+ *             the stack's output out (no final norm, no vocabulary head).
+ *   kv_cache  model dtype [L][2][max_batch][Hkv][max_seq][d] (K block, then V):
+ *             slots 0..seq_lens[b]-1 hold request b's cached, already-rotated
+ *             keys and values. The step writes the new K/V at slot seq_lens[b]
+ *             (rounded to the cache dtype, nearest even) and attends over
+ *             seq_lens[b] + 1 entries.
+ *   seq_lens  int32 [batch], device: cached length of each request before the
+ *             step. Not modified: the caller advances it.
+ * Two launches (a queue/event prologue and the persistent kernel). Dense
+ * handles only; a MoE handle runs the same step with routed experts.
+ * Errors: PMK_ERR_ARG (batch outside [1, max_batch], null pointer), a pending
+ * device error from an earlier call, PMK_ERR_DEVICE. */
+int decode_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq_lens, int32_t batch, void* stream);
+
+/* One step of a stack of MoE decoder layers for `tokens` tokens, each its own
+ * request (Event Tensor summary, Key observations, observation 2: attention,
+ * then TopK, then grouping, then the grouped GEMM; Core method, two kinds of
+ * dynamism: topk decides which expert's event each grouping task updates, each
+ * expert counter starts at its routed-token count, and the exp_indptr prefix
+ * sum decides which grouped-GEMM tiles an expert triggers). Arguments as for
+ * decode_step; `routing` (nullable) receives the last layer's routing.
+ * Requires a handle made with n_experts > 0. Errors as for decode_step. */
+int moe_layer_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq_lens, int32_t tokens,
+                   const pmk_routing* routing, void* stream);
+
+/* Synchronise the device, free the workspace and the handle. NULL is a no-op. */
+int decode_layer_destroy(pmk_handle* h);
+
+/* Static description of a status code. */
+const char* pmk_strerror(int status);
+
+/* Synchronise the handle's last stream and return the device error word
+ * (PMK_OK, PMK_ERR_TIMEOUT or PMK_ERR_SEQ), then clear it. */
+int pmk_get_device_error(pmk_handle* h);
+
+/* Launch configuration and sizes of a handle. */
+int pmk_query(const pmk_handle* h, pmk_info* out);
+
+/* Per-launch timing of the persistent kernel with HIP events recorded on the
+ * call's stream around that launch only. enable != 0 starts a new window;
+ * pmk_timing_read synchronises, returns the summed milliseconds and the number
+ * of timed launches since the window started. */
+int pmk_timing_enable(pmk_handle* h, int enable);
+int pmk_timing_read(pmk_handle* h, double* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PMK_H */

@@ -1,0 +1,302 @@
+// pmk_api.hip -- host runtime behind the C ABI of include/pmk.h: argument
+// checks, workspace carving, the RoPE table, launch of the prologue and the
+// persistent kernel, device-error readback and optional per-launch timing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "pmk_internal.h"
+
+using namespace pmk;
+
+struct pmk_handle {
+  pmk_model_desc desc;
+  int device = 0;
+  Dims dm{};
+  Workspace ws{};
+  void* ws_base = nullptr;
+  size_t ws_bytes = 0;
+  LayerPtrs* d_layers = nullptr;
+  hipStream_t last_stream = nullptr;
+  unsigned long long watchdog_ticks = 0;
+  bool timing = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> tev;
+  size_t tused = 0;
+};
+
+namespace {
+
+int elem_bytes(int dtype) { return dtype == PMK_BF16 ? 2 : 4; }
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+int check_desc(const pmk_model_desc* d) {
+  if (!d || d->abi_version != PMK_ABI_VERSION) return PMK_ERR_ARG;
+  if (d->dtype != PMK_F32 && d->dtype != PMK_BF16) return PMK_ERR_ARG;
+  if (d->n_layers < 1 || d->hidden < 8 || d->hidden % 8) return PMK_ERR_ARG;
+  if (d->n_q_heads < 1 || d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads) return PMK_ERR_ARG;
+  if (d->head_dim < 2 || d->head_dim % 2) return PMK_ERR_ARG;
+  if (d->max_batch < 1 || d->max_seq < 1) return PMK_ERR_ARG;
+  if (!(d->rms_eps > 0.f) || !(d->rope_theta > 0.f)) return PMK_ERR_ARG;
+  if (d->n_experts < 0) return PMK_ERR_ARG;
+  if (d->n_experts == 0 && (d->ffn_dim < 8 || d->ffn_dim % 8)) return PMK_ERR_ARG;
+  if (d->n_experts > 0 && (d->top_k < 1 || d->top_k > d->n_experts || d->expert_ffn_dim < 8 ||
+                           d->expert_ffn_dim % 8))
+    return PMK_ERR_ARG;
+  // shapes this build implements
+  if (d->head_dim * elem_bytes(d->dtype) != 256) return PMK_ERR_UNSUPPORTED;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return PMK_ERR_UNSUPPORTED;
+  if ((d->n_q_heads * d->head_dim) % 8) return PMK_ERR_UNSUPPORTED;
+  if (d->hidden > kXsFloats || d->ffn_dim > kXsFloats || d->n_q_heads * d->head_dim > kXsFloats)
+    return PMK_ERR_UNSUPPORTED;
+  if (d->n_experts > 0) return PMK_ERR_UNSUPPORTED;
+  return PMK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pmk_strerror(int s) {
+  switch (s) {
+    case PMK_OK: return "ok";
+    case PMK_ERR_ARG: return "invalid argument";
+    case PMK_ERR_OOM: return "device allocation failed";
+    case PMK_ERR_DEVICE: return "HIP runtime call failed";
+    case PMK_ERR_TIMEOUT: return "an event wait exceeded the watchdog; the step was abandoned";
+    case PMK_ERR_SEQ: return "a request length is outside [0, max_seq); the step did not run";
+    case PMK_ERR_UNSUPPORTED:
+      return "shape not implemented: needs head_dim*sizeof(dtype) == 256, Hq/Hkv in {1,2,4,8}, "
+             "H, F, Hq*d <= 32768 and multiples of 8, and (in this build) a dense stack";
+    default: return "unknown status";
+  }
+}
+
+int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_handle** out) {
+  if (!out) return PMK_ERR_ARG;
+  *out = nullptr;
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (!w || w->n_layers != desc->n_layers || !w->layers) return PMK_ERR_ARG;
+  const bool moe = desc->n_experts > 0;
+  for (int l = 0; l < desc->n_layers; ++l) {
+    const pmk_layer_weights& L = w->layers[l];
+    if (!L.attn_norm || !L.w_qkv || !L.w_o || !L.ffn_norm) return PMK_ERR_ARG;
+    if (!moe && (!L.w_gate || !L.w_up || !L.w_down)) return PMK_ERR_ARG;
+    if (moe && (!L.w_router || !L.w_exp_gate || !L.w_exp_up || !L.w_exp_down)) return PMK_ERR_ARG;
+  }
+  pmk_handle* h = new (std::nothrow) pmk_handle();
+  if (!h) return PMK_ERR_OOM;
+  h->desc = *desc;
+  if (hipGetDevice(&h->device) != hipSuccess) { delete h; return PMK_ERR_DEVICE; }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, h->device) != hipSuccess) { delete h; return PMK_ERR_DEVICE; }
+
+  Dims& dm = h->dm;
+  dm.L = desc->n_layers; dm.H = desc->hidden; dm.Hq = desc->n_q_heads; dm.Hkv = desc->n_kv_heads;
+  dm.d = desc->head_dim; dm.F = desc->ffn_dim; dm.E = desc->n_experts; dm.k = desc->top_k;
+  dm.Fe = desc->expert_ffn_dim; dm.max_batch = desc->max_batch; dm.max_seq = desc->max_seq;
+  dm.max_chunks = ceil_div(desc->max_seq, kAttnChunk);
+  dm.eps = desc->rms_eps;
+  dm.grid = prop.multiProcessorCount;
+  dm.moe = moe ? 1 : 0;
+  const int G = dm.grid;
+  dm.qkv_units = (dm.Hq + 2 * dm.Hkv) * dm.d / 2;
+  dm.qkv_tiles = std::min(G, dm.qkv_units);
+  dm.o_tiles = std::min(G, dm.H);
+  dm.gu_tiles = moe ? 0 : std::min(G, dm.F);
+  dm.down_tiles = moe ? 0 : std::min(G, dm.H);
+  dm.router_tiles = 0;
+  // rows per tile must fit the LDS output staging at batch block 1
+  if (2 * ceil_div(dm.qkv_units, dm.qkv_tiles) > kYsFloats || (!moe && 2 * ceil_div(dm.F, dm.gu_tiles) > kYsFloats) ||
+      ceil_div(dm.H, dm.o_tiles) > kYsFloats) {
+    delete h;
+    return PMK_ERR_UNSUPPORTED;
+  }
+  const long attn_max = (long)dm.max_batch * dm.Hkv * dm.max_chunks;
+  dm.max_queue = ceil_div(dm.qkv_tiles, G) + ceil_div(dm.o_tiles, G) + (moe ? 0 : ceil_div(dm.gu_tiles, G)) +
+                 (moe ? 0 : ceil_div(dm.down_tiles, G)) + ceil_div(attn_max, G) + 8;
+
+  // workspace carving
+  const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
+  const int Gq = dm.Hq / dm.Hkv;
+  struct Part { void** p; size_t bytes; };
+  Workspace& ws = h->ws;
+  std::vector<Part> parts = {
+      {(void**)&ws.qkv, (size_t)dm.max_batch * qkv_dim * 4},
+      {(void**)&ws.o, (size_t)dm.max_batch * dm.Hq * dm.d * 4},
+      {(void**)&ws.h1, (size_t)dm.max_batch * dm.H * 4},
+      {(void**)&ws.act, (size_t)dm.max_batch * std::max(dm.F, 1) * 4},
+      {(void**)&ws.part, (size_t)dm.max_batch * dm.Hkv * dm.max_chunks * Gq * (dm.d + 2) * 4},
+      {(void**)&ws.rope, (size_t)dm.max_seq * (dm.d / 2) * 8},
+      {(void**)&ws.ev, (size_t)dm.L * EV_COUNT * kEvInts * 4},
+      {(void**)&ws.mctr, (size_t)dm.L * dm.max_batch * dm.Hkv * kCtr * 4},
+      {(void**)&ws.chunk_base, (size_t)(dm.max_batch + 1) * 4},
+      {(void**)&ws.queue, (size_t)G * dm.max_queue * 16},
+      {(void**)&ws.qlen, (size_t)G * 4},
+      {(void**)&ws.err, 64 * 4},
+      {(void**)&ws.args, sizeof(StepArgs)},
+  };
+  size_t total = 0;
+  for (auto& p : parts) total += align256(p.bytes);
+  void* base = nullptr;
+  if (hipMalloc(&base, total) != hipSuccess) { delete h; return PMK_ERR_OOM; }
+  h->ws_base = base;
+  h->ws_bytes = total;
+  size_t off = 0;
+  for (auto& p : parts) {
+    *p.p = (char*)base + off;
+    off += align256(p.bytes);
+  }
+  auto fail = [&](int code) {
+    decode_layer_destroy(h);
+    return code;
+  };
+  if (hipMemset(base, 0, total) != hipSuccess) return fail(PMK_ERR_DEVICE);
+
+  // RoPE table: angle pos * theta^(-2i/d) in double, cos/sin rounded to float
+  {
+    const int half = dm.d / 2;
+    std::vector<float> tab((size_t)dm.max_seq * half * 2);
+    for (int p = 0; p < dm.max_seq; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double phi = (double)p * std::pow((double)desc->rope_theta, -2.0 * i / (double)dm.d);
+        tab[((size_t)p * half + i) * 2] = (float)std::cos(phi);
+        tab[((size_t)p * half + i) * 2 + 1] = (float)std::sin(phi);
+      }
+    if (hipMemcpy(ws.rope, tab.data(), tab.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
+      return fail(PMK_ERR_DEVICE);
+  }
+  // layer pointer table
+  {
+    std::vector<LayerPtrs> lp(dm.L);
+    for (int l = 0; l < dm.L; ++l) {
+      const pmk_layer_weights& L = w->layers[l];
+      lp[l] = LayerPtrs{L.attn_norm, L.w_qkv, L.w_o, L.ffn_norm, L.w_gate, L.w_up, L.w_down,
+                        L.w_router, L.w_exp_gate, L.w_exp_up, L.w_exp_down};
+    }
+    if (hipMalloc(&h->d_layers, sizeof(LayerPtrs) * dm.L) != hipSuccess) return fail(PMK_ERR_OOM);
+    if (hipMemcpy(h->d_layers, lp.data(), sizeof(LayerPtrs) * dm.L, hipMemcpyHostToDevice) != hipSuccess)
+      return fail(PMK_ERR_DEVICE);
+  }
+  if (prepare_main(desc->dtype) != hipSuccess) return fail(PMK_ERR_DEVICE);
+  const int wd = desc->watchdog_ms > 0 ? desc->watchdog_ms : 2000;
+  h->watchdog_ticks = (unsigned long long)wd * 100000ull;   // s_memrealtime: 100 MHz
+  *out = h;
+  return PMK_OK;
+}
+
+static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_lens, int32_t batch,
+                    const pmk_routing* rout, void* stream) {
+  if (!h || !hidden || !kv || !seq_lens) return PMK_ERR_ARG;
+  if (batch < 1 || batch > h->dm.max_batch) return PMK_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  StepArgs a{};
+  a.dm = h->dm;
+  a.ws = h->ws;
+  a.layers = h->d_layers;
+  a.hidden = hidden;
+  a.kv = kv;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.watchdog_ticks = h->watchdog_ticks;
+  if (rout) a.rout = *rout;
+  h->last_stream = s;
+  if (launch_prologue(a, s) != hipSuccess) return PMK_ERR_DEVICE;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (h->timing) {
+    if (h->tused == h->tev.size()) {
+      hipEvent_t x, y;
+      if (hipEventCreate(&x) != hipSuccess || hipEventCreate(&y) != hipSuccess) return PMK_ERR_DEVICE;
+      h->tev.emplace_back(x, y);
+    }
+    e0 = h->tev[h->tused].first;
+    e1 = h->tev[h->tused].second;
+    ++h->tused;
+    if (hipEventRecord(e0, s) != hipSuccess) return PMK_ERR_DEVICE;
+  }
+  if (launch_main(a, h->desc.dtype, s) != hipSuccess) return PMK_ERR_DEVICE;
+  if (e1 && hipEventRecord(e1, s) != hipSuccess) return PMK_ERR_DEVICE;
+  return PMK_OK;
+}
+
+int decode_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq_lens, int32_t batch, void* stream) {
+  if (h && h->dm.moe) return PMK_ERR_UNSUPPORTED;
+  return run_step(h, hidden, kv_cache, seq_lens, batch, nullptr, stream);
+}
+
+int moe_layer_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq_lens, int32_t tokens,
+                   const pmk_routing* routing, void* stream) {
+  if (!h) return PMK_ERR_ARG;
+  if (!h->dm.moe) return PMK_ERR_ARG;
+  return run_step(h, hidden, kv_cache, seq_lens, tokens, routing, stream);
+}
+
+int decode_layer_destroy(pmk_handle* h) {
+  if (!h) return PMK_OK;
+  int rc = PMK_OK;
+  if (hipDeviceSynchronize() != hipSuccess) rc = PMK_ERR_DEVICE;
+  for (auto& p : h->tev) {
+    (void)hipEventDestroy(p.first);
+    (void)hipEventDestroy(p.second);
+  }
+  if (h->d_layers) (void)hipFree(h->d_layers);
+  if (h->ws_base) (void)hipFree(h->ws_base);
+  delete h;
+  return rc;
+}
+
+int pmk_get_device_error(pmk_handle* h) {
+  if (!h) return PMK_ERR_ARG;
+  if (hipStreamSynchronize(h->last_stream) != hipSuccess) return PMK_ERR_DEVICE;
+  int e = 0;
+  if (hipMemcpy(&e, h->ws.err, 4, hipMemcpyDeviceToHost) != hipSuccess) return PMK_ERR_DEVICE;
+  if (e != 0 && hipMemset(h->ws.err, 0, 64 * 4) != hipSuccess) return PMK_ERR_DEVICE;
+  if (hipDeviceSynchronize() != hipSuccess) return PMK_ERR_DEVICE;
+  return e;
+}
+
+int pmk_query(const pmk_handle* h, pmk_info* out) {
+  if (!h || !out) return PMK_ERR_ARG;
+  std::memset(out, 0, sizeof(*out));
+  out->grid = h->dm.grid;
+  out->block = kBlock;
+  out->lds_bytes = kLdsBytes;
+  out->moe_bm = kMoeBM;
+  out->attn_chunk = kAttnChunk;
+  out->max_queue = h->dm.max_queue;
+  out->workspace_bytes = (int64_t)h->ws_bytes;
+  out->arch = 950;
+  return PMK_OK;
+}
+
+int pmk_timing_enable(pmk_handle* h, int enable) {
+  if (!h) return PMK_ERR_ARG;
+  if (h->tused && hipStreamSynchronize(h->last_stream) != hipSuccess) return PMK_ERR_DEVICE;
+  h->timing = enable != 0;
+  h->tused = 0;
+  return PMK_OK;
+}
+
+int pmk_timing_read(pmk_handle* h, double* total_ms, int32_t* launches) {
+  if (!h || !total_ms || !launches) return PMK_ERR_ARG;
+  double sum = 0.0;
+  for (size_t i = 0; i < h->tused; ++i) {
+    if (hipEventSynchronize(h->tev[i].second) != hipSuccess) return PMK_ERR_DEVICE;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, h->tev[i].first, h->tev[i].second) != hipSuccess) return PMK_ERR_DEVICE;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int32_t)h->tused;
+  return PMK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// pmk_device.h -- device-side building blocks of the persistent decode kernel:
+// device-coherent loads/stores, event notify/wait, wave reductions, bfloat16
+// conversion. gfx950 (CDNA4) only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pmk_internal.h"
+
+namespace pmk {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup data: every intermediate that one workgroup writes and
+// another reads within a step is stored and loaded with device-coherent (sc1)
+// accesses, which go through to the coherence point shared by all XCDs instead
+// of stopping in a per-XCD L2. Together with `s_waitcnt vmcnt(0)` before a
+// counter update, that is what lets a relaxed agent-scope counter carry the
+// data dependency without a full L2 write-back on notify or an L2 invalidate
+// on wait. Weights and already-cached KV entries are immutable during a step
+// and use ordinary cached loads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float ldc(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ldci(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stci(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int atomic_add_relaxed(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+// 16-byte device-coherent load/store at byte offset `off` from a wave-uniform base.
+__device__ __forceinline__ f4v ldc4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
+}
+__device__ __forceinline__ void stc4(__amdgpu_buffer_rsrc_t r, int off, f4v v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, v), r, off, 0, 16);
+}
+
+// Wait until every vector memory operation of this wave has completed
+// (stores acknowledged by the coherence point).
+__device__ __forceinline__ void vm_drain() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ unsigned long long now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// ---------------------------------------------------------------------------
+// Events (Event Tensor summary, Core method: notify = atomic decrement,
+// wait = spin until zero). An event is kEvInts ints: [0] is what waiters spin
+// on; [1 + x] are sub-counters that spread the decrements of many producers
+// over 8 addresses; the producer that takes a sub-counter to zero decrements
+// [0]. The prologue arms [0] with the number of non-empty sub-counters and
+// each sub-counter with its producer count (flat events: [0] = producers).
+// ---------------------------------------------------------------------------
+
+// Whole workgroup: publish this workgroup's completed stores, then notify.
+__device__ __forceinline__ void wg_notify(int* ev, int sub) {
+  vm_drain();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (sub >= 0) {
+      if (atomic_add_relaxed(ev + (1 + sub) * kCtr, -1) == 1) atomic_add_relaxed(ev, -1);
+    } else {
+      atomic_add_relaxed(ev, -1);
+    }
+  }
+}
+
+// Thread 0 only: spin until *ev == 0. Returns false on abort or watchdog
+// expiry (then the error word holds PMK_ERR_TIMEOUT and the abort flag is set,
+// so every other waiting workgroup also leaves its loop).
+__device__ __forceinline__ bool spin_zero(const int* ev, int* err, unsigned long long ticks) {
+  if (ldci(ev) == 0) return true;
+  unsigned long long t0 = now_ticks();
+  for (int it = 0;; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    if (ldci(ev) == 0) return true;
+    if ((it & 15) == 15) {
+      if (ldci(err + 16) != 0) return false;
+      if (now_ticks() - t0 > ticks) {
+        int expected = 0;
+        __hip_atomic_compare_exchange_strong(err, &expected, (int)PMK_ERR_TIMEOUT, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        stci(err + 16, 1);
+        return false;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave reductions (wave64).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// Sum over each aligned group of 16 lanes (a KV row of 256 bytes).
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 8, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 1, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16 <-> float
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+// float -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float rnd(float f) { return f; }
+  static __device__ __forceinline__ void put(float* p, float f) { *p = f; }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float rnd(float f) { return __uint_as_float((uint32_t)f2bf(f) << 16); }
+  static __device__ __forceinline__ void put(uint16_t* p, float f) { *p = f2bf(f); }
+};
+
+// 8 consecutive elements (16 B of bfloat16, or 32 B of float) -> float[8].
+template <typename T> struct Raw8;
+template <> struct Raw8<uint16_t> {
+  uint4 v;
+  __device__ __forceinline__ void load(const uint16_t* p) { v = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+  __device__ __forceinline__ void to(float (&f)[8]) const {
+    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+    f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+  }
+};
+template <> struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void zero() { a = make_float4(0, 0, 0, 0); b = a; }
+  __device__ __forceinline__ void to(float (&f)[8]) const {
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+};
+
+}  // namespace pmk

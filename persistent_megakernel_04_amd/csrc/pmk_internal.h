@@ -1,0 +1,119 @@
+// pmk_internal.h -- definitions shared by the host runtime (pmk_api.hip) and the
+// device code (pmk_kernels.hip) of libpmk. Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pmk.h"
+
+namespace pmk {
+
+constexpr int kBlock = 512;              // threads per persistent workgroup: 8 wave64
+constexpr int kWaves = kBlock / 64;
+constexpr int kSubs = 8;                 // sub-counters of a hierarchical event
+constexpr int kCtr = 16;                 // ints between two counters (64 bytes)
+constexpr int kEvInts = (1 + kSubs) * kCtr;
+constexpr int kAttnChunk = 128;          // KV positions per attention tile task
+constexpr int kMoeBM = 8;                // token rows per grouped-GEMM tile
+constexpr int kXsFloats = 32768;         // LDS staging of GEMV inputs: 128 KiB
+constexpr int kYsFloats = 4096;          // LDS GEMV outputs: 16 KiB
+constexpr int kMiscFloats = 1024;        // LDS scalars, flags, reductions: 4 KiB
+constexpr int kLdsBytes = (kXsFloats + kYsFloats + kMiscFloats) * 4;
+constexpr int kMaxTopK = 8;
+
+// Task types of the per-workgroup queue (one layer's worth; replayed per layer).
+enum TaskType : int {
+  T_QKV = 1,      // a = tile: RMSNorm1 + QKV rows + RoPE + KV append
+  T_ATTN = 2,     // a = b, b = kv group g, c = chunk: split-K GQA attention (+ merge by the last chunk)
+  T_O = 3,        // a = tile: O-projection rows + residual
+  T_GU = 4,       // a = tile: RMSNorm2 + gate/up rows + SwiGLU
+  T_DOWN = 5,     // a = tile: down-projection rows + residual (dense layer output)
+  T_ROUTER = 6,   // a = tile: RMSNorm2 + router logits rows
+  T_ROUTE = 7,    // top-k, gates, expert grouping, expert-event arming (one workgroup)
+  T_MGU = 8,      // slot: this workgroup's share of the grouped gate/up GEMM tasks
+  T_MDOWN = 9,    // slot: this workgroup's share of the grouped down GEMM tasks
+  T_COMBINE = 10  // slot: this workgroup's share of the per-token gated combine
+};
+
+// Events of one layer. Each event is a block of kEvInts ints: [0] is the
+// counter that waiters spin on; [1 + x] (x < kSubs) are sub-counters for
+// hierarchical notification (the last notifier of a sub-counter decrements
+// [0]). Flat events are decremented at [0] directly.
+enum EventId : int {
+  EV_QKV = 0, EV_ATTN, EV_O, EV_GU, EV_DOWN, EV_ROUTER, EV_ROUTE, EV_MGU, EV_MDOWN, EV_COUNT
+};
+
+struct LayerPtrs {
+  const float* attn_norm;
+  const void* w_qkv;
+  const void* w_o;
+  const float* ffn_norm;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* w_router;
+  const void* w_exp_gate;
+  const void* w_exp_up;
+  const void* w_exp_down;
+};
+
+struct Dims {
+  int L, H, Hq, Hkv, d, F, E, k, Fe;
+  int max_batch, max_seq, max_chunks;
+  float eps;
+  int grid;
+  int qkv_units;                     // (Hq + 2 Hkv) d / 2 rotation pairs
+  int qkv_tiles, o_tiles, gu_tiles, down_tiles, router_tiles;
+  int max_queue;
+  int moe;                           // 1 = MoE layers
+};
+
+// Device workspace (one allocation, carved by the host).
+struct Workspace {
+  float* qkv;          // [max_batch][(Hq + 2 Hkv) d]   rotated q, k; v
+  float* o;            // [max_batch][Hq d]             merged attention output
+  float* h1;           // [max_batch][H]                residual after attention
+  float* act;          // [max_batch][F]                SwiGLU output (dense)
+  float* part;         // [max_batch][Hkv][max_chunks][G][d + 2]  attention partials
+  float2* rope;        // [max_seq][d / 2]              (cos, sin)
+  int* ev;             // [L][EV_COUNT][kEvInts]
+  int* mctr;           // [L][max_batch][Hkv][kCtr]     attention merge counters
+  int* chunk_base;     // [max_batch + 1]               prefix sum of chunks per request
+  int4* queue;         // [grid][max_queue]
+  int* qlen;           // [grid]
+  int* err;            // [0] error word, [16] abort flag
+  void* args;          // a copy of this step's StepArgs, written by the prologue
+  // MoE
+  float* logits;       // [max_batch][E]
+  float* u2;           // [max_batch][H]                normalised FFN input
+  int* topk_idx;       // [max_batch][k]
+  float* topk_w;       // [max_batch][k]
+  int* exp_indptr;     // [E + 1]
+  int* tile_indptr;    // [E + 1]
+  int* sorted_tok;     // [max_batch k]
+  int* sorted_slot;    // [max_batch k]
+  int* pos_of;         // [max_batch][k]  row of (t, j) in the grouped order
+  int* moe_info;       // [0] gate/up tasks, [1] down tasks, [2] n-split gate/up, [3] n-split down, [4] tiles
+  int* ectr;           // [L][E][kCtr]                  per-expert counters (gate/up -> down)
+  float* mact;         // [max_batch k][Fe]             expert SwiGLU rows, grouped order
+  float* mout;         // [max_batch k][H]              expert down rows, grouped order
+};
+
+struct StepArgs {
+  Dims dm;
+  Workspace ws;
+  const LayerPtrs* layers;   // device array [L]
+  float* hidden;
+  void* kv;
+  const int32_t* seq_lens;
+  int batch;
+  unsigned long long watchdog_ticks;   // s_memrealtime ticks (100 MHz)
+  pmk_routing rout;                    // optional routing outputs (device pointers)
+};
+
+// Launch wrappers (defined in pmk_kernels.hip).
+hipError_t launch_prologue(const StepArgs& a, hipStream_t s);
+hipError_t launch_main(const StepArgs& a, int dtype, hipStream_t s);
+hipError_t prepare_main(int dtype);
+
+}  // namespace pmk

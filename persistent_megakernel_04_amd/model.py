@@ -1,0 +1,109 @@
+"""A handle on the decode library, holding torch tensors for device memory.
+
+PyTorch provides device memory and streams only; every operation of the decode
+step runs inside libpmk.so's kernels. The methods below pass data pointers and
+the current HIP stream through the C ABI with the same names as the C entry
+points.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _abi
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+class DecodeModel:
+    """Wraps decode_layer_init / decode_step / moe_layer_step / decode_layer_destroy.
+
+    ``layers`` is a list of dicts of device tensors in the library layout
+    (see include/pmk.h); the tensors must stay alive while the model is used
+    (this object keeps references)."""
+
+    def __init__(self, *, dtype: str, n_layers: int, hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                 ffn_dim: int = 0, n_experts: int = 0, top_k: int = 0, expert_ffn_dim: int = 0,
+                 max_batch: int, max_seq: int, rms_eps: float = 1e-5, rope_theta: float = 10000.0,
+                 layers: list, watchdog_ms: int = 0):
+        self.lib = _abi.load()
+        d = _abi.ModelDesc()
+        d.abi_version = _abi.PMK_ABI_VERSION
+        d.dtype = _abi.PMK_BF16 if dtype == "bf16" else _abi.PMK_F32
+        d.n_layers, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim = n_layers, hidden, n_q_heads, n_kv_heads, head_dim
+        d.ffn_dim, d.n_experts, d.top_k, d.expert_ffn_dim = ffn_dim, n_experts, top_k, expert_ffn_dim
+        d.max_batch, d.max_seq, d.rms_eps, d.rope_theta, d.watchdog_ms = max_batch, max_seq, rms_eps, rope_theta, watchdog_ms
+        self.desc = d
+        self._layers = layers
+        arr = (_abi.LayerWeights * n_layers)()
+        for i, L in enumerate(layers):
+            for f in _abi.LAYER_FIELDS:
+                t = L.get(f)
+                setattr(arr[i], f, None if t is None else t.data_ptr())
+        self._arr = arr
+        w = _abi.Weights(n_layers, arr)
+        h = ctypes.c_void_p()
+        _abi.check(self.lib.decode_layer_init(ctypes.byref(d), ctypes.byref(w), ctypes.byref(h)), "decode_layer_init")
+        self.handle = h
+
+    @classmethod
+    def from_workload(cls, w, layers, max_batch, max_seq, n_layers=None, watchdog_ms=0):
+        return cls(dtype=w.dtype, n_layers=w.n_layers if n_layers is None else n_layers, hidden=w.hidden,
+                   n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn_dim=w.ffn_dim,
+                   n_experts=w.n_experts, top_k=w.top_k, expert_ffn_dim=w.expert_ffn_dim, max_batch=max_batch,
+                   max_seq=max_seq, rms_eps=w.rms_eps, rope_theta=w.rope_theta, layers=layers,
+                   watchdog_ms=watchdog_ms)
+
+    # -- entry points -------------------------------------------------------
+    def decode_step(self, hidden: torch.Tensor, kv_cache: torch.Tensor, seq_lens: torch.Tensor) -> int:
+        """Raw status of decode_step (0 = launched)."""
+        return self.lib.decode_step(self.handle, _ptr(hidden), _ptr(kv_cache), _ptr(seq_lens),
+                                    int(hidden.shape[0]), _stream())
+
+    def moe_layer_step(self, hidden, kv_cache, seq_lens, routing: dict | None = None) -> int:
+        r = None
+        if routing is not None:
+            r = _abi.Routing(*[None if routing.get(f) is None else routing[f].data_ptr() for f in _abi.ROUTING_FIELDS])
+        return self.lib.moe_layer_step(self.handle, _ptr(hidden), _ptr(kv_cache), _ptr(seq_lens),
+                                       int(hidden.shape[0]), None if r is None else ctypes.byref(r), _stream())
+
+    def step(self, hidden, kv_cache, seq_lens, routing=None):
+        """Checked call: decode_step (dense) or moe_layer_step (MoE)."""
+        if self.desc.n_experts:
+            _abi.check(self.moe_layer_step(hidden, kv_cache, seq_lens, routing), "moe_layer_step")
+        else:
+            _abi.check(self.decode_step(hidden, kv_cache, seq_lens), "decode_step")
+
+    def device_error(self) -> int:
+        return self.lib.pmk_get_device_error(self.handle)
+
+    def info(self) -> dict:
+        i = _abi.Info()
+        _abi.check(self.lib.pmk_query(self.handle, ctypes.byref(i)), "pmk_query")
+        return {f: getattr(i, f) for f, _ in _abi.Info._fields_ if f != "reserved"}
+
+    def timing_enable(self, on: bool = True):
+        _abi.check(self.lib.pmk_timing_enable(self.handle, 1 if on else 0), "pmk_timing_enable")
+
+    def timing_read(self):
+        ms, n = ctypes.c_double(), ctypes.c_int32()
+        _abi.check(self.lib.pmk_timing_read(self.handle, ctypes.byref(ms), ctypes.byref(n)), "pmk_timing_read")
+        return ms.value, n.value
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.decode_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

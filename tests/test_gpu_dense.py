@@ -1,0 +1,113 @@
+"""GPU parity of decode_step against the CPU oracle (through the C ABI).
+
+Each case prints its name, shape and seed tag before touching the GPU, so a
+failure can be traced from whatever output survives.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _cases import build_case, make_model, oracle_inputs, rel_l2, run_oracle_dense, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def check_dense(orc, case, tol, requests=None, kv_tol=None):
+    inp = oracle_inputs(case, requests)
+    model = make_model(case)
+    announce(f"decode_step {case.w.name} L={case.n_layers} B={case.hidden.shape[0]} lens={to_np(case.seq_lens).tolist()[:8]}")
+    model.step(case.hidden, case.kv, case.seq_lens)
+    torch.cuda.synchronize()
+    assert model.device_error() == 0
+    ref, kv_ref = run_oracle_dense(orc, case, inp)
+    got = to_np(case.hidden).astype(np.float64)[inp["requests"]]
+    err = rel_l2(got, ref)
+    print(f"  rel_l2(hidden) = {err:.3e} (tol {tol})", flush=True)
+    assert err <= tol
+    # the appended K/V entries of every layer, compared in float
+    kv_gpu = case.kv[:, :, inp["requests"]] if requests is not None else case.kv
+    sl = inp["seq_lens"]
+    for i, s in enumerate(sl):
+        a = kv_gpu[:, :, i, :, int(s)].float().cpu().numpy()
+        ref_bits = kv_ref[:, :, i, :, int(s)]
+        b = (ref_bits.astype(np.uint32) << 16).view(np.float32) if ref_bits.dtype == np.uint16 else ref_bits
+        e = rel_l2(a, b)
+        assert e <= (kv_tol if kv_tol is not None else tol), f"appended K/V of request {i}: {e}"
+    model.close()
+    return err
+
+
+def test_c1_tiny_f32(orc):
+    w = synth.get_workload("c1_tiny_f32")
+    case = build_case(w, 1, [128], tag="t1")
+    check_dense(orc, case, w.tol)
+
+
+def test_c1_shapes_ragged_batch_multichunk(orc):
+    """Tiny fp32 layer, batch 3 with ragged lengths spanning several 128-entry
+    attention chunks and the empty-cache case."""
+    w = synth.get_workload("c1_tiny_f32")
+    case = build_case(w, 3, [0, 127, 300], max_seq=512, tag="t2")
+    check_dense(orc, case, w.tol)
+
+
+def test_c1_shapes_two_layers_random_gains(orc):
+    w = synth.get_workload("c1_tiny_f32")
+    case = build_case(w, 2, [5, 257], n_layers=2, max_seq=300, tag="t3", random_gains=True)
+    check_dense(orc, case, w.tol)
+
+
+def test_8b_shape_two_layers_b1(orc):
+    w = synth.get_workload("c2_8b_b1")
+    case = build_case(w, 1, [512], n_layers=2, max_seq=640, tag="t4")
+    check_dense(orc, case, w.tol)
+
+
+def test_8b_shape_ragged_b4(orc):
+    w = synth.get_workload("c3_8b_sweep")
+    lens = synth.ragged_lengths(4, 512, 8192, ("c3_8b_sweep", "lens", 4))
+    case = build_case(w, 4, lens, n_layers=2, max_seq=8193, tag="t5")
+    check_dense(orc, case, w.tol)
+
+
+def test_shape_changes_reuse_handle(orc):
+    """One handle, three calls with different batch sizes and lengths: the
+    queues and event counts are rebuilt on the device each call."""
+    w = synth.get_workload("c1_tiny_f32")
+    base = build_case(w, 4, [10, 20, 30, 40], max_seq=400, max_batch=4, tag="t6")
+    model = make_model(base)
+    for B, lens in ((1, [130]), (4, [3, 260, 99, 384]), (2, [0, 1])):
+        hidden = synth.make_hidden(w, B, B, device="cuda", tag="t6")
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        case = base.__class__(w, 1, base.layers, base.kv, hidden, sl, 4, 400)
+        inp = oracle_inputs(case, list(range(B)))
+        # oracle on the first B request slots of the cache
+        inp["kv"] = np.ascontiguousarray(to_np(base.kv[:, :, :B]))
+        announce(f"reuse handle B={B} lens={lens}")
+        model.step(hidden, base.kv, sl)
+        torch.cuda.synchronize()
+        assert model.device_error() == 0
+        ref, _ = run_oracle_dense(orc, case, inp)
+        assert rel_l2(to_np(hidden), ref) <= w.tol
+    model.close()
+
+
+def test_bad_length_is_reported_and_step_skipped():
+    w = synth.get_workload("c1_tiny_f32")
+    case = build_case(w, 2, [3, 4], max_seq=64, tag="t7")
+    model = make_model(case)
+    before = case.hidden.clone()
+    bad = torch.tensor([3, 64], dtype=torch.int32, device="cuda")
+    announce("bad seq_len")
+    assert model.decode_step(case.hidden, case.kv, bad) == 0     # launched; the device rejects it
+    torch.cuda.synchronize()
+    assert model.device_error() == 5                                # PMK_ERR_SEQ
+    assert torch.equal(case.hidden, before)
+    assert model.device_error() == 0                                # cleared by the read
+    assert model.decode_step(case.hidden, case.kv, case.seq_lens[:0]) == 1   # batch 0: PMK_ERR_ARG
+    model.close()
