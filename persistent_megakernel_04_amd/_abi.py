@@ -16,7 +16,7 @@ PMK_OK, PMK_ERR_ARG, PMK_ERR_OOM, PMK_ERR_DEVICE, PMK_ERR_TIMEOUT, PMK_ERR_SEQ, 
 PMK_F32, PMK_BF16 = 0, 1
 
 EXPORTS = ("decode_layer_init", "decode_step", "moe_layer_step", "decode_layer_destroy", "pmk_strerror",
-           "pmk_get_device_error", "pmk_query", "pmk_timing_enable", "pmk_timing_read")
+           "pmk_get_device_error", "pmk_query", "pmk_timing_enable", "pmk_timing_read", "pmk_trace_attach")
 
 i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -83,6 +83,8 @@ def load():
     L.pmk_timing_enable.restype = i32
     L.pmk_timing_read.argtypes = [vp, P(ctypes.c_double), P(i32)]
     L.pmk_timing_read.restype = i32
+    L.pmk_trace_attach.argtypes = [vp, vp, i32]
+    L.pmk_trace_attach.restype = i32
     _lib = L
     return L
 

@@ -26,6 +26,8 @@ struct pmk_handle {
   hipStream_t last_stream = nullptr;
   unsigned long long watchdog_ticks = 0;
   bool timing = false;
+  uint32_t* trace = nullptr;
+  int trace_cap = 0;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> tev;
   size_t tused = 0;
 };
@@ -208,6 +210,8 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
   a.batch = batch;
   a.watchdog_ticks = h->watchdog_ticks;
   if (rout) a.rout = *rout;
+  a.trace = h->trace;
+  a.trace_cap = h->trace_cap;
   h->last_stream = s;
   if (launch_prologue(a, s) != hipSuccess) return PMK_ERR_DEVICE;
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -274,6 +278,14 @@ int pmk_query(const pmk_handle* h, pmk_info* out) {
   out->max_queue = h->dm.max_queue;
   out->workspace_bytes = (int64_t)h->ws_bytes;
   out->arch = 950;
+  return PMK_OK;
+}
+
+int pmk_trace_attach(pmk_handle* h, uint32_t* buf, int32_t entries_per_wg) {
+  if (!h) return PMK_ERR_ARG;
+  if (buf && entries_per_wg < 2) return PMK_ERR_ARG;
+  h->trace = buf;
+  h->trace_cap = buf ? entries_per_wg : 0;
   return PMK_OK;
 }
 

@@ -109,6 +109,8 @@ struct StepArgs {
   int batch;
   unsigned long long watchdog_ticks;   // s_memrealtime ticks (100 MHz)
   pmk_routing rout;                    // optional routing outputs (device pointers)
+  uint32_t* trace;                     // optional task trace [grid][trace_cap][4], caller-owned
+  int trace_cap;                       // entries per workgroup (entry 0 is the header)
 };
 
 // Launch wrappers (defined in pmk_kernels.hip).

@@ -472,11 +472,14 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
   const int n = a.ws.qlen[wg];
   const int4* q = a.ws.queue + (size_t)wg * dm.max_queue;
   const int G = dm.Hq / dm.Hkv;
+  uint32_t* tr = a.trace ? a.trace + (size_t)wg * a.trace_cap * 4 : nullptr;
+  int tn = 1;
   for (int l = 0; l < dm.L; ++l) {
     Ctx c{a, l, wg, lds, lds + kXsFloats, misc};
     unsigned passed = 0;
     for (int t = 0; t < n; ++t) {
       const int4 task = q[t];
+      const uint32_t t_begin = (uint32_t)now_ticks();
       int need = -1, need_l = l;
       switch (task.x) {
         case T_QKV: if (l > 0) { need = EV_DOWN; need_l = l - 1; } break;
@@ -495,6 +498,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           passed |= bit;
         }
       }
+      const uint32_t t_waited = (uint32_t)now_ticks();
       switch (task.x) {
         case T_QKV: {
           const int nu = (int)((long)(task.y + 1) * dm.qkv_units / dm.qkv_tiles) -
@@ -529,17 +533,29 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
         }
         default: break;
       }
+      if (tr && threadIdx.x == 0 && tn < a.trace_cap) {
+        const uint32_t t_end = (uint32_t)now_ticks();
+        uint32_t* e = tr + (size_t)tn * 4;
+        e[0] = (uint32_t)task.x | ((uint32_t)l << 8) | ((uint32_t)(task.y & 0xffff) << 16);
+        e[1] = t_begin;
+        e[2] = t_waited;
+        e[3] = t_end;
+        ++tn;
+      }
     }
   }
+  if (tr && threadIdx.x == 0) tr[0] = (uint32_t)(tn - 1);
 }
 
 // ---------------------------------------------------------------------------
 // The per-step prologue: validate lengths, build queues, arm events.
 // ---------------------------------------------------------------------------
+// Number of the first `tiles` tasks of a stage (task t runs on workgroup
+// t % grid and notifies sub-counter (t % grid) & (kSubs - 1)) that notify
+// sub-counter x.
 __device__ __forceinline__ int sub_count(int tiles, int grid, int x) {
-  int n = 0;
-  for (int t = 0; t < tiles; ++t) n += (((t % grid) & (kSubs - 1)) == x);
-  return n;
+  auto below = [x](int n) { return n > x ? (n - x + kSubs - 1) / kSubs : 0; };   // w < n with w % kSubs == x
+  return (tiles / grid) * below(grid) + below(tiles % grid);
 }
 
 __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {

@@ -97,6 +97,12 @@ class DecodeModel:
         _abi.check(self.lib.pmk_timing_read(self.handle, ctypes.byref(ms), ctypes.byref(n)), "pmk_timing_read")
         return ms.value, n.value
 
+    def trace_attach(self, buf, entries_per_wg: int = 0):
+        """Attach a device uint32/int32 tensor of grid * entries_per_wg * 4 elements as the task trace
+        (None detaches)."""
+        _abi.check(self.lib.pmk_trace_attach(self.handle, _ptr(buf), int(entries_per_wg)), "pmk_trace_attach")
+        self._trace = buf
+
     def close(self):
         if getattr(self, "handle", None):
             self.lib.decode_layer_destroy(self.handle)
