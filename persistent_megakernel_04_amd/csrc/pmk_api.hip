@@ -55,10 +55,19 @@ int check_desc(const pmk_model_desc* d) {
   if (d->head_dim * elem_bytes(d->dtype) != 256) return PMK_ERR_UNSUPPORTED;
   const int G = d->n_q_heads / d->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PMK_ERR_UNSUPPORTED;
-  if ((d->n_q_heads * d->head_dim) % 8) return PMK_ERR_UNSUPPORTED;
-  if (d->hidden > kXsFloats || d->ffn_dim > kXsFloats || d->n_q_heads * d->head_dim > kXsFloats)
-    return PMK_ERR_UNSUPPORTED;
-  if (d->n_experts > 0) return PMK_ERR_UNSUPPORTED;
+  if (d->max_batch > kMaxBatchAll) return PMK_ERR_UNSUPPORTED;
+  // every GEMV depth must leave room for one staged input row in LDS (float32
+  // inputs, or bfloat16 hi + lo pairs: 4 bytes per element either way)
+  const int xrow_max = kXsBytes / 4 - 64;
+  if (d->hidden > xrow_max || d->n_q_heads * d->head_dim > xrow_max) return PMK_ERR_UNSUPPORTED;
+  if (d->n_experts == 0 && d->ffn_dim > xrow_max) return PMK_ERR_UNSUPPORTED;
+  if (d->n_experts > 0) {
+    // a grouped-GEMM tile stages all of its kMoeBM rows at once
+    const int moe_k_max = kXsBytes / (4 * kMoeBM) - 8;
+    if (d->n_experts > kMaxExperts || d->top_k > kMaxTopK || d->expert_ffn_dim > moe_k_max ||
+        d->hidden > moe_k_max || d->expert_ffn_dim < 16 || d->hidden < 16)
+      return PMK_ERR_UNSUPPORTED;
+  }
   return PMK_OK;
 }
 
@@ -75,8 +84,9 @@ const char* pmk_strerror(int s) {
     case PMK_ERR_TIMEOUT: return "an event wait exceeded the watchdog; the step was abandoned";
     case PMK_ERR_SEQ: return "a request length is outside [0, max_seq); the step did not run";
     case PMK_ERR_UNSUPPORTED:
-      return "shape not implemented: needs head_dim*sizeof(dtype) == 256, Hq/Hkv in {1,2,4,8}, "
-             "H, F, Hq*d <= 32768 and multiples of 8, and (in this build) a dense stack";
+      return "shape not implemented: needs head_dim*sizeof(dtype) == 256, Hq/Hkv in {1,2,4,8}, max_batch <= 1024, "
+             "GEMV depths that fit one LDS input row, and for MoE E <= 512, top_k <= 8, H and Fe small enough "
+             "for 16 staged rows";
     default: return "unknown status";
   }
 }
@@ -105,7 +115,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   dm.L = desc->n_layers; dm.H = desc->hidden; dm.Hq = desc->n_q_heads; dm.Hkv = desc->n_kv_heads;
   dm.d = desc->head_dim; dm.F = desc->ffn_dim; dm.E = desc->n_experts; dm.k = desc->top_k;
   dm.Fe = desc->expert_ffn_dim; dm.max_batch = desc->max_batch; dm.max_seq = desc->max_seq;
-  dm.max_chunks = ceil_div(desc->max_seq, kAttnChunk);
+  dm.max_chunks = ceil_div(desc->max_seq, kMinChunk);
   dm.eps = desc->rms_eps;
   dm.grid = prop.multiProcessorCount;
   dm.moe = moe ? 1 : 0;
@@ -115,28 +125,33 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   dm.o_tiles = std::min(G, dm.H);
   dm.gu_tiles = moe ? 0 : std::min(G, dm.F);
   dm.down_tiles = moe ? 0 : std::min(G, dm.H);
-  dm.router_tiles = 0;
-  // rows per tile must fit the LDS output staging at batch block 1
+  dm.router_tiles = moe ? ceil_div(dm.E, 16) : 0;
+  dm.max_tiles = moe ? ceil_div((long)dm.max_batch * dm.k, kMoeBM) + dm.E : 0;
+  // rows per tile must fit the LDS output staging for one input row
   if (2 * ceil_div(dm.qkv_units, dm.qkv_tiles) > kYsFloats || (!moe && 2 * ceil_div(dm.F, dm.gu_tiles) > kYsFloats) ||
       ceil_div(dm.H, dm.o_tiles) > kYsFloats) {
     delete h;
     return PMK_ERR_UNSUPPORTED;
   }
   const long attn_max = (long)dm.max_batch * dm.Hkv * dm.max_chunks;
-  dm.max_queue = ceil_div(dm.qkv_tiles, G) + ceil_div(dm.o_tiles, G) + (moe ? 0 : ceil_div(dm.gu_tiles, G)) +
-                 (moe ? 0 : ceil_div(dm.down_tiles, G)) + ceil_div(attn_max, G) + 8;
+  dm.max_queue = ceil_div(dm.qkv_tiles, G) + ceil_div(dm.o_tiles, G) + ceil_div(attn_max, G) + 8;
+  if (moe)
+    dm.max_queue += ceil_div((long)dm.router_tiles * ceil_div(dm.max_batch, kMaxNb), G) + 4;
+  else
+    dm.max_queue += ceil_div(dm.gu_tiles, G) + ceil_div(dm.down_tiles, G);
 
   // workspace carving
   const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
   const int Gq = dm.Hq / dm.Hkv;
   struct Part { void** p; size_t bytes; };
   Workspace& ws = h->ws;
+  const size_t TK = (size_t)dm.max_batch * std::max(dm.k, 1);
   std::vector<Part> parts = {
       {(void**)&ws.qkv, (size_t)dm.max_batch * qkv_dim * 4},
       {(void**)&ws.o, (size_t)dm.max_batch * dm.Hq * dm.d * 4},
       {(void**)&ws.h1, (size_t)dm.max_batch * dm.H * 4},
       {(void**)&ws.act, (size_t)dm.max_batch * std::max(dm.F, 1) * 4},
-      {(void**)&ws.part, (size_t)dm.max_batch * dm.Hkv * dm.max_chunks * Gq * (dm.d + 2) * 4},
+      {(void**)&ws.part, (size_t)dm.max_batch * dm.Hkv * dm.max_chunks * Gq * (dm.d + 4) * 4},
       {(void**)&ws.rope, (size_t)dm.max_seq * (dm.d / 2) * 8},
       {(void**)&ws.ev, (size_t)dm.L * EV_COUNT * kEvInts * 4},
       {(void**)&ws.mctr, (size_t)dm.L * dm.max_batch * dm.Hkv * kCtr * 4},
@@ -146,6 +161,23 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
       {(void**)&ws.err, 64 * 4},
       {(void**)&ws.args, sizeof(StepArgs)},
   };
+  if (moe) {
+    const std::vector<Part> mp = {
+        {(void**)&ws.logits, (size_t)dm.max_batch * dm.E * 4},
+        {(void**)&ws.topk_idx, TK * 4},
+        {(void**)&ws.topk_w, TK * 4},
+        {(void**)&ws.exp_indptr, (size_t)(dm.E + 1) * 4},
+        {(void**)&ws.sorted_tok, TK * 4},
+        {(void**)&ws.sorted_slot, TK * 4},
+        {(void**)&ws.pos_of, TK * 4},
+        {(void**)&ws.tile_info, (size_t)dm.max_tiles * 2 * 4},
+        {(void**)&ws.moe_info, 64 * 4},
+        {(void**)&ws.ectr, (size_t)dm.L * dm.E * kCtr * 4},
+        {(void**)&ws.mact, TK * dm.Fe * 4},
+        {(void**)&ws.mout, TK * dm.H * 4},
+    };
+    parts.insert(parts.end(), mp.begin(), mp.end());
+  }
   size_t total = 0;
   for (auto& p : parts) total += align256(p.bytes);
   void* base = nullptr;
@@ -187,6 +219,15 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     if (hipMalloc(&h->d_layers, sizeof(LayerPtrs) * dm.L) != hipSuccess) return fail(PMK_ERR_OOM);
     if (hipMemcpy(h->d_layers, lp.data(), sizeof(LayerPtrs) * dm.L, hipMemcpyHostToDevice) != hipSuccess)
       return fail(PMK_ERR_DEVICE);
+  }
+  // a valid argument block from the start (each step's prologue rewrites it)
+  {
+    StepArgs a0{};
+    a0.dm = dm;
+    a0.ws = ws;
+    a0.layers = h->d_layers;
+    a0.attn_chunk = kMaxChunk;
+    if (hipMemcpy(ws.args, &a0, sizeof(a0), hipMemcpyHostToDevice) != hipSuccess) return fail(PMK_ERR_DEVICE);
   }
   if (prepare_main(desc->dtype) != hipSuccess) return fail(PMK_ERR_DEVICE);
   const int wd = desc->watchdog_ms > 0 ? desc->watchdog_ms : 2000;
@@ -232,7 +273,6 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
 }
 
 int decode_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq_lens, int32_t batch, void* stream) {
-  if (h && h->dm.moe) return PMK_ERR_UNSUPPORTED;
   return run_step(h, hidden, kv_cache, seq_lens, batch, nullptr, stream);
 }
 
@@ -274,7 +314,7 @@ int pmk_query(const pmk_handle* h, pmk_info* out) {
   out->block = kBlock;
   out->lds_bytes = kLdsBytes;
   out->moe_bm = kMoeBM;
-  out->attn_chunk = kAttnChunk;
+  out->attn_chunk = kMaxChunk;
   out->max_queue = h->dm.max_queue;
   out->workspace_bytes = (int64_t)h->ws_bytes;
   out->arch = 950;

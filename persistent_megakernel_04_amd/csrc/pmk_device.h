@@ -11,6 +11,7 @@ namespace pmk {
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef unsigned u4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // Cross-workgroup data: every intermediate that one workgroup writes and
@@ -47,6 +48,16 @@ __device__ __forceinline__ f4v ldc4(__amdgpu_buffer_rsrc_t r, int off) {
 }
 __device__ __forceinline__ void stc4(__amdgpu_buffer_rsrc_t r, int off, f4v v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, v), r, off, 0, 16);
+}
+
+// 16-byte load of immutable data (weights, cached KV) through the global
+// address space: a generic pointer would compile to a flat load, which also
+// counts against the LDS wait counter, so every LDS wait would stall on all
+// weight loads in flight.
+typedef const __attribute__((address_space(1))) u4v* gptr_u4;
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  const u4v v = *(gptr_u4)(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Wait until every vector memory operation of this wave has completed
@@ -97,6 +108,15 @@ __device__ __forceinline__ bool spin_zero(const int* ev, int* err, unsigned long
       }
     }
   }
+}
+
+// Whole workgroup: wait until *ev == 0 (thread 0 spins, the others park at the
+// barrier). `flag` is an LDS int. Returns false if the step was abandoned.
+__device__ __forceinline__ bool wg_wait(const int* ev, int* err, unsigned long long ticks, int* flag) {
+  if (!ev) return true;
+  if (threadIdx.x == 0) *flag = spin_zero(ev, err, ticks) ? 1 : 0;
+  __syncthreads();
+  return *flag != 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -163,6 +183,61 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void zero() { a = make_float4(0, 0, 0, 0); b = a; }
   __device__ __forceinline__ void to(float (&f)[8]) const {
     f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Matrix-core step of the weight-streaming GEMV. One "chunk" is one 16-byte
+// load per lane: lane l holds 16 bytes of weight row (l & 15) of a 16-row group
+// at k-slot group (l >> 4), and the matching 16 bytes of the staged input row
+// (l & 15). One chunk covers KSTEP consecutive k of 16 rows.
+//  bfloat16: one v_mfma_f32_16x16x32_bf16 (8 k per lane group);
+//  float:    four v_mfma_f32_16x16x4_f32 (4 k per lane group, one per MFMA).
+// The 16x16 result D[m][j] (input row m, weight row j) sits in lane
+// j + 16 * (m / 4), element m % 4.
+// ---------------------------------------------------------------------------
+template <typename WT> struct MM;
+template <> struct MM<uint16_t> {
+  static constexpr int EPL = 8;     // elements per 16-byte load
+  static constexpr int KSTEP = 32;
+  static constexpr int XPAD = 8;    // LDS row padding (elements)
+  typedef uint16_t XT;
+  static __device__ __forceinline__ f4v mac(uint4 x, uint4 w, f4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8v, x), __builtin_bit_cast(bf8v, w), c, 0, 0, 0);
+  }
+  // four consecutive inputs -> LDS (8 bytes)
+  static __device__ __forceinline__ void put4(XT* p, f4v v) {
+    uint2 w;
+    w.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
+    w.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    *reinterpret_cast<uint2*>(p) = w;
+  }
+  // two-term split x = hi + lo, both bfloat16 (hi nearest to x, lo nearest to
+  // the remainder): products with bfloat16 weights are exact in the MFMA's
+  // float32 accumulation, so the pair carries x to about 2^-16 relative
+  static __device__ __forceinline__ void put4_split(XT* hi, XT* lo, f4v v) {
+    const f4v h = {__uint_as_float((uint32_t)f2bf(v.x) << 16), __uint_as_float((uint32_t)f2bf(v.y) << 16),
+                   __uint_as_float((uint32_t)f2bf(v.z) << 16), __uint_as_float((uint32_t)f2bf(v.w) << 16)};
+    put4(hi, h);
+    put4(lo, v - h);
+  }
+};
+template <> struct MM<float> {
+  static constexpr int EPL = 4;
+  static constexpr int KSTEP = 16;
+  static constexpr int XPAD = 4;
+  typedef float XT;
+  static __device__ __forceinline__ f4v mac(uint4 x, uint4 w, f4v c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.x), __uint_as_float(w.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.y), __uint_as_float(w.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.z), __uint_as_float(w.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(x.w), __uint_as_float(w.w), c, 0, 0, 0);
+    return c;
+  }
+  static __device__ __forceinline__ void put4(XT* p, f4v v) { *reinterpret_cast<f4v*>(p) = v; }
+  static __device__ __forceinline__ void put4_split(XT* hi, XT* lo, f4v v) {
+    put4(hi, v);
+    put4(lo, f4v{0.f, 0.f, 0.f, 0.f});
   }
 };
 

@@ -13,26 +13,34 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kSubs = 8;                 // sub-counters of a hierarchical event
 constexpr int kCtr = 16;                 // ints between two counters (64 bytes)
 constexpr int kEvInts = (1 + kSubs) * kCtr;
-constexpr int kAttnChunk = 128;          // KV positions per attention tile task
-constexpr int kMoeBM = 8;                // token rows per grouped-GEMM tile
-constexpr int kXsFloats = 32768;         // LDS staging of GEMV inputs: 128 KiB
-constexpr int kYsFloats = 4096;          // LDS GEMV outputs: 16 KiB
-constexpr int kMiscFloats = 1024;        // LDS scalars, flags, reductions: 4 KiB
-constexpr int kLdsBytes = (kXsFloats + kYsFloats + kMiscFloats) * 4;
+constexpr int kMinChunk = 64;            // smallest attention chunk (KV positions per tile task)
+constexpr int kMaxChunk = 256;           // largest attention chunk
+constexpr int kMoeBM = 16;               // token rows per grouped-GEMM tile (one MFMA row block)
 constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxNb = 16;               // batch rows per GEMV pass (MFMA M)
+constexpr int kMaxBatchAll = 1024;       // largest max_batch (prologue LDS)
+
+// LDS layout (bytes): [xs: GEMV inputs | red: cross-wave sums | ys: GEMV outputs | misc]
+constexpr int kXsBytes = 131584;
+constexpr int kRedBytes = 16384;
+constexpr int kYsBytes = 8192;
+constexpr int kMiscBytes = 2048;
+constexpr int kLdsBytes = kXsBytes + kRedBytes + kYsBytes + kMiscBytes;
+constexpr int kYsFloats = kYsBytes / 4;
 
 // Task types of the per-workgroup queue (one layer's worth; replayed per layer).
 enum TaskType : int {
-  T_QKV = 1,      // a = tile: RMSNorm1 + QKV rows + RoPE + KV append
-  T_ATTN = 2,     // a = b, b = kv group g, c = chunk: split-K GQA attention (+ merge by the last chunk)
-  T_O = 3,        // a = tile: O-projection rows + residual
-  T_GU = 4,       // a = tile: RMSNorm2 + gate/up rows + SwiGLU
-  T_DOWN = 5,     // a = tile: down-projection rows + residual (dense layer output)
-  T_ROUTER = 6,   // a = tile: RMSNorm2 + router logits rows
+  T_QKV = 1,      // y = tile: RMSNorm1 + QKV rows + RoPE + KV append
+  T_ATTN = 2,     // y = b, z = kv group g, w = chunk: split-K GQA attention (+ merge by the last chunk)
+  T_O = 3,        // y = tile: O-projection rows + residual
+  T_GU = 4,       // y = tile: RMSNorm2 + gate/up rows + SwiGLU
+  T_DOWN = 5,     // y = tile: down-projection rows + residual (dense layer output)
+  T_ROUTER = 6,   // y = row tile, z = token block: RMSNorm2 + router logits
   T_ROUTE = 7,    // top-k, gates, expert grouping, expert-event arming (one workgroup)
-  T_MGU = 8,      // slot: this workgroup's share of the grouped gate/up GEMM tasks
-  T_MDOWN = 9,    // slot: this workgroup's share of the grouped down GEMM tasks
-  T_COMBINE = 10  // slot: this workgroup's share of the per-token gated combine
+  T_MGU = 8,      // this workgroup's share of the grouped gate/up GEMM tasks
+  T_MDOWN = 9,    // this workgroup's share of the grouped down GEMM tasks
+  T_COMBINE = 10  // this workgroup's share of the per-token gated combine (MoE layer output)
 };
 
 // Events of one layer. Each event is a block of kEvInts ints: [0] is the
@@ -40,7 +48,7 @@ enum TaskType : int {
 // hierarchical notification (the last notifier of a sub-counter decrements
 // [0]). Flat events are decremented at [0] directly.
 enum EventId : int {
-  EV_QKV = 0, EV_ATTN, EV_O, EV_GU, EV_DOWN, EV_ROUTER, EV_ROUTE, EV_MGU, EV_MDOWN, EV_COUNT
+  EV_QKV = 0, EV_ATTN, EV_O, EV_GU, EV_DOWN, EV_ROUTER, EV_ROUTE, EV_MDOWN, EV_COUNT
 };
 
 struct LayerPtrs {
@@ -66,6 +74,7 @@ struct Dims {
   int qkv_tiles, o_tiles, gu_tiles, down_tiles, router_tiles;
   int max_queue;
   int moe;                           // 1 = MoE layers
+  int max_tiles;                     // MoE: bound on grouped-GEMM row tiles
 };
 
 // Device workspace (one allocation, carved by the host).
@@ -74,7 +83,7 @@ struct Workspace {
   float* o;            // [max_batch][Hq d]             merged attention output
   float* h1;           // [max_batch][H]                residual after attention
   float* act;          // [max_batch][F]                SwiGLU output (dense)
-  float* part;         // [max_batch][Hkv][max_chunks][G][d + 2]  attention partials
+  float* part;         // [max_batch][Hkv][max_chunks][G][d + 4]  attention partials (acc, max, sum, pad)
   float2* rope;        // [max_seq][d / 2]              (cos, sin)
   int* ev;             // [L][EV_COUNT][kEvInts]
   int* mctr;           // [L][max_batch][Hkv][kCtr]     attention merge counters
@@ -85,15 +94,14 @@ struct Workspace {
   void* args;          // a copy of this step's StepArgs, written by the prologue
   // MoE
   float* logits;       // [max_batch][E]
-  float* u2;           // [max_batch][H]                normalised FFN input
   int* topk_idx;       // [max_batch][k]
   float* topk_w;       // [max_batch][k]
   int* exp_indptr;     // [E + 1]
-  int* tile_indptr;    // [E + 1]
   int* sorted_tok;     // [max_batch k]
   int* sorted_slot;    // [max_batch k]
   int* pos_of;         // [max_batch][k]  row of (t, j) in the grouped order
-  int* moe_info;       // [0] gate/up tasks, [1] down tasks, [2] n-split gate/up, [3] n-split down, [4] tiles
+  int* tile_info;      // [max_tiles][2]  (expert, first grouped row) of each row tile
+  int* moe_info;       // [0] gate/up tasks, [1] down tasks, [2] gate/up slices, [3] down slices, [4] tiles
   int* ectr;           // [L][E][kCtr]                  per-expert counters (gate/up -> down)
   float* mact;         // [max_batch k][Fe]             expert SwiGLU rows, grouped order
   float* mout;         // [max_batch k][H]              expert down rows, grouped order
@@ -107,6 +115,7 @@ struct StepArgs {
   void* kv;
   const int32_t* seq_lens;
   int batch;
+  int attn_chunk;                      // KV positions per attention task this step (set by the prologue)
   unsigned long long watchdog_ticks;   // s_memrealtime ticks (100 MHz)
   pmk_routing rout;                    // optional routing outputs (device pointers)
   uint32_t* trace;                     // optional task trace [grid][trace_cap][4], caller-owned

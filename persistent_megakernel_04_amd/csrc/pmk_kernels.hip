@@ -2,35 +2,69 @@
 //
 // One decode step = two launches on the caller's stream:
 //  1. pmk_prologue (one workgroup): reads (batch, seq_lens) on the device,
-//     checks every length, derives the attention chunk count of each request,
-//     writes each persistent workgroup's task queue for one layer, and arms
-//     every event counter of every layer. This is the runtime instantiation of
-//     a dependency template whose batch and length dimensions are symbolic
-//     (Event Tensor summary, Core method, two kinds of dynamism: shape
-//     dynamism), so a new batch size or new lengths need no recompilation.
+//     checks every length, picks the attention chunk size, writes each
+//     persistent workgroup's task queue for one layer, and arms every event
+//     counter of every layer. This is the runtime instantiation of a dependency
+//     template whose batch and length dimensions are symbolic (Event Tensor
+//     summary, Core method, two kinds of dynamism: shape dynamism), so a new
+//     batch size or new lengths need no recompilation.
 //  2. pmk_main (one workgroup per compute unit, cooperative launch so that all
 //     are co-resident): every workgroup replays its queue for layer 0, 1, ...,
 //     waiting on the events its tasks consume and notifying the events they
 //     produce (same page, Core method, Event Tensor abstraction and ETC
 //     compiler and scheduling: static scheduling with per-SM queues and a
-//     persistent main loop).
+//     persistent main loop). Each task issues the loads of its weights (or KV
+//     entries) before it waits on its input event (same page, the optional
+//     weight-prefetch pass), so HBM keeps streaming across dependencies.
 //
-// Deadlock freedom: each queue lists its tasks in stage order (QKV, attention,
-// O, FFN stages) and every task only waits on events produced by earlier
-// stages of the same layer or by the previous layer. All workgroups are
-// resident, so by induction on (layer, stage) the earliest unfinished stage
-// always has all its producers done. Every wait is bounded by a watchdog; on
-// expiry the step is abandoned (error word + abort flag), so every wave exits.
+// MoE layers (same page, Key observations, observation 2, and Core method, two
+// kinds of dynamism: data-dependent events) run attention, then router logits,
+// then one workgroup's top-k + grouping (which fills exp_indptr and the tile
+// list and arms one counter per expert with that expert's gate/up task count),
+// then grouped gate/up tasks that each notify their expert's counter, grouped
+// down tasks that wait on their expert's counter, and a per-token combine.
+//
+// Deadlock freedom: each queue lists its tasks in stage order and every task
+// only waits on events produced by earlier stages of the same layer or by the
+// previous layer. All workgroups are resident, so by induction on (layer,
+// stage) the earliest unfinished stage always has all its producers done. Every
+// wait is bounded by a watchdog; on expiry the step is abandoned (error word +
+// abort flag), so every wave exits.
 #include "pmk_device.h"
 
 namespace pmk {
 
-// LDS layout (floats): [xs: GEMV inputs | ys: GEMV outputs | misc]
-constexpr int MISC_RSTD = 0;    // 8 floats: per-row 1/rms of the staged batch block
-constexpr int MISC_RED = 16;    // kWaves * 8 floats: block reduction scratch
-constexpr int MISC_FLAG = 96;   // int: broadcast flag
-constexpr int MISC_OK = 100;    // int: wait result
-constexpr int MISC_ROUTE = 128; // MoE routing scratch (ints)
+// ---------------------------------------------------------------------------
+// LDS
+// ---------------------------------------------------------------------------
+struct Lds {
+  void* xs;        // GEMV input rows (MM<WT>::XT), attention scratch, routing scratch
+  float* red;      // cross-wave partial sums
+  float* ys;       // GEMV outputs [R][nb]
+  float* rstd;     // [kMaxNb] 1/rms of the staged rows
+  float* ssp;      // [kMaxNb][kWaves] per-wave partial sums of squares
+  int* flag;       // wait / last-arriver broadcast
+  uint32_t* tclk;  // [0]: clock when the current task's input event was seen (trace)
+};
+
+__device__ __forceinline__ Lds lds_layout(char* base) {
+  Lds s;
+  s.xs = base;
+  s.red = reinterpret_cast<float*>(base + kXsBytes);
+  s.ys = reinterpret_cast<float*>(base + kXsBytes + kRedBytes);
+  char* m = base + kXsBytes + kRedBytes + kYsBytes;
+  s.rstd = reinterpret_cast<float*>(m);                   // 16 floats
+  s.ssp = reinterpret_cast<float*>(m + 64);               // 128 floats
+  s.flag = reinterpret_cast<int*>(m + 64 + 512);          // 1 int
+  s.tclk = reinterpret_cast<uint32_t*>(m + 64 + 512 + 16);
+  return s;
+}
+
+struct Ctx {
+  const StepArgs& a;
+  int l, wg;
+  Lds s;
+};
 
 __device__ __forceinline__ int* ev_ptr(const StepArgs& a, int layer, int e) {
   return a.ws.ev + ((size_t)layer * EV_COUNT + e) * kEvInts;
@@ -40,176 +74,468 @@ __device__ __forceinline__ size_t kv_off(const Dims& dm, int l, int which, int b
   return (((((size_t)l * 2 + which) * dm.max_batch + b) * dm.Hkv + g) * (size_t)dm.max_seq + pos) * dm.d;
 }
 
+__device__ __forceinline__ bool ctx_wait(const Ctx& c, const int* ev) {
+  if (!ev) return true;
+  const bool ok = wg_wait(ev, c.a.ws.err, c.a.watchdog_ticks, c.s.flag);
+  if (threadIdx.x == 0) *c.s.tclk = (uint32_t)now_ticks();
+  return ok;
+}
+
 // ---------------------------------------------------------------------------
-// Staging of a GEMV input block: xs[b][k] = src[b][k] * gain[k] for b < nb,
-// zero rows for nb <= b < BB. With `norm`, misc[MISC_RSTD + b] = 1/sqrt(mean
-// src[b]^2 + eps) (RMSNorm folded into the GEMV: the dot product uses x*gain
-// and the epilogue multiplies by rstd). src is device-coherent data.
+// The weight-streaming GEMV tile engine.
+//
+//   ys[j][m] = sum_k W[row(j)][k] * xs[m][k],  j < R, m < nb <= 16,
+//   xs[m] = src row m (or src row gather[m]) * gain, rounded to the MFMA input
+//   type; with `norm`, rstd[m] = 1 / sqrt(mean src[m]^2 + eps) (RMSNorm folded
+//   into the GEMV: the epilogue multiplies by rstd).
+//
+// The R rows form RG = ceil(R / 16) row groups, taken RGM at a time; the 8
+// waves split the k range; each wave streams its k slice of the row groups as
+// 16-byte-per-lane loads (16 rows x 64 contiguous bytes per load instruction)
+// through a register ring of KSD k-steps x RGM row groups (16 loads, 16 KiB per
+// wave). The ring is filled before the input event is awaited and refilled as
+// it is consumed. Partial
+// sums of the 8 waves are added in LDS in wave order (deterministic).
 // ---------------------------------------------------------------------------
-template <int BB>
-__device__ void stage_x(const float* src, int ld, int nb, int K, const float* gain, bool norm, float eps,
-                        float* xs, float* misc) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float ss[BB];
+enum RowMode : int { ROWS_CONTIG = 0, ROWS_QKV = 1, ROWS_PAIR = 2 };
+
+struct GemvRows {
+  int mode;
+  const void* base;    // the matrix (CONTIG, QKV) or the first matrix (PAIR)
+  const void* base2;   // PAIR: the second matrix
+  int r0;              // CONTIG/PAIR: first row; QKV: first rotation unit
+  int half;            // PAIR: rows taken from each matrix; QKV: head_dim / 2
+};
+
+template <typename WT>
+__device__ __forceinline__ const WT* row_ptr(const GemvRows& rw, int j, int K) {
+  const WT* b = reinterpret_cast<const WT*>(rw.base);
+  if (rw.mode == ROWS_QKV) {
+    // local row 2u is (head h, i), 2u + 1 is (h, i + d/2): the two rows of a rotation pair
+    const int unit = rw.r0 + (j >> 1), h = unit / rw.half, i = unit - h * rw.half;
+    return b + (size_t)(h * 2 * rw.half + i + (j & 1) * rw.half) * K;
+  }
+  if (rw.mode == ROWS_PAIR && j >= rw.half)
+    return reinterpret_cast<const WT*>(rw.base2) + (size_t)(rw.r0 + j - rw.half) * K;
+  return b + (size_t)(rw.r0 + j) * K;
+}
+
+struct GemvIn {
+  const float* src;    // float32 rows (written this step by other workgroups: device-coherent loads)
+  int ld;              // row stride (elements)
+  const int* gather;   // nullable: staged row m <- src row gather[m] (device-coherent)
+  const float* gain;   // nullable: elementwise gain (RMSNorm weight)
+  int norm;            // compute rstd
+  float eps;
+};
+
+// Stage nb input rows into LDS as the MFMA input type, rows XS apart (SPLIT:
+// each row as a hi part and a lo part, XS apart, rows 2 XS apart), zero
+// beyond K up to Kp; per-row sum of squares -> rstd (when in.norm). Each wave
+// takes 256-element blocks of the rows; a block's sum of squares is a wave
+// reduction added to that wave's slot, and the 8 slots are summed in order.
+template <typename WT, bool SPLIT>
+__device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int Kp, int XS, const Lds& s) {
+  typedef typename MM<WT>::XT XT;
+  XT* xs = reinterpret_cast<XT*>(s.xs);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int BPR = (Kp + 255) >> 8, NBK = nb * BPR;
+  if (lane == 0)
+    for (int m = 0; m < nb; ++m) s.ssp[m * kWaves + wave] = 0.f;
+  for (int base = wave; base < NBK; base += kWaves * 8) {
+    f4v v[8];
 #pragma unroll
-  for (int b = 0; b < BB; ++b) ss[b] = 0.f;
-  const int k4 = K >> 2;
-#pragma unroll
-  for (int b = 0; b < BB; ++b) {
-    float* xr = xs + b * K;
-    if (b < nb) {
-      const auto r = rsrc(src + (size_t)b * ld);
-      for (int i = tid; i < k4; i += kBlock) {
-        f4v v = ldc4(r, i * 16);
-        ss[b] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        if (gain) {
-          const float4 gg = reinterpret_cast<const float4*>(gain)[i];
-          v.x *= gg.x; v.y *= gg.y; v.z *= gg.z; v.w *= gg.w;
+    for (int u = 0; u < 8; ++u) {
+      const int blk = base + u * kWaves;
+      v[u] = f4v{0.f, 0.f, 0.f, 0.f};
+      if (blk < NBK) {
+        const int m = blk / BPR, k = (blk - m * BPR) * 256 + lane * 4;
+        if (k < K) {
+          const int srow = in.gather ? ldci(in.gather + m) : m;
+          v[u] = ldc4(rsrc(in.src + (size_t)srow * in.ld), k * 4);
         }
-        reinterpret_cast<f4v*>(xr)[i] = v;
       }
-    } else {
-      for (int i = tid; i < k4; i += kBlock) reinterpret_cast<f4v*>(xr)[i] = f4v{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int blk = base + u * kWaves;
+      if (blk >= NBK) continue;
+      const int m = blk / BPR, k = (blk - m * BPR) * 256 + lane * 4;
+      f4v x = v[u];
+      if (in.norm) {
+        const float ss = wave_sum(x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w);
+        if (lane == 0) s.ssp[m * kWaves + wave] += ss;
+      }
+      if (in.gain && k < K) {
+        const float4 g = *reinterpret_cast<const float4*>(in.gain + k);
+        x.x *= g.x; x.y *= g.y; x.z *= g.z; x.w *= g.w;
+      }
+      if (k < Kp) {
+        if (SPLIT)
+          MM<WT>::put4_split(xs + (size_t)m * 2 * XS + k, xs + (size_t)m * 2 * XS + XS + k, x);
+        else
+          MM<WT>::put4(xs + (size_t)m * XS + k, x);
+      }
     }
   }
-  if (norm) {
+  __syncthreads();
+  if (in.norm && threadIdx.x < nb) {
+    float ss = 0.f;
+    for (int w = 0; w < kWaves; ++w) ss += s.ssp[threadIdx.x * kWaves + w];
+    s.rstd[threadIdx.x] = 1.0f / sqrtf(ss / (float)K + in.eps);
+  }
+  __syncthreads();
+}
+
+// Per-lane row pointers of row groups [rg0, rg0 + RGM) and the first KSD
+// k-steps of the ring (padded rows and k-steps repeat valid addresses; their
+// products are never accumulated).
+template <typename WT, int RGM, int KSD>
+__device__ __forceinline__ void ring_fill(uint4 (&ring)[KSD][RGM], const WT* (&rp)[RGM], const GemvRows& rw,
+                                          int rg0, int RG, int R, int K, int kl0, int nks_c, int mrow) {
+  typedef MM<WT> T;
 #pragma unroll
-    for (int b = 0; b < BB; ++b) {
-      float s = wave_sum(ss[b]);
-      if (lane == 0) misc[MISC_RED + wave * 8 + b] = s;
+  for (int rg = 0; rg < RGM; ++rg) {
+    const int j = min(min(rg0 + rg, RG - 1) * 16 + mrow, R - 1);
+    rp[rg] = row_ptr<WT>(rw, j, K);
+  }
+#pragma unroll
+  for (int d = 0; d < KSD; ++d) {
+    const int k = min(kl0 + min(d, nks_c) * T::KSTEP, K - T::EPL);
+#pragma unroll
+    for (int rg = 0; rg < RGM; ++rg) ring[d][rg] = ldg16(rp[rg] + k);
+  }
+}
+
+// Returns false if the wait was abandoned (nothing was computed). SPLIT: the
+// input rows are carried as bfloat16 hi + lo pairs, two MFMAs per chunk.
+template <typename WT, int RGM, bool SPLIT>
+__device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb, const int* wait_ev) {
+  typedef MM<WT> T;
+  typedef typename T::XT XT;
+  constexpr int KSD = 16 / RGM;   // 16 chunks (16 KiB per wave) in flight
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, mrow = lane & 15;
+  const int NKS = (K + T::KSTEP - 1) / T::KSTEP;
+  const int ks_lo = wave * NKS / kWaves, nks = (wave + 1) * NKS / kWaves - ks_lo;
+  const int nks_c = nks > 0 ? nks - 1 : 0;
+  const int RG = (R + 15) >> 4;
+  const int Kp = NKS * T::KSTEP, XS = Kp + T::XPAD;
+  const int kl0 = ks_lo * T::KSTEP + grp * T::EPL;   // this lane's first k
+  const int kmax = K - T::EPL;
+
+  uint4 ring[KSD][RGM];
+  const WT* rp[RGM];
+  ring_fill<WT, RGM, KSD>(ring, rp, rw, 0, RG, R, K, kl0, nks_c, mrow);
+  if (!ctx_wait(c, wait_ev)) return false;
+  stage_rows<WT, SPLIT>(in, nb, K, Kp, XS, c.s);
+
+  const XT* xrow = reinterpret_cast<const XT*>(c.s.xs) + (size_t)(mrow < nb ? mrow : 0) * (SPLIT ? 2 : 1) * XS + kl0;
+  const bool xon = mrow < nb;
+  const int per = kRedBytes / 4 / (kWaves * 16 * nb);
+  const int rgb = per < 1 ? 1 : per;
+  for (int rg0 = 0; rg0 < RG; rg0 += RGM) {
+    if (rg0 > 0) ring_fill<WT, RGM, KSD>(ring, rp, rw, rg0, RG, R, K, kl0, nks_c, mrow);
+    const int rgn = min(RGM, RG - rg0);   // row groups of this round that hold real rows
+    f4v acc[RGM];
+#pragma unroll
+    for (int rg = 0; rg < RGM; ++rg) acc[rg] = f4v{0.f, 0.f, 0.f, 0.f};
+    // Branch-free body, so the compiler's wait counts stay exact (a branch
+    // here makes it wait for every load in flight before each MFMA): steps
+    // past this wave's range multiply a zero input; padded row groups
+    // accumulate values that are never read.
+    for (int ks0 = 0; ks0 < nks; ks0 += KSD) {
+#pragma unroll
+      for (int d = 0; d < KSD; ++d) {
+        const int ks = ks0 + d;
+        uint4 xa = *reinterpret_cast<const uint4*>(xrow + min(ks, nks_c) * T::KSTEP);
+        const bool on = xon && ks < nks;
+        xa.x = on ? xa.x : 0u;
+        xa.y = on ? xa.y : 0u;
+        xa.z = on ? xa.z : 0u;
+        xa.w = on ? xa.w : 0u;
+#pragma unroll
+        for (int rg = 0; rg < RGM; ++rg) acc[rg] = T::mac(xa, ring[d][rg], acc[rg]);
+        if (SPLIT) {
+          uint4 xl = *reinterpret_cast<const uint4*>(xrow + XS + min(ks, nks_c) * T::KSTEP);
+          xl.x = on ? xl.x : 0u;
+          xl.y = on ? xl.y : 0u;
+          xl.z = on ? xl.z : 0u;
+          xl.w = on ? xl.w : 0u;
+#pragma unroll
+          for (int rg = 0; rg < RGM; ++rg) acc[rg] = T::mac(xl, ring[d][rg], acc[rg]);
+        }
+        const int k = min(kl0 + min(ks + KSD, nks_c) * T::KSTEP, kmax);
+#pragma unroll
+        for (int rg = 0; rg < RGM; ++rg) ring[d][rg] = ldg16(rp[rg] + k);
+      }
     }
-    __syncthreads();
-    if (tid < BB) {
-      float s = 0.f;
-      for (int w = 0; w < kWaves; ++w) s += misc[MISC_RED + w * 8 + tid];
-      misc[MISC_RSTD + tid] = 1.0f / sqrtf(s / (float)K + eps);
+    // cross-wave reduction of these row groups, rgb at a time
+    for (int g0 = 0; g0 < rgn; g0 += rgb) {
+      const int g1 = min(rgn, g0 + rgb);
+#pragma unroll
+      for (int rg = 0; rg < RGM; ++rg) {
+        if (rg >= g0 && rg < g1) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = grp * 4 + e;
+            if (m < nb) c.s.red[((wave * rgb + (rg - g0)) * nb + m) * 16 + mrow] = acc[rg][e];
+          }
+        }
+      }
+      __syncthreads();
+      const int cnt = (g1 - g0) * nb * 16;
+      for (int t = tid; t < cnt; t += kBlock) {
+        const int jj = t & 15, mm = (t >> 4) % nb, rl = (t >> 4) / nb;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += c.s.red[((w * rgb + rl) * nb + mm) * 16 + jj];
+        const int j = (rg0 + g0 + rl) * 16 + jj;
+        if (j < R) c.s.ys[j * nb + mm] = sum;
+      }
+      __syncthreads();
     }
+  }
+  return true;
+}
+
+// bfloat16 weights take their inputs as hi + lo pairs: a single bfloat16
+// rounding of every activation (2^-9 relative) compounds through a deep stack
+// beyond a 1e-2 output tolerance; the pair carries float32-level accuracy.
+template <typename WT> struct SplitIn { static constexpr bool value = sizeof(WT) == 2; };
+
+template <typename WT>
+__device__ __forceinline__ bool gemv_any(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
+                                         const int* wev) {
+  constexpr bool SP = SplitIn<WT>::value;
+  const int RG = (R + 15) >> 4;
+  if (RG <= 1) return gemv<WT, 1, SP>(c, rw, R, K, in, nb, wev);
+  if (RG <= 2) return gemv<WT, 2, SP>(c, rw, R, K, in, nb, wev);
+  if (RG <= 4) return gemv<WT, 4, SP>(c, rw, R, K, in, nb, wev);
+  return gemv<WT, 8, SP>(c, rw, R, K, in, nb, wev);
+}
+
+// Input rows per GEMV pass for depth K and R output rows: what the LDS input
+// and output staging hold, at most 16 (one MFMA row block).
+template <typename WT>
+__device__ __forceinline__ int pass_rows(int K, int R) {
+  typedef MM<WT> T;
+  const int Kp = ((K + T::KSTEP - 1) / T::KSTEP) * T::KSTEP;
+  int nb = kXsBytes / ((SplitIn<WT>::value ? 2 : 1) * (Kp + T::XPAD) * (int)sizeof(typename T::XT));
+  const int ny = kYsFloats / R;
+  if (ny < nb) nb = ny;
+  return nb < kMaxNb ? nb : kMaxNb;
+}
+
+// ---------------------------------------------------------------------------
+// GEMV passes. Every projection of the step is a sequence of GEMV passes: the
+// rows of one tile (or of one expert slice) against up to 16 staged input
+// rows, then an epilogue that consumes the result. A task yields its passes in
+// order (a batch wider than one pass takes several; a MoE share takes one per
+// grouped task), and the main loop runs each through the one GEMV engine.
+// ---------------------------------------------------------------------------
+enum Epi : int { E_QKV = 0, E_O, E_GU, E_DOWN, E_ROUTER, E_MGU, E_MDOWN };
+
+struct Pass {
+  GemvRows rw;
+  GemvIn in;
+  int R, K, nb;
+  const int* wev;   // event the pass waits on (after its weights are in flight)
+  int epi;
+  int b0;           // first batch row (dense, router) or first grouped row (MoE)
+  int r0;           // first rotation unit (QKV), output row, or expert column
+  int n;            // QKV: rotation units; GU / MoE gate-up: rows per matrix; else rows
+  int e;            // MoE: expert
+};
+
+// Pass p of a GEMV task; false once the task has no pass p.
+template <typename WT>
+__device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, const int* wev, Pass& ps) {
+  const StepArgs& a = c.a;
+  const Dims& dm = a.dm;
+  const LayerPtrs& Lp = a.layers[c.l];
+  const int tile = task.y;
+  ps.wev = p == 0 ? wev : nullptr;
+  ps.e = 0;
+  switch (task.x) {
+    case T_QKV: {   // RMSNorm1 + QKV rotation pairs of the tile
+      const int u0 = (int)((long)tile * dm.qkv_units / dm.qkv_tiles);
+      const int nu = (int)((long)(tile + 1) * dm.qkv_units / dm.qkv_tiles) - u0;
+      const int nbb = pass_rows<WT>(dm.H, 2 * nu), b0 = p * nbb;
+      if (b0 >= a.batch) return false;
+      ps.rw = GemvRows{ROWS_QKV, Lp.w_qkv, nullptr, u0, dm.d >> 1};
+      ps.in = GemvIn{a.hidden + (size_t)b0 * dm.H, dm.H, nullptr, Lp.attn_norm, 1, dm.eps};
+      ps.R = 2 * nu; ps.K = dm.H; ps.nb = min(nbb, a.batch - b0);
+      ps.epi = E_QKV; ps.b0 = b0; ps.r0 = u0; ps.n = nu;
+      return true;
+    }
+    case T_O: {     // O-projection rows of the tile
+      const int K = dm.Hq * dm.d;
+      const int r0 = (int)((long)tile * dm.H / dm.o_tiles), R = (int)((long)(tile + 1) * dm.H / dm.o_tiles) - r0;
+      const int nbb = pass_rows<WT>(K, R), b0 = p * nbb;
+      if (b0 >= a.batch) return false;
+      ps.rw = GemvRows{ROWS_CONTIG, Lp.w_o, nullptr, r0, 0};
+      ps.in = GemvIn{a.ws.o + (size_t)b0 * K, K, nullptr, nullptr, 0, 0.f};
+      ps.R = R; ps.K = K; ps.nb = min(nbb, a.batch - b0);
+      ps.epi = E_O; ps.b0 = b0; ps.r0 = r0; ps.n = R;
+      return true;
+    }
+    case T_GU: {    // RMSNorm2 + gate and up rows of the tile
+      const int r0 = (int)((long)tile * dm.F / dm.gu_tiles), Rh = (int)((long)(tile + 1) * dm.F / dm.gu_tiles) - r0;
+      const int nbb = pass_rows<WT>(dm.H, 2 * Rh), b0 = p * nbb;
+      if (b0 >= a.batch) return false;
+      ps.rw = GemvRows{ROWS_PAIR, Lp.w_gate, Lp.w_up, r0, Rh};
+      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, Lp.ffn_norm, 1, dm.eps};
+      ps.R = 2 * Rh; ps.K = dm.H; ps.nb = min(nbb, a.batch - b0);
+      ps.epi = E_GU; ps.b0 = b0; ps.r0 = r0; ps.n = Rh;
+      return true;
+    }
+    case T_DOWN: {  // down-projection rows of the tile
+      const int r0 = (int)((long)tile * dm.H / dm.down_tiles), R = (int)((long)(tile + 1) * dm.H / dm.down_tiles) - r0;
+      const int nbb = pass_rows<WT>(dm.F, R), b0 = p * nbb;
+      if (b0 >= a.batch) return false;
+      ps.rw = GemvRows{ROWS_CONTIG, Lp.w_down, nullptr, r0, 0};
+      ps.in = GemvIn{a.ws.act + (size_t)b0 * dm.F, dm.F, nullptr, nullptr, 0, 0.f};
+      ps.R = R; ps.K = dm.F; ps.nb = min(nbb, a.batch - b0);
+      ps.epi = E_DOWN; ps.b0 = b0; ps.r0 = r0; ps.n = R;
+      return true;
+    }
+    case T_ROUTER: {  // RMSNorm2 + router rows [16 y, 16 y + 16) for the token block [16 z, 16 z + 16)
+      const int bend = min(a.batch, (task.z + 1) * kMaxNb);
+      const int nbb = pass_rows<WT>(dm.H, 16), b0 = task.z * kMaxNb + p * nbb;
+      if (b0 >= bend) return false;
+      const int r0 = tile * 16;
+      ps.rw = GemvRows{ROWS_CONTIG, Lp.w_router, nullptr, r0, 0};
+      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, Lp.ffn_norm, 1, dm.eps};
+      ps.R = min(16, dm.E - r0); ps.K = dm.H; ps.nb = min(nbb, bend - b0);
+      ps.epi = E_ROUTER; ps.b0 = b0; ps.r0 = r0; ps.n = ps.R;
+      return true;
+    }
+    case T_MGU: {   // grouped gate/up task i = (row tile i / sg, Fe slice i % sg) of this workgroup's share
+      const int i = c.wg + p * dm.grid;
+      if (i >= ldci(a.ws.moe_info + 0)) return false;
+      const int sg = ldci(a.ws.moe_info + 2), t = i / sg, sl = i - t * sg;
+      const int e = ldci(a.ws.tile_info + 2 * t), row0 = ldci(a.ws.tile_info + 2 * t + 1);
+      const int f0 = (int)((long)sl * dm.Fe / sg), Rh = (int)((long)(sl + 1) * dm.Fe / sg) - f0;
+      const size_t eo = (size_t)e * dm.Fe * dm.H;
+      ps.rw = GemvRows{ROWS_PAIR, reinterpret_cast<const WT*>(Lp.w_exp_gate) + eo,
+                       reinterpret_cast<const WT*>(Lp.w_exp_up) + eo, f0, Rh};
+      // the tile's rows: its routed tokens' FFN inputs (RMSNorm2 of h1), gathered
+      ps.in = GemvIn{a.ws.h1, dm.H, a.ws.sorted_tok + row0, Lp.ffn_norm, 1, dm.eps};
+      ps.R = 2 * Rh; ps.K = dm.H; ps.nb = min(kMoeBM, ldci(a.ws.exp_indptr + e + 1) - row0);
+      ps.epi = E_MGU; ps.b0 = row0; ps.r0 = f0; ps.n = Rh; ps.e = e;
+      return true;
+    }
+    case T_MDOWN: {  // grouped down task i = (row tile i / sd, H slice i % sd); waits on its expert's counter
+      const int i = c.wg + p * dm.grid;
+      if (i >= ldci(a.ws.moe_info + 1)) return false;
+      const int sd = ldci(a.ws.moe_info + 3), t = i / sd, sl = i - t * sd;
+      const int e = ldci(a.ws.tile_info + 2 * t), row0 = ldci(a.ws.tile_info + 2 * t + 1);
+      const int h0 = (int)((long)sl * dm.H / sd), R = (int)((long)(sl + 1) * dm.H / sd) - h0;
+      ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(Lp.w_exp_down) + (size_t)e * dm.H * dm.Fe, nullptr, h0,
+                       0};
+      ps.in = GemvIn{a.ws.mact + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f};
+      ps.R = R; ps.K = dm.Fe; ps.nb = min(kMoeBM, ldci(a.ws.exp_indptr + e + 1) - row0);
+      ps.wev = a.ws.ectr + ((size_t)c.l * dm.E + e) * kCtr;
+      ps.epi = E_MDOWN; ps.b0 = row0; ps.r0 = h0; ps.n = R; ps.e = e;
+      return true;
+    }
+    default: return false;
+  }
+}
+
+// Consume a pass's result (ys[j][m], rstd[m] in LDS) and store its outputs.
+template <typename WT>
+__device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps) {
+  const StepArgs& a = c.a;
+  const Dims& dm = a.dm;
+  const int nb = ps.nb, b0 = ps.b0;
+  const float* ys = c.s.ys;
+  switch (ps.epi) {
+    case E_QKV: {   // RoPE at each request's position, then q/k/v out and the K/V append
+      const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
+      for (int idx = threadIdx.x; idx < ps.n * nb; idx += kBlock) {
+        const int ju = idx / nb, m = idx - ju * nb;
+        const int unit = ps.r0 + ju, h = unit / half, i = unit - h * half;
+        const float r = c.s.rstd[m];
+        float y1 = ys[(2 * ju) * nb + m] * r, y2 = ys[(2 * ju + 1) * nb + m] * r;
+        const int bb = b0 + m, pos = a.seq_lens[bb];
+        if (h < dm.Hq + dm.Hkv) {
+          const float2 cs = a.ws.rope[(size_t)pos * half + i];
+          const float t1 = y1 * cs.x - y2 * cs.y, t2 = y2 * cs.x + y1 * cs.y;
+          y1 = t1;
+          y2 = t2;
+        }
+        float* dst = a.ws.qkv + (size_t)bb * qkv_dim + h * dm.d + i;
+        stc(dst, y1);
+        stc(dst + half, y2);
+        if (h >= dm.Hq) {
+          const int kvh = h - dm.Hq, which = kvh / dm.Hkv, g = kvh - which * dm.Hkv;
+          WT* cp = reinterpret_cast<WT*>(a.kv) + kv_off(dm, c.l, which, bb, g, pos);
+          Elem<WT>::put(cp + i, y1);
+          Elem<WT>::put(cp + i + half, y2);
+        }
+      }
+      break;
+    }
+    case E_O:       // h1 = x + W_o o
+    case E_DOWN: {  // x' = h1 + W_down act (the layer output, into hidden)
+      const float* res = ps.epi == E_O ? a.hidden : a.ws.h1;
+      float* out = ps.epi == E_O ? a.ws.h1 : a.hidden;
+      for (int idx = threadIdx.x; idx < ps.n * nb; idx += kBlock) {
+        const int j = idx / nb, m = idx - j * nb;
+        const size_t off = (size_t)(b0 + m) * dm.H + ps.r0 + j;
+        stc(out + off, ldc(res + off) + ys[j * nb + m]);
+      }
+      break;
+    }
+    case E_GU:      // act = silu(gate) * up
+    case E_MGU: {
+      const int Rh = ps.n;
+      float* out = ps.epi == E_GU ? a.ws.act : a.ws.mact;
+      const int ld = ps.epi == E_GU ? dm.F : dm.Fe;
+      for (int idx = threadIdx.x; idx < Rh * nb; idx += kBlock) {
+        const int j = idx / nb, m = idx - j * nb;
+        const float r = c.s.rstd[m];
+        const float gt = ys[j * nb + m] * r, up = ys[(Rh + j) * nb + m] * r;
+        stc(out + (size_t)(b0 + m) * ld + ps.r0 + j, gt / (1.0f + __expf(-gt)) * up);
+      }
+      if (ps.epi == E_MGU) {   // this task of expert e is done
+        wg_notify(a.ws.ectr + ((size_t)c.l * dm.E + ps.e) * kCtr, -1);
+        return;
+      }
+      break;
+    }
+    case E_ROUTER: {
+      for (int idx = threadIdx.x; idx < ps.n * nb; idx += kBlock) {
+        const int j = idx / nb, m = idx - j * nb;
+        stc(a.ws.logits + (size_t)(b0 + m) * dm.E + ps.r0 + j, ys[j * nb + m] * c.s.rstd[m]);
+      }
+      break;
+    }
+    case E_MDOWN: {
+      for (int idx = threadIdx.x; idx < ps.n * nb; idx += kBlock) {
+        const int j = idx / nb, m = idx - j * nb;
+        stc(a.ws.mout + (size_t)(b0 + m) * dm.H + ps.r0 + j, ys[j * nb + m]);
+      }
+      break;
+    }
+    default: break;
   }
   __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
-// GEMV core: ys[j][b] = sum_k W[row(j)][k] xs[b][k] for j < R, b < BB.
-// Wave w takes rows w, w+8, ...; each lane streams 16 B of a row per load
-// (a wave reads 1 KiB contiguous per instruction), U loads in flight per wave.
+// Split-K GQA decode attention for (request b, KV head g, chunk ci): the G
+// query heads of group g against positions [ci*ck, min((ci+1)*ck, S+1)).
+// Lanes 16r..16r+15 of a wave hold one KV position (16 bytes each, so a 256-B
+// row); a wave covers 4 positions per step and the workgroup 32; ITS steps
+// cover the chunk. The cached rows are loaded before the QKV event is awaited
+// (they do not depend on this step); the new position S uses this step's
+// rotated k and v, rounded exactly as they were stored into the cache. A chunk
+// writes its (acc, max, sum) partial; the workgroup that completes the last
+// chunk of (b, g) merges all partials by log-sum-exp and notifies. A request
+// with a single chunk writes its output directly.
 // ---------------------------------------------------------------------------
-struct RowsContig {
-  int r0;
-  __device__ __forceinline__ int operator()(int j) const { return r0 + j; }
-};
-// QKV tiles are in rotation pairs: local row 2u is (h, i), 2u+1 is (h, i + d/2).
-struct RowsQkv {
-  int u0, d;
-  __device__ __forceinline__ int operator()(int j) const {
-    const int half = d >> 1, unit = u0 + (j >> 1);
-    return (unit / half) * d + (unit % half) + (j & 1) * half;
-  }
-};
-
-template <typename WT, int BB, typename RowMap>
-__device__ void gemv(const WT* __restrict__ W, int K, int R, RowMap rm, const float* xs, float* ys) {
-  constexpr int U = sizeof(WT) == 2 ? 8 : 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nch = (K + 511) >> 9;
-  for (int j = wave; j < R; j += kWaves) {
-    const WT* wr = W + (size_t)rm(j) * K;
-    float acc[BB];
-#pragma unroll
-    for (int b = 0; b < BB; ++b) acc[b] = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += U) {
-      Raw8<WT> raw[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = ((c0 + u) << 9) + (lane << 3);
-        if (c0 + u < nch && k < K) raw[u].load(wr + k); else raw[u].zero();
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = ((c0 + u) << 9) + (lane << 3);
-        if (c0 + u < nch && k < K) {
-          float w[8];
-          raw[u].to(w);
-#pragma unroll
-          for (int b = 0; b < BB; ++b) {
-            const float4 x0 = *reinterpret_cast<const float4*>(xs + b * K + k);
-            const float4 x1 = *reinterpret_cast<const float4*>(xs + b * K + k + 4);
-            acc[b] += w[0] * x0.x + w[1] * x0.y + w[2] * x0.z + w[3] * x0.w +
-                      w[4] * x1.x + w[5] * x1.y + w[6] * x1.z + w[7] * x1.w;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < BB; ++b) {
-      const float s = wave_sum(acc[b]);
-      if (lane == 0) ys[j * BB + b] = s;
-    }
-  }
-}
-
-// Largest batch block (1, 2, 4 or 8) that fits the LDS staging for a GEMV of
-// depth K producing R rows, and is not wider than the batch needs.
-__device__ __forceinline__ int pick_bb(int batch, int K, int R) {
-  int lim = kXsFloats / K;
-  if (kYsFloats / R < lim) lim = kYsFloats / R;
-  int bb = 8;
-  while (bb > 1 && (bb > lim || (bb >> 1) >= batch)) bb >>= 1;
-  return bb;
-}
-
-// ---------------------------------------------------------------------------
-// Task bodies
-// ---------------------------------------------------------------------------
-struct Ctx {
-  const StepArgs& a;
-  int l, wg;
-  float* xs;
-  float* ys;
-  float* misc;
-};
-
-// RMSNorm1 + QKV rows of one tile + RoPE + KV append.
-template <typename WT, int BB>
-__device__ __noinline__ void task_qkv(const Ctx c, int tile) {
-  const StepArgs& a = c.a;
-  const Dims& dm = a.dm;
-  const LayerPtrs& L = a.layers[c.l];
-  const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
-  const int u0 = (int)((long)tile * dm.qkv_units / dm.qkv_tiles);
-  const int u1 = (int)((long)(tile + 1) * dm.qkv_units / dm.qkv_tiles);
-  const int nu = u1 - u0;
-  for (int b0 = 0; b0 < a.batch; b0 += BB) {
-    const int nb = min(BB, a.batch - b0);
-    stage_x<BB>(a.hidden + (size_t)b0 * dm.H, dm.H, nb, dm.H, L.attn_norm, true, dm.eps, c.xs, c.misc);
-    gemv<WT, BB>(reinterpret_cast<const WT*>(L.w_qkv), dm.H, 2 * nu, RowsQkv{u0, dm.d}, c.xs, c.ys);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < nu * nb; idx += kBlock) {
-      const int ju = idx / nb, b = idx - ju * nb;
-      const int unit = u0 + ju, h = unit / half, i = unit - h * half;
-      const float r = c.misc[MISC_RSTD + b];
-      float y1 = c.ys[(2 * ju) * BB + b] * r, y2 = c.ys[(2 * ju + 1) * BB + b] * r;
-      const int bb = b0 + b, pos = a.seq_lens[bb];
-      if (h < dm.Hq + dm.Hkv) {
-        const float2 cs = a.ws.rope[(size_t)pos * half + i];
-        const float t1 = y1 * cs.x - y2 * cs.y, t2 = y2 * cs.x + y1 * cs.y;
-        y1 = t1;
-        y2 = t2;
-      }
-      float* dst = a.ws.qkv + (size_t)bb * qkv_dim + h * dm.d + i;
-      stc(dst, y1);
-      stc(dst + half, y2);
-      if (h >= dm.Hq) {
-        const int kvh = h - dm.Hq, which = kvh / dm.Hkv, g = kvh - which * dm.Hkv;
-        WT* cp = reinterpret_cast<WT*>(a.kv) + kv_off(dm, c.l, which, bb, g, pos);
-        Elem<WT>::put(cp + i, y1);
-        Elem<WT>::put(cp + i + half, y2);
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// A KV row slice of 16 bytes (8 bfloat16 or 4 float) as raw bits.
 template <typename KT> __device__ __forceinline__ void unpack_row(const uint4 r, float (&f)[16 / sizeof(KT)]);
 template <> __device__ __forceinline__ void unpack_row<uint16_t>(const uint4 r, float (&f)[8]) {
   f[0] = bf_lo(r.x); f[1] = bf_hi(r.x); f[2] = bf_lo(r.y); f[3] = bf_hi(r.y);
@@ -221,87 +547,81 @@ template <> __device__ __forceinline__ void unpack_row<float>(const uint4 r, flo
 // Device-coherent float row slice -> cache-dtype bits (rounded like the KV append).
 template <typename KT> __device__ __forceinline__ uint4 pack_row(const float* p);
 template <> __device__ __forceinline__ uint4 pack_row<uint16_t>(const float* p) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(ldc(p + 2 * i)) | ((uint32_t)f2bf(ldc(p + 2 * i + 1)) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  const auto r = rsrc(p);
+  const f4v a = ldc4(r, 0), b = ldc4(r, 16);
+  return make_uint4((uint32_t)f2bf(a.x) | ((uint32_t)f2bf(a.y) << 16), (uint32_t)f2bf(a.z) | ((uint32_t)f2bf(a.w) << 16),
+                    (uint32_t)f2bf(b.x) | ((uint32_t)f2bf(b.y) << 16), (uint32_t)f2bf(b.z) | ((uint32_t)f2bf(b.w) << 16));
 }
 template <> __device__ __forceinline__ uint4 pack_row<float>(const float* p) {
-  return make_uint4(__float_as_uint(ldc(p)), __float_as_uint(ldc(p + 1)), __float_as_uint(ldc(p + 2)),
-                    __float_as_uint(ldc(p + 3)));
+  const f4v a = ldc4(rsrc(p), 0);
+  return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
 }
 
-// Split-K GQA decode attention for (request b, KV head g, chunk ci): the G
-// query heads of group g against positions [ci*CK, min((ci+1)*CK, S+1)).
-// Writes the chunk's (acc, max, sum) partial; the workgroup that completes the
-// last chunk of (b, g) merges all partials by log-sum-exp and notifies.
-template <typename KT, int G>
-__device__ __noinline__ void task_attn(const Ctx c, int b, int g, int ci) {
+template <typename KT, int HB, int ITS>
+__device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, const int* wev) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   constexpr int EPL = 16 / (int)sizeof(KT);   // elements per lane (16 B)
   constexpr int D = 16 * EPL;                 // head_dim: 128 (bf16) or 64 (f32)
-  constexpr int ITS = kAttnChunk / (kWaves * 4);
+  constexpr int DP = D + 4;                   // partial record: acc[D], max, sum, pad
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rs = lane >> 4, li = lane & 15;
+  const int G = dm.Hq / dm.Hkv;               // query heads of the group, a multiple of HB
+  const int ck = ITS * 32;
   const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * D;
   const int S = a.seq_lens[b], n = S + 1;
-  const int p0 = ci * kAttnChunk, p1 = min(n, p0 + kAttnChunk);
+  const int p0 = ci * ck, p1 = min(n, p0 + ck);
+  const int nc = (n + ck - 1) / ck;
+
+  const KT* Kb = reinterpret_cast<const KT*>(a.kv) + kv_off(dm, c.l, 0, b, g, 0) + li * EPL;
+  const KT* Vb = reinterpret_cast<const KT*>(a.kv) + kv_off(dm, c.l, 1, b, g, 0) + li * EPL;
+  uint4 kr[ITS], vr[ITS];
+  const int pmax = S > 0 ? S - 1 : 0;
+#pragma unroll
+  for (int it = 0; it < ITS; ++it) {
+    const int p = min(p0 + it * 32 + wave * 4 + rs, pmax);   // cached slots only (others replaced or unused)
+    kr[it] = ldg16(Kb + (size_t)p * D);
+    vr[it] = ldg16(Vb + (size_t)p * D);
+  }
+  if (!ctx_wait(c, wev)) return false;
+
+  float* sw = reinterpret_cast<float*>(c.s.xs);     // [kWaves][G][DP] per-wave partials
+  float* qs = sw + kWaves * 8 * DP;                  // [G][D] this group's rotated queries
+  const float* qrow = a.ws.qkv + (size_t)b * qkv_dim + (size_t)g * G * D;
+  for (int t = tid; t < G * D / 4; t += kBlock) *reinterpret_cast<f4v*>(qs + 4 * t) = ldc4(rsrc(qrow), 16 * t);
+  uint4 kn = make_uint4(0, 0, 0, 0), vn = kn;
+  if (S >= p0 && S < p1) {
+    kn = pack_row<KT>(a.ws.qkv + (size_t)b * qkv_dim + (size_t)(dm.Hq + g) * D + li * EPL);
+    vn = pack_row<KT>(a.ws.qkv + (size_t)b * qkv_dim + (size_t)(dm.Hq + dm.Hkv + g) * D + li * EPL);
+  }
+  __syncthreads();
   const float qscale = 1.4426950408889634f / sqrtf((float)D);   // 1/sqrt(d), in log2 units
 
-  const float* qrow = a.ws.qkv + (size_t)b * qkv_dim + (size_t)g * G * D;
-  float q[G][EPL];
+  for (int h0 = 0; h0 < G; h0 += HB) {
+    float q[HB][EPL], m[HB], ls[HB], acc[HB][EPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int h = 0; h < HB; ++h) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) q[h][e] = ldc(qrow + h * D + li * EPL + e) * qscale;
-
-  const KT* Kb = reinterpret_cast<const KT*>(a.kv) + kv_off(dm, c.l, 0, b, g, 0);
-  const KT* Vb = reinterpret_cast<const KT*>(a.kv) + kv_off(dm, c.l, 1, b, g, 0);
-  const float* knew = a.ws.qkv + (size_t)b * qkv_dim + (size_t)(dm.Hq + g) * D;
-  const float* vnew = a.ws.qkv + (size_t)b * qkv_dim + (size_t)(dm.Hq + dm.Hkv + g) * D;
-
-  float m[G], ls[G], acc[G][EPL];
+      for (int e = 0; e < EPL; ++e) q[h][e] = qs[(h0 + h) * D + li * EPL + e] * qscale;
+      m[h] = -INFINITY;
+      ls[h] = 0.f;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    ls[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
-  }
-  // KV rows in flight per lane group, kept as raw 16-byte vectors until use:
-  // all ITS iterations for small groups, two at a time for G = 8
-  constexpr int ITB = G >= 8 ? 2 : ITS;
-#pragma unroll
-  for (int it0 = 0; it0 < ITS; it0 += ITB) {
-    uint4 kr[ITB], vr[ITB];
-#pragma unroll
-    for (int ib = 0; ib < ITB; ++ib) {
-      const int p = p0 + (it0 + ib) * (kWaves * 4) + wave * 4 + rs;
-      if (p < p1 && p != S) {
-        kr[ib] = *reinterpret_cast<const uint4*>(Kb + (size_t)p * D + li * EPL);
-        vr[ib] = *reinterpret_cast<const uint4*>(Vb + (size_t)p * D + li * EPL);
-      } else if (p == S) {
-        // the new token: this step's rotated k and v, rounded exactly as they
-        // were stored into the cache
-        kr[ib] = pack_row<KT>(knew + li * EPL);
-        vr[ib] = pack_row<KT>(vnew + li * EPL);
-      }
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
     }
 #pragma unroll
-    for (int ib = 0; ib < ITB; ++ib) {
-      const int p = p0 + (it0 + ib) * (kWaves * 4) + wave * 4 + rs;
+    for (int it = 0; it < ITS; ++it) {
+      const int p = p0 + it * 32 + wave * 4 + rs;
       if (p < p1) {
         float kf[EPL], vf[EPL];
-        unpack_row<KT>(kr[ib], kf);
-        unpack_row<KT>(vr[ib], vf);
+        unpack_row<KT>(p == S ? kn : kr[it], kf);
+        unpack_row<KT>(p == S ? vn : vr[it], vf);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float s = 0.f;
+        for (int h = 0; h < HB; ++h) {
+          float sc = 0.f;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) s += q[h][e] * kf[e];
-          s = sum16(s);
-          const float mn = fmaxf(m[h], s);
-          const float al = exp2f(m[h] - mn), pe = exp2f(s - mn);
+          for (int e = 0; e < EPL; ++e) sc += q[h][e] * kf[e];
+          sc = sum16(sc);
+          const float mn = fmaxf(m[h], sc);
+          const float al = exp2f(m[h] - mn), pe = exp2f(sc - mn);
           ls[h] = ls[h] * al + pe;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * al + pe * vf[e];
@@ -309,236 +629,379 @@ __device__ __noinline__ void task_attn(const Ctx c, int b, int g, int ci) {
         }
       }
     }
-  }
-  // combine the 4 row slots of the wave
-  float* sw = c.xs;   // [kWaves][G][D + 2]
+    // combine the 4 position slots of the wave into this wave's LDS record
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float M = fmaxf(m[h], __shfl_xor(m[h], 16, 64));
-    M = fmaxf(M, __shfl_xor(M, 32, 64));
-    const float sc = (M == -INFINITY) ? 0.f : exp2f(m[h] - M);
-    float lw = ls[h] * sc;
-    lw += __shfl_xor(lw, 16, 64);
-    lw += __shfl_xor(lw, 32, 64);
-    float* dst = sw + (wave * G + h) * (D + 2);
+    for (int h = 0; h < HB; ++h) {
+      float M = fmaxf(m[h], __shfl_xor(m[h], 16, 64));
+      M = fmaxf(M, __shfl_xor(M, 32, 64));
+      const float sc = (M == -INFINITY) ? 0.f : exp2f(m[h] - M);
+      float lw = ls[h] * sc;
+      lw += __shfl_xor(lw, 16, 64);
+      lw += __shfl_xor(lw, 32, 64);
+      float* dst = sw + (wave * G + h0 + h) * DP;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      float v = acc[h][e] * sc;
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (rs == 0) dst[li * EPL + e] = v;
+      for (int e = 0; e < EPL; ++e) {
+        float v = acc[h][e] * sc;
+        v += __shfl_xor(v, 16, 64);
+        v += __shfl_xor(v, 32, 64);
+        if (rs == 0) dst[li * EPL + e] = v;
+      }
+      if (lane == 0) { dst[D] = M; dst[D + 1] = lw; }
     }
-    if (lane == 0) { dst[D] = M; dst[D + 1] = lw; }
   }
   __syncthreads();
-  // combine waves, write this chunk's partial
-  float* part = a.ws.part + (((size_t)b * dm.Hkv + g) * dm.max_chunks + ci) * G * (D + 2);
-  for (int t = tid; t < G * D; t += kBlock) {
-    const int h = t / D, e = t - h * D;
+  // combine the 8 waves: this chunk's partial (or the output for a single chunk)
+  float* o = a.ws.o + (size_t)b * dm.Hq * D + (size_t)g * G * D;
+  float* part = a.ws.part + (((size_t)b * dm.Hkv + g) * dm.max_chunks + ci) * G * DP;
+  for (int t = tid; t < G * D / 4; t += kBlock) {
+    const int h = t / (D / 4), e0 = (t - h * (D / 4)) * 4;
     float M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sw[(w * G + h) * (D + 2) + D]);
-    float Ls = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sw[(w * G + h) * DP + D]);
+    float Ls = 0.f;
+    f4v A = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float* s = sw + (w * G + h) * (D + 2);
-      const float f = (s[D] == -INFINITY) ? 0.f : exp2f(s[D] - M);
-      Ls += s[D + 1] * f;
-      A += s[e] * f;
+      const float* sp = sw + (w * G + h) * DP;
+      const float f = (sp[D] == -INFINITY) ? 0.f : exp2f(sp[D] - M);
+      Ls += sp[D + 1] * f;
+      A += *reinterpret_cast<const f4v*>(sp + e0) * f;
     }
-    stc(part + h * (D + 2) + e, A);
-    if (e == 0) { stc(part + h * (D + 2) + D, M); stc(part + h * (D + 2) + D + 1, Ls); }
+    if (nc == 1) {
+      stc4(rsrc(o + h * D), e0 * 4, A / Ls);
+    } else {
+      const auto r = rsrc(part + h * DP);
+      stc4(r, e0 * 4, A);
+      if (e0 == 0) stc4(r, D * 4, f4v{M, Ls, 0.f, 0.f});
+    }
+  }
+  if (nc == 1) {
+    wg_notify(ev_ptr(a, c.l, EV_ATTN), -1);
+    return true;
   }
   // the last chunk task of (b, g) to finish merges the partials
   vm_drain();
   __syncthreads();
-  int* flag = reinterpret_cast<int*>(c.misc + MISC_FLAG);
   if (tid == 0) {
     int* mc = a.ws.mctr + (((size_t)c.l * dm.max_batch + b) * dm.Hkv + g) * kCtr;
-    *flag = (atomic_add_relaxed(mc, -1) == 1);
+    *c.s.flag = (atomic_add_relaxed(mc, -1) == 1);
   }
   __syncthreads();
-  if (*flag) {
-    const int nc = (n + kAttnChunk - 1) / kAttnChunk;
-    const float* pb = a.ws.part + ((size_t)b * dm.Hkv + g) * dm.max_chunks * G * (D + 2);
-    float* o = a.ws.o + (size_t)b * dm.Hq * D + (size_t)g * G * D;
-    for (int t = tid; t < G * D; t += kBlock) {
-      const int h = t / D, e = t - h * D;
-      float M = -INFINITY;
-      for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, ldc(pb + ((size_t)cc * G + h) * (D + 2) + D));
-      float Ls = 0.f, A = 0.f;
-      for (int cc = 0; cc < nc; ++cc) {
-        const float* s = pb + ((size_t)cc * G + h) * (D + 2);
-        const float f = exp2f(ldc(s + D) - M);
-        Ls += ldc(s + D + 1) * f;
-        A += ldc(s + e) * f;
+  if (*c.s.flag) {
+    const float* pb = a.ws.part + ((size_t)b * dm.Hkv + g) * dm.max_chunks * G * DP;
+    for (int t = tid; t < G * D / 4; t += kBlock) {
+      const int h = t / (D / 4), e0 = (t - h * (D / 4)) * 4;
+      float M = -INFINITY, Ls = 0.f;
+      f4v A = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < nc; c0 += 8) {
+        f4v ms[8], as[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int cc = min(c0 + u, nc - 1);
+          const auto r = rsrc(pb + ((size_t)cc * G + h) * DP);
+          as[u] = ldc4(r, e0 * 4);
+          ms[u] = ldc4(r, D * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (c0 + u < nc) {
+            const float mn = fmaxf(M, ms[u].x);
+            const float fo = (M == -INFINITY) ? 0.f : exp2f(M - mn), fc = exp2f(ms[u].x - mn);
+            Ls = Ls * fo + ms[u].y * fc;
+            A = A * fo + as[u] * fc;
+            M = mn;
+          }
+        }
       }
-      stc(o + h * D + e, A / Ls);
+      stc4(rsrc(o + h * D), e0 * 4, A / Ls);
     }
     wg_notify(ev_ptr(a, c.l, EV_ATTN), -1);
   }
   __syncthreads();
+  return true;
 }
 
-// O-projection rows [r0, r1) of a tile + residual: h1 = x + W_o o.
-template <typename WT, int BB>
-__device__ __noinline__ void task_o(const Ctx c, int tile) {
+template <typename KT, int HB>
+__device__ __forceinline__ bool attn_its(const Ctx& c, int b, int g, int ci, int ck, const int* wev) {
+  if (ck <= 64) return task_attn<KT, HB, 2>(c, b, g, ci, wev);
+  if (ck <= 128) return task_attn<KT, HB, 4>(c, b, g, ci, wev);
+  return task_attn<KT, HB, 8>(c, b, g, ci, wev);
+}
+
+template <typename KT>
+__device__ __forceinline__ bool attn_dispatch(const Ctx& c, int b, int g, int ci, const int* wev) {
+  const int G = c.a.dm.Hq / c.a.dm.Hkv, ck = c.a.attn_chunk;
+  if (G >= 4) return attn_its<KT, 4>(c, b, g, ci, ck, wev);
+  if (G == 2) return attn_its<KT, 2>(c, b, g, ci, ck, wev);
+  return attn_its<KT, 1>(c, b, g, ci, ck, wev);
+}
+
+// ---------------------------------------------------------------------------
+// MoE routing and combine
+// ---------------------------------------------------------------------------
+
+// Wave-wide inclusive prefix sum.
+__device__ __forceinline__ int wave_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Top-k, gates and expert grouping for all tokens (one workgroup).
+//   topk:     per token, the k largest float32 logits ordered by (logit desc,
+//             index asc): ties go to the lower expert index;
+//   gates:    softmax over the k selected logits;
+//   grouping: exp_indptr = prefix sum of per-expert routed rows (last = T k),
+//             tile_indptr = prefix sum of ceil(count / kMoeBM), sorted_tok /
+//             sorted_slot = routed (token, slot) ordered by expert then token;
+//   arming:   the counter of expert e starts at e's number of gate/up tasks
+//             (its row tiles x gate/up slices) -- the data-dependent event.
+__device__ __forceinline__ bool task_route(const Ctx& c, const int* wev) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
-  const LayerPtrs& L = a.layers[c.l];
-  const int K = dm.Hq * dm.d;
-  const int r0 = (int)((long)tile * dm.H / dm.o_tiles), r1 = (int)((long)(tile + 1) * dm.H / dm.o_tiles);
-  const int R = r1 - r0;
-  for (int b0 = 0; b0 < a.batch; b0 += BB) {
-    const int nb = min(BB, a.batch - b0);
-    stage_x<BB>(a.ws.o + (size_t)b0 * K, K, nb, K, nullptr, false, 0.f, c.xs, c.misc);
-    gemv<WT, BB>(reinterpret_cast<const WT*>(L.w_o), K, R, RowsContig{r0}, c.xs, c.ys);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < R * nb; idx += kBlock) {
-      const int j = idx / nb, b = idx - j * nb;
-      const size_t off = (size_t)(b0 + b) * dm.H + r0 + j;
-      stc(a.ws.h1 + off, ldc(a.hidden + off) + c.ys[j * BB + b]);
+  if (!ctx_wait(c, wev)) return false;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.batch, E = dm.E, k = dm.k, Tk = T * k, G = dm.grid;
+  int* sidx = reinterpret_cast<int*>(c.s.xs);   // [T k]
+  int* cnt = sidx + dm.max_batch * kMaxTopK;     // [E]
+  int* ptr = cnt + kMaxExperts;                  // [E + 1]
+  int* tptr = ptr + kMaxExperts + 1;             // [E + 1]
+  constexpr int EPLN = kMaxExperts / 64;
+  constexpr int NONE = 0x7fffffff;
+  for (int t = wave; t < T; t += kWaves) {
+    float z[EPLN];
+    unsigned taken = 0;
+#pragma unroll
+    for (int i = 0; i < EPLN; ++i) {
+      const int e = lane + 64 * i;
+      z[i] = e < E ? ldc(a.ws.logits + (size_t)t * E + e) : -INFINITY;
     }
-    __syncthreads();
+    float zsel[kMaxTopK];
+    int isel[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      zsel[j] = 0.f;
+      isel[j] = 0;
+      if (j >= k) continue;
+      // this lane's best untaken entry by (logit desc, index asc), then the wave's
+      float bv = -INFINITY;
+      int bi = NONE;
+#pragma unroll
+      for (int i = 0; i < EPLN; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E && !(taken & (1u << i)) && (bi == NONE || z[i] > bv || (z[i] == bv && e < bi))) {
+          bv = z[i];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (oi != NONE && (bi == NONE || ov > bv || (ov == bv && oi < bi))) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+      zsel[j] = bv;
+      isel[j] = bi;
+    }
+    if (lane == 0) {
+      float w[kMaxTopK], sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        w[j] = j < k ? __expf(zsel[j] - zsel[0]) : 0.f;
+        sum += w[j];
+      }
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j < k) {
+          sidx[t * k + j] = isel[j];
+          stc(a.ws.topk_w + t * k + j, w[j] / sum);
+        }
+      }
+    }
   }
+  __syncthreads();
+  for (int e = tid; e < E; e += kBlock) {
+    int n = 0;
+    for (int i = 0; i < Tk; ++i) n += sidx[i] == e;
+    cnt[e] = n;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int carry = 0, tcarry = 0;
+    if (lane == 0) { ptr[0] = 0; tptr[0] = 0; }
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int v = e < E ? cnt[e] : 0, tv = (v + kMoeBM - 1) / kMoeBM;
+      const int s = wave_scan(v) + carry, ts = wave_scan(tv) + tcarry;
+      if (e < E) { ptr[e + 1] = s; tptr[e + 1] = ts; }
+      carry = __shfl(s, 63, 64);
+      tcarry = __shfl(ts, 63, 64);
+    }
+  }
+  __syncthreads();
+  const int ntiles = tptr[E];
+  // gate/up slices of Fe and down slices of H per row tile: about two tasks
+  // per workgroup, each slice at least 16 rows and at most what the LDS output
+  // staging holds for 16 token rows
+  const int target = (2 * G + ntiles - 1) / ntiles;
+  const int sg = min(max(target, (2 * dm.Fe * kMaxNb + kYsFloats - 1) / kYsFloats), max(dm.Fe / 16, 1));
+  const int sd = min(max(target, (dm.H * kMaxNb + kYsFloats - 1) / kYsFloats), max(dm.H / 16, 1));
+  for (int e = tid; e < E; e += kBlock) {
+    // scatter in (expert, token) order; a token selects an expert at most once
+    int pos = ptr[e];
+    for (int i = 0; i < Tk; ++i) {
+      if (sidx[i] == e) {
+        stci(a.ws.sorted_tok + pos, i / k);
+        stci(a.ws.sorted_slot + pos, i % k);
+        stci(a.ws.pos_of + i, pos);
+        ++pos;
+      }
+    }
+    for (int tt = tptr[e]; tt < tptr[e + 1]; ++tt) {
+      stci(a.ws.tile_info + 2 * tt, e);
+      stci(a.ws.tile_info + 2 * tt + 1, ptr[e] + (tt - tptr[e]) * kMoeBM);
+    }
+    stci(a.ws.ectr + ((size_t)c.l * E + e) * kCtr, (tptr[e + 1] - tptr[e]) * sg);
+    stci(a.ws.exp_indptr + e + 1, ptr[e + 1]);
+  }
+  for (int i = tid; i < Tk; i += kBlock) stci(a.ws.topk_idx + i, sidx[i]);
+  if (tid == 0) {
+    stci(a.ws.exp_indptr, 0);
+    stci(a.ws.moe_info + 0, ntiles * sg);
+    stci(a.ws.moe_info + 1, ntiles * sd);
+    stci(a.ws.moe_info + 2, sg);
+    stci(a.ws.moe_info + 3, sd);
+    stci(a.ws.moe_info + 4, ntiles);
+  }
+  // routing outputs of the last layer for the caller
+  if (c.l == dm.L - 1) {
+    const pmk_routing& r = a.rout;
+    for (int i = tid; i < Tk; i += kBlock) {
+      if (r.topk_idx) r.topk_idx[i] = sidx[i];
+      if (r.topk_w) r.topk_w[i] = ldc(a.ws.topk_w + i);
+    }
+    if (r.router_logits)
+      for (int i = tid; i < T * E; i += kBlock) r.router_logits[i] = ldc(a.ws.logits + i);
+    for (int e = tid; e <= E; e += kBlock) {
+      if (r.exp_indptr) r.exp_indptr[e] = ptr[e];
+      if (r.tile_indptr) r.tile_indptr[e] = tptr[e];
+    }
+  }
+  // the scattered order is read back once the stores above have landed
+  vm_drain();
+  __syncthreads();
+  if (c.l == dm.L - 1 && (a.rout.sorted_tok || a.rout.sorted_slot)) {
+    for (int i = tid; i < Tk; i += kBlock) {
+      if (a.rout.sorted_tok) a.rout.sorted_tok[i] = ldci(a.ws.sorted_tok + i);
+      if (a.rout.sorted_slot) a.rout.sorted_slot[i] = ldci(a.ws.sorted_slot + i);
+    }
+  }
+  wg_notify(ev_ptr(a, c.l, EV_ROUTE), -1);
+  return true;
 }
 
-// RMSNorm2 + gate and up rows [r0, r1) + SwiGLU: act = silu(gate) * up.
-template <typename WT, int BB>
-__device__ __noinline__ void task_gu(const Ctx c, int tile) {
+// Per-token combine: x'_t = h1_t + sum_j w_tj * Y[pos(t, j)], slots in order j = 0..k-1.
+__device__ __forceinline__ bool task_combine(const Ctx& c, const int* wev) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
-  const LayerPtrs& L = a.layers[c.l];
-  const int r0 = (int)((long)tile * dm.F / dm.gu_tiles), r1 = (int)((long)(tile + 1) * dm.F / dm.gu_tiles);
-  const int R = r1 - r0;
-  for (int b0 = 0; b0 < a.batch; b0 += BB) {
-    const int nb = min(BB, a.batch - b0);
-    stage_x<BB>(a.ws.h1 + (size_t)b0 * dm.H, dm.H, nb, dm.H, L.ffn_norm, true, dm.eps, c.xs, c.misc);
-    gemv<WT, BB>(reinterpret_cast<const WT*>(L.w_gate), dm.H, R, RowsContig{r0}, c.xs, c.ys);
-    gemv<WT, BB>(reinterpret_cast<const WT*>(L.w_up), dm.H, R, RowsContig{r0}, c.xs, c.ys + R * BB);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < R * nb; idx += kBlock) {
-      const int j = idx / nb, b = idx - j * nb;
-      const float r = c.misc[MISC_RSTD + b];
-      const float gt = c.ys[j * BB + b] * r, up = c.ys[(R + j) * BB + b] * r;
-      stc(a.ws.act + (size_t)(b0 + b) * dm.F + r0 + j, gt / (1.0f + __expf(-gt)) * up);
+  if (!ctx_wait(c, wev)) return false;
+  for (int t = c.wg; t < a.batch; t += dm.grid) {
+    for (int i = threadIdx.x; i < dm.H / 4; i += kBlock) {
+      f4v x = ldc4(rsrc(a.ws.h1 + (size_t)t * dm.H), i * 16);
+      for (int j = 0; j < dm.k; ++j) {
+        const float w = ldc(a.ws.topk_w + t * dm.k + j);
+        const int p = ldci(a.ws.pos_of + t * dm.k + j);
+        x += ldc4(rsrc(a.ws.mout + (size_t)p * dm.H), i * 16) * w;
+      }
+      stc4(rsrc(a.hidden + (size_t)t * dm.H), i * 16, x);
     }
-    __syncthreads();
   }
+  return true;
 }
-
-// Down-projection rows [r0, r1) + residual: x' = h1 + W_down act (written to hidden).
-template <typename WT, int BB>
-__device__ __noinline__ void task_down(const Ctx c, int tile) {
-  const StepArgs& a = c.a;
-  const Dims& dm = a.dm;
-  const LayerPtrs& L = a.layers[c.l];
-  const int r0 = (int)((long)tile * dm.H / dm.down_tiles), r1 = (int)((long)(tile + 1) * dm.H / dm.down_tiles);
-  const int R = r1 - r0;
-  for (int b0 = 0; b0 < a.batch; b0 += BB) {
-    const int nb = min(BB, a.batch - b0);
-    stage_x<BB>(a.ws.act + (size_t)b0 * dm.F, dm.F, nb, dm.F, nullptr, false, 0.f, c.xs, c.misc);
-    gemv<WT, BB>(reinterpret_cast<const WT*>(L.w_down), dm.F, R, RowsContig{r0}, c.xs, c.ys);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < R * nb; idx += kBlock) {
-      const int j = idx / nb, b = idx - j * nb;
-      const size_t off = (size_t)(b0 + b) * dm.H + r0 + j;
-      stc(a.hidden + off, ldc(a.ws.h1 + off) + c.ys[j * BB + b]);
-    }
-    __syncthreads();
-  }
-}
-
-#define PMK_BB_DISPATCH(FN, WT, bb, ...)          \
-  switch (bb) {                                   \
-    case 8: FN<WT, 8>(__VA_ARGS__); break;        \
-    case 4: FN<WT, 4>(__VA_ARGS__); break;        \
-    case 2: FN<WT, 2>(__VA_ARGS__); break;        \
-    default: FN<WT, 1>(__VA_ARGS__); break;       \
-  }
 
 // ---------------------------------------------------------------------------
 // The persistent kernel
 // ---------------------------------------------------------------------------
 template <typename WT>
 __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict__ pa) {
-  extern __shared__ float lds[];
+  extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const StepArgs& a = *pa;
   const Dims& dm = a.dm;
   const int wg = blockIdx.x;
-  float* misc = lds + kXsFloats + kYsFloats;
-  int* okp = reinterpret_cast<int*>(misc + MISC_OK);
-  if (threadIdx.x == 0) *okp = (ldci(a.ws.err) == 0);
+  const Lds s = lds_layout(lds_raw);
+  if (threadIdx.x == 0) *s.flag = (ldci(a.ws.err) == 0);
   __syncthreads();
-  if (!*okp) return;
+  if (!*s.flag) return;
   const int n = a.ws.qlen[wg];
   const int4* q = a.ws.queue + (size_t)wg * dm.max_queue;
-  const int G = dm.Hq / dm.Hkv;
   uint32_t* tr = a.trace ? a.trace + (size_t)wg * a.trace_cap * 4 : nullptr;
   int tn = 1;
   for (int l = 0; l < dm.L; ++l) {
-    Ctx c{a, l, wg, lds, lds + kXsFloats, misc};
+    const Ctx c{a, l, wg, s};
     unsigned passed = 0;
+    // the event a task type waits on, or nullptr once this workgroup has seen it at zero
+    auto need = [&](int e, int el) -> const int* {
+      const unsigned bit = 1u << (e + (el != l ? 16 : 0));
+      if (passed & bit) return nullptr;
+      passed |= bit;
+      return ev_ptr(a, el, e);
+    };
     for (int t = 0; t < n; ++t) {
       const int4 task = q[t];
       const uint32_t t_begin = (uint32_t)now_ticks();
-      int need = -1, need_l = l;
+      if (tr && threadIdx.x == 0) *s.tclk = t_begin;
+      bool ok = true;
+      int notify = -1;   // event this task notifies through sub-counter (wg % kSubs)
       switch (task.x) {
-        case T_QKV: if (l > 0) { need = EV_DOWN; need_l = l - 1; } break;
-        case T_ATTN: need = EV_QKV; break;
-        case T_O: need = EV_ATTN; break;
-        case T_GU: need = EV_O; break;
-        case T_DOWN: need = EV_GU; break;
-        default: break;
-      }
-      if (need >= 0) {
-        const unsigned bit = 1u << (need + (need_l != l ? 16 : 0));
-        if (!(passed & bit)) {
-          if (threadIdx.x == 0) *okp = spin_zero(ev_ptr(a, need_l, need), a.ws.err, a.watchdog_ticks);
-          __syncthreads();
-          if (!*okp) return;
-          passed |= bit;
-        }
-      }
-      const uint32_t t_waited = (uint32_t)now_ticks();
-      switch (task.x) {
-        case T_QKV: {
-          const int nu = (int)((long)(task.y + 1) * dm.qkv_units / dm.qkv_tiles) -
-                         (int)((long)task.y * dm.qkv_units / dm.qkv_tiles);
-          PMK_BB_DISPATCH(task_qkv, WT, pick_bb(a.batch, dm.H, 2 * nu), c, task.y);
-          wg_notify(ev_ptr(a, l, EV_QKV), wg & (kSubs - 1));
-          break;
-        }
         case T_ATTN:
-          if (G == 8) task_attn<WT, 8>(c, task.y, task.z, task.w);
-          else if (G == 4) task_attn<WT, 4>(c, task.y, task.z, task.w);
-          else if (G == 2) task_attn<WT, 2>(c, task.y, task.z, task.w);
-          else task_attn<WT, 1>(c, task.y, task.z, task.w);
+          ok = attn_dispatch<WT>(c, task.y, task.z, task.w, need(EV_QKV, l));
           break;
-        case T_O: {
-          const int R = (int)((long)(task.y + 1) * dm.H / dm.o_tiles) - (int)((long)task.y * dm.H / dm.o_tiles);
-          PMK_BB_DISPATCH(task_o, WT, pick_bb(a.batch, dm.Hq * dm.d, R), c, task.y);
-          wg_notify(ev_ptr(a, l, EV_O), wg & (kSubs - 1));
+        case T_ROUTE:
+          ok = task_route(c, need(EV_ROUTER, l));
+          break;
+        case T_COMBINE:
+          ok = task_combine(c, need(EV_MDOWN, l));
+          notify = EV_DOWN;
+          break;
+        default: {   // GEMV tasks
+          const int* wev = nullptr;
+          switch (task.x) {
+            case T_QKV: wev = l > 0 ? need(EV_DOWN, l - 1) : nullptr; notify = EV_QKV; break;
+            case T_O: wev = need(EV_ATTN, l); notify = EV_O; break;
+            case T_GU: wev = need(EV_O, l); notify = EV_GU; break;
+            case T_DOWN: wev = need(EV_GU, l); notify = EV_DOWN; break;
+            case T_ROUTER: wev = need(EV_O, l); notify = EV_ROUTER; break;
+            case T_MGU:   // the share's size is known once routing is done
+              ok = ctx_wait(c, need(EV_ROUTE, l));
+              break;
+            case T_MDOWN: notify = EV_MDOWN; break;
+            default: break;
+          }
+          for (int p = 0; ok; ++p) {
+            Pass ps;
+            if (!make_pass<WT>(c, task, p, wev, ps)) break;
+            ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev);
+            if (ok) epilogue<WT>(c, ps);
+          }
           break;
         }
-        case T_GU: {
-          const int R = (int)((long)(task.y + 1) * dm.F / dm.gu_tiles) - (int)((long)task.y * dm.F / dm.gu_tiles);
-          PMK_BB_DISPATCH(task_gu, WT, pick_bb(a.batch, dm.H, 2 * R), c, task.y);
-          wg_notify(ev_ptr(a, l, EV_GU), wg & (kSubs - 1));
-          break;
-        }
-        case T_DOWN: {
-          const int R = (int)((long)(task.y + 1) * dm.H / dm.down_tiles) - (int)((long)task.y * dm.H / dm.down_tiles);
-          PMK_BB_DISPATCH(task_down, WT, pick_bb(a.batch, dm.F, R), c, task.y);
-          wg_notify(ev_ptr(a, l, EV_DOWN), wg & (kSubs - 1));
-          break;
-        }
-        default: break;
       }
+      if (ok && notify >= 0) wg_notify(ev_ptr(a, l, notify), wg & (kSubs - 1));
+      if (!ok) return;
       if (tr && threadIdx.x == 0 && tn < a.trace_cap) {
         const uint32_t t_end = (uint32_t)now_ticks();
         uint32_t* e = tr + (size_t)tn * 4;
         e[0] = (uint32_t)task.x | ((uint32_t)l << 8) | ((uint32_t)(task.y & 0xffff) << 16);
         e[1] = t_begin;
-        e[2] = t_waited;
+        e[2] = *s.tclk;
         e[3] = t_end;
         ++tn;
       }
@@ -558,13 +1021,29 @@ __device__ __forceinline__ int sub_count(int tiles, int grid, int x) {
   return (tiles / grid) * below(grid) + below(tiles % grid);
 }
 
+__device__ __forceinline__ void arm_tiles(int* ev, int tiles, int grid) {
+  int top = 0;
+  for (int x = 0; x < kSubs; ++x) {
+    const int cnt = sub_count(tiles, grid, x);
+    ev[(1 + x) * kCtr] = cnt;
+    top += cnt > 0;
+  }
+  ev[0] = top;
+}
+
 __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   const Dims& dm = a.dm;
   const int tid = threadIdx.x, B = a.batch, G = dm.grid;
-  if (tid == 0) *reinterpret_cast<StepArgs*>(a.ws.args) = a;
   __shared__ int bad;
   __shared__ int total_attn;
-  if (tid == 0) bad = (ldci(a.ws.err) != 0) ? 1 : 0;
+  __shared__ int cb[kMaxBatchAll + 1];
+  StepArgs* copy = reinterpret_cast<StepArgs*>(a.ws.args);
+  if (tid == 0) {
+    // the persistent kernel reads this step's arguments from here, on every
+    // path (it first checks the error word through it)
+    *copy = a;
+    bad = (ldci(a.ws.err) != 0) ? 1 : 0;
+  }
   __syncthreads();
   for (int b = tid; b < B; b += blockDim.x) {
     const int s = a.seq_lens[b];
@@ -582,21 +1061,36 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   }
   if (tid == 0) {
     a.ws.err[16] = 0;   // abort flag
+    // attention chunk: the largest of 256/128/64 positions that still gives
+    // every workgroup a task (small latency-bound batches get small chunks)
+    int ck = kMaxChunk;
+    while (ck > kMinChunk) {
+      long tasks = 0;
+      for (int b = 0; b < B; ++b) tasks += (a.seq_lens[b] + ck) / ck;
+      if (tasks * dm.Hkv >= G) break;
+      ck >>= 1;
+    }
     int acc = 0;
     for (int b = 0; b < B; ++b) {
-      a.ws.chunk_base[b] = acc;
-      acc += (a.seq_lens[b] + kAttnChunk) / kAttnChunk;   // ceil((S + 1) / CK)
+      cb[b] = acc;
+      acc += (a.seq_lens[b] + ck) / ck;   // ceil((S + 1) / ck)
     }
-    a.ws.chunk_base[B] = acc;
+    cb[B] = acc;
     total_attn = acc * dm.Hkv;
+    copy->attn_chunk = ck;
   }
   __syncthreads();
-  const int* cb = a.ws.chunk_base;
-  // queues: stage order QKV, attention, O, gate/up, down
+  const int router_tasks = dm.moe ? dm.router_tiles * ((B + kMaxNb - 1) / kMaxNb) : 0;
+  // queues: stage order QKV, attention, O, then gate/up, down (dense) or
+  // router, route, grouped gate/up, grouped down, combine (MoE)
   for (int w = tid; w < G; w += blockDim.x) {
     int4* q = a.ws.queue + (size_t)w * dm.max_queue;
     int n = 0;
-    for (int t = w; t < dm.qkv_tiles; t += G) { if (n < dm.max_queue) q[n] = make_int4(T_QKV, t, 0, 0); ++n; }
+    auto push = [&](int4 v) {
+      if (n < dm.max_queue) q[n] = v;
+      ++n;
+    };
+    for (int t = w; t < dm.qkv_tiles; t += G) push(make_int4(T_QKV, t, 0, 0));
     for (int i = w; i < total_attn; i += G) {
       int lo = 0, hi = B;   // find b: Hkv*cb[b] <= i < Hkv*cb[b+1]
       while (hi - lo > 1) {
@@ -604,12 +1098,19 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
         if (dm.Hkv * cb[mid] <= i) lo = mid; else hi = mid;
       }
       const int r = i - dm.Hkv * cb[lo], nc = cb[lo + 1] - cb[lo];
-      if (n < dm.max_queue) q[n] = make_int4(T_ATTN, lo, r / nc, r % nc);
-      ++n;
+      push(make_int4(T_ATTN, lo, r / nc, r % nc));
     }
-    for (int t = w; t < dm.o_tiles; t += G) { if (n < dm.max_queue) q[n] = make_int4(T_O, t, 0, 0); ++n; }
-    for (int t = w; t < dm.gu_tiles; t += G) { if (n < dm.max_queue) q[n] = make_int4(T_GU, t, 0, 0); ++n; }
-    for (int t = w; t < dm.down_tiles; t += G) { if (n < dm.max_queue) q[n] = make_int4(T_DOWN, t, 0, 0); ++n; }
+    for (int t = w; t < dm.o_tiles; t += G) push(make_int4(T_O, t, 0, 0));
+    if (!dm.moe) {
+      for (int t = w; t < dm.gu_tiles; t += G) push(make_int4(T_GU, t, 0, 0));
+      for (int t = w; t < dm.down_tiles; t += G) push(make_int4(T_DOWN, t, 0, 0));
+    } else {
+      for (int i = w; i < router_tasks; i += G) push(make_int4(T_ROUTER, i % dm.router_tiles, i / dm.router_tiles, 0));
+      if (w == G - 1) push(make_int4(T_ROUTE, 0, 0, 0));
+      push(make_int4(T_MGU, 0, 0, 0));
+      push(make_int4(T_MDOWN, 0, 0, 0));
+      push(make_int4(T_COMBINE, 0, 0, 0));
+    }
     a.ws.qlen[w] = n <= dm.max_queue ? n : 0;
     if (n > dm.max_queue) atomicOr(&bad, 4);
   }
@@ -617,23 +1118,16 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   for (int idx = tid; idx < dm.L * EV_COUNT; idx += blockDim.x) {
     const int e = idx % EV_COUNT;
     int* ev = a.ws.ev + (size_t)idx * kEvInts;
-    int tiles = 0;
-    if (e == EV_QKV) tiles = dm.qkv_tiles;
-    else if (e == EV_O) tiles = dm.o_tiles;
-    else if (e == EV_GU) tiles = dm.gu_tiles;
-    else if (e == EV_DOWN) tiles = dm.down_tiles;
-    if (tiles > 0) {
-      int top = 0;
-      for (int x = 0; x < kSubs; ++x) {
-        const int cnt = sub_count(tiles, G, x);
-        ev[(1 + x) * kCtr] = cnt;
-        top += cnt > 0;
-      }
-      ev[0] = top;
-    } else if (e == EV_ATTN) {
-      ev[0] = B * dm.Hkv;
-    } else {
-      ev[0] = 0;
+    switch (e) {
+      case EV_QKV: arm_tiles(ev, dm.qkv_tiles, G); break;
+      case EV_ATTN: ev[0] = B * dm.Hkv; break;
+      case EV_O: arm_tiles(ev, dm.o_tiles, G); break;
+      case EV_GU: arm_tiles(ev, dm.moe ? 0 : dm.gu_tiles, G); break;
+      case EV_DOWN: arm_tiles(ev, dm.moe ? G : dm.down_tiles, G); break;   // MoE: one combine slot per workgroup
+      case EV_ROUTER: arm_tiles(ev, router_tasks, G); break;
+      case EV_ROUTE: ev[0] = dm.moe ? 1 : 0; break;
+      case EV_MDOWN: arm_tiles(ev, dm.moe ? G : 0, G); break;
+      default: ev[0] = 0; break;
     }
   }
   for (int idx = tid; idx < dm.L * B * dm.Hkv; idx += blockDim.x) {

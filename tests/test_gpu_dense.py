@@ -111,3 +111,54 @@ def test_bad_length_is_reported_and_step_skipped():
     assert model.device_error() == 0                                # cleared by the read
     assert model.decode_step(case.hidden, case.kv, case.seq_lens[:0]) == 1   # batch 0: PMK_ERR_ARG
     model.close()
+
+
+def test_consecutive_steps_chain(orc):
+    """Three decode steps in a row on one handle: each step's output and K/V
+    append feed the next (lengths advance by one), against the oracle chained
+    the same way."""
+    w = synth.get_workload("c2_8b_b1")
+    case = build_case(w, 2, [40, 200], n_layers=2, max_seq=260, tag="t8")
+    inp = oracle_inputs(case)
+    model = make_model(case)
+    desc = orc.make_desc(w, 2, 260, n_layers=2)
+    kv_ref, h_ref = inp["kv"], inp["hidden"]
+    lens = np.array([40, 200], np.int32)
+    for step in range(3):
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        announce(f"chained step {step} lens={lens.tolist()}")
+        model.step(case.hidden, case.kv, sl)
+        torch.cuda.synchronize()
+        assert model.device_error() == 0
+        h_ref = orc.decode_stack(desc, inp["layers"], kv_ref, lens, h_ref)
+        err = rel_l2(to_np(case.hidden), h_ref)
+        print(f"  step {step}: rel_l2 = {err:.3e}", flush=True)
+        assert err <= w.tol
+        lens = lens + 1
+    model.close()
+
+
+def test_8b_full_stack_b1_bench_config(orc):
+    """The benchmark's workload: the full 32-layer 8B-shaped stack, batch 1,
+    512 cached positions, one step, every output element against the oracle."""
+    w = synth.get_workload("c2_8b_b1")
+    case = build_case(w, 1, [512], max_seq=613, tag="")
+    check_dense(orc, case, w.tol)
+
+
+def test_8b_full_stack_b16_ragged_sampled(orc):
+    """Batch 16 with ragged lengths in [512, 8192] over the full 32-layer stack;
+    the oracle recomputes two sampled requests (requests are independent)."""
+    w = synth.get_workload("c3_8b_sweep")
+    lens = synth.ragged_lengths(16, 512, 8192, ("c3_8b_sweep", "lens", 16))
+    case = build_case(w, 16, lens, max_seq=int(lens.max()) + 2, tag="t9")
+    check_dense(orc, case, w.tol, requests=[int(np.argmax(lens)), int(np.argmin(lens))])
+
+
+def test_70b_shape_four_layers_b8_sampled(orc):
+    """Llama-70B-shaped layers (H 8192, 64/8 heads, FFN 28672), batch 8 with
+    lengths in [8192, 16384]; four layers, two sampled requests."""
+    w = synth.get_workload("c5_70b")
+    lens = synth.ragged_lengths(8, 8192, 16384, ("c5_70b", "lens", 8))
+    case = build_case(w, 8, lens, n_layers=4, max_seq=int(lens.max()) + 2, tag="t10")
+    check_dense(orc, case, w.tol, requests=[0, 5])

@@ -1,0 +1,164 @@
+"""GPU parity of moe_layer_step against the CPU oracle (through the C ABI).
+
+Routing is checked three ways:
+  * the GPU's routing outputs are consistent with the GPU's own float32 router
+    logits (top-k by logit desc / index asc, gates = softmax of the selection,
+    exp_indptr / tile_indptr / sorted_tok / sorted_slot from the definition);
+  * against the oracle (which rounds its logits to float32 and takes the same
+    decision): every token routes identically except where the oracle's k-th /
+    (k+1)-th logit gap is below twice the measured logit difference (a near
+    tie, counted); outputs of identically routed tokens match to the tolerance,
+    and with no near ties the grouping arrays match bit for bit;
+  * an all-zero router makes every logit exactly 0, so routing is fixed by the
+    tie rule alone and must match the oracle exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth.workloads import Workload
+from _cases import build_case, oracle_inputs, rel_l2, to_np
+
+pytestmark = pytest.mark.gpu
+
+TINY_MOE_F32 = Workload(name="tiny_moe_f32", dtype="f32", n_layers=1, hidden=256, n_q_heads=4, n_kv_heads=2,
+                        head_dim=64, ffn_dim=0, n_experts=8, top_k=2, expert_ffn_dim=64, tol=1e-5)
+SMALL_MOE_BF16 = Workload(name="small_moe_bf16", dtype="bf16", n_layers=1, hidden=512, n_q_heads=8, n_kv_heads=2,
+                          head_dim=128, ffn_dim=0, n_experts=16, top_k=4, expert_ffn_dim=128, tol=1e-2)
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def routing_buffers(T, E, k, dev="cuda"):
+    i32 = dict(dtype=torch.int32, device=dev)
+    return {"topk_idx": torch.full((T, k), -1, **i32), "topk_w": torch.zeros((T, k), dtype=torch.float32, device=dev),
+            "router_logits": torch.zeros((T, E), dtype=torch.float32, device=dev),
+            "exp_indptr": torch.full((E + 1,), -1, **i32), "tile_indptr": torch.full((E + 1,), -1, **i32),
+            "sorted_tok": torch.full((T * k,), -1, **i32), "sorted_slot": torch.full((T * k,), -1, **i32)}
+
+
+def check_routing_self_consistent(r, T, E, k, bm):
+    """The GPU routing outputs against the definition, on the GPU's own logits."""
+    z = r["router_logits"].astype(np.float32)
+    idx = r["topk_idx"]
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -z[t]))       # logit desc, then index asc
+        np.testing.assert_array_equal(idx[t], order[:k], err_msg=f"token {t}")
+        sel = z[t, idx[t]].astype(np.float64)
+        g = np.exp(sel - sel.max())
+        np.testing.assert_allclose(r["topk_w"][t], g / g.sum(), rtol=1e-5, atol=1e-7)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    np.testing.assert_array_equal(r["exp_indptr"], np.concatenate([[0], np.cumsum(counts)]))
+    np.testing.assert_array_equal(r["tile_indptr"], np.concatenate([[0], np.cumsum((counts + bm - 1) // bm)]))
+    pairs = sorted((int(idx[t, j]), t, j) for t in range(T) for j in range(k))
+    np.testing.assert_array_equal(r["sorted_tok"], [p[1] for p in pairs])
+    np.testing.assert_array_equal(r["sorted_slot"], [p[2] for p in pairs])
+
+
+def run_moe(orc, w, T, lens, tag, max_seq=None, zero_router=False, random_gains=False):
+    case = build_case(w, T, lens, max_seq=max_seq, tag=tag, random_gains=random_gains)
+    if zero_router:
+        case.layers[0]["w_router"].zero_()
+    inp = oracle_inputs(case)
+    from persistent_megakernel_04_amd import DecodeModel
+    model = DecodeModel.from_workload(w, case.layers, case.max_batch, case.max_seq)
+    bm = model.info()["moe_bm"]
+    rb = routing_buffers(T, w.n_experts, w.top_k)
+    announce(f"moe_layer_step {w.name} T={T} lens={list(lens)[:6]} zero_router={zero_router}")
+    assert model.moe_layer_step(case.hidden, case.kv, case.seq_lens, rb) == 0
+    torch.cuda.synchronize()
+    assert model.device_error() == 0
+    got = to_np(case.hidden).astype(np.float64)
+    r_gpu = {k: to_np(v) for k, v in rb.items()}
+    desc = orc.make_desc(w, T, case.max_seq, n_layers=1)
+    kv_ref = inp["kv"][0]
+    ref, r_ref = orc.moe_layer(desc, inp["layers"][0], kv_ref, inp["seq_lens"], inp["hidden"], bm)
+    model.close()
+    return case, got, ref, r_gpu, r_ref, bm, kv_ref
+
+
+def compare_moe(w, T, got, ref, r_gpu, r_ref, bm):
+    E, k = w.n_experts, w.top_k
+    check_routing_self_consistent(r_gpu, T, E, k, bm)
+    dz = np.abs(r_gpu["router_logits"].astype(np.float64) - r_ref["router_logits"].astype(np.float64))
+    zerr = float(dz.max())
+    same = np.all(r_gpu["topk_idx"] == r_ref["topk_idx"], axis=1)
+    near = 0
+    for t in np.nonzero(~same)[0]:
+        zs = np.sort(r_ref["router_logits"][t].astype(np.float64))[::-1]
+        gap = zs[k - 1] - zs[k]
+        assert gap <= 2 * zerr, f"token {t} routed differently with a logit gap {gap} > 2 x {zerr}"
+        near += 1
+    err = rel_l2(got[same], ref[same]) if same.any() else 0.0
+    print(f"  logit max diff {zerr:.2e}, near-tie tokens {near}/{T}, rel_l2(hidden) = {err:.3e} (tol {w.tol})",
+          flush=True)
+    assert err <= w.tol
+    if near == 0:
+        for key in ("exp_indptr", "tile_indptr", "sorted_tok", "sorted_slot", "topk_idx"):
+            np.testing.assert_array_equal(r_gpu[key], r_ref[key], err_msg=key)
+        np.testing.assert_allclose(r_gpu["topk_w"], r_ref["topk_w"], rtol=1e-3, atol=1e-5)
+    return near
+
+
+def test_moe_tiny_f32(orc):
+    w = TINY_MOE_F32
+    T, lens = 5, [0, 7, 64, 130, 33]
+    case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, lens, "m1", max_seq=200, random_gains=True)
+    assert compare_moe(w, T, got, ref, rg, rr, bm) == 0
+
+
+def test_moe_small_bf16_two_router_blocks(orc):
+    """20 tokens: two router token blocks, several tiles for the busiest experts."""
+    w = SMALL_MOE_BF16
+    T = 20
+    lens = synth.ragged_lengths(T, 1, 300, ("small_moe", "lens"))
+    case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, lens, "m2", max_seq=301)
+    compare_moe(w, T, got, ref, rg, rr, bm)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_moe_qwen3_30b_a3b_shape(orc, T):
+    """The Qwen3-30B-A3B-shaped MoE layer (128 experts, top-8, expert FFN 768),
+    each token its own request with 2048 cached positions."""
+    w = synth.get_workload("c4_moe")
+    case, got, ref, rg, rr, bm, kv_ref = run_moe(orc, w, T, [2048] * T, f"m3_{T}", max_seq=2049)
+    compare_moe(w, T, got, ref, rg, rr, bm)
+    # the appended K/V entries
+    a = case.kv[0, :, :, :, 2048].float().cpu().numpy()
+    b = (kv_ref[:, :T, :, 2048].astype(np.uint32) << 16).view(np.float32)
+    assert rel_l2(a, b) <= w.tol
+
+
+def test_moe_forced_tie_bit_exact(orc):
+    """All-zero router: every logit is exactly 0, so each token takes experts
+    0..k-1 with gates 1/k; routing and grouping match the oracle exactly."""
+    w = synth.get_workload("c4_moe")
+    T = 6
+    case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, [5, 100, 2047, 0, 64, 900], "m4", max_seq=2049,
+                                            zero_router=True)
+    np.testing.assert_array_equal(rg["router_logits"], 0.0)
+    np.testing.assert_array_equal(rg["topk_idx"], np.tile(np.arange(8), (T, 1)))
+    np.testing.assert_array_equal(rg["topk_w"], np.full((T, 8), 0.125, np.float32))
+    assert compare_moe(w, T, got, ref, rg, rr, bm) == 0
+
+
+def test_decode_step_on_moe_handle_matches_moe_layer_step(orc):
+    """decode_step on a MoE handle runs the same routed layer (no routing outputs)."""
+    w = SMALL_MOE_BF16
+    T = 3
+    case = build_case(w, T, [10, 20, 30], max_seq=64, tag="m5")
+    inp = oracle_inputs(case)
+    from persistent_megakernel_04_amd import DecodeModel
+    model = DecodeModel.from_workload(w, case.layers, case.max_batch, case.max_seq)
+    announce("decode_step on a MoE handle")
+    assert model.decode_step(case.hidden, case.kv, case.seq_lens) == 0
+    torch.cuda.synchronize()
+    assert model.device_error() == 0
+    bm = model.info()["moe_bm"]
+    ref, _ = orc.moe_layer(orc.make_desc(w, T, 64, n_layers=1), inp["layers"][0], inp["kv"][0], inp["seq_lens"],
+                           inp["hidden"], bm)
+    assert rel_l2(to_np(case.hidden), ref) <= w.tol
+    model.close()
