@@ -140,6 +140,8 @@ def main():
     ap.add_argument("--batch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true", help="first run a plain 2 GiB device-to-device copy "
+                    "(a kernel of known traffic, for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--trace", default=None, help="after the timed steps, run one traced step and write a "
                     "per-stage summary of the task trace to this file")
     args = ap.parse_args()
@@ -163,6 +165,14 @@ def main():
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU (the HIP library has no CPU path)")
     dev = "cuda"
+    if args.copy_probe:
+        src = torch.empty(1 << 29, dtype=torch.float32, device=dev).fill_(1.0)   # 2 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 3 x copy of 2 GiB (reads 2 GiB, writes 2 GiB each)")
+        del src, dst
     w = synth.get_workload(args.workload)
     B = args.batch if args.batch is not None else w.batches[0]
     K, W = args.steps, args.warmup
@@ -236,7 +246,7 @@ def main():
     if args.trace:
         from persistent_megakernel_04_amd import trace as ptrace
         cap = 4096
-        tbuf = torch.zeros((info["grid"], cap, 4), dtype=torch.int32, device=dev)
+        tbuf = torch.zeros((info["grid"], cap, 8), dtype=torch.int32, device=dev)
         model.trace_attach(tbuf, cap)
         model.step(hid_work[0], kv, steps_lens[0])
         torch.cuda.synchronize()

@@ -177,14 +177,19 @@ int pmk_timing_enable(pmk_handle* h, int enable);
 int pmk_timing_read(pmk_handle* h, double* total_ms, int32_t* launches);
 
 /* Task trace for profiling the schedule. `buf` is a caller-owned device buffer
- * of grid * entries_per_wg * 4 uint32 (grid from pmk_query); NULL detaches.
+ * of grid * entries_per_wg * 8 uint32 (grid from pmk_query); NULL detaches.
  * While attached, every call records, per workgroup w, at
- * buf[(w * entries_per_wg + i) * 4 + 0..3] for i >= 1:
+ * buf[(w * entries_per_wg + i) * 8 + 0..7] for i >= 1:
  *   [0] task type | layer << 8 | (first task coordinate & 0xffff) << 16
  *   [1] low 32 bits of the 100 MHz device clock when the task was taken
- *   [2] the same clock once its input event was satisfied
- *   [3] the same clock when it had finished and notified
- * and at entry i = 0, element [0], the number of tasks recorded (tasks beyond
+ *   [2] the clock once its input event was satisfied
+ *   [3] the clock once its GEMV inputs were staged in LDS
+ *   [4] the clock once wave 0 had streamed its weights
+ *   [5] the clock once the partial sums were reduced
+ *   [6] the clock once the epilogue had stored its outputs
+ *   [7] the clock when it had finished and notified
+ * (a phase the task does not have repeats the previous clock), and at entry
+ * i = 0, element [0], the number of tasks recorded (tasks beyond
  * entries_per_wg - 1 are dropped). Each call overwrites the buffer.
  * Errors: PMK_ERR_ARG (null handle, entries_per_wg < 2 with a buffer). */
 int pmk_trace_attach(pmk_handle* h, uint32_t* buf, int32_t entries_per_wg);

@@ -68,77 +68,112 @@ __device__ __forceinline__ unsigned long long now_ticks() { return __builtin_amd
 
 // ---------------------------------------------------------------------------
 // Events (Event Tensor summary, Core method: notify = atomic decrement,
-// wait = spin until zero). An event is kEvInts ints: [0] is what waiters spin
-// on; [1 + x] are sub-counters that spread the decrements of many producers
-// over 8 addresses; the producer that takes a sub-counter to zero decrements
-// [0]. The prologue arms [0] with the number of non-empty sub-counters and
-// each sub-counter with its producer count (flat events: [0] = producers).
+// wait = spin until zero). An event is kEvInts ints holding 1 + kSubs
+// counters 64 bytes apart: [0] and sub-counters [1 + x], x < kSubs. The event
+// has fired when all of them are zero. Notifiers decrement one of them (a
+// stage with many notifying tasks spreads them over the sub-counters, so no
+// single address takes every decrement) with an atomic whose result is not
+// awaited; the waiting wave reads all of them at once and votes.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int* ev_slot(int* ev, int sub) { return sub >= 0 ? ev + (1 + sub) * kCtr : ev; }
 
-// Whole workgroup: publish this workgroup's completed stores, then notify.
+// Whole workgroup: publish this workgroup's completed stores, then notify
+// (sub < 0: counter [0]).
 __device__ __forceinline__ void wg_notify(int* ev, int sub) {
   vm_drain();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    if (sub >= 0) {
-      if (atomic_add_relaxed(ev + (1 + sub) * kCtr, -1) == 1) atomic_add_relaxed(ev, -1);
-    } else {
-      atomic_add_relaxed(ev, -1);
-    }
-  }
+  if (threadIdx.x == 0) (void)__hip_atomic_fetch_add(ev_slot(ev, sub), -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 only: spin until *ev == 0. Returns false on abort or watchdog
-// expiry (then the error word holds PMK_ERR_TIMEOUT and the abort flag is set,
-// so every other waiting workgroup also leaves its loop).
-__device__ __forceinline__ bool spin_zero(const int* ev, int* err, unsigned long long ticks) {
-  if (ldci(ev) == 0) return true;
-  unsigned long long t0 = now_ticks();
+// Wave 0 only: spin until the event's counters are all zero (`subs` = number
+// of sub-counters to read besides [0]; 0 for a bare counter). Returns false on
+// abort or watchdog expiry (then the error word holds PMK_ERR_TIMEOUT and the
+// abort flag is set, so every other waiting workgroup also leaves its loop).
+__device__ __forceinline__ bool spin_zero(const int* ev, int subs, int* err, unsigned long long ticks) {
+  const int lane = threadIdx.x & 63;
+  const int* mine = ev + (lane <= subs ? lane : 0) * kCtr;
+  if (__all(ldci(mine) == 0)) return true;
+  const unsigned long long t0 = now_ticks();
   for (int it = 0;; ++it) {
     __builtin_amdgcn_s_sleep(1);
-    if (ldci(ev) == 0) return true;
+    if (__all(ldci(mine) == 0)) return true;
     if ((it & 15) == 15) {
       if (ldci(err + 16) != 0) return false;
       if (now_ticks() - t0 > ticks) {
-        int expected = 0;
-        __hip_atomic_compare_exchange_strong(err, &expected, (int)PMK_ERR_TIMEOUT, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT);
-        stci(err + 16, 1);
+        if (lane == 0) {
+          int expected = 0;
+          __hip_atomic_compare_exchange_strong(err, &expected, (int)PMK_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          stci(err + 16, 1);
+        }
         return false;
       }
     }
   }
 }
 
-// Whole workgroup: wait until *ev == 0 (thread 0 spins, the others park at the
-// barrier). `flag` is an LDS int. Returns false if the step was abandoned.
-__device__ __forceinline__ bool wg_wait(const int* ev, int* err, unsigned long long ticks, int* flag) {
+// Whole workgroup: wait until the event has fired (wave 0 spins, the others
+// park at the barrier). `flag` is an LDS int. Returns false if the step was
+// abandoned.
+__device__ __forceinline__ bool wg_wait(const int* ev, int subs, int* err, unsigned long long ticks, int* flag) {
   if (!ev) return true;
-  if (threadIdx.x == 0) *flag = spin_zero(ev, err, ticks) ? 1 : 0;
+  if (threadIdx.x < 64) {
+    const bool ok = spin_zero(ev, subs, err, ticks);
+    if (threadIdx.x == 0) *flag = ok ? 1 : 0;
+  }
   __syncthreads();
   return *flag != 0;
 }
 
 // ---------------------------------------------------------------------------
-// Wave reductions (wave64).
+// Wave reductions (wave64) without the LDS crossbar: DPP moves within a row of
+// 16 lanes (quad permutes, half-row and row mirrors) and the gfx950 permlane
+// swaps between rows (16: rows 0<->1 and 2<->3; 32: rows 0,1 <-> 2,3).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-// Sum over each aligned group of 16 lanes (a KV row of 256 bytes).
+// Sum over each row of 16 lanes (every lane of the row gets it).
 __device__ __forceinline__ float sum16(float v) {
-  v += __shfl_xor(v, 8, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 1, 64);
+  v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);   // row_half_mirror
+  v += dpp<0x140>(v);   // row_mirror
   return v;
+}
+// Row exchange between two registers holding the same value: afterwards one
+// holds rows (0, 0, 2, 2) and the other (1, 1, 3, 3) for the 16-lane swap, or
+// (lo, lo) and (hi, hi) for the 32-lane swap. Written as inline assembly (two
+// read-write register operands, with the hazard padding the swap needs): the
+// compiler's lowering of the builtin here returns one register for both halves.
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  __asm__ volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+// Sum / max over the 4 rows, lane by lane (lane i gets the value of lanes i, i^16, i^32, i^48).
+__device__ __forceinline__ float xrow_sum(float v) {
+  float a = v, b = v;
+  swap16(a, b);
+  float c = a + b, d = c;
+  swap32(c, d);
+  return c + d;
+}
+__device__ __forceinline__ float xrow_max(float v) {
+  float a = v, b = v;
+  swap16(a, b);
+  float c = fmaxf(a, b), d = c;
+  swap32(c, d);
+  return fmaxf(c, d);
+}
+__device__ __forceinline__ float wave_sum(float v) { return xrow_sum(sum16(v)); }
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return xrow_max(v);
 }
 
 // ---------------------------------------------------------------------------

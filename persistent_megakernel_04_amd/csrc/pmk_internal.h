@@ -116,9 +116,10 @@ struct StepArgs {
   const int32_t* seq_lens;
   int batch;
   int attn_chunk;                      // KV positions per attention task this step (set by the prologue)
+  int attn_merge_o;                    // 1: O-projection inputs merge the attention partials (set by the prologue)
   unsigned long long watchdog_ticks;   // s_memrealtime ticks (100 MHz)
   pmk_routing rout;                    // optional routing outputs (device pointers)
-  uint32_t* trace;                     // optional task trace [grid][trace_cap][4], caller-owned
+  uint32_t* trace;                     // optional task trace [grid][trace_cap][8], caller-owned
   int trace_cap;                       // entries per workgroup (entry 0 is the header)
 };
 

@@ -44,7 +44,7 @@ struct Lds {
   float* rstd;     // [kMaxNb] 1/rms of the staged rows
   float* ssp;      // [kMaxNb][kWaves] per-wave partial sums of squares
   int* flag;       // wait / last-arriver broadcast
-  uint32_t* tclk;  // [0]: clock when the current task's input event was seen (trace)
+  uint32_t* tclk;  // [8] phase clocks of the current task (trace): see the trace record layout
 };
 
 __device__ __forceinline__ Lds lds_layout(char* base) {
@@ -56,7 +56,7 @@ __device__ __forceinline__ Lds lds_layout(char* base) {
   s.rstd = reinterpret_cast<float*>(m);                   // 16 floats
   s.ssp = reinterpret_cast<float*>(m + 64);               // 128 floats
   s.flag = reinterpret_cast<int*>(m + 64 + 512);          // 1 int
-  s.tclk = reinterpret_cast<uint32_t*>(m + 64 + 512 + 16);
+  s.tclk = reinterpret_cast<uint32_t*>(m + 64 + 512 + 16);   // 8 clocks
   return s;
 }
 
@@ -74,10 +74,11 @@ __device__ __forceinline__ size_t kv_off(const Dims& dm, int l, int which, int b
   return (((((size_t)l * 2 + which) * dm.max_batch + b) * dm.Hkv + g) * (size_t)dm.max_seq + pos) * dm.d;
 }
 
-__device__ __forceinline__ bool ctx_wait(const Ctx& c, const int* ev) {
+// Wait on an event (its [0] and kSubs sub-counters) or, with subs = 0, on a bare counter.
+__device__ __forceinline__ bool ctx_wait(const Ctx& c, const int* ev, int subs = kSubs) {
   if (!ev) return true;
-  const bool ok = wg_wait(ev, c.a.ws.err, c.a.watchdog_ticks, c.s.flag);
-  if (threadIdx.x == 0) *c.s.tclk = (uint32_t)now_ticks();
+  const bool ok = wg_wait(ev, subs, c.a.ws.err, c.a.watchdog_ticks, c.s.flag);
+  if (threadIdx.x == 0) c.s.tclk[1] = (uint32_t)now_ticks();
   return ok;
 }
 
@@ -89,13 +90,13 @@ __device__ __forceinline__ bool ctx_wait(const Ctx& c, const int* ev) {
 //   type; with `norm`, rstd[m] = 1 / sqrt(mean src[m]^2 + eps) (RMSNorm folded
 //   into the GEMV: the epilogue multiplies by rstd).
 //
-// The R rows form RG = ceil(R / 16) row groups, taken RGM at a time; the 8
-// waves split the k range; each wave streams its k slice of the row groups as
-// 16-byte-per-lane loads (16 rows x 64 contiguous bytes per load instruction)
-// through a register ring of KSD k-steps x RGM row groups (16 loads, 16 KiB per
+// The R rows form RG = ceil(R / 16) row groups. Each wave streams its work
+// items (row group x k range) row-group-major as 16-byte-per-lane loads (16
+// rows x 64 contiguous bytes per load instruction, consecutive instructions
+// walking along the same rows) through a register ring of 16 loads (16 KiB per
 // wave). The ring is filled before the input event is awaited and refilled as
-// it is consumed. Partial
-// sums of the 8 waves are added in LDS in wave order (deterministic).
+// it is consumed, flowing from one item into the next. Partial sums of waves
+// that share a row group are added in LDS in wave order (deterministic).
 // ---------------------------------------------------------------------------
 enum RowMode : int { ROWS_CONTIG = 0, ROWS_QKV = 1, ROWS_PAIR = 2 };
 
@@ -127,6 +128,7 @@ struct GemvIn {
   const float* gain;   // nullable: elementwise gain (RMSNorm weight)
   int norm;            // compute rstd
   float eps;
+  int merge_b0;        // >= 0: the rows are the attention outputs of requests merge_b0.. (merged from partials)
 };
 
 // Stage nb input rows into LDS as the MFMA input type, rows XS apart (SPLIT:
@@ -187,114 +189,206 @@ __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int 
   __syncthreads();
 }
 
-// Per-lane row pointers of row groups [rg0, rg0 + RGM) and the first KSD
-// k-steps of the ring (padded rows and k-steps repeat valid addresses; their
-// products are never accumulated).
-template <typename WT, int RGM, int KSD>
-__device__ __forceinline__ void ring_fill(uint4 (&ring)[KSD][RGM], const WT* (&rp)[RGM], const GemvRows& rw,
-                                          int rg0, int RG, int R, int K, int kl0, int nks_c, int mrow) {
-  typedef MM<WT> T;
+// Stage the O-projection inputs of nb requests by merging their attention
+// chunk partials (acc, max, sum per query head; the chunk tasks wrote them and
+// notified) by log-sum-exp: o = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M).
+// Used when every request has at most 8 chunks and each thread stages at most
+// two 4-element units, so all partial loads of a thread are in flight at once.
+template <typename WT, bool SP>
+__device__ __forceinline__ void stage_attn_merge(const StepArgs& a, const GemvIn& in, int nb, int K, int Kp, int XS,
+                                                 const Lds& s) {
+  typedef typename MM<WT>::XT XT;
+  XT* xs = reinterpret_cast<XT*>(s.xs);
+  const Dims& dm = a.dm;
+  const int d = dm.d, G = dm.Hq / dm.Hkv, DP = d + 4, ck = a.attn_chunk;
+  const int K4 = Kp / 4;   // 4-element units per row (K = Hq d, a multiple of 4; zero beyond K)
 #pragma unroll
-  for (int rg = 0; rg < RGM; ++rg) {
-    const int j = min(min(rg0 + rg, RG - 1) * 16 + mrow, R - 1);
-    rp[rg] = row_ptr<WT>(rw, j, K);
+  for (int u = 0; u < 2; ++u) {
+    const int unit = threadIdx.x + u * kBlock;
+    if (unit >= nb * K4) continue;
+    const int m = unit / K4, k = (unit - m * K4) * 4;
+    f4v x = {0.f, 0.f, 0.f, 0.f};
+    if (k < K) {
+      const int b = in.merge_b0 + m, nc = (a.seq_lens[b] + ck) / ck;
+      const int h = k / d, e = k - h * d, g = h / G, hh = h - g * G;
+      const float* base = a.ws.part + ((size_t)b * dm.Hkv + g) * dm.max_chunks * G * DP + hh * DP;
+      f4v av[8], mv[8];
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const auto r = rsrc(base + (size_t)min(cc, nc - 1) * G * DP);
+        av[cc] = ldc4(r, e * 4);
+        mv[cc] = ldc4(r, d * 4);
+      }
+      float M = -INFINITY, L = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc)
+        if (cc < nc) M = fmaxf(M, mv[cc].x);
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        if (cc < nc) {
+          const float f = exp2f(mv[cc].x - M);
+          L += mv[cc].y * f;
+          x += av[cc] * f;
+        }
+      }
+      x = x / L;
+    }
+    if (SP)
+      MM<WT>::put4_split(xs + (size_t)m * 2 * XS + k, xs + (size_t)m * 2 * XS + XS + k, x);
+    else
+      MM<WT>::put4(xs + (size_t)m * XS + k, x);
   }
-#pragma unroll
-  for (int d = 0; d < KSD; ++d) {
-    const int k = min(kl0 + min(d, nks_c) * T::KSTEP, K - T::EPL);
-#pragma unroll
-    for (int rg = 0; rg < RGM; ++rg) ring[d][rg] = ldg16(rp[rg] + k);
-  }
+  __syncthreads();
 }
 
-// Returns false if the wait was abandoned (nothing was computed). SPLIT: the
+// One wave's share of a GEMV pass: work items (row group, k-step range)
+// streamed one after another. Tiles of fewer than 8 row groups split each row
+// group's k range over 8 / RG waves (their partial sums are added in LDS);
+// tiles of 8 or more give each wave whole row groups rg, rg + 8, ...
+struct WaveItems {
+  int n;        // items of this wave
+  int rg0;      // row group of the first item
+  int rg_step;  // row group step between consecutive items
+  int ks_lo;    // every item covers k-steps [ks_lo, ks_lo + nks)
+  int nks;
+};
+
+__device__ __forceinline__ int k_split(int RG) { return RG >= kWaves ? 1 : kWaves / RG; }
+
+__device__ __forceinline__ WaveItems wave_items(int RG, int NKS, int wave) {
+  WaveItems it;
+  const int ks = k_split(RG);
+  if (ks == 1) {
+    it.n = wave < RG ? (RG - wave + kWaves - 1) / kWaves : 0;
+    it.rg0 = wave;
+    it.rg_step = kWaves;
+    it.ks_lo = 0;
+    it.nks = NKS;
+  } else {
+    const bool busy = wave < RG * ks;
+    const int sl = wave % ks;
+    it.n = busy ? 1 : 0;
+    it.rg0 = busy ? wave / ks : 0;
+    it.rg_step = 0;
+    it.ks_lo = sl * NKS / ks;
+    it.nks = (sl + 1) * NKS / ks - it.ks_lo;
+  }
+  return it;
+}
+
+// Returns false if the wait was abandoned (nothing was computed). SP: the
 // input rows are carried as bfloat16 hi + lo pairs, two MFMAs per chunk.
-template <typename WT, int RGM, bool SPLIT>
-__device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb, const int* wait_ev) {
+template <typename WT, bool SP>
+__device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
+                                     const int* wait_ev, int wait_subs) {
   typedef MM<WT> T;
   typedef typename T::XT XT;
-  constexpr int KSD = 16 / RGM;   // 16 chunks (16 KiB per wave) in flight
+  constexpr int D = 16;   // loads in flight per wave (16 KiB; 128 KiB per workgroup)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, mrow = lane & 15;
-  const int NKS = (K + T::KSTEP - 1) / T::KSTEP;
-  const int ks_lo = wave * NKS / kWaves, nks = (wave + 1) * NKS / kWaves - ks_lo;
-  const int nks_c = nks > 0 ? nks - 1 : 0;
-  const int RG = (R + 15) >> 4;
+  const int NKS = (K + T::KSTEP - 1) / T::KSTEP, RG = (R + 15) >> 4;
   const int Kp = NKS * T::KSTEP, XS = Kp + T::XPAD;
-  const int kl0 = ks_lo * T::KSTEP + grp * T::EPL;   // this lane's first k
-  const int kmax = K - T::EPL;
+  const int kmax = K - T::EPL, kg = grp * T::EPL;
+  const WaveItems wi = wave_items(RG, NKS, wave);
+  const int nks = wi.nks, nks_c = nks > 0 ? nks - 1 : 0;
+  // consecutive items stream without a bubble when an item is a whole number of rings
+  const bool chain = nks % D == 0;
+  auto item_rows = [&](int it) -> const WT* {
+    const int rg = min(wi.rg0 + min(it, max(wi.n - 1, 0)) * wi.rg_step, RG - 1);
+    return row_ptr<WT>(rw, min(rg * 16 + mrow, R - 1), K);   // padded rows repeat a valid row
+  };
+  auto kofs = [&](int ks) { return min((wi.ks_lo + ks) * T::KSTEP + kg, kmax); };
 
-  uint4 ring[KSD][RGM];
-  const WT* rp[RGM];
-  ring_fill<WT, RGM, KSD>(ring, rp, rw, 0, RG, R, K, kl0, nks_c, mrow);
-  if (!ctx_wait(c, wait_ev)) return false;
-  stage_rows<WT, SPLIT>(in, nb, K, Kp, XS, c.s);
-
-  const XT* xrow = reinterpret_cast<const XT*>(c.s.xs) + (size_t)(mrow < nb ? mrow : 0) * (SPLIT ? 2 : 1) * XS + kl0;
-  const bool xon = mrow < nb;
-  const int per = kRedBytes / 4 / (kWaves * 16 * nb);
-  const int rgb = per < 1 ? 1 : per;
-  for (int rg0 = 0; rg0 < RG; rg0 += RGM) {
-    if (rg0 > 0) ring_fill<WT, RGM, KSD>(ring, rp, rw, rg0, RG, R, K, kl0, nks_c, mrow);
-    const int rgn = min(RGM, RG - rg0);   // row groups of this round that hold real rows
-    f4v acc[RGM];
+  uint4 ring[D];
+  const WT* cur = item_rows(0);
+  const WT* nxt = item_rows(1);
+  if (wi.n > 0) {
 #pragma unroll
-    for (int rg = 0; rg < RGM; ++rg) acc[rg] = f4v{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < D; ++d) ring[d] = ldg16(cur + kofs(min(d, nks_c)));
+  }
+  if (!ctx_wait(c, wait_ev, wait_subs)) return false;
+  if (in.merge_b0 >= 0)
+    stage_attn_merge<WT, SP>(c.a, in, nb, K, Kp, XS, c.s);
+  else
+    stage_rows<WT, SP>(in, nb, K, Kp, XS, c.s);
+  if (tid == 0) c.s.tclk[2] = (uint32_t)now_ticks();
+
+  const XT* xrow = reinterpret_cast<const XT*>(c.s.xs) + (size_t)(mrow < nb ? mrow : 0) * (SP ? 2 : 1) * XS +
+                   wi.ks_lo * T::KSTEP + kg;
+  const bool xon = mrow < nb;
+  const int KSPL = k_split(RG);
+  for (int it = 0; it < wi.n; ++it) {
+    if (it > 0 && !chain) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) ring[d] = ldg16(cur + kofs(min(d, nks_c)));
+    }
+    const bool has_next = chain && it + 1 < wi.n;
+    f4v acc = {0.f, 0.f, 0.f, 0.f};
+    // the input fragments of the next k-step are read from LDS one step ahead
+    uint4 xa_n = *reinterpret_cast<const uint4*>(xrow), xl_n = make_uint4(0, 0, 0, 0);
+    if (SP) xl_n = *reinterpret_cast<const uint4*>(xrow + XS);
     // Branch-free body, so the compiler's wait counts stay exact (a branch
     // here makes it wait for every load in flight before each MFMA): steps
-    // past this wave's range multiply a zero input; padded row groups
-    // accumulate values that are never read.
-    for (int ks0 = 0; ks0 < nks; ks0 += KSD) {
+    // past the item multiply a zero input.
+    for (int ks0 = 0; ks0 < nks; ks0 += D) {
 #pragma unroll
-      for (int d = 0; d < KSD; ++d) {
+      for (int d = 0; d < D; ++d) {
         const int ks = ks0 + d;
-        uint4 xa = *reinterpret_cast<const uint4*>(xrow + min(ks, nks_c) * T::KSTEP);
         const bool on = xon && ks < nks;
+        uint4 xa = xa_n, xl = xl_n;
+        const int xo = min(ks + 1, nks_c) * T::KSTEP;
+        xa_n = *reinterpret_cast<const uint4*>(xrow + xo);
+        if (SP) xl_n = *reinterpret_cast<const uint4*>(xrow + XS + xo);
         xa.x = on ? xa.x : 0u;
         xa.y = on ? xa.y : 0u;
         xa.z = on ? xa.z : 0u;
         xa.w = on ? xa.w : 0u;
-#pragma unroll
-        for (int rg = 0; rg < RGM; ++rg) acc[rg] = T::mac(xa, ring[d][rg], acc[rg]);
-        if (SPLIT) {
-          uint4 xl = *reinterpret_cast<const uint4*>(xrow + XS + min(ks, nks_c) * T::KSTEP);
+        acc = T::mac(xa, ring[d], acc);
+        if (SP) {
           xl.x = on ? xl.x : 0u;
           xl.y = on ? xl.y : 0u;
           xl.z = on ? xl.z : 0u;
           xl.w = on ? xl.w : 0u;
-#pragma unroll
-          for (int rg = 0; rg < RGM; ++rg) acc[rg] = T::mac(xl, ring[d][rg], acc[rg]);
+          acc = T::mac(xl, ring[d], acc);
         }
-        const int k = min(kl0 + min(ks + KSD, nks_c) * T::KSTEP, kmax);
-#pragma unroll
-        for (int rg = 0; rg < RGM; ++rg) ring[d][rg] = ldg16(rp[rg] + k);
+        // refill: k-step ks + D of this item, else the next item's first steps
+        const int nk = ks + D;
+        const bool here = nk < nks;
+        const WT* bp = (here || !has_next) ? cur : nxt;
+        const int kk = here ? nk : (has_next ? nk - nks : nks_c);
+        ring[d] = ldg16(bp + kofs(kk));
+        // keep the refill here: left to itself the scheduler sinks all refills
+        // to the end of the unrolled body, and the ring degrades to batches
+        // that drain to zero loads in flight
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // cross-wave reduction of these row groups, rgb at a time
-    for (int g0 = 0; g0 < rgn; g0 += rgb) {
-      const int g1 = min(rgn, g0 + rgb);
+    // D[m][j] of this item's row group: lane (j + 16 * (m / 4)), element m % 4
+    const int rg = wi.rg0 + it * wi.rg_step;
 #pragma unroll
-      for (int rg = 0; rg < RGM; ++rg) {
-        if (rg >= g0 && rg < g1) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int m = grp * 4 + e;
-            if (m < nb) c.s.red[((wave * rgb + (rg - g0)) * nb + m) * 16 + mrow] = acc[rg][e];
-          }
-        }
+    for (int e = 0; e < 4; ++e) {
+      const int m = grp * 4 + e, j = rg * 16 + mrow;
+      if (KSPL == 1) {
+        if (m < nb && j < R) c.s.ys[j * nb + m] = acc[e];
+      } else if (m < nb) {
+        c.s.red[(wave * nb + m) * 16 + mrow] = acc[e];
       }
-      __syncthreads();
-      const int cnt = (g1 - g0) * nb * 16;
-      for (int t = tid; t < cnt; t += kBlock) {
-        const int jj = t & 15, mm = (t >> 4) % nb, rl = (t >> 4) / nb;
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) sum += c.s.red[((w * rgb + rl) * nb + mm) * 16 + jj];
-        const int j = (rg0 + g0 + rl) * 16 + jj;
-        if (j < R) c.s.ys[j * nb + mm] = sum;
-      }
-      __syncthreads();
     }
+    cur = nxt;
+    nxt = item_rows(it + 2);
   }
+  if (tid == 0) c.s.tclk[3] = (uint32_t)now_ticks();
+  __syncthreads();
+  if (KSPL > 1) {   // add the k slices of each row group, in slice order
+    for (int t = tid; t < RG * nb * 16; t += kBlock) {
+      const int jj = t & 15, mm = (t >> 4) % nb, rg = (t >> 4) / nb;
+      float sum = 0.f;
+      for (int sl = 0; sl < KSPL; ++sl) sum += c.s.red[((rg * KSPL + sl) * nb + mm) * 16 + jj];
+      const int j = rg * 16 + jj;
+      if (j < R) c.s.ys[j * nb + mm] = sum;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) c.s.tclk[4] = (uint32_t)now_ticks();
   return true;
 }
 
@@ -305,13 +399,8 @@ template <typename WT> struct SplitIn { static constexpr bool value = sizeof(WT)
 
 template <typename WT>
 __device__ __forceinline__ bool gemv_any(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
-                                         const int* wev) {
-  constexpr bool SP = SplitIn<WT>::value;
-  const int RG = (R + 15) >> 4;
-  if (RG <= 1) return gemv<WT, 1, SP>(c, rw, R, K, in, nb, wev);
-  if (RG <= 2) return gemv<WT, 2, SP>(c, rw, R, K, in, nb, wev);
-  if (RG <= 4) return gemv<WT, 4, SP>(c, rw, R, K, in, nb, wev);
-  return gemv<WT, 8, SP>(c, rw, R, K, in, nb, wev);
+                                         const int* wev, int wsubs) {
+  return gemv<WT, SplitIn<WT>::value>(c, rw, R, K, in, nb, wev, wsubs);
 }
 
 // Input rows per GEMV pass for depth K and R output rows: what the LDS input
@@ -340,6 +429,7 @@ struct Pass {
   GemvIn in;
   int R, K, nb;
   const int* wev;   // event the pass waits on (after its weights are in flight)
+  int wsubs;        // its sub-counters (0: a bare counter)
   int epi;
   int b0;           // first batch row (dense, router) or first grouped row (MoE)
   int r0;           // first rotation unit (QKV), output row, or expert column
@@ -355,6 +445,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   const LayerPtrs& Lp = a.layers[c.l];
   const int tile = task.y;
   ps.wev = p == 0 ? wev : nullptr;
+  ps.wsubs = kSubs;
   ps.e = 0;
   switch (task.x) {
     case T_QKV: {   // RMSNorm1 + QKV rotation pairs of the tile
@@ -363,7 +454,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int nbb = pass_rows<WT>(dm.H, 2 * nu), b0 = p * nbb;
       if (b0 >= a.batch) return false;
       ps.rw = GemvRows{ROWS_QKV, Lp.w_qkv, nullptr, u0, dm.d >> 1};
-      ps.in = GemvIn{a.hidden + (size_t)b0 * dm.H, dm.H, nullptr, Lp.attn_norm, 1, dm.eps};
+      ps.in = GemvIn{a.hidden + (size_t)b0 * dm.H, dm.H, nullptr, Lp.attn_norm, 1, dm.eps, -1};
       ps.R = 2 * nu; ps.K = dm.H; ps.nb = min(nbb, a.batch - b0);
       ps.epi = E_QKV; ps.b0 = b0; ps.r0 = u0; ps.n = nu;
       return true;
@@ -374,7 +465,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int nbb = pass_rows<WT>(K, R), b0 = p * nbb;
       if (b0 >= a.batch) return false;
       ps.rw = GemvRows{ROWS_CONTIG, Lp.w_o, nullptr, r0, 0};
-      ps.in = GemvIn{a.ws.o + (size_t)b0 * K, K, nullptr, nullptr, 0, 0.f};
+      ps.in = GemvIn{a.ws.o + (size_t)b0 * K, K, nullptr, nullptr, 0, 0.f, a.attn_merge_o ? b0 : -1};
       ps.R = R; ps.K = K; ps.nb = min(nbb, a.batch - b0);
       ps.epi = E_O; ps.b0 = b0; ps.r0 = r0; ps.n = R;
       return true;
@@ -384,7 +475,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int nbb = pass_rows<WT>(dm.H, 2 * Rh), b0 = p * nbb;
       if (b0 >= a.batch) return false;
       ps.rw = GemvRows{ROWS_PAIR, Lp.w_gate, Lp.w_up, r0, Rh};
-      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, Lp.ffn_norm, 1, dm.eps};
+      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, Lp.ffn_norm, 1, dm.eps, -1};
       ps.R = 2 * Rh; ps.K = dm.H; ps.nb = min(nbb, a.batch - b0);
       ps.epi = E_GU; ps.b0 = b0; ps.r0 = r0; ps.n = Rh;
       return true;
@@ -394,7 +485,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int nbb = pass_rows<WT>(dm.F, R), b0 = p * nbb;
       if (b0 >= a.batch) return false;
       ps.rw = GemvRows{ROWS_CONTIG, Lp.w_down, nullptr, r0, 0};
-      ps.in = GemvIn{a.ws.act + (size_t)b0 * dm.F, dm.F, nullptr, nullptr, 0, 0.f};
+      ps.in = GemvIn{a.ws.act + (size_t)b0 * dm.F, dm.F, nullptr, nullptr, 0, 0.f, -1};
       ps.R = R; ps.K = dm.F; ps.nb = min(nbb, a.batch - b0);
       ps.epi = E_DOWN; ps.b0 = b0; ps.r0 = r0; ps.n = R;
       return true;
@@ -405,7 +496,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       if (b0 >= bend) return false;
       const int r0 = tile * 16;
       ps.rw = GemvRows{ROWS_CONTIG, Lp.w_router, nullptr, r0, 0};
-      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, Lp.ffn_norm, 1, dm.eps};
+      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, Lp.ffn_norm, 1, dm.eps, -1};
       ps.R = min(16, dm.E - r0); ps.K = dm.H; ps.nb = min(nbb, bend - b0);
       ps.epi = E_ROUTER; ps.b0 = b0; ps.r0 = r0; ps.n = ps.R;
       return true;
@@ -420,7 +511,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       ps.rw = GemvRows{ROWS_PAIR, reinterpret_cast<const WT*>(Lp.w_exp_gate) + eo,
                        reinterpret_cast<const WT*>(Lp.w_exp_up) + eo, f0, Rh};
       // the tile's rows: its routed tokens' FFN inputs (RMSNorm2 of h1), gathered
-      ps.in = GemvIn{a.ws.h1, dm.H, a.ws.sorted_tok + row0, Lp.ffn_norm, 1, dm.eps};
+      ps.in = GemvIn{a.ws.h1, dm.H, a.ws.sorted_tok + row0, Lp.ffn_norm, 1, dm.eps, -1};
       ps.R = 2 * Rh; ps.K = dm.H; ps.nb = min(kMoeBM, ldci(a.ws.exp_indptr + e + 1) - row0);
       ps.epi = E_MGU; ps.b0 = row0; ps.r0 = f0; ps.n = Rh; ps.e = e;
       return true;
@@ -433,9 +524,10 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int h0 = (int)((long)sl * dm.H / sd), R = (int)((long)(sl + 1) * dm.H / sd) - h0;
       ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(Lp.w_exp_down) + (size_t)e * dm.H * dm.Fe, nullptr, h0,
                        0};
-      ps.in = GemvIn{a.ws.mact + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f};
+      ps.in = GemvIn{a.ws.mact + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f, -1};
       ps.R = R; ps.K = dm.Fe; ps.nb = min(kMoeBM, ldci(a.ws.exp_indptr + e + 1) - row0);
       ps.wev = a.ws.ectr + ((size_t)c.l * dm.E + e) * kCtr;
+      ps.wsubs = 0;
       ps.epi = E_MDOWN; ps.b0 = row0; ps.r0 = h0; ps.n = R; ps.e = e;
       return true;
     }
@@ -443,9 +535,28 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   }
 }
 
+// The residual an O / down pass adds (hidden, resp. h1): thread t holds
+// elements t, t + kBlock, ... of the [R][nb] tile (R nb <= kYsFloats).
+constexpr int kResid = kYsFloats / kBlock;
+__device__ __forceinline__ const float* resid_src(const StepArgs& a, const Pass& ps) {
+  return ps.epi == E_O ? a.hidden : a.ws.h1;
+}
+__device__ __forceinline__ void load_resid(const StepArgs& a, const Pass& ps, float (&r)[kResid]) {
+  const float* res = resid_src(a, ps);
+#pragma unroll
+  for (int k = 0; k < kResid; ++k) {
+    const int idx = threadIdx.x + k * kBlock;
+    if (idx < ps.n * ps.nb) {
+      const int j = idx / ps.nb, m = idx - j * ps.nb;
+      r[k] = ldc(res + (size_t)(ps.b0 + m) * a.dm.H + ps.r0 + j);
+    }
+  }
+}
+
 // Consume a pass's result (ys[j][m], rstd[m] in LDS) and store its outputs.
+// `resid` holds the O / down residual when it was loaded ahead (have_resid).
 template <typename WT>
-__device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps) {
+__device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, float (&resid)[kResid], bool have_resid) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   const int nb = ps.nb, b0 = ps.b0;
@@ -479,12 +590,15 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps) {
     }
     case E_O:       // h1 = x + W_o o
     case E_DOWN: {  // x' = h1 + W_down act (the layer output, into hidden)
-      const float* res = ps.epi == E_O ? a.hidden : a.ws.h1;
+      if (!have_resid) load_resid(a, ps, resid);
       float* out = ps.epi == E_O ? a.ws.h1 : a.hidden;
-      for (int idx = threadIdx.x; idx < ps.n * nb; idx += kBlock) {
-        const int j = idx / nb, m = idx - j * nb;
-        const size_t off = (size_t)(b0 + m) * dm.H + ps.r0 + j;
-        stc(out + off, ldc(res + off) + ys[j * nb + m]);
+#pragma unroll
+      for (int k = 0; k < kResid; ++k) {
+        const int idx = threadIdx.x + k * kBlock;
+        if (idx < ps.n * nb) {
+          const int j = idx / nb, m = idx - j * nb;
+          stc(out + (size_t)(b0 + m) * dm.H + ps.r0 + j, resid[k] + ys[j * nb + m]);
+        }
       }
       break;
     }
@@ -558,7 +672,7 @@ template <> __device__ __forceinline__ uint4 pack_row<float>(const float* p) {
 }
 
 template <typename KT, int HB, int ITS>
-__device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, const int* wev) {
+__device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, int tix, const int* wev) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   constexpr int EPL = 16 / (int)sizeof(KT);   // elements per lane (16 B)
@@ -594,9 +708,17 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, co
     vn = pack_row<KT>(a.ws.qkv + (size_t)b * qkv_dim + (size_t)(dm.Hq + dm.Hkv + g) * D + li * EPL);
   }
   __syncthreads();
+  if (tid == 0) c.s.tclk[2] = (uint32_t)now_ticks();
   const float qscale = 1.4426950408889634f / sqrtf((float)D);   // 1/sqrt(d), in log2 units
 
   for (int h0 = 0; h0 < G; h0 += HB) {
+    // keep the KV rows packed across head groups (unpacking them once for all
+    // groups would hold 16 floats per row live and spill)
+#pragma unroll
+    for (int it = 0; it < ITS; ++it) {
+      __asm__ volatile("" : "+v"(kr[it].x), "+v"(kr[it].y), "+v"(kr[it].z), "+v"(kr[it].w));
+      __asm__ volatile("" : "+v"(vr[it].x), "+v"(vr[it].y), "+v"(vr[it].z), "+v"(vr[it].w));
+    }
     float q[HB][EPL], m[HB], ls[HB], acc[HB][EPL];
 #pragma unroll
     for (int h = 0; h < HB; ++h) {
@@ -632,24 +754,20 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, co
     // combine the 4 position slots of the wave into this wave's LDS record
 #pragma unroll
     for (int h = 0; h < HB; ++h) {
-      float M = fmaxf(m[h], __shfl_xor(m[h], 16, 64));
-      M = fmaxf(M, __shfl_xor(M, 32, 64));
+      const float M = xrow_max(m[h]);
       const float sc = (M == -INFINITY) ? 0.f : exp2f(m[h] - M);
-      float lw = ls[h] * sc;
-      lw += __shfl_xor(lw, 16, 64);
-      lw += __shfl_xor(lw, 32, 64);
+      const float lw = xrow_sum(ls[h] * sc);
       float* dst = sw + (wave * G + h0 + h) * DP;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        float v = acc[h][e] * sc;
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
+        const float v = xrow_sum(acc[h][e] * sc);
         if (rs == 0) dst[li * EPL + e] = v;
       }
       if (lane == 0) { dst[D] = M; dst[D + 1] = lw; }
     }
   }
   __syncthreads();
+  if (tid == 0) c.s.tclk[3] = (uint32_t)now_ticks();
   // combine the 8 waves: this chunk's partial (or the output for a single chunk)
   float* o = a.ws.o + (size_t)b * dm.Hq * D + (size_t)g * G * D;
   float* part = a.ws.part + (((size_t)b * dm.Hkv + g) * dm.max_chunks + ci) * G * DP;
@@ -667,7 +785,7 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, co
       Ls += sp[D + 1] * f;
       A += *reinterpret_cast<const f4v*>(sp + e0) * f;
     }
-    if (nc == 1) {
+    if (nc == 1 && !a.attn_merge_o) {
       stc4(rsrc(o + h * D), e0 * 4, A / Ls);
     } else {
       const auto r = rsrc(part + h * DP);
@@ -675,8 +793,12 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, co
       if (e0 == 0) stc4(r, D * 4, f4v{M, Ls, 0.f, 0.f});
     }
   }
+  if (a.attn_merge_o) {   // the O-projection merges the partials as it stages its inputs
+    wg_notify(ev_ptr(a, c.l, EV_ATTN), tix & (kSubs - 1));
+    return true;
+  }
   if (nc == 1) {
-    wg_notify(ev_ptr(a, c.l, EV_ATTN), -1);
+    wg_notify(ev_ptr(a, c.l, EV_ATTN), (b * dm.Hkv + g) & (kSubs - 1));
     return true;
   }
   // the last chunk task of (b, g) to finish merges the partials
@@ -687,23 +809,24 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, co
     *c.s.flag = (atomic_add_relaxed(mc, -1) == 1);
   }
   __syncthreads();
+  if (tid == 0) c.s.tclk[4] = (uint32_t)now_ticks();
   if (*c.s.flag) {
     const float* pb = a.ws.part + ((size_t)b * dm.Hkv + g) * dm.max_chunks * G * DP;
     for (int t = tid; t < G * D / 4; t += kBlock) {
       const int h = t / (D / 4), e0 = (t - h * (D / 4)) * 4;
       float M = -INFINITY, Ls = 0.f;
       f4v A = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = 0; c0 < nc; c0 += 8) {
-        f4v ms[8], as[8];
+      for (int c0 = 0; c0 < nc; c0 += 16) {   // 16 chunks' loads in flight at once
+        f4v ms[16], as[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           const int cc = min(c0 + u, nc - 1);
           const auto r = rsrc(pb + ((size_t)cc * G + h) * DP);
           as[u] = ldc4(r, e0 * 4);
           ms[u] = ldc4(r, D * 4);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 16; ++u) {
           if (c0 + u < nc) {
             const float mn = fmaxf(M, ms[u].x);
             const float fo = (M == -INFINITY) ? 0.f : exp2f(M - mn), fc = exp2f(ms[u].x - mn);
@@ -715,25 +838,25 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, co
       }
       stc4(rsrc(o + h * D), e0 * 4, A / Ls);
     }
-    wg_notify(ev_ptr(a, c.l, EV_ATTN), -1);
+    wg_notify(ev_ptr(a, c.l, EV_ATTN), (b * dm.Hkv + g) & (kSubs - 1));
   }
   __syncthreads();
   return true;
 }
 
 template <typename KT, int HB>
-__device__ __forceinline__ bool attn_its(const Ctx& c, int b, int g, int ci, int ck, const int* wev) {
-  if (ck <= 64) return task_attn<KT, HB, 2>(c, b, g, ci, wev);
-  if (ck <= 128) return task_attn<KT, HB, 4>(c, b, g, ci, wev);
-  return task_attn<KT, HB, 8>(c, b, g, ci, wev);
+__device__ __forceinline__ bool attn_its(const Ctx& c, int b, int g, int ci, int tix, int ck, const int* wev) {
+  if (ck <= 64) return task_attn<KT, HB, 2>(c, b, g, ci, tix, wev);
+  if (ck <= 128) return task_attn<KT, HB, 4>(c, b, g, ci, tix, wev);
+  return task_attn<KT, HB, 8>(c, b, g, ci, tix, wev);
 }
 
 template <typename KT>
-__device__ __forceinline__ bool attn_dispatch(const Ctx& c, int b, int g, int ci, const int* wev) {
+__device__ __forceinline__ bool attn_dispatch(const Ctx& c, int b, int g, int ci, int tix, const int* wev) {
   const int G = c.a.dm.Hq / c.a.dm.Hkv, ck = c.a.attn_chunk;
-  if (G >= 4) return attn_its<KT, 4>(c, b, g, ci, ck, wev);
-  if (G == 2) return attn_its<KT, 2>(c, b, g, ci, ck, wev);
-  return attn_its<KT, 1>(c, b, g, ci, ck, wev);
+  if (G >= 4) return attn_its<KT, 4>(c, b, g, ci, tix, ck, wev);
+  if (G == 2) return attn_its<KT, 2>(c, b, g, ci, tix, ck, wev);
+  return attn_its<KT, 1>(c, b, g, ci, tix, ck, wev);
 }
 
 // ---------------------------------------------------------------------------
@@ -942,7 +1065,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
   if (!*s.flag) return;
   const int n = a.ws.qlen[wg];
   const int4* q = a.ws.queue + (size_t)wg * dm.max_queue;
-  uint32_t* tr = a.trace ? a.trace + (size_t)wg * a.trace_cap * 4 : nullptr;
+  uint32_t* tr = a.trace ? a.trace + (size_t)wg * a.trace_cap * 8 : nullptr;
   int tn = 1;
   for (int l = 0; l < dm.L; ++l) {
     const Ctx c{a, l, wg, s};
@@ -954,15 +1077,20 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
       passed |= bit;
       return ev_ptr(a, el, e);
     };
+    // whether an earlier task of this workgroup already waited on the event
+    auto seen = [&](int e, int el) -> bool { return (passed & (1u << (e + (el != l ? 16 : 0)))) != 0; };
     for (int t = 0; t < n; ++t) {
-      const int4 task = q[t];
+      int4 task = q[t];
+      const int tix = task.x >> 8;   // attention tasks: the task's index within the stage
+      task.x &= 0xff;
       const uint32_t t_begin = (uint32_t)now_ticks();
-      if (tr && threadIdx.x == 0) *s.tclk = t_begin;
+      if (tr && threadIdx.x == 0)
+        for (int i = 1; i < 7; ++i) s.tclk[i] = t_begin;
       bool ok = true;
       int notify = -1;   // event this task notifies through sub-counter (wg % kSubs)
       switch (task.x) {
         case T_ATTN:
-          ok = attn_dispatch<WT>(c, task.y, task.z, task.w, need(EV_QKV, l));
+          ok = attn_dispatch<WT>(c, task.y, task.z, task.w, tix, need(EV_QKV, l));
           break;
         case T_ROUTE:
           ok = task_route(c, need(EV_ROUTER, l));
@@ -988,8 +1116,14 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           for (int p = 0; ok; ++p) {
             Pass ps;
             if (!make_pass<WT>(c, task, p, wev, ps)) break;
-            ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev);
-            if (ok) epilogue<WT>(c, ps);
+            // the residual of O (the layer input) / down (h1) is final once this
+            // workgroup has seen the event that produced it: load it before waiting
+            float resid[kResid];
+            const bool early = (ps.epi == E_O && (l == 0 || seen(EV_DOWN, l - 1))) || (ps.epi == E_DOWN && seen(EV_O, l));
+            if (early) load_resid(a, ps, resid);
+            ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs);
+            if (ok) epilogue<WT>(c, ps, resid, early);
+            if (threadIdx.x == 0) s.tclk[5] = (uint32_t)now_ticks();
           }
           break;
         }
@@ -998,11 +1132,12 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
       if (!ok) return;
       if (tr && threadIdx.x == 0 && tn < a.trace_cap) {
         const uint32_t t_end = (uint32_t)now_ticks();
-        uint32_t* e = tr + (size_t)tn * 4;
+        uint32_t* e = tr + (size_t)tn * 8;
         e[0] = (uint32_t)task.x | ((uint32_t)l << 8) | ((uint32_t)(task.y & 0xffff) << 16);
         e[1] = t_begin;
-        e[2] = *s.tclk;
-        e[3] = t_end;
+#pragma unroll
+        for (int i = 1; i < 6; ++i) e[1 + i] = s.tclk[i];
+        e[7] = t_end;
         ++tn;
       }
     }
@@ -1021,21 +1156,30 @@ __device__ __forceinline__ int sub_count(int tiles, int grid, int x) {
   return (tiles / grid) * below(grid) + below(tiles % grid);
 }
 
+// Arm an event whose `tiles` notifying tasks run on workgroups t % grid and
+// notify sub-counter (t % grid) % kSubs; [0] stays at zero.
 __device__ __forceinline__ void arm_tiles(int* ev, int tiles, int grid) {
-  int top = 0;
-  for (int x = 0; x < kSubs; ++x) {
-    const int cnt = sub_count(tiles, grid, x);
-    ev[(1 + x) * kCtr] = cnt;
-    top += cnt > 0;
-  }
-  ev[0] = top;
+  ev[0] = 0;
+  for (int x = 0; x < kSubs; ++x) ev[(1 + x) * kCtr] = sub_count(tiles, grid, x);
+}
+
+// Arm an event with n notifiers indexed i that notify sub-counter i % kSubs.
+__device__ __forceinline__ void arm_indexed(int* ev, int n) {
+  ev[0] = 0;
+  for (int x = 0; x < kSubs; ++x) ev[(1 + x) * kCtr] = n > x ? (n - x + kSubs - 1) / kSubs : 0;
+}
+
+// Arm an event on counter [0] alone.
+__device__ __forceinline__ void arm_flat(int* ev, int n) {
+  ev[0] = n;
+  for (int x = 0; x < kSubs; ++x) ev[(1 + x) * kCtr] = 0;
 }
 
 __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   const Dims& dm = a.dm;
   const int tid = threadIdx.x, B = a.batch, G = dm.grid;
   __shared__ int bad;
-  __shared__ int total_attn;
+  __shared__ int total_attn, merge_s;
   __shared__ int cb[kMaxBatchAll + 1];
   StepArgs* copy = reinterpret_cast<StepArgs*>(a.ws.args);
   if (tid == 0) {
@@ -1061,15 +1205,32 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   }
   if (tid == 0) {
     a.ws.err[16] = 0;   // abort flag
-    // attention chunk: the largest of 256/128/64 positions that still gives
-    // every workgroup a task (small latency-bound batches get small chunks)
-    int ck = kMaxChunk;
-    while (ck > kMinChunk) {
-      long tasks = 0;
-      for (int b = 0; b < B; ++b) tasks += (a.seq_lens[b] + ck) / ck;
-      if (tasks * dm.Hkv >= G) break;
-      ck >>= 1;
+    // attention chunk. Small batches whose O-projection inputs fit one
+    // merging pass (see stage_attn_merge) take the smallest chunk that keeps
+    // every request within 8 chunks and let the O-projection merge the
+    // partials; otherwise the largest of 256/128/64 positions that still gives
+    // every workgroup a task, with the last chunk of a request merging.
+    int ck = kMaxChunk, merge = 0;
+    auto max_nc = [&](int c) {
+      int mx = 0;
+      for (int b = 0; b < B; ++b) mx = max(mx, (a.seq_lens[b] + c) / c);
+      return mx;
+    };
+    if (B * dm.Hq * dm.d <= 2 * kBlock * 4) {
+      int c = kMinChunk;
+      while (c < kMaxChunk && max_nc(c) > 8) c <<= 1;
+      if (max_nc(c) <= 8) { ck = c; merge = 1; }
     }
+    if (!merge) {
+      while (ck > kMinChunk) {
+        long tasks = 0;
+        for (int b = 0; b < B; ++b) tasks += (a.seq_lens[b] + ck) / ck;
+        if (tasks * dm.Hkv >= G) break;
+        ck >>= 1;
+      }
+    }
+    copy->attn_merge_o = merge;
+    merge_s = merge;
     int acc = 0;
     for (int b = 0; b < B; ++b) {
       cb[b] = acc;
@@ -1098,7 +1259,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
         if (dm.Hkv * cb[mid] <= i) lo = mid; else hi = mid;
       }
       const int r = i - dm.Hkv * cb[lo], nc = cb[lo + 1] - cb[lo];
-      push(make_int4(T_ATTN, lo, r / nc, r % nc));
+      push(make_int4(T_ATTN | (i << 8), lo, r / nc, r % nc));
     }
     for (int t = w; t < dm.o_tiles; t += G) push(make_int4(T_O, t, 0, 0));
     if (!dm.moe) {
@@ -1120,14 +1281,15 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     int* ev = a.ws.ev + (size_t)idx * kEvInts;
     switch (e) {
       case EV_QKV: arm_tiles(ev, dm.qkv_tiles, G); break;
-      case EV_ATTN: ev[0] = B * dm.Hkv; break;
+      // one notifier per chunk task (partials merged by the O-projection), or per (request, KV head)
+      case EV_ATTN: arm_indexed(ev, merge_s ? total_attn : B * dm.Hkv); break;
       case EV_O: arm_tiles(ev, dm.o_tiles, G); break;
       case EV_GU: arm_tiles(ev, dm.moe ? 0 : dm.gu_tiles, G); break;
       case EV_DOWN: arm_tiles(ev, dm.moe ? G : dm.down_tiles, G); break;   // MoE: one combine slot per workgroup
       case EV_ROUTER: arm_tiles(ev, router_tasks, G); break;
-      case EV_ROUTE: ev[0] = dm.moe ? 1 : 0; break;
+      case EV_ROUTE: arm_flat(ev, dm.moe ? 1 : 0); break;
       case EV_MDOWN: arm_tiles(ev, dm.moe ? G : 0, G); break;
-      default: ev[0] = 0; break;
+      default: arm_flat(ev, 0); break;
     }
   }
   for (int idx = tid; idx < dm.L * B * dm.Hkv; idx += blockDim.x) {

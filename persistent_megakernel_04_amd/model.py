@@ -98,7 +98,7 @@ class DecodeModel:
         return ms.value, n.value
 
     def trace_attach(self, buf, entries_per_wg: int = 0):
-        """Attach a device uint32/int32 tensor of grid * entries_per_wg * 4 elements as the task trace
+        """Attach a device uint32/int32 tensor of grid * entries_per_wg * 8 elements as the task trace
         (None detaches)."""
         _abi.check(self.lib.pmk_trace_attach(self.handle, _ptr(buf), int(entries_per_wg)), "pmk_trace_attach")
         self._trace = buf
