@@ -178,6 +178,9 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     };
     parts.insert(parts.end(), mp.begin(), mp.end());
   }
+  // step intermediates are addressed with 32-bit byte offsets from one buffer base
+  for (auto& p : parts)
+    if (p.bytes >= ((size_t)1 << 31)) { delete h; return PMK_ERR_ARG; }
   size_t total = 0;
   for (auto& p : parts) total += align256(p.bytes);
   void* base = nullptr;

@@ -35,10 +35,26 @@ __device__ __forceinline__ int ldci(const int* p) {
 __device__ __forceinline__ void stci(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Device-coherent load of a value that is the same for the whole wave (one
+// address), kept in a scalar register: the compiler cannot tell that an
+// atomic load's result is uniform, and addresses built from it would need a
+// loop over lanes.
+__device__ __forceinline__ int ldsu(const int* p) { return __builtin_amdgcn_readfirstlane(ldci(p)); }
+// Plain load of a wave-uniform int through a generic pointer, kept scalar.
+__device__ __forceinline__ int ldu(const int* p) { return __builtin_amdgcn_readfirstlane(*p); }
+__device__ __forceinline__ int4 ldu4(const int4* p) {
+  const int4 v = *p;
+  return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                   __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+}
 __device__ __forceinline__ int atomic_add_relaxed(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Buffer resource for device-coherent 16-byte accesses. `base` must be
+// wave-uniform (per-lane differences go into the byte offset): a varying base
+// compiles to a loop over the distinct values that also waits for every
+// memory operation in flight.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
@@ -64,6 +80,11 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
 // (stores acknowledged by the coherence point).
 __device__ __forceinline__ void vm_drain() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// This thread's wave within the workgroup, as a wave-uniform (scalar) value:
+// derived from threadIdx.x the compiler would treat it as varying per lane,
+// and every address built from it would be too.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 __device__ __forceinline__ unsigned long long now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
 
 // ---------------------------------------------------------------------------
@@ -83,6 +104,15 @@ __device__ __forceinline__ void wg_notify(int* ev, int sub) {
   vm_drain();
   __syncthreads();
   if (threadIdx.x == 0) (void)__hip_atomic_fetch_add(ev_slot(ev, sub), -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One wave: publish this wave's completed stores, then notify. Used where that
+// wave alone stored what the event covers; the other waves of the workgroup
+// keep their own loads in flight.
+__device__ __forceinline__ void wave_notify(int* ev, int sub) {
+  vm_drain();
+  if ((threadIdx.x & 63) == 0)
+    (void)__hip_atomic_fetch_add(ev_slot(ev, sub), -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wave 0 only: spin until the event's counters are all zero (`subs` = number
@@ -122,7 +152,7 @@ __device__ __forceinline__ bool wg_wait(const int* ev, int subs, int* err, unsig
     if (threadIdx.x == 0) *flag = ok ? 1 : 0;
   }
   __syncthreads();
-  return *flag != 0;
+  return __builtin_amdgcn_readfirstlane(*flag) != 0;   // same for every lane: keep it scalar
 }
 
 // ---------------------------------------------------------------------------

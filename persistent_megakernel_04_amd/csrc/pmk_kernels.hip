@@ -74,9 +74,15 @@ __device__ __forceinline__ size_t kv_off(const Dims& dm, int l, int which, int b
   return (((((size_t)l * 2 + which) * dm.max_batch + b) * dm.Hkv + g) * (size_t)dm.max_seq + pos) * dm.d;
 }
 
-// Wait on an event (its [0] and kSubs sub-counters) or, with subs = 0, on a bare counter.
+// Wait on an event (its [0] and kSubs sub-counters) or, with subs = 0, on a
+// bare counter. Always a workgroup barrier, also with no event: every task
+// begins with one before it writes LDS, since wave 0 may still be reading the
+// previous GEMV pass's results in LDS when the other waves start the task.
 __device__ __forceinline__ bool ctx_wait(const Ctx& c, const int* ev, int subs = kSubs) {
-  if (!ev) return true;
+  if (!ev) {
+    __syncthreads();
+    return true;
+  }
   const bool ok = wg_wait(ev, subs, c.a.ws.err, c.a.watchdog_ticks, c.s.flag);
   if (threadIdx.x == 0) c.s.tclk[1] = (uint32_t)now_ticks();
   return ok;
@@ -140,8 +146,9 @@ template <typename WT, bool SPLIT>
 __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int Kp, int XS, const Lds& s) {
   typedef typename MM<WT>::XT XT;
   XT* xs = reinterpret_cast<XT*>(s.xs);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int BPR = (Kp + 255) >> 8, NBK = nb * BPR;
+  const auto src = rsrc(in.src);
   if (lane == 0)
     for (int m = 0; m < nb; ++m) s.ssp[m * kWaves + wave] = 0.f;
   for (int base = wave; base < NBK; base += kWaves * 8) {
@@ -154,7 +161,7 @@ __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int 
         const int m = blk / BPR, k = (blk - m * BPR) * 256 + lane * 4;
         if (k < K) {
           const int srow = in.gather ? ldci(in.gather + m) : m;
-          v[u] = ldc4(rsrc(in.src + (size_t)srow * in.ld), k * 4);
+          v[u] = ldc4(src, (srow * in.ld + k) * 4);
         }
       }
     }
@@ -202,6 +209,7 @@ __device__ __forceinline__ void stage_attn_merge(const StepArgs& a, const GemvIn
   const Dims& dm = a.dm;
   const int d = dm.d, G = dm.Hq / dm.Hkv, DP = d + 4, ck = a.attn_chunk;
   const int K4 = Kp / 4;   // 4-element units per row (K = Hq d, a multiple of 4; zero beyond K)
+  const auto pr = rsrc(a.ws.part);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int unit = threadIdx.x + u * kBlock;
@@ -211,13 +219,13 @@ __device__ __forceinline__ void stage_attn_merge(const StepArgs& a, const GemvIn
     if (k < K) {
       const int b = in.merge_b0 + m, nc = (a.seq_lens[b] + ck) / ck;
       const int h = k / d, e = k - h * d, g = h / G, hh = h - g * G;
-      const float* base = a.ws.part + ((size_t)b * dm.Hkv + g) * dm.max_chunks * G * DP + hh * DP;
+      const int base = ((b * dm.Hkv + g) * dm.max_chunks * G + hh) * DP;   // floats; part is < 2 GiB
       f4v av[8], mv[8];
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        const auto r = rsrc(base + (size_t)min(cc, nc - 1) * G * DP);
-        av[cc] = ldc4(r, e * 4);
-        mv[cc] = ldc4(r, d * 4);
+        const int o = (base + min(cc, nc - 1) * G * DP) * 4;
+        av[cc] = ldc4(pr, o + e * 4);
+        mv[cc] = ldc4(pr, o + d * 4);
       }
       float M = -INFINITY, L = 0.f;
 #pragma unroll
@@ -276,35 +284,82 @@ __device__ __forceinline__ WaveItems wave_items(int RG, int NKS, int wave) {
   return it;
 }
 
+// A wave's weight stream for one GEMV pass, as far as another pass needs it
+// to prefetch: the row of this lane in the wave's first item and the item's
+// k range. `on` is false when the wave has no item in that pass.
+constexpr int kRing = 16;   // loads in flight per wave (16 KiB; 128 KiB per workgroup)
+
+template <typename WT>
+struct Stream {
+  const WT* rows;
+  int ks_lo, kmax, nks_c, on;
+};
+
+template <typename WT>
+__device__ __forceinline__ int stream_ofs(const Stream<WT>& st, int ks) {
+  return min((st.ks_lo + ks) * MM<WT>::KSTEP + (int)((threadIdx.x & 63) >> 4) * MM<WT>::EPL, st.kmax);
+}
+
+template <typename WT>
+__device__ __forceinline__ Stream<WT> stream_of(const GemvRows& rw, int R, int K, int wave) {
+  typedef MM<WT> T;
+  const int NKS = (K + T::KSTEP - 1) / T::KSTEP, RG = (R + 15) >> 4;
+  const WaveItems wi = wave_items(RG, NKS, wave);
+  Stream<WT> st;
+  st.on = wi.n > 0;
+  st.rows = row_ptr<WT>(rw, min(min(wi.rg0, RG - 1) * 16 + (int)(threadIdx.x & 15), R - 1), K);
+  st.ks_lo = wi.ks_lo;
+  st.kmax = K - T::EPL;
+  st.nks_c = wi.nks > 0 ? wi.nks - 1 : 0;
+  return st;
+}
+
+template <typename WT>
+__device__ __forceinline__ Stream<WT> no_stream() {
+  Stream<WT> st;
+  st.rows = nullptr;
+  st.ks_lo = st.kmax = st.nks_c = st.on = 0;
+  return st;
+}
+
 // Returns false if the wait was abandoned (nothing was computed). SP: the
 // input rows are carried as bfloat16 hi + lo pairs, two MFMAs per chunk.
+//
+// Ring flow across passes: `pre` says whether this wave's ring already holds
+// the first kRing steps of this pass (issued by the previous pass's last
+// steps); on return it says whether the ring now holds those of `nx`, the
+// pass that follows. So a wave's weight loads run on from one pass into the
+// next without draining while the pass's results are stored and the next
+// input event is awaited. Every item is streamed as a whole number of ring
+// lengths (steps past its end multiply a zero input and re-read its last
+// step), which keeps the slot of a step fixed.
 template <typename WT, bool SP>
 __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
-                                     const int* wait_ev, int wait_subs) {
+                                     const int* wait_ev, int wait_subs, uint4 (&ring)[kRing], bool& pre,
+                                     const Stream<WT>& nx) {
   typedef MM<WT> T;
   typedef typename T::XT XT;
-  constexpr int D = 16;   // loads in flight per wave (16 KiB; 128 KiB per workgroup)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, mrow = lane & 15;
+  constexpr int D = kRing;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), grp = lane >> 4, mrow = lane & 15;
   const int NKS = (K + T::KSTEP - 1) / T::KSTEP, RG = (R + 15) >> 4;
   const int Kp = NKS * T::KSTEP, XS = Kp + T::XPAD;
   const int kmax = K - T::EPL, kg = grp * T::EPL;
   const WaveItems wi = wave_items(RG, NKS, wave);
   const int nks = wi.nks, nks_c = nks > 0 ? nks - 1 : 0;
-  // consecutive items stream without a bubble when an item is a whole number of rings
-  const bool chain = nks % D == 0;
+  const int nks_pad = nks > D ? (nks + D - 1) / D * D : D;
   auto item_rows = [&](int it) -> const WT* {
     const int rg = min(wi.rg0 + min(it, max(wi.n - 1, 0)) * wi.rg_step, RG - 1);
     return row_ptr<WT>(rw, min(rg * 16 + mrow, R - 1), K);   // padded rows repeat a valid row
   };
   auto kofs = [&](int ks) { return min((wi.ks_lo + ks) * T::KSTEP + kg, kmax); };
 
-  uint4 ring[D];
   const WT* cur = item_rows(0);
   const WT* nxt = item_rows(1);
-  if (wi.n > 0) {
+  if (!pre && wi.n > 0) {
 #pragma unroll
     for (int d = 0; d < D; ++d) ring[d] = ldg16(cur + kofs(min(d, nks_c)));
   }
+  pre = nx.on && wi.n > 0;
   if (!ctx_wait(c, wait_ev, wait_subs)) return false;
   if (in.merge_b0 >= 0)
     stage_attn_merge<WT, SP>(c.a, in, nb, K, Kp, XS, c.s);
@@ -317,19 +372,14 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
   const bool xon = mrow < nb;
   const int KSPL = k_split(RG);
   for (int it = 0; it < wi.n; ++it) {
-    if (it > 0 && !chain) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) ring[d] = ldg16(cur + kofs(min(d, nks_c)));
-    }
-    const bool has_next = chain && it + 1 < wi.n;
+    const bool has_next = it + 1 < wi.n;
     f4v acc = {0.f, 0.f, 0.f, 0.f};
     // the input fragments of the next k-step are read from LDS one step ahead
     uint4 xa_n = *reinterpret_cast<const uint4*>(xrow), xl_n = make_uint4(0, 0, 0, 0);
     if (SP) xl_n = *reinterpret_cast<const uint4*>(xrow + XS);
     // Branch-free body, so the compiler's wait counts stay exact (a branch
-    // here makes it wait for every load in flight before each MFMA): steps
-    // past the item multiply a zero input.
-    for (int ks0 = 0; ks0 < nks; ks0 += D) {
+    // here makes it wait for every load in flight before each MFMA).
+    for (int ks0 = 0; ks0 < nks_pad; ks0 += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int ks = ks0 + d;
@@ -350,12 +400,15 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
           xl.w = on ? xl.w : 0u;
           acc = T::mac(xl, ring[d], acc);
         }
-        // refill: k-step ks + D of this item, else the next item's first steps
-        const int nk = ks + D;
-        const bool here = nk < nks;
-        const WT* bp = (here || !has_next) ? cur : nxt;
-        const int kk = here ? nk : (has_next ? nk - nks : nks_c);
-        ring[d] = ldg16(bp + kofs(kk));
+        // refill with the step kRing ahead: of this item, else of the next
+        // item, else of the next pass (else a re-read of the last step)
+        const int nk = ks + D, nn = nk - nks_pad;
+        const bool here = nk < nks_pad, into_item = !here && has_next, into_pass = !here && !has_next && nx.on;
+        const WT* bp = into_item ? nxt : (into_pass ? nx.rows : cur);
+        const int off = here ? kofs(min(nk, nks_c))
+                             : (into_item ? kofs(min(nn, nks_c)) : (into_pass ? stream_ofs(nx, min(nn, nx.nks_c))
+                                                                               : kofs(nks_c)));
+        ring[d] = ldg16(bp + off);
         // keep the refill here: left to itself the scheduler sinks all refills
         // to the end of the unrolled body, and the ring degrades to batches
         // that drain to zero loads in flight
@@ -399,8 +452,9 @@ template <typename WT> struct SplitIn { static constexpr bool value = sizeof(WT)
 
 template <typename WT>
 __device__ __forceinline__ bool gemv_any(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
-                                         const int* wev, int wsubs) {
-  return gemv<WT, SplitIn<WT>::value>(c, rw, R, K, in, nb, wev, wsubs);
+                                         const int* wev, int wsubs, uint4 (&ring)[kRing], bool& pre,
+                                         const Stream<WT>& nx) {
+  return gemv<WT, SplitIn<WT>::value>(c, rw, R, K, in, nb, wev, wsubs, ring, pre, nx);
 }
 
 // Input rows per GEMV pass for depth K and R output rows: what the LDS input
@@ -503,29 +557,29 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
     }
     case T_MGU: {   // grouped gate/up task i = (row tile i / sg, Fe slice i % sg) of this workgroup's share
       const int i = c.wg + p * dm.grid;
-      if (i >= ldci(a.ws.moe_info + 0)) return false;
-      const int sg = ldci(a.ws.moe_info + 2), t = i / sg, sl = i - t * sg;
-      const int e = ldci(a.ws.tile_info + 2 * t), row0 = ldci(a.ws.tile_info + 2 * t + 1);
+      if (i >= ldsu(a.ws.moe_info + 0)) return false;
+      const int sg = ldsu(a.ws.moe_info + 2), t = i / sg, sl = i - t * sg;
+      const int e = ldsu(a.ws.tile_info + 2 * t), row0 = ldsu(a.ws.tile_info + 2 * t + 1);
       const int f0 = (int)((long)sl * dm.Fe / sg), Rh = (int)((long)(sl + 1) * dm.Fe / sg) - f0;
       const size_t eo = (size_t)e * dm.Fe * dm.H;
       ps.rw = GemvRows{ROWS_PAIR, reinterpret_cast<const WT*>(Lp.w_exp_gate) + eo,
                        reinterpret_cast<const WT*>(Lp.w_exp_up) + eo, f0, Rh};
       // the tile's rows: its routed tokens' FFN inputs (RMSNorm2 of h1), gathered
       ps.in = GemvIn{a.ws.h1, dm.H, a.ws.sorted_tok + row0, Lp.ffn_norm, 1, dm.eps, -1};
-      ps.R = 2 * Rh; ps.K = dm.H; ps.nb = min(kMoeBM, ldci(a.ws.exp_indptr + e + 1) - row0);
+      ps.R = 2 * Rh; ps.K = dm.H; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
       ps.epi = E_MGU; ps.b0 = row0; ps.r0 = f0; ps.n = Rh; ps.e = e;
       return true;
     }
     case T_MDOWN: {  // grouped down task i = (row tile i / sd, H slice i % sd); waits on its expert's counter
       const int i = c.wg + p * dm.grid;
-      if (i >= ldci(a.ws.moe_info + 1)) return false;
-      const int sd = ldci(a.ws.moe_info + 3), t = i / sd, sl = i - t * sd;
-      const int e = ldci(a.ws.tile_info + 2 * t), row0 = ldci(a.ws.tile_info + 2 * t + 1);
+      if (i >= ldsu(a.ws.moe_info + 1)) return false;
+      const int sd = ldsu(a.ws.moe_info + 3), t = i / sd, sl = i - t * sd;
+      const int e = ldsu(a.ws.tile_info + 2 * t), row0 = ldsu(a.ws.tile_info + 2 * t + 1);
       const int h0 = (int)((long)sl * dm.H / sd), R = (int)((long)(sl + 1) * dm.H / sd) - h0;
       ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(Lp.w_exp_down) + (size_t)e * dm.H * dm.Fe, nullptr, h0,
                        0};
       ps.in = GemvIn{a.ws.mact + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f, -1};
-      ps.R = R; ps.K = dm.Fe; ps.nb = min(kMoeBM, ldci(a.ws.exp_indptr + e + 1) - row0);
+      ps.R = R; ps.K = dm.Fe; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
       ps.wev = a.ws.ectr + ((size_t)c.l * dm.E + e) * kCtr;
       ps.wsubs = 0;
       ps.epi = E_MDOWN; ps.b0 = row0; ps.r0 = h0; ps.n = R; ps.e = e;
@@ -536,7 +590,10 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
 }
 
 // The residual an O / down pass adds (hidden, resp. h1): thread t holds
-// elements t, t + kBlock, ... of the [R][nb] tile (R nb <= kYsFloats).
+// elements t, t + kBlock, ... of the [R][nb] tile (R nb <= kYsFloats). It is
+// final once this workgroup has seen the event that produced it, so it is
+// loaded before the pass's weights are waited on, and added into ys by the
+// whole workgroup once the pass's sums are there.
 constexpr int kResid = kYsFloats / kBlock;
 __device__ __forceinline__ const float* resid_src(const StepArgs& a, const Pass& ps) {
   return ps.epi == E_O ? a.hidden : a.ws.h1;
@@ -552,19 +609,28 @@ __device__ __forceinline__ void load_resid(const StepArgs& a, const Pass& ps, fl
     }
   }
 }
+__device__ __forceinline__ void add_resid(const Lds& s, const Pass& ps, const float (&r)[kResid]) {
+#pragma unroll
+  for (int k = 0; k < kResid; ++k) {
+    const int idx = threadIdx.x + k * kBlock;
+    if (idx < ps.n * ps.nb) s.ys[idx] += r[k];   // ys is [R][nb]: idx = j nb + m
+  }
+  __syncthreads();
+}
 
-// Consume a pass's result (ys[j][m], rstd[m] in LDS) and store its outputs.
-// `resid` holds the O / down residual when it was loaded ahead (have_resid).
+// Wave 0 alone consumes a pass's result (ys[j][m], rstd[m] in LDS) and stores
+// its outputs, while the other waves go on streaming the next pass's weights.
+// `have_resid`: the O / down residual is already in ys.
 template <typename WT>
-__device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, float (&resid)[kResid], bool have_resid) {
+__device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have_resid) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
-  const int nb = ps.nb, b0 = ps.b0;
+  const int nb = ps.nb, b0 = ps.b0, lane = threadIdx.x & 63;
   const float* ys = c.s.ys;
   switch (ps.epi) {
     case E_QKV: {   // RoPE at each request's position, then q/k/v out and the K/V append
       const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
-      for (int idx = threadIdx.x; idx < ps.n * nb; idx += kBlock) {
+      for (int idx = lane; idx < ps.n * nb; idx += 64) {
         const int ju = idx / nb, m = idx - ju * nb;
         const int unit = ps.r0 + ju, h = unit / half, i = unit - h * half;
         const float r = c.s.rstd[m];
@@ -590,15 +656,12 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, float (&r
     }
     case E_O:       // h1 = x + W_o o
     case E_DOWN: {  // x' = h1 + W_down act (the layer output, into hidden)
-      if (!have_resid) load_resid(a, ps, resid);
+      const float* res = resid_src(a, ps);
       float* out = ps.epi == E_O ? a.ws.h1 : a.hidden;
-#pragma unroll
-      for (int k = 0; k < kResid; ++k) {
-        const int idx = threadIdx.x + k * kBlock;
-        if (idx < ps.n * nb) {
-          const int j = idx / nb, m = idx - j * nb;
-          stc(out + (size_t)(b0 + m) * dm.H + ps.r0 + j, resid[k] + ys[j * nb + m]);
-        }
+      for (int idx = lane; idx < ps.n * nb; idx += 64) {
+        const int j = idx / nb, m = idx - j * nb;
+        const size_t o = (size_t)(b0 + m) * dm.H + ps.r0 + j;
+        stc(out + o, (have_resid ? 0.f : ldc(res + o)) + ys[idx]);
       }
       break;
     }
@@ -607,27 +670,25 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, float (&r
       const int Rh = ps.n;
       float* out = ps.epi == E_GU ? a.ws.act : a.ws.mact;
       const int ld = ps.epi == E_GU ? dm.F : dm.Fe;
-      for (int idx = threadIdx.x; idx < Rh * nb; idx += kBlock) {
+      for (int idx = lane; idx < Rh * nb; idx += 64) {
         const int j = idx / nb, m = idx - j * nb;
         const float r = c.s.rstd[m];
         const float gt = ys[j * nb + m] * r, up = ys[(Rh + j) * nb + m] * r;
         stc(out + (size_t)(b0 + m) * ld + ps.r0 + j, gt / (1.0f + __expf(-gt)) * up);
       }
-      if (ps.epi == E_MGU) {   // this task of expert e is done
-        wg_notify(a.ws.ectr + ((size_t)c.l * dm.E + ps.e) * kCtr, -1);
-        return;
-      }
+      if (ps.epi == E_MGU)   // this task of expert e is done
+        wave_notify(a.ws.ectr + ((size_t)c.l * dm.E + ps.e) * kCtr, -1);
       break;
     }
     case E_ROUTER: {
-      for (int idx = threadIdx.x; idx < ps.n * nb; idx += kBlock) {
+      for (int idx = lane; idx < ps.n * nb; idx += 64) {
         const int j = idx / nb, m = idx - j * nb;
         stc(a.ws.logits + (size_t)(b0 + m) * dm.E + ps.r0 + j, ys[j * nb + m] * c.s.rstd[m]);
       }
       break;
     }
     case E_MDOWN: {
-      for (int idx = threadIdx.x; idx < ps.n * nb; idx += kBlock) {
+      for (int idx = lane; idx < ps.n * nb; idx += 64) {
         const int j = idx / nb, m = idx - j * nb;
         stc(a.ws.mout + (size_t)(b0 + m) * dm.H + ps.r0 + j, ys[j * nb + m]);
       }
@@ -635,7 +696,6 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, float (&r
     }
     default: break;
   }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -659,15 +719,14 @@ template <> __device__ __forceinline__ void unpack_row<float>(const uint4 r, flo
   f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y); f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
 }
 // Device-coherent float row slice -> cache-dtype bits (rounded like the KV append).
-template <typename KT> __device__ __forceinline__ uint4 pack_row(const float* p);
-template <> __device__ __forceinline__ uint4 pack_row<uint16_t>(const float* p) {
-  const auto r = rsrc(p);
-  const f4v a = ldc4(r, 0), b = ldc4(r, 16);
+template <typename KT> __device__ __forceinline__ uint4 pack_row(__amdgpu_buffer_rsrc_t r, int off);
+template <> __device__ __forceinline__ uint4 pack_row<uint16_t>(__amdgpu_buffer_rsrc_t r, int off) {
+  const f4v a = ldc4(r, off), b = ldc4(r, off + 16);
   return make_uint4((uint32_t)f2bf(a.x) | ((uint32_t)f2bf(a.y) << 16), (uint32_t)f2bf(a.z) | ((uint32_t)f2bf(a.w) << 16),
                     (uint32_t)f2bf(b.x) | ((uint32_t)f2bf(b.y) << 16), (uint32_t)f2bf(b.z) | ((uint32_t)f2bf(b.w) << 16));
 }
-template <> __device__ __forceinline__ uint4 pack_row<float>(const float* p) {
-  const f4v a = ldc4(rsrc(p), 0);
+template <> __device__ __forceinline__ uint4 pack_row<float>(__amdgpu_buffer_rsrc_t r, int off) {
+  const f4v a = ldc4(r, off);
   return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
 }
 
@@ -678,11 +737,11 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
   constexpr int EPL = 16 / (int)sizeof(KT);   // elements per lane (16 B)
   constexpr int D = 16 * EPL;                 // head_dim: 128 (bf16) or 64 (f32)
   constexpr int DP = D + 4;                   // partial record: acc[D], max, sum, pad
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, rs = lane >> 4, li = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), rs = lane >> 4, li = lane & 15;
   const int G = dm.Hq / dm.Hkv;               // query heads of the group, a multiple of HB
   const int ck = ITS * 32;
   const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * D;
-  const int S = a.seq_lens[b], n = S + 1;
+  const int S = ldu(a.seq_lens + b), n = S + 1;
   const int p0 = ci * ck, p1 = min(n, p0 + ck);
   const int nc = (n + ck - 1) / ck;
 
@@ -704,8 +763,9 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
   for (int t = tid; t < G * D / 4; t += kBlock) *reinterpret_cast<f4v*>(qs + 4 * t) = ldc4(rsrc(qrow), 16 * t);
   uint4 kn = make_uint4(0, 0, 0, 0), vn = kn;
   if (S >= p0 && S < p1) {
-    kn = pack_row<KT>(a.ws.qkv + (size_t)b * qkv_dim + (size_t)(dm.Hq + g) * D + li * EPL);
-    vn = pack_row<KT>(a.ws.qkv + (size_t)b * qkv_dim + (size_t)(dm.Hq + dm.Hkv + g) * D + li * EPL);
+    const auto qr = rsrc(a.ws.qkv + (size_t)b * qkv_dim);
+    kn = pack_row<KT>(qr, ((dm.Hq + g) * D + li * EPL) * 4);
+    vn = pack_row<KT>(qr, ((dm.Hq + dm.Hkv + g) * D + li * EPL) * 4);
   }
   __syncthreads();
   if (tid == 0) c.s.tclk[2] = (uint32_t)now_ticks();
@@ -771,6 +831,7 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
   // combine the 8 waves: this chunk's partial (or the output for a single chunk)
   float* o = a.ws.o + (size_t)b * dm.Hq * D + (size_t)g * G * D;
   float* part = a.ws.part + (((size_t)b * dm.Hkv + g) * dm.max_chunks + ci) * G * DP;
+  const auto orr = rsrc(o), prr = rsrc(part);
   for (int t = tid; t < G * D / 4; t += kBlock) {
     const int h = t / (D / 4), e0 = (t - h * (D / 4)) * 4;
     float M = -INFINITY;
@@ -786,11 +847,10 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
       A += *reinterpret_cast<const f4v*>(sp + e0) * f;
     }
     if (nc == 1 && !a.attn_merge_o) {
-      stc4(rsrc(o + h * D), e0 * 4, A / Ls);
+      stc4(orr, (h * D + e0) * 4, A / Ls);
     } else {
-      const auto r = rsrc(part + h * DP);
-      stc4(r, e0 * 4, A);
-      if (e0 == 0) stc4(r, D * 4, f4v{M, Ls, 0.f, 0.f});
+      stc4(prr, (h * DP + e0) * 4, A);
+      if (e0 == 0) stc4(prr, (h * DP + D) * 4, f4v{M, Ls, 0.f, 0.f});
     }
   }
   if (a.attn_merge_o) {   // the O-projection merges the partials as it stages its inputs
@@ -810,8 +870,8 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
   }
   __syncthreads();
   if (tid == 0) c.s.tclk[4] = (uint32_t)now_ticks();
-  if (*c.s.flag) {
-    const float* pb = a.ws.part + ((size_t)b * dm.Hkv + g) * dm.max_chunks * G * DP;
+  if (__builtin_amdgcn_readfirstlane(*c.s.flag)) {
+    const auto pbr = rsrc(a.ws.part + ((size_t)b * dm.Hkv + g) * dm.max_chunks * G * DP);
     for (int t = tid; t < G * D / 4; t += kBlock) {
       const int h = t / (D / 4), e0 = (t - h * (D / 4)) * 4;
       float M = -INFINITY, Ls = 0.f;
@@ -821,9 +881,9 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const int cc = min(c0 + u, nc - 1);
-          const auto r = rsrc(pb + ((size_t)cc * G + h) * DP);
-          as[u] = ldc4(r, e0 * 4);
-          ms[u] = ldc4(r, D * 4);
+          const int ro = ((cc * G + h) * DP) * 4;
+          as[u] = ldc4(pbr, ro + e0 * 4);
+          ms[u] = ldc4(pbr, ro + D * 4);
         }
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
@@ -836,7 +896,7 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
           }
         }
       }
-      stc4(rsrc(o + h * D), e0 * 4, A / Ls);
+      stc4(orr, (h * D + e0) * 4, A / Ls);
     }
     wg_notify(ev_ptr(a, c.l, EV_ATTN), (b * dm.Hkv + g) & (kSubs - 1));
   }
@@ -848,7 +908,8 @@ template <typename KT, int HB>
 __device__ __forceinline__ bool attn_its(const Ctx& c, int b, int g, int ci, int tix, int ck, const int* wev) {
   if (ck <= 64) return task_attn<KT, HB, 2>(c, b, g, ci, tix, wev);
   if (ck <= 128) return task_attn<KT, HB, 4>(c, b, g, ci, tix, wev);
-  return task_attn<KT, HB, 8>(c, b, g, ci, tix, wev);
+  // 256-position chunks hold 16 KV rows per lane: two query heads at a time keep them in registers
+  return task_attn<KT, (HB > 2 ? 2 : HB), 8>(c, b, g, ci, tix, wev);
 }
 
 template <typename KT>
@@ -887,7 +948,7 @@ __device__ __forceinline__ bool task_route(const Ctx& c, const int* wev) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   if (!ctx_wait(c, wev)) return false;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int T = a.batch, E = dm.E, k = dm.k, Tk = T * k, G = dm.grid;
   int* sidx = reinterpret_cast<int*>(c.s.xs);   // [T k]
   int* cnt = sidx + dm.max_batch * kMaxTopK;     // [E]
@@ -1036,13 +1097,14 @@ __device__ __forceinline__ bool task_combine(const Ctx& c, const int* wev) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   if (!ctx_wait(c, wev)) return false;
+  const auto mo = rsrc(a.ws.mout);   // routed rows: T k H floats, < 2 GiB
   for (int t = c.wg; t < a.batch; t += dm.grid) {
     for (int i = threadIdx.x; i < dm.H / 4; i += kBlock) {
       f4v x = ldc4(rsrc(a.ws.h1 + (size_t)t * dm.H), i * 16);
       for (int j = 0; j < dm.k; ++j) {
         const float w = ldc(a.ws.topk_w + t * dm.k + j);
         const int p = ldci(a.ws.pos_of + t * dm.k + j);
-        x += ldc4(rsrc(a.ws.mout + (size_t)p * dm.H), i * 16) * w;
+        x += ldc4(mo, (p * dm.H) * 4 + i * 16) * w;
       }
       stc4(rsrc(a.hidden + (size_t)t * dm.H), i * 16, x);
     }
@@ -1053,92 +1115,176 @@ __device__ __forceinline__ bool task_combine(const Ctx& c, const int* wev) {
 // ---------------------------------------------------------------------------
 // The persistent kernel
 // ---------------------------------------------------------------------------
+// GEMV task types whose passes can be built ahead of time: their weights do
+// not depend on this step's data, except the grouped expert tasks, whose rows
+// are known once routing is done.
+__device__ __forceinline__ bool gemv_task(int type) {
+  return type == T_QKV || type == T_O || type == T_GU || type == T_DOWN || type == T_ROUTER || type == T_MGU ||
+         type == T_MDOWN;
+}
+__device__ __forceinline__ bool chainable(int type, bool routed) {
+  return type == T_QKV || type == T_O || type == T_GU || type == T_DOWN || type == T_ROUTER ||
+         (routed && (type == T_MGU || type == T_MDOWN));
+}
+
+// This wave's stream of the GEMV pass that runs after pass p of queue entry t
+// (layer l) on this workgroup, when that pass's weights can be named now;
+// else none (the next pass then fills its ring itself).
+template <typename WT>
+__device__ __forceinline__ Stream<WT> next_stream(const StepArgs& a, const Lds& s, int wg, const int4* q, int n, int l,
+                                                  int t, int4 task, int p, bool routed) {
+  const int wave = wave_id();
+  Pass ps;
+  {
+    const Ctx c{a, l, wg, s};
+    if (chainable(task.x, routed) && make_pass<WT>(c, task, p + 1, nullptr, ps))
+      return stream_of<WT>(ps.rw, ps.R, ps.K, wave);
+  }
+  int4 nt;
+  int nl = l;
+  if (t + 1 < n) {
+    nt = ldu4(q + t + 1);
+  } else if (l + 1 < a.dm.L) {
+    nt = ldu4(q);
+    nl = l + 1;
+  } else {
+    return no_stream<WT>();
+  }
+  nt.x &= 0xff;
+  if (!chainable(nt.x, nl == l && routed)) return no_stream<WT>();
+  const Ctx c{a, nl, wg, s};
+  if (!make_pass<WT>(c, nt, 0, nullptr, ps)) return no_stream<WT>();
+  return stream_of<WT>(ps.rw, ps.R, ps.K, wave);
+}
+
 template <typename WT>
 __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict__ pa) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const StepArgs& a = *pa;
   const Dims& dm = a.dm;
-  const int wg = blockIdx.x;
+  const int wg = blockIdx.x, wave = wave_id();
   const Lds s = lds_layout(lds_raw);
   if (threadIdx.x == 0) *s.flag = (ldci(a.ws.err) == 0);
   __syncthreads();
-  if (!*s.flag) return;
-  const int n = a.ws.qlen[wg];
+  if (!__builtin_amdgcn_readfirstlane(*s.flag)) return;
+  const int n = ldu(a.ws.qlen + wg);
   const int4* q = a.ws.queue + (size_t)wg * dm.max_queue;
   uint32_t* tr = a.trace ? a.trace + (size_t)wg * a.trace_cap * 8 : nullptr;
   int tn = 1;
-  for (int l = 0; l < dm.L; ++l) {
-    const Ctx c{a, l, wg, s};
-    unsigned passed = 0;
-    // the event a task type waits on, or nullptr once this workgroup has seen it at zero
-    auto need = [&](int e, int el) -> const int* {
-      const unsigned bit = 1u << (e + (el != l ? 16 : 0));
-      if (passed & bit) return nullptr;
-      passed |= bit;
-      return ev_ptr(a, el, e);
-    };
-    // whether an earlier task of this workgroup already waited on the event
-    auto seen = [&](int e, int el) -> bool { return (passed & (1u << (e + (el != l ? 16 : 0)))) != 0; };
-    for (int t = 0; t < n; ++t) {
-      int4 task = q[t];
+  int l = 0, t = 0;
+  unsigned passed = 0;   // events of layer l (bit e) and l - 1 (bit 16 + e) this workgroup has seen fired
+  // the event a task type waits on, or nullptr once this workgroup has seen it at zero
+  auto need = [&](int e, int el) -> const int* {
+    const unsigned bit = 1u << (e + (el != l ? 16 : 0));
+    if (passed & bit) return nullptr;
+    passed |= bit;
+    return ev_ptr(a, el, e);
+  };
+  // whether an earlier task of this workgroup already waited on the event
+  auto seen = [&](int e, int el) -> bool { return (passed & (1u << (e + (el != l ? 16 : 0)))) != 0; };
+  auto advance = [&]() {
+    if (++t == n) {
+      t = 0;
+      ++l;
+      passed = 0;
+    }
+  };
+  auto record = [&](int type, uint32_t t_begin) {
+    if (tr && threadIdx.x == 0 && tn < a.trace_cap) {
+      const uint32_t t_end = (uint32_t)now_ticks();
+      uint32_t* e = tr + (size_t)tn * 8;
+      e[0] = (uint32_t)type | ((uint32_t)l << 8) | ((uint32_t)(ldu4(q + t).y & 0xffff) << 16);
+      e[1] = t_begin;
+#pragma unroll
+      for (int i = 1; i < 6; ++i) e[1 + i] = s.tclk[i];
+      e[7] = t_end;
+      ++tn;
+    }
+  };
+  auto begin = [&]() -> uint32_t {
+    const uint32_t t0 = (uint32_t)now_ticks();
+    if (tr && threadIdx.x == 0)
+      for (int i = 1; i < 7; ++i) s.tclk[i] = t0;
+    return t0;
+  };
+  if (n > 0) {
+    while (l < dm.L) {
+      int4 task = ldu4(q + t);
       const int tix = task.x >> 8;   // attention tasks: the task's index within the stage
       task.x &= 0xff;
-      const uint32_t t_begin = (uint32_t)now_ticks();
-      if (tr && threadIdx.x == 0)
-        for (int i = 1; i < 7; ++i) s.tclk[i] = t_begin;
-      bool ok = true;
-      int notify = -1;   // event this task notifies through sub-counter (wg % kSubs)
-      switch (task.x) {
-        case T_ATTN:
-          ok = attn_dispatch<WT>(c, task.y, task.z, task.w, tix, need(EV_QKV, l));
-          break;
-        case T_ROUTE:
-          ok = task_route(c, need(EV_ROUTER, l));
-          break;
-        case T_COMBINE:
-          ok = task_combine(c, need(EV_MDOWN, l));
-          notify = EV_DOWN;
-          break;
-        default: {   // GEMV tasks
-          const int* wev = nullptr;
-          switch (task.x) {
-            case T_QKV: wev = l > 0 ? need(EV_DOWN, l - 1) : nullptr; notify = EV_QKV; break;
-            case T_O: wev = need(EV_ATTN, l); notify = EV_O; break;
-            case T_GU: wev = need(EV_O, l); notify = EV_GU; break;
-            case T_DOWN: wev = need(EV_GU, l); notify = EV_DOWN; break;
-            case T_ROUTER: wev = need(EV_O, l); notify = EV_ROUTER; break;
-            case T_MGU:   // the share's size is known once routing is done
-              ok = ctx_wait(c, need(EV_ROUTE, l));
-              break;
-            case T_MDOWN: notify = EV_MDOWN; break;
-            default: break;
-          }
-          for (int p = 0; ok; ++p) {
-            Pass ps;
-            if (!make_pass<WT>(c, task, p, wev, ps)) break;
-            // the residual of O (the layer input) / down (h1) is final once this
-            // workgroup has seen the event that produced it: load it before waiting
-            float resid[kResid];
-            const bool early = (ps.epi == E_O && (l == 0 || seen(EV_DOWN, l - 1))) || (ps.epi == E_DOWN && seen(EV_O, l));
-            if (early) load_resid(a, ps, resid);
-            ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs);
-            if (ok) epilogue<WT>(c, ps, resid, early);
-            if (threadIdx.x == 0) s.tclk[5] = (uint32_t)now_ticks();
-          }
-          break;
+      if (!gemv_task(task.x)) {
+        const Ctx c{a, l, wg, s};
+        const uint32_t t_begin = begin();
+        bool ok = true;
+        switch (task.x) {
+          case T_ATTN:
+            ok = attn_dispatch<WT>(c, task.y, task.z, task.w, tix, need(EV_QKV, l));
+            break;
+          case T_ROUTE:
+            ok = task_route(c, need(EV_ROUTER, l));
+            break;
+          case T_COMBINE:
+            ok = task_combine(c, need(EV_MDOWN, l));
+            if (ok) wg_notify(ev_ptr(a, l, EV_DOWN), wg & (kSubs - 1));
+            break;
+          default: break;
         }
+        if (!ok) return;
+        record(task.x, t_begin);
+        advance();
+        continue;
       }
-      if (ok && notify >= 0) wg_notify(ev_ptr(a, l, notify), wg & (kSubs - 1));
-      if (!ok) return;
-      if (tr && threadIdx.x == 0 && tn < a.trace_cap) {
-        const uint32_t t_end = (uint32_t)now_ticks();
-        uint32_t* e = tr + (size_t)tn * 8;
-        e[0] = (uint32_t)task.x | ((uint32_t)l << 8) | ((uint32_t)(task.y & 0xffff) << 16);
-        e[1] = t_begin;
-#pragma unroll
-        for (int i = 1; i < 6; ++i) e[1 + i] = s.tclk[i];
-        e[7] = t_end;
-        ++tn;
+      // A run of consecutive GEMV tasks (across layers too): each wave's
+      // weight ring is carried from one pass into the next. It exists only
+      // within the run, so it holds no registers during the other tasks.
+      uint4 ring[kRing];
+      bool pre = false;
+      for (;;) {
+        const Ctx c{a, l, wg, s};
+        const uint32_t t_begin = begin();
+        bool ok = true;
+        int notify = -1;   // event this task notifies through sub-counter (wg % kSubs)
+        const int* wev = nullptr;
+        switch (task.x) {
+          case T_QKV: wev = l > 0 ? need(EV_DOWN, l - 1) : nullptr; notify = EV_QKV; break;
+          case T_O: wev = need(EV_ATTN, l); notify = EV_O; break;
+          case T_GU: wev = need(EV_O, l); notify = EV_GU; break;
+          case T_DOWN: wev = need(EV_GU, l); notify = EV_DOWN; break;
+          case T_ROUTER: wev = need(EV_O, l); notify = EV_ROUTER; break;
+          case T_MGU:   // the share's size is known once routing is done
+            ok = ctx_wait(c, need(EV_ROUTE, l));
+            break;
+          case T_MDOWN: notify = EV_MDOWN; break;
+          default: break;
+        }
+        const bool routed = seen(EV_ROUTE, l);
+        for (int p = 0; ok; ++p) {
+          Pass ps;
+          if (!make_pass<WT>(c, task, p, wev, ps)) break;
+          Stream<WT> nx = next_stream<WT>(a, s, wg, q, n, l, t, task, p, routed);
+          // wave 0 stores the pass's outputs and notifies: it must reach its
+          // drain with no weight loads of the next pass in flight
+          if (wave == 0) nx.on = 0;
+          // the residual of O (the layer input) / down (h1) is final once this
+          // workgroup has seen the event that produced it: load it before waiting
+          float resid[kResid];
+          const bool early =
+              (ps.epi == E_O && (l == 0 || seen(EV_DOWN, l - 1))) || (ps.epi == E_DOWN && seen(EV_O, l));
+          if (early) load_resid(a, ps, resid);
+          ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs, ring, pre, nx);
+          if (!ok) break;
+          if (early) add_resid(s, ps, resid);
+          if (wave == 0) epilogue<WT>(c, ps, early);
+          if (threadIdx.x == 0) s.tclk[5] = (uint32_t)now_ticks();
+        }
+        if (!ok) return;
+        if (notify >= 0 && wave == 0) wave_notify(ev_ptr(a, l, notify), wg & (kSubs - 1));
+        record(task.x, t_begin);
+        advance();
+        if (l >= dm.L) break;
+        task = ldu4(q + t);
+        task.x &= 0xff;
+        if (!gemv_task(task.x)) break;
       }
     }
   }
