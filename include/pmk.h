@@ -183,10 +183,13 @@ int pmk_timing_read(pmk_handle* h, double* total_ms, int32_t* launches);
  *   [0] task type | layer << 8 | (first task coordinate & 0xffff) << 16
  *   [1] low 32 bits of the 100 MHz device clock when the task was taken
  *   [2] the clock once its input event was satisfied
- *   [3] the clock once its GEMV inputs were staged in LDS
- *   [4] the clock once wave 0 had streamed its weights
- *   [5] the clock once the partial sums were reduced
- *   [6] the clock once the epilogue had stored its outputs
+ *   [3] the clock once its inputs were staged in LDS
+ *   [4] the clock once wave 0 had streamed its weights (attention: once
+ *       wave 0 had gone through its KV positions)
+ *   [5] the clock once the partial sums were reduced (attention: once every
+ *       wave had)
+ *   [6] the clock once the epilogue had stored its outputs (attention: once
+ *       its outputs were issued)
  *   [7] the clock when it had finished and notified
  * (a phase the task does not have repeats the previous clock), and at entry
  * i = 0, element [0], the number of tasks recorded (tasks beyond

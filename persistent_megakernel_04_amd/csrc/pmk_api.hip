@@ -128,7 +128,9 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   dm.router_tiles = moe ? ceil_div(dm.E, 16) : 0;
   dm.max_tiles = moe ? ceil_div((long)dm.max_batch * dm.k, kMoeBM) + dm.E : 0;
   // rows per tile must fit the LDS output staging for one input row
-  if (2 * ceil_div(dm.qkv_units, dm.qkv_tiles) > kYsFloats || (!moe && 2 * ceil_div(dm.F, dm.gu_tiles) > kYsFloats) ||
+  // a step may put its few attention tasks on workgroups of their own and the
+  // QKV tiles on the others (at least three quarters of the grid)
+  if (2 * ceil_div(dm.qkv_units, std::min(G - G / 4, dm.qkv_units)) > kYsFloats || (!moe && 2 * ceil_div(dm.F, dm.gu_tiles) > kYsFloats) ||
       ceil_div(dm.H, dm.o_tiles) > kYsFloats) {
     delete h;
     return PMK_ERR_UNSUPPORTED;
@@ -178,9 +180,10 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     };
     parts.insert(parts.end(), mp.begin(), mp.end());
   }
-  // step intermediates are addressed with 32-bit byte offsets from one buffer base
+  // step intermediates are addressed with 32-bit byte offsets from one buffer
+  // base, and stay below the kernels' out-of-range marker offset (1 GiB)
   for (auto& p : parts)
-    if (p.bytes >= ((size_t)1 << 31)) { delete h; return PMK_ERR_ARG; }
+    if (p.bytes >= ((size_t)1 << 30)) { delete h; return PMK_ERR_ARG; }
   size_t total = 0;
   for (auto& p : parts) total += align256(p.bytes);
   void* base = nullptr;
@@ -230,6 +233,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     a0.ws = ws;
     a0.layers = h->d_layers;
     a0.attn_chunk = kMaxChunk;
+    a0.qkv_tiles = dm.qkv_tiles;
     if (hipMemcpy(ws.args, &a0, sizeof(a0), hipMemcpyHostToDevice) != hipSuccess) return fail(PMK_ERR_DEVICE);
   }
   if (prepare_main(desc->dtype) != hipSuccess) return fail(PMK_ERR_DEVICE);
@@ -252,6 +256,7 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
   a.kv = kv;
   a.seq_lens = seq_lens;
   a.batch = batch;
+  a.qkv_tiles = h->dm.qkv_tiles;
   a.watchdog_ticks = h->watchdog_ticks;
   if (rout) a.rout = *rout;
   a.trace = h->trace;

@@ -58,9 +58,22 @@ __device__ __forceinline__ int atomic_add_relaxed(int* p, int v) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
+// Buffer resource covering exactly `bytes` (< kNoRecord): a load at a byte
+// offset at or past the range returns zeros without touching memory (the
+// descriptor's range check), so kNoRecord + a small offset is a safe "no
+// data" address for it.
+constexpr int kNoRecord = 1 << 30;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
 // 16-byte device-coherent load/store at byte offset `off` from a wave-uniform base.
 __device__ __forceinline__ f4v ldc4(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
+}
+typedef unsigned u2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2 ldc2(__amdgpu_buffer_rsrc_t r, int off) {
+  const u2v v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16);
+  return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
 }
 __device__ __forceinline__ void stc4(__amdgpu_buffer_rsrc_t r, int off, f4v v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, v), r, off, 0, 16);
@@ -75,6 +88,9 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
   const u4v v = *(gptr_u4)(p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+
+typedef const __attribute__((address_space(1))) uint32_t* gptr_u32;
+__device__ __forceinline__ uint32_t ldg4(const void* p) { return *(gptr_u32)(p); }
 
 // Wait until every vector memory operation of this wave has completed
 // (stores acknowledged by the coherence point).
@@ -169,6 +185,14 @@ __device__ __forceinline__ float sum16(float v) {
   v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
   v += dpp<0x141>(v);   // row_half_mirror
   v += dpp<0x140>(v);   // row_mirror
+  return v;
+}
+// Max over each row of 16 lanes (every lane of the row gets it).
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
   return v;
 }
 // Row exchange between two registers holding the same value: afterwards one

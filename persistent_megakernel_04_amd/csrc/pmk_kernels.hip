@@ -209,7 +209,7 @@ __device__ __forceinline__ void stage_attn_merge(const StepArgs& a, const GemvIn
   const Dims& dm = a.dm;
   const int d = dm.d, G = dm.Hq / dm.Hkv, DP = d + 4, ck = a.attn_chunk;
   const int K4 = Kp / 4;   // 4-element units per row (K = Hq d, a multiple of 4; zero beyond K)
-  const auto pr = rsrc(a.ws.part);
+  const auto pr = rsrc_n(a.ws.part, dm.max_batch * dm.Hkv * dm.max_chunks * G * DP * 4);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int unit = threadIdx.x + u * kBlock;
@@ -223,7 +223,9 @@ __device__ __forceinline__ void stage_attn_merge(const StepArgs& a, const GemvIn
       f4v av[8], mv[8];
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
-        const int o = (base + min(cc, nc - 1) * G * DP) * 4;
+        // a chunk the request does not have reads past the buffer's range:
+        // zeros, with no memory access
+        const int o = cc < nc ? (base + cc * G * DP) * 4 : kNoRecord;
         av[cc] = ldc4(pr, o + e * 4);
         mv[cc] = ldc4(pr, o + d * 4);
       }
@@ -503,8 +505,8 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   ps.e = 0;
   switch (task.x) {
     case T_QKV: {   // RMSNorm1 + QKV rotation pairs of the tile
-      const int u0 = (int)((long)tile * dm.qkv_units / dm.qkv_tiles);
-      const int nu = (int)((long)(tile + 1) * dm.qkv_units / dm.qkv_tiles) - u0;
+      const int u0 = (int)((long)tile * dm.qkv_units / a.qkv_tiles);
+      const int nu = (int)((long)(tile + 1) * dm.qkv_units / a.qkv_tiles) - u0;
       const int nbb = pass_rows<WT>(dm.H, 2 * nu), b0 = p * nbb;
       if (b0 >= a.batch) return false;
       ps.rw = GemvRows{ROWS_QKV, Lp.w_qkv, nullptr, u0, dm.d >> 1};
@@ -730,6 +732,93 @@ template <> __device__ __forceinline__ uint4 pack_row<float>(__amdgpu_buffer_rsr
   return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
 }
 
+// The end of an attention chunk task, once every wave has left its partial
+// (acc[D], max, sum per query head; log2 units) in LDS at sw[wave][h][DP]:
+// combine the 8 waves into this chunk's partial (or the output, for a request
+// with a single chunk), then notify; without the O-projection merge, the last
+// chunk task of (b, g) to finish merges all partials by log-sum-exp.
+template <int D>
+__device__ __forceinline__ bool attn_finish(const Ctx& c, int b, int g, int ci, int tix, int nc, int G,
+                                           const float* sw) {
+  const StepArgs& a = c.a;
+  const Dims& dm = a.dm;
+  constexpr int DP = D + 4;
+  const int tid = threadIdx.x;
+  float* o = a.ws.o + (size_t)b * dm.Hq * D + (size_t)g * G * D;
+  float* part = a.ws.part + (((size_t)b * dm.Hkv + g) * dm.max_chunks + ci) * G * DP;
+  const auto orr = rsrc(o), prr = rsrc(part);
+  for (int t = tid; t < G * D / 4; t += kBlock) {
+    const int h = t / (D / 4), e0 = (t - h * (D / 4)) * 4;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sw[(w * G + h) * DP + D]);
+    float Ls = 0.f;
+    f4v A = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float* sp = sw + (w * G + h) * DP;
+      const float f = (sp[D] == -INFINITY) ? 0.f : exp2f(sp[D] - M);
+      Ls += sp[D + 1] * f;
+      A += *reinterpret_cast<const f4v*>(sp + e0) * f;
+    }
+    if (nc == 1 && !a.attn_merge_o) {
+      stc4(orr, (h * D + e0) * 4, A / Ls);
+    } else {
+      stc4(prr, (h * DP + e0) * 4, A);
+      if (e0 == 0) stc4(prr, (h * DP + D) * 4, f4v{M, Ls, 0.f, 0.f});
+    }
+  }
+  if (tid == 0) c.s.tclk[5] = (uint32_t)now_ticks();   // outputs issued
+  if (a.attn_merge_o) {   // the O-projection merges the partials as it stages its inputs
+    wg_notify(ev_ptr(a, c.l, EV_ATTN), tix & (kSubs - 1));
+    return true;
+  }
+  if (nc == 1) {
+    wg_notify(ev_ptr(a, c.l, EV_ATTN), (b * dm.Hkv + g) & (kSubs - 1));
+    return true;
+  }
+  // the last chunk task of (b, g) to finish merges the partials
+  vm_drain();
+  __syncthreads();
+  if (tid == 0) {
+    int* mc = a.ws.mctr + (((size_t)c.l * dm.max_batch + b) * dm.Hkv + g) * kCtr;
+    *c.s.flag = (atomic_add_relaxed(mc, -1) == 1);
+  }
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(*c.s.flag)) {
+    const auto pbr = rsrc(a.ws.part + ((size_t)b * dm.Hkv + g) * dm.max_chunks * G * DP);
+    for (int t = tid; t < G * D / 4; t += kBlock) {
+      const int h = t / (D / 4), e0 = (t - h * (D / 4)) * 4;
+      float M = -INFINITY, Ls = 0.f;
+      f4v A = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < nc; c0 += 16) {   // 16 chunks' loads in flight at once
+        f4v ms[16], as[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int cc = min(c0 + u, nc - 1);
+          const int ro = ((cc * G + h) * DP) * 4;
+          as[u] = ldc4(pbr, ro + e0 * 4);
+          ms[u] = ldc4(pbr, ro + D * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (c0 + u < nc) {
+            const float mn = fmaxf(M, ms[u].x);
+            const float fo = (M == -INFINITY) ? 0.f : exp2f(M - mn), fc = exp2f(ms[u].x - mn);
+            Ls = Ls * fo + ms[u].y * fc;
+            A = A * fo + as[u] * fc;
+            M = mn;
+          }
+        }
+      }
+      stc4(orr, (h * D + e0) * 4, A / Ls);
+    }
+    wg_notify(ev_ptr(a, c.l, EV_ATTN), (b * dm.Hkv + g) & (kSubs - 1));
+  }
+  __syncthreads();
+  return true;
+}
+
 template <typename KT, int HB, int ITS>
 __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, int tix, const int* wev) {
   const StepArgs& a = c.a;
@@ -826,82 +915,181 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
       if (lane == 0) { dst[D] = M; dst[D + 1] = lw; }
     }
   }
+  if (tid == 0) c.s.tclk[3] = (uint32_t)now_ticks();   // wave 0's positions done
   __syncthreads();
-  if (tid == 0) c.s.tclk[3] = (uint32_t)now_ticks();
-  // combine the 8 waves: this chunk's partial (or the output for a single chunk)
-  float* o = a.ws.o + (size_t)b * dm.Hq * D + (size_t)g * G * D;
-  float* part = a.ws.part + (((size_t)b * dm.Hkv + g) * dm.max_chunks + ci) * G * DP;
-  const auto orr = rsrc(o), prr = rsrc(part);
-  for (int t = tid; t < G * D / 4; t += kBlock) {
-    const int h = t / (D / 4), e0 = (t - h * (D / 4)) * 4;
-    float M = -INFINITY;
+  if (tid == 0) c.s.tclk[4] = (uint32_t)now_ticks();   // every wave's
+  return attn_finish<D>(c, b, g, ci, tix, nc, G, sw);
+}
+
+// Split-K GQA decode attention with bfloat16 KV and head_dim 128, at most 8
+// query heads per KV head (same task as task_attn, other engine). Each wave
+// takes 16-position tiles (TW of them: tile t covers positions
+// p0 + (wave + 8 t) * 16 ..). Scores come from the matrix cores: the G query
+// heads (rows, padded to 16) times the tile's K rows (columns), the rows
+// loaded as 16-row x 64-byte MFMA fragments exactly like GEMV weights, the
+// queries as hi + lo bfloat16 pairs (float32-level products). The softmax of
+// a wave's positions is plain (no running rescale): row max and sum are DPP
+// reductions over the tile's 16 lanes. P V runs on the vector ALUs with each
+// lane owning two head_dim elements over all of the wave's positions, the
+// probabilities broadcast through LDS, so no cross-lane reduction is needed.
+// GP: query heads rounded up to 4 or 8.
+template <int TW, int GP>
+__device__ __forceinline__ bool task_attn_mm(const Ctx& c, int b, int g, int ci, int tix, const int* wev) {
+  const StepArgs& a = c.a;
+  const Dims& dm = a.dm;
+  typedef MM<uint16_t> T;
+  constexpr int D = 128, DP = D + 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), j = lane & 15, r = lane >> 4;
+  const int G = dm.Hq / dm.Hkv;
+  const int ck = a.attn_chunk;
+  const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * D;
+  const int S = ldu(a.seq_lens + b), n = S + 1;
+  const int p0 = ci * ck, p1 = min(n, p0 + ck);
+  const int nc = (n + ck - 1) / ck;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kv) + kv_off(dm, c.l, 0, b, g, 0);
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.kv) + kv_off(dm, c.l, 1, b, g, 0);
+  const int pmax = S > 0 ? S - 1 : 0;   // cached slots only (slot S is this step's)
+  // the cached rows, before the QKV event: K as MFMA fragments (lane (j, r):
+  // row tb + j, elements 32 s + 8 r ..), V as one element pair per lane per row
+  uint4 kr[TW][4];
+  uint32_t vr[TW][16];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sw[(w * G + h) * DP + D]);
-    float Ls = 0.f;
-    f4v A = {0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TW; ++t) {
+    const int tb = p0 + (wave + kWaves * t) * 16;
+    const uint16_t* kp = Kb + (size_t)min(tb + j, pmax) * D + r * 8;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* sp = sw + (w * G + h) * DP;
-      const float f = (sp[D] == -INFINITY) ? 0.f : exp2f(sp[D] - M);
-      Ls += sp[D + 1] * f;
-      A += *reinterpret_cast<const f4v*>(sp + e0) * f;
+    for (int s4 = 0; s4 < 4; ++s4) kr[t][s4] = ldg16(kp + s4 * 32);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) vr[t][i] = ldg4(Vb + (size_t)min(tb + i, pmax) * D + 2 * lane);
+  }
+  if (!ctx_wait(c, wev)) return false;
+
+  // A operand: query head j of the group (zero beyond G), q * log2(e) / sqrt(d) as hi + lo
+  const auto qr = rsrc_n(a.ws.qkv + (size_t)b * qkv_dim, qkv_dim * 4);
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);
+  uint4 qh[4], ql[4];
+  {
+    const int qo = j < G ? ((g * G + j) * D + r * 8) * 4 : kNoRecord;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const f4v x0 = ldc4(qr, qo + s4 * 128) * qscale, x1 = ldc4(qr, qo + s4 * 128 + 16) * qscale;
+      uint16_t hb[8], lb[8];
+      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hb[e] = f2bf(xv[e]);
+        lb[e] = f2bf(xv[e] - __uint_as_float((uint32_t)hb[e] << 16));
+      }
+      qh[s4] = make_uint4(hb[0] | ((uint32_t)hb[1] << 16), hb[2] | ((uint32_t)hb[3] << 16),
+                          hb[4] | ((uint32_t)hb[5] << 16), hb[6] | ((uint32_t)hb[7] << 16));
+      ql[s4] = make_uint4(lb[0] | ((uint32_t)lb[1] << 16), lb[2] | ((uint32_t)lb[3] << 16),
+                          lb[4] | ((uint32_t)lb[5] << 16), lb[6] | ((uint32_t)lb[7] << 16));
     }
-    if (nc == 1 && !a.attn_merge_o) {
-      stc4(orr, (h * D + e0) * 4, A / Ls);
-    } else {
-      stc4(prr, (h * DP + e0) * 4, A);
-      if (e0 == 0) stc4(prr, (h * DP + D) * 4, f4v{M, Ls, 0.f, 0.f});
+  }
+  // position S takes this step's rotated k and v, rounded as the KV append stores them
+  if (S >= p0 && S < p1) {
+    const int tt = (S - p0) >> 4, jj = (S - p0) & 15;
+    if (tt % kWaves == wave) {
+      const int ts = tt / kWaves;
+      const int ko = j == jj ? ((dm.Hq + g) * D + r * 8) * 4 : kNoRecord;
+      const float2 vv = ldc2(qr, ((dm.Hq + dm.Hkv + g) * D + 2 * lane) * 4);
+      const uint32_t vn = (uint32_t)f2bf(vv.x) | ((uint32_t)f2bf(vv.y) << 16);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const f4v x0 = ldc4(qr, ko + s4 * 128), x1 = ldc4(qr, ko + s4 * 128 + 16);
+        const uint4 kn = make_uint4((uint32_t)f2bf(x0.x) | ((uint32_t)f2bf(x0.y) << 16),
+                                    (uint32_t)f2bf(x0.z) | ((uint32_t)f2bf(x0.w) << 16),
+                                    (uint32_t)f2bf(x1.x) | ((uint32_t)f2bf(x1.y) << 16),
+                                    (uint32_t)f2bf(x1.z) | ((uint32_t)f2bf(x1.w) << 16));
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+          if (t == ts && j == jj) kr[t][s4] = kn;
+      }
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (t == ts && i == jj) vr[t][i] = vn;
     }
   }
-  if (a.attn_merge_o) {   // the O-projection merges the partials as it stages its inputs
-    wg_notify(ev_ptr(a, c.l, EV_ATTN), tix & (kSubs - 1));
-    return true;
-  }
-  if (nc == 1) {
-    wg_notify(ev_ptr(a, c.l, EV_ATTN), (b * dm.Hkv + g) & (kSubs - 1));
-    return true;
-  }
-  // the last chunk task of (b, g) to finish merges the partials
-  vm_drain();
-  __syncthreads();
-  if (tid == 0) {
-    int* mc = a.ws.mctr + (((size_t)c.l * dm.max_batch + b) * dm.Hkv + g) * kCtr;
-    *c.s.flag = (atomic_add_relaxed(mc, -1) == 1);
-  }
-  __syncthreads();
-  if (tid == 0) c.s.tclk[4] = (uint32_t)now_ticks();
-  if (__builtin_amdgcn_readfirstlane(*c.s.flag)) {
-    const auto pbr = rsrc(a.ws.part + ((size_t)b * dm.Hkv + g) * dm.max_chunks * G * DP);
-    for (int t = tid; t < G * D / 4; t += kBlock) {
-      const int h = t / (D / 4), e0 = (t - h * (D / 4)) * 4;
-      float M = -INFINITY, Ls = 0.f;
-      f4v A = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = 0; c0 < nc; c0 += 16) {   // 16 chunks' loads in flight at once
-        f4v ms[16], as[16];
+  if (tid == 0) c.s.tclk[2] = (uint32_t)now_ticks();
+
+  // scores: lane (j + 16 rr), element e holds head 4 rr + e at position tb + j
+  f4v sc[TW];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int cc = min(c0 + u, nc - 1);
-          const int ro = ((cc * G + h) * DP) * 4;
-          as[u] = ldc4(pbr, ro + e0 * 4);
-          ms[u] = ldc4(pbr, ro + D * 4);
-        }
+  for (int t = 0; t < TW; ++t) {
+    sc[t] = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          if (c0 + u < nc) {
-            const float mn = fmaxf(M, ms[u].x);
-            const float fo = (M == -INFINITY) ? 0.f : exp2f(M - mn), fc = exp2f(ms[u].x - mn);
-            Ls = Ls * fo + ms[u].y * fc;
-            A = A * fo + as[u] * fc;
-            M = mn;
-          }
+    for (int s4 = 0; s4 < 4; ++s4) {
+      sc[t] = T::mac(qh[s4], kr[t][s4], sc[t]);
+      sc[t] = T::mac(ql[s4], kr[t][s4], sc[t]);
+    }
+  }
+  bool valid[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) valid[t] = p0 + (wave + kWaves * t) * 16 + j < p1;
+  float mx[4], ls[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) m = fmaxf(m, valid[t] ? sc[t][e] : -INFINITY);
+    mx[e] = max16(m);
+    float l = 0.f;
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      const float pe = valid[t] ? exp2f(sc[t][e] - mx[e]) : 0.f;
+      sc[t][e] = pe;
+      l += pe;
+    }
+    ls[e] = sum16(l);
+  }
+  // probabilities to LDS, [t][position][head], for the broadcast reads of P V
+  float* sw = reinterpret_cast<float*>(c.s.xs);                         // [kWaves][G][DP] wave partials
+  float* pb = sw + kWaves * 8 * DP + wave * (TW * 16 * GP);             // this wave's [TW][16][GP]
+  if (r < GP / 4) {
+#pragma unroll
+    for (int t = 0; t < TW; ++t) *reinterpret_cast<f4v*>(pb + (t * 16 + j) * GP + 4 * r) = sc[t];
+  }
+  float acc[GP][2];
+#pragma unroll
+  for (int h = 0; h < GP; ++h) acc[h][0] = acc[h][1] = 0.f;
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float v0 = bf_lo(vr[t][i]), v1 = bf_hi(vr[t][i]);
+#pragma unroll
+      for (int h4 = 0; h4 < GP / 4; ++h4) {
+        const f4v pp = *reinterpret_cast<const f4v*>(pb + (t * 16 + i) * GP + 4 * h4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[4 * h4 + e][0] += pp[e] * v0;
+          acc[4 * h4 + e][1] += pp[e] * v1;
         }
       }
-      stc4(orr, (h * D + e0) * 4, A / Ls);
+      // one position at a time: left alone, the compiler sinks every
+      // accumulation to the final store and holds all TW * 16 * GP
+      // probabilities and V pairs live until then
+#pragma unroll
+      for (int h = 0; h < GP; ++h) __asm__ volatile("" : "+v"(acc[h][0]), "+v"(acc[h][1]));
     }
-    wg_notify(ev_ptr(a, c.l, EV_ATTN), (b * dm.Hkv + g) & (kSubs - 1));
   }
+  // this wave's partial per head: acc (2 elements per lane), max and sum (uniform)
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    if (h < G) {
+      float* dst = sw + (wave * G + h) * DP;
+      *reinterpret_cast<float2*>(dst + 2 * lane) = make_float2(acc[h][0], acc[h][1]);
+      const int M = __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx[h & 3]), 16 * (h >> 2));
+      const int L = __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls[h & 3]), 16 * (h >> 2));
+      if (lane == 0) { dst[D] = __builtin_bit_cast(float, M); dst[D + 1] = __builtin_bit_cast(float, L); }
+    }
+  }
+  if (tid == 0) c.s.tclk[3] = (uint32_t)now_ticks();   // wave 0's positions done
   __syncthreads();
-  return true;
+  if (tid == 0) c.s.tclk[4] = (uint32_t)now_ticks();   // every wave's
+  return attn_finish<D>(c, b, g, ci, tix, nc, G, sw);
 }
 
 template <typename KT, int HB>
@@ -915,6 +1103,12 @@ __device__ __forceinline__ bool attn_its(const Ctx& c, int b, int g, int ci, int
 template <typename KT>
 __device__ __forceinline__ bool attn_dispatch(const Ctx& c, int b, int g, int ci, int tix, const int* wev) {
   const int G = c.a.dm.Hq / c.a.dm.Hkv, ck = c.a.attn_chunk;
+  if constexpr (sizeof(KT) == 2) {
+    if (c.a.dm.d == 128 && G <= 8) {
+      if (G <= 4) return ck > 128 ? task_attn_mm<2, 4>(c, b, g, ci, tix, wev) : task_attn_mm<1, 4>(c, b, g, ci, tix, wev);
+      return ck > 128 ? task_attn_mm<2, 8>(c, b, g, ci, tix, wev) : task_attn_mm<1, 8>(c, b, g, ci, tix, wev);
+    }
+  }
   if (G >= 4) return attn_its<KT, 4>(c, b, g, ci, tix, ck, wev);
   if (G == 2) return attn_its<KT, 2>(c, b, g, ci, tix, ck, wev);
   return attn_its<KT, 1>(c, b, g, ci, tix, ck, wev);
@@ -1266,10 +1460,12 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           // drain with no weight loads of the next pass in flight
           if (wave == 0) nx.on = 0;
           // the residual of O (the layer input) / down (h1) is final once this
-          // workgroup has seen the event that produced it: load it before waiting
+          // workgroup has seen the event that produced it, or one that fires
+          // only after it (every QKV tile waits for the previous layer's down
+          // stage): load it before waiting
           float resid[kResid];
-          const bool early =
-              (ps.epi == E_O && (l == 0 || seen(EV_DOWN, l - 1))) || (ps.epi == E_DOWN && seen(EV_O, l));
+          const bool early = (ps.epi == E_O && (l == 0 || seen(EV_DOWN, l - 1) || seen(EV_QKV, l))) ||
+                             (ps.epi == E_DOWN && seen(EV_O, l));
           if (early) load_resid(a, ps, resid);
           ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs, ring, pre, nx);
           if (!ok) break;
@@ -1325,7 +1521,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   const Dims& dm = a.dm;
   const int tid = threadIdx.x, B = a.batch, G = dm.grid;
   __shared__ int bad;
-  __shared__ int total_attn, merge_s;
+  __shared__ int total_attn, merge_s, qkv_tiles_s, attn_wg0_s;
   __shared__ int cb[kMaxBatchAll + 1];
   StepArgs* copy = reinterpret_cast<StepArgs*>(a.ws.args);
   if (tid == 0) {
@@ -1385,6 +1581,15 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     cb[B] = acc;
     total_attn = acc * dm.Hkv;
     copy->attn_chunk = ck;
+    // A few attention tasks (at most a quarter of the grid) get workgroups of
+    // their own, the last ones, which hold no QKV tile: their task comes first
+    // in the layer, so its KV rows stream in while the QKV tiles run on the
+    // other workgroups. Otherwise the attention tasks follow the QKV tiles on
+    // every workgroup.
+    const int own = (merge && total_attn <= G / 4) ? total_attn : 0;
+    attn_wg0_s = own ? G - own : G;
+    qkv_tiles_s = min(G - own, dm.qkv_units);
+    copy->qkv_tiles = qkv_tiles_s;
   }
   __syncthreads();
   const int router_tasks = dm.moe ? dm.router_tiles * ((B + kMaxNb - 1) / kMaxNb) : 0;
@@ -1397,8 +1602,9 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       if (n < dm.max_queue) q[n] = v;
       ++n;
     };
-    for (int t = w; t < dm.qkv_tiles; t += G) push(make_int4(T_QKV, t, 0, 0));
-    for (int i = w; i < total_attn; i += G) {
+    const int aw0 = attn_wg0_s;
+    for (int t = w; t < qkv_tiles_s; t += G) push(make_int4(T_QKV, t, 0, 0));
+    for (int i = aw0 < G ? w - aw0 : w; i >= 0 && i < total_attn; i += (aw0 < G ? total_attn : G)) {
       int lo = 0, hi = B;   // find b: Hkv*cb[b] <= i < Hkv*cb[b+1]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -1426,7 +1632,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     const int e = idx % EV_COUNT;
     int* ev = a.ws.ev + (size_t)idx * kEvInts;
     switch (e) {
-      case EV_QKV: arm_tiles(ev, dm.qkv_tiles, G); break;
+      case EV_QKV: arm_tiles(ev, qkv_tiles_s, G); break;
       // one notifier per chunk task (partials merged by the O-projection), or per (request, KV head)
       case EV_ATTN: arm_indexed(ev, merge_s ? total_attn : B * dm.Hkv); break;
       case EV_O: arm_tiles(ev, dm.o_tiles, G); break;

@@ -1,12 +1,13 @@
 """Decode and summarise the task trace written by libpmk (pmk_trace_attach).
 
 Each record is one task run by one persistent workgroup, with the 100 MHz
-device clock at seven points: taken, input event satisfied, GEMV inputs staged,
-weights streamed (wave 0), partial sums reduced, outputs stored, notified. The
-summary gives, per stage of a layer, when the first workgroup started it and
-the last one finished, and how the tasks' time splits over those phases,
-averaged over layers: where a step's time goes between the HBM-bound work and
-the synchronisation around it.
+device clock at seven points: taken, input event satisfied, inputs staged,
+weights streamed by wave 0 (attention: wave 0's positions done), partial sums
+reduced (attention: every wave done), outputs stored (attention: issued),
+notified. The summary gives, per stage of a layer, when the first workgroup
+started it and the last one finished, and how the tasks' time splits over
+those phases, averaged over layers: where a step's time goes between the
+HBM-bound work and the synchronisation around it.
 """
 from __future__ import annotations
 
