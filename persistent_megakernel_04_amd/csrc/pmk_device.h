@@ -23,17 +23,30 @@ typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 // on wait. Weights and already-cached KV entries are immutable during a step
 // and use ordinary cached loads.
 // ---------------------------------------------------------------------------
+//
+// Every access here goes through the global address space: through a generic
+// pointer it would compile to a FLAT instruction, which also counts against
+// the LDS wait counter, so each later LDS wait would wait for it as well (a
+// store: until the coherence point acknowledges it).
+template <typename T> __device__ __forceinline__ const __attribute__((address_space(1))) T* gp(const T* p) {
+  return (const __attribute__((address_space(1))) T*)p;
+}
+template <typename T> __device__ __forceinline__ __attribute__((address_space(1))) T* gp(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+// Plain global load of a field (a pointer, say) of an immutable struct.
+template <typename T> __device__ __forceinline__ T ldp(const T* field) { return *gp(field); }
 __device__ __forceinline__ float ldc(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void stc(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int ldci(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void stci(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Device-coherent load of a value that is the same for the whole wave (one
 // address), kept in a scalar register: the compiler cannot tell that an
@@ -41,14 +54,15 @@ __device__ __forceinline__ void stci(int* p, int v) {
 // loop over lanes.
 __device__ __forceinline__ int ldsu(const int* p) { return __builtin_amdgcn_readfirstlane(ldci(p)); }
 // Plain load of a wave-uniform int through a generic pointer, kept scalar.
-__device__ __forceinline__ int ldu(const int* p) { return __builtin_amdgcn_readfirstlane(*p); }
+__device__ __forceinline__ int ldu(const int* p) { return __builtin_amdgcn_readfirstlane(*gp(p)); }
 __device__ __forceinline__ int4 ldu4(const int4* p) {
-  const int4 v = *p;
+  typedef int i4v __attribute__((ext_vector_type(4)));
+  const i4v v = *gp(reinterpret_cast<const i4v*>(p));
   return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
                    __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
 }
 __device__ __forceinline__ int atomic_add_relaxed(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Buffer resource for device-coherent 16-byte accesses. `base` must be
@@ -119,7 +133,7 @@ __device__ __forceinline__ int* ev_slot(int* ev, int sub) { return sub >= 0 ? ev
 __device__ __forceinline__ void wg_notify(int* ev, int sub) {
   vm_drain();
   __syncthreads();
-  if (threadIdx.x == 0) (void)__hip_atomic_fetch_add(ev_slot(ev, sub), -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) (void)atomic_add_relaxed(ev_slot(ev, sub), -1);
 }
 
 // One wave: publish this wave's completed stores, then notify. Used where that
@@ -128,7 +142,7 @@ __device__ __forceinline__ void wg_notify(int* ev, int sub) {
 __device__ __forceinline__ void wave_notify(int* ev, int sub) {
   vm_drain();
   if ((threadIdx.x & 63) == 0)
-    (void)__hip_atomic_fetch_add(ev_slot(ev, sub), -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    (void)atomic_add_relaxed(ev_slot(ev, sub), -1);
 }
 
 // Wave 0 only: spin until the event's counters are all zero (`subs` = number
@@ -148,7 +162,7 @@ __device__ __forceinline__ bool spin_zero(const int* ev, int subs, int* err, uns
       if (now_ticks() - t0 > ticks) {
         if (lane == 0) {
           int expected = 0;
-          __hip_atomic_compare_exchange_strong(err, &expected, (int)PMK_ERR_TIMEOUT, __ATOMIC_RELAXED,
+          __hip_atomic_compare_exchange_strong(gp(err), &expected, (int)PMK_ERR_TIMEOUT, __ATOMIC_RELAXED,
                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           stci(err + 16, 1);
         }
@@ -245,11 +259,11 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static __device__ __forceinline__ float rnd(float f) { return f; }
-  static __device__ __forceinline__ void put(float* p, float f) { *p = f; }
+  static __device__ __forceinline__ void put(float* p, float f) { *gp(p) = f; }
 };
 template <> struct Elem<uint16_t> {
   static __device__ __forceinline__ float rnd(float f) { return __uint_as_float((uint32_t)f2bf(f) << 16); }
-  static __device__ __forceinline__ void put(uint16_t* p, float f) { *p = f2bf(f); }
+  static __device__ __forceinline__ void put(uint16_t* p, float f) { *gp(p) = f2bf(f); }
 };
 
 // 8 consecutive elements (16 B of bfloat16, or 32 B of float) -> float[8].

@@ -176,7 +176,7 @@ __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int 
         if (lane == 0) s.ssp[m * kWaves + wave] += ss;
       }
       if (in.gain && k < K) {
-        const float4 g = *reinterpret_cast<const float4*>(in.gain + k);
+        const f4v g = *gp(reinterpret_cast<const f4v*>(in.gain + k));
         x.x *= g.x; x.y *= g.y; x.z *= g.z; x.w *= g.w;
       }
       if (k < Kp) {
@@ -217,7 +217,7 @@ __device__ __forceinline__ void stage_attn_merge(const StepArgs& a, const GemvIn
     const int m = unit / K4, k = (unit - m * K4) * 4;
     f4v x = {0.f, 0.f, 0.f, 0.f};
     if (k < K) {
-      const int b = in.merge_b0 + m, nc = (a.seq_lens[b] + ck) / ck;
+      const int b = in.merge_b0 + m, nc = (*gp(a.seq_lens + b) + ck) / ck;
       const int h = k / d, e = k - h * d, g = h / G, hh = h - g * G;
       const int base = ((b * dm.Hkv + g) * dm.max_chunks * G + hh) * DP;   // floats; part is < 2 GiB
       f4v av[8], mv[8];
@@ -498,7 +498,7 @@ template <typename WT>
 __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, const int* wev, Pass& ps) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
-  const LayerPtrs& Lp = a.layers[c.l];
+  const LayerPtrs* Lp = a.layers + c.l;   // its fields are read with global loads (ldp)
   const int tile = task.y;
   ps.wev = p == 0 ? wev : nullptr;
   ps.wsubs = kSubs;
@@ -509,8 +509,8 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int nu = (int)((long)(tile + 1) * dm.qkv_units / a.qkv_tiles) - u0;
       const int nbb = pass_rows<WT>(dm.H, 2 * nu), b0 = p * nbb;
       if (b0 >= a.batch) return false;
-      ps.rw = GemvRows{ROWS_QKV, Lp.w_qkv, nullptr, u0, dm.d >> 1};
-      ps.in = GemvIn{a.hidden + (size_t)b0 * dm.H, dm.H, nullptr, Lp.attn_norm, 1, dm.eps, -1};
+      ps.rw = GemvRows{ROWS_QKV, ldp(&Lp->w_qkv), nullptr, u0, dm.d >> 1};
+      ps.in = GemvIn{a.hidden + (size_t)b0 * dm.H, dm.H, nullptr, ldp(&Lp->attn_norm), 1, dm.eps, -1};
       ps.R = 2 * nu; ps.K = dm.H; ps.nb = min(nbb, a.batch - b0);
       ps.epi = E_QKV; ps.b0 = b0; ps.r0 = u0; ps.n = nu;
       return true;
@@ -520,7 +520,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int r0 = (int)((long)tile * dm.H / dm.o_tiles), R = (int)((long)(tile + 1) * dm.H / dm.o_tiles) - r0;
       const int nbb = pass_rows<WT>(K, R), b0 = p * nbb;
       if (b0 >= a.batch) return false;
-      ps.rw = GemvRows{ROWS_CONTIG, Lp.w_o, nullptr, r0, 0};
+      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_o), nullptr, r0, 0};
       ps.in = GemvIn{a.ws.o + (size_t)b0 * K, K, nullptr, nullptr, 0, 0.f, a.attn_merge_o ? b0 : -1};
       ps.R = R; ps.K = K; ps.nb = min(nbb, a.batch - b0);
       ps.epi = E_O; ps.b0 = b0; ps.r0 = r0; ps.n = R;
@@ -530,8 +530,8 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int r0 = (int)((long)tile * dm.F / dm.gu_tiles), Rh = (int)((long)(tile + 1) * dm.F / dm.gu_tiles) - r0;
       const int nbb = pass_rows<WT>(dm.H, 2 * Rh), b0 = p * nbb;
       if (b0 >= a.batch) return false;
-      ps.rw = GemvRows{ROWS_PAIR, Lp.w_gate, Lp.w_up, r0, Rh};
-      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, Lp.ffn_norm, 1, dm.eps, -1};
+      ps.rw = GemvRows{ROWS_PAIR, ldp(&Lp->w_gate), ldp(&Lp->w_up), r0, Rh};
+      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
       ps.R = 2 * Rh; ps.K = dm.H; ps.nb = min(nbb, a.batch - b0);
       ps.epi = E_GU; ps.b0 = b0; ps.r0 = r0; ps.n = Rh;
       return true;
@@ -540,7 +540,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int r0 = (int)((long)tile * dm.H / dm.down_tiles), R = (int)((long)(tile + 1) * dm.H / dm.down_tiles) - r0;
       const int nbb = pass_rows<WT>(dm.F, R), b0 = p * nbb;
       if (b0 >= a.batch) return false;
-      ps.rw = GemvRows{ROWS_CONTIG, Lp.w_down, nullptr, r0, 0};
+      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_down), nullptr, r0, 0};
       ps.in = GemvIn{a.ws.act + (size_t)b0 * dm.F, dm.F, nullptr, nullptr, 0, 0.f, -1};
       ps.R = R; ps.K = dm.F; ps.nb = min(nbb, a.batch - b0);
       ps.epi = E_DOWN; ps.b0 = b0; ps.r0 = r0; ps.n = R;
@@ -551,8 +551,8 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int nbb = pass_rows<WT>(dm.H, 16), b0 = task.z * kMaxNb + p * nbb;
       if (b0 >= bend) return false;
       const int r0 = tile * 16;
-      ps.rw = GemvRows{ROWS_CONTIG, Lp.w_router, nullptr, r0, 0};
-      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, Lp.ffn_norm, 1, dm.eps, -1};
+      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_router), nullptr, r0, 0};
+      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
       ps.R = min(16, dm.E - r0); ps.K = dm.H; ps.nb = min(nbb, bend - b0);
       ps.epi = E_ROUTER; ps.b0 = b0; ps.r0 = r0; ps.n = ps.R;
       return true;
@@ -564,10 +564,10 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int e = ldsu(a.ws.tile_info + 2 * t), row0 = ldsu(a.ws.tile_info + 2 * t + 1);
       const int f0 = (int)((long)sl * dm.Fe / sg), Rh = (int)((long)(sl + 1) * dm.Fe / sg) - f0;
       const size_t eo = (size_t)e * dm.Fe * dm.H;
-      ps.rw = GemvRows{ROWS_PAIR, reinterpret_cast<const WT*>(Lp.w_exp_gate) + eo,
-                       reinterpret_cast<const WT*>(Lp.w_exp_up) + eo, f0, Rh};
+      ps.rw = GemvRows{ROWS_PAIR, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_gate)) + eo,
+                       reinterpret_cast<const WT*>(ldp(&Lp->w_exp_up)) + eo, f0, Rh};
       // the tile's rows: its routed tokens' FFN inputs (RMSNorm2 of h1), gathered
-      ps.in = GemvIn{a.ws.h1, dm.H, a.ws.sorted_tok + row0, Lp.ffn_norm, 1, dm.eps, -1};
+      ps.in = GemvIn{a.ws.h1, dm.H, a.ws.sorted_tok + row0, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
       ps.R = 2 * Rh; ps.K = dm.H; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
       ps.epi = E_MGU; ps.b0 = row0; ps.r0 = f0; ps.n = Rh; ps.e = e;
       return true;
@@ -578,7 +578,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int sd = ldsu(a.ws.moe_info + 3), t = i / sd, sl = i - t * sd;
       const int e = ldsu(a.ws.tile_info + 2 * t), row0 = ldsu(a.ws.tile_info + 2 * t + 1);
       const int h0 = (int)((long)sl * dm.H / sd), R = (int)((long)(sl + 1) * dm.H / sd) - h0;
-      ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(Lp.w_exp_down) + (size_t)e * dm.H * dm.Fe, nullptr, h0,
+      ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_down)) + (size_t)e * dm.H * dm.Fe, nullptr, h0,
                        0};
       ps.in = GemvIn{a.ws.mact + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f, -1};
       ps.R = R; ps.K = dm.Fe; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
@@ -637,9 +637,10 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
         const int unit = ps.r0 + ju, h = unit / half, i = unit - h * half;
         const float r = c.s.rstd[m];
         float y1 = ys[(2 * ju) * nb + m] * r, y2 = ys[(2 * ju + 1) * nb + m] * r;
-        const int bb = b0 + m, pos = a.seq_lens[bb];
+        const int bb = b0 + m, pos = *gp(a.seq_lens + bb);
         if (h < dm.Hq + dm.Hkv) {
-          const float2 cs = a.ws.rope[(size_t)pos * half + i];
+          typedef float f2v __attribute__((ext_vector_type(2)));
+          const f2v cs = *gp(reinterpret_cast<const f2v*>(a.ws.rope + (size_t)pos * half + i));
           const float t1 = y1 * cs.x - y2 * cs.y, t2 = y2 * cs.x + y1 * cs.y;
           y1 = t1;
           y2 = t2;
@@ -1263,14 +1264,14 @@ __device__ __forceinline__ bool task_route(const Ctx& c, const int* wev) {
   if (c.l == dm.L - 1) {
     const pmk_routing& r = a.rout;
     for (int i = tid; i < Tk; i += kBlock) {
-      if (r.topk_idx) r.topk_idx[i] = sidx[i];
-      if (r.topk_w) r.topk_w[i] = ldc(a.ws.topk_w + i);
+      if (r.topk_idx) *gp(r.topk_idx + i) = sidx[i];
+      if (r.topk_w) *gp(r.topk_w + i) = ldc(a.ws.topk_w + i);
     }
     if (r.router_logits)
-      for (int i = tid; i < T * E; i += kBlock) r.router_logits[i] = ldc(a.ws.logits + i);
+      for (int i = tid; i < T * E; i += kBlock) *gp(r.router_logits + i) = ldc(a.ws.logits + i);
     for (int e = tid; e <= E; e += kBlock) {
-      if (r.exp_indptr) r.exp_indptr[e] = ptr[e];
-      if (r.tile_indptr) r.tile_indptr[e] = tptr[e];
+      if (r.exp_indptr) *gp(r.exp_indptr + e) = ptr[e];
+      if (r.tile_indptr) *gp(r.tile_indptr + e) = tptr[e];
     }
   }
   // the scattered order is read back once the stores above have landed
@@ -1278,8 +1279,8 @@ __device__ __forceinline__ bool task_route(const Ctx& c, const int* wev) {
   __syncthreads();
   if (c.l == dm.L - 1 && (a.rout.sorted_tok || a.rout.sorted_slot)) {
     for (int i = tid; i < Tk; i += kBlock) {
-      if (a.rout.sorted_tok) a.rout.sorted_tok[i] = ldci(a.ws.sorted_tok + i);
-      if (a.rout.sorted_slot) a.rout.sorted_slot[i] = ldci(a.ws.sorted_slot + i);
+      if (a.rout.sorted_tok) *gp(a.rout.sorted_tok + i) = ldci(a.ws.sorted_tok + i);
+      if (a.rout.sorted_slot) *gp(a.rout.sorted_slot + i) = ldci(a.ws.sorted_slot + i);
     }
   }
   wg_notify(ev_ptr(a, c.l, EV_ROUTE), -1);
@@ -1386,7 +1387,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
   auto record = [&](int type, uint32_t t_begin) {
     if (tr && threadIdx.x == 0 && tn < a.trace_cap) {
       const uint32_t t_end = (uint32_t)now_ticks();
-      uint32_t* e = tr + (size_t)tn * 8;
+      __attribute__((address_space(1))) uint32_t* e = gp(tr + (size_t)tn * 8);
       e[0] = (uint32_t)type | ((uint32_t)l << 8) | ((uint32_t)(ldu4(q + t).y & 0xffff) << 16);
       e[1] = t_begin;
 #pragma unroll
@@ -1484,7 +1485,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
       }
     }
   }
-  if (tr && threadIdx.x == 0) tr[0] = (uint32_t)(tn - 1);
+  if (tr && threadIdx.x == 0) *gp(tr) = (uint32_t)(tn - 1);
 }
 
 // ---------------------------------------------------------------------------
