@@ -286,59 +286,23 @@ __device__ __forceinline__ WaveItems wave_items(int RG, int NKS, int wave) {
   return it;
 }
 
-// A wave's weight stream for one GEMV pass, as far as another pass needs it
-// to prefetch: the row of this lane in the wave's first item and the item's
-// k range. `on` is false when the wave has no item in that pass.
 constexpr int kRing = 16;   // loads in flight per wave (16 KiB; 128 KiB per workgroup)
-
-template <typename WT>
-struct Stream {
-  const WT* rows;
-  int ks_lo, kmax, nks_c, on;
-};
-
-template <typename WT>
-__device__ __forceinline__ int stream_ofs(const Stream<WT>& st, int ks) {
-  return min((st.ks_lo + ks) * MM<WT>::KSTEP + (int)((threadIdx.x & 63) >> 4) * MM<WT>::EPL, st.kmax);
-}
-
-template <typename WT>
-__device__ __forceinline__ Stream<WT> stream_of(const GemvRows& rw, int R, int K, int wave) {
-  typedef MM<WT> T;
-  const int NKS = (K + T::KSTEP - 1) / T::KSTEP, RG = (R + 15) >> 4;
-  const WaveItems wi = wave_items(RG, NKS, wave);
-  Stream<WT> st;
-  st.on = wi.n > 0;
-  st.rows = row_ptr<WT>(rw, min(min(wi.rg0, RG - 1) * 16 + (int)(threadIdx.x & 15), R - 1), K);
-  st.ks_lo = wi.ks_lo;
-  st.kmax = K - T::EPL;
-  st.nks_c = wi.nks > 0 ? wi.nks - 1 : 0;
-  return st;
-}
-
-template <typename WT>
-__device__ __forceinline__ Stream<WT> no_stream() {
-  Stream<WT> st;
-  st.rows = nullptr;
-  st.ks_lo = st.kmax = st.nks_c = st.on = 0;
-  return st;
-}
 
 // Returns false if the wait was abandoned (nothing was computed). SP: the
 // input rows are carried as bfloat16 hi + lo pairs, two MFMAs per chunk.
 //
-// Ring flow across passes: `pre` says whether this wave's ring already holds
-// the first kRing steps of this pass (issued by the previous pass's last
-// steps); on return it says whether the ring now holds those of `nx`, the
-// pass that follows. So a wave's weight loads run on from one pass into the
-// next without draining while the pass's results are stored and the next
-// input event is awaited. Every item is streamed as a whole number of ring
+// Each wave fills its ring before the input event is awaited, so its first
+// kRing steps stream in during the wait; the ring then flows from one item of
+// the wave into the next. Every item is streamed as a whole number of ring
 // lengths (steps past its end multiply a zero input and re-read its last
-// step), which keeps the slot of a step fixed.
+// step), which keeps the slot of a step fixed; the last block of the pass
+// issues no refills. (Carrying the ring on into the next pass, so that a
+// pass's last steps prefetch the next one, was measured slower: the workgroups
+// that finish a stage early then take HBM bandwidth from the ones that gate
+// the stage's event.)
 template <typename WT, bool SP>
 __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
-                                     const int* wait_ev, int wait_subs, uint4 (&ring)[kRing], bool& pre,
-                                     const Stream<WT>& nx) {
+                                     const int* wait_ev, int wait_subs) {
   typedef MM<WT> T;
   typedef typename T::XT XT;
   constexpr int D = kRing;
@@ -355,13 +319,13 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
   };
   auto kofs = [&](int ks) { return min((wi.ks_lo + ks) * T::KSTEP + kg, kmax); };
 
+  uint4 ring[D];
   const WT* cur = item_rows(0);
   const WT* nxt = item_rows(1);
-  if (!pre && wi.n > 0) {
+  if (wi.n > 0) {
 #pragma unroll
     for (int d = 0; d < D; ++d) ring[d] = ldg16(cur + kofs(min(d, nks_c)));
   }
-  pre = nx.on && wi.n > 0;
   if (!ctx_wait(c, wait_ev, wait_subs)) return false;
   if (in.merge_b0 >= 0)
     stage_attn_merge<WT, SP>(c.a, in, nb, K, Kp, XS, c.s);
@@ -379,43 +343,48 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
     // the input fragments of the next k-step are read from LDS one step ahead
     uint4 xa_n = *reinterpret_cast<const uint4*>(xrow), xl_n = make_uint4(0, 0, 0, 0);
     if (SP) xl_n = *reinterpret_cast<const uint4*>(xrow + XS);
-    // Branch-free body, so the compiler's wait counts stay exact (a branch
+    // one k-step: the input fragment (zero past the item, or for a row >= nb)
+    // times ring slot d, reading the next step's fragment ahead
+    auto step = [&](int ks, int d) {
+      const bool on = xon && ks < nks;
+      uint4 xa = xa_n, xl = xl_n;
+      const int xo = min(ks + 1, nks_c) * T::KSTEP;
+      xa_n = *reinterpret_cast<const uint4*>(xrow + xo);
+      if (SP) xl_n = *reinterpret_cast<const uint4*>(xrow + XS + xo);
+      xa.x = on ? xa.x : 0u;
+      xa.y = on ? xa.y : 0u;
+      xa.z = on ? xa.z : 0u;
+      xa.w = on ? xa.w : 0u;
+      acc = T::mac(xa, ring[d], acc);
+      if (SP) {
+        xl.x = on ? xl.x : 0u;
+        xl.y = on ? xl.y : 0u;
+        xl.z = on ? xl.z : 0u;
+        xl.w = on ? xl.w : 0u;
+        acc = T::mac(xl, ring[d], acc);
+      }
+    };
+    // Branch-free blocks, so the compiler's wait counts stay exact (a branch
     // here makes it wait for every load in flight before each MFMA).
-    for (int ks0 = 0; ks0 < nks_pad; ks0 += D) {
+    const int nrefill = has_next ? nks_pad : nks_pad - D;   // the last block of the pass refills nothing
+    for (int ks0 = 0; ks0 < nrefill; ks0 += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int ks = ks0 + d;
-        const bool on = xon && ks < nks;
-        uint4 xa = xa_n, xl = xl_n;
-        const int xo = min(ks + 1, nks_c) * T::KSTEP;
-        xa_n = *reinterpret_cast<const uint4*>(xrow + xo);
-        if (SP) xl_n = *reinterpret_cast<const uint4*>(xrow + XS + xo);
-        xa.x = on ? xa.x : 0u;
-        xa.y = on ? xa.y : 0u;
-        xa.z = on ? xa.z : 0u;
-        xa.w = on ? xa.w : 0u;
-        acc = T::mac(xa, ring[d], acc);
-        if (SP) {
-          xl.x = on ? xl.x : 0u;
-          xl.y = on ? xl.y : 0u;
-          xl.z = on ? xl.z : 0u;
-          xl.w = on ? xl.w : 0u;
-          acc = T::mac(xl, ring[d], acc);
-        }
-        // refill with the step kRing ahead: of this item, else of the next
-        // item, else of the next pass (else a re-read of the last step)
-        const int nk = ks + D, nn = nk - nks_pad;
-        const bool here = nk < nks_pad, into_item = !here && has_next, into_pass = !here && !has_next && nx.on;
-        const WT* bp = into_item ? nxt : (into_pass ? nx.rows : cur);
-        const int off = here ? kofs(min(nk, nks_c))
-                             : (into_item ? kofs(min(nn, nks_c)) : (into_pass ? stream_ofs(nx, min(nn, nx.nks_c))
-                                                                               : kofs(nks_c)));
-        ring[d] = ldg16(bp + off);
+        step(ks, d);
+        // refill with the step kRing ahead: of this item, else of the next item
+        const int nk = ks + D;
+        const bool here = nk < nks_pad;
+        ring[d] = ldg16((here ? cur : nxt) + kofs(here ? min(nk, nks_c) : min(nk - nks_pad, nks_c)));
         // keep the refill here: left to itself the scheduler sinks all refills
         // to the end of the unrolled body, and the ring degrades to batches
         // that drain to zero loads in flight
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if (!has_next) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) step(nks_pad - D + d, d);
     }
     // D[m][j] of this item's row group: lane (j + 16 * (m / 4)), element m % 4
     const int rg = wi.rg0 + it * wi.rg_step;
@@ -454,9 +423,8 @@ template <typename WT> struct SplitIn { static constexpr bool value = sizeof(WT)
 
 template <typename WT>
 __device__ __forceinline__ bool gemv_any(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
-                                         const int* wev, int wsubs, uint4 (&ring)[kRing], bool& pre,
-                                         const Stream<WT>& nx) {
-  return gemv<WT, SplitIn<WT>::value>(c, rw, R, K, in, nb, wev, wsubs, ring, pre, nx);
+                                         const int* wev, int wsubs) {
+  return gemv<WT, SplitIn<WT>::value>(c, rw, R, K, in, nb, wev, wsubs);
 }
 
 // Input rows per GEMV pass for depth K and R output rows: what the LDS input
@@ -1310,48 +1278,11 @@ __device__ __forceinline__ bool task_combine(const Ctx& c, const int* wev) {
 // ---------------------------------------------------------------------------
 // The persistent kernel
 // ---------------------------------------------------------------------------
-// GEMV task types whose passes can be built ahead of time: their weights do
-// not depend on this step's data, except the grouped expert tasks, whose rows
-// are known once routing is done.
+// Task types that run as GEMV passes.
 __device__ __forceinline__ bool gemv_task(int type) {
   return type == T_QKV || type == T_O || type == T_GU || type == T_DOWN || type == T_ROUTER || type == T_MGU ||
          type == T_MDOWN;
 }
-__device__ __forceinline__ bool chainable(int type, bool routed) {
-  return type == T_QKV || type == T_O || type == T_GU || type == T_DOWN || type == T_ROUTER ||
-         (routed && (type == T_MGU || type == T_MDOWN));
-}
-
-// This wave's stream of the GEMV pass that runs after pass p of queue entry t
-// (layer l) on this workgroup, when that pass's weights can be named now;
-// else none (the next pass then fills its ring itself).
-template <typename WT>
-__device__ __forceinline__ Stream<WT> next_stream(const StepArgs& a, const Lds& s, int wg, const int4* q, int n, int l,
-                                                  int t, int4 task, int p, bool routed) {
-  const int wave = wave_id();
-  Pass ps;
-  {
-    const Ctx c{a, l, wg, s};
-    if (chainable(task.x, routed) && make_pass<WT>(c, task, p + 1, nullptr, ps))
-      return stream_of<WT>(ps.rw, ps.R, ps.K, wave);
-  }
-  int4 nt;
-  int nl = l;
-  if (t + 1 < n) {
-    nt = ldu4(q + t + 1);
-  } else if (l + 1 < a.dm.L) {
-    nt = ldu4(q);
-    nl = l + 1;
-  } else {
-    return no_stream<WT>();
-  }
-  nt.x &= 0xff;
-  if (!chainable(nt.x, nl == l && routed)) return no_stream<WT>();
-  const Ctx c{a, nl, wg, s};
-  if (!make_pass<WT>(c, nt, 0, nullptr, ps)) return no_stream<WT>();
-  return stream_of<WT>(ps.rw, ps.R, ps.K, wave);
-}
-
 template <typename WT>
 __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict__ pa) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
@@ -1429,11 +1360,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
         advance();
         continue;
       }
-      // A run of consecutive GEMV tasks (across layers too): each wave's
-      // weight ring is carried from one pass into the next. It exists only
-      // within the run, so it holds no registers during the other tasks.
-      uint4 ring[kRing];
-      bool pre = false;
+      // a run of consecutive GEMV tasks (across layers too)
       for (;;) {
         const Ctx c{a, l, wg, s};
         const uint32_t t_begin = begin();
@@ -1452,14 +1379,9 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           case T_MDOWN: notify = EV_MDOWN; break;
           default: break;
         }
-        const bool routed = seen(EV_ROUTE, l);
         for (int p = 0; ok; ++p) {
           Pass ps;
           if (!make_pass<WT>(c, task, p, wev, ps)) break;
-          Stream<WT> nx = next_stream<WT>(a, s, wg, q, n, l, t, task, p, routed);
-          // wave 0 stores the pass's outputs and notifies: it must reach its
-          // drain with no weight loads of the next pass in flight
-          if (wave == 0) nx.on = 0;
           // the residual of O (the layer input) / down (h1) is final once this
           // workgroup has seen the event that produced it, or one that fires
           // only after it (every QKV tile waits for the previous layer's down
@@ -1468,7 +1390,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           const bool early = (ps.epi == E_O && (l == 0 || seen(EV_DOWN, l - 1) || seen(EV_QKV, l))) ||
                              (ps.epi == E_DOWN && seen(EV_O, l));
           if (early) load_resid(a, ps, resid);
-          ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs, ring, pre, nx);
+          ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs);
           if (!ok) break;
           if (early) add_resid(s, ps, resid);
           if (wave == 0) epilogue<WT>(c, ps, early);
