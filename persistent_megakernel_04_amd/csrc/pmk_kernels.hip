@@ -255,6 +255,8 @@ __device__ __forceinline__ void stage_attn_merge(const StepArgs& a, const GemvIn
 // streamed one after another. Tiles of fewer than 8 row groups split each row
 // group's k range over 8 / RG waves (their partial sums are added in LDS);
 // tiles of 8 or more give each wave whole row groups rg, rg + 8, ...
+constexpr int kRing = 16;   // weight loads in flight per wave (16 KiB; 128 KiB per workgroup)
+
 struct WaveItems {
   int n;        // items of this wave
   int rg0;      // row group of the first item
@@ -280,13 +282,14 @@ __device__ __forceinline__ WaveItems wave_items(int RG, int NKS, int wave) {
     it.n = busy ? 1 : 0;
     it.rg0 = busy ? wave / ks : 0;
     it.rg_step = 0;
-    it.ks_lo = sl * NKS / ks;
-    it.nks = (sl + 1) * NKS / ks - it.ks_lo;
+    // slices of whole ring lengths, so that no wave pads its range with
+    // dummy steps (the last slice ends at NKS)
+    const int NB = (NKS + kRing - 1) / kRing;
+    it.ks_lo = min(sl * NB / ks * kRing, NKS);
+    it.nks = min((sl + 1) * NB / ks * kRing, NKS) - it.ks_lo;
   }
   return it;
 }
-
-constexpr int kRing = 16;   // loads in flight per wave (16 KiB; 128 KiB per workgroup)
 
 // Returns false if the wait was abandoned (nothing was computed). SP: the
 // input rows are carried as bfloat16 hi + lo pairs, two MFMAs per chunk.
