@@ -119,6 +119,8 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   dm.eps = desc->rms_eps;
   dm.grid = prop.multiProcessorCount;
   dm.moe = moe ? 1 : 0;
+  dm.kstep = desc->dtype == PMK_BF16 ? 32 : 16;
+  dm.xpad = desc->dtype == PMK_BF16 ? 8 : 4;
   const int G = dm.grid;
   dm.qkv_units = (dm.Hq + 2 * dm.Hkv) * dm.d / 2;
   dm.qkv_tiles = std::min(G, dm.qkv_units);
@@ -127,13 +129,29 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   dm.down_tiles = moe ? 0 : std::min(G, dm.H);
   dm.router_tiles = moe ? ceil_div(dm.E, 16) : 0;
   dm.max_tiles = moe ? ceil_div((long)dm.max_batch * dm.k, kMoeBM) + dm.E : 0;
-  // rows per tile must fit the LDS output staging for one input row
-  // a step may put its few attention tasks on workgroups of their own and the
-  // QKV tiles on the others (at least three quarters of the grid)
-  if (2 * ceil_div(dm.qkv_units, std::min(G - G / 4, dm.qkv_units)) > kYsFloats || (!moe && 2 * ceil_div(dm.F, dm.gu_tiles) > kYsFloats) ||
-      ceil_div(dm.H, dm.o_tiles) > kYsFloats) {
-    delete h;
-    return PMK_ERR_UNSUPPORTED;
+  // Dense stages: one input row of the whole depth and a tile's outputs must
+  // fit the LDS (a step may put its few attention tasks on workgroups of their
+  // own and the QKV tiles on the others, at least three quarters of the grid).
+  // Split-K partials: the largest need over batches of up to 16 rows.
+  const int K4[4] = {dm.H, dm.Hq * dm.d, dm.H, dm.F};
+  const int U4[4] = {dm.qkv_units, dm.H, dm.F, dm.H};
+  const int R4[4] = {2, 1, 2, 1};
+  size_t kpart_floats = 16;
+  for (int st = 0; st < 4; ++st) {
+    if (moe && st >= 2) continue;
+    const int tiles_min = std::min(st == 0 ? G - G / 4 : G, U4[st]);
+    const long row_bytes = 4L * (ceil_div(K4[st], dm.kstep) * dm.kstep + dm.xpad);
+    if (row_bytes + 16 + 4L * ceil_div(U4[st], tiles_min) * R4[st] > kXyBytes) {
+      delete h;
+      return PMK_ERR_UNSUPPORTED;
+    }
+    for (int nb = 2; nb <= std::min(dm.max_batch, kMaxNb); ++nb)
+      for (int avail : {G - G / 4, G}) {
+        const StageGeo g = stage_geo(K4[st], U4[st], R4[st], nb, avail, dm.kstep, dm.xpad);
+        if (g.ks > 1)
+          kpart_floats = std::max(kpart_floats, (size_t)g.tiles * g.ks *
+                                                    ((size_t)ceil_div(U4[st], g.tiles) * R4[st] * nb + 16));
+      }
   }
   const long attn_max = (long)dm.max_batch * dm.Hkv * dm.max_chunks;
   dm.max_queue = ceil_div(dm.qkv_tiles, G) + ceil_div(dm.o_tiles, G) + ceil_div(attn_max, G) + 8;
@@ -162,6 +180,8 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
       {(void**)&ws.qlen, (size_t)G * 4},
       {(void**)&ws.err, 64 * 4},
       {(void**)&ws.args, sizeof(StepArgs)},
+      {(void**)&ws.kpart, kpart_floats * 4},
+      {(void**)&ws.tctr, (size_t)4 * G * kCtr * 4},
   };
   if (moe) {
     const std::vector<Part> mp = {
@@ -234,6 +254,10 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     a0.layers = h->d_layers;
     a0.attn_chunk = kMaxChunk;
     a0.qkv_tiles = dm.qkv_tiles;
+    a0.geo[0] = StageGeo{1, dm.qkv_tiles, dm.H};
+    a0.geo[1] = StageGeo{1, dm.o_tiles, dm.Hq * dm.d};
+    a0.geo[2] = StageGeo{1, std::max(dm.gu_tiles, 1), dm.H};
+    a0.geo[3] = StageGeo{1, std::max(dm.down_tiles, 1), std::max(dm.F, 1)};
     if (hipMemcpy(ws.args, &a0, sizeof(a0), hipMemcpyHostToDevice) != hipSuccess) return fail(PMK_ERR_DEVICE);
   }
   if (prepare_main(desc->dtype) != hipSuccess) return fail(PMK_ERR_DEVICE);

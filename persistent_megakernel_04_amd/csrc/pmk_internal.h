@@ -21,13 +21,47 @@ constexpr int kMaxExperts = 512;
 constexpr int kMaxNb = 16;               // batch rows per GEMV pass (MFMA M)
 constexpr int kMaxBatchAll = 1024;       // largest max_batch (prologue LDS)
 
-// LDS layout (bytes): [xs: GEMV inputs | red: cross-wave sums | ys: GEMV outputs | misc]
-constexpr int kXsBytes = 131584;
-constexpr int kRedBytes = 16384;
-constexpr int kYsBytes = 8192;
+// LDS layout (bytes): [xy: a GEMV pass's staged inputs (xs), then its outputs
+// (ys) | red: cross-wave partial sums | misc]. Attention and routing use the xy
+// region as scratch.
+constexpr int kXyBytes = 147968;
+constexpr int kRedBytes = 8192;
 constexpr int kMiscBytes = 2048;
-constexpr int kLdsBytes = kXsBytes + kRedBytes + kYsBytes + kMiscBytes;
-constexpr int kYsFloats = kYsBytes / 4;
+constexpr int kLdsBytes = kXyBytes + kRedBytes + kMiscBytes;
+constexpr int kXsBytes = 131584;         // staged inputs of a pass at most (the rest of xy holds ys)
+constexpr int kYsFloats = 2048;          // outputs of a pass whose residual is loaded ahead (O, down)
+constexpr int kRingK = 16;               // weight loads in flight per wave
+
+// A dense GEMV stage's work split for one step: `ks` slices of the depth K
+// times `tiles` row tiles, one task each. With ks > 1 every task stores its
+// partial sums and the last task of a row tile to finish adds the slices (in
+// slice order) and runs the stage's epilogue. Chosen so that a task's staged
+// input rows (nb rows of its slice, 4 bytes per element: bfloat16 hi + lo, or
+// float) and its outputs fit the xy region; ks = 1 whenever the whole depth
+// fits, always so for a single row. kstep: the k elements of one weight load
+// step (32 bfloat16 or 16 float); xpad: LDS row padding (elements). Slices
+// are whole ring lengths (16 steps) but the last.
+constexpr int kMaxKs = 8;                // K slices of a split stage at most
+struct StageGeo {
+  int ks, tiles, kr;    // kr: slice length (elements); the last slice ends at K
+};
+__host__ __device__ inline StageGeo stage_geo(int K, int units, int urows, int nb, int avail, int kstep, int xpad) {
+  const int grain = kRingK * kstep;
+  for (int ks = 1;; ++ks) {
+    int kr = (K + ks - 1) / ks;
+    kr = (kr + grain - 1) / grain * grain;
+    if (kr > K) kr = K;
+    const int kse = (K + kr - 1) / kr;
+    int tiles = avail / kse;
+    if (tiles > units) tiles = units;
+    if (tiles < 1) tiles = 1;
+    const int rows = (units + tiles - 1) / tiles * urows;
+    const long xs = (long)nb * ((kr + kstep - 1) / kstep * kstep + xpad) * 4;
+    const long need = (xs + 15) / 16 * 16 + (long)rows * nb * 4;
+    if (kse > kMaxKs) return StageGeo{0, 0, 0};   // no split fits: passes over the batch instead
+    if (need <= kXyBytes || kr <= grain) return StageGeo{kse, tiles, kr};
+  }
+}
 
 // Task types of the per-workgroup queue (one layer's worth; replayed per layer).
 enum TaskType : int {
@@ -74,6 +108,7 @@ struct Dims {
   int qkv_tiles, o_tiles, gu_tiles, down_tiles, router_tiles;
   int max_queue;
   int moe;                           // 1 = MoE layers
+  int kstep, xpad;                   // GEMV: k elements per weight load step, LDS row padding (by dtype)
   int max_tiles;                     // MoE: bound on grouped-GEMM row tiles
 };
 
@@ -92,6 +127,8 @@ struct Workspace {
   int* qlen;           // [grid]
   int* err;            // [0] error word, [16] abort flag
   void* args;          // a copy of this step's StepArgs, written by the prologue
+  float* kpart;        // split-K partial sums: [tile][slice][rows nb + 16] of the current stage
+  int* tctr;           // [4][grid * kCtr] per row tile: slices done (reset by the last one)
   // MoE
   float* logits;       // [max_batch][E]
   int* topk_idx;       // [max_batch][k]
@@ -118,6 +155,7 @@ struct StepArgs {
   int attn_chunk;                      // KV positions per attention task this step (set by the prologue)
   int attn_merge_o;                    // 1: O-projection inputs merge the attention partials (set by the prologue)
   int qkv_tiles;                       // QKV tiles this step, on workgroups 0.. (set by the prologue)
+  StageGeo geo[4];                     // QKV, O, gate/up, down split of this step (set by the prologue)
   unsigned long long watchdog_ticks;   // s_memrealtime ticks (100 MHz)
   pmk_routing rout;                    // optional routing outputs (device pointers)
   uint32_t* trace;                     // optional task trace [grid][trace_cap][8], caller-owned

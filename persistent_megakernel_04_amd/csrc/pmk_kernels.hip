@@ -38,9 +38,9 @@ namespace pmk {
 // LDS
 // ---------------------------------------------------------------------------
 struct Lds {
-  void* xs;        // GEMV input rows (MM<WT>::XT), attention scratch, routing scratch
+  void* xs;        // the xy region: a GEMV pass's input rows (MM<WT>::XT) then its outputs
+                   // [R][nb] (see Pass::ys); attention and routing scratch
   float* red;      // cross-wave partial sums
-  float* ys;       // GEMV outputs [R][nb]
   float* rstd;     // [kMaxNb] 1/rms of the staged rows
   float* ssp;      // [kMaxNb][kWaves] per-wave partial sums of squares
   int* flag;       // wait / last-arriver broadcast
@@ -50,9 +50,8 @@ struct Lds {
 __device__ __forceinline__ Lds lds_layout(char* base) {
   Lds s;
   s.xs = base;
-  s.red = reinterpret_cast<float*>(base + kXsBytes);
-  s.ys = reinterpret_cast<float*>(base + kXsBytes + kRedBytes);
-  char* m = base + kXsBytes + kRedBytes + kYsBytes;
+  s.red = reinterpret_cast<float*>(base + kXyBytes);
+  char* m = base + kXyBytes + kRedBytes;
   s.rstd = reinterpret_cast<float*>(m);                   // 16 floats
   s.ssp = reinterpret_cast<float*>(m + 64);               // 128 floats
   s.flag = reinterpret_cast<int*>(m + 64 + 512);          // 1 int
@@ -112,19 +111,21 @@ struct GemvRows {
   const void* base2;   // PAIR: the second matrix
   int r0;              // CONTIG/PAIR: first row; QKV: first rotation unit
   int half;            // PAIR: rows taken from each matrix; QKV: head_dim / 2
+  int ld;              // row stride of the matrix (elements)
+  int k0;              // first column of the pass (a K slice)
 };
 
 template <typename WT>
-__device__ __forceinline__ const WT* row_ptr(const GemvRows& rw, int j, int K) {
-  const WT* b = reinterpret_cast<const WT*>(rw.base);
+__device__ __forceinline__ const WT* row_ptr(const GemvRows& rw, int j) {
+  const WT* b = reinterpret_cast<const WT*>(rw.base) + rw.k0;
   if (rw.mode == ROWS_QKV) {
     // local row 2u is (head h, i), 2u + 1 is (h, i + d/2): the two rows of a rotation pair
     const int unit = rw.r0 + (j >> 1), h = unit / rw.half, i = unit - h * rw.half;
-    return b + (size_t)(h * 2 * rw.half + i + (j & 1) * rw.half) * K;
+    return b + (size_t)(h * 2 * rw.half + i + (j & 1) * rw.half) * rw.ld;
   }
   if (rw.mode == ROWS_PAIR && j >= rw.half)
-    return reinterpret_cast<const WT*>(rw.base2) + (size_t)(rw.r0 + j - rw.half) * K;
-  return b + (size_t)(rw.r0 + j) * K;
+    return reinterpret_cast<const WT*>(rw.base2) + rw.k0 + (size_t)(rw.r0 + j - rw.half) * rw.ld;
+  return b + (size_t)(rw.r0 + j) * rw.ld;
 }
 
 struct GemvIn {
@@ -132,7 +133,7 @@ struct GemvIn {
   int ld;              // row stride (elements)
   const int* gather;   // nullable: staged row m <- src row gather[m] (device-coherent)
   const float* gain;   // nullable: elementwise gain (RMSNorm weight)
-  int norm;            // compute rstd
+  int norm;            // 1: rstd[m] = 1 / rms of the staged rows; 2: leave their raw sum of squares
   float eps;
   int merge_b0;        // >= 0: the rows are the attention outputs of requests merge_b0.. (merged from partials)
 };
@@ -191,7 +192,7 @@ __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int 
   if (in.norm && threadIdx.x < nb) {
     float ss = 0.f;
     for (int w = 0; w < kWaves; ++w) ss += s.ssp[threadIdx.x * kWaves + w];
-    s.rstd[threadIdx.x] = 1.0f / sqrtf(ss / (float)K + in.eps);
+    s.rstd[threadIdx.x] = in.norm == 2 ? ss : 1.0f / sqrtf(ss / (float)K + in.eps);
   }
   __syncthreads();
 }
@@ -305,7 +306,7 @@ __device__ __forceinline__ WaveItems wave_items(int RG, int NKS, int wave) {
 // the stage's event.)
 template <typename WT, bool SP>
 __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
-                                     const int* wait_ev, int wait_subs) {
+                                     const int* wait_ev, int wait_subs, float* ys) {
   typedef MM<WT> T;
   typedef typename T::XT XT;
   constexpr int D = kRing;
@@ -318,7 +319,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
   const int nks_pad = nks > D ? (nks + D - 1) / D * D : D;
   auto item_rows = [&](int it) -> const WT* {
     const int rg = min(wi.rg0 + min(it, max(wi.n - 1, 0)) * wi.rg_step, RG - 1);
-    return row_ptr<WT>(rw, min(rg * 16 + mrow, R - 1), K);   // padded rows repeat a valid row
+    return row_ptr<WT>(rw, min(rg * 16 + mrow, R - 1));   // padded rows repeat a valid row
   };
   auto kofs = [&](int ks) { return min((wi.ks_lo + ks) * T::KSTEP + kg, kmax); };
 
@@ -395,7 +396,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
     for (int e = 0; e < 4; ++e) {
       const int m = grp * 4 + e, j = rg * 16 + mrow;
       if (KSPL == 1) {
-        if (m < nb && j < R) c.s.ys[j * nb + m] = acc[e];
+        if (m < nb && j < R) ys[j * nb + m] = acc[e];
       } else if (m < nb) {
         c.s.red[(wave * nb + m) * 16 + mrow] = acc[e];
       }
@@ -411,7 +412,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
       float sum = 0.f;
       for (int sl = 0; sl < KSPL; ++sl) sum += c.s.red[((rg * KSPL + sl) * nb + mm) * 16 + jj];
       const int j = rg * 16 + jj;
-      if (j < R) c.s.ys[j * nb + mm] = sum;
+      if (j < R) ys[j * nb + mm] = sum;
     }
     __syncthreads();
   }
@@ -426,19 +427,23 @@ template <typename WT> struct SplitIn { static constexpr bool value = sizeof(WT)
 
 template <typename WT>
 __device__ __forceinline__ bool gemv_any(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
-                                         const int* wev, int wsubs) {
-  return gemv<WT, SplitIn<WT>::value>(c, rw, R, K, in, nb, wev, wsubs);
+                                         const int* wev, int wsubs, float* ys) {
+  return gemv<WT, SplitIn<WT>::value>(c, rw, R, K, in, nb, wev, wsubs, ys);
 }
 
-// Input rows per GEMV pass for depth K and R output rows: what the LDS input
-// and output staging hold, at most 16 (one MFMA row block).
+// Bytes of one staged input row of depth K in LDS (bfloat16 hi + lo, or float).
 template <typename WT>
-__device__ __forceinline__ int pass_rows(int K, int R) {
+__device__ __forceinline__ int xs_row_bytes(int K) {
   typedef MM<WT> T;
   const int Kp = ((K + T::KSTEP - 1) / T::KSTEP) * T::KSTEP;
-  int nb = kXsBytes / ((SplitIn<WT>::value ? 2 : 1) * (Kp + T::XPAD) * (int)sizeof(typename T::XT));
-  const int ny = kYsFloats / R;
-  if (ny < nb) nb = ny;
+  return (SplitIn<WT>::value ? 2 : 1) * (Kp + T::XPAD) * (int)sizeof(typename T::XT);
+}
+
+// Input rows per GEMV pass for depth K and R output rows: what the xy region
+// holds (the rows, then the [R][nb] outputs), at most 16 (one MFMA row block).
+template <typename WT>
+__device__ __forceinline__ int pass_rows(int K, int R) {
+  const int nb = (kXyBytes - 16) / (xs_row_bytes<WT>(K) + 4 * R);
   return nb < kMaxNb ? nb : kMaxNb;
 }
 
@@ -454,7 +459,7 @@ enum Epi : int { E_QKV = 0, E_O, E_GU, E_DOWN, E_ROUTER, E_MGU, E_MDOWN };
 struct Pass {
   GemvRows rw;
   GemvIn in;
-  int R, K, nb;
+  int R, K, nb;     // output rows, depth of this pass (its K slice), input rows
   const int* wev;   // event the pass waits on (after its weights are in flight)
   int wsubs;        // its sub-counters (0: a bare counter)
   int epi;
@@ -462,9 +467,23 @@ struct Pass {
   int r0;           // first rotation unit (QKV), output row, or expert column
   int n;            // QKV: rotation units; GU / MoE gate-up: rows per matrix; else rows
   int e;            // MoE: expert
+  int stage;        // dense stage 0..3 (QKV, O, gate/up, down), -1 otherwise
+  int tile, slice, ks;   // row tile, K slice, slices of the stage (1: no split)
+  int kfull;        // the stage's whole depth
+  int rs;           // split-K record stride (floats): outputs of the stage's largest tile + 16
+  float* ys;        // the pass's outputs [R][nb] in LDS, after its staged inputs
 };
 
-// Pass p of a GEMV task; false once the task has no pass p.
+// Row tile `tile` of `units` units split in `tiles`: first unit and count.
+__device__ __forceinline__ int2 tile_units(int tile, int units, int tiles) {
+  const int u0 = (int)((long)tile * units / tiles);
+  return make_int2(u0, (int)((long)(tile + 1) * units / tiles) - u0);
+}
+
+// Pass p of a GEMV task; false once the task has no pass p. Dense stages take
+// their split from this step's geometry: task (tile, K slice) covers all
+// batch rows in one pass when the depth is split, else passes of what the LDS
+// holds (a task whose stage is not split has slice 0).
 template <typename WT>
 __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, const int* wev, Pass& ps) {
   const StepArgs& a = c.a;
@@ -474,59 +493,76 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   ps.wev = p == 0 ? wev : nullptr;
   ps.wsubs = kSubs;
   ps.e = 0;
+  ps.stage = -1;
+  ps.tile = tile;
+  ps.slice = 0;
+  ps.ks = 1;
+  // the K slice of a dense task, its rows per pass and first batch row
+  int k0 = 0, kn = 0, b0 = 0, nbb = 0;
+  auto dense = [&](int stage, int K, int R, int units, int urows) -> bool {
+    const StageGeo& g = a.geo[stage];
+    k0 = task.z * g.kr;
+    kn = min(K, k0 + g.kr) - k0;
+    nbb = g.ks > 1 ? kMaxNb : pass_rows<WT>(kn, R);
+    b0 = p * nbb;
+    if (b0 >= a.batch || (g.ks > 1 && p > 0)) return false;
+    ps.stage = stage;
+    ps.slice = task.z;
+    ps.ks = g.ks;
+    ps.kfull = K;
+    ps.K = kn;
+    ps.R = R;
+    ps.nb = min(nbb, a.batch - b0);
+    ps.b0 = b0;
+    ps.rs = (units + g.tiles - 1) / g.tiles * urows * ps.nb + 16;
+    return true;
+  };
   switch (task.x) {
     case T_QKV: {   // RMSNorm1 + QKV rotation pairs of the tile
-      const int u0 = (int)((long)tile * dm.qkv_units / a.qkv_tiles);
-      const int nu = (int)((long)(tile + 1) * dm.qkv_units / a.qkv_tiles) - u0;
-      const int nbb = pass_rows<WT>(dm.H, 2 * nu), b0 = p * nbb;
-      if (b0 >= a.batch) return false;
-      ps.rw = GemvRows{ROWS_QKV, ldp(&Lp->w_qkv), nullptr, u0, dm.d >> 1};
-      ps.in = GemvIn{a.hidden + (size_t)b0 * dm.H, dm.H, nullptr, ldp(&Lp->attn_norm), 1, dm.eps, -1};
-      ps.R = 2 * nu; ps.K = dm.H; ps.nb = min(nbb, a.batch - b0);
-      ps.epi = E_QKV; ps.b0 = b0; ps.r0 = u0; ps.n = nu;
-      return true;
+      const int2 u = tile_units(tile, dm.qkv_units, a.geo[0].tiles);
+      if (!dense(0, dm.H, 2 * u.y, dm.qkv_units, 2)) return false;
+      ps.rw = GemvRows{ROWS_QKV, ldp(&Lp->w_qkv), nullptr, u.x, dm.d >> 1, dm.H, k0};
+      ps.in = GemvIn{a.hidden + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->attn_norm) + k0, ps.ks > 1 ? 2 : 1,
+                     dm.eps, -1};
+      ps.epi = E_QKV; ps.r0 = u.x; ps.n = u.y;
+      break;
     }
     case T_O: {     // O-projection rows of the tile
       const int K = dm.Hq * dm.d;
-      const int r0 = (int)((long)tile * dm.H / dm.o_tiles), R = (int)((long)(tile + 1) * dm.H / dm.o_tiles) - r0;
-      const int nbb = pass_rows<WT>(K, R), b0 = p * nbb;
-      if (b0 >= a.batch) return false;
-      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_o), nullptr, r0, 0};
-      ps.in = GemvIn{a.ws.o + (size_t)b0 * K, K, nullptr, nullptr, 0, 0.f, a.attn_merge_o ? b0 : -1};
-      ps.R = R; ps.K = K; ps.nb = min(nbb, a.batch - b0);
-      ps.epi = E_O; ps.b0 = b0; ps.r0 = r0; ps.n = R;
-      return true;
+      const int2 u = tile_units(tile, dm.H, a.geo[1].tiles);
+      if (!dense(1, K, u.y, dm.H, 1)) return false;
+      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_o), nullptr, u.x, 0, K, k0};
+      ps.in = GemvIn{a.ws.o + (size_t)b0 * K + k0, K, nullptr, nullptr, 0, 0.f, a.attn_merge_o ? b0 : -1};
+      ps.epi = E_O; ps.r0 = u.x; ps.n = u.y;
+      break;
     }
     case T_GU: {    // RMSNorm2 + gate and up rows of the tile
-      const int r0 = (int)((long)tile * dm.F / dm.gu_tiles), Rh = (int)((long)(tile + 1) * dm.F / dm.gu_tiles) - r0;
-      const int nbb = pass_rows<WT>(dm.H, 2 * Rh), b0 = p * nbb;
-      if (b0 >= a.batch) return false;
-      ps.rw = GemvRows{ROWS_PAIR, ldp(&Lp->w_gate), ldp(&Lp->w_up), r0, Rh};
-      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
-      ps.R = 2 * Rh; ps.K = dm.H; ps.nb = min(nbb, a.batch - b0);
-      ps.epi = E_GU; ps.b0 = b0; ps.r0 = r0; ps.n = Rh;
-      return true;
+      const int2 u = tile_units(tile, dm.F, a.geo[2].tiles);
+      if (!dense(2, dm.H, 2 * u.y, dm.F, 2)) return false;
+      ps.rw = GemvRows{ROWS_PAIR, ldp(&Lp->w_gate), ldp(&Lp->w_up), u.x, u.y, dm.H, k0};
+      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->ffn_norm) + k0, ps.ks > 1 ? 2 : 1,
+                     dm.eps, -1};
+      ps.epi = E_GU; ps.r0 = u.x; ps.n = u.y;
+      break;
     }
     case T_DOWN: {  // down-projection rows of the tile
-      const int r0 = (int)((long)tile * dm.H / dm.down_tiles), R = (int)((long)(tile + 1) * dm.H / dm.down_tiles) - r0;
-      const int nbb = pass_rows<WT>(dm.F, R), b0 = p * nbb;
-      if (b0 >= a.batch) return false;
-      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_down), nullptr, r0, 0};
-      ps.in = GemvIn{a.ws.act + (size_t)b0 * dm.F, dm.F, nullptr, nullptr, 0, 0.f, -1};
-      ps.R = R; ps.K = dm.F; ps.nb = min(nbb, a.batch - b0);
-      ps.epi = E_DOWN; ps.b0 = b0; ps.r0 = r0; ps.n = R;
-      return true;
+      const int2 u = tile_units(tile, dm.H, a.geo[3].tiles);
+      if (!dense(3, dm.F, u.y, dm.H, 1)) return false;
+      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_down), nullptr, u.x, 0, dm.F, k0};
+      ps.in = GemvIn{a.ws.act + (size_t)b0 * dm.F + k0, dm.F, nullptr, nullptr, 0, 0.f, -1};
+      ps.epi = E_DOWN; ps.r0 = u.x; ps.n = u.y;
+      break;
     }
     case T_ROUTER: {  // RMSNorm2 + router rows [16 y, 16 y + 16) for the token block [16 z, 16 z + 16)
       const int bend = min(a.batch, (task.z + 1) * kMaxNb);
-      const int nbb = pass_rows<WT>(dm.H, 16), b0 = task.z * kMaxNb + p * nbb;
-      if (b0 >= bend) return false;
+      const int nbr = pass_rows<WT>(dm.H, 16), br = task.z * kMaxNb + p * nbr;
+      if (br >= bend) return false;
       const int r0 = tile * 16;
-      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_router), nullptr, r0, 0};
-      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H, dm.H, nullptr, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
-      ps.R = min(16, dm.E - r0); ps.K = dm.H; ps.nb = min(nbb, bend - b0);
-      ps.epi = E_ROUTER; ps.b0 = b0; ps.r0 = r0; ps.n = ps.R;
-      return true;
+      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_router), nullptr, r0, 0, dm.H, 0};
+      ps.in = GemvIn{a.ws.h1 + (size_t)br * dm.H, dm.H, nullptr, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
+      ps.R = min(16, dm.E - r0); ps.K = dm.H; ps.kfull = dm.H; ps.nb = min(nbr, bend - br);
+      ps.epi = E_ROUTER; ps.b0 = br; ps.r0 = r0; ps.n = ps.R;
+      break;
     }
     case T_MGU: {   // grouped gate/up task i = (row tile i / sg, Fe slice i % sg) of this workgroup's share
       const int i = c.wg + p * dm.grid;
@@ -536,12 +572,12 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int f0 = (int)((long)sl * dm.Fe / sg), Rh = (int)((long)(sl + 1) * dm.Fe / sg) - f0;
       const size_t eo = (size_t)e * dm.Fe * dm.H;
       ps.rw = GemvRows{ROWS_PAIR, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_gate)) + eo,
-                       reinterpret_cast<const WT*>(ldp(&Lp->w_exp_up)) + eo, f0, Rh};
+                       reinterpret_cast<const WT*>(ldp(&Lp->w_exp_up)) + eo, f0, Rh, dm.H, 0};
       // the tile's rows: its routed tokens' FFN inputs (RMSNorm2 of h1), gathered
       ps.in = GemvIn{a.ws.h1, dm.H, a.ws.sorted_tok + row0, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
-      ps.R = 2 * Rh; ps.K = dm.H; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
+      ps.R = 2 * Rh; ps.K = dm.H; ps.kfull = dm.H; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
       ps.epi = E_MGU; ps.b0 = row0; ps.r0 = f0; ps.n = Rh; ps.e = e;
-      return true;
+      break;
     }
     case T_MDOWN: {  // grouped down task i = (row tile i / sd, H slice i % sd); waits on its expert's counter
       const int i = c.wg + p * dm.grid;
@@ -549,17 +585,20 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int sd = ldsu(a.ws.moe_info + 3), t = i / sd, sl = i - t * sd;
       const int e = ldsu(a.ws.tile_info + 2 * t), row0 = ldsu(a.ws.tile_info + 2 * t + 1);
       const int h0 = (int)((long)sl * dm.H / sd), R = (int)((long)(sl + 1) * dm.H / sd) - h0;
-      ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_down)) + (size_t)e * dm.H * dm.Fe, nullptr, h0,
-                       0};
+      ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_down)) + (size_t)e * dm.H * dm.Fe,
+                       nullptr, h0, 0, dm.Fe, 0};
       ps.in = GemvIn{a.ws.mact + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f, -1};
-      ps.R = R; ps.K = dm.Fe; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
+      ps.R = R; ps.K = dm.Fe; ps.kfull = dm.Fe; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
       ps.wev = a.ws.ectr + ((size_t)c.l * dm.E + e) * kCtr;
       ps.wsubs = 0;
       ps.epi = E_MDOWN; ps.b0 = row0; ps.r0 = h0; ps.n = R; ps.e = e;
-      return true;
+      break;
     }
     default: return false;
   }
+  ps.ys = reinterpret_cast<float*>(reinterpret_cast<char*>(c.s.xs) +
+                                   (ps.nb * xs_row_bytes<WT>(ps.K) + 15) / 16 * 16);
+  return true;
 }
 
 // The residual an O / down pass adds (hidden, resp. h1): thread t holds
@@ -582,13 +621,57 @@ __device__ __forceinline__ void load_resid(const StepArgs& a, const Pass& ps, fl
     }
   }
 }
-__device__ __forceinline__ void add_resid(const Lds& s, const Pass& ps, const float (&r)[kResid]) {
+__device__ __forceinline__ void add_resid(const Pass& ps, const float (&r)[kResid]) {
 #pragma unroll
   for (int k = 0; k < kResid; ++k) {
     const int idx = threadIdx.x + k * kBlock;
-    if (idx < ps.n * ps.nb) s.ys[idx] += r[k];   // ys is [R][nb]: idx = j nb + m
+    if (idx < ps.n * ps.nb) ps.ys[idx] += r[k];   // ys is [R][nb]: idx = j nb + m
   }
   __syncthreads();
+}
+
+// Split-K: store this slice's partial sums (ys, and for a normed stage the
+// rows' raw sums of squares over the slice), count the slice done, and let
+// the last slice task of the row tile add every slice, in slice order (its
+// own from LDS), into ys and turn the sums of squares into 1 / rms over the
+// whole depth. Returns whether this task is that last one (the others have
+// nothing more to do for the tile).
+__device__ __forceinline__ bool reduce_slices(const Ctx& c, const Pass& ps) {
+  const StepArgs& a = c.a;
+  const int tid = threadIdx.x, n = ps.R * ps.nb, rs = ps.rs;
+  const bool normed = ps.in.norm != 0;
+  float* part = a.ws.kpart + (size_t)ps.tile * ps.ks * rs;
+  for (int i = tid; i < n; i += kBlock) stc(part + ps.slice * rs + i, ps.ys[i]);
+  if (normed && tid < ps.nb) stc(part + ps.slice * rs + n + tid, c.s.rstd[tid]);
+  vm_drain();
+  __syncthreads();
+  if (tid == 0) {
+    int* ctr = a.ws.tctr + ((size_t)ps.stage * a.dm.grid + ps.tile) * kCtr;
+    const int last = atomic_add_relaxed(ctr, 1) == ps.ks - 1;
+    if (last) stci(ctr, 0);   // every slice has counted: ready for this stage of the next layer
+    *c.s.flag = last;
+  }
+  __syncthreads();
+  if (!__builtin_amdgcn_readfirstlane(*c.s.flag)) return false;
+  // every element's slices are loaded together, then added in order
+  for (int i = tid; i < n + 16; i += kBlock) {
+    const bool row = i < n, sq = !row && normed && i - n < ps.nb;
+    if (!row && !sq) continue;
+    float v[kMaxKs];
+#pragma unroll
+    for (int sl = 0; sl < kMaxKs; ++sl)
+      v[sl] = (sl < ps.ks && sl != ps.slice) ? ldc(part + sl * rs + i) : 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kMaxKs; ++sl)
+      if (sl < ps.ks) sum += sl == ps.slice ? (row ? ps.ys[i] : c.s.rstd[i - n]) : v[sl];
+    if (row)
+      ps.ys[i] = sum;
+    else
+      c.s.rstd[i - n] = 1.0f / sqrtf(sum / (float)ps.kfull + ps.in.eps);
+  }
+  __syncthreads();
+  return true;
 }
 
 // Wave 0 alone consumes a pass's result (ys[j][m], rstd[m] in LDS) and stores
@@ -599,7 +682,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   const int nb = ps.nb, b0 = ps.b0, lane = threadIdx.x & 63;
-  const float* ys = c.s.ys;
+  const float* ys = ps.ys;
   switch (ps.epi) {
     case E_QKV: {   // RoPE at each request's position, then q/k/v out and the K/V append
       const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
@@ -1382,6 +1465,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           case T_MDOWN: notify = EV_MDOWN; break;
           default: break;
         }
+        bool done = true;   // this task finished its row tile (not so for a split-K slice that was not the last)
         for (int p = 0; ok; ++p) {
           Pass ps;
           if (!make_pass<WT>(c, task, p, wev, ps)) break;
@@ -1390,17 +1474,25 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           // only after it (every QKV tile waits for the previous layer's down
           // stage): load it before waiting
           float resid[kResid];
-          const bool early = (ps.epi == E_O && (l == 0 || seen(EV_DOWN, l - 1) || seen(EV_QKV, l))) ||
-                             (ps.epi == E_DOWN && seen(EV_O, l));
+          const bool early = ps.R * ps.nb <= kYsFloats &&
+                             ((ps.epi == E_O && (l == 0 || seen(EV_DOWN, l - 1) || seen(EV_QKV, l))) ||
+                              (ps.epi == E_DOWN && seen(EV_O, l)));
           if (early) load_resid(a, ps, resid);
-          ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs);
+          ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs, ps.ys);
           if (!ok) break;
-          if (early) add_resid(s, ps, resid);
+          if (ps.ks > 1 && !reduce_slices(c, ps)) {
+            done = false;
+            break;
+          }
+          if (early) add_resid(ps, resid);
           if (wave == 0) epilogue<WT>(c, ps, early);
           if (threadIdx.x == 0) s.tclk[5] = (uint32_t)now_ticks();
         }
         if (!ok) return;
-        if (notify >= 0 && wave == 0) wave_notify(ev_ptr(a, l, notify), wg & (kSubs - 1));
+        // dense stages notify per row tile (by the last slice of a split tile), the others per workgroup
+        const bool dense = task.x == T_QKV || task.x == T_O || task.x == T_GU || task.x == T_DOWN;
+        const int sub = (dense ? task.y : wg) & (kSubs - 1);
+        if (done && notify >= 0 && wave == 0) wave_notify(ev_ptr(a, l, notify), sub);
         record(task.x, t_begin);
         advance();
         if (l >= dm.L) break;
@@ -1448,6 +1540,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   const int tid = threadIdx.x, B = a.batch, G = dm.grid;
   __shared__ int bad;
   __shared__ int total_attn, merge_s, qkv_tiles_s, attn_wg0_s;
+  __shared__ StageGeo geo_s[4];
   __shared__ int cb[kMaxBatchAll + 1];
   StepArgs* copy = reinterpret_cast<StepArgs*>(a.ws.args);
   if (tid == 0) {
@@ -1514,7 +1607,19 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     // every workgroup.
     const int own = (merge && total_attn <= G / 4) ? total_attn : 0;
     attn_wg0_s = own ? G - own : G;
-    qkv_tiles_s = min(G - own, dm.qkv_units);
+    // each dense stage's split (see stage_geo): up to 16 rows, one pass over
+    // K slices that fit the LDS; beyond, passes of rows over the whole depth
+    const int K4[4] = {dm.H, dm.Hq * dm.d, dm.H, dm.F};
+    const int U4[4] = {dm.qkv_units, dm.H, dm.F, dm.H};
+    const int R4[4] = {2, 1, 2, 1};
+    for (int st = 0; st < 4; ++st) {
+      const int avail = st == 0 ? G - own : G;
+      StageGeo g = B <= kMaxNb ? stage_geo(K4[st], U4[st], R4[st], B, avail, dm.kstep, dm.xpad) : StageGeo{0, 0, 0};
+      if (g.ks == 0) g = StageGeo{1, min(avail, U4[st]), K4[st]};
+      geo_s[st] = g;
+      copy->geo[st] = g;
+    }
+    qkv_tiles_s = geo_s[0].tiles;
     copy->qkv_tiles = qkv_tiles_s;
   }
   __syncthreads();
@@ -1529,7 +1634,12 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       ++n;
     };
     const int aw0 = attn_wg0_s;
-    for (int t = w; t < qkv_tiles_s; t += G) push(make_int4(T_QKV, t, 0, 0));
+    // task i of a dense stage: row tile i / ks, K slice i % ks, on workgroup i % G
+    auto stage_tasks = [&](int type, int st) {
+      const StageGeo g = geo_s[st];
+      for (int i = w; i < g.tiles * g.ks; i += G) push(make_int4(type, i / g.ks, i % g.ks, 0));
+    };
+    stage_tasks(T_QKV, 0);
     for (int i = aw0 < G ? w - aw0 : w; i >= 0 && i < total_attn; i += (aw0 < G ? total_attn : G)) {
       int lo = 0, hi = B;   // find b: Hkv*cb[b] <= i < Hkv*cb[b+1]
       while (hi - lo > 1) {
@@ -1539,10 +1649,10 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       const int r = i - dm.Hkv * cb[lo], nc = cb[lo + 1] - cb[lo];
       push(make_int4(T_ATTN | (i << 8), lo, r / nc, r % nc));
     }
-    for (int t = w; t < dm.o_tiles; t += G) push(make_int4(T_O, t, 0, 0));
+    stage_tasks(T_O, 1);
     if (!dm.moe) {
-      for (int t = w; t < dm.gu_tiles; t += G) push(make_int4(T_GU, t, 0, 0));
-      for (int t = w; t < dm.down_tiles; t += G) push(make_int4(T_DOWN, t, 0, 0));
+      stage_tasks(T_GU, 2);
+      stage_tasks(T_DOWN, 3);
     } else {
       for (int i = w; i < router_tasks; i += G) push(make_int4(T_ROUTER, i % dm.router_tiles, i / dm.router_tiles, 0));
       if (w == G - 1) push(make_int4(T_ROUTE, 0, 0, 0));
@@ -1558,18 +1668,22 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     const int e = idx % EV_COUNT;
     int* ev = a.ws.ev + (size_t)idx * kEvInts;
     switch (e) {
-      case EV_QKV: arm_tiles(ev, qkv_tiles_s, G); break;
+      // dense stages: one notifier per row tile, on sub-counter tile % kSubs
+      case EV_QKV: arm_indexed(ev, geo_s[0].tiles); break;
       // one notifier per chunk task (partials merged by the O-projection), or per (request, KV head)
       case EV_ATTN: arm_indexed(ev, merge_s ? total_attn : B * dm.Hkv); break;
-      case EV_O: arm_tiles(ev, dm.o_tiles, G); break;
-      case EV_GU: arm_tiles(ev, dm.moe ? 0 : dm.gu_tiles, G); break;
-      case EV_DOWN: arm_tiles(ev, dm.moe ? G : dm.down_tiles, G); break;   // MoE: one combine slot per workgroup
+      case EV_O: arm_indexed(ev, geo_s[1].tiles); break;
+      case EV_GU: arm_indexed(ev, dm.moe ? 0 : geo_s[2].tiles); break;
+      case EV_DOWN:   // MoE: one combine slot per workgroup
+        if (dm.moe) arm_tiles(ev, G, G); else arm_indexed(ev, geo_s[3].tiles);
+        break;
       case EV_ROUTER: arm_tiles(ev, router_tasks, G); break;
       case EV_ROUTE: arm_flat(ev, dm.moe ? 1 : 0); break;
       case EV_MDOWN: arm_tiles(ev, dm.moe ? G : 0, G); break;
       default: arm_flat(ev, 0); break;
     }
   }
+  for (int idx = tid; idx < 4 * G; idx += blockDim.x) a.ws.tctr[idx * kCtr] = 0;
   for (int idx = tid; idx < dm.L * B * dm.Hkv; idx += blockDim.x) {
     const int l = idx / (B * dm.Hkv), rem = idx - l * B * dm.Hkv, b = rem / dm.Hkv, g = rem - b * dm.Hkv;
     a.ws.mctr[(((size_t)l * dm.max_batch + b) * dm.Hkv + g) * kCtr] = cb[b + 1] - cb[b];

@@ -162,3 +162,27 @@ def test_70b_shape_four_layers_b8_sampled(orc):
     lens = synth.ragged_lengths(8, 8192, 16384, ("c5_70b", "lens", 8))
     case = build_case(w, 8, lens, n_layers=4, max_seq=int(lens.max()) + 2, tag="t10")
     check_dense(orc, case, w.tol, requests=[0, 5])
+
+
+@pytest.mark.parametrize("B", [8, 12, 16])
+def test_8b_shape_split_k_every_request(orc, B):
+    """Batches whose staged inputs outgrow the LDS: the projections run as K
+    slices whose partial sums the last slice task of each row tile adds (down
+    in 4 to 7 slices, the 4096-deep projections in 2 at batch 12 and 16).
+    Two layers, every request and every output element against the oracle."""
+    w = synth.get_workload("c3_8b_sweep")
+    lens = synth.ragged_lengths(B, 512, 2048, ("c3_8b_sweep", "split_k", B))
+    case = build_case(w, B, lens, n_layers=2, max_seq=int(lens.max()) + 2, tag=f"t11_{B}")
+    check_dense(orc, case, w.tol)
+
+
+F32_MID = synth.Workload(name="f32_mid", dtype="f32", n_layers=2, hidden=1024, n_q_heads=8, n_kv_heads=2,
+                         head_dim=64, ffn_dim=4096, tol=1e-5)
+
+
+def test_f32_split_k_batch16(orc):
+    """float32 weights at batch 16: the 4096-deep down projection's inputs
+    (256 KiB staged) take two K slices; the result stays at float32 accuracy."""
+    lens = synth.ragged_lengths(16, 1, 300, ("f32_mid", "lens"))
+    case = build_case(F32_MID, 16, lens, max_seq=302, tag="t12")
+    check_dense(orc, case, F32_MID.tol)
