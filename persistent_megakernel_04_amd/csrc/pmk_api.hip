@@ -115,12 +115,16 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   dm.L = desc->n_layers; dm.H = desc->hidden; dm.Hq = desc->n_q_heads; dm.Hkv = desc->n_kv_heads;
   dm.d = desc->head_dim; dm.F = desc->ffn_dim; dm.E = desc->n_experts; dm.k = desc->top_k;
   dm.Fe = desc->expert_ffn_dim; dm.max_batch = desc->max_batch; dm.max_seq = desc->max_seq;
-  dm.max_chunks = ceil_div(desc->max_seq, kMinChunk);
+  // attention partial slots per (request, KV head): chunks of kMinChunk, or
+  // streamed pieces of at least that many positions, one more when a range
+  // starts inside a workgroup's share
+  dm.max_chunks = ceil_div(desc->max_seq, kMinChunk) + 1;
   dm.eps = desc->rms_eps;
   dm.grid = prop.multiProcessorCount;
   dm.moe = moe ? 1 : 0;
   dm.kstep = desc->dtype == PMK_BF16 ? 32 : 16;
   dm.xpad = desc->dtype == PMK_BF16 ? 8 : 4;
+  dm.attn_mm = desc->dtype == PMK_BF16 && dm.d == 128 && dm.Hq / dm.Hkv <= 8;
   const int G = dm.grid;
   dm.qkv_units = (dm.Hq + 2 * dm.Hkv) * dm.d / 2;
   dm.qkv_tiles = std::min(G, dm.qkv_units);
@@ -154,7 +158,9 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
       }
   }
   const long attn_max = (long)dm.max_batch * dm.Hkv * dm.max_chunks;
-  dm.max_queue = ceil_div(dm.qkv_tiles, G) + ceil_div(dm.o_tiles, G) + ceil_div(attn_max, G) + 8;
+  // a workgroup's attention share may also hold one piece of every (request, KV head)
+  dm.max_queue = ceil_div(dm.qkv_tiles, G) + ceil_div(dm.o_tiles, G) + ceil_div(attn_max, G) +
+                 dm.max_batch * dm.Hkv + 8;
   if (moe)
     dm.max_queue += ceil_div((long)dm.router_tiles * ceil_div(dm.max_batch, kMaxNb), G) + 4;
   else

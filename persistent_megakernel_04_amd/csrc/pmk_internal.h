@@ -74,7 +74,8 @@ enum TaskType : int {
   T_ROUTE = 7,    // top-k, gates, expert grouping, expert-event arming (one workgroup)
   T_MGU = 8,      // this workgroup's share of the grouped gate/up GEMM tasks
   T_MDOWN = 9,    // this workgroup's share of the grouped down GEMM tasks
-  T_COMBINE = 10  // this workgroup's share of the per-token gated combine (MoE layer output)
+  T_COMBINE = 10, // this workgroup's share of the per-token gated combine (MoE layer output)
+  T_ATTS = 11     // x >> 8: piece | pieces << 12, y = b | g << 16, z..w: positions: streamed attention piece
 };
 
 // Events of one layer. Each event is a block of kEvInts ints: [0] is the
@@ -109,6 +110,7 @@ struct Dims {
   int max_queue;
   int moe;                           // 1 = MoE layers
   int kstep, xpad;                   // GEMV: k elements per weight load step, LDS row padding (by dtype)
+  int attn_mm;                       // 1: matrix-core attention (bfloat16 KV, head_dim 128, <= 8 heads per KV head)
   int max_tiles;                     // MoE: bound on grouped-GEMM row tiles
 };
 

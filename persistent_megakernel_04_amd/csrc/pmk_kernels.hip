@@ -1147,6 +1147,188 @@ __device__ __forceinline__ bool task_attn_mm(const Ctx& c, int b, int g, int ci,
   return attn_finish<D>(c, b, g, ci, tix, nc, G, sw);
 }
 
+// Streamed split-K attention for bfloat16 KV with head_dim 128 and at most 8
+// query heads per KV head: positions [p0, p1) of request b, KV head g, the
+// piece `piece` of the npieces the (b, g) positions were cut into. The piece
+// is cut into 16-position tiles dealt to the waves in turn; a wave streams
+// its tiles through two register buffers (the next tile's K and V rows load
+// while the current one is computed) with an online softmax: a running max
+// and sum per head, the accumulators rescaled when the max grows. Scores come
+// from the matrix cores as in task_attn_mm (query hi + lo pairs against the
+// tile's K rows), P V from the vector ALUs with the probabilities broadcast
+// through LDS.
+struct AttnTile {
+  uint4 k[4];        // lane (j, r): K row j of the tile, elements 32 s + 8 r ..
+  uint32_t v[16];    // V rows 0..15 of the tile: this lane's element pair
+};
+
+template <int GP>
+__device__ __forceinline__ bool task_attn_stream(const Ctx& c, int b, int g, int p0, int p1, int piece, int npieces,
+                                                 const int* wev) {
+  const StepArgs& a = c.a;
+  const Dims& dm = a.dm;
+  typedef MM<uint16_t> T;
+  constexpr int D = 128, DP = D + 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), j = lane & 15, r = lane >> 4;
+  const int G = dm.Hq / dm.Hkv;
+  const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * D;
+  const int S = ldu(a.seq_lens + b);
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kv) + kv_off(dm, c.l, 0, b, g, 0);
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.kv) + kv_off(dm, c.l, 1, b, g, 0);
+  const int pmax = S > 0 ? S - 1 : 0;   // cached slots only (slot S is this step's)
+  const int nt = (p1 - p0 + 15) >> 4;   // tiles of the piece
+  const int ntw = nt > wave ? (nt - wave + kWaves - 1) / kWaves : 0;   // this wave's: wave, wave + 8, ...
+  auto load = [&](AttnTile& t, int i) {
+    const int tb = p0 + (wave + kWaves * i) * 16;
+    const uint16_t* kp = Kb + (size_t)min(tb + j, pmax) * D + r * 8;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = ldg16(kp + s4 * 32);
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) t.v[ii] = ldg4(Vb + (size_t)min(tb + ii, pmax) * D + 2 * lane);
+  };
+  AttnTile t0, t1;
+  if (ntw > 0) load(t0, 0);
+  if (ntw > 1) load(t1, 1);
+  if (!ctx_wait(c, wev)) return false;
+
+  // A operand: query head j of the group (zero beyond G), q * log2(e) / sqrt(d) as hi + lo
+  const auto qr = rsrc_n(a.ws.qkv + (size_t)b * qkv_dim, qkv_dim * 4);
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);
+  uint4 qh[4], ql[4];
+  {
+    const int qo = j < G ? ((g * G + j) * D + r * 8) * 4 : kNoRecord;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const f4v x0 = ldc4(qr, qo + s4 * 128) * qscale, x1 = ldc4(qr, qo + s4 * 128 + 16) * qscale;
+      const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t h0 = f2bf(xv[2 * e]), h1 = f2bf(xv[2 * e + 1]);
+        const uint16_t l0 = f2bf(xv[2 * e] - __uint_as_float((uint32_t)h0 << 16));
+        const uint16_t l1 = f2bf(xv[2 * e + 1] - __uint_as_float((uint32_t)h1 << 16));
+        hw[e] = h0 | ((uint32_t)h1 << 16);
+        lw[e] = l0 | ((uint32_t)l1 << 16);
+      }
+      qh[s4] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      ql[s4] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
+  }
+  // position S takes this step's rotated k and v (rounded as the KV append
+  // stores them): row jj of this wave's tile iS, if the piece holds S
+  int iS = -1, jj = 0;
+  uint4 kn[4];
+  uint32_t vn = 0;
+  if (S >= p0 && S < p1 && ((S - p0) >> 4) % kWaves == wave) {
+    iS = ((S - p0) >> 4) / kWaves;
+    jj = (S - p0) & 15;
+    const int ko = j == jj ? ((dm.Hq + g) * D + r * 8) * 4 : kNoRecord;
+    const float2 vv = ldc2(qr, ((dm.Hq + dm.Hkv + g) * D + 2 * lane) * 4);
+    vn = (uint32_t)f2bf(vv.x) | ((uint32_t)f2bf(vv.y) << 16);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const f4v x0 = ldc4(qr, ko + s4 * 128), x1 = ldc4(qr, ko + s4 * 128 + 16);
+      kn[s4] = make_uint4((uint32_t)f2bf(x0.x) | ((uint32_t)f2bf(x0.y) << 16),
+                          (uint32_t)f2bf(x0.z) | ((uint32_t)f2bf(x0.w) << 16),
+                          (uint32_t)f2bf(x1.x) | ((uint32_t)f2bf(x1.y) << 16),
+                          (uint32_t)f2bf(x1.z) | ((uint32_t)f2bf(x1.w) << 16));
+    }
+  }
+  if (tid == 0) c.s.tclk[2] = (uint32_t)now_ticks();
+
+  float* sw = reinterpret_cast<float*>(c.s.xs);                // [kWaves][G][DP] wave partials
+  float* pb = sw + kWaves * 8 * DP + wave * (16 * GP);         // this wave's [16][GP] probabilities
+  // running max and sum of head 4 rr + e in row rr's lanes, element e
+  float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, ls[4] = {0.f, 0.f, 0.f, 0.f};
+  float acc[GP][2];
+#pragma unroll
+  for (int h = 0; h < GP; ++h) acc[h][0] = acc[h][1] = 0.f;
+  auto process = [&](AttnTile& t, int i) {
+    if (i == iS) {   // uniform
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        if (j == jj) t.k[s4] = kn[s4];
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii)
+        if (ii == jj) t.v[ii] = vn;
+    }
+    f4v sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      sc = T::mac(qh[s4], t.k[s4], sc);
+      sc = T::mac(ql[s4], t.k[s4], sc);
+    }
+    const bool valid = p0 + (wave + kWaves * i) * 16 + j < p1;
+    float scale[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float mn = fmaxf(mx[e], max16(valid ? sc[e] : -INFINITY));
+      scale[e] = mx[e] == -INFINITY ? 0.f : exp2f(mx[e] - mn);
+      const float pe = valid ? exp2f(sc[e] - mn) : 0.f;
+      ls[e] = ls[e] * scale[e] + sum16(pe);
+      mx[e] = mn;
+      sc[e] = pe;
+    }
+    if (r < GP / 4) *reinterpret_cast<f4v*>(pb + j * GP + 4 * r) = sc;
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scale[h & 3]),
+                                                                          16 * (h >> 2)));
+      acc[h][0] *= f;
+      acc[h][1] *= f;
+    }
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) {
+      const float v0 = bf_lo(t.v[ii]), v1 = bf_hi(t.v[ii]);
+#pragma unroll
+      for (int h4 = 0; h4 < GP / 4; ++h4) {
+        const f4v pp = *reinterpret_cast<const f4v*>(pb + ii * GP + 4 * h4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[4 * h4 + e][0] += pp[e] * v0;
+          acc[4 * h4 + e][1] += pp[e] * v1;
+        }
+      }
+      // one position at a time (left alone, the compiler sinks the
+      // accumulations and holds every probability and V pair live)
+#pragma unroll
+      for (int h = 0; h < GP; ++h) __asm__ volatile("" : "+v"(acc[h][0]), "+v"(acc[h][1]));
+    }
+  };
+  // two buffers: while one tile is computed the next one's rows load; the
+  // main loop is branch-free so its waits stay exact, the tail handles the
+  // last one to three tiles
+  int i = 0;
+  for (; i + 3 < ntw; i += 2) {
+    process(t0, i);
+    load(t0, i + 2);
+    process(t1, i + 1);
+    load(t1, i + 3);
+  }
+  if (i < ntw) {
+    process(t0, i);
+    if (i + 2 < ntw) load(t0, i + 2);
+  }
+  if (i + 1 < ntw) process(t1, i + 1);
+  if (i + 2 < ntw) process(t0, i + 2);
+
+  // this wave's partial per head: acc (2 elements per lane), max and sum
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    if (h < G) {
+      float* dst = sw + (wave * G + h) * DP;
+      *reinterpret_cast<float2*>(dst + 2 * lane) = make_float2(acc[h][0], acc[h][1]);
+      const int M = __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx[h & 3]), 16 * (h >> 2));
+      const int L = __builtin_amdgcn_readlane(__builtin_bit_cast(int, ls[h & 3]), 16 * (h >> 2));
+      if (lane == 0) { dst[D] = __builtin_bit_cast(float, M); dst[D + 1] = __builtin_bit_cast(float, L); }
+    }
+  }
+  if (tid == 0) c.s.tclk[3] = (uint32_t)now_ticks();   // wave 0's positions done
+  __syncthreads();
+  if (tid == 0) c.s.tclk[4] = (uint32_t)now_ticks();   // every wave's
+  return attn_finish<D>(c, b, g, piece, 0, npieces, G, sw);
+}
+
 template <typename KT, int HB>
 __device__ __forceinline__ bool attn_its(const Ctx& c, int b, int g, int ci, int tix, int ck, const int* wev) {
   if (ck <= 64) return task_attn<KT, HB, 2>(c, b, g, ci, tix, wev);
@@ -1432,6 +1614,15 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           case T_ATTN:
             ok = attn_dispatch<WT>(c, task.y, task.z, task.w, tix, need(EV_QKV, l));
             break;
+          case T_ATTS: {   // x: piece << 8 | pieces << 20, y: b | g << 16, z/w: positions [z, w)
+            const int b = task.y & 0xffff, g = task.y >> 16, piece = tix & 0xfff, np = tix >> 12;
+            const int* wev = need(EV_QKV, l);
+            if constexpr (sizeof(WT) == 2) {
+              ok = dm.Hq / dm.Hkv <= 4 ? task_attn_stream<4>(c, b, g, task.z, task.w, piece, np, wev)
+                                       : task_attn_stream<8>(c, b, g, task.z, task.w, piece, np, wev);
+            }
+            break;
+          }
           case T_ROUTE:
             ok = task_route(c, need(EV_ROUTER, l));
             break;
@@ -1539,7 +1730,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   const Dims& dm = a.dm;
   const int tid = threadIdx.x, B = a.batch, G = dm.grid;
   __shared__ int bad;
-  __shared__ int total_attn, merge_s, qkv_tiles_s, attn_wg0_s;
+  __shared__ int total_attn, merge_s, qkv_tiles_s, attn_wg0_s, stream_s, share_s;
   __shared__ StageGeo geo_s[4];
   __shared__ int cb[kMaxBatchAll + 1];
   StepArgs* copy = reinterpret_cast<StepArgs*>(a.ws.args);
@@ -1592,13 +1783,22 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     }
     copy->attn_merge_o = merge;
     merge_s = merge;
+    // Without the O-projection merge, the matrix-core attention streams its
+    // positions: all (request, KV head) position ranges, laid end to end,
+    // are cut into equal shares, one per workgroup (at least 64 positions),
+    // and each piece of a range within a share is a task. cb then holds the
+    // prefix sum of the requests' positions (S + 1), else of their chunks.
+    const int stream = !merge && dm.attn_mm;
+    stream_s = stream;
     int acc = 0;
     for (int b = 0; b < B; ++b) {
       cb[b] = acc;
-      acc += (a.seq_lens[b] + ck) / ck;   // ceil((S + 1) / ck)
+      acc += stream ? a.seq_lens[b] + 1 : (a.seq_lens[b] + ck) / ck;   // ceil((S + 1) / ck)
     }
     cb[B] = acc;
     total_attn = acc * dm.Hkv;
+    const long P = (long)acc * dm.Hkv;
+    share_s = max(64, (int)((P + G - 1) / G + 15) / 16 * 16);
     copy->attn_chunk = ck;
     // A few attention tasks (at most a quarter of the grid) get workgroups of
     // their own, the last ones, which hold no QKV tile: their task comes first
@@ -1640,7 +1840,25 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       for (int i = w; i < g.tiles * g.ks; i += G) push(make_int4(type, i / g.ks, i % g.ks, 0));
     };
     stage_tasks(T_QKV, 0);
-    for (int i = aw0 < G ? w - aw0 : w; i >= 0 && i < total_attn; i += (aw0 < G ? total_attn : G)) {
+    if (stream_s) {   // this workgroup's share of the laid-out positions
+      const long share = share_s, hi = min((long)(w + 1) * share, (long)total_attn);
+      for (long pos = (long)w * share; pos < hi;) {
+        int lo = 0, up = B;   // request b: Hkv*cb[b] <= pos < Hkv*cb[b+1]
+        while (up - lo > 1) {
+          const int mid = (lo + up) >> 1;
+          if ((long)dm.Hkv * cb[mid] <= pos) lo = mid; else up = mid;
+        }
+        const int len = cb[lo + 1] - cb[lo];
+        const int g = (int)((pos - (long)dm.Hkv * cb[lo]) / len);
+        const long seg0 = (long)dm.Hkv * cb[lo] + (long)g * len, seg1 = seg0 + len, e = min(hi, seg1);
+        // pieces of a range are cut at multiples of the share: this is piece
+        // w - seg0 / share of (seg1 - 1) / share - seg0 / share + 1
+        const int piece = w - (int)(seg0 / share), np = (int)((seg1 - 1) / share - seg0 / share) + 1;
+        push(make_int4(T_ATTS | (piece << 8) | (np << 20), lo | (g << 16), (int)(pos - seg0), (int)(e - seg0)));
+        pos = e;
+      }
+    }
+    for (int i = aw0 < G ? w - aw0 : w; !stream_s && i >= 0 && i < total_attn; i += (aw0 < G ? total_attn : G)) {
       int lo = 0, hi = B;   // find b: Hkv*cb[b] <= i < Hkv*cb[b+1]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
@@ -1684,9 +1902,15 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     }
   }
   for (int idx = tid; idx < 4 * G; idx += blockDim.x) a.ws.tctr[idx * kCtr] = 0;
+  // attention merge counters: the pieces (streamed) or chunks of each (request, KV head)
   for (int idx = tid; idx < dm.L * B * dm.Hkv; idx += blockDim.x) {
     const int l = idx / (B * dm.Hkv), rem = idx - l * B * dm.Hkv, b = rem / dm.Hkv, g = rem - b * dm.Hkv;
-    a.ws.mctr[(((size_t)l * dm.max_batch + b) * dm.Hkv + g) * kCtr] = cb[b + 1] - cb[b];
+    int n = cb[b + 1] - cb[b];
+    if (stream_s) {
+      const long seg0 = (long)dm.Hkv * cb[b] + (long)g * n, seg1 = seg0 + n;
+      n = (int)((seg1 - 1) / share_s - seg0 / share_s) + 1;
+    }
+    a.ws.mctr[(((size_t)l * dm.max_batch + b) * dm.Hkv + g) * kCtr] = n;
   }
   __syncthreads();
   if (tid == 0 && (bad & 4)) {
