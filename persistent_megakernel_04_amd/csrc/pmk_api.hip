@@ -169,14 +169,17 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   // workspace carving
   const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
   const int Gq = dm.Hq / dm.Hkv;
-  struct Part { void** p; size_t bytes; };
+  // per_layer: the part holds one slice per layer (each addressed from its own base)
+  struct Part { void** p; size_t bytes; size_t per_layer = 0; };
   Workspace& ws = h->ws;
   const size_t TK = (size_t)dm.max_batch * std::max(dm.k, 1);
   std::vector<Part> parts = {
-      {(void**)&ws.qkv, (size_t)dm.max_batch * qkv_dim * 4},
-      {(void**)&ws.o, (size_t)dm.max_batch * dm.Hq * dm.d * 4},
-      {(void**)&ws.h1, (size_t)dm.max_batch * dm.H * 4},
-      {(void**)&ws.act, (size_t)dm.max_batch * std::max(dm.F, 1) * 4},
+      {(void**)&ws.qkv, (size_t)dm.L * dm.max_batch * qkv_dim * 4, (size_t)dm.max_batch * qkv_dim * 4},
+      {(void**)&ws.o, (size_t)dm.L * dm.max_batch * dm.Hq * dm.d * 4, (size_t)dm.max_batch * dm.Hq * dm.d * 4},
+      {(void**)&ws.h1, (size_t)dm.L * dm.max_batch * dm.H * 4, (size_t)dm.max_batch * dm.H * 4},
+      {(void**)&ws.act, (size_t)dm.L * dm.max_batch * std::max(dm.F, 1) * 4,
+       (size_t)dm.max_batch * std::max(dm.F, 1) * 4},
+      {(void**)&ws.hid, (size_t)std::max(dm.L - 1, 1) * dm.max_batch * dm.H * 4, (size_t)dm.max_batch * dm.H * 4},
       {(void**)&ws.part, (size_t)dm.max_batch * dm.Hkv * dm.max_chunks * Gq * (dm.d + 4) * 4},
       {(void**)&ws.rope, (size_t)dm.max_seq * (dm.d / 2) * 8},
       {(void**)&ws.ev, (size_t)dm.L * EV_COUNT * kEvInts * 4},
@@ -201,7 +204,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
         {(void**)&ws.tile_info, (size_t)dm.max_tiles * 2 * 4},
         {(void**)&ws.moe_info, 64 * 4},
         {(void**)&ws.ectr, (size_t)dm.L * dm.E * kCtr * 4},
-        {(void**)&ws.mact, TK * dm.Fe * 4},
+        {(void**)&ws.mact, (size_t)dm.L * TK * dm.Fe * 4, TK * dm.Fe * 4},
         {(void**)&ws.mout, TK * dm.H * 4},
     };
     parts.insert(parts.end(), mp.begin(), mp.end());
@@ -209,7 +212,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   // step intermediates are addressed with 32-bit byte offsets from one buffer
   // base, and stay below the kernels' out-of-range marker offset (1 GiB)
   for (auto& p : parts)
-    if (p.bytes >= ((size_t)1 << 30)) { delete h; return PMK_ERR_ARG; }
+    if ((p.per_layer ? p.per_layer : p.bytes) >= ((size_t)1 << 30)) { delete h; return PMK_ERR_ARG; }
   size_t total = 0;
   for (auto& p : parts) total += align256(p.bytes);
   void* base = nullptr;

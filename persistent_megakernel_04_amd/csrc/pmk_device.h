@@ -34,8 +34,16 @@ template <typename T> __device__ __forceinline__ const __attribute__((address_sp
 template <typename T> __device__ __forceinline__ __attribute__((address_space(1))) T* gp(T* p) {
   return (__attribute__((address_space(1))) T*)p;
 }
-// Plain global load of a field (a pointer, say) of an immutable struct.
-template <typename T> __device__ __forceinline__ T ldp(const T* field) { return *gp(field); }
+// A pointer that is the same for the whole wave, kept in scalar registers.
+template <typename T> __device__ __forceinline__ T* uptr(T* p) {
+  const unsigned long long v = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return (T*)(((unsigned long long)hi << 32) | lo);
+}
+// Plain global load of a pointer field of an immutable struct (the same for
+// the whole wave; kept scalar, so descriptors built from it need no loop).
+template <typename T> __device__ __forceinline__ T* ldp(T* const* field) { return uptr(*gp(field)); }
 __device__ __forceinline__ float ldc(const float* p) {
   return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -84,7 +92,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_n(const void* base, int b
 __device__ __forceinline__ f4v ldc4(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
 }
+// The same loads through the caches, for per-layer activations (written once
+// per step before any workgroup reads them).
+__device__ __forceinline__ f4v ldk4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(f4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 typedef unsigned u2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2 ldk2(__amdgpu_buffer_rsrc_t r, int off) {
+  const u2v v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
+}
 __device__ __forceinline__ float2 ldc2(__amdgpu_buffer_rsrc_t r, int off) {
   const u2v v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16);
   return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));

@@ -116,10 +116,12 @@ struct Dims {
 
 // Device workspace (one allocation, carved by the host).
 struct Workspace {
-  float* qkv;          // [max_batch][(Hq + 2 Hkv) d]   rotated q, k; v
-  float* o;            // [max_batch][Hq d]             merged attention output
-  float* h1;           // [max_batch][H]                residual after attention
-  float* act;          // [max_batch][F]                SwiGLU output (dense)
+  // per-layer activations (each written once per step; see qkv_of in the kernels)
+  float* qkv;          // [L][max_batch][(Hq + 2 Hkv) d]   rotated q, k; v
+  float* o;            // [L][max_batch][Hq d]             merged attention output
+  float* h1;           // [L][max_batch][H]                residual after attention
+  float* act;          // [L][max_batch][F]                SwiGLU output (dense)
+  float* hid;          // [L - 1][max_batch][H]            layer outputs feeding the next layer
   float* part;         // [max_batch][Hkv][max_chunks][G][d + 4]  attention partials (acc, max, sum, pad)
   float2* rope;        // [max_seq][d / 2]              (cos, sin)
   int* ev;             // [L][EV_COUNT][kEvInts]
@@ -142,7 +144,7 @@ struct Workspace {
   int* tile_info;      // [max_tiles][2]  (expert, first grouped row) of each row tile
   int* moe_info;       // [0] gate/up tasks, [1] down tasks, [2] gate/up slices, [3] down slices, [4] tiles
   int* ectr;           // [L][E][kCtr]                  per-expert counters (gate/up -> down)
-  float* mact;         // [max_batch k][Fe]             expert SwiGLU rows, grouped order
+  float* mact;         // [L][max_batch k][Fe]          expert SwiGLU rows, grouped order (per layer)
   float* mout;         // [max_batch k][H]              expert down rows, grouped order
 };
 

@@ -65,6 +65,33 @@ struct Ctx {
   Lds s;
 };
 
+// Per-layer activations. Each buffer is written once per step, by the stage
+// that produces it, and read only after that stage's event; a reader's L2
+// therefore never holds an older copy of its lines (the L2s are invalidated
+// at every kernel start), and the staged reads use ordinary cached loads, so
+// the workgroups of an XCD share one fetch of a row through their L2. The
+// stack's input is the caller's hidden (layer 0 reads it) and its output goes
+// back there (the last layer writes it).
+__device__ __forceinline__ float* qkv_of(const StepArgs& a, int l) {
+  return a.ws.qkv + (size_t)l * a.dm.max_batch * (a.dm.Hq + 2 * a.dm.Hkv) * a.dm.d;
+}
+__device__ __forceinline__ float* o_of(const StepArgs& a, int l) {
+  return a.ws.o + (size_t)l * a.dm.max_batch * a.dm.Hq * a.dm.d;
+}
+__device__ __forceinline__ float* h1_of(const StepArgs& a, int l) { return a.ws.h1 + (size_t)l * a.dm.max_batch * a.dm.H; }
+__device__ __forceinline__ float* act_of(const StepArgs& a, int l) {
+  return a.ws.act + (size_t)l * a.dm.max_batch * a.dm.F;
+}
+__device__ __forceinline__ float* mact_of(const StepArgs& a, int l) {
+  return a.ws.mact + (size_t)l * a.dm.max_batch * a.dm.k * a.dm.Fe;
+}
+__device__ __forceinline__ const float* hid_in(const StepArgs& a, int l) {
+  return l == 0 ? a.hidden : a.ws.hid + (size_t)(l - 1) * a.dm.max_batch * a.dm.H;
+}
+__device__ __forceinline__ float* hid_out(const StepArgs& a, int l) {
+  return l == a.dm.L - 1 ? a.hidden : a.ws.hid + (size_t)l * a.dm.max_batch * a.dm.H;
+}
+
 __device__ __forceinline__ int* ev_ptr(const StepArgs& a, int layer, int e) {
   return a.ws.ev + ((size_t)layer * EV_COUNT + e) * kEvInts;
 }
@@ -141,8 +168,11 @@ struct GemvIn {
 // Stage nb input rows into LDS as the MFMA input type, rows XS apart (SPLIT:
 // each row as a hi part and a lo part, XS apart, rows 2 XS apart), zero
 // beyond K up to Kp; per-row sum of squares -> rstd (when in.norm). Each wave
-// takes 256-element blocks of the rows; a block's sum of squares is a wave
-// reduction added to that wave's slot, and the 8 slots are summed in order.
+// takes 256-element blocks of the rows, eight at a time: their loads (and
+// the gains') are issued together with no branch between them, so each one
+// waits only for itself. A block's sum of squares is a wave reduction added
+// to that wave's slot, and the 8 slots are summed in order. The sources are
+// per-layer activations: cached loads.
 template <typename WT, bool SPLIT>
 __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int Kp, int XS, const Lds& s) {
   typedef typename MM<WT>::XT XT;
@@ -150,36 +180,35 @@ __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int BPR = (Kp + 255) >> 8, NBK = nb * BPR;
   const auto src = rsrc(in.src);
+  // no gain: a descriptor with an empty range reads zeros, replaced by ones below
+  const auto grs = rsrc_n(in.gain ? (const void*)in.gain : (const void*)in.src, in.gain ? K * 4 : 0);
+  const bool has_gain = in.gain != nullptr;
+  // gathered rows: lane m holds the source row of staged row m
+  const int gidx = (in.gather && lane < nb) ? ldci(in.gather + lane) : lane;
   if (lane == 0)
     for (int m = 0; m < nb; ++m) s.ssp[m * kWaves + wave] = 0.f;
   for (int base = wave; base < NBK; base += kWaves * 8) {
-    f4v v[8];
+    f4v v[8], gv[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int blk = base + u * kWaves;
-      v[u] = f4v{0.f, 0.f, 0.f, 0.f};
-      if (blk < NBK) {
-        const int m = blk / BPR, k = (blk - m * BPR) * 256 + lane * 4;
-        if (k < K) {
-          const int srow = in.gather ? ldci(in.gather + m) : m;
-          v[u] = ldc4(src, (srow * in.ld + k) * 4);
-        }
-      }
+      const int blk = min(base + u * kWaves, NBK - 1);   // past the end: a valid block, not used
+      const int m = blk / BPR, k = (blk - m * BPR) * 256 + lane * 4;
+      const int srow = __builtin_amdgcn_readlane(gidx, m);
+      const int kc = min(k, K - 4);                      // beyond K: a valid element, zeroed below
+      v[u] = ldk4(src, (srow * in.ld + kc) * 4);
+      gv[u] = ldk4(grs, kc * 4);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int blk = base + u * kWaves;
       if (blk >= NBK) continue;
       const int m = blk / BPR, k = (blk - m * BPR) * 256 + lane * 4;
-      f4v x = v[u];
+      f4v x = k < K ? v[u] : f4v{0.f, 0.f, 0.f, 0.f};
       if (in.norm) {
         const float ss = wave_sum(x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w);
         if (lane == 0) s.ssp[m * kWaves + wave] += ss;
       }
-      if (in.gain && k < K) {
-        const f4v g = *gp(reinterpret_cast<const f4v*>(in.gain + k));
-        x.x *= g.x; x.y *= g.y; x.z *= g.z; x.w *= g.w;
-      }
+      x *= has_gain ? gv[u] : f4v{1.f, 1.f, 1.f, 1.f};
       if (k < Kp) {
         if (SPLIT)
           MM<WT>::put4_split(xs + (size_t)m * 2 * XS + k, xs + (size_t)m * 2 * XS + XS + k, x);
@@ -471,6 +500,7 @@ struct Pass {
   int tile, slice, ks;   // row tile, K slice, slices of the stage (1: no split)
   int kfull;        // the stage's whole depth
   int rs;           // split-K record stride (floats): outputs of the stage's largest tile + 16
+  int l;            // layer
   float* ys;        // the pass's outputs [R][nb] in LDS, after its staged inputs
 };
 
@@ -494,13 +524,14 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   ps.wsubs = kSubs;
   ps.e = 0;
   ps.stage = -1;
+  ps.l = c.l;
   ps.tile = tile;
   ps.slice = 0;
   ps.ks = 1;
   // the K slice of a dense task, its rows per pass and first batch row
   int k0 = 0, kn = 0, b0 = 0, nbb = 0;
   auto dense = [&](int stage, int K, int R, int units, int urows) -> bool {
-    const StageGeo& g = a.geo[stage];
+    const StageGeo g{ldu(&a.geo[stage].ks), ldu(&a.geo[stage].tiles), ldu(&a.geo[stage].kr)};
     k0 = task.z * g.kr;
     kn = min(K, k0 + g.kr) - k0;
     nbb = g.ks > 1 ? kMaxNb : pass_rows<WT>(kn, R);
@@ -519,37 +550,37 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   };
   switch (task.x) {
     case T_QKV: {   // RMSNorm1 + QKV rotation pairs of the tile
-      const int2 u = tile_units(tile, dm.qkv_units, a.geo[0].tiles);
+      const int2 u = tile_units(tile, dm.qkv_units, ldu(&a.geo[0].tiles));
       if (!dense(0, dm.H, 2 * u.y, dm.qkv_units, 2)) return false;
       ps.rw = GemvRows{ROWS_QKV, ldp(&Lp->w_qkv), nullptr, u.x, dm.d >> 1, dm.H, k0};
-      ps.in = GemvIn{a.hidden + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->attn_norm) + k0, ps.ks > 1 ? 2 : 1,
-                     dm.eps, -1};
+      ps.in = GemvIn{hid_in(a, c.l) + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->attn_norm) + k0,
+                     ps.ks > 1 ? 2 : 1, dm.eps, -1};
       ps.epi = E_QKV; ps.r0 = u.x; ps.n = u.y;
       break;
     }
     case T_O: {     // O-projection rows of the tile
       const int K = dm.Hq * dm.d;
-      const int2 u = tile_units(tile, dm.H, a.geo[1].tiles);
+      const int2 u = tile_units(tile, dm.H, ldu(&a.geo[1].tiles));
       if (!dense(1, K, u.y, dm.H, 1)) return false;
       ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_o), nullptr, u.x, 0, K, k0};
-      ps.in = GemvIn{a.ws.o + (size_t)b0 * K + k0, K, nullptr, nullptr, 0, 0.f, a.attn_merge_o ? b0 : -1};
+      ps.in = GemvIn{o_of(a, c.l) + (size_t)b0 * K + k0, K, nullptr, nullptr, 0, 0.f, a.attn_merge_o ? b0 : -1};
       ps.epi = E_O; ps.r0 = u.x; ps.n = u.y;
       break;
     }
     case T_GU: {    // RMSNorm2 + gate and up rows of the tile
-      const int2 u = tile_units(tile, dm.F, a.geo[2].tiles);
+      const int2 u = tile_units(tile, dm.F, ldu(&a.geo[2].tiles));
       if (!dense(2, dm.H, 2 * u.y, dm.F, 2)) return false;
       ps.rw = GemvRows{ROWS_PAIR, ldp(&Lp->w_gate), ldp(&Lp->w_up), u.x, u.y, dm.H, k0};
-      ps.in = GemvIn{a.ws.h1 + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->ffn_norm) + k0, ps.ks > 1 ? 2 : 1,
-                     dm.eps, -1};
+      ps.in = GemvIn{h1_of(a, c.l) + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->ffn_norm) + k0,
+                     ps.ks > 1 ? 2 : 1, dm.eps, -1};
       ps.epi = E_GU; ps.r0 = u.x; ps.n = u.y;
       break;
     }
     case T_DOWN: {  // down-projection rows of the tile
-      const int2 u = tile_units(tile, dm.H, a.geo[3].tiles);
+      const int2 u = tile_units(tile, dm.H, ldu(&a.geo[3].tiles));
       if (!dense(3, dm.F, u.y, dm.H, 1)) return false;
       ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_down), nullptr, u.x, 0, dm.F, k0};
-      ps.in = GemvIn{a.ws.act + (size_t)b0 * dm.F + k0, dm.F, nullptr, nullptr, 0, 0.f, -1};
+      ps.in = GemvIn{act_of(a, c.l) + (size_t)b0 * dm.F + k0, dm.F, nullptr, nullptr, 0, 0.f, -1};
       ps.epi = E_DOWN; ps.r0 = u.x; ps.n = u.y;
       break;
     }
@@ -559,7 +590,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       if (br >= bend) return false;
       const int r0 = tile * 16;
       ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_router), nullptr, r0, 0, dm.H, 0};
-      ps.in = GemvIn{a.ws.h1 + (size_t)br * dm.H, dm.H, nullptr, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
+      ps.in = GemvIn{h1_of(a, c.l) + (size_t)br * dm.H, dm.H, nullptr, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
       ps.R = min(16, dm.E - r0); ps.K = dm.H; ps.kfull = dm.H; ps.nb = min(nbr, bend - br);
       ps.epi = E_ROUTER; ps.b0 = br; ps.r0 = r0; ps.n = ps.R;
       break;
@@ -574,7 +605,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       ps.rw = GemvRows{ROWS_PAIR, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_gate)) + eo,
                        reinterpret_cast<const WT*>(ldp(&Lp->w_exp_up)) + eo, f0, Rh, dm.H, 0};
       // the tile's rows: its routed tokens' FFN inputs (RMSNorm2 of h1), gathered
-      ps.in = GemvIn{a.ws.h1, dm.H, a.ws.sorted_tok + row0, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
+      ps.in = GemvIn{h1_of(a, c.l), dm.H, a.ws.sorted_tok + row0, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
       ps.R = 2 * Rh; ps.K = dm.H; ps.kfull = dm.H; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
       ps.epi = E_MGU; ps.b0 = row0; ps.r0 = f0; ps.n = Rh; ps.e = e;
       break;
@@ -587,7 +618,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int h0 = (int)((long)sl * dm.H / sd), R = (int)((long)(sl + 1) * dm.H / sd) - h0;
       ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_down)) + (size_t)e * dm.H * dm.Fe,
                        nullptr, h0, 0, dm.Fe, 0};
-      ps.in = GemvIn{a.ws.mact + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f, -1};
+      ps.in = GemvIn{mact_of(a, c.l) + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f, -1};
       ps.R = R; ps.K = dm.Fe; ps.kfull = dm.Fe; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
       ps.wev = a.ws.ectr + ((size_t)c.l * dm.E + e) * kCtr;
       ps.wsubs = 0;
@@ -608,7 +639,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
 // whole workgroup once the pass's sums are there.
 constexpr int kResid = kYsFloats / kBlock;
 __device__ __forceinline__ const float* resid_src(const StepArgs& a, const Pass& ps) {
-  return ps.epi == E_O ? a.hidden : a.ws.h1;
+  return ps.epi == E_O ? hid_in(a, ps.l) : h1_of(a, ps.l);
 }
 __device__ __forceinline__ void load_resid(const StepArgs& a, const Pass& ps, float (&r)[kResid]) {
   const float* res = resid_src(a, ps);
@@ -699,7 +730,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
           y1 = t1;
           y2 = t2;
         }
-        float* dst = a.ws.qkv + (size_t)bb * qkv_dim + h * dm.d + i;
+        float* dst = qkv_of(a, c.l) + (size_t)bb * qkv_dim + h * dm.d + i;
         stc(dst, y1);
         stc(dst + half, y2);
         if (h >= dm.Hq) {
@@ -714,7 +745,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
     case E_O:       // h1 = x + W_o o
     case E_DOWN: {  // x' = h1 + W_down act (the layer output, into hidden)
       const float* res = resid_src(a, ps);
-      float* out = ps.epi == E_O ? a.ws.h1 : a.hidden;
+      float* out = ps.epi == E_O ? h1_of(a, c.l) : hid_out(a, c.l);
       for (int idx = lane; idx < ps.n * nb; idx += 64) {
         const int j = idx / nb, m = idx - j * nb;
         const size_t o = (size_t)(b0 + m) * dm.H + ps.r0 + j;
@@ -725,7 +756,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
     case E_GU:      // act = silu(gate) * up
     case E_MGU: {
       const int Rh = ps.n;
-      float* out = ps.epi == E_GU ? a.ws.act : a.ws.mact;
+      float* out = ps.epi == E_GU ? act_of(a, c.l) : mact_of(a, c.l);
       const int ld = ps.epi == E_GU ? dm.F : dm.Fe;
       for (int idx = lane; idx < Rh * nb; idx += 64) {
         const int j = idx / nb, m = idx - j * nb;
@@ -778,12 +809,12 @@ template <> __device__ __forceinline__ void unpack_row<float>(const uint4 r, flo
 // Device-coherent float row slice -> cache-dtype bits (rounded like the KV append).
 template <typename KT> __device__ __forceinline__ uint4 pack_row(__amdgpu_buffer_rsrc_t r, int off);
 template <> __device__ __forceinline__ uint4 pack_row<uint16_t>(__amdgpu_buffer_rsrc_t r, int off) {
-  const f4v a = ldc4(r, off), b = ldc4(r, off + 16);
+  const f4v a = ldk4(r, off), b = ldk4(r, off + 16);
   return make_uint4((uint32_t)f2bf(a.x) | ((uint32_t)f2bf(a.y) << 16), (uint32_t)f2bf(a.z) | ((uint32_t)f2bf(a.w) << 16),
                     (uint32_t)f2bf(b.x) | ((uint32_t)f2bf(b.y) << 16), (uint32_t)f2bf(b.z) | ((uint32_t)f2bf(b.w) << 16));
 }
 template <> __device__ __forceinline__ uint4 pack_row<float>(__amdgpu_buffer_rsrc_t r, int off) {
-  const f4v a = ldc4(r, off);
+  const f4v a = ldk4(r, off);
   return make_uint4(__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z), __float_as_uint(a.w));
 }
 
@@ -799,7 +830,7 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, int b, int g, int ci, 
   const Dims& dm = a.dm;
   constexpr int DP = D + 4;
   const int tid = threadIdx.x;
-  float* o = a.ws.o + (size_t)b * dm.Hq * D + (size_t)g * G * D;
+  float* o = o_of(a, c.l) + (size_t)b * dm.Hq * D + (size_t)g * G * D;
   float* part = a.ws.part + (((size_t)b * dm.Hkv + g) * dm.max_chunks + ci) * G * DP;
   const auto orr = rsrc(o), prr = rsrc(part);
   for (int t = tid; t < G * D / 4; t += kBlock) {
@@ -903,11 +934,11 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
 
   float* sw = reinterpret_cast<float*>(c.s.xs);     // [kWaves][G][DP] per-wave partials
   float* qs = sw + kWaves * 8 * DP;                  // [G][D] this group's rotated queries
-  const float* qrow = a.ws.qkv + (size_t)b * qkv_dim + (size_t)g * G * D;
-  for (int t = tid; t < G * D / 4; t += kBlock) *reinterpret_cast<f4v*>(qs + 4 * t) = ldc4(rsrc(qrow), 16 * t);
+  const float* qrow = qkv_of(a, c.l) + (size_t)b * qkv_dim + (size_t)g * G * D;
+  for (int t = tid; t < G * D / 4; t += kBlock) *reinterpret_cast<f4v*>(qs + 4 * t) = ldk4(rsrc(qrow), 16 * t);
   uint4 kn = make_uint4(0, 0, 0, 0), vn = kn;
   if (S >= p0 && S < p1) {
-    const auto qr = rsrc(a.ws.qkv + (size_t)b * qkv_dim);
+    const auto qr = rsrc(qkv_of(a, c.l) + (size_t)b * qkv_dim);
     kn = pack_row<KT>(qr, ((dm.Hq + g) * D + li * EPL) * 4);
     vn = pack_row<KT>(qr, ((dm.Hq + dm.Hkv + g) * D + li * EPL) * 4);
   }
@@ -1020,14 +1051,14 @@ __device__ __forceinline__ bool task_attn_mm(const Ctx& c, int b, int g, int ci,
   if (!ctx_wait(c, wev)) return false;
 
   // A operand: query head j of the group (zero beyond G), q * log2(e) / sqrt(d) as hi + lo
-  const auto qr = rsrc_n(a.ws.qkv + (size_t)b * qkv_dim, qkv_dim * 4);
+  const auto qr = rsrc_n(qkv_of(a, c.l) + (size_t)b * qkv_dim, qkv_dim * 4);
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
   uint4 qh[4], ql[4];
   {
     const int qo = j < G ? ((g * G + j) * D + r * 8) * 4 : kNoRecord;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const f4v x0 = ldc4(qr, qo + s4 * 128) * qscale, x1 = ldc4(qr, qo + s4 * 128 + 16) * qscale;
+      const f4v x0 = ldk4(qr, qo + s4 * 128) * qscale, x1 = ldk4(qr, qo + s4 * 128 + 16) * qscale;
       uint16_t hb[8], lb[8];
       const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
@@ -1047,11 +1078,11 @@ __device__ __forceinline__ bool task_attn_mm(const Ctx& c, int b, int g, int ci,
     if (tt % kWaves == wave) {
       const int ts = tt / kWaves;
       const int ko = j == jj ? ((dm.Hq + g) * D + r * 8) * 4 : kNoRecord;
-      const float2 vv = ldc2(qr, ((dm.Hq + dm.Hkv + g) * D + 2 * lane) * 4);
+      const float2 vv = ldk2(qr, ((dm.Hq + dm.Hkv + g) * D + 2 * lane) * 4);
       const uint32_t vn = (uint32_t)f2bf(vv.x) | ((uint32_t)f2bf(vv.y) << 16);
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) {
-        const f4v x0 = ldc4(qr, ko + s4 * 128), x1 = ldc4(qr, ko + s4 * 128 + 16);
+        const f4v x0 = ldk4(qr, ko + s4 * 128), x1 = ldk4(qr, ko + s4 * 128 + 16);
         const uint4 kn = make_uint4((uint32_t)f2bf(x0.x) | ((uint32_t)f2bf(x0.y) << 16),
                                     (uint32_t)f2bf(x0.z) | ((uint32_t)f2bf(x0.w) << 16),
                                     (uint32_t)f2bf(x1.x) | ((uint32_t)f2bf(x1.y) << 16),
@@ -1192,14 +1223,14 @@ __device__ __forceinline__ bool task_attn_stream(const Ctx& c, int b, int g, int
   if (!ctx_wait(c, wev)) return false;
 
   // A operand: query head j of the group (zero beyond G), q * log2(e) / sqrt(d) as hi + lo
-  const auto qr = rsrc_n(a.ws.qkv + (size_t)b * qkv_dim, qkv_dim * 4);
+  const auto qr = rsrc_n(qkv_of(a, c.l) + (size_t)b * qkv_dim, qkv_dim * 4);
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
   uint4 qh[4], ql[4];
   {
     const int qo = j < G ? ((g * G + j) * D + r * 8) * 4 : kNoRecord;
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const f4v x0 = ldc4(qr, qo + s4 * 128) * qscale, x1 = ldc4(qr, qo + s4 * 128 + 16) * qscale;
+      const f4v x0 = ldk4(qr, qo + s4 * 128) * qscale, x1 = ldk4(qr, qo + s4 * 128 + 16) * qscale;
       const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       uint32_t hw[4], lw[4];
 #pragma unroll
@@ -1223,11 +1254,11 @@ __device__ __forceinline__ bool task_attn_stream(const Ctx& c, int b, int g, int
     iS = ((S - p0) >> 4) / kWaves;
     jj = (S - p0) & 15;
     const int ko = j == jj ? ((dm.Hq + g) * D + r * 8) * 4 : kNoRecord;
-    const float2 vv = ldc2(qr, ((dm.Hq + dm.Hkv + g) * D + 2 * lane) * 4);
+    const float2 vv = ldk2(qr, ((dm.Hq + dm.Hkv + g) * D + 2 * lane) * 4);
     vn = (uint32_t)f2bf(vv.x) | ((uint32_t)f2bf(vv.y) << 16);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
-      const f4v x0 = ldc4(qr, ko + s4 * 128), x1 = ldc4(qr, ko + s4 * 128 + 16);
+      const f4v x0 = ldk4(qr, ko + s4 * 128), x1 = ldk4(qr, ko + s4 * 128 + 16);
       kn[s4] = make_uint4((uint32_t)f2bf(x0.x) | ((uint32_t)f2bf(x0.y) << 16),
                           (uint32_t)f2bf(x0.z) | ((uint32_t)f2bf(x0.w) << 16),
                           (uint32_t)f2bf(x1.x) | ((uint32_t)f2bf(x1.y) << 16),
@@ -1531,13 +1562,13 @@ __device__ __forceinline__ bool task_combine(const Ctx& c, const int* wev) {
   const auto mo = rsrc(a.ws.mout);   // routed rows: T k H floats, < 2 GiB
   for (int t = c.wg; t < a.batch; t += dm.grid) {
     for (int i = threadIdx.x; i < dm.H / 4; i += kBlock) {
-      f4v x = ldc4(rsrc(a.ws.h1 + (size_t)t * dm.H), i * 16);
+      f4v x = ldk4(rsrc(h1_of(a, c.l) + (size_t)t * dm.H), i * 16);
       for (int j = 0; j < dm.k; ++j) {
         const float w = ldc(a.ws.topk_w + t * dm.k + j);
         const int p = ldci(a.ws.pos_of + t * dm.k + j);
         x += ldc4(mo, (p * dm.H) * 4 + i * 16) * w;
       }
-      stc4(rsrc(a.hidden + (size_t)t * dm.H), i * 16, x);
+      stc4(rsrc(hid_out(a, c.l) + (size_t)t * dm.H), i * 16, x);
     }
   }
   return true;
