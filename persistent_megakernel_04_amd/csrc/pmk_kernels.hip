@@ -293,30 +293,48 @@ struct WaveItems {
   int rg_step;  // row group step between consecutive items
   int ks_lo;    // every item covers k-steps [ks_lo, ks_lo + nks)
   int nks;
+  int sl;       // the wave's k slice (0 when waves own whole row groups)
 };
 
-__device__ __forceinline__ int k_split(int RG) { return RG >= kWaves ? 1 : kWaves / RG; }
+// Waves per row group's k range. Fewer than 8 row groups: 8 / RG waves each,
+// or, when that leaves waves idle (RG = 3, 5, 6, 7) and the partial sums fit
+// the cross-wave buffer, every wave takes one eighth of the k range of every
+// row group. 8 or more row groups: waves own whole row groups.
+__device__ __forceinline__ int k_split(int RG, int nb) {
+  if (RG >= kWaves) return 1;
+  if (kWaves % RG != 0 && RG * kWaves * nb * 16 <= kRedBytes / 4) return kWaves;
+  return kWaves / RG;
+}
 
-__device__ __forceinline__ WaveItems wave_items(int RG, int NKS, int wave) {
+__device__ __forceinline__ WaveItems wave_items(int RG, int NKS, int nb, int wave) {
   WaveItems it;
-  const int ks = k_split(RG);
+  const int ks = k_split(RG, nb);
+  // slices of whole ring lengths, so that no wave pads its range with
+  // dummy steps (the last slice ends at NKS)
+  const int NB = (NKS + kRing - 1) / kRing;
+  auto slice = [&](int sl) {
+    it.sl = sl;
+    it.ks_lo = min(sl * NB / ks * kRing, NKS);
+    it.nks = min((sl + 1) * NB / ks * kRing, NKS) - it.ks_lo;
+  };
   if (ks == 1) {
     it.n = wave < RG ? (RG - wave + kWaves - 1) / kWaves : 0;
     it.rg0 = wave;
     it.rg_step = kWaves;
+    it.sl = 0;
     it.ks_lo = 0;
     it.nks = NKS;
+  } else if (ks * RG > kWaves) {   // every wave: its slice of every row group
+    it.n = RG;
+    it.rg0 = 0;
+    it.rg_step = 1;
+    slice(wave);
   } else {
     const bool busy = wave < RG * ks;
-    const int sl = wave % ks;
     it.n = busy ? 1 : 0;
     it.rg0 = busy ? wave / ks : 0;
     it.rg_step = 0;
-    // slices of whole ring lengths, so that no wave pads its range with
-    // dummy steps (the last slice ends at NKS)
-    const int NB = (NKS + kRing - 1) / kRing;
-    it.ks_lo = min(sl * NB / ks * kRing, NKS);
-    it.nks = min((sl + 1) * NB / ks * kRing, NKS) - it.ks_lo;
+    slice(wave % ks);
   }
   return it;
 }
@@ -343,7 +361,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
   const int NKS = (K + T::KSTEP - 1) / T::KSTEP, RG = (R + 15) >> 4;
   const int Kp = NKS * T::KSTEP, XS = Kp + T::XPAD;
   const int kmax = K - T::EPL, kg = grp * T::EPL;
-  const WaveItems wi = wave_items(RG, NKS, wave);
+  const WaveItems wi = wave_items(RG, NKS, nb, wave);
   const int nks = wi.nks, nks_c = nks > 0 ? nks - 1 : 0;
   const int nks_pad = nks > D ? (nks + D - 1) / D * D : D;
   auto item_rows = [&](int it) -> const WT* {
@@ -369,7 +387,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
   const XT* xrow = reinterpret_cast<const XT*>(c.s.xs) + (size_t)(mrow < nb ? mrow : 0) * (SP ? 2 : 1) * XS +
                    wi.ks_lo * T::KSTEP + kg;
   const bool xon = mrow < nb;
-  const int KSPL = k_split(RG);
+  const int KSPL = k_split(RG, nb);
   for (int it = 0; it < wi.n; ++it) {
     const bool has_next = it + 1 < wi.n;
     f4v acc = {0.f, 0.f, 0.f, 0.f};
@@ -427,7 +445,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
       if (KSPL == 1) {
         if (m < nb && j < R) ys[j * nb + m] = acc[e];
       } else if (m < nb) {
-        c.s.red[(wave * nb + m) * 16 + mrow] = acc[e];
+        c.s.red[((rg * KSPL + wi.sl) * nb + m) * 16 + mrow] = acc[e];
       }
     }
     cur = nxt;
