@@ -142,6 +142,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true", help="first run a plain 2 GiB device-to-device copy "
                     "(a kernel of known traffic, for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--schedule", default="fused", choices=["fused", "layer", "stage", "barrier"],
+                    help="fused: the whole stack in one persistent launch per step (the default); layer / stage: "
+                    "an ablation that puts a kernel boundary after every layer / every stage of a layer; barrier: "
+                    "one launch with a grid-wide barrier after every stage")
     ap.add_argument("--trace", default=None, help="after the timed steps, run one traced step and write a "
                     "per-stage summary of the task trace to this file")
     args = ap.parse_args()
@@ -201,6 +205,9 @@ def main():
         cpu_case = Case(w, L, layers, kv, hid[0].clone(), steps_lens[0].clone(), B, max_seq)
 
     model = DecodeModel.from_workload(w, layers, B, max_seq)
+    model.set_schedule(args.schedule)
+    stages_per_layer = 8 if w.n_experts else 5
+    launches = {"fused": 2, "barrier": 2, "layer": 1 + L, "stage": 1 + L * stages_per_layer}[args.schedule]
     info = model.info()
     log(f"handle: grid={info['grid']} block={info['block']} lds={info['lds_bytes']} "
         f"workspace={info['workspace_bytes'] / 2**20:.1f} MiB")
@@ -224,14 +231,14 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
-    main_ms, launches = model.timing_read()
+    main_ms, timed_steps = model.timing_read()
     model.timing_enable(False)
     err = model.device_error()
     if err != 0:
         sys.exit(f"device error {err} during the timed steps")
-    assert launches == K, (launches, K)
+    assert timed_steps == K, (timed_steps, K)
     ms_per_step = total_ms / K
-    avg_main_ms = main_ms / launches
+    avg_main_ms = main_ms / timed_steps
 
     # algorithmic bytes: average over the K steps (lengths grow by one per step)
     by = [step_bytes(w, (lens0 + i).tolist()) for i in range(K)]
@@ -277,7 +284,8 @@ def main():
                       "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn": w.ffn_dim,
                       "experts": w.n_experts, "global_batch": B,
                       "seq_len_start": [int(x) for x in lens0[:8]], "weights": w.dtype, "kv_cache": w.dtype,
-                      "accumulate": "f32", "parallelism": "single GPU", "launches_per_step": 2},
+                      "accumulate": "f32", "parallelism": "single GPU", "schedule": args.schedule,
+                      "launches_per_step": launches},
            "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 

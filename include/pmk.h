@@ -176,6 +176,30 @@ int pmk_query(const pmk_handle* h, pmk_info* out);
 int pmk_timing_enable(pmk_handle* h, int enable);
 int pmk_timing_read(pmk_handle* h, double* total_ms, int32_t* launches);
 
+/* Schedule of a step (an ablation of the fused design; Event Tensor summary,
+ * Evaluation: the gain of fine-grained pipelining over kernel boundaries):
+ *   PMK_SCHED_FUSED      one persistent launch per step, stages chained by
+ *                        events (the default);
+ *   PMK_SCHED_PER_LAYER  one launch of the same persistent kernel per layer:
+ *                        events inside a layer, a kernel boundary between layers;
+ *   PMK_SCHED_PER_STAGE  one launch per stage of each layer (QKV, attention, O,
+ *                        gate/up, down; MoE: router, routing, expert gate/up,
+ *                        expert down, combine): every grid-wide event becomes
+ *                        a kernel boundary;
+ *   PMK_SCHED_BARRIER    one persistent launch per step with a grid-wide
+ *                        barrier after every stage: no workgroup starts a task
+ *                        of the next stage (nor its weight prefetch) before
+ *                        every workgroup has finished the current one (the
+ *                        pages' unfused megakernel).
+ * The same task code and results in every mode (per-step prologue included);
+ * timing (pmk_timing_*) covers all persistent launches of a step. Applies to
+ * later calls. Errors: PMK_ERR_ARG (null handle, unknown mode). */
+#define PMK_SCHED_FUSED 0
+#define PMK_SCHED_PER_LAYER 1
+#define PMK_SCHED_PER_STAGE 2
+#define PMK_SCHED_BARRIER 3
+int pmk_set_schedule(pmk_handle* h, int32_t mode);
+
 /* Task trace for profiling the schedule. `buf` is a caller-owned device buffer
  * of grid * entries_per_wg * 8 uint32 (grid from pmk_query); NULL detaches.
  * While attached, every call records, per workgroup w, at

@@ -30,6 +30,7 @@ struct pmk_handle {
   int trace_cap = 0;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> tev;
   size_t tused = 0;
+  int sched = PMK_SCHED_FUSED;
 };
 
 namespace {
@@ -191,6 +192,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
       {(void**)&ws.args, sizeof(StepArgs)},
       {(void**)&ws.kpart, kpart_floats * 4},
       {(void**)&ws.tctr, (size_t)4 * G * kCtr * 4},
+      {(void**)&ws.bar, (size_t)dm.L * kMaxStages * kEvInts * 4},
   };
   if (moe) {
     const std::vector<Part> mp = {
@@ -294,6 +296,7 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
   if (rout) a.rout = *rout;
   a.trace = h->trace;
   a.trace_cap = h->trace_cap;
+  a.barrier = h->sched == PMK_SCHED_BARRIER;
   h->last_stream = s;
   if (launch_prologue(a, s) != hipSuccess) return PMK_ERR_DEVICE;
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -308,8 +311,30 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
     ++h->tused;
     if (hipEventRecord(e0, s) != hipSuccess) return PMK_ERR_DEVICE;
   }
-  if (launch_main(a, h->desc.dtype, s) != hipSuccess) return PMK_ERR_DEVICE;
+  const int L = h->dm.L;
+  if (h->sched == PMK_SCHED_FUSED || h->sched == PMK_SCHED_BARRIER) {
+    if (launch_main(a, h->desc.dtype, s, RunSpec{0, L, kAllTypes, a.barrier}) != hipSuccess) return PMK_ERR_DEVICE;
+  } else {
+    // the stages of a layer, in queue order; a per-layer schedule runs them all in one launch
+    auto bit = [](int t) { return 1u << t; };
+    std::vector<unsigned> stages = {bit(T_QKV), bit(T_ATTN) | bit(T_ATTS), bit(T_O)};
+    if (h->dm.moe)
+      for (int t : {T_ROUTER, T_ROUTE, T_MGU, T_MDOWN, T_COMBINE}) stages.push_back(bit(t));
+    else
+      for (int t : {T_GU, T_DOWN}) stages.push_back(bit(t));
+    if (h->sched == PMK_SCHED_PER_LAYER) stages = {kAllTypes};
+    for (int l = 0; l < L; ++l)
+      for (unsigned types : stages)
+        if (launch_main(a, h->desc.dtype, s, RunSpec{l, l + 1, types, 0}) != hipSuccess) return PMK_ERR_DEVICE;
+  }
   if (e1 && hipEventRecord(e1, s) != hipSuccess) return PMK_ERR_DEVICE;
+  return PMK_OK;
+}
+
+int pmk_set_schedule(pmk_handle* h, int32_t mode) {
+  if (!h || mode < PMK_SCHED_FUSED || mode > PMK_SCHED_BARRIER)
+    return PMK_ERR_ARG;
+  h->sched = mode;
   return PMK_OK;
 }
 

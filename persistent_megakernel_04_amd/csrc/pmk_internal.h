@@ -20,6 +20,7 @@ constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxNb = 16;               // batch rows per GEMV pass (MFMA M)
 constexpr int kMaxBatchAll = 1024;       // largest max_batch (prologue LDS)
+constexpr int kMaxStages = 8;            // stages of a layer (MoE: QKV, attention, O, router, route, gate/up, down, combine)
 
 // LDS layout (bytes): [xy: a GEMV pass's staged inputs (xs), then its outputs
 // (ys) | red: cross-wave partial sums | misc]. Attention and routing use the xy
@@ -133,6 +134,7 @@ struct Workspace {
   void* args;          // a copy of this step's StepArgs, written by the prologue
   float* kpart;        // split-K partial sums: [tile][slice][rows nb + 16] of the current stage
   int* tctr;           // [4][grid * kCtr] per row tile: slices done (reset by the last one)
+  int* bar;            // [L][kMaxStages][kEvInts]     stage barriers (barrier schedule only)
   // MoE
   float* logits;       // [max_batch][E]
   int* topk_idx;       // [max_batch][k]
@@ -164,11 +166,22 @@ struct StepArgs {
   pmk_routing rout;                    // optional routing outputs (device pointers)
   uint32_t* trace;                     // optional task trace [grid][trace_cap][8], caller-owned
   int trace_cap;                       // entries per workgroup (entry 0 is the header)
+  int barrier;                         // 1: the barrier schedule (the prologue arms ws.bar)
 };
+
+// What one launch of the persistent kernel runs: layers [l0, l1), and of
+// their queue entries only the task types whose bit (1 << type) is set;
+// barrier: a grid-wide barrier after every stage of every layer.
+struct RunSpec {
+  int l0, l1;
+  unsigned types;
+  int barrier;
+};
+constexpr unsigned kAllTypes = 0xffffffffu;
 
 // Launch wrappers (defined in pmk_kernels.hip).
 hipError_t launch_prologue(const StepArgs& a, hipStream_t s);
-hipError_t launch_main(const StepArgs& a, int dtype, hipStream_t s);
+hipError_t launch_main(const StepArgs& a, int dtype, hipStream_t s, RunSpec rs);
 hipError_t prepare_main(int dtype);
 
 }  // namespace pmk

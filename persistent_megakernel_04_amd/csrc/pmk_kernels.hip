@@ -1600,8 +1600,25 @@ __device__ __forceinline__ bool gemv_task(int type) {
   return type == T_QKV || type == T_O || type == T_GU || type == T_DOWN || type == T_ROUTER || type == T_MGU ||
          type == T_MDOWN;
 }
-template <typename WT>
-__global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict__ pa) {
+// Stage of a task type within its layer, in queue order.
+__device__ __forceinline__ int stage_of(int type) {
+  switch (type) {
+    case T_QKV: return 0;
+    case T_ATTN: case T_ATTS: return 1;
+    case T_O: return 2;
+    case T_GU: case T_ROUTER: return 3;
+    case T_DOWN: case T_ROUTE: return 4;
+    case T_MGU: return 5;
+    case T_MDOWN: return 6;
+    default: return 7;
+  }
+}
+
+// kPart: a launch of an ablation schedule, which runs the layers and task
+// types `rs` names, with a grid-wide barrier after every stage if rs.barrier;
+// the fused launch (kPart false) runs everything, chained by events alone.
+template <typename WT, bool kPart>
+__global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict__ pa, RunSpec rs) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const StepArgs& a = *pa;
   const Dims& dm = a.dm;
@@ -1613,8 +1630,24 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
   const int n = ldu(a.ws.qlen + wg);
   const int4* q = a.ws.queue + (size_t)wg * dm.max_queue;
   uint32_t* tr = a.trace ? a.trace + (size_t)wg * a.trace_cap * 8 : nullptr;
-  int tn = 1;
-  int l = 0, t = 0;
+  // records accumulate over the launches of a step (the prologue zeroes the counts)
+  int tn = tr ? ldu(reinterpret_cast<const int*>(tr)) + 1 : 1;
+  const int l_end = kPart ? rs.l1 : dm.L;
+  auto mine = [&](int type) { return !kPart || ((rs.types >> type) & 1u); };
+  int l = kPart ? rs.l0 : 0, t = 0;
+  // barrier schedule: barrier i = l * ns + stage is passed once every
+  // workgroup has finished its tasks of that stage; `arrived` counts the
+  // barriers this workgroup has arrived at (it arrives at every one, waits on
+  // the last before its first task of a later stage, and arrives at the rest
+  // when its queue ends)
+  const bool bars = kPart && rs.barrier;
+  const int ns = dm.moe ? kMaxStages : 5;
+  int arrived = 0;
+  auto barrier_to = [&](int bi) -> bool {
+    if (arrived >= bi) return true;
+    for (; arrived < bi; ++arrived) wg_notify(a.ws.bar + (size_t)arrived * kEvInts, wg & (kSubs - 1));
+    return ctx_wait(Ctx{a, l, wg, s}, a.ws.bar + (size_t)(bi - 1) * kEvInts);
+  };
   unsigned passed = 0;   // events of layer l (bit e) and l - 1 (bit 16 + e) this workgroup has seen fired
   // the event a task type waits on, or nullptr once this workgroup has seen it at zero
   auto need = [&](int e, int el) -> const int* {
@@ -1651,10 +1684,15 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
     return t0;
   };
   if (n > 0) {
-    while (l < dm.L) {
+    while (l < l_end) {
       int4 task = ldu4(q + t);
       const int tix = task.x >> 8;   // attention tasks: the task's index within the stage
       task.x &= 0xff;
+      if (!mine(task.x)) {   // not this launch's (a per-stage schedule)
+        advance();
+        continue;
+      }
+      if (bars && !barrier_to(l * ns + stage_of(task.x))) return;
       if (!gemv_task(task.x)) {
         const Ctx c{a, l, wg, s};
         const uint32_t t_begin = begin();
@@ -1735,13 +1773,15 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
         if (done && notify >= 0 && wave == 0) wave_notify(ev_ptr(a, l, notify), sub);
         record(task.x, t_begin);
         advance();
-        if (l >= dm.L) break;
+        if (l >= l_end || bars) break;
         task = ldu4(q + t);
         task.x &= 0xff;
-        if (!gemv_task(task.x)) break;
+        if (!gemv_task(task.x) || !mine(task.x)) break;
       }
     }
   }
+  if (bars)   // the last barrier has no waiter
+    for (; arrived < dm.L * ns - 1; ++arrived) wg_notify(a.ws.bar + (size_t)arrived * kEvInts, wg & (kSubs - 1));
   if (tr && threadIdx.x == 0) *gp(tr) = (uint32_t)(tn - 1);
 }
 
@@ -1951,6 +1991,10 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     }
   }
   for (int idx = tid; idx < 4 * G; idx += blockDim.x) a.ws.tctr[idx * kCtr] = 0;
+  if (a.barrier)   // every workgroup arrives at every stage barrier
+    for (int idx = tid; idx < dm.L * kMaxStages; idx += blockDim.x) arm_tiles(a.ws.bar + (size_t)idx * kEvInts, G, G);
+  if (a.trace)
+    for (int w = tid; w < G; w += blockDim.x) a.trace[(size_t)w * a.trace_cap * 8] = 0;
   // attention merge counters: the pieces (streamed) or chunks of each (request, KV head)
   for (int idx = tid; idx < dm.L * B * dm.Hkv; idx += blockDim.x) {
     const int l = idx / (B * dm.Hkv), rem = idx - l * B * dm.Hkv, b = rem / dm.Hkv, g = rem - b * dm.Hkv;
@@ -1972,9 +2016,17 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
 // ---------------------------------------------------------------------------
 // Launch wrappers
 // ---------------------------------------------------------------------------
+static const void* main_fn(int dtype, bool part) {
+  if (dtype == PMK_BF16) return part ? (const void*)pmk_main<uint16_t, true> : (const void*)pmk_main<uint16_t, false>;
+  return part ? (const void*)pmk_main<float, true> : (const void*)pmk_main<float, false>;
+}
+
 hipError_t prepare_main(int dtype) {
-  const void* f = dtype == PMK_BF16 ? (const void*)pmk_main<uint16_t> : (const void*)pmk_main<float>;
-  return hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  for (bool part : {false, true}) {
+    const hipError_t e = hipFuncSetAttribute(main_fn(dtype, part), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_prologue(const StepArgs& a, hipStream_t s) {
@@ -1982,11 +2034,11 @@ hipError_t launch_prologue(const StepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_main(const StepArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_main(const StepArgs& a, int dtype, hipStream_t s, RunSpec rs) {
   const StepArgs* pa = reinterpret_cast<const StepArgs*>(a.ws.args);
-  void* args[] = {&pa};
-  const void* f = dtype == PMK_BF16 ? (const void*)pmk_main<uint16_t> : (const void*)pmk_main<float>;
-  return hipLaunchCooperativeKernel(f, dim3(a.dm.grid), dim3(kBlock), args, kLdsBytes, s);
+  void* args[] = {&pa, &rs};
+  const bool part = rs.l0 != 0 || rs.l1 != a.dm.L || rs.types != kAllTypes || rs.barrier;
+  return hipLaunchCooperativeKernel(main_fn(dtype, part), dim3(a.dm.grid), dim3(kBlock), args, kLdsBytes, s);
 }
 
 }  // namespace pmk

@@ -103,6 +103,13 @@ class DecodeModel:
         _abi.check(self.lib.pmk_trace_attach(self.handle, _ptr(buf), int(entries_per_wg)), "pmk_trace_attach")
         self._trace = buf
 
+    def set_schedule(self, mode):
+        """'fused' (one persistent launch per step, stages chained by events), 'layer' (one launch per layer),
+        'stage' (one launch per stage of each layer) or 'barrier' (one launch, a grid-wide barrier after every
+        stage): the same task code in every mode."""
+        m = _abi.SCHEDULES[mode] if isinstance(mode, str) else int(mode)
+        _abi.check(self.lib.pmk_set_schedule(self.handle, m), "pmk_set_schedule")
+
     def close(self):
         if getattr(self, "handle", None):
             self.lib.decode_layer_destroy(self.handle)

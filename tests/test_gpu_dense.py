@@ -17,10 +17,13 @@ def announce(msg):
     print(f"[case] {msg}", flush=True)
 
 
-def check_dense(orc, case, tol, requests=None, kv_tol=None):
+def check_dense(orc, case, tol, requests=None, kv_tol=None, sched=None):
     inp = oracle_inputs(case, requests)
     model = make_model(case)
-    announce(f"decode_step {case.w.name} L={case.n_layers} B={case.hidden.shape[0]} lens={to_np(case.seq_lens).tolist()[:8]}")
+    if sched is not None:
+        model.set_schedule(sched)
+    announce(f"decode_step {case.w.name} L={case.n_layers} B={case.hidden.shape[0]} "
+             f"lens={to_np(case.seq_lens).tolist()[:8]} schedule={sched or 'fused'}")
     model.step(case.hidden, case.kv, case.seq_lens)
     torch.cuda.synchronize()
     assert model.device_error() == 0
@@ -186,3 +189,17 @@ def test_f32_split_k_batch16(orc):
     lens = synth.ragged_lengths(16, 1, 300, ("f32_mid", "lens"))
     case = build_case(F32_MID, 16, lens, max_seq=302, tag="t12")
     check_dense(orc, case, F32_MID.tol)
+
+
+@pytest.mark.parametrize("sched", ["layer", "stage", "barrier"])
+@pytest.mark.parametrize("B", [1, 4])
+def test_unfused_schedules_match_oracle(orc, sched, B):
+    """The ablation schedules (one launch of the persistent kernel per layer or
+    per stage of each layer, or one launch with a grid-wide barrier after every
+    stage) run the same tasks: the same results, at batch 1 (attention on
+    workgroups of its own, partials merged by the O-projection) and batch 4
+    (streamed attention, down projection split over K)."""
+    w = synth.get_workload("c3_8b_sweep")
+    lens = [512] if B == 1 else synth.ragged_lengths(B, 512, 2048, ("c3_8b_sweep", "sched", B))
+    case = build_case(w, B, lens, n_layers=2, max_seq=int(max(lens)) + 2, tag=f"t13_{sched}_{B}")
+    check_dense(orc, case, w.tol, sched=sched)

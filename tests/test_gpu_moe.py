@@ -58,13 +58,15 @@ def check_routing_self_consistent(r, T, E, k, bm):
     np.testing.assert_array_equal(r["sorted_slot"], [p[2] for p in pairs])
 
 
-def run_moe(orc, w, T, lens, tag, max_seq=None, zero_router=False, random_gains=False):
+def run_moe(orc, w, T, lens, tag, max_seq=None, zero_router=False, random_gains=False, sched=None):
     case = build_case(w, T, lens, max_seq=max_seq, tag=tag, random_gains=random_gains)
     if zero_router:
         case.layers[0]["w_router"].zero_()
     inp = oracle_inputs(case)
     from persistent_megakernel_04_amd import DecodeModel
     model = DecodeModel.from_workload(w, case.layers, case.max_batch, case.max_seq)
+    if sched is not None:
+        model.set_schedule(sched)
     bm = model.info()["moe_bm"]
     rb = routing_buffers(T, w.n_experts, w.top_k)
     announce(f"moe_layer_step {w.name} T={T} lens={list(lens)[:6]} zero_router={zero_router}")
@@ -162,3 +164,15 @@ def test_decode_step_on_moe_handle_matches_moe_layer_step(orc):
                            inp["hidden"], bm)
     assert rel_l2(to_np(case.hidden), ref) <= w.tol
     model.close()
+
+
+@pytest.mark.parametrize("sched", ["stage", "barrier"])
+def test_moe_unfused_schedules(orc, sched):
+    """Router, routing, expert gate/up, expert down and combine each behind a
+    kernel boundary, or behind a grid-wide barrier: routing and outputs as
+    fused."""
+    w = SMALL_MOE_BF16
+    T = 12
+    lens = synth.ragged_lengths(T, 1, 200, ("small_moe", "sched"))
+    case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, lens, f"m6_{sched}", max_seq=201, sched=sched)
+    compare_moe(w, T, got, ref, rg, rr, bm)
