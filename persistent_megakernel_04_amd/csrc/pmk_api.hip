@@ -126,6 +126,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   dm.kstep = desc->dtype == PMK_BF16 ? 32 : 16;
   dm.xpad = desc->dtype == PMK_BF16 ? 8 : 4;
   dm.attn_mm = desc->dtype == PMK_BF16 && dm.d == 128 && dm.Hq / dm.Hkv <= 8;
+  dm.merge_b = std::min(dm.max_batch, kMergeFloats / (dm.Hq * dm.d));
   const int G = dm.grid;
   dm.qkv_units = (dm.Hq + 2 * dm.Hkv) * dm.d / 2;
   dm.qkv_tiles = std::min(G, dm.qkv_units);
@@ -182,6 +183,8 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
        (size_t)dm.max_batch * std::max(dm.F, 1) * 4},
       {(void**)&ws.hid, (size_t)std::max(dm.L - 1, 1) * dm.max_batch * dm.H * 4, (size_t)dm.max_batch * dm.H * 4},
       {(void**)&ws.part, (size_t)dm.max_batch * dm.Hkv * dm.max_chunks * Gq * (dm.d + 4) * 4},
+      {(void**)&ws.mpart, (size_t)dm.L * std::max(dm.merge_b, 1) * dm.Hkv * kMergeChunks * Gq * (dm.d + 4) * 4,
+       (size_t)std::max(dm.merge_b, 1) * dm.Hkv * kMergeChunks * Gq * (dm.d + 4) * 4},
       {(void**)&ws.rope, (size_t)dm.max_seq * (dm.d / 2) * 8},
       {(void**)&ws.ev, (size_t)dm.L * EV_COUNT * kEvInts * 4},
       {(void**)&ws.mctr, (size_t)dm.L * dm.max_batch * dm.Hkv * kCtr * 4},

@@ -266,11 +266,14 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-// float -> bfloat16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// float -> bfloat16 bits, round to nearest even (the hardware conversion,
+// v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two floats -> packed bfloat16 pair (a in the low half), one conversion
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), b2));
 }
 
 template <typename T> struct Elem;
@@ -327,18 +330,15 @@ template <> struct MM<uint16_t> {
   }
   // four consecutive inputs -> LDS (8 bytes)
   static __device__ __forceinline__ void put4(XT* p, f4v v) {
-    uint2 w;
-    w.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
-    w.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
-    *reinterpret_cast<uint2*>(p) = w;
+    *reinterpret_cast<uint2*>(p) = make_uint2(pk_bf16(v.x, v.y), pk_bf16(v.z, v.w));
   }
   // two-term split x = hi + lo, both bfloat16 (hi nearest to x, lo nearest to
   // the remainder): products with bfloat16 weights are exact in the MFMA's
   // float32 accumulation, so the pair carries x to about 2^-16 relative
   static __device__ __forceinline__ void put4_split(XT* hi, XT* lo, f4v v) {
-    const f4v h = {__uint_as_float((uint32_t)f2bf(v.x) << 16), __uint_as_float((uint32_t)f2bf(v.y) << 16),
-                   __uint_as_float((uint32_t)f2bf(v.z) << 16), __uint_as_float((uint32_t)f2bf(v.w) << 16)};
-    put4(hi, h);
+    const uint32_t h01 = pk_bf16(v.x, v.y), h23 = pk_bf16(v.z, v.w);
+    const f4v h = {bf_lo(h01), bf_hi(h01), bf_lo(h23), bf_hi(h23)};
+    *reinterpret_cast<uint2*>(hi) = make_uint2(h01, h23);
     put4(lo, v - h);
   }
 };

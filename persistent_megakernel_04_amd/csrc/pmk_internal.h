@@ -15,6 +15,8 @@ constexpr int kCtr = 16;                 // ints between two counters (64 bytes)
 constexpr int kEvInts = (1 + kSubs) * kCtr;
 constexpr int kMinChunk = 64;            // smallest attention chunk (KV positions per tile task)
 constexpr int kMaxChunk = 256;           // largest attention chunk
+constexpr int kMergeChunks = 8;          // chunks per request at most when the O-projection merges the partials
+constexpr int kMergeFloats = 4096;       // O-projection inputs (batch rows x Hq d) that one merging pass stages
 constexpr int kMoeBM = 16;               // token rows per grouped-GEMM tile (one MFMA row block)
 constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 512;
@@ -112,6 +114,7 @@ struct Dims {
   int moe;                           // 1 = MoE layers
   int kstep, xpad;                   // GEMV: k elements per weight load step, LDS row padding (by dtype)
   int attn_mm;                       // 1: matrix-core attention (bfloat16 KV, head_dim 128, <= 8 heads per KV head)
+  int merge_b;                       // largest batch whose attention partials the O-projection merges (0: none)
   int max_tiles;                     // MoE: bound on grouped-GEMM row tiles
 };
 
@@ -124,6 +127,7 @@ struct Workspace {
   float* act;          // [L][max_batch][F]                SwiGLU output (dense)
   float* hid;          // [L - 1][max_batch][H]            layer outputs feeding the next layer
   float* part;         // [max_batch][Hkv][max_chunks][G][d + 4]  attention partials (acc, max, sum, pad)
+  float* mpart;        // [L][merge_b][Hkv][kMergeChunks][G][d + 4]  the same, per layer, when the O-projection merges
   float2* rope;        // [max_seq][d / 2]              (cos, sin)
   int* ev;             // [L][EV_COUNT][kEvInts]
   int* mctr;           // [L][max_batch][Hkv][kCtr]     attention merge counters

@@ -82,6 +82,9 @@ __device__ __forceinline__ float* h1_of(const StepArgs& a, int l) { return a.ws.
 __device__ __forceinline__ float* act_of(const StepArgs& a, int l) {
   return a.ws.act + (size_t)l * a.dm.max_batch * a.dm.F;
 }
+__device__ __forceinline__ float* mpart_of(const StepArgs& a, int l) {
+  return a.ws.mpart + (size_t)l * a.dm.merge_b * a.dm.Hkv * kMergeChunks * (a.dm.Hq / a.dm.Hkv) * (a.dm.d + 4);
+}
 __device__ __forceinline__ float* mact_of(const StepArgs& a, int l) {
   return a.ws.mact + (size_t)l * a.dm.max_batch * a.dm.k * a.dm.Fe;
 }
@@ -168,11 +171,12 @@ struct GemvIn {
 // Stage nb input rows into LDS as the MFMA input type, rows XS apart (SPLIT:
 // each row as a hi part and a lo part, XS apart, rows 2 XS apart), zero
 // beyond K up to Kp; per-row sum of squares -> rstd (when in.norm). Each wave
-// takes 256-element blocks of the rows, eight at a time: their loads (and
-// the gains') are issued together with no branch between them, so each one
-// waits only for itself. A block's sum of squares is a wave reduction added
-// to that wave's slot, and the 8 slots are summed in order. The sources are
-// per-layer activations: cached loads.
+// takes an eighth of the rows' 256-element blocks, contiguous, eight blocks
+// at a time: their loads (and the gains') are issued together with no branch
+// between them, so each one waits only for itself. A wave's sum of squares
+// over each row it touches is one wave reduction into that wave's slot, and
+// the 8 slots are summed in order. The sources are per-layer activations:
+// cached loads.
 template <typename WT, bool SPLIT>
 __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int Kp, int XS, const Lds& s) {
   typedef typename MM<WT>::XT XT;
@@ -187,35 +191,45 @@ __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int 
   const int gidx = (in.gather && lane < nb) ? ldci(in.gather + lane) : lane;
   if (lane == 0)
     for (int m = 0; m < nb; ++m) s.ssp[m * kWaves + wave] = 0.f;
-  for (int base = wave; base < NBK; base += kWaves * 8) {
-    f4v v[8], gv[8];
+  // wave w stages the contiguous blocks [w NBK / 8, (w + 1) NBK / 8), one row
+  // segment at a time: a lane sums its squares over the segment, and the
+  // wave adds them up once per segment
+  const int wb1 = (wave + 1) * NBK / kWaves;
+  for (int s0 = wave * NBK / kWaves; s0 < wb1;) {
+    const int m = s0 / BPR, s1 = min(wb1, (m + 1) * BPR);
+    const int srow = __builtin_amdgcn_readlane(gidx, m);
+    float ssq = 0.f;
+    for (int base = s0; base < s1; base += 8) {
+      f4v v[8], gv[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int blk = min(base + u * kWaves, NBK - 1);   // past the end: a valid block, not used
-      const int m = blk / BPR, k = (blk - m * BPR) * 256 + lane * 4;
-      const int srow = __builtin_amdgcn_readlane(gidx, m);
-      const int kc = min(k, K - 4);                      // beyond K: a valid element, zeroed below
-      v[u] = ldk4(src, (srow * in.ld + kc) * 4);
-      gv[u] = ldk4(grs, kc * 4);
-    }
+      for (int u = 0; u < 8; ++u) {
+        const int blk = min(base + u, s1 - 1);   // past the segment: a valid block, not used
+        const int k = (blk - m * BPR) * 256 + lane * 4;
+        const int kc = min(k, K - 4);            // beyond K: a valid element, zeroed below
+        v[u] = ldk4(src, (srow * in.ld + kc) * 4);
+        gv[u] = ldk4(grs, kc * 4);
+      }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int blk = base + u * kWaves;
-      if (blk >= NBK) continue;
-      const int m = blk / BPR, k = (blk - m * BPR) * 256 + lane * 4;
-      f4v x = k < K ? v[u] : f4v{0.f, 0.f, 0.f, 0.f};
-      if (in.norm) {
-        const float ss = wave_sum(x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w);
-        if (lane == 0) s.ssp[m * kWaves + wave] += ss;
-      }
-      x *= has_gain ? gv[u] : f4v{1.f, 1.f, 1.f, 1.f};
-      if (k < Kp) {
-        if (SPLIT)
-          MM<WT>::put4_split(xs + (size_t)m * 2 * XS + k, xs + (size_t)m * 2 * XS + XS + k, x);
-        else
-          MM<WT>::put4(xs + (size_t)m * XS + k, x);
+      for (int u = 0; u < 8; ++u) {
+        const int blk = base + u;
+        if (blk >= s1) continue;
+        const int k = (blk - m * BPR) * 256 + lane * 4;
+        f4v x = k < K ? v[u] : f4v{0.f, 0.f, 0.f, 0.f};
+        ssq += x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+        x *= has_gain ? gv[u] : f4v{1.f, 1.f, 1.f, 1.f};
+        if (k < Kp) {
+          if (SPLIT)
+            MM<WT>::put4_split(xs + (size_t)m * 2 * XS + k, xs + (size_t)m * 2 * XS + XS + k, x);
+          else
+            MM<WT>::put4(xs + (size_t)m * XS + k, x);
+        }
       }
     }
+    if (in.norm) {
+      const float ss = wave_sum(ssq);
+      if (lane == 0) s.ssp[m * kWaves + wave] += ss;
+    }
+    s0 = s1;
   }
   __syncthreads();
   if (in.norm && threadIdx.x < nb) {
@@ -231,15 +245,17 @@ __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int 
 // notified) by log-sum-exp: o = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M).
 // Used when every request has at most 8 chunks and each thread stages at most
 // two 4-element units, so all partial loads of a thread are in flight at once.
+// The partials are this layer's (written once in the step): cached loads.
 template <typename WT, bool SP>
-__device__ __forceinline__ void stage_attn_merge(const StepArgs& a, const GemvIn& in, int nb, int K, int Kp, int XS,
-                                                 const Lds& s) {
+__device__ __forceinline__ void stage_attn_merge(const StepArgs& a, int l, const GemvIn& in, int nb, int K, int Kp,
+                                                 int XS, const Lds& s) {
   typedef typename MM<WT>::XT XT;
   XT* xs = reinterpret_cast<XT*>(s.xs);
   const Dims& dm = a.dm;
   const int d = dm.d, G = dm.Hq / dm.Hkv, DP = d + 4, ck = a.attn_chunk;
   const int K4 = Kp / 4;   // 4-element units per row (K = Hq d, a multiple of 4; zero beyond K)
-  const auto pr = rsrc_n(a.ws.part, dm.max_batch * dm.Hkv * dm.max_chunks * G * DP * 4);
+  // this layer's partials: written once in the step, so read through the caches
+  const auto pr = rsrc_n(mpart_of(a, l), dm.merge_b * dm.Hkv * kMergeChunks * G * DP * 4);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int unit = threadIdx.x + u * kBlock;
@@ -249,22 +265,22 @@ __device__ __forceinline__ void stage_attn_merge(const StepArgs& a, const GemvIn
     if (k < K) {
       const int b = in.merge_b0 + m, nc = (*gp(a.seq_lens + b) + ck) / ck;
       const int h = k / d, e = k - h * d, g = h / G, hh = h - g * G;
-      const int base = ((b * dm.Hkv + g) * dm.max_chunks * G + hh) * DP;   // floats; part is < 2 GiB
-      f4v av[8], mv[8];
+      const int base = ((b * dm.Hkv + g) * kMergeChunks * G + hh) * DP;
+      f4v av[kMergeChunks], mv[kMergeChunks];
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
+      for (int cc = 0; cc < kMergeChunks; ++cc) {
         // a chunk the request does not have reads past the buffer's range:
         // zeros, with no memory access
         const int o = cc < nc ? (base + cc * G * DP) * 4 : kNoRecord;
-        av[cc] = ldc4(pr, o + e * 4);
-        mv[cc] = ldc4(pr, o + d * 4);
+        av[cc] = ldk4(pr, o + e * 4);
+        mv[cc] = ldk4(pr, o + d * 4);
       }
       float M = -INFINITY, L = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc)
+      for (int cc = 0; cc < kMergeChunks; ++cc)
         if (cc < nc) M = fmaxf(M, mv[cc].x);
 #pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
+      for (int cc = 0; cc < kMergeChunks; ++cc) {
         if (cc < nc) {
           const float f = exp2f(mv[cc].x - M);
           L += mv[cc].y * f;
@@ -379,7 +395,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
   }
   if (!ctx_wait(c, wait_ev, wait_subs)) return false;
   if (in.merge_b0 >= 0)
-    stage_attn_merge<WT, SP>(c.a, in, nb, K, Kp, XS, c.s);
+    stage_attn_merge<WT, SP>(c.a, c.l, in, nb, K, Kp, XS, c.s);
   else
     stage_rows<WT, SP>(in, nb, K, Kp, XS, c.s);
   if (tid == 0) c.s.tclk[2] = (uint32_t)now_ticks();
@@ -395,8 +411,8 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
     uint4 xa_n = *reinterpret_cast<const uint4*>(xrow), xl_n = make_uint4(0, 0, 0, 0);
     if (SP) xl_n = *reinterpret_cast<const uint4*>(xrow + XS);
     // one k-step: the input fragment (zero past the item, or for a row >= nb)
-    // times ring slot d, reading the next step's fragment ahead
-    auto step = [&](int ks, int d) {
+    // times weights w, reading the next step's fragment ahead
+    auto step = [&](int ks, const uint4 w) {
       const bool on = xon && ks < nks;
       uint4 xa = xa_n, xl = xl_n;
       const int xo = min(ks + 1, nks_c) * T::KSTEP;
@@ -406,13 +422,13 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
       xa.y = on ? xa.y : 0u;
       xa.z = on ? xa.z : 0u;
       xa.w = on ? xa.w : 0u;
-      acc = T::mac(xa, ring[d], acc);
+      acc = T::mac(xa, w, acc);
       if (SP) {
         xl.x = on ? xl.x : 0u;
         xl.y = on ? xl.y : 0u;
         xl.z = on ? xl.z : 0u;
         xl.w = on ? xl.w : 0u;
-        acc = T::mac(xl, ring[d], acc);
+        acc = T::mac(xl, w, acc);
       }
     };
     // Branch-free blocks, so the compiler's wait counts stay exact (a branch
@@ -422,7 +438,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         const int ks = ks0 + d;
-        step(ks, d);
+        step(ks, ring[d]);
         // refill with the step kRing ahead: of this item, else of the next item
         const int nk = ks + D;
         const bool here = nk < nks_pad;
@@ -435,7 +451,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
     }
     if (!has_next) {
 #pragma unroll
-      for (int d = 0; d < D; ++d) step(nks_pad - D + d, d);
+      for (int d = 0; d < D; ++d) step(nks_pad - D + d, ring[d]);
     }
     // D[m][j] of this item's row group: lane (j + 16 * (m / 4)), element m % 4
     const int rg = wi.rg0 + it * wi.rg_step;
@@ -849,7 +865,8 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, int b, int g, int ci, 
   constexpr int DP = D + 4;
   const int tid = threadIdx.x;
   float* o = o_of(a, c.l) + (size_t)b * dm.Hq * D + (size_t)g * G * D;
-  float* part = a.ws.part + (((size_t)b * dm.Hkv + g) * dm.max_chunks + ci) * G * DP;
+  float* part = a.attn_merge_o ? mpart_of(a, c.l) + (((size_t)b * dm.Hkv + g) * kMergeChunks + ci) * G * DP
+                               : a.ws.part + (((size_t)b * dm.Hkv + g) * dm.max_chunks + ci) * G * DP;
   const auto orr = rsrc(o), prr = rsrc(part);
   for (int t = tid; t < G * D / 4; t += kBlock) {
     const int h = t / (D / 4), e0 = (t - h * (D / 4)) * 4;
@@ -1857,10 +1874,10 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       for (int b = 0; b < B; ++b) mx = max(mx, (a.seq_lens[b] + c) / c);
       return mx;
     };
-    if (B * dm.Hq * dm.d <= 2 * kBlock * 4) {
+    if (B <= dm.merge_b) {
       int c = kMinChunk;
-      while (c < kMaxChunk && max_nc(c) > 8) c <<= 1;
-      if (max_nc(c) <= 8) { ck = c; merge = 1; }
+      while (c < kMaxChunk && max_nc(c) > kMergeChunks) c <<= 1;
+      if (max_nc(c) <= kMergeChunks) { ck = c; merge = 1; }
     }
     if (!merge) {
       while (ck > kMinChunk) {
