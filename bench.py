@@ -146,6 +146,9 @@ def main():
                     help="fused: the whole stack in one persistent launch per step (the default); layer / stage: "
                     "an ablation that puts a kernel boundary after every layer / every stage of a layer; barrier: "
                     "one launch with a grid-wide barrier after every stage")
+    ap.add_argument("--moe-scheduler", default="static", choices=["static", "dynamic"],
+                    help="MoE workloads: grouped expert tasks as fixed per-workgroup shares (static) or popped from "
+                    "a per-layer queue (dynamic)")
     ap.add_argument("--trace", default=None, help="after the timed steps, run one traced step and write a "
                     "per-stage summary of the task trace to this file")
     args = ap.parse_args()
@@ -206,6 +209,8 @@ def main():
 
     model = DecodeModel.from_workload(w, layers, B, max_seq)
     model.set_schedule(args.schedule)
+    if w.n_experts:
+        model.set_moe_scheduler(args.moe_scheduler)
     stages_per_layer = 8 if w.n_experts else 5
     launches = {"fused": 2, "barrier": 2, "layer": 1 + L, "stage": 1 + L * stages_per_layer}[args.schedule]
     info = model.info()
@@ -240,8 +245,19 @@ def main():
     ms_per_step = total_ms / K
     avg_main_ms = main_ms / timed_steps
 
-    # algorithmic bytes: average over the K steps (lengths grow by one per step)
-    by = [step_bytes(w, (lens0 + i).tolist()) for i in range(K)]
+    # algorithmic bytes: average over the K steps (lengths grow by one per step;
+    # a MoE step reads the experts its tokens selected, taken from an untimed
+    # replay of each step's routing)
+    touched = [None] * K
+    if w.n_experts:
+        topk = torch.empty((B, w.top_k), dtype=torch.int32, device=dev)
+        for i in range(K):
+            replay = hid[i].clone()
+            model.step(replay, kv, steps_lens[i], routing={"topk_idx": topk})
+            torch.cuda.synchronize()
+            touched[i] = int(torch.unique(topk).numel())
+        log(f"experts touched per step: {touched[:8]}{'...' if K > 8 else ''}")
+    by = [step_bytes(w, (lens0 + i).tolist(), touched[i]) for i in range(K)]
     bytes_avg = sum(b["total"] for b in by) / K
     achieved = bytes_avg / (avg_main_ms * 1e-3) / 1e9
     step_gbs = bytes_avg / (ms_per_step * 1e-3) / 1e9
@@ -285,6 +301,7 @@ def main():
                       "experts": w.n_experts, "global_batch": B,
                       "seq_len_start": [int(x) for x in lens0[:8]], "weights": w.dtype, "kv_cache": w.dtype,
                       "accumulate": "f32", "parallelism": "single GPU", "schedule": args.schedule,
+                      **({"moe_scheduler": args.moe_scheduler} if w.n_experts else {}),
                       "launches_per_step": launches},
            "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)

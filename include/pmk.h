@@ -200,6 +200,22 @@ int pmk_timing_read(pmk_handle* h, double* total_ms, int32_t* launches);
 #define PMK_SCHED_BARRIER 3
 int pmk_set_schedule(pmk_handle* h, int32_t mode);
 
+/* How the grouped expert GEMM tasks of a MoE layer reach workgroups (Event
+ * Tensor summary, Core method: static and dynamic scheduling):
+ *   PMK_MOE_STATIC   each workgroup runs a fixed share of the gate/up tasks,
+ *                    then of the down tasks, each down task waiting on its
+ *                    expert's counter (the default);
+ *   PMK_MOE_DYNAMIC  workgroups pop task indices from one counter per layer:
+ *                    first the gate/up tasks, then down tasks from a ready
+ *                    queue that the last gate/up task of each expert fills
+ *                    with that expert's down tasks when the expert's counter
+ *                    reaches zero.
+ * Same results either way. Ignored by dense handles; applies to later calls.
+ * Errors: PMK_ERR_ARG (null handle, unknown mode). */
+#define PMK_MOE_STATIC 0
+#define PMK_MOE_DYNAMIC 1
+int pmk_set_moe_scheduler(pmk_handle* h, int32_t mode);
+
 /* Task trace for profiling the schedule. `buf` is a caller-owned device buffer
  * of grid * entries_per_wg * 8 uint32 (grid from pmk_query); NULL detaches.
  * While attached, every call records, per workgroup w, at

@@ -18,10 +18,13 @@ PMK_F32, PMK_BF16 = 0, 1
 # pmk_set_schedule modes (include/pmk.h)
 SCHED_FUSED, SCHED_PER_LAYER, SCHED_PER_STAGE, SCHED_BARRIER = 0, 1, 2, 3
 SCHEDULES = {"fused": SCHED_FUSED, "layer": SCHED_PER_LAYER, "stage": SCHED_PER_STAGE, "barrier": SCHED_BARRIER}
+# pmk_set_moe_scheduler modes
+MOE_STATIC, MOE_DYNAMIC = 0, 1
+MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC}
 
 EXPORTS = ("decode_layer_init", "decode_step", "moe_layer_step", "decode_layer_destroy", "pmk_strerror",
            "pmk_get_device_error", "pmk_query", "pmk_timing_enable", "pmk_timing_read", "pmk_trace_attach",
-           "pmk_set_schedule")
+           "pmk_set_schedule", "pmk_set_moe_scheduler")
 
 i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -92,6 +95,8 @@ def load():
     L.pmk_trace_attach.restype = i32
     L.pmk_set_schedule.argtypes = [vp, i32]
     L.pmk_set_schedule.restype = i32
+    L.pmk_set_moe_scheduler.argtypes = [vp, i32]
+    L.pmk_set_moe_scheduler.restype = i32
     _lib = L
     return L
 

@@ -31,6 +31,7 @@ struct pmk_handle {
   std::vector<std::pair<hipEvent_t, hipEvent_t>> tev;
   size_t tused = 0;
   int sched = PMK_SCHED_FUSED;
+  int moe_sched = PMK_MOE_STATIC;
 };
 
 namespace {
@@ -135,6 +136,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   dm.down_tiles = moe ? 0 : std::min(G, dm.H);
   dm.router_tiles = moe ? ceil_div(dm.E, 16) : 0;
   dm.max_tiles = moe ? ceil_div((long)dm.max_batch * dm.k, kMoeBM) + dm.E : 0;
+  dm.max_down = dm.max_tiles * std::max(dm.H / 16, 1);
   // Dense stages: one input row of the whole depth and a tile's outputs must
   // fit the LDS (a step may put its few attention tasks on workgroups of their
   // own and the QKV tiles on the others, at least three quarters of the grid).
@@ -209,6 +211,9 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
         {(void**)&ws.tile_info, (size_t)dm.max_tiles * 2 * 4},
         {(void**)&ws.moe_info, 64 * 4},
         {(void**)&ws.ectr, (size_t)dm.L * dm.E * kCtr * 4},
+        {(void**)&ws.tile_ptr, (size_t)(dm.E + 1) * 4},
+        {(void**)&ws.rq, (size_t)dm.L * dm.max_down * 4},
+        {(void**)&ws.mq, (size_t)dm.L * 2 * kCtr * 4},
         {(void**)&ws.mact, (size_t)dm.L * TK * dm.Fe * 4, TK * dm.Fe * 4},
         {(void**)&ws.mout, TK * dm.H * 4},
     };
@@ -300,6 +305,7 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
   a.trace = h->trace;
   a.trace_cap = h->trace_cap;
   a.barrier = h->sched == PMK_SCHED_BARRIER;
+  a.moe_dyn = h->dm.moe && h->moe_sched == PMK_MOE_DYNAMIC;
   h->last_stream = s;
   if (launch_prologue(a, s) != hipSuccess) return PMK_ERR_DEVICE;
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -331,6 +337,12 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
         if (launch_main(a, h->desc.dtype, s, RunSpec{l, l + 1, types, 0}) != hipSuccess) return PMK_ERR_DEVICE;
   }
   if (e1 && hipEventRecord(e1, s) != hipSuccess) return PMK_ERR_DEVICE;
+  return PMK_OK;
+}
+
+int pmk_set_moe_scheduler(pmk_handle* h, int32_t mode) {
+  if (!h || (mode != PMK_MOE_STATIC && mode != PMK_MOE_DYNAMIC)) return PMK_ERR_ARG;
+  h->moe_sched = mode;
   return PMK_OK;
 }
 

@@ -189,6 +189,31 @@ __device__ __forceinline__ bool spin_zero(const int* ev, int subs, int* err, uns
   }
 }
 
+// Wave 0 only: spin until *p is nonzero and return it; 0 on abort or
+// watchdog expiry (which sets the error word and the abort flag as above).
+__device__ __forceinline__ int spin_nonzero(const int* p, int* err, unsigned long long ticks) {
+  int v = ldci(p);
+  if (v != 0) return v;
+  const unsigned long long t0 = now_ticks();
+  for (int it = 0;; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    v = ldci(p);
+    if (v != 0) return v;
+    if ((it & 15) == 15) {
+      if (ldci(err + 16) != 0) return 0;
+      if (now_ticks() - t0 > ticks) {
+        if ((threadIdx.x & 63) == 0) {
+          int expected = 0;
+          __hip_atomic_compare_exchange_strong(gp(err), &expected, (int)PMK_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          stci(err + 16, 1);
+        }
+        return 0;
+      }
+    }
+  }
+}
+
 // Whole workgroup: wait until the event has fired (wave 0 spins, the others
 // park at the barrier). `flag` is an LDS int. Returns false if the step was
 // abandoned.

@@ -116,6 +116,7 @@ struct Dims {
   int attn_mm;                       // 1: matrix-core attention (bfloat16 KV, head_dim 128, <= 8 heads per KV head)
   int merge_b;                       // largest batch whose attention partials the O-projection merges (0: none)
   int max_tiles;                     // MoE: bound on grouped-GEMM row tiles
+  int max_down;                      // MoE: bound on grouped down tasks (row tiles x H slices)
 };
 
 // Device workspace (one allocation, carved by the host).
@@ -150,6 +151,9 @@ struct Workspace {
   int* tile_info;      // [max_tiles][2]  (expert, first grouped row) of each row tile
   int* moe_info;       // [0] gate/up tasks, [1] down tasks, [2] gate/up slices, [3] down slices, [4] tiles
   int* ectr;           // [L][E][kCtr]                  per-expert counters (gate/up -> down)
+  int* tile_ptr;       // [E + 1]                       first row tile of each expert (tile_indptr)
+  int* rq;             // [L][max_down]                 dynamic: ready down tasks, index + 1 (0: not yet pushed)
+  int* mq;             // [L][2][kCtr]                  dynamic: pop counter, push counter
   float* mact;         // [L][max_batch k][Fe]          expert SwiGLU rows, grouped order (per layer)
   float* mout;         // [max_batch k][H]              expert down rows, grouped order
 };
@@ -171,6 +175,7 @@ struct StepArgs {
   uint32_t* trace;                     // optional task trace [grid][trace_cap][8], caller-owned
   int trace_cap;                       // entries per workgroup (entry 0 is the header)
   int barrier;                         // 1: the barrier schedule (the prologue arms ws.bar)
+  int moe_dyn;                         // 1: grouped expert tasks popped from a per-layer queue
 };
 
 // What one launch of the persistent kernel runs: layers [l0, l1), and of

@@ -562,6 +562,19 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   ps.tile = tile;
   ps.slice = 0;
   ps.ks = 1;
+  // grouped down task i = (row tile i / sd, H slice i % sd); waits on its expert's counter
+  auto mdown = [&](int i) {
+    const int sd = ldsu(a.ws.moe_info + 3), t = i / sd, sl = i - t * sd;
+    const int e = ldsu(a.ws.tile_info + 2 * t), row0 = ldsu(a.ws.tile_info + 2 * t + 1);
+    const int h0 = (int)((long)sl * dm.H / sd), R = (int)((long)(sl + 1) * dm.H / sd) - h0;
+    ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_down)) + (size_t)e * dm.H * dm.Fe,
+                     nullptr, h0, 0, dm.Fe, 0};
+    ps.in = GemvIn{mact_of(a, c.l) + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f, -1};
+    ps.R = R; ps.K = dm.Fe; ps.kfull = dm.Fe; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
+    ps.wev = a.ws.ectr + ((size_t)c.l * dm.E + e) * kCtr;
+    ps.wsubs = 0;
+    ps.epi = E_MDOWN; ps.b0 = row0; ps.r0 = h0; ps.n = R; ps.e = e;
+  };
   // the K slice of a dense task, its rows per pass and first batch row
   int k0 = 0, kn = 0, b0 = 0, nbb = 0;
   auto dense = [&](int stage, int K, int R, int units, int urows) -> bool {
@@ -629,9 +642,34 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       ps.epi = E_ROUTER; ps.b0 = br; ps.r0 = r0; ps.n = ps.R;
       break;
     }
-    case T_MGU: {   // grouped gate/up task i = (row tile i / sg, Fe slice i % sg) of this workgroup's share
-      const int i = c.wg + p * dm.grid;
-      if (i >= ldsu(a.ws.moe_info + 0)) return false;
+    case T_MGU: {   // grouped gate/up task i = (row tile i / sg, Fe slice i % sg)
+      int i = c.wg + p * dm.grid;   // static: this workgroup's share
+      const int nmgu = ldsu(a.ws.moe_info + 0);
+      if (a.moe_dyn) {
+        // dynamic: the next index of the layer's queue, gate/up tasks [0, nmgu),
+        // then down tasks in the order their experts became ready
+        if (threadIdx.x == 0) *c.s.flag = atomic_add_relaxed(a.ws.mq + (size_t)c.l * 2 * kCtr, 1);
+        __syncthreads();
+        i = __builtin_amdgcn_readfirstlane(*c.s.flag);
+        __syncthreads();
+        if (i >= nmgu) {
+          const int j = i - nmgu;
+          if (j >= ldsu(a.ws.moe_info + 1)) return false;
+          if (threadIdx.x < 64) {
+            const int v = spin_nonzero(a.ws.rq + (size_t)c.l * dm.max_down + j, a.ws.err, a.watchdog_ticks);
+            if (threadIdx.x == 0) *c.s.flag = v;
+          }
+          __syncthreads();
+          const int v = __builtin_amdgcn_readfirstlane(*c.s.flag);
+          __syncthreads();
+          if (v == 0) return false;   // abandoned step
+          mdown(v - 1);
+          ps.wev = nullptr;           // ready once queued
+          break;
+        }
+      } else if (i >= nmgu) {
+        return false;
+      }
       const int sg = ldsu(a.ws.moe_info + 2), t = i / sg, sl = i - t * sg;
       const int e = ldsu(a.ws.tile_info + 2 * t), row0 = ldsu(a.ws.tile_info + 2 * t + 1);
       const int f0 = (int)((long)sl * dm.Fe / sg), Rh = (int)((long)(sl + 1) * dm.Fe / sg) - f0;
@@ -644,19 +682,10 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       ps.epi = E_MGU; ps.b0 = row0; ps.r0 = f0; ps.n = Rh; ps.e = e;
       break;
     }
-    case T_MDOWN: {  // grouped down task i = (row tile i / sd, H slice i % sd); waits on its expert's counter
+    case T_MDOWN: {  // static: this workgroup's share of the down tasks (dynamic: popped with the gate/up ones)
       const int i = c.wg + p * dm.grid;
-      if (i >= ldsu(a.ws.moe_info + 1)) return false;
-      const int sd = ldsu(a.ws.moe_info + 3), t = i / sd, sl = i - t * sd;
-      const int e = ldsu(a.ws.tile_info + 2 * t), row0 = ldsu(a.ws.tile_info + 2 * t + 1);
-      const int h0 = (int)((long)sl * dm.H / sd), R = (int)((long)(sl + 1) * dm.H / sd) - h0;
-      ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_down)) + (size_t)e * dm.H * dm.Fe,
-                       nullptr, h0, 0, dm.Fe, 0};
-      ps.in = GemvIn{mact_of(a, c.l) + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f, -1};
-      ps.R = R; ps.K = dm.Fe; ps.kfull = dm.Fe; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
-      ps.wev = a.ws.ectr + ((size_t)c.l * dm.E + e) * kCtr;
-      ps.wsubs = 0;
-      ps.epi = E_MDOWN; ps.b0 = row0; ps.r0 = h0; ps.n = R; ps.e = e;
+      if (a.moe_dyn || i >= ldsu(a.ws.moe_info + 1)) return false;
+      mdown(i);
       break;
     }
     default: return false;
@@ -798,8 +827,23 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
         const float gt = ys[j * nb + m] * r, up = ys[(Rh + j) * nb + m] * r;
         stc(out + (size_t)(b0 + m) * ld + ps.r0 + j, gt / (1.0f + __expf(-gt)) * up);
       }
-      if (ps.epi == E_MGU)   // this task of expert e is done
-        wave_notify(a.ws.ectr + ((size_t)c.l * dm.E + ps.e) * kCtr, -1);
+      if (ps.epi == E_MGU) {   // this task of expert e is done
+        int* ec = a.ws.ectr + ((size_t)c.l * dm.E + ps.e) * kCtr;
+        if (!a.moe_dyn) {
+          wave_notify(ec, -1);
+        } else {
+          // the expert's last gate/up task queues the expert's down tasks
+          vm_drain();
+          const int left = __shfl(lane == 0 ? atomic_add_relaxed(ec, -1) : 0, 0, 64);
+          if (left == 1) {
+            const int t0 = ldci(a.ws.tile_ptr + ps.e), t1 = ldci(a.ws.tile_ptr + ps.e + 1);
+            const int sd = ldci(a.ws.moe_info + 3), n = (t1 - t0) * sd;
+            const int slot = __shfl(lane == 0 ? atomic_add_relaxed(a.ws.mq + ((size_t)c.l * 2 + 1) * kCtr, n) : 0, 0, 64);
+            int* rq = a.ws.rq + (size_t)c.l * dm.max_down + slot;
+            for (int i = lane; i < n; i += 64) stci(rq + i, t0 * sd + i + 1);
+          }
+        }
+      }
       break;
     }
     case E_ROUTER: {
@@ -1441,26 +1485,79 @@ __device__ __forceinline__ int wave_scan(int v) {
 //             sorted_slot = routed (token, slot) ordered by expert then token;
 //   arming:   the counter of expert e starts at e's number of gate/up tasks
 //             (its row tiles x gate/up slices) -- the data-dependent event.
+// A logit as an unsigned key whose order is the float order (-0 taken as +0).
+__device__ __forceinline__ uint32_t ord_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// Largest (hi, lo) pair over each row of 16 lanes, every lane of the row gets it.
+template <int CTRL> __device__ __forceinline__ void key_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, CTRL, 0xF, 0xF, false);
+  const uint32_t ol = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, CTRL, 0xF, 0xF, false);
+  const bool take = oh > hi || (oh == hi && ol > lo);
+  hi = take ? oh : hi;
+  lo = take ? ol : lo;
+}
+// Over groups of GS = 16 lanes (a row) or 64 (the wave).
+template <int GS> __device__ __forceinline__ void key_max(uint32_t& hi, uint32_t& lo) {
+  key_step<0xB1>(hi, lo);
+  key_step<0x4E>(hi, lo);
+  key_step<0x141>(hi, lo);
+  key_step<0x140>(hi, lo);
+  if constexpr (GS == 64) {
+    auto cross = [&](auto swap) {
+      float ah = __uint_as_float(hi), bh = ah, al = __uint_as_float(lo), bl = al;
+      swap(ah, bh);
+      swap(al, bl);
+      const uint32_t h0 = __float_as_uint(ah), l0 = __float_as_uint(al);
+      const uint32_t h1 = __float_as_uint(bh), l1 = __float_as_uint(bl);
+      const bool take = h1 > h0 || (h1 == h0 && l1 > l0);
+      hi = take ? h1 : h0;
+      lo = take ? l1 : l0;
+    };
+    cross([](float& x, float& y) { swap16(x, y); });
+    cross([](float& x, float& y) { swap32(x, y); });
+  }
+}
+
+// GS lanes per token (16 while the experts fit 8 per lane, else the wave).
+template <int GS>
 __device__ __forceinline__ bool task_route(const Ctx& c, const int* wev) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   if (!ctx_wait(c, wev)) return false;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-  const int T = a.batch, E = dm.E, k = dm.k, Tk = T * k, G = dm.grid;
+  const int T = a.batch, E = dm.E, k = dm.k, Tk = T * k, G = dm.grid, TW = (T + 31) >> 5;
   int* sidx = reinterpret_cast<int*>(c.s.xs);   // [T k]
   int* cnt = sidx + dm.max_batch * kMaxTopK;     // [E]
   int* ptr = cnt + kMaxExperts;                  // [E + 1]
   int* tptr = ptr + kMaxExperts + 1;             // [E + 1]
-  constexpr int EPLN = kMaxExperts / 64;
-  constexpr int NONE = 0x7fffffff;
-  for (int t = wave; t < T; t += kWaves) {
-    float z[EPLN];
-    unsigned taken = 0;
+  // [E][TW]: bit t of expert e's row is set when token t selected e
+  uint32_t* sel = reinterpret_cast<uint32_t*>(tptr + kMaxExperts + 1);
+  for (int i = tid; i < E * TW; i += kBlock) sel[i] = 0;
+  __syncthreads();
+  // top-k: a token per group of GS lanes, lane r of the group holding experts
+  // r, r + GS, ...; k rounds of a group-wide maximum of (logit, -index) keys.
+  // The next tokens' logits are loaded while these are selected.
+  constexpr int EPG = 8, TPW = 64 / GS;   // experts per lane, tokens per wave
+  const int row = lane / GS, rl = lane % GS, ng = (E + GS - 1) / GS;
+  auto load = [&](int t, float (&z)[EPG]) {
 #pragma unroll
-    for (int i = 0; i < EPLN; ++i) {
-      const int e = lane + 64 * i;
-      z[i] = e < E ? ldc(a.ws.logits + (size_t)t * E + e) : -INFINITY;
+    for (int i = 0; i < EPG; ++i) {
+      const int e = rl + GS * i;
+      z[i] = (t < T && i < ng && e < E) ? ldc(a.ws.logits + (size_t)t * E + e) : 0.f;
     }
+  };
+  float z[EPG];
+  load(wave * TPW + row, z);
+  for (int t0 = wave * TPW; t0 < T; t0 += kWaves * TPW) {
+    const int t = t0 + row;
+    float zn[EPG];
+    load(t + kWaves * TPW, zn);
+    uint32_t taken = 0;
     float zsel[kMaxTopK];
     int isel[kMaxTopK];
 #pragma unroll
@@ -1468,50 +1565,52 @@ __device__ __forceinline__ bool task_route(const Ctx& c, const int* wev) {
       zsel[j] = 0.f;
       isel[j] = 0;
       if (j >= k) continue;
-      // this lane's best untaken entry by (logit desc, index asc), then the wave's
-      float bv = -INFINITY;
-      int bi = NONE;
+      uint32_t bh = 0, bl = 0;   // below every valid key
 #pragma unroll
-      for (int i = 0; i < EPLN; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !(taken & (1u << i)) && (bi == NONE || z[i] > bv || (z[i] == bv && e < bi))) {
-          bv = z[i];
-          bi = e;
+      for (int i = 0; i < EPG; ++i) {
+        const int e = rl + GS * i;
+        if (i < ng && e < E && !(taken & (1u << i))) {
+          const uint32_t kh = ord_key(z[i]), kl = ~(uint32_t)e;
+          if (kh > bh || (kh == bh && kl > bl)) {
+            bh = kh;
+            bl = kl;
+          }
         }
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (oi != NONE && (bi == NONE || ov > bv || (ov == bv && oi < bi))) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-      zsel[j] = bv;
+      key_max<GS>(bh, bl);
+      const int bi = (int)~bl;
+      if (bi % GS == rl) taken |= 1u << (bi / GS);
+      zsel[j] = key_value(bh);
       isel[j] = bi;
     }
-    if (lane == 0) {
-      float w[kMaxTopK], sum = 0.f;
+    if (t < T) {
+      if (rl == 0) {
+        float w[kMaxTopK], sum = 0.f;
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        w[j] = j < k ? __expf(zsel[j] - zsel[0]) : 0.f;
-        sum += w[j];
-      }
+        for (int j = 0; j < kMaxTopK; ++j) {
+          w[j] = j < k ? __expf(zsel[j] - zsel[0]) : 0.f;
+          sum += w[j];
+        }
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j < k) {
-          sidx[t * k + j] = isel[j];
-          stc(a.ws.topk_w + t * k + j, w[j] / sum);
+        for (int j = 0; j < kMaxTopK; ++j) {
+          if (j < k) {
+            sidx[t * k + j] = isel[j];
+            stc(a.ws.topk_w + t * k + j, w[j] / sum);
+          }
         }
       }
+      int mine = 0;
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) mine = rl == j ? isel[j] : mine;
+      if (rl < k) atomicOr(&sel[mine * TW + (t >> 5)], 1u << (t & 31));
     }
+#pragma unroll
+    for (int i = 0; i < EPG; ++i) z[i] = zn[i];
   }
   __syncthreads();
   for (int e = tid; e < E; e += kBlock) {
     int n = 0;
-    for (int i = 0; i < Tk; ++i) n += sidx[i] == e;
+    for (int w = 0; w < TW; ++w) n += __popc(sel[e * TW + w]);
     cnt[e] = n;
   }
   __syncthreads();
@@ -1535,27 +1634,35 @@ __device__ __forceinline__ bool task_route(const Ctx& c, const int* wev) {
   const int target = (2 * G + ntiles - 1) / ntiles;
   const int sg = min(max(target, (2 * dm.Fe * kMaxNb + kYsFloats - 1) / kYsFloats), max(dm.Fe / 16, 1));
   const int sd = min(max(target, (dm.H * kMaxNb + kYsFloats - 1) / kYsFloats), max(dm.H / 16, 1));
+  // scatter in (expert, token) order: (t, j) goes after the tokens below t
+  // that selected the same expert (a token selects an expert at most once)
+  for (int i = tid; i < Tk; i += kBlock) {
+    const int t = i / k, e = sidx[i];
+    const uint32_t* r = sel + e * TW;
+    int rank = __popc(r[t >> 5] & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < (t >> 5); ++w) rank += __popc(r[w]);
+    const int pos = ptr[e] + rank;
+    stci(a.ws.sorted_tok + pos, t);
+    stci(a.ws.sorted_slot + pos, i - t * k);
+    stci(a.ws.pos_of + i, pos);
+  }
   for (int e = tid; e < E; e += kBlock) {
-    // scatter in (expert, token) order; a token selects an expert at most once
-    int pos = ptr[e];
-    for (int i = 0; i < Tk; ++i) {
-      if (sidx[i] == e) {
-        stci(a.ws.sorted_tok + pos, i / k);
-        stci(a.ws.sorted_slot + pos, i % k);
-        stci(a.ws.pos_of + i, pos);
-        ++pos;
-      }
-    }
     for (int tt = tptr[e]; tt < tptr[e + 1]; ++tt) {
       stci(a.ws.tile_info + 2 * tt, e);
       stci(a.ws.tile_info + 2 * tt + 1, ptr[e] + (tt - tptr[e]) * kMoeBM);
     }
     stci(a.ws.ectr + ((size_t)c.l * E + e) * kCtr, (tptr[e + 1] - tptr[e]) * sg);
     stci(a.ws.exp_indptr + e + 1, ptr[e + 1]);
+    stci(a.ws.tile_ptr + e + 1, tptr[e + 1]);
+  }
+  if (a.moe_dyn) {   // this layer's task queue: empty, nothing popped or pushed yet
+    for (int i = tid; i < ntiles * sd; i += kBlock) stci(a.ws.rq + (size_t)c.l * dm.max_down + i, 0);
+    if (tid < 2) stci(a.ws.mq + ((size_t)c.l * 2 + tid) * kCtr, 0);
   }
   for (int i = tid; i < Tk; i += kBlock) stci(a.ws.topk_idx + i, sidx[i]);
   if (tid == 0) {
     stci(a.ws.exp_indptr, 0);
+    stci(a.ws.tile_ptr, 0);
     stci(a.ws.moe_info + 0, ntiles * sg);
     stci(a.ws.moe_info + 1, ntiles * sd);
     stci(a.ws.moe_info + 2, sg);
@@ -1728,7 +1835,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
             break;
           }
           case T_ROUTE:
-            ok = task_route(c, need(EV_ROUTER, l));
+            ok = dm.E <= 128 ? task_route<16>(c, need(EV_ROUTER, l)) : task_route<64>(c, need(EV_ROUTER, l));
             break;
           case T_COMBINE:
             ok = task_combine(c, need(EV_MDOWN, l));

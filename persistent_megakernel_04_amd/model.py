@@ -110,6 +110,12 @@ class DecodeModel:
         m = _abi.SCHEDULES[mode] if isinstance(mode, str) else int(mode)
         _abi.check(self.lib.pmk_set_schedule(self.handle, m), "pmk_set_schedule")
 
+    def set_moe_scheduler(self, mode):
+        """'static' (each workgroup a fixed share of the grouped expert tasks) or 'dynamic' (tasks popped from
+        a per-layer queue, down tasks queued as their experts' gate/up tasks finish)."""
+        m = _abi.MOE_SCHEDULERS[mode] if isinstance(mode, str) else int(mode)
+        _abi.check(self.lib.pmk_set_moe_scheduler(self.handle, m), "pmk_set_moe_scheduler")
+
     def close(self):
         if getattr(self, "handle", None):
             self.lib.decode_layer_destroy(self.handle)

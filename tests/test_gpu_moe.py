@@ -58,7 +58,8 @@ def check_routing_self_consistent(r, T, E, k, bm):
     np.testing.assert_array_equal(r["sorted_slot"], [p[2] for p in pairs])
 
 
-def run_moe(orc, w, T, lens, tag, max_seq=None, zero_router=False, random_gains=False, sched=None):
+def run_moe(orc, w, T, lens, tag, max_seq=None, zero_router=False, random_gains=False, sched=None,
+            moe_sched=None):
     case = build_case(w, T, lens, max_seq=max_seq, tag=tag, random_gains=random_gains)
     if zero_router:
         case.layers[0]["w_router"].zero_()
@@ -67,6 +68,8 @@ def run_moe(orc, w, T, lens, tag, max_seq=None, zero_router=False, random_gains=
     model = DecodeModel.from_workload(w, case.layers, case.max_batch, case.max_seq)
     if sched is not None:
         model.set_schedule(sched)
+    if moe_sched is not None:
+        model.set_moe_scheduler(moe_sched)
     bm = model.info()["moe_bm"]
     rb = routing_buffers(T, w.n_experts, w.top_k)
     announce(f"moe_layer_step {w.name} T={T} lens={list(lens)[:6]} zero_router={zero_router}")
@@ -175,4 +178,24 @@ def test_moe_unfused_schedules(orc, sched):
     T = 12
     lens = synth.ragged_lengths(T, 1, 200, ("small_moe", "sched"))
     case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, lens, f"m6_{sched}", max_seq=201, sched=sched)
+    compare_moe(w, T, got, ref, rg, rr, bm)
+
+
+@pytest.mark.parametrize("T", [1, 16, 128])
+def test_moe_dynamic_scheduler(orc, T):
+    """Grouped expert tasks popped from the layer's queue, down tasks queued by
+    the last gate/up task of their expert: routing bit-exact and outputs
+    within tolerance, from one token (8 experts) to 128 (every expert)."""
+    w = synth.get_workload("c4_moe")
+    lens = synth.ragged_lengths(T, 1, 2048, ("c4_moe", "dyn", T))
+    case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, lens, f"m7_{T}", max_seq=2049, moe_sched="dynamic")
+    compare_moe(w, T, got, ref, rg, rr, bm)
+
+
+def test_moe_dynamic_small_bf16(orc):
+    """The dynamic queue on a layer with few experts and rows per tile."""
+    w = SMALL_MOE_BF16
+    T = 20
+    lens = synth.ragged_lengths(T, 1, 300, ("small_moe", "lens"))
+    case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, lens, "m8", max_seq=301, moe_sched="dynamic")
     compare_moe(w, T, got, ref, rg, rr, bm)
