@@ -167,6 +167,17 @@ def test_70b_shape_four_layers_b8_sampled(orc):
     check_dense(orc, case, w.tol, requests=[0, 5])
 
 
+@pytest.mark.parametrize("B", [64, 128])
+def test_8b_shape_large_batch_sampled(orc, B):
+    """The batch sweep's two largest points: passes of 16 rows over every
+    projection, attention in equal shares of the laid-out positions; two
+    layers, lengths in [512, 8192], three sampled requests."""
+    w = synth.get_workload("c3_8b_sweep")
+    lens = synth.ragged_lengths(B, 512, 8192, ("c3_8b_sweep", "lens", B))
+    case = build_case(w, B, lens, n_layers=2, max_seq=int(lens.max()) + 2, tag=f"t14_{B}")
+    check_dense(orc, case, w.tol, requests=[int(np.argmax(lens)), int(np.argmin(lens)), B - 1])
+
+
 @pytest.mark.parametrize("B", [8, 12, 16])
 def test_8b_shape_split_k_every_request(orc, B):
     """Batches whose staged inputs outgrow the LDS: the projections run as K

@@ -199,3 +199,14 @@ def test_moe_dynamic_small_bf16(orc):
     lens = synth.ragged_lengths(T, 1, 300, ("small_moe", "lens"))
     case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, lens, "m8", max_seq=301, moe_sched="dynamic")
     compare_moe(w, T, got, ref, rg, rr, bm)
+
+
+@pytest.mark.parametrize("sched", ["static", "dynamic"])
+def test_moe_1024_tokens(orc, sched):
+    """The MoE layer at 1024 tokens (every expert several row tiles deep), short
+    KV lengths so the oracle stays quick: routing and outputs of every token."""
+    w = synth.get_workload("c4_moe")
+    T = 1024
+    lens = synth.ragged_lengths(T, 1, 64, ("c4_moe", "big", T))
+    case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, lens, f"m9_{sched}", max_seq=65, moe_sched=sched)
+    compare_moe(w, T, got, ref, rg, rr, bm)
