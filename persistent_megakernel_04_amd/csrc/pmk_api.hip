@@ -156,15 +156,21 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     for (int nb = 2; nb <= std::min(dm.max_batch, kMaxNb); ++nb)
       for (int avail : {G - G / 4, G}) {
         const StageGeo g = stage_geo(K4[st], U4[st], R4[st], nb, avail, dm.kstep, dm.xpad);
+        // more than 16 rows: the same split for 16, one record per batch block
+        const size_t blocks = nb == kMaxNb ? (size_t)ceil_div(dm.max_batch, kMaxNb) : 1;
         if (g.ks > 1)
-          kpart_floats = std::max(kpart_floats, (size_t)g.tiles * g.ks *
+          kpart_floats = std::max(kpart_floats, blocks * g.tiles * g.ks *
                                                     ((size_t)ceil_div(U4[st], g.tiles) * R4[st] * nb + 16));
       }
   }
   const long attn_max = (long)dm.max_batch * dm.Hkv * dm.max_chunks;
   // a workgroup's attention share may also hold one piece of every (request, KV head)
+  // batch blocks: a dense stage's (tile, slice, block) tasks, slices and tiles
+  // of a stage at most the grid, in groups of 8 per block
+  const int nblk = ceil_div(dm.max_batch, kMaxNb);
+  dm.tctr_stride = G * nblk;
   dm.max_queue = ceil_div(dm.qkv_tiles, G) + ceil_div(dm.o_tiles, G) + ceil_div(attn_max, G) +
-                 dm.max_batch * dm.Hkv + 8;
+                 dm.max_batch * dm.Hkv + 8 + 4 * (ceil_div((G + 8) * nblk, G) + 1);
   if (moe)
     dm.max_queue += ceil_div((long)dm.router_tiles * ceil_div(dm.max_batch, kMaxNb), G) + 4;
   else
@@ -196,7 +202,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
       {(void**)&ws.err, 64 * 4},
       {(void**)&ws.args, sizeof(StepArgs)},
       {(void**)&ws.kpart, kpart_floats * 4},
-      {(void**)&ws.tctr, (size_t)4 * G * kCtr * 4},
+      {(void**)&ws.tctr, (size_t)4 * dm.tctr_stride * kCtr * 4},
       {(void**)&ws.bar, (size_t)dm.L * kMaxStages * kEvInts * 4},
   };
   if (moe) {
@@ -273,10 +279,10 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     a0.layers = h->d_layers;
     a0.attn_chunk = kMaxChunk;
     a0.qkv_tiles = dm.qkv_tiles;
-    a0.geo[0] = StageGeo{1, dm.qkv_tiles, dm.H};
-    a0.geo[1] = StageGeo{1, dm.o_tiles, dm.Hq * dm.d};
-    a0.geo[2] = StageGeo{1, std::max(dm.gu_tiles, 1), dm.H};
-    a0.geo[3] = StageGeo{1, std::max(dm.down_tiles, 1), std::max(dm.F, 1)};
+    a0.geo[0] = StageGeo{1, dm.qkv_tiles, dm.H, 1};
+    a0.geo[1] = StageGeo{1, dm.o_tiles, dm.Hq * dm.d, 1};
+    a0.geo[2] = StageGeo{1, std::max(dm.gu_tiles, 1), dm.H, 1};
+    a0.geo[3] = StageGeo{1, std::max(dm.down_tiles, 1), std::max(dm.F, 1), 1};
     if (hipMemcpy(ws.args, &a0, sizeof(a0), hipMemcpyHostToDevice) != hipSuccess) return fail(PMK_ERR_DEVICE);
   }
   if (prepare_main(desc->dtype) != hipSuccess) return fail(PMK_ERR_DEVICE);

@@ -47,6 +47,7 @@ constexpr int kRingK = 16;               // weight loads in flight per wave
 constexpr int kMaxKs = 8;                // K slices of a split stage at most
 struct StageGeo {
   int ks, tiles, kr;    // kr: slice length (elements); the last slice ends at K
+  int blk;              // > 1: the batch in blocks of 16 rows, each (tile, slice, block) a task of its own
 };
 __host__ __device__ inline StageGeo stage_geo(int K, int units, int urows, int nb, int avail, int kstep, int xpad) {
   const int grain = kRingK * kstep;
@@ -61,8 +62,8 @@ __host__ __device__ inline StageGeo stage_geo(int K, int units, int urows, int n
     const int rows = (units + tiles - 1) / tiles * urows;
     const long xs = (long)nb * ((kr + kstep - 1) / kstep * kstep + xpad) * 4;
     const long need = (xs + 15) / 16 * 16 + (long)rows * nb * 4;
-    if (kse > kMaxKs) return StageGeo{0, 0, 0};   // no split fits: passes over the batch instead
-    if (need <= kXyBytes || kr <= grain) return StageGeo{kse, tiles, kr};
+    if (kse > kMaxKs) return StageGeo{0, 0, 0, 1};   // no split fits: passes over the batch instead
+    if (need <= kXyBytes || kr <= grain) return StageGeo{kse, tiles, kr, 1};
   }
 }
 
@@ -116,6 +117,7 @@ struct Dims {
   int attn_mm;                       // 1: matrix-core attention (bfloat16 KV, head_dim 128, <= 8 heads per KV head)
   int merge_b;                       // largest batch whose attention partials the O-projection merges (0: none)
   int max_tiles;                     // MoE: bound on grouped-GEMM row tiles
+  int tctr_stride;                   // split-K tile counters per stage: grid x batch blocks
   int max_down;                      // MoE: bound on grouped down tasks (row tiles x H slices)
 };
 
@@ -138,7 +140,7 @@ struct Workspace {
   int* err;            // [0] error word, [16] abort flag
   void* args;          // a copy of this step's StepArgs, written by the prologue
   float* kpart;        // split-K partial sums: [tile][slice][rows nb + 16] of the current stage
-  int* tctr;           // [4][grid * kCtr] per row tile: slices done (reset by the last one)
+  int* tctr;           // [4][tctr_stride][kCtr] per (batch block, row tile): slices done (reset by the last one)
   int* bar;            // [L][kMaxStages][kEvInts]     stage barriers (barrier schedule only)
   // MoE
   float* logits;       // [max_batch][E]

@@ -578,12 +578,15 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   // the K slice of a dense task, its rows per pass and first batch row
   int k0 = 0, kn = 0, b0 = 0, nbb = 0;
   auto dense = [&](int stage, int K, int R, int units, int urows) -> bool {
-    const StageGeo g{ldu(&a.geo[stage].ks), ldu(&a.geo[stage].tiles), ldu(&a.geo[stage].kr)};
+    const StageGeo g{ldu(&a.geo[stage].ks), ldu(&a.geo[stage].tiles), ldu(&a.geo[stage].kr),
+                     ldu(&a.geo[stage].blk)};
+    const bool one = g.ks > 1 || g.blk > 1;   // one pass of up to 16 rows: batch block task.w
     k0 = task.z * g.kr;
     kn = min(K, k0 + g.kr) - k0;
-    nbb = g.ks > 1 ? kMaxNb : pass_rows<WT>(kn, R);
-    b0 = p * nbb;
-    if (b0 >= a.batch || (g.ks > 1 && p > 0)) return false;
+    nbb = one ? kMaxNb : pass_rows<WT>(kn, R);
+    b0 = task.w * kMaxNb + p * nbb;
+    if (b0 >= a.batch || (one && p > 0)) return false;
+    ps.tile = tile + task.w * g.tiles;   // the split record and counter of (block, tile)
     ps.stage = stage;
     ps.slice = task.z;
     ps.ks = g.ks;
@@ -592,7 +595,8 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
     ps.R = R;
     ps.nb = min(nbb, a.batch - b0);
     ps.b0 = b0;
-    ps.rs = (units + g.tiles - 1) / g.tiles * urows * ps.nb + 16;
+    // one record stride for every block of the stage (the last may be short)
+    ps.rs = (units + g.tiles - 1) / g.tiles * urows * (g.blk > 1 ? kMaxNb : ps.nb) + 16;
     return true;
   };
   switch (task.x) {
@@ -740,7 +744,7 @@ __device__ __forceinline__ bool reduce_slices(const Ctx& c, const Pass& ps) {
   vm_drain();
   __syncthreads();
   if (tid == 0) {
-    int* ctr = a.ws.tctr + ((size_t)ps.stage * a.dm.grid + ps.tile) * kCtr;
+    int* ctr = a.ws.tctr + ((size_t)ps.stage * a.dm.tctr_stride + ps.tile) * kCtr;
     const int last = atomic_add_relaxed(ctr, 1) == ps.ks - 1;
     if (last) stci(ctr, 0);   // every slice has counted: ready for this stage of the next layer
     *c.s.flag = last;
@@ -1927,10 +1931,11 @@ __device__ __forceinline__ void arm_tiles(int* ev, int tiles, int grid) {
   for (int x = 0; x < kSubs; ++x) ev[(1 + x) * kCtr] = sub_count(tiles, grid, x);
 }
 
-// Arm an event with n notifiers indexed i that notify sub-counter i % kSubs.
-__device__ __forceinline__ void arm_indexed(int* ev, int n) {
+// Arm an event with n notifiers indexed i that notify sub-counter i % kSubs,
+// each `mult` times.
+__device__ __forceinline__ void arm_indexed(int* ev, int n, int mult = 1) {
   ev[0] = 0;
-  for (int x = 0; x < kSubs; ++x) ev[(1 + x) * kCtr] = n > x ? (n - x + kSubs - 1) / kSubs : 0;
+  for (int x = 0; x < kSubs; ++x) ev[(1 + x) * kCtr] = (n > x ? (n - x + kSubs - 1) / kSubs : 0) * mult;
 }
 
 // Arm an event on counter [0] alone.
@@ -2021,14 +2026,17 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     const int own = (merge && total_attn <= G / 4) ? total_attn : 0;
     attn_wg0_s = own ? G - own : G;
     // each dense stage's split (see stage_geo): up to 16 rows, one pass over
-    // K slices that fit the LDS; beyond, passes of rows over the whole depth
+    // K slices that fit the LDS; beyond, the split of 16 rows for every block
+    // of 16 (or, where no split fits, passes of rows over the whole depth)
     const int K4[4] = {dm.H, dm.Hq * dm.d, dm.H, dm.F};
     const int U4[4] = {dm.qkv_units, dm.H, dm.F, dm.H};
     const int R4[4] = {2, 1, 2, 1};
     for (int st = 0; st < 4; ++st) {
       const int avail = st == 0 ? G - own : G;
-      StageGeo g = B <= kMaxNb ? stage_geo(K4[st], U4[st], R4[st], B, avail, dm.kstep, dm.xpad) : StageGeo{0, 0, 0};
-      if (g.ks == 0) g = StageGeo{1, min(avail, U4[st]), K4[st]};
+      // more than 16 rows: the split of 16, and every 16-row block its own tasks
+      StageGeo g = stage_geo(K4[st], U4[st], R4[st], min(B, kMaxNb), avail, dm.kstep, dm.xpad);
+      if (B > kMaxNb && g.ks) g.blk = (B + kMaxNb - 1) / kMaxNb;
+      if (g.ks == 0) g = StageGeo{1, min(avail, U4[st]), K4[st], 1};
       geo_s[st] = g;
       copy->geo[st] = g;
     }
@@ -2047,10 +2055,23 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       ++n;
     };
     const int aw0 = attn_wg0_s;
-    // task i of a dense stage: row tile i / ks, K slice i % ks, on workgroup i % G
+    // task i of a dense stage: row tile i / ks, K slice i % ks, on workgroup
+    // i % G. In batch blocks, the blocks of one (tile, slice) go to
+    // workgroups 8 apart, which share an L2 (one XCD), so that they stream the
+    // same weights together: groups of 8 (tile, slice) pairs, each group's
+    // blocks one after another.
     auto stage_tasks = [&](int type, int st) {
       const StageGeo g = geo_s[st];
-      for (int i = w; i < g.tiles * g.ks; i += G) push(make_int4(type, i / g.ks, i % g.ks, 0));
+      const int TS = g.tiles * g.ks;
+      if (g.blk <= 1) {
+        for (int i = w; i < TS; i += G) push(make_int4(type, i / g.ks, i % g.ks, 0));
+        return;
+      }
+      const int per = 8 * g.blk;
+      for (int i = w; i < (TS + 7) / 8 * per; i += G) {
+        const int grp = i / per, r = i - grp * per, ts = grp * 8 + (r & 7);
+        if (ts < TS) push(make_int4(type, ts / g.ks, ts % g.ks, r >> 3));
+      }
     };
     stage_tasks(T_QKV, 0);
     if (stream_s) {   // this workgroup's share of the laid-out positions
@@ -2099,14 +2120,14 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     const int e = idx % EV_COUNT;
     int* ev = a.ws.ev + (size_t)idx * kEvInts;
     switch (e) {
-      // dense stages: one notifier per row tile, on sub-counter tile % kSubs
-      case EV_QKV: arm_indexed(ev, geo_s[0].tiles); break;
+      // dense stages: one notifier per row tile (and batch block), on sub-counter tile % kSubs
+      case EV_QKV: arm_indexed(ev, geo_s[0].tiles, geo_s[0].blk); break;
       // one notifier per chunk task (partials merged by the O-projection), or per (request, KV head)
       case EV_ATTN: arm_indexed(ev, merge_s ? total_attn : B * dm.Hkv); break;
-      case EV_O: arm_indexed(ev, geo_s[1].tiles); break;
-      case EV_GU: arm_indexed(ev, dm.moe ? 0 : geo_s[2].tiles); break;
+      case EV_O: arm_indexed(ev, geo_s[1].tiles, geo_s[1].blk); break;
+      case EV_GU: arm_indexed(ev, dm.moe ? 0 : geo_s[2].tiles, geo_s[2].blk); break;
       case EV_DOWN:   // MoE: one combine slot per workgroup
-        if (dm.moe) arm_tiles(ev, G, G); else arm_indexed(ev, geo_s[3].tiles);
+        if (dm.moe) arm_tiles(ev, G, G); else arm_indexed(ev, geo_s[3].tiles, geo_s[3].blk);
         break;
       case EV_ROUTER: arm_tiles(ev, router_tasks, G); break;
       case EV_ROUTE: arm_flat(ev, dm.moe ? 1 : 0); break;
@@ -2114,7 +2135,10 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       default: arm_flat(ev, 0); break;
     }
   }
-  for (int idx = tid; idx < 4 * G; idx += blockDim.x) a.ws.tctr[idx * kCtr] = 0;
+  for (int idx = tid; idx < 4 * G * ((B + kMaxNb - 1) / kMaxNb); idx += blockDim.x) {
+    const int used = G * ((B + kMaxNb - 1) / kMaxNb), st = idx / used;   // (block, tile) records of each stage
+    a.ws.tctr[((size_t)st * dm.tctr_stride + idx - st * used) * kCtr] = 0;
+  }
   if (a.barrier)   // every workgroup arrives at every stage barrier
     for (int idx = tid; idx < dm.L * kMaxStages; idx += blockDim.x) arm_tiles(a.ws.bar + (size_t)idx * kEvInts, G, G);
   if (a.trace)
