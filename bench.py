@@ -231,8 +231,10 @@ def main():
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
+    h0 = time.perf_counter()
     for i in range(K):
         model.step(hid_work[i], kv, steps_lens[i])
+    host_us = (time.perf_counter() - h0) / K * 1e6   # host time to submit a step (the launches are asynchronous)
     e1.record()
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
@@ -301,6 +303,7 @@ def main():
                       "experts": w.n_experts, "global_batch": B,
                       "seq_len_start": [int(x) for x in lens0[:8]], "weights": w.dtype, "kv_cache": w.dtype,
                       "accumulate": "f32", "parallelism": "single GPU", "schedule": args.schedule,
+                      "host_submit_us_per_step": round(host_us, 1),
                       **({"moe_scheduler": args.moe_scheduler} if w.n_experts else {}),
                       "launches_per_step": launches},
            "roofline": roofline, "cpu_baseline": cpu}

@@ -84,4 +84,22 @@ def summary(rec: np.ndarray) -> str:
                      "".join(f"{np.mean(parts[c]):>8.2f}" for c in cols) + f"{np.mean(wmax):>10.2f}")
     per_layer = [rec[rec["layer"] == l]["t1"].max() - rec[rec["layer"] == l]["t0"].min() for l in layers]
     lines.append(f"layer span (first take to last finish): mean {np.mean(per_layer):.2f} us")
+    s = sync_overhead(rec)
+    lines.append(f"event waits: {s['wait_us']:.1f} us per workgroup ({100 * s['wait_frac']:.1f} % of its span), "
+                 f"{s['spin_total_us']:.0f} workgroup-us in all; between tasks {s['between_us']:.1f} us per workgroup")
     return "\n".join(lines)
+
+
+def sync_overhead(rec: np.ndarray) -> dict:
+    """Synchronisation cost of a traced step, per workgroup: the time its tasks spent between being taken and
+    their input event being seen (spinning, with their weight loads in flight), and the time outside any task,
+    against the workgroup's span from its first take to its last finish."""
+    waits, spans, between = [], [], []
+    for w in np.unique(rec["wg"]):
+        r = rec[rec["wg"] == w]
+        span = float(r["t1"].max() - r["t0"].min())
+        waits.append(float(np.sum(r["ready"] - r["t0"])))
+        between.append(span - float(np.sum(r["t1"] - r["t0"])))
+        spans.append(span)
+    return {"wait_us": float(np.mean(waits)), "wait_frac": float(np.sum(waits) / max(np.sum(spans), 1e-9)),
+            "spin_total_us": float(np.sum(waits)), "between_us": float(np.mean(between))}
