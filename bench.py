@@ -149,6 +149,10 @@ def main():
     ap.add_argument("--moe-scheduler", default="static", choices=["static", "dynamic"],
                     help="MoE workloads: grouped expert tasks as fixed per-workgroup shares (static) or popped from "
                     "a per-layer queue (dynamic)")
+    ap.add_argument("--flush-cache", action="store_true",
+                    help="between timed steps, write a 1 GiB buffer so that no weight stays in the 256 MB "
+                    "memory-side cache (for working sets that fit it, e.g. the MoE layer at one token); the "
+                    "roofline then rests on the persistent kernel's own launch times, which exclude the writes")
     ap.add_argument("--trace", default=None, help="after the timed steps, run one traced step and write a "
                     "per-stage summary of the task trace to this file")
     args = ap.parse_args()
@@ -230,9 +234,12 @@ def main():
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush_cache else None
     e0.record()
     h0 = time.perf_counter()
     for i in range(K):
+        if flush is not None:
+            flush.fill_(float(i))
         model.step(hid_work[i], kv, steps_lens[i])
     host_us = (time.perf_counter() - h0) / K * 1e6   # host time to submit a step (the launches are asynchronous)
     e1.record()
@@ -303,7 +310,7 @@ def main():
                       "experts": w.n_experts, "global_batch": B,
                       "seq_len_start": [int(x) for x in lens0[:8]], "weights": w.dtype, "kv_cache": w.dtype,
                       "accumulate": "f32", "parallelism": "single GPU", "schedule": args.schedule,
-                      "host_submit_us_per_step": round(host_us, 1),
+                      "host_submit_us_per_step": round(host_us, 1), "cache_flushed": bool(args.flush_cache),
                       **({"moe_scheduler": args.moe_scheduler} if w.n_experts else {}),
                       "launches_per_step": launches},
            "roofline": roofline, "cpu_baseline": cpu}
