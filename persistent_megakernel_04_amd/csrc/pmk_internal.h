@@ -14,6 +14,7 @@ constexpr int kSubs = 8;                 // sub-counters of a hierarchical event
 constexpr int kCtr = 16;                 // ints between two counters (64 bytes)
 constexpr int kEvInts = (1 + kSubs) * kCtr;
 constexpr int kMinChunk = 64;            // smallest attention chunk (KV positions per tile task)
+constexpr int kPieceCost = 320;          // streamed attention: a piece's fixed cost in KV positions
 constexpr int kMaxChunk = 256;           // largest attention chunk
 constexpr int kMergeChunks = 8;          // chunks per request at most when the O-projection merges the partials
 constexpr int kMergeFloats = 4096;       // O-projection inputs (batch rows x Hq d) that one merging pass stages

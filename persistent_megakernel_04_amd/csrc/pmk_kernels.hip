@@ -2016,7 +2016,10 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     }
     cb[B] = acc;
     total_attn = acc * dm.Hkv;
-    const long P = (long)acc * dm.Hkv;
+    // streamed shares: every (request, KV head) range is laid out behind a
+    // lead of kPieceCost positions (what a piece costs beyond its positions),
+    // so that a share that starts a range holds fewer positions
+    const long P = stream ? (long)dm.Hkv * (acc + (long)B * kPieceCost) : (long)acc * dm.Hkv;
     share_s = max(64, (int)((P + G - 1) / G + 15) / 16 * 16);
     copy->attn_chunk = ck;
     // A few attention tasks (at most a quarter of the grid) get workgroups of
@@ -2075,21 +2078,26 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       }
     };
     stage_tasks(T_QKV, 0);
-    if (stream_s) {   // this workgroup's share of the laid-out positions
-      const long share = share_s, hi = min((long)(w + 1) * share, (long)total_attn);
+    if (stream_s) {   // this workgroup's share of the laid-out ranges
+      // range (b, g) spans [seg0, seg0 + kPieceCost + S_b + 1): its lead, then its positions
+      auto start = [&](int b) { return (long)dm.Hkv * (cb[b] + (long)b * kPieceCost); };
+      const long share = share_s, hi = min((long)(w + 1) * share, start(B));
       for (long pos = (long)w * share; pos < hi;) {
-        int lo = 0, up = B;   // request b: Hkv*cb[b] <= pos < Hkv*cb[b+1]
+        int lo = 0, up = B;   // request b: start(b) <= pos < start(b + 1)
         while (up - lo > 1) {
           const int mid = (lo + up) >> 1;
-          if ((long)dm.Hkv * cb[mid] <= pos) lo = mid; else up = mid;
+          if (start(mid) <= pos) lo = mid; else up = mid;
         }
-        const int len = cb[lo + 1] - cb[lo];
-        const int g = (int)((pos - (long)dm.Hkv * cb[lo]) / len);
-        const long seg0 = (long)dm.Hkv * cb[lo] + (long)g * len, seg1 = seg0 + len, e = min(hi, seg1);
-        // pieces of a range are cut at multiples of the share: this is piece
-        // w - seg0 / share of (seg1 - 1) / share - seg0 / share + 1
-        const int piece = w - (int)(seg0 / share), np = (int)((seg1 - 1) / share - seg0 / share) + 1;
-        push(make_int4(T_ATTS | (piece << 8) | (np << 20), lo | (g << 16), (int)(pos - seg0), (int)(e - seg0)));
+        const int len = cb[lo + 1] - cb[lo], span = len + kPieceCost;
+        const int g = (int)((pos - start(lo)) / span);
+        const long seg0 = start(lo) + (long)g * span, r0 = seg0 + kPieceCost, seg1 = seg0 + span;
+        const long e = min(hi, seg1), p0 = max(pos, r0);
+        if (e > p0) {
+          // pieces of a range are cut at multiples of the share: this is piece
+          // w - r0 / share of (seg1 - 1) / share - r0 / share + 1
+          const int piece = w - (int)(r0 / share), np = (int)((seg1 - 1) / share - r0 / share) + 1;
+          push(make_int4(T_ATTS | (piece << 8) | (np << 20), lo | (g << 16), (int)(p0 - r0), (int)(e - r0)));
+        }
         pos = e;
       }
     }
@@ -2148,9 +2156,9 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   for (int idx = tid; idx < dm.L * B * dm.Hkv; idx += blockDim.x) {
     const int l = idx / (B * dm.Hkv), rem = idx - l * B * dm.Hkv, b = rem / dm.Hkv, g = rem - b * dm.Hkv;
     int n = cb[b + 1] - cb[b];
-    if (stream_s) {
-      const long seg0 = (long)dm.Hkv * cb[b] + (long)g * n, seg1 = seg0 + n;
-      n = (int)((seg1 - 1) / share_s - seg0 / share_s) + 1;
+    if (stream_s) {   // the workgroups whose shares meet the range's positions
+      const long r0 = (long)dm.Hkv * (cb[b] + (long)b * kPieceCost) + (long)g * (n + kPieceCost) + kPieceCost;
+      n = (int)((r0 + n - 1) / share_s - r0 / share_s) + 1;
     }
     a.ws.mctr[(((size_t)l * dm.max_batch + b) * dm.Hkv + g) * kCtr] = n;
   }
