@@ -41,9 +41,23 @@ template <typename T> __device__ __forceinline__ T* uptr(T* p) {
   const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
   return (T*)(((unsigned long long)hi << 32) | lo);
 }
-// Plain global load of a pointer field of an immutable struct (the same for
-// the whole wave; kept scalar, so descriptors built from it need no loop).
-template <typename T> __device__ __forceinline__ T* ldp(T* const* field) { return uptr(*gp(field)); }
+// Loads of data that nothing writes while the persistent kernel runs (the
+// queues, the step's split, layer pointers, request lengths: written by the
+// host or by the prologue kernel before it) at a wave-uniform address, through
+// the constant address space: scalar loads via the scalar cache, which do not
+// wait behind the wave's vector loads in flight. Kept scalar.
+typedef const __attribute__((address_space(4))) int* kptr_i;
+__device__ __forceinline__ int ldku(const int* p) { return __builtin_amdgcn_readfirstlane(*(kptr_i)(p)); }
+__device__ __forceinline__ int4 ldku4(const int4* p) {
+  typedef int i4v __attribute__((ext_vector_type(4)));
+  const i4v v = *(const __attribute__((address_space(4))) i4v*)(p);
+  return make_int4(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y),
+                   __builtin_amdgcn_readfirstlane(v.z), __builtin_amdgcn_readfirstlane(v.w));
+}
+// A pointer field of an immutable struct (the same for the whole wave).
+template <typename T> __device__ __forceinline__ T* ldp(T* const* field) {
+  return uptr(*(T* const __attribute__((address_space(4)))*)(field));
+}
 __device__ __forceinline__ float ldc(const float* p) {
   return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

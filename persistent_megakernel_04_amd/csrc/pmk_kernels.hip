@@ -579,8 +579,8 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   // the K slice of a dense task, its rows per pass and first batch row
   int k0 = 0, kn = 0, b0 = 0, nbb = 0;
   auto dense = [&](int stage, int K, int R, int units, int urows) -> bool {
-    const StageGeo g{ldu(&a.geo[stage].ks), ldu(&a.geo[stage].tiles), ldu(&a.geo[stage].kr),
-                     ldu(&a.geo[stage].blk)};
+    const StageGeo g{ldku(&a.geo[stage].ks), ldku(&a.geo[stage].tiles), ldku(&a.geo[stage].kr),
+                     ldku(&a.geo[stage].blk)};
     const bool one = g.ks > 1 || g.blk > 1;   // one pass of up to 16 rows: batch block task.w
     k0 = task.z * g.kr;
     kn = min(K, k0 + g.kr) - k0;
@@ -602,7 +602,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   };
   switch (task.x) {
     case T_QKV: {   // RMSNorm1 + QKV rotation pairs of the tile
-      const int2 u = tile_units(tile, dm.qkv_units, ldu(&a.geo[0].tiles));
+      const int2 u = tile_units(tile, dm.qkv_units, ldku(&a.geo[0].tiles));
       if (!dense(0, dm.H, 2 * u.y, dm.qkv_units, 2)) return false;
       ps.rw = GemvRows{ROWS_QKV, ldp(&Lp->w_qkv), nullptr, u.x, dm.d >> 1, dm.H, k0};
       ps.in = GemvIn{hid_in(a, c.l) + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->attn_norm) + k0,
@@ -612,7 +612,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
     }
     case T_O: {     // O-projection rows of the tile
       const int K = dm.Hq * dm.d;
-      const int2 u = tile_units(tile, dm.H, ldu(&a.geo[1].tiles));
+      const int2 u = tile_units(tile, dm.H, ldku(&a.geo[1].tiles));
       if (!dense(1, K, u.y, dm.H, 1)) return false;
       ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_o), nullptr, u.x, 0, K, k0};
       ps.in = GemvIn{o_of(a, c.l) + (size_t)b0 * K + k0, K, nullptr, nullptr, 0, 0.f, a.attn_merge_o ? b0 : -1};
@@ -620,7 +620,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       break;
     }
     case T_GU: {    // RMSNorm2 + gate and up rows of the tile
-      const int2 u = tile_units(tile, dm.F, ldu(&a.geo[2].tiles));
+      const int2 u = tile_units(tile, dm.F, ldku(&a.geo[2].tiles));
       if (!dense(2, dm.H, 2 * u.y, dm.F, 2)) return false;
       ps.rw = GemvRows{ROWS_PAIR, ldp(&Lp->w_gate), ldp(&Lp->w_up), u.x, u.y, dm.H, k0};
       ps.in = GemvIn{h1_of(a, c.l) + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->ffn_norm) + k0,
@@ -629,7 +629,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       break;
     }
     case T_DOWN: {  // down-projection rows of the tile
-      const int2 u = tile_units(tile, dm.H, ldu(&a.geo[3].tiles));
+      const int2 u = tile_units(tile, dm.H, ldku(&a.geo[3].tiles));
       if (!dense(3, dm.F, u.y, dm.H, 1)) return false;
       ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_down), nullptr, u.x, 0, dm.F, k0};
       ps.in = GemvIn{act_of(a, c.l) + (size_t)b0 * dm.F + k0, dm.F, nullptr, nullptr, 0, 0.f, -1};
@@ -1000,7 +1000,7 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
   const int G = dm.Hq / dm.Hkv;               // query heads of the group, a multiple of HB
   const int ck = ITS * 32;
   const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * D;
-  const int S = ldu(a.seq_lens + b), n = S + 1;
+  const int S = ldku(a.seq_lens + b), n = S + 1;
   const int p0 = ci * ck, p1 = min(n, p0 + ck);
   const int nc = (n + ck - 1) / ck;
 
@@ -1113,7 +1113,7 @@ __device__ __forceinline__ bool task_attn_mm(const Ctx& c, int b, int g, int ci,
   const int G = dm.Hq / dm.Hkv;
   const int ck = a.attn_chunk;
   const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * D;
-  const int S = ldu(a.seq_lens + b), n = S + 1;
+  const int S = ldku(a.seq_lens + b), n = S + 1;
   const int p0 = ci * ck, p1 = min(n, p0 + ck);
   const int nc = (n + ck - 1) / ck;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kv) + kv_off(dm, c.l, 0, b, g, 0);
@@ -1287,7 +1287,7 @@ __device__ __forceinline__ bool task_attn_stream(const Ctx& c, int b, int g, int
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), j = lane & 15, r = lane >> 4;
   const int G = dm.Hq / dm.Hkv;
   const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * D;
-  const int S = ldu(a.seq_lens + b);
+  const int S = ldku(a.seq_lens + b);
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.kv) + kv_off(dm, c.l, 0, b, g, 0);
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.kv) + kv_off(dm, c.l, 1, b, g, 0);
   const int pmax = S > 0 ? S - 1 : 0;   // cached slots only (slot S is this step's)
@@ -1756,7 +1756,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
   if (threadIdx.x == 0) *s.flag = (ldci(a.ws.err) == 0);
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*s.flag)) return;
-  const int n = ldu(a.ws.qlen + wg);
+  const int n = ldku(a.ws.qlen + wg);
   const int4* q = a.ws.queue + (size_t)wg * dm.max_queue;
   uint32_t* tr = a.trace ? a.trace + (size_t)wg * a.trace_cap * 8 : nullptr;
   // records accumulate over the launches of a step (the prologue zeroes the counts)
@@ -1798,7 +1798,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
     if (tr && threadIdx.x == 0 && tn < a.trace_cap) {
       const uint32_t t_end = (uint32_t)now_ticks();
       __attribute__((address_space(1))) uint32_t* e = gp(tr + (size_t)tn * 8);
-      e[0] = (uint32_t)type | ((uint32_t)l << 8) | ((uint32_t)(ldu4(q + t).y & 0xffff) << 16);
+      e[0] = (uint32_t)type | ((uint32_t)l << 8) | ((uint32_t)(ldku4(q + t).y & 0xffff) << 16);
       e[1] = t_begin;
 #pragma unroll
       for (int i = 1; i < 6; ++i) e[1 + i] = s.tclk[i];
@@ -1814,7 +1814,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
   };
   if (n > 0) {
     while (l < l_end) {
-      int4 task = ldu4(q + t);
+      int4 task = ldku4(q + t);
       const int tix = task.x >> 8;   // attention tasks: the task's index within the stage
       task.x &= 0xff;
       if (!mine(task.x)) {   // not this launch's (a per-stage schedule)
@@ -1903,7 +1903,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
         record(task.x, t_begin);
         advance();
         if (l >= l_end || bars) break;
-        task = ldu4(q + t);
+        task = ldku4(q + t);
         task.x &= 0xff;
         if (!gemv_task(task.x) || !mine(task.x)) break;
       }
