@@ -1,0 +1,51 @@
+// Checks the dense stages' work split (stage_geo in pmk_internal.h) on the
+// host: for every depth, row count, batch and grid share used by the decode
+// shapes, the split it returns covers the depth with whole ring-length
+// slices, fits the LDS, keeps the tile count within the grid, and splits
+// nothing at batch 1. Prints "ok <cases>" or the first failing case.
+#include <cstdio>
+
+#include "../../persistent_megakernel_04_amd/csrc/pmk_internal.h"
+
+using namespace pmk;
+
+int main() {
+  const int Ks[] = {256, 512, 688, 2048, 4096, 5120, 8192, 14336, 28672};
+  const int units[] = {64, 128, 344, 688, 2048, 3072, 4096, 5120, 8192, 14336, 28672};
+  const int urows[] = {1, 2};
+  const int avails[] = {192, 256};   // the grid (256 CUs) and its share without the attention workgroups
+  const int steps[][2] = {{32, 8}, {16, 4}};   // bfloat16 and float: k per load step, LDS row padding
+  long cases = 0;
+  for (auto& st : steps)
+    for (int K : Ks)
+      for (int U : units)
+        for (int R : urows)
+          for (int nb = 1; nb <= kMaxNb; ++nb)
+            for (int avail : avails) {
+              ++cases;
+              const StageGeo g = stage_geo(K, U, R, nb, avail, st[0], st[1]);
+              const int grain = kRingK * st[0];
+              auto fail = [&](const char* why) {
+                std::printf("FAIL %s: K %d units %d urows %d nb %d avail %d kstep %d -> ks %d tiles %d kr %d\n", why, K,
+                            U, R, nb, avail, st[0], g.ks, g.tiles, g.kr);
+                return 1;
+              };
+              if (g.blk != 1) return fail("blk");
+              if (g.ks == 0) {   // no split within kMaxKs slices: the caller makes passes instead
+                const int kr8 = ((K + kMaxKs - 1) / kMaxKs + grain - 1) / grain * grain, t8 = avail / kMaxKs;
+                const long rows8 = (long)(U + t8 - 1) / t8 * R;
+                if (nb * (kr8 + st[1]) * 4L + rows8 * nb * 4 + 16 <= kXyBytes) return fail("gave up on a split that fits");
+                continue;
+              }
+              if (g.ks < 1 || g.ks > kMaxKs) return fail("slice count");
+              if (g.tiles < 1 || g.tiles > U || (g.tiles > avail && g.tiles > 1)) return fail("tile count");
+              if ((long)(g.ks - 1) * g.kr >= K || (long)g.ks * g.kr < K) return fail("slices do not cover K");
+              if (g.kr != K && g.kr % grain != 0) return fail("slice not whole ring lengths");
+              const long rows = (long)(U + g.tiles - 1) / g.tiles * R;
+              const long xs = (long)nb * ((g.kr + st[0] - 1) / st[0] * st[0] + st[1]) * 4;
+              if ((xs + 15) / 16 * 16 + rows * nb * 4 > kXyBytes && g.kr > grain) return fail("does not fit the LDS");
+              if (nb == 1 && K <= 28672 && g.ks != 1) return fail("split at batch 1");
+            }
+  std::printf("ok %ld\n", cases);
+  return 0;
+}
