@@ -235,16 +235,21 @@ def main():
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush_cache else None
+    # per-step events around each call (prologue + persistent kernel), for the spread of step times
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     e0.record()
     h0 = time.perf_counter()
     for i in range(K):
         if flush is not None:
             flush.fill_(float(i))
+        marks[i][0].record()
         model.step(hid_work[i], kv, steps_lens[i])
+        marks[i][1].record()
     host_us = (time.perf_counter() - h0) / K * 1e6   # host time to submit a step (the launches are asynchronous)
     e1.record()
     torch.cuda.synchronize()
     total_ms = e0.elapsed_time(e1)
+    step_ms = sorted(a.elapsed_time(b) for a, b in marks)
     main_ms, timed_steps = model.timing_read()
     model.timing_enable(False)
     err = model.device_error()
@@ -313,7 +318,17 @@ def main():
                       "host_submit_us_per_step": round(host_us, 1), "cache_flushed": bool(args.flush_cache),
                       **({"moe_scheduler": args.moe_scheduler} if w.n_experts else {}),
                       "launches_per_step": launches},
-           "roofline": roofline, "cpu_baseline": cpu}
+           "roofline": roofline, "cpu_baseline": cpu,
+           "step_ms_stats": {"median": round(step_ms[len(step_ms) // 2], 4), "min": round(step_ms[0], 4),
+                             "max": round(step_ms[-1], 4)}}
+    if w.n_experts:
+        # the grouped expert GEMMs' arithmetic (gate, up, down: 2 flops per multiply-add) against the bf16
+        # matrix cores' dense peak, over the persistent kernel's time
+        flops = 2.0 * B * w.top_k * 3 * w.hidden * w.expert_ffn_dim
+        out["moe_mfma"] = {"expert_tflop_per_step": round(flops / 1e12, 5),
+                           "achieved_tflops": round(flops / (avg_main_ms * 1e-3) / 1e12, 3),
+                           "peak_tflops": 2500.0,
+                           "util": round(flops / (avg_main_ms * 1e-3) / 2.5e15, 6)}
     print(json.dumps(out), flush=True)
 
 
