@@ -264,18 +264,20 @@ __device__ __forceinline__ void stage_attn_merge(const StepArgs& a, int l, const
     f4v x = {0.f, 0.f, 0.f, 0.f};
     if (k < K) {
       const int b = in.merge_b0 + m;
+      // the request's chunk count: for one request through the scalar cache,
+      // so that the partial loads below issue at once
+      const int nc = ((nb == 1 ? ldku(a.seq_lens + in.merge_b0) : *gp(a.seq_lens + b)) + ck) / ck;
       const int h = k / d, e = k - h * d, g = h / G, hh = h - g * G;
       const int base = ((b * dm.Hkv + g) * kMergeChunks * G + hh) * DP;
-      // every chunk slot is read, with the request's length in flight too
-      // (slots past its chunk count hold stale values, never used)
       f4v av[kMergeChunks], mv[kMergeChunks];
 #pragma unroll
       for (int cc = 0; cc < kMergeChunks; ++cc) {
-        const int o = (base + cc * G * DP) * 4;
+        // a chunk the request does not have reads past the buffer's range:
+        // zeros, with no memory access
+        const int o = cc < nc ? (base + cc * G * DP) * 4 : kNoRecord;
         av[cc] = ldk4(pr, o + e * 4);
         mv[cc] = ldk4(pr, o + d * 4);
       }
-      const int nc = (*gp(a.seq_lens + b) + ck) / ck;
       float M = -INFINITY, L = 0.f;
 #pragma unroll
       for (int cc = 0; cc < kMergeChunks; ++cc)
