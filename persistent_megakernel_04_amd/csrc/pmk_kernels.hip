@@ -1954,6 +1954,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   __shared__ int total_attn, merge_s, qkv_tiles_s, attn_wg0_s, stream_s, share_s;
   __shared__ StageGeo geo_s[4];
   __shared__ int cb[kMaxBatchAll + 1];
+  __shared__ int sl[kMaxBatchAll];   // the requests' lengths, read once
   StepArgs* copy = reinterpret_cast<StepArgs*>(a.ws.args);
   if (tid == 0) {
     // the persistent kernel reads this step's arguments from here, on every
@@ -1964,6 +1965,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   __syncthreads();
   for (int b = tid; b < B; b += blockDim.x) {
     const int s = a.seq_lens[b];
+    sl[b] = s;
     if (s < 0 || s >= dm.max_seq) atomicOr(&bad, 2);
   }
   __syncthreads();
@@ -1986,7 +1988,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     int ck = kMaxChunk, merge = 0;
     auto max_nc = [&](int c) {
       int mx = 0;
-      for (int b = 0; b < B; ++b) mx = max(mx, (a.seq_lens[b] + c) / c);
+      for (int b = 0; b < B; ++b) mx = max(mx, (sl[b] + c) / c);
       return mx;
     };
     if (B <= dm.merge_b) {
@@ -1997,7 +1999,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     if (!merge) {
       while (ck > kMinChunk) {
         long tasks = 0;
-        for (int b = 0; b < B; ++b) tasks += (a.seq_lens[b] + ck) / ck;
+        for (int b = 0; b < B; ++b) tasks += (sl[b] + ck) / ck;
         if (tasks * dm.Hkv >= G) break;
         ck >>= 1;
       }
@@ -2014,7 +2016,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     int acc = 0;
     for (int b = 0; b < B; ++b) {
       cb[b] = acc;
-      acc += stream ? a.seq_lens[b] + 1 : (a.seq_lens[b] + ck) / ck;   // ceil((S + 1) / ck)
+      acc += stream ? sl[b] + 1 : (sl[b] + ck) / ck;   // ceil((S + 1) / ck)
     }
     cb[B] = acc;
     total_attn = acc * dm.Hkv;
