@@ -214,3 +214,17 @@ def test_unfused_schedules_match_oracle(orc, sched, B):
     lens = [512] if B == 1 else synth.ragged_lengths(B, 512, 2048, ("c3_8b_sweep", "sched", B))
     case = build_case(w, B, lens, n_layers=2, max_seq=int(max(lens)) + 2, tag=f"t13_{sched}_{B}")
     check_dense(orc, case, w.tol, sched=sched)
+
+
+def test_schedule_setters_reject_unknown_modes(orc):
+    """pmk_set_schedule / pmk_set_moe_scheduler on a live handle: unknown
+    modes are rejected and leave the handle working (fused step still matches)."""
+    from persistent_megakernel_04_amd import _abi
+    w = synth.get_workload("c1_tiny_f32")
+    case = build_case(w, 1, [40], max_seq=64, tag="t15")
+    model = make_model(case)
+    assert model.lib.pmk_set_schedule(model.handle, 9) == _abi.PMK_ERR_ARG
+    assert model.lib.pmk_set_schedule(model.handle, -1) == _abi.PMK_ERR_ARG
+    assert model.lib.pmk_set_moe_scheduler(model.handle, 2) == _abi.PMK_ERR_ARG
+    model.close()
+    check_dense(orc, case, w.tol)
