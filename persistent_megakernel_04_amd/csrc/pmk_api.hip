@@ -140,7 +140,8 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   // Dense stages: one input row of the whole depth and a tile's outputs must
   // fit the LDS (a step may put its few attention tasks on workgroups of their
   // own and the QKV tiles on the others, at least three quarters of the grid).
-  // Split-K partials: the largest need over batches of up to 16 rows.
+  // Split-K partials: the largest need over batches of up to 16 rows (records
+  // of whole 16-byte units).
   const int K4[4] = {dm.H, dm.Hq * dm.d, dm.H, dm.F};
   const int U4[4] = {dm.qkv_units, dm.H, dm.F, dm.H};
   const int R4[4] = {2, 1, 2, 1};
@@ -160,7 +161,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
         const size_t blocks = nb == kMaxNb ? (size_t)ceil_div(dm.max_batch, kMaxNb) : 1;
         if (g.ks > 1)
           kpart_floats = std::max(kpart_floats, blocks * g.tiles * g.ks *
-                                                    ((size_t)ceil_div(U4[st], g.tiles) * R4[st] * nb + 16));
+                                                    (((size_t)ceil_div(U4[st], g.tiles) * R4[st] * nb + 16 + 3) & ~(size_t)3));
       }
   }
   const long attn_max = (long)dm.max_batch * dm.Hkv * dm.max_chunks;

@@ -123,6 +123,13 @@ __device__ __forceinline__ float2 ldc2(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ void stc4(__amdgpu_buffer_rsrc_t r, int off, f4v v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, v), r, off, 0, 16);
 }
+// Device-coherent 16-byte load straight into LDS (no registers): lane i's 16
+// bytes land at dst + 16 i, dst being wave-uniform (it goes to M0). A lane
+// whose offset is past the descriptor's range writes zeros there. The data is
+// in LDS once this wave's vector-memory counter has drained (vm_drain).
+__device__ __forceinline__ void ldc4_lds(__amdgpu_buffer_rsrc_t r, int off, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 16);
+}
 
 // 16-byte load of immutable data (weights, cached KV) through the global
 // address space: a generic pointer would compile to a flat load, which also

@@ -598,8 +598,9 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
     ps.R = R;
     ps.nb = min(nbb, a.batch - b0);
     ps.b0 = b0;
-    // one record stride for every block of the stage (the last may be short)
-    ps.rs = (units + g.tiles - 1) / g.tiles * urows * (g.blk > 1 ? kMaxNb : ps.nb) + 16;
+    // one record stride for every block of the stage (the last may be short),
+    // a whole number of 16-byte units
+    ps.rs = ((units + g.tiles - 1) / g.tiles * urows * (g.blk > 1 ? kMaxNb : ps.nb) + 16 + 3) & ~3;
     return true;
   };
   switch (task.x) {
@@ -737,13 +738,24 @@ __device__ __forceinline__ void add_resid(const Pass& ps, const float (&r)[kResi
 // own from LDS), into ys and turn the sums of squares into 1 / rms over the
 // whole depth. Returns whether this task is that last one (the others have
 // nothing more to do for the tile).
+//
+// A record is the slice's n = R nb sums then, normed, its nb sums of squares,
+// records rs floats apart (rs a multiple of 4). Records move as 16-byte
+// units. The last task pulls the other slices' records into the staged-input
+// region of LDS, which the pass no longer reads, with loads that go straight
+// to LDS: one round trip to the coherence point for the whole tile, and no
+// registers held (a loop of register loads paid one round trip per element
+// group, which made these tasks the last of their stage by 5-15 us).
 __device__ __forceinline__ bool reduce_slices(const Ctx& c, const Pass& ps) {
   const StepArgs& a = c.a;
-  const int tid = threadIdx.x, n = ps.R * ps.nb, rs = ps.rs;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), n = ps.R * ps.nb, rs = ps.rs;
   const bool normed = ps.in.norm != 0;
-  float* part = a.ws.kpart + (size_t)ps.tile * ps.ks * rs;
-  for (int i = tid; i < n; i += kBlock) stc(part + ps.slice * rs + i, ps.ys[i]);
-  if (normed && tid < ps.nb) stc(part + ps.slice * rs + n + tid, c.s.rstd[tid]);
+  const int nrec = n + (normed ? ps.nb : 0), U = (nrec + 3) >> 2;
+  float* part = uptr(a.ws.kpart + (size_t)ps.tile * ps.ks * rs);
+  const auto prs = rsrc_n(part, ps.ks * rs * 4);
+  auto own = [&](int i) -> float { return i < n ? ps.ys[i] : (i < nrec ? c.s.rstd[i - n] : 0.f); };
+  for (int u = tid; u < U; u += kBlock)
+    stc4(prs, (ps.slice * rs + 4 * u) * 4, f4v{own(4 * u), own(4 * u + 1), own(4 * u + 2), own(4 * u + 3)});
   vm_drain();
   __syncthreads();
   if (tid == 0) {
@@ -754,22 +766,43 @@ __device__ __forceinline__ bool reduce_slices(const Ctx& c, const Pass& ps) {
   }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*c.s.flag)) return false;
-  // every element's slices are loaded together, then added in order
-  for (int i = tid; i < n + 16; i += kBlock) {
-    const bool row = i < n, sq = !row && normed && i - n < ps.nb;
-    if (!row && !sq) continue;
-    float v[kMaxKs];
+  // the other slices, in slice order, each in 1 KiB blocks (one wave load
+  // each) below ys; lanes past a record load into their block's padding
+  const int UB = (U + 63) >> 6;
+  const int ys_off = (int)(reinterpret_cast<char*>(ps.ys) - reinterpret_cast<char*>(c.s.xs));
+  char* land = reinterpret_cast<char*>(c.s.xs);
+  const float* landf = reinterpret_cast<const float*>(land);
+  if ((ps.ks - 1) * UB * 1024 <= ys_off) {
+    for (int id = wave; id < (ps.ks - 1) * UB; id += kWaves) {
+      const int oi = id / UB, blk = id - oi * UB, sl = oi + (oi >= ps.slice ? 1 : 0);
+      ldc4_lds(prs, (sl * rs + (blk * 64 + lane) * 4) * 4, land + (oi * UB + blk) * 1024);
+    }
+    vm_drain();
+    __syncthreads();
+    for (int i = tid; i < nrec; i += kBlock) {
+      float sum = 0.f;
+      for (int sl = 0; sl < ps.ks; ++sl)
+        sum += sl == ps.slice ? own(i) : landf[(sl - (sl > ps.slice ? 1 : 0)) * UB * 256 + i];
+      if (i < n)
+        ps.ys[i] = sum;
+      else
+        c.s.rstd[i - n] = 1.0f / sqrtf(sum / (float)ps.kfull + ps.in.eps);
+    }
+  } else {   // records too large for the free LDS: register loads, element by element
+    for (int i = tid; i < nrec; i += kBlock) {
+      float v[kMaxKs];
 #pragma unroll
-    for (int sl = 0; sl < kMaxKs; ++sl)
-      v[sl] = (sl < ps.ks && sl != ps.slice) ? ldc(part + sl * rs + i) : 0.f;
-    float sum = 0.f;
+      for (int sl = 0; sl < kMaxKs; ++sl)
+        v[sl] = (sl < ps.ks && sl != ps.slice) ? ldc(part + sl * rs + i) : 0.f;
+      float sum = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < kMaxKs; ++sl)
-      if (sl < ps.ks) sum += sl == ps.slice ? (row ? ps.ys[i] : c.s.rstd[i - n]) : v[sl];
-    if (row)
-      ps.ys[i] = sum;
-    else
-      c.s.rstd[i - n] = 1.0f / sqrtf(sum / (float)ps.kfull + ps.in.eps);
+      for (int sl = 0; sl < kMaxKs; ++sl)
+        if (sl < ps.ks) sum += sl == ps.slice ? own(i) : v[sl];
+      if (i < n)
+        ps.ys[i] = sum;
+      else
+        c.s.rstd[i - n] = 1.0f / sqrtf(sum / (float)ps.kfull + ps.in.eps);
+    }
   }
   __syncthreads();
   return true;
@@ -777,37 +810,61 @@ __device__ __forceinline__ bool reduce_slices(const Ctx& c, const Pass& ps) {
 
 // Wave 0 alone consumes a pass's result (ys[j][m], rstd[m] in LDS) and stores
 // its outputs, while the other waves go on streaming the next pass's weights.
-// `have_resid`: the O / down residual is already in ys.
+// `have_resid`: the O / down residual is already in ys. Consecutive lanes take
+// consecutive outputs j of one batch row m, so each store instruction writes
+// whole runs of a row: with the batch index fastest, one instruction wrote 16
+// rows' 16-byte pieces, and such scattered device-coherent partial-line
+// stores took a wave 5-13 us per tile at 16 rows.
+// Threads t0, t0 + nt, ... of the workgroup take the outputs: wave 0 alone
+// (t0 = lane, nt = 64), or, for the last slice task of a split tile, every
+// wave (t0 = threadIdx.x, nt = kBlock). The MoE gate/up case notifies its
+// expert from lane 0 of the calling wave and is only run by wave 0.
 template <typename WT>
-__device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have_resid) {
+__device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have_resid, int t0, int nt) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   const int nb = ps.nb, b0 = ps.b0, lane = threadIdx.x & 63;
   const float* ys = ps.ys;
   switch (ps.epi) {
     case E_QKV: {   // RoPE at each request's position, then q/k/v out and the K/V append
-      const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
-      for (int idx = lane; idx < ps.n * nb; idx += 64) {
-        const int ju = idx / nb, m = idx - ju * nb;
-        const int unit = ps.r0 + ju, h = unit / half, i = unit - h * half;
-        const float r = c.s.rstd[m];
-        float y1 = ys[(2 * ju) * nb + m] * r, y2 = ys[(2 * ju + 1) * nb + m] * r;
-        const int bb = b0 + m, pos = *gp(a.seq_lens + bb);
-        if (h < dm.Hq + dm.Hkv) {
-          typedef float f2v __attribute__((ext_vector_type(2)));
-          const f2v cs = *gp(reinterpret_cast<const f2v*>(a.ws.rope + (size_t)pos * half + i));
-          const float t1 = y1 * cs.x - y2 * cs.y, t2 = y2 * cs.x + y1 * cs.y;
-          y1 = t1;
-          y2 = t2;
+      const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d, ni = ps.n * nb;
+      // lane m < nb holds request b0 + m's position; the rotation rows of
+      // eight items per lane are loaded together (one latency per eight
+      // items, not two dependent ones per item)
+      const int posl = *gp(a.seq_lens + b0 + (lane < nb ? lane : 0));
+      const auto rrs = rsrc_n(a.ws.rope, dm.max_seq * half * 8);
+      for (int base = 0; base < ni; base += nt * 8) {
+        float2 cs[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int idx = base + t0 + nt * u, m = idx / ps.n, ju = idx - m * ps.n;
+          const int unit = ps.r0 + ju, h = unit / half, i = unit - h * half;
+          const int pos = __shfl(posl, m, 64);
+          cs[u] = ldk2(rrs, idx < ni && h < dm.Hq + dm.Hkv ? (pos * half + i) * 8 : kNoRecord);
         }
-        float* dst = qkv_of(a, c.l) + (size_t)bb * qkv_dim + h * dm.d + i;
-        stc(dst, y1);
-        stc(dst + half, y2);
-        if (h >= dm.Hq) {
-          const int kvh = h - dm.Hq, which = kvh / dm.Hkv, g = kvh - which * dm.Hkv;
-          WT* cp = reinterpret_cast<WT*>(a.kv) + kv_off(dm, c.l, which, bb, g, pos);
-          Elem<WT>::put(cp + i, y1);
-          Elem<WT>::put(cp + i + half, y2);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int idx = base + t0 + nt * u;
+          if (idx >= ni) break;
+          const int m = idx / ps.n, ju = idx - m * ps.n;
+          const int unit = ps.r0 + ju, h = unit / half, i = unit - h * half;
+          const float r = c.s.rstd[m];
+          float y1 = ys[(2 * ju) * nb + m] * r, y2 = ys[(2 * ju + 1) * nb + m] * r;
+          const int bb = b0 + m, pos = __shfl(posl, m, 64);
+          if (h < dm.Hq + dm.Hkv) {
+            const float t1 = y1 * cs[u].x - y2 * cs[u].y, t2 = y2 * cs[u].x + y1 * cs[u].y;
+            y1 = t1;
+            y2 = t2;
+          }
+          float* dst = qkv_of(a, c.l) + (size_t)bb * qkv_dim + h * dm.d + i;
+          stc(dst, y1);
+          stc(dst + half, y2);
+          if (h >= dm.Hq) {
+            const int kvh = h - dm.Hq, which = kvh / dm.Hkv, g = kvh - which * dm.Hkv;
+            WT* cp = reinterpret_cast<WT*>(a.kv) + kv_off(dm, c.l, which, bb, g, pos);
+            Elem<WT>::put(cp + i, y1);
+            Elem<WT>::put(cp + i + half, y2);
+          }
         }
       }
       break;
@@ -816,10 +873,10 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
     case E_DOWN: {  // x' = h1 + W_down act (the layer output, into hidden)
       const float* res = resid_src(a, ps);
       float* out = ps.epi == E_O ? h1_of(a, c.l) : hid_out(a, c.l);
-      for (int idx = lane; idx < ps.n * nb; idx += 64) {
-        const int j = idx / nb, m = idx - j * nb;
+      for (int idx = t0; idx < ps.n * nb; idx += nt) {
+        const int m = idx / ps.n, j = idx - m * ps.n;
         const size_t o = (size_t)(b0 + m) * dm.H + ps.r0 + j;
-        stc(out + o, (have_resid ? 0.f : ldc(res + o)) + ys[idx]);
+        stc(out + o, (have_resid ? 0.f : ldc(res + o)) + ys[j * nb + m]);
       }
       break;
     }
@@ -828,8 +885,8 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
       const int Rh = ps.n;
       float* out = ps.epi == E_GU ? act_of(a, c.l) : mact_of(a, c.l);
       const int ld = ps.epi == E_GU ? dm.F : dm.Fe;
-      for (int idx = lane; idx < Rh * nb; idx += 64) {
-        const int j = idx / nb, m = idx - j * nb;
+      for (int idx = t0; idx < Rh * nb; idx += nt) {
+        const int m = idx / Rh, j = idx - m * Rh;
         const float r = c.s.rstd[m];
         const float gt = ys[j * nb + m] * r, up = ys[(Rh + j) * nb + m] * r;
         stc(out + (size_t)(b0 + m) * ld + ps.r0 + j, gt / (1.0f + __expf(-gt)) * up);
@@ -854,15 +911,15 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
       break;
     }
     case E_ROUTER: {
-      for (int idx = lane; idx < ps.n * nb; idx += 64) {
-        const int j = idx / nb, m = idx - j * nb;
+      for (int idx = t0; idx < ps.n * nb; idx += nt) {
+        const int m = idx / ps.n, j = idx - m * ps.n;
         stc(a.ws.logits + (size_t)(b0 + m) * dm.E + ps.r0 + j, ys[j * nb + m] * c.s.rstd[m]);
       }
       break;
     }
     case E_MDOWN: {
-      for (int idx = lane; idx < ps.n * nb; idx += 64) {
-        const int j = idx / nb, m = idx - j * nb;
+      for (int idx = t0; idx < ps.n * nb; idx += nt) {
+        const int m = idx / ps.n, j = idx - m * ps.n;
         stc(a.ws.mout + (size_t)(b0 + m) * dm.H + ps.r0 + j, ys[j * nb + m]);
       }
       break;
@@ -1875,6 +1932,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           default: break;
         }
         bool done = true;   // this task finished its row tile (not so for a split-K slice that was not the last)
+        bool split_last = false;   // it finished a split tile as its last slice task (a split task has one pass)
         for (int p = 0; ok; ++p) {
           Pass ps;
           if (!make_pass<WT>(c, task, p, wev, ps)) break;
@@ -1893,15 +1951,26 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
             done = false;
             break;
           }
+          split_last = ps.ks > 1;
           if (early) add_resid(ps, resid);
-          if (wave == 0) epilogue<WT>(c, ps, early);
+          // a split tile's last slice task is its stage's critical path: every
+          // wave stores the outputs and the workgroup notifies together,
+          // before any wave issues the next task's weight loads (those would
+          // hold the stores back in the compute unit's memory queue)
+          if (split_last || wave == 0)
+            epilogue<WT>(c, ps, early, split_last ? (int)threadIdx.x : (int)(threadIdx.x & 63), split_last ? kBlock : 64);
           if (threadIdx.x == 0) s.tclk[5] = (uint32_t)now_ticks();
         }
         if (!ok) return;
         // dense stages notify per row tile (by the last slice of a split tile), the others per workgroup
         const bool dense = task.x == T_QKV || task.x == T_O || task.x == T_GU || task.x == T_DOWN;
         const int sub = (dense ? task.y : wg) & (kSubs - 1);
-        if (done && notify >= 0 && wave == 0) wave_notify(ev_ptr(a, l, notify), sub);
+        if (done && notify >= 0) {
+          if (split_last)
+            wg_notify(ev_ptr(a, l, notify), sub);
+          else if (wave == 0)
+            wave_notify(ev_ptr(a, l, notify), sub);
+        }
         record(task.x, t_begin);
         advance();
         if (l >= l_end || bars) break;
