@@ -139,7 +139,8 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   dm.max_down = dm.max_tiles * std::max(dm.H / 16, 1);
   // Dense stages: one input row of the whole depth and a tile's outputs must
   // fit the LDS (a step may put its few attention tasks on workgroups of their
-  // own and the QKV tiles on the others, at least three quarters of the grid).
+  // own and the QKV and O tiles on the others, at least three quarters of the
+  // grid).
   // Split-K partials: the largest need over batches of up to 16 rows (records
   // of whole 16-byte units).
   const int K4[4] = {dm.H, dm.Hq * dm.d, dm.H, dm.F};
@@ -148,7 +149,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   size_t kpart_floats = 16;
   for (int st = 0; st < 4; ++st) {
     if (moe && st >= 2) continue;
-    const int tiles_min = std::min(st == 0 ? G - G / 4 : G, U4[st]);
+    const int tiles_min = std::min(st <= 1 ? G - G / 4 : G, U4[st]);
     const long row_bytes = 4L * (ceil_div(K4[st], dm.kstep) * dm.kstep + dm.xpad);
     if (row_bytes + 16 + 4L * ceil_div(U4[st], tiles_min) * R4[st] > kXyBytes) {
       delete h;

@@ -2096,10 +2096,12 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     share_s = max(64, (int)((P + G - 1) / G + 15) / 16 * 16);
     copy->attn_chunk = ck;
     // A few attention tasks (at most a quarter of the grid) get workgroups of
-    // their own, the last ones, which hold no QKV tile: their task comes first
-    // in the layer, so its KV rows stream in while the QKV tiles run on the
-    // other workgroups. Otherwise the attention tasks follow the QKV tiles on
-    // every workgroup.
+    // their own, the last ones, which hold no QKV or O tile: their task comes
+    // first in the layer, so its KV rows stream in while the QKV tiles run on
+    // the other workgroups, and they go on to gate/up when it is done (an O
+    // tile there would start only after attention and have its whole weight
+    // tile still to load, which held the O event back by ~5 us at batch 1).
+    // Otherwise the attention tasks follow the QKV tiles on every workgroup.
     const int own = (merge && total_attn <= G / 4) ? total_attn : 0;
     attn_wg0_s = own ? G - own : G;
     // each dense stage's split (see stage_geo): up to 16 rows, one pass over
@@ -2109,7 +2111,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     const int U4[4] = {dm.qkv_units, dm.H, dm.F, dm.H};
     const int R4[4] = {2, 1, 2, 1};
     for (int st = 0; st < 4; ++st) {
-      const int avail = st == 0 ? G - own : G;
+      const int avail = st <= 1 ? G - own : G;
       // more than 16 rows: the split of 16, and every 16-row block its own tasks
       StageGeo g = stage_geo(K4[st], U4[st], R4[st], min(B, kMaxNb), avail, dm.kstep, dm.xpad);
       if (B > kMaxNb && g.ks) g.blk = (B + kMaxNb - 1) / kMaxNb;
