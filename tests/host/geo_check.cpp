@@ -2,7 +2,11 @@
 // host: for every depth, row count, batch and grid share used by the decode
 // shapes, the split it returns covers the depth with whole ring-length
 // slices, fits the LDS, keeps the tile count within the grid, and splits
-// nothing at batch 1. Prints "ok <cases>" or the first failing case.
+// nothing at batch 1. For a split, the slice record (a tile's sums, then its
+// rows' sums of squares) has a stride of whole 16-byte units that covers it,
+// and the last slice task's landing area for the other slices' records (1 KiB
+// blocks per slice) fits below the pass outputs in LDS, so the records are
+// pulled in one round trip. Prints "ok <cases>" or the first failing case.
 #include <cstdio>
 
 #include "../../persistent_megakernel_04_amd/csrc/pmk_internal.h"
@@ -45,7 +49,42 @@ int main() {
               const long xs = (long)nb * ((g.kr + st[0] - 1) / st[0] * st[0] + st[1]) * 4;
               if ((xs + 15) / 16 * 16 + rows * nb * 4 > kXyBytes && g.kr > grain) return fail("does not fit the LDS");
               if (nb == 1 && K <= 28672 && g.ks != 1) return fail("split at batch 1");
+              if (g.ks > 1) {
+                // the kernel's record stride (rows of the stage's largest tile) and a normed record's length
+                const long rs = ((long)(U + g.tiles - 1) / g.tiles * R * nb + 16 + 3) & ~3L;
+                const long nrec = rows * nb + nb, units4 = (nrec + 3) / 4;
+                if (rs % 4 != 0 || 4 * units4 > rs) return fail("record stride");
+              }
             }
+  // The decode workloads' own splits pull the other slices' records into LDS
+  // in one round trip (the kernel falls back to register loads otherwise,
+  // e.g. for the 70B-shaped gate/up tiles at 10 to 16 rows).
+  struct Shape { int H, Hq, Hkv, d, F, nb_lo, nb_hi; };
+  const Shape shapes[] = {{4096, 32, 8, 128, 14336, 2, 16},   // 8B-shaped stack, batch 2..16 (and 16-row blocks)
+                          {2048, 32, 4, 128, 0, 2, 16},       // MoE layer's attention projections
+                          {8192, 64, 8, 128, 28672, 8, 8}};   // 70B-shaped stack, batch 8
+  for (const Shape& sh : shapes)
+    for (int st = 0; st < 4; ++st) {
+      if (st >= 2 && sh.F == 0) continue;
+      const int K4[4] = {sh.H, sh.Hq * sh.d, sh.H, sh.F};
+      const int U4[4] = {(sh.Hq + 2 * sh.Hkv) * sh.d / 2, sh.H, sh.F, sh.H};
+      const int R4[4] = {2, 1, 2, 1};
+      for (int nb = sh.nb_lo; nb <= sh.nb_hi; ++nb)
+        for (int avail : avails) {
+          ++cases;
+          const StageGeo g = stage_geo(K4[st], U4[st], R4[st], nb, avail, 32, 8);
+          if (g.ks <= 1) continue;
+          const long rows = (long)(U4[st] + g.tiles - 1) / g.tiles * R4[st];
+          const long xs = (long)nb * ((g.kr + 31) / 32 * 32 + 8) * 4;
+          const long units4 = (rows * nb + nb + 3) / 4;
+          const long land = (long)(g.ks - 1) * ((units4 + 63) / 64) * 1024;
+          if (land > (xs + 15) / 16 * 16) {
+            std::printf("FAIL slice records do not fit below the outputs: H %d stage %d nb %d avail %d ks %d\n", sh.H,
+                        st, nb, avail, g.ks);
+            return 1;
+          }
+        }
+    }
   std::printf("ok %ld\n", cases);
   return 0;
 }

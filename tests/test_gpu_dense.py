@@ -167,6 +167,17 @@ def test_70b_shape_four_layers_b8_sampled(orc):
     check_dense(orc, case, w.tol, requests=[0, 5])
 
 
+def test_70b_shape_b12_split_records_beyond_lds(orc):
+    """A 70B-shaped layer at batch 12: gate/up runs in 4 K slices whose partial
+    records (896 rows x 12 per tile) are too large to pull into LDS, so the last
+    slice task of each tile adds them through register loads instead. One
+    layer, lengths in [256, 1024], every request against the oracle."""
+    w = synth.get_workload("c5_70b")
+    lens = synth.ragged_lengths(12, 256, 1024, ("c5_70b", "lens", 12))
+    case = build_case(w, 12, lens, n_layers=1, max_seq=int(lens.max()) + 2, tag="t16")
+    check_dense(orc, case, w.tol)
+
+
 @pytest.mark.parametrize("B", [64, 128])
 def test_8b_shape_large_batch_sampled(orc, B):
     """The batch sweep's two largest points: passes of 16 rows over every
