@@ -308,7 +308,9 @@ def main():
 
     out = {"metric": METRIC, "value": round(B * K / (total_ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
            "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           # the projections' matrix-core arithmetic: bf16 operands (activations as bf16 hi + lo pairs)
+           # with float32 accumulation for bf16 weights; float32 throughout for float32 weights
+           "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
            "data": "synthetic (seeded N(0,0.02) weights, N(0,1) KV cache and inputs)",
            "config": {"workload": w.name, "layers": L, "hidden": w.hidden, "q_heads": w.n_q_heads,
                       "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn": w.ffn_dim,
