@@ -153,6 +153,9 @@ def main():
                     help="between timed steps, write a 1 GiB buffer so that no weight stays in the 256 MB "
                     "memory-side cache (for working sets that fit it, e.g. the MoE layer at one token); the "
                     "roofline then rests on the persistent kernel's own launch times, which exclude the writes")
+    ap.add_argument("--seq-range", type=int, nargs=2, default=None, metavar=("LO", "HI"),
+                    help="cached lengths uniform on [LO, HI] instead of the workload's own (e.g. batches beyond 128, "
+                    "whose cache at the sweep's lengths would not fit in HBM)")
     ap.add_argument("--trace", default=None, help="after the timed steps, run one traced step and write a "
                     "per-stage summary of the task trace to this file")
     args = ap.parse_args()
@@ -188,7 +191,12 @@ def main():
     B = args.batch if args.batch is not None else w.batches[0]
     K, W = args.steps, args.warmup
     # per-step lengths: request b holds lens0[b] + i cached entries at step i
-    if w.seq_lo == w.seq_hi:
+    if args.seq_range is not None:
+        lo, hi = args.seq_range
+        if not 0 <= lo <= hi:
+            sys.exit("--seq-range needs 0 <= LO <= HI")
+        lens0 = synth.ragged_lengths(B, lo, hi, (w.name, "lens", B, lo, hi))
+    elif w.seq_lo == w.seq_hi:
         lens0 = np.full(B, w.seq_lo, np.int32)
     else:
         lens0 = synth.ragged_lengths(B, w.seq_lo, w.seq_hi, (w.name, "lens", B))
@@ -315,7 +323,9 @@ def main():
            "config": {"workload": w.name, "layers": L, "hidden": w.hidden, "q_heads": w.n_q_heads,
                       "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "ffn": w.ffn_dim,
                       "experts": w.n_experts, "global_batch": B,
-                      "seq_len_start": [int(x) for x in lens0[:8]], "weights": w.dtype, "kv_cache": w.dtype,
+                      "seq_len_start": [int(x) for x in lens0[:8]],
+                      **({"seq_range": list(args.seq_range)} if args.seq_range is not None else {}),
+                      "weights": w.dtype, "kv_cache": w.dtype,
                       "accumulate": "f32", "parallelism": "single GPU", "schedule": args.schedule,
                       "host_submit_us_per_step": round(host_us, 1), "cache_flushed": bool(args.flush_cache),
                       **({"moe_scheduler": args.moe_scheduler} if w.n_experts else {}),

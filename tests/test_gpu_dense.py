@@ -189,6 +189,18 @@ def test_8b_shape_large_batch_sampled(orc, B):
     check_dense(orc, case, w.tol, requests=[int(np.argmax(lens)), int(np.argmin(lens)), B - 1])
 
 
+@pytest.mark.parametrize("B", [256, 512])
+def test_8b_shape_batch_beyond_128_sampled(orc, B):
+    """Decode batches beyond the sweep's largest point (16 to 32 blocks of 16
+    rows per projection, thousands of attention pieces per layer), with short
+    contexts in [16, 512] so that the cache stays small; two layers, three
+    sampled requests."""
+    w = synth.get_workload("c3_8b_sweep")
+    lens = synth.ragged_lengths(B, 16, 512, ("c3_8b_sweep", "lens_short", B))
+    case = build_case(w, B, lens, n_layers=2, max_seq=int(lens.max()) + 2, tag=f"t17_{B}")
+    check_dense(orc, case, w.tol, requests=[int(np.argmax(lens)), int(np.argmin(lens)), B - 1])
+
+
 @pytest.mark.parametrize("B", [8, 12, 16])
 def test_8b_shape_split_k_every_request(orc, B):
     """Batches whose staged inputs outgrow the LDS: the projections run as K
