@@ -181,6 +181,15 @@ struct StepArgs {
   int moe_dyn;                         // 1: grouped expert tasks popped from a per-layer queue
 };
 
+// Which task paths an instantiation of the persistent kernel carries: all of
+// them (the ablation schedules, float32 weights), or, for the fused bfloat16
+// kernel, those of a dense decoder layer or those of a MoE layer only. A dense
+// handle never queues routing, grouped-expert or combine tasks, and a MoE
+// handle never queues dense gate/up or down tasks; dropping the other kind's
+// code halves the fused kernel (about 360 to 170 KB of instructions) and frees
+// registers, which took 2-3 % off the batch-1 and batch-4 steps.
+enum KernelPaths : int { KP_ALL = 0, KP_DENSE = 1, KP_MOE = 2 };
+
 // What one launch of the persistent kernel runs: layers [l0, l1), and of
 // their queue entries only the task types whose bit (1 << type) is set;
 // barrier: a grid-wide barrier after every stage of every layer.

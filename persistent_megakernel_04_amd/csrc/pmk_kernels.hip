@@ -551,12 +551,17 @@ __device__ __forceinline__ int2 tile_units(int tile, int units, int tiles) {
 // their split from this step's geometry: task (tile, K slice) covers all
 // batch rows in one pass when the depth is split, else passes of what the LDS
 // holds (a task whose stage is not split has slice 0).
-template <typename WT>
+template <typename WT, int KP>
 __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, const int* wev, Pass& ps) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   const LayerPtrs* Lp = a.layers + c.l;   // its fields are read with global loads (ldp)
   const int tile = task.y;
+  if constexpr (KP == KP_DENSE) {
+    if (task.x != T_QKV && task.x != T_O && task.x != T_GU && task.x != T_DOWN) return false;
+  } else if constexpr (KP == KP_MOE) {
+    if (task.x == T_GU || task.x == T_DOWN) return false;
+  }
   ps.wev = p == 0 ? wev : nullptr;
   ps.wsubs = kSubs;
   ps.e = 0;
@@ -819,12 +824,17 @@ __device__ __forceinline__ bool reduce_slices(const Ctx& c, const Pass& ps) {
 // (t0 = lane, nt = 64), or, for the last slice task of a split tile, every
 // wave (t0 = threadIdx.x, nt = kBlock). The MoE gate/up case notifies its
 // expert from lane 0 of the calling wave and is only run by wave 0.
-template <typename WT>
+template <typename WT, int KP>
 __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have_resid, int t0, int nt) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   const int nb = ps.nb, b0 = ps.b0, lane = threadIdx.x & 63;
   const float* ys = ps.ys;
+  if constexpr (KP == KP_DENSE) {
+    if (ps.epi > E_DOWN) return;
+  } else if constexpr (KP == KP_MOE) {
+    if (ps.epi == E_GU || ps.epi == E_DOWN) return;
+  }
   switch (ps.epi) {
     case E_QKV: {   // RoPE at each request's position, then q/k/v out and the K/V append
       const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d, ni = ps.n * nb;
@@ -1515,14 +1525,15 @@ template <typename KT>
 __device__ __forceinline__ bool attn_dispatch(const Ctx& c, int b, int g, int ci, int tix, const int* wev) {
   const int G = c.a.dm.Hq / c.a.dm.Hkv, ck = c.a.attn_chunk;
   if constexpr (sizeof(KT) == 2) {
-    if (c.a.dm.d == 128 && G <= 8) {
-      if (G <= 4) return ck > 128 ? task_attn_mm<2, 4>(c, b, g, ci, tix, wev) : task_attn_mm<1, 4>(c, b, g, ci, tix, wev);
-      return ck > 128 ? task_attn_mm<2, 8>(c, b, g, ci, tix, wev) : task_attn_mm<1, 8>(c, b, g, ci, tix, wev);
-    }
+    // bfloat16 caches: decode_layer_init admits head_dim 128 with at most 8
+    // query heads per KV head only, all on the matrix cores
+    if (G <= 4) return ck > 128 ? task_attn_mm<2, 4>(c, b, g, ci, tix, wev) : task_attn_mm<1, 4>(c, b, g, ci, tix, wev);
+    return ck > 128 ? task_attn_mm<2, 8>(c, b, g, ci, tix, wev) : task_attn_mm<1, 8>(c, b, g, ci, tix, wev);
+  } else {
+    if (G >= 4) return attn_its<KT, 4>(c, b, g, ci, tix, ck, wev);
+    if (G == 2) return attn_its<KT, 2>(c, b, g, ci, tix, ck, wev);
+    return attn_its<KT, 1>(c, b, g, ci, tix, ck, wev);
   }
-  if (G >= 4) return attn_its<KT, 4>(c, b, g, ci, tix, ck, wev);
-  if (G == 2) return attn_its<KT, 2>(c, b, g, ci, tix, ck, wev);
-  return attn_its<KT, 1>(c, b, g, ci, tix, ck, wev);
 }
 
 // ---------------------------------------------------------------------------
@@ -1805,7 +1816,7 @@ __device__ __forceinline__ int stage_of(int type) {
 // kPart: a launch of an ablation schedule, which runs the layers and task
 // types `rs` names, with a grid-wide barrier after every stage if rs.barrier;
 // the fused launch (kPart false) runs everything, chained by events alone.
-template <typename WT, bool kPart>
+template <typename WT, bool kPart, int KP>
 __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict__ pa, RunSpec rs) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   const StepArgs& a = *pa;
@@ -1899,11 +1910,14 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
             break;
           }
           case T_ROUTE:
-            ok = dm.E <= 128 ? task_route<16>(c, need(EV_ROUTER, l)) : task_route<64>(c, need(EV_ROUTER, l));
+            if constexpr (KP != KP_DENSE)
+              ok = dm.E <= 128 ? task_route<16>(c, need(EV_ROUTER, l)) : task_route<64>(c, need(EV_ROUTER, l));
             break;
           case T_COMBINE:
-            ok = task_combine(c, need(EV_MDOWN, l));
-            if (ok) wg_notify(ev_ptr(a, l, EV_DOWN), wg & (kSubs - 1));
+            if constexpr (KP != KP_DENSE) {
+              ok = task_combine(c, need(EV_MDOWN, l));
+              if (ok) wg_notify(ev_ptr(a, l, EV_DOWN), wg & (kSubs - 1));
+            }
             break;
           default: break;
         }
@@ -1935,7 +1949,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
         bool split_last = false;   // it finished a split tile as its last slice task (a split task has one pass)
         for (int p = 0; ok; ++p) {
           Pass ps;
-          if (!make_pass<WT>(c, task, p, wev, ps)) break;
+          if (!make_pass<WT, KP>(c, task, p, wev, ps)) break;
           // the residual of O (the layer input) / down (h1) is final once this
           // workgroup has seen the event that produced it, or one that fires
           // only after it (every QKV tile waits for the previous layer's down
@@ -1958,7 +1972,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           // before any wave issues the next task's weight loads (those would
           // hold the stores back in the compute unit's memory queue)
           if (split_last || wave == 0)
-            epilogue<WT>(c, ps, early, split_last ? (int)threadIdx.x : (int)(threadIdx.x & 63), split_last ? kBlock : 64);
+            epilogue<WT, KP>(c, ps, early, split_last ? (int)threadIdx.x : (int)(threadIdx.x & 63), split_last ? kBlock : 64);
           if (threadIdx.x == 0) s.tclk[5] = (uint32_t)now_ticks();
         }
         if (!ok) return;
@@ -2248,16 +2262,21 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
 // ---------------------------------------------------------------------------
 // Launch wrappers
 // ---------------------------------------------------------------------------
-static const void* main_fn(int dtype, bool part) {
-  if (dtype == PMK_BF16) return part ? (const void*)pmk_main<uint16_t, true> : (const void*)pmk_main<uint16_t, false>;
-  return part ? (const void*)pmk_main<float, true> : (const void*)pmk_main<float, false>;
+static const void* main_fn(int dtype, bool part, bool moe) {
+  if (dtype == PMK_BF16) {
+    if (part) return (const void*)pmk_main<uint16_t, true, KP_ALL>;
+    return moe ? (const void*)pmk_main<uint16_t, false, KP_MOE> : (const void*)pmk_main<uint16_t, false, KP_DENSE>;
+  }
+  return part ? (const void*)pmk_main<float, true, KP_ALL> : (const void*)pmk_main<float, false, KP_ALL>;
 }
 
 hipError_t prepare_main(int dtype) {
-  for (bool part : {false, true}) {
-    const hipError_t e = hipFuncSetAttribute(main_fn(dtype, part), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-  }
+  for (bool part : {false, true})
+    for (bool moe : {false, true}) {
+      const hipError_t e =
+          hipFuncSetAttribute(main_fn(dtype, part, moe), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      if (e != hipSuccess) return e;
+    }
   return hipSuccess;
 }
 
@@ -2270,7 +2289,8 @@ hipError_t launch_main(const StepArgs& a, int dtype, hipStream_t s, RunSpec rs) 
   const StepArgs* pa = reinterpret_cast<const StepArgs*>(a.ws.args);
   void* args[] = {&pa, &rs};
   const bool part = rs.l0 != 0 || rs.l1 != a.dm.L || rs.types != kAllTypes || rs.barrier;
-  return hipLaunchCooperativeKernel(main_fn(dtype, part), dim3(a.dm.grid), dim3(kBlock), args, kLdsBytes, s);
+  return hipLaunchCooperativeKernel(main_fn(dtype, part, a.dm.moe != 0), dim3(a.dm.grid), dim3(kBlock), args,
+                                    kLdsBytes, s);
 }
 
 }  // namespace pmk
