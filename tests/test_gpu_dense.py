@@ -189,6 +189,28 @@ def test_8b_shape_large_batch_sampled(orc, B):
     check_dense(orc, case, w.tol, requests=[int(np.argmax(lens)), int(np.argmin(lens)), B - 1])
 
 
+def test_8b_shape_last_cache_slot_and_empty(orc):
+    """The append goes to the cache's last slot (length max_seq - 1) for one
+    request, next to an empty cache and a one-entry cache; every request
+    against the oracle."""
+    w = synth.get_workload("c3_8b_sweep")
+    case = build_case(w, 3, [699, 0, 1], n_layers=1, max_seq=700, tag="t18")
+    check_dense(orc, case, w.tol)
+
+
+def test_8b_shape_largest_batch_short_caches(orc):
+    """The largest batch a handle takes (1024 requests: 64 blocks of 16 rows per
+    projection), lengths in [0, 24] in a 25-slot cache, so several requests
+    start empty and several append into the last slot; one layer, four
+    sampled requests."""
+    w = synth.get_workload("c3_8b_sweep")
+    B = 1024
+    lens = synth.ragged_lengths(B, 0, 24, ("c3_8b_sweep", "lens_max_batch", B))
+    case = build_case(w, B, lens, n_layers=1, max_seq=25, tag="t19")
+    full = int(np.flatnonzero(lens == 24)[0])
+    check_dense(orc, case, w.tol, requests=[int(np.argmin(lens)), full, B // 2, B - 1])
+
+
 @pytest.mark.parametrize("B", [256, 512])
 def test_8b_shape_batch_beyond_128_sampled(orc, B):
     """Decode batches beyond the sweep's largest point (16 to 32 blocks of 16
