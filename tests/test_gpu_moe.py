@@ -28,6 +28,13 @@ SMALL_MOE_BF16 = Workload(name="small_moe_bf16", dtype="bf16", n_layers=1, hidde
                           head_dim=128, ffn_dim=0, n_experts=16, top_k=4, expert_ffn_dim=128, tol=1e-2)
 
 
+def wide_moe(E):
+    """More than 128 experts (up to the library's 512): a token's top-k runs over
+    the whole wave, 8 experts per lane."""
+    return Workload(name=f"wide_moe_{E}", dtype="bf16", n_layers=1, hidden=512, n_q_heads=8, n_kv_heads=2,
+                    head_dim=128, ffn_dim=0, n_experts=E, top_k=8, expert_ffn_dim=64, tol=1e-2)
+
+
 def announce(msg):
     print(f"[case] {msg}", flush=True)
 
@@ -144,6 +151,29 @@ def test_moe_forced_tie_bit_exact(orc):
     T = 6
     case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, [5, 100, 2047, 0, 64, 900], "m4", max_seq=2049,
                                             zero_router=True)
+    np.testing.assert_array_equal(rg["router_logits"], 0.0)
+    np.testing.assert_array_equal(rg["topk_idx"], np.tile(np.arange(8), (T, 1)))
+    np.testing.assert_array_equal(rg["topk_w"], np.full((T, 8), 0.125, np.float32))
+    assert compare_moe(w, T, got, ref, rg, rr, bm) == 0
+
+
+@pytest.mark.parametrize("E", [256, 512])
+def test_moe_many_experts(orc, E):
+    """256 and 512 experts, top-8, 24 tokens: routing over the whole wave, most
+    experts with one or no token."""
+    w = wide_moe(E)
+    T = 24
+    lens = synth.ragged_lengths(T, 1, 200, ("wide_moe", "lens", E))
+    case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, lens, f"m7_{E}", max_seq=201)
+    compare_moe(w, T, got, ref, rg, rr, bm)
+
+
+def test_moe_many_experts_forced_tie_bit_exact(orc):
+    """512 experts with an all-zero router: the tie rule across the whole wave
+    gives every token experts 0..7 with gates 1/8, exactly as the oracle."""
+    w = wide_moe(512)
+    T = 5
+    case, got, ref, rg, rr, bm, _ = run_moe(orc, w, T, [3, 0, 150, 64, 199], "m8", max_seq=201, zero_router=True)
     np.testing.assert_array_equal(rg["router_logits"], 0.0)
     np.testing.assert_array_equal(rg["topk_idx"], np.tile(np.arange(8), (T, 1)))
     np.testing.assert_array_equal(rg["topk_w"], np.full((T, 8), 0.125, np.float32))
