@@ -189,6 +189,15 @@ def test_8b_shape_large_batch_sampled(orc, B):
     check_dense(orc, case, w.tol, requests=[int(np.argmax(lens)), int(np.argmin(lens)), B - 1])
 
 
+def test_8b_shape_b1_256_position_chunks(orc):
+    """Batch 1 with 1500 cached positions: 6 attention chunks of 256 positions
+    (the longest chunk the O-projection merge takes), each on a workgroup of
+    its own."""
+    w = synth.get_workload("c2_8b_b1")
+    case = build_case(w, 1, [1500], n_layers=2, max_seq=1600, tag="t20")
+    check_dense(orc, case, w.tol)
+
+
 def test_8b_shape_last_cache_slot_and_empty(orc):
     """The append goes to the cache's last slot (length max_seq - 1) for one
     request, next to an empty cache and a one-entry cache; every request

@@ -144,6 +144,15 @@ def test_moe_qwen3_30b_a3b_shape(orc, T):
     assert rel_l2(a, b) <= w.tol
 
 
+@pytest.mark.parametrize("S", [1000, 1800])
+def test_moe_one_token_merged_attention(orc, S):
+    """One token with fewer than 2048 cached positions: 8 chunks of 128 or of
+    256 positions for 8 query heads per KV head, merged by the O-projection."""
+    w = synth.get_workload("c4_moe")
+    case, got, ref, rg, rr, bm, _ = run_moe(orc, w, 1, [S], f"m9_{S}", max_seq=S + 1)
+    compare_moe(w, 1, got, ref, rg, rr, bm)
+
+
 def test_moe_forced_tie_bit_exact(orc):
     """All-zero router: every logit is exactly 0, so each token takes experts
     0..k-1 with gates 1/k; routing and grouping match the oracle exactly."""
