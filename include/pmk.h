@@ -216,6 +216,16 @@ int pmk_set_schedule(pmk_handle* h, int32_t mode);
 #define PMK_MOE_DYNAMIC 1
 int pmk_set_moe_scheduler(pmk_handle* h, int32_t mode);
 
+/* The event-wait limit of later calls, in microseconds (100 ticks of the
+ * device's 100 MHz clock each); 0 restores the limit set at init
+ * (desc->watchdog_ms). A wait that exceeds it abandons the step: the device
+ * error word takes PMK_ERR_TIMEOUT, the abort flag makes every workgroup leave
+ * the step, and later steps are skipped until pmk_get_device_error has read
+ * (and cleared) the word; the next step then re-arms every counter. For
+ * callers with a latency budget and for tests of that path.
+ * Errors: PMK_ERR_ARG (null handle, negative limit). */
+int pmk_set_watchdog_us(pmk_handle* h, int32_t us);
+
 /* Task trace for profiling the schedule. `buf` is a caller-owned device buffer
  * of grid * entries_per_wg * 8 uint32 (grid from pmk_query); NULL detaches.
  * While attached, every call records, per workgroup w, at

@@ -24,7 +24,7 @@ MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC}
 
 EXPORTS = ("decode_layer_init", "decode_step", "moe_layer_step", "decode_layer_destroy", "pmk_strerror",
            "pmk_get_device_error", "pmk_query", "pmk_timing_enable", "pmk_timing_read", "pmk_trace_attach",
-           "pmk_set_schedule", "pmk_set_moe_scheduler")
+           "pmk_set_schedule", "pmk_set_moe_scheduler", "pmk_set_watchdog_us")
 
 i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -97,6 +97,8 @@ def load():
     L.pmk_set_schedule.restype = i32
     L.pmk_set_moe_scheduler.argtypes = [vp, i32]
     L.pmk_set_moe_scheduler.restype = i32
+    L.pmk_set_watchdog_us.argtypes = [vp, i32]
+    L.pmk_set_watchdog_us.restype = i32
     _lib = L
     return L
 

@@ -25,6 +25,7 @@ struct pmk_handle {
   LayerPtrs* d_layers = nullptr;
   hipStream_t last_stream = nullptr;
   unsigned long long watchdog_ticks = 0;
+  unsigned long long watchdog_init = 0;   // the limit from the descriptor
   bool timing = false;
   uint32_t* trace = nullptr;
   int trace_cap = 0;
@@ -290,6 +291,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   if (prepare_main(desc->dtype) != hipSuccess) return fail(PMK_ERR_DEVICE);
   const int wd = desc->watchdog_ms > 0 ? desc->watchdog_ms : 2000;
   h->watchdog_ticks = (unsigned long long)wd * 100000ull;   // s_memrealtime: 100 MHz
+  h->watchdog_init = h->watchdog_ticks;
   *out = h;
   return PMK_OK;
 }
@@ -384,6 +386,12 @@ int decode_layer_destroy(pmk_handle* h) {
   if (h->ws_base) (void)hipFree(h->ws_base);
   delete h;
   return rc;
+}
+
+int pmk_set_watchdog_us(pmk_handle* h, int32_t us) {
+  if (!h || us < 0) return PMK_ERR_ARG;
+  h->watchdog_ticks = us == 0 ? h->watchdog_init : (unsigned long long)us * 100ull;
+  return PMK_OK;
 }
 
 int pmk_get_device_error(pmk_handle* h) {

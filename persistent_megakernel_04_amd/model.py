@@ -116,6 +116,10 @@ class DecodeModel:
         m = _abi.MOE_SCHEDULERS[mode] if isinstance(mode, str) else int(mode)
         _abi.check(self.lib.pmk_set_moe_scheduler(self.handle, m), "pmk_set_moe_scheduler")
 
+    def set_watchdog_us(self, us: int):
+        """Event-wait limit of later steps in microseconds; 0 restores the limit set at init."""
+        _abi.check(self.lib.pmk_set_watchdog_us(self.handle, int(us)), "pmk_set_watchdog_us")
+
     def close(self):
         if getattr(self, "handle", None):
             self.lib.decode_layer_destroy(self.handle)

@@ -50,6 +50,7 @@ def test_strerror_and_null_handle_errors_need_no_gpu():
     assert lib.pmk_trace_attach(None, None, 0) == _abi.PMK_ERR_ARG
     assert lib.pmk_set_schedule(None, _abi.SCHED_FUSED) == _abi.PMK_ERR_ARG
     assert lib.pmk_set_moe_scheduler(None, _abi.MOE_DYNAMIC) == _abi.PMK_ERR_ARG
+    assert lib.pmk_set_watchdog_us(None, 1) == _abi.PMK_ERR_ARG
     assert lib.pmk_timing_enable(None, 1) == _abi.PMK_ERR_ARG
     out = ctypes.c_void_p()
     assert lib.decode_layer_init(None, None, ctypes.byref(out)) == _abi.PMK_ERR_ARG

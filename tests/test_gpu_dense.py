@@ -116,6 +116,37 @@ def test_bad_length_is_reported_and_step_skipped():
     model.close()
 
 
+def test_watchdog_abandons_step_then_handle_recovers(orc):
+    """A 1 us event-wait limit, forced from the host, makes the step's first
+    long wait expire: the step is abandoned with PMK_ERR_TIMEOUT and every
+    workgroup leaves it (the kernel returns). With the limit restored and the
+    inputs put back, the same handle runs a step that matches the oracle."""
+    from persistent_megakernel_04_amd import _abi
+    w = synth.get_workload("c2_8b_b1")
+    case = build_case(w, 1, [512], n_layers=2, max_seq=600, tag="t21")
+    hidden0, kv0 = case.hidden.clone(), case.kv.clone()
+    model = make_model(case)
+    model.set_watchdog_us(1)
+    announce("decode_step with a 1 us watchdog")
+    model.step(case.hidden, case.kv, case.seq_lens)
+    torch.cuda.synchronize()
+    assert model.device_error() == _abi.PMK_ERR_TIMEOUT
+    assert model.device_error() == 0   # reading the error word cleared it
+    model.set_watchdog_us(0)
+    case.hidden.copy_(hidden0)
+    case.kv.copy_(kv0)
+    inp = oracle_inputs(case)
+    announce("decode_step after recovery")
+    model.step(case.hidden, case.kv, case.seq_lens)
+    torch.cuda.synchronize()
+    assert model.device_error() == 0
+    ref, _ = run_oracle_dense(orc, case, inp)
+    err = rel_l2(to_np(case.hidden).astype(np.float64), ref)
+    print(f"  rel_l2(hidden) after recovery = {err:.3e}", flush=True)
+    assert err <= w.tol
+    model.close()
+
+
 def test_consecutive_steps_chain(orc):
     """Three decode steps in a row on one handle: each step's output and K/V
     append feed the next (lengths advance by one), against the oracle chained
