@@ -161,9 +161,10 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
         const StageGeo g = stage_geo(K4[st], U4[st], R4[st], nb, avail, dm.kstep, dm.xpad);
         // more than 16 rows: the same split for 16, one record per batch block
         const size_t blocks = nb == kMaxNb ? (size_t)ceil_div(dm.max_batch, kMaxNb) : 1;
-        if (g.ks > 1)
-          kpart_floats = std::max(kpart_floats, blocks * g.tiles * g.ks *
-                                                    (((size_t)ceil_div(U4[st], g.tiles) * R4[st] * nb + 16 + 3) & ~(size_t)3));
+        if (g.ks > 1) {
+          const size_t rec = ((size_t)ceil_div(U4[st], g.tiles) * R4[st] * nb + 16 + 3) & ~(size_t)3;
+          kpart_floats = std::max(kpart_floats, blocks * g.tiles * g.ks * rec);
+        }
       }
   }
   const long attn_max = (long)dm.max_batch * dm.Hkv * dm.max_chunks;

@@ -1971,8 +1971,10 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
           // wave stores the outputs and the workgroup notifies together,
           // before any wave issues the next task's weight loads (those would
           // hold the stores back in the compute unit's memory queue)
-          if (split_last || wave == 0)
-            epilogue<WT, KP>(c, ps, early, split_last ? (int)threadIdx.x : (int)(threadIdx.x & 63), split_last ? kBlock : 64);
+          if (split_last || wave == 0) {
+            const int t0 = split_last ? (int)threadIdx.x : (int)(threadIdx.x & 63);
+            epilogue<WT, KP>(c, ps, early, t0, split_last ? kBlock : 64);
+          }
           if (threadIdx.x == 0) s.tclk[5] = (uint32_t)now_ticks();
         }
         if (!ok) return;
