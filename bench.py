@@ -156,6 +156,10 @@ def main():
     ap.add_argument("--seq-range", type=int, nargs=2, default=None, metavar=("LO", "HI"),
                     help="cached lengths uniform on [LO, HI] instead of the workload's own (e.g. batches beyond 128, "
                     "whose cache at the sweep's lengths would not fit in HBM)")
+    ap.add_argument("--weight-layout", default="auto", choices=["auto", "rows", "tiles"],
+                    help="bfloat16 weights row-major, or packed once before timing into the 16-row tile layout "
+                    "(one contiguous 1 KiB block per wave-wide load, streamed non-temporally); auto: tiles when "
+                    "the packed copies fit beside the row-major weights and the KV cache")
     ap.add_argument("--trace", default=None, help="after the timed steps, run one traced step and write a "
                     "per-stage summary of the task trace to this file")
     args = ap.parse_args()
@@ -219,7 +223,13 @@ def main():
         # the oracle's sample sees step 0's inputs, taken before any GPU step
         cpu_case = Case(w, L, layers, kv, hid[0].clone(), steps_lens[0].clone(), B, max_seq)
 
-    model = DecodeModel.from_workload(w, layers, B, max_seq)
+    layout = args.weight_layout
+    if layout == "auto":
+        weight_bytes = sum(t.numel() * t.element_size() for Ld in layers for t in Ld.values() if t is not None)
+        free = torch.cuda.mem_get_info()[0]
+        layout = "tiles" if w.dtype == "bf16" and weight_bytes + (8 << 30) < free else "rows"
+    model = DecodeModel.from_workload(w, layers, B, max_seq, weight_layout=layout)
+    log(f"weight layout: {layout}")
     model.set_schedule(args.schedule)
     if w.n_experts:
         model.set_moe_scheduler(args.moe_scheduler)
@@ -327,6 +337,7 @@ def main():
                       **({"seq_range": list(args.seq_range)} if args.seq_range is not None else {}),
                       "weights": w.dtype, "kv_cache": w.dtype,
                       "accumulate": "f32", "parallelism": "single GPU", "schedule": args.schedule,
+                      "weight_layout": layout,
                       "host_submit_us_per_step": round(host_us, 1), "cache_flushed": bool(args.flush_cache),
                       **({"moe_scheduler": args.moe_scheduler} if w.n_experts else {}),
                       "launches_per_step": launches},

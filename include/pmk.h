@@ -18,7 +18,9 @@
  *  - All tensor arguments are device pointers (hipMalloc'd or equivalent) and
  *    stay owned by the caller. The library never copies or frees them.
  *  - Weights are row-major [out][in] in the model dtype (float32 or bfloat16
- *    as raw 16-bit patterns); RMSNorm gains are always float32.
+ *    as raw 16-bit patterns), or, for bfloat16 with weight_layout =
+ *    PMK_TILES, in the tile layout that pmk_pack_weights writes; RMSNorm gains
+ *    are always float32.
  *  - Calls are stream-ordered and asynchronous; `stream` is a hipStream_t
  *    passed as void* (NULL = the null stream). One handle serves one stream at a
  *    time: calls on one handle must not overlap.
@@ -50,6 +52,10 @@ enum pmk_status {
 
 enum pmk_dtype { PMK_F32 = 0, PMK_BF16 = 1 };
 
+/* Storage of the weight matrices: row-major, or 16-row tiles (see
+ * pmk_pack_weights). The arithmetic, and so every output bit, is the same. */
+enum pmk_weight_layout { PMK_ROWS = 0, PMK_TILES = 1 };
+
 /* Model description. Dense stack when n_experts == 0, MoE layers otherwise. */
 typedef struct pmk_model_desc {
   int32_t abi_version;       /* must be PMK_ABI_VERSION */
@@ -68,7 +74,9 @@ typedef struct pmk_model_desc {
   float rms_eps;             /* e.g. 1e-5 */
   float rope_theta;          /* e.g. 10000 */
   int32_t watchdog_ms;       /* event-wait limit before the step is abandoned; 0 = 2000 */
-  int32_t reserved[6];       /* zero */
+  int32_t weight_layout;     /* pmk_weight_layout; PMK_TILES: bfloat16 only, with H, Hq d, F and Fe multiples
+                                of 32 and (Hq + 2 Hkv) d and E multiples of 16 (else PMK_ERR_UNSUPPORTED) */
+  int32_t reserved[5];       /* zero */
 } pmk_model_desc;
 
 /* One layer's weights (device pointers, caller-owned). Dense layers use
@@ -225,6 +233,25 @@ int pmk_set_moe_scheduler(pmk_handle* h, int32_t mode);
  * callers with a latency budget and for tests of that path.
  * Errors: PMK_ERR_ARG (null handle, negative limit). */
 int pmk_set_watchdog_us(pmk_handle* h, int32_t us);
+
+/* Writes a copy of the bfloat16 matrix src [rows][cols] (row-major) into dst
+ * in the tile layout that a handle with weight_layout = PMK_TILES reads. The
+ * decode step reads each weight matrix once as a stream of 16-row groups
+ * (the weight-streaming tile tasks of the persistent megakernel, Event Tensor
+ * summary page, Core method); in the tile layout the 16 rows of a group are
+ * interleaved per 32-column step, so that every wave-wide 16-byte-per-lane
+ * load reads one contiguous 1 KiB block: the 16-byte piece holding row r,
+ * columns 32 s + 8 g .. 32 s + 8 g + 7 (g < 4) is piece
+ *   ((r / 16) * (cols / 32) + s) * 64 + (r % 16) + 16 g
+ * of dst. A stack of matrices with the same cols (the experts of a layer,
+ * [E][rows][cols]) packs as one matrix of E rows rows. dst has the same size
+ * as src (rows * cols * 2 bytes) and is caller-owned; the copy is ordered on
+ * `stream` (hipStream_t as void*, NULL = null stream) and src may be freed
+ * once it has run.
+ * Errors: PMK_ERR_ARG (null or unaligned (16-byte) pointer, rows not a
+ * positive multiple of 16, cols not a positive multiple of 32, overlapping
+ * src and dst), PMK_ERR_DEVICE (launch failed). */
+int pmk_pack_weights(const void* src, void* dst, int64_t rows, int64_t cols, void* stream);
 
 /* Task trace for profiling the schedule. `buf` is a caller-owned device buffer
  * of grid * entries_per_wg * 8 uint32 (grid from pmk_query); NULL detaches.

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(PKG, "libpmk.so")
 PMK_ABI_VERSION = 1
 PMK_OK, PMK_ERR_ARG, PMK_ERR_OOM, PMK_ERR_DEVICE, PMK_ERR_TIMEOUT, PMK_ERR_SEQ, PMK_ERR_UNSUPPORTED = range(7)
 PMK_F32, PMK_BF16 = 0, 1
+PMK_ROWS, PMK_TILES = 0, 1
 
 # pmk_set_schedule modes (include/pmk.h)
 SCHED_FUSED, SCHED_PER_LAYER, SCHED_PER_STAGE, SCHED_BARRIER = 0, 1, 2, 3
@@ -24,7 +25,7 @@ MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC}
 
 EXPORTS = ("decode_layer_init", "decode_step", "moe_layer_step", "decode_layer_destroy", "pmk_strerror",
            "pmk_get_device_error", "pmk_query", "pmk_timing_enable", "pmk_timing_read", "pmk_trace_attach",
-           "pmk_set_schedule", "pmk_set_moe_scheduler", "pmk_set_watchdog_us")
+           "pmk_set_schedule", "pmk_set_moe_scheduler", "pmk_set_watchdog_us", "pmk_pack_weights")
 
 i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -33,7 +34,7 @@ class ModelDesc(ctypes.Structure):
     _fields_ = [("abi_version", i32), ("dtype", i32), ("n_layers", i32), ("hidden", i32), ("n_q_heads", i32),
                 ("n_kv_heads", i32), ("head_dim", i32), ("ffn_dim", i32), ("n_experts", i32), ("top_k", i32),
                 ("expert_ffn_dim", i32), ("max_batch", i32), ("max_seq", i32), ("rms_eps", f32),
-                ("rope_theta", f32), ("watchdog_ms", i32), ("reserved", i32 * 6)]
+                ("rope_theta", f32), ("watchdog_ms", i32), ("weight_layout", i32), ("reserved", i32 * 5)]
 
 
 LAYER_FIELDS = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate", "w_up", "w_down", "w_router",
@@ -99,6 +100,8 @@ def load():
     L.pmk_set_moe_scheduler.restype = i32
     L.pmk_set_watchdog_us.argtypes = [vp, i32]
     L.pmk_set_watchdog_us.restype = i32
+    L.pmk_pack_weights.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
+    L.pmk_pack_weights.restype = i32
     _lib = L
     return L
 

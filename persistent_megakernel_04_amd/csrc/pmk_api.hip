@@ -50,6 +50,7 @@ int check_desc(const pmk_model_desc* d) {
   if (d->max_batch < 1 || d->max_seq < 1) return PMK_ERR_ARG;
   if (!(d->rms_eps > 0.f) || !(d->rope_theta > 0.f)) return PMK_ERR_ARG;
   if (d->n_experts < 0) return PMK_ERR_ARG;
+  if (d->weight_layout != PMK_ROWS && d->weight_layout != PMK_TILES) return PMK_ERR_ARG;
   if (d->n_experts == 0 && (d->ffn_dim < 8 || d->ffn_dim % 8)) return PMK_ERR_ARG;
   if (d->n_experts > 0 && (d->top_k < 1 || d->top_k > d->n_experts || d->expert_ffn_dim < 8 ||
                            d->expert_ffn_dim % 8))
@@ -59,6 +60,13 @@ int check_desc(const pmk_model_desc* d) {
   const int G = d->n_q_heads / d->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PMK_ERR_UNSUPPORTED;
   if (d->max_batch > kMaxBatchAll) return PMK_ERR_UNSUPPORTED;
+  if (d->weight_layout == PMK_TILES) {
+    // bfloat16 only; every matrix in whole 16-row groups and 32-column steps
+    const int qd = d->n_q_heads * d->head_dim, qkv = (d->n_q_heads + 2 * d->n_kv_heads) * d->head_dim;
+    if (d->dtype != PMK_BF16 || d->hidden % 32 || qd % 32 || qkv % 16) return PMK_ERR_UNSUPPORTED;
+    if (d->n_experts == 0 && d->ffn_dim % 32) return PMK_ERR_UNSUPPORTED;
+    if (d->n_experts > 0 && (d->expert_ffn_dim % 32 || d->n_experts % 16)) return PMK_ERR_UNSUPPORTED;
+  }
   // every GEMV depth must leave room for one staged input row in LDS (float32
   // inputs, or bfloat16 hi + lo pairs: 4 bytes per element either way)
   const int xrow_max = kXsBytes / 4 - 64;
@@ -89,7 +97,8 @@ const char* pmk_strerror(int s) {
     case PMK_ERR_UNSUPPORTED:
       return "shape not implemented: needs head_dim*sizeof(dtype) == 256, Hq/Hkv in {1,2,4,8}, max_batch <= 1024, "
              "GEMV depths that fit one LDS input row, and for MoE E <= 512, top_k <= 8, H and Fe small enough "
-             "for 16 staged rows";
+             "for 16 staged rows; the tile weight layout needs bfloat16, H, Hq d, F and Fe multiples of 32, "
+             "(Hq + 2 Hkv) d and E multiples of 16";
     default: return "unknown status";
   }
 }
@@ -128,6 +137,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   dm.kstep = desc->dtype == PMK_BF16 ? 32 : 16;
   dm.xpad = desc->dtype == PMK_BF16 ? 8 : 4;
   dm.attn_mm = desc->dtype == PMK_BF16 && dm.d == 128 && dm.Hq / dm.Hkv <= 8;
+  dm.wtiles = desc->weight_layout == PMK_TILES ? 1 : 0;
   dm.merge_b = std::min(dm.max_batch, kMergeFloats / (dm.Hq * dm.d));
   const int G = dm.grid;
   dm.qkv_units = (dm.Hq + 2 * dm.Hkv) * dm.d / 2;
@@ -289,7 +299,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     a0.geo[3] = StageGeo{1, std::max(dm.down_tiles, 1), std::max(dm.F, 1), 1};
     if (hipMemcpy(ws.args, &a0, sizeof(a0), hipMemcpyHostToDevice) != hipSuccess) return fail(PMK_ERR_DEVICE);
   }
-  if (prepare_main(desc->dtype) != hipSuccess) return fail(PMK_ERR_DEVICE);
+  if (prepare_main(desc->dtype, dm.wtiles) != hipSuccess) return fail(PMK_ERR_DEVICE);
   const int wd = desc->watchdog_ms > 0 ? desc->watchdog_ms : 2000;
   h->watchdog_ticks = (unsigned long long)wd * 100000ull;   // s_memrealtime: 100 MHz
   h->watchdog_init = h->watchdog_ticks;
@@ -392,6 +402,17 @@ int decode_layer_destroy(pmk_handle* h) {
 int pmk_set_watchdog_us(pmk_handle* h, int32_t us) {
   if (!h || us < 0) return PMK_ERR_ARG;
   h->watchdog_ticks = us == 0 ? h->watchdog_init : (unsigned long long)us * 100ull;
+  return PMK_OK;
+}
+
+int pmk_pack_weights(const void* src, void* dst, int64_t rows, int64_t cols, void* stream) {
+  if (!src || !dst || rows <= 0 || cols <= 0 || rows % 16 || cols % 32) return PMK_ERR_ARG;
+  if (rows > INT64_MAX / 2 / cols) return PMK_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) return PMK_ERR_ARG;
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t n = (uintptr_t)(rows * cols * 2);
+  if (s < d + n && d < s + n) return PMK_ERR_ARG;   // the two must not overlap
+  if (launch_pack(src, dst, rows, cols, reinterpret_cast<hipStream_t>(stream)) != hipSuccess) return PMK_ERR_DEVICE;
   return PMK_OK;
 }
 

@@ -140,6 +140,12 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
   const u4v v = *(gptr_u4)(p);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// The same as a streaming (non-temporal) load: for weights read once per step
+// whose wave-wide loads cover whole 1 KiB blocks.
+__device__ __forceinline__ uint4 ldg16_nt(const void* p) {
+  const u4v v = __builtin_nontemporal_load((gptr_u4)(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 typedef const __attribute__((address_space(1))) uint32_t* gptr_u32;
 __device__ __forceinline__ uint32_t ldg4(const void* p) { return *(gptr_u32)(p); }

@@ -120,6 +120,7 @@ struct Dims {
   int max_tiles;                     // MoE: bound on grouped-GEMM row tiles
   int tctr_stride;                   // split-K tile counters per stage: grid x batch blocks
   int max_down;                      // MoE: bound on grouped down tasks (row tiles x H slices)
+  int wtiles;                        // 1: bfloat16 weights in the tile layout (pmk_pack_weights)
 };
 
 // Device workspace (one allocation, carved by the host).
@@ -188,7 +189,9 @@ struct StepArgs {
 // handle never queues dense gate/up or down tasks; dropping the other kind's
 // code halves the fused kernel (about 360 to 170 KB of instructions) and frees
 // registers, which took 2-3 % off the batch-1 and batch-4 steps.
-enum KernelPaths : int { KP_ALL = 0, KP_DENSE = 1, KP_MOE = 2 };
+// KP_TILES (added to either): bfloat16 weights in the 16-row tile layout that
+// pmk_pack_weights writes, streamed with non-temporal loads.
+enum KernelPaths : int { KP_ALL = 0, KP_DENSE = 1, KP_MOE = 2, KP_TILES = 4 };
 
 // What one launch of the persistent kernel runs: layers [l0, l1), and of
 // their queue entries only the task types whose bit (1 << type) is set;
@@ -203,6 +206,7 @@ constexpr unsigned kAllTypes = 0xffffffffu;
 // Launch wrappers (defined in pmk_kernels.hip).
 hipError_t launch_prologue(const StepArgs& a, hipStream_t s);
 hipError_t launch_main(const StepArgs& a, int dtype, hipStream_t s, RunSpec rs);
-hipError_t prepare_main(int dtype);
+hipError_t prepare_main(int dtype, int wtiles);
+hipError_t launch_pack(const void* src, void* dst, long rows, long cols, hipStream_t s);
 
 }  // namespace pmk

@@ -145,17 +145,28 @@ struct GemvRows {
   int k0;              // first column of the pass (a K slice)
 };
 
-template <typename WT>
+// Where row `row` of a weight matrix with `ld` columns starts at column k0:
+// row-major, or (PK) in the tile layout, where the 16 rows of a row group are
+// interleaved per 32-column step so that one wave-wide load reads a contiguous
+// 1 KiB block: the 16-byte piece of (row r, columns 32 s + 8 g .. + 7) is
+// piece ((r / 16) (ld / 32) + s) 64 + r % 16 + 16 g. For PK the returned
+// pointer is that of the piece g = 0; a step advances it by 512 elements.
+template <typename WT, bool PK>
+__device__ __forceinline__ const WT* wrow(const void* base, size_t row, int ld, int k0) {
+  const WT* b = reinterpret_cast<const WT*>(base);
+  if (PK) return b + (row >> 4) * 16 * (size_t)ld + (row & 15) * 8 + (size_t)(k0 >> 5) * 512;
+  return b + row * ld + k0;
+}
+
+template <typename WT, bool PK>
 __device__ __forceinline__ const WT* row_ptr(const GemvRows& rw, int j) {
-  const WT* b = reinterpret_cast<const WT*>(rw.base) + rw.k0;
   if (rw.mode == ROWS_QKV) {
     // local row 2u is (head h, i), 2u + 1 is (h, i + d/2): the two rows of a rotation pair
     const int unit = rw.r0 + (j >> 1), h = unit / rw.half, i = unit - h * rw.half;
-    return b + (size_t)(h * 2 * rw.half + i + (j & 1) * rw.half) * rw.ld;
+    return wrow<WT, PK>(rw.base, (size_t)(h * 2 * rw.half + i + (j & 1) * rw.half), rw.ld, rw.k0);
   }
-  if (rw.mode == ROWS_PAIR && j >= rw.half)
-    return reinterpret_cast<const WT*>(rw.base2) + rw.k0 + (size_t)(rw.r0 + j - rw.half) * rw.ld;
-  return b + (size_t)(rw.r0 + j) * rw.ld;
+  if (rw.mode == ROWS_PAIR && j >= rw.half) return wrow<WT, PK>(rw.base2, (size_t)(rw.r0 + j - rw.half), rw.ld, rw.k0);
+  return wrow<WT, PK>(rw.base, (size_t)(rw.r0 + j), rw.ld, rw.k0);
 }
 
 struct GemvIn {
@@ -370,7 +381,7 @@ __device__ __forceinline__ WaveItems wave_items(int RG, int NKS, int nb, int wav
 // pass's last steps prefetch the next one, was measured slower: the workgroups
 // that finish a stage early then take HBM bandwidth from the ones that gate
 // the stage's event.)
-template <typename WT, bool SP>
+template <typename WT, bool SP, bool PK>
 __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
                                      const int* wait_ev, int wait_subs, float* ys) {
   typedef MM<WT> T;
@@ -385,16 +396,23 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
   const int nks_pad = nks > D ? (nks + D - 1) / D * D : D;
   auto item_rows = [&](int it) -> const WT* {
     const int rg = min(wi.rg0 + min(it, max(wi.n - 1, 0)) * wi.rg_step, RG - 1);
-    return row_ptr<WT>(rw, min(rg * 16 + mrow, R - 1));   // padded rows repeat a valid row
+    return row_ptr<WT, PK>(rw, min(rg * 16 + mrow, R - 1));   // padded rows repeat a valid row
   };
-  auto kofs = [&](int ks) { return min((wi.ks_lo + ks) * T::KSTEP + kg, kmax); };
+  auto kofs = [&](int ks) {
+    if constexpr (PK) return min(wi.ks_lo + ks, NKS - 1) * 512 + grp * 128;
+    else return min((wi.ks_lo + ks) * T::KSTEP + kg, kmax);
+  };
+  auto ldw = [&](const WT* p) {
+    if constexpr (PK) return ldg16_nt(p);
+    else return ldg16(p);
+  };
 
   uint4 ring[D];
   const WT* cur = item_rows(0);
   const WT* nxt = item_rows(1);
   if (wi.n > 0) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) ring[d] = ldg16(cur + kofs(min(d, nks_c)));
+    for (int d = 0; d < D; ++d) ring[d] = ldw(cur + kofs(min(d, nks_c)));
   }
   if (!ctx_wait(c, wait_ev, wait_subs)) return false;
   if (in.merge_b0 >= 0)
@@ -445,7 +463,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
         // refill with the step kRing ahead: of this item, else of the next item
         const int nk = ks + D;
         const bool here = nk < nks_pad;
-        ring[d] = ldg16((here ? cur : nxt) + kofs(here ? min(nk, nks_c) : min(nk - nks_pad, nks_c)));
+        ring[d] = ldw((here ? cur : nxt) + kofs(here ? min(nk, nks_c) : min(nk - nks_pad, nks_c)));
         // keep the refill here: left to itself the scheduler sinks all refills
         // to the end of the unrolled body, and the ring degrades to batches
         // that drain to zero loads in flight
@@ -491,10 +509,10 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
 // beyond a 1e-2 output tolerance; the pair carries float32-level accuracy.
 template <typename WT> struct SplitIn { static constexpr bool value = sizeof(WT) == 2; };
 
-template <typename WT>
+template <typename WT, bool PK>
 __device__ __forceinline__ bool gemv_any(const Ctx& c, const GemvRows& rw, int R, int K, const GemvIn& in, int nb,
                                          const int* wev, int wsubs, float* ys) {
-  return gemv<WT, SplitIn<WT>::value>(c, rw, R, K, in, nb, wev, wsubs, ys);
+  return gemv<WT, SplitIn<WT>::value, PK>(c, rw, R, K, in, nb, wev, wsubs, ys);
 }
 
 // Bytes of one staged input row of depth K in LDS (bfloat16 hi + lo, or float).
@@ -557,9 +575,9 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
   const Dims& dm = a.dm;
   const LayerPtrs* Lp = a.layers + c.l;   // its fields are read with global loads (ldp)
   const int tile = task.y;
-  if constexpr (KP == KP_DENSE) {
+  if constexpr ((KP & 3) == KP_DENSE) {
     if (task.x != T_QKV && task.x != T_O && task.x != T_GU && task.x != T_DOWN) return false;
-  } else if constexpr (KP == KP_MOE) {
+  } else if constexpr ((KP & 3) == KP_MOE) {
     if (task.x == T_GU || task.x == T_DOWN) return false;
   }
   ps.wev = p == 0 ? wev : nullptr;
@@ -830,9 +848,9 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
   const Dims& dm = a.dm;
   const int nb = ps.nb, b0 = ps.b0, lane = threadIdx.x & 63;
   const float* ys = ps.ys;
-  if constexpr (KP == KP_DENSE) {
+  if constexpr ((KP & 3) == KP_DENSE) {
     if (ps.epi > E_DOWN) return;
-  } else if constexpr (KP == KP_MOE) {
+  } else if constexpr ((KP & 3) == KP_MOE) {
     if (ps.epi == E_GU || ps.epi == E_DOWN) return;
   }
   switch (ps.epi) {
@@ -1910,11 +1928,11 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
             break;
           }
           case T_ROUTE:
-            if constexpr (KP != KP_DENSE)
+            if constexpr ((KP & 3) != KP_DENSE)
               ok = dm.E <= 128 ? task_route<16>(c, need(EV_ROUTER, l)) : task_route<64>(c, need(EV_ROUTER, l));
             break;
           case T_COMBINE:
-            if constexpr (KP != KP_DENSE) {
+            if constexpr ((KP & 3) != KP_DENSE) {
               ok = task_combine(c, need(EV_MDOWN, l));
               if (ok) wg_notify(ev_ptr(a, l, EV_DOWN), wg & (kSubs - 1));
             }
@@ -1959,7 +1977,7 @@ __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict
                              ((ps.epi == E_O && (l == 0 || seen(EV_DOWN, l - 1) || seen(EV_QKV, l))) ||
                               (ps.epi == E_DOWN && seen(EV_O, l)));
           if (early) load_resid(a, ps, resid);
-          ok = gemv_any<WT>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs, ps.ys);
+          ok = gemv_any<WT, (KP & KP_TILES) != 0>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs, ps.ys);
           if (!ok) break;
           if (ps.ks > 1 && !reduce_slices(c, ps)) {
             done = false;
@@ -2264,7 +2282,12 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
 // ---------------------------------------------------------------------------
 // Launch wrappers
 // ---------------------------------------------------------------------------
-static const void* main_fn(int dtype, bool part, bool moe) {
+static const void* main_fn(int dtype, bool part, bool moe, bool tiles) {
+  if (dtype == PMK_BF16 && tiles) {
+    if (part) return (const void*)pmk_main<uint16_t, true, KP_ALL | KP_TILES>;
+    return moe ? (const void*)pmk_main<uint16_t, false, KP_MOE | KP_TILES>
+               : (const void*)pmk_main<uint16_t, false, KP_DENSE | KP_TILES>;
+  }
   if (dtype == PMK_BF16) {
     if (part) return (const void*)pmk_main<uint16_t, true, KP_ALL>;
     return moe ? (const void*)pmk_main<uint16_t, false, KP_MOE> : (const void*)pmk_main<uint16_t, false, KP_DENSE>;
@@ -2272,14 +2295,36 @@ static const void* main_fn(int dtype, bool part, bool moe) {
   return part ? (const void*)pmk_main<float, true, KP_ALL> : (const void*)pmk_main<float, false, KP_ALL>;
 }
 
-hipError_t prepare_main(int dtype) {
+hipError_t prepare_main(int dtype, int wtiles) {
   for (bool part : {false, true})
     for (bool moe : {false, true}) {
-      const hipError_t e =
-          hipFuncSetAttribute(main_fn(dtype, part, moe), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+      const hipError_t e = hipFuncSetAttribute(main_fn(dtype, part, moe, wtiles != 0),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
       if (e != hipSuccess) return e;
     }
   return hipSuccess;
+}
+
+// Writes a bfloat16 [rows][cols] matrix (rows % 16 == 0, cols % 32 == 0) in
+// the tile layout: 16-byte piece q = (rg (cols / 32) + s) 64 + r + 16 g holds
+// row 16 rg + r, columns 32 s + 8 g .. + 7. One thread per piece; the writes
+// are contiguous, the reads 64-byte runs.
+__global__ void __launch_bounds__(256) pmk_pack(const uint4* __restrict__ src, uint4* __restrict__ dst, long rows,
+                                                long cols) {
+  const long n = rows * cols / 8, nks = cols / 32;
+  for (long q = blockIdx.x * 256L + threadIdx.x; q < n; q += (long)gridDim.x * 256) {
+    const long lp = q & 63, t = q >> 6, rg = t / nks, st = t - rg * nks;
+    const long row = rg * 16 + (lp & 15), col = st * 32 + (lp >> 4) * 8;
+    dst[q] = src[(row * cols + col) >> 3];
+  }
+}
+
+hipError_t launch_pack(const void* src, void* dst, long rows, long cols, hipStream_t s) {
+  const long n = rows * cols / 8;
+  const long need = (n + 255) / 256, blocks = need < 65536 ? need : 65536;
+  hipLaunchKernelGGL(pmk_pack, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const uint4*>(src),
+                     reinterpret_cast<uint4*>(dst), rows, cols);
+  return hipGetLastError();
 }
 
 hipError_t launch_prologue(const StepArgs& a, hipStream_t s) {
@@ -2291,7 +2336,8 @@ hipError_t launch_main(const StepArgs& a, int dtype, hipStream_t s, RunSpec rs) 
   const StepArgs* pa = reinterpret_cast<const StepArgs*>(a.ws.args);
   void* args[] = {&pa, &rs};
   const bool part = rs.l0 != 0 || rs.l1 != a.dm.L || rs.types != kAllTypes || rs.barrier;
-  return hipLaunchCooperativeKernel(main_fn(dtype, part, a.dm.moe != 0), dim3(a.dm.grid), dim3(kBlock), args,
+  return hipLaunchCooperativeKernel(main_fn(dtype, part, a.dm.moe != 0, a.dm.wtiles != 0), dim3(a.dm.grid),
+                                    dim3(kBlock), args,
                                     kLdsBytes, s);
 }
 

@@ -22,6 +22,28 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+# weight matrices of a layer (the RMSNorm gains stay as they are)
+MATRIX_FIELDS = ("w_qkv", "w_o", "w_gate", "w_up", "w_down", "w_router", "w_exp_gate", "w_exp_up", "w_exp_down")
+
+
+def pack_weights(t: torch.Tensor) -> torch.Tensor:
+    """pmk_pack_weights: a new tensor holding the bfloat16 weight tensor t
+    ([..., rows, cols], the leading dimensions stacked) in the tile layout."""
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError("pack_weights takes a contiguous bfloat16 device tensor")
+    cols = t.shape[-1]
+    out = torch.empty_like(t)
+    _abi.check(_abi.load().pmk_pack_weights(_ptr(t), _ptr(out), t.numel() // cols, cols, _stream()),
+               "pmk_pack_weights")
+    return out
+
+
+def pack_layers(layers: list) -> list:
+    """Each layer dict with its weight matrices replaced by tile-layout copies."""
+    return [{k: (pack_weights(v) if k in MATRIX_FIELDS and v is not None else v) for k, v in L.items()}
+            for L in layers]
+
+
 class DecodeModel:
     """Wraps decode_layer_init / decode_step / moe_layer_step / decode_layer_destroy.
 
@@ -32,7 +54,7 @@ class DecodeModel:
     def __init__(self, *, dtype: str, n_layers: int, hidden: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
                  ffn_dim: int = 0, n_experts: int = 0, top_k: int = 0, expert_ffn_dim: int = 0,
                  max_batch: int, max_seq: int, rms_eps: float = 1e-5, rope_theta: float = 10000.0,
-                 layers: list, watchdog_ms: int = 0):
+                 layers: list, watchdog_ms: int = 0, weight_layout: str = "rows"):
         self.lib = _abi.load()
         d = _abi.ModelDesc()
         d.abi_version = _abi.PMK_ABI_VERSION
@@ -40,6 +62,9 @@ class DecodeModel:
         d.n_layers, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim = n_layers, hidden, n_q_heads, n_kv_heads, head_dim
         d.ffn_dim, d.n_experts, d.top_k, d.expert_ffn_dim = ffn_dim, n_experts, top_k, expert_ffn_dim
         d.max_batch, d.max_seq, d.rms_eps, d.rope_theta, d.watchdog_ms = max_batch, max_seq, rms_eps, rope_theta, watchdog_ms
+        if weight_layout not in ("rows", "tiles"):
+            raise ValueError(f"weight_layout must be 'rows' or 'tiles', not {weight_layout!r}")
+        d.weight_layout = _abi.PMK_TILES if weight_layout == "tiles" else _abi.PMK_ROWS
         self.desc = d
         self._layers = layers
         arr = (_abi.LayerWeights * n_layers)()
@@ -54,12 +79,17 @@ class DecodeModel:
         self.handle = h
 
     @classmethod
-    def from_workload(cls, w, layers, max_batch, max_seq, n_layers=None, watchdog_ms=0):
+    def from_workload(cls, w, layers, max_batch, max_seq, n_layers=None, watchdog_ms=0, weight_layout="rows"):
+        """weight_layout "tiles": `layers` are row-major and are packed into
+        tile-layout copies held by the model (twice the weight memory while the
+        caller keeps its tensors)."""
+        if weight_layout == "tiles":
+            layers = pack_layers(layers)
         return cls(dtype=w.dtype, n_layers=w.n_layers if n_layers is None else n_layers, hidden=w.hidden,
                    n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn_dim=w.ffn_dim,
                    n_experts=w.n_experts, top_k=w.top_k, expert_ffn_dim=w.expert_ffn_dim, max_batch=max_batch,
                    max_seq=max_seq, rms_eps=w.rms_eps, rope_theta=w.rope_theta, layers=layers,
-                   watchdog_ms=watchdog_ms)
+                   watchdog_ms=watchdog_ms, weight_layout=weight_layout)
 
     # -- entry points -------------------------------------------------------
     def decode_step(self, hidden: torch.Tensor, kv_cache: torch.Tensor, seq_lens: torch.Tensor) -> int:

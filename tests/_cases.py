@@ -75,7 +75,7 @@ def run_oracle_dense(orc, case: Case, inp) -> tuple[np.ndarray, np.ndarray]:
     return out, kv
 
 
-def make_model(case: Case, watchdog_ms: int = 0):
+def make_model(case: Case, watchdog_ms: int = 0, weight_layout: str = "rows"):
     from persistent_megakernel_04_amd import DecodeModel
     return DecodeModel.from_workload(case.w, case.layers, case.max_batch, case.max_seq, n_layers=case.n_layers,
-                                     watchdog_ms=watchdog_ms)
+                                     watchdog_ms=watchdog_ms, weight_layout=weight_layout)
