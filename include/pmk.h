@@ -238,11 +238,11 @@ int pmk_set_watchdog_us(pmk_handle* h, int32_t us);
  * in the tile layout that a handle with weight_layout = PMK_TILES reads. The
  * decode step reads each weight matrix once as a stream of 16-row groups
  * (the weight-streaming tile tasks of the persistent megakernel, Event Tensor
- * summary page, Core method); in the tile layout the 16 rows of a group are
- * interleaved per 32-column step, so that every wave-wide 16-byte-per-lane
- * load reads one contiguous 1 KiB block: the 16-byte piece holding row r,
- * columns 32 s + 8 g .. 32 s + 8 g + 7 (g < 4) is piece
- *   ((r / 16) * (cols / 32) + s) * 64 + (r % 16) + 16 g
+ * summary page, Core method). The tile layout cuts the matrix into 16-row x
+ * 32-column tiles and stores them one after another, row group major, each
+ * tile row-major (1 KiB), so that every wave-wide 16-byte-per-lane load of a
+ * row group's k-step reads one contiguous 1 KiB block: element (r, c) is at
+ *   ((r / 16) * (cols / 32) + c / 32) * 512 + (r % 16) * 32 + c % 32
  * of dst. A stack of matrices with the same cols (the experts of a layer,
  * [E][rows][cols]) packs as one matrix of E rows rows. dst has the same size
  * as src (rows * cols * 2 bytes) and is caller-owned; the copy is ordered on

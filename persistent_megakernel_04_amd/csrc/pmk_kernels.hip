@@ -146,15 +146,15 @@ struct GemvRows {
 };
 
 // Where row `row` of a weight matrix with `ld` columns starts at column k0:
-// row-major, or (PK) in the tile layout, where the 16 rows of a row group are
-// interleaved per 32-column step so that one wave-wide load reads a contiguous
-// 1 KiB block: the 16-byte piece of (row r, columns 32 s + 8 g .. + 7) is
-// piece ((r / 16) (ld / 32) + s) 64 + r % 16 + 16 g. For PK the returned
-// pointer is that of the piece g = 0; a step advances it by 512 elements.
+// row-major, or (PK) in the tile layout: the matrix cut into 16-row x
+// 32-column tiles, stored one after another (row group major), each tile
+// row-major, so that one wave-wide load of a k-step reads a contiguous 1 KiB
+// tile. For PK the returned pointer is that of the row's first 8 elements in
+// the tile of column k0; a step advances it by one tile (512 elements).
 template <typename WT, bool PK>
 __device__ __forceinline__ const WT* wrow(const void* base, size_t row, int ld, int k0) {
   const WT* b = reinterpret_cast<const WT*>(base);
-  if (PK) return b + (row >> 4) * 16 * (size_t)ld + (row & 15) * 8 + (size_t)(k0 >> 5) * 512;
+  if (PK) return b + (row >> 4) * 16 * (size_t)ld + (row & 15) * 32 + (size_t)(k0 >> 5) * 512;
   return b + row * ld + k0;
 }
 
@@ -399,7 +399,7 @@ __device__ __forceinline__ bool gemv(const Ctx& c, const GemvRows& rw, int R, in
     return row_ptr<WT, PK>(rw, min(rg * 16 + mrow, R - 1));   // padded rows repeat a valid row
   };
   auto kofs = [&](int ks) {
-    if constexpr (PK) return min(wi.ks_lo + ks, NKS - 1) * 512 + grp * 128;
+    if constexpr (PK) return min(wi.ks_lo + ks, NKS - 1) * 512 + kg;
     else return min((wi.ks_lo + ks) * T::KSTEP + kg, kmax);
   };
   auto ldw = [&](const WT* p) {
@@ -2306,15 +2306,16 @@ hipError_t prepare_main(int dtype, int wtiles) {
 }
 
 // Writes a bfloat16 [rows][cols] matrix (rows % 16 == 0, cols % 32 == 0) in
-// the tile layout: 16-byte piece q = (rg (cols / 32) + s) 64 + r + 16 g holds
-// row 16 rg + r, columns 32 s + 8 g .. + 7. One thread per piece; the writes
-// are contiguous, the reads 64-byte runs.
+// the tile layout: 16 x 32 tiles in row-group-major order, each row-major, so
+// 16-byte piece q = (rg (cols / 32) + s) 64 + 4 r + g holds row 16 rg + r,
+// columns 32 s + 8 g .. + 7. One thread per piece; the writes are contiguous,
+// the reads 64-byte runs.
 __global__ void __launch_bounds__(256) pmk_pack(const uint4* __restrict__ src, uint4* __restrict__ dst, long rows,
                                                 long cols) {
   const long n = rows * cols / 8, nks = cols / 32;
   for (long q = blockIdx.x * 256L + threadIdx.x; q < n; q += (long)gridDim.x * 256) {
     const long lp = q & 63, t = q >> 6, rg = t / nks, st = t - rg * nks;
-    const long row = rg * 16 + (lp & 15), col = st * 32 + (lp >> 4) * 8;
+    const long row = rg * 16 + (lp >> 2), col = st * 32 + (lp & 3) * 8;
     dst[q] = src[(row * cols + col) >> 3];
   }
 }

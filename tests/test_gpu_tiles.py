@@ -21,16 +21,13 @@ def announce(msg):
 
 
 def tile_layout_reference(m: np.ndarray) -> np.ndarray:
-    """The layout written out from its definition: 16-byte piece
-    ((r // 16) * (cols // 32) + s) * 64 + r % 16 + 16 g holds row r, columns
-    32 s + 8 g .. 32 s + 8 g + 7."""
+    """The layout written out from its definition: element (r, c) at
+    ((r // 16) * (cols // 32) + c // 32) * 512 + (r % 16) * 32 + c % 32."""
     rows, cols = m.shape
     out = np.empty(rows * cols, m.dtype)
     for r in range(rows):
-        for s in range(cols // 32):
-            for g in range(4):
-                q = ((r // 16) * (cols // 32) + s) * 64 + r % 16 + 16 * g
-                out[q * 8:(q + 1) * 8] = m[r, 32 * s + 8 * g:32 * s + 8 * g + 8]
+        for c in range(cols):
+            out[((r // 16) * (cols // 32) + c // 32) * 512 + (r % 16) * 32 + c % 32] = m[r, c]
     return out
 
 
@@ -55,13 +52,14 @@ def test_pack_large_stacked_matrix_sampled():
     src = torch.randint(-32768, 32767, (E, rows, cols), generator=gen, dtype=torch.int16, device="cuda")
     got = pack_weights(src.view(torch.bfloat16)).view(torch.int16)
     torch.cuda.synchronize()
-    src_np, got_np = to_np(src).reshape(E * rows, cols), to_np(got).reshape(-1, 8)
+    src_np, got_np = to_np(src).reshape(E * rows, cols), to_np(got).reshape(-1, 8)   # 16-byte pieces
     rng = np.random.default_rng(12)
     n = 8192
     r, s, g = rng.integers(0, E * rows, n), rng.integers(0, cols // 32, n), rng.integers(0, 4, n)
-    q = ((r // 16) * (cols // 32) + s) * 64 + r % 16 + 16 * g
-    want = src_np[r[:, None], (32 * s + 8 * g)[:, None] + np.arange(8)]
-    np.testing.assert_array_equal(got_np[q], want)
+    c = 32 * s + 8 * g
+    at = ((r // 16) * (cols // 32) + c // 32) * 512 + (r % 16) * 32 + c % 32   # element index of (r, c)
+    want = src_np[r[:, None], c[:, None] + np.arange(8)]
+    np.testing.assert_array_equal(got_np[at // 8], want)
 
 
 def run_dense(case, layout, sched=None):
