@@ -131,6 +131,17 @@ def cpu_baseline(case, budget_s: float = 12.0) -> dict:
                        f"compute, extrapolated to the full stack; host copies excluded")}
 
 
+class RowMajorLayers:
+    """Layer l's row-major tensors, regenerated on demand from the same seeds."""
+
+    def __init__(self, w, device):
+        self.w, self.device = w, device
+
+    def __getitem__(self, l):
+        import synth
+        return synth.make_layer_weights(self.w, l, device=self.device)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,9 +168,9 @@ def main():
                     help="cached lengths uniform on [LO, HI] instead of the workload's own (e.g. batches beyond 128, "
                     "whose cache at the sweep's lengths would not fit in HBM)")
     ap.add_argument("--weight-layout", default="auto", choices=["auto", "rows", "tiles"],
-                    help="bfloat16 weights row-major, or packed once before timing into the 16-row tile layout "
-                    "(one contiguous 1 KiB block per wave-wide load, streamed non-temporally); auto: tiles when "
-                    "the packed copies fit beside the row-major weights and the KV cache")
+                    help="weights row-major, or (bfloat16) packed layer by layer, before timing, into the tile "
+                    "layout: 16 x 32 tiles, each a contiguous 1 KiB block that one wave-wide load reads, streamed "
+                    "non-temporally; auto: tiles for bfloat16 workloads")
     ap.add_argument("--trace", default=None, help="after the timed steps, run one traced step and write a "
                     "per-stage summary of the task trace to this file")
     args = ap.parse_args()
@@ -179,6 +190,7 @@ def main():
     from _cases import Case
 
     from persistent_megakernel_04_amd import DecodeModel
+    from persistent_megakernel_04_amd.model import pack_layers
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU (the HIP library has no CPU path)")
@@ -210,7 +222,15 @@ def main():
         f"F={w.ffn_dim} E={w.n_experts} dtype={w.dtype} B={B} max_seq={max_seq} steps={K} warmup={W}")
 
     t0 = time.perf_counter()
-    layers = [synth.make_layer_weights(w, l, device=dev) for l in range(L)]
+    layout = args.weight_layout
+    if layout == "auto":
+        layout = "tiles" if w.dtype == "bf16" else "rows"
+    if layout == "tiles":
+        # each layer packed as it is generated; the row-major copy is dropped
+        # (the 70B-shaped stack would not fit twice)
+        layers = [pack_layers([synth.make_layer_weights(w, l, device=dev)])[0] for l in range(L)]
+    else:
+        layers = [synth.make_layer_weights(w, l, device=dev) for l in range(L)]
     kv = synth.make_kv_cache(w, B, max_seq, device=dev, n_layers=L)
     hid = torch.stack([synth.make_hidden(w, B, i, device=dev) for i in range(max(K, W, 1))])   # [steps][B][H]
     steps_lens = torch.tensor(np.stack([lens0 + i for i in range(max(K, W, 1))]), dtype=torch.int32, device=dev)
@@ -221,14 +241,11 @@ def main():
     cpu_case = None
     if not args.no_cpu_baseline:
         # the oracle's sample sees step 0's inputs, taken before any GPU step
-        cpu_case = Case(w, L, layers, kv, hid[0].clone(), steps_lens[0].clone(), B, max_seq)
+        # the oracle takes row-major layers: regenerated one at a time (same seeds) when packed
+        cpu_layers = layers if layout == "rows" else RowMajorLayers(w, dev)
+        cpu_case = Case(w, L, cpu_layers, kv, hid[0].clone(), steps_lens[0].clone(), B, max_seq)
 
-    layout = args.weight_layout
-    if layout == "auto":
-        weight_bytes = sum(t.numel() * t.element_size() for Ld in layers for t in Ld.values() if t is not None)
-        free = torch.cuda.mem_get_info()[0]
-        layout = "tiles" if w.dtype == "bf16" and weight_bytes + (8 << 30) < free else "rows"
-    model = DecodeModel.from_workload(w, layers, B, max_seq, weight_layout=layout)
+    model = DecodeModel.from_workload(w, layers, B, max_seq, weight_layout=layout, pack=False)
     log(f"weight layout: {layout}")
     model.set_schedule(args.schedule)
     if w.n_experts:

@@ -79,11 +79,13 @@ class DecodeModel:
         self.handle = h
 
     @classmethod
-    def from_workload(cls, w, layers, max_batch, max_seq, n_layers=None, watchdog_ms=0, weight_layout="rows"):
-        """weight_layout "tiles": `layers` are row-major and are packed into
-        tile-layout copies held by the model (twice the weight memory while the
-        caller keeps its tensors)."""
-        if weight_layout == "tiles":
+    def from_workload(cls, w, layers, max_batch, max_seq, n_layers=None, watchdog_ms=0, weight_layout="rows",
+                      pack=True):
+        """weight_layout "tiles": with pack, `layers` are row-major and are
+        packed into tile-layout copies held by the model (twice the weight
+        memory while the caller keeps its tensors); without, they already are
+        in the tile layout (pack_layers)."""
+        if weight_layout == "tiles" and pack:
             layers = pack_layers(layers)
         return cls(dtype=w.dtype, n_layers=w.n_layers if n_layers is None else n_layers, hidden=w.hidden,
                    n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ffn_dim=w.ffn_dim,
