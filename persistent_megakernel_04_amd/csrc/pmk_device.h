@@ -149,6 +149,9 @@ __device__ __forceinline__ uint4 ldg16_nt(const void* p) {
 
 typedef const __attribute__((address_space(1))) uint32_t* gptr_u32;
 __device__ __forceinline__ uint32_t ldg4(const void* p) { return *(gptr_u32)(p); }
+// The same as a streaming (non-temporal) load: for cached KV rows read once per
+// step, whose wave-wide loads cover whole 128-byte lines.
+__device__ __forceinline__ uint32_t ldg4_nt(const void* p) { return __builtin_nontemporal_load((gptr_u32)(p)); }
 
 // Wait until every vector memory operation of this wave has completed
 // (stores acknowledged by the coherence point).

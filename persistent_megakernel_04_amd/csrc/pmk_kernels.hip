@@ -1217,7 +1217,7 @@ __device__ __forceinline__ bool task_attn_mm(const Ctx& c, int b, int g, int ci,
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) kr[t][s4] = ldg16(kp + s4 * 32);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) vr[t][i] = ldg4(Vb + (size_t)min(tb + i, pmax) * D + 2 * lane);
+    for (int i = 0; i < 16; ++i) vr[t][i] = ldg4_nt(Vb + (size_t)min(tb + i, pmax) * D + 2 * lane);
   }
   if (!ctx_wait(c, wev)) return false;
 
@@ -1386,7 +1386,7 @@ __device__ __forceinline__ bool task_attn_stream(const Ctx& c, int b, int g, int
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) t.k[s4] = ldg16(kp + s4 * 32);
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii) t.v[ii] = ldg4(Vb + (size_t)min(tb + ii, pmax) * D + 2 * lane);
+    for (int ii = 0; ii < 16; ++ii) t.v[ii] = ldg4_nt(Vb + (size_t)min(tb + ii, pmax) * D + 2 * lane);
   };
   AttnTile t0, t1;
   if (ntw > 0) load(t0, 0);
