@@ -23,6 +23,12 @@ def test_bad_step_counts_are_refused():
     assert run_bench("--warmup", "-1").returncode != 0
 
 
+def test_unknown_weight_layout_is_refused():
+    r = run_bench("--weight-layout", "columns")
+    assert r.returncode != 0
+    assert "weight-layout" in r.stderr
+
+
 def test_step_bytes_counts_weights_once_and_each_kv_entry_once():
     """The 8B-shaped stack at batch 1 with 512 cached positions: 218.1 M
     parameters per layer in bfloat16 plus two float32 norm gains, 32 layers;
