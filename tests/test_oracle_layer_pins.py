@@ -135,6 +135,71 @@ def test_query_rotated_at_seq_len(orc):
     assert s[0] != pytest.approx(s[1])
 
 
+def test_appended_value_not_rotated_at_seq_len(orc):
+    """d = 2, S = 5: RoPE turns q and k only. The value written at slot S is
+    the plain projection W_v u, and attention reads that entry: with W_q = 0
+    every score is 0, so o is the mean of the S + 1 values, and W_o selecting
+    o gives h1 = x + [o, 0, 0]. A value rotated by the angle S (in the cache or
+    only inside attention) fails both checks."""
+    rng = np.random.default_rng(27)
+    w = tiny(hidden=4, n_q_heads=1, n_kv_heads=1, head_dim=2, ffn_dim=4)
+    L = rnd_layer(rng, w)
+    L["w_qkv"][0:2] = 0                              # q = 0: uniform attention weights
+    L["w_o"] = np.eye(4, 2, dtype=np.float32)        # h1 = x + [o, 0, 0]
+    L["w_down"][:] = 0
+    S = 5
+    kv = rnd_kv(rng, w, 1, 8)
+    cached_v = kv[1, 0, 0, :S].astype(np.float64).copy()
+    x = rng.standard_normal((1, 4))
+    out = orc.decode_layer(orc.make_desc(w, 1, 8), L, kv, [S], x)
+    u = rms(x[0], L["attn_norm"], 1e-5)
+    v = L["w_qkv"][4:6].astype(np.float64) @ u
+    v_rot = np.array([v[0] * math.cos(S) - v[1] * math.sin(S), v[1] * math.cos(S) + v[0] * math.sin(S)])
+    assert np.abs(v_rot - v).max() > 1e-2            # the mistake would be visible
+    np.testing.assert_allclose(kv[1, 0, 0, S], v.astype(np.float32), rtol=1e-6)
+    expect = (cached_v.sum(axis=0) + v.astype(np.float32).astype(np.float64)) / (S + 1)
+    np.testing.assert_allclose(out[0, :2] - x[0, :2], expect, rtol=1e-10, atol=1e-12)
+    np.testing.assert_array_equal(out[0, 2:], x[0, 2:])
+
+
+def _bf16_bits(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _bf16_val(b):
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("S", [0, 3])
+def test_attention_reads_appended_entry_rounded_to_cache_dtype(orc, S):
+    """bfloat16 cache: the new K/V entry is stored rounded to bfloat16, and
+    attention reads the stored (rounded) entry, not the unrounded projection.
+    W_q = 0 makes every score 0, so o = mean of the S + 1 stored values; with
+    S = 0 it is the rounded new value alone. W_o selects o and W_down = 0, so
+    x' - x = [o, 0, 0]. The expected o is built from the entry rounded by hand
+    (round_bf16, pinned separately); attending over the unrounded v misses it
+    by far more than the tolerance."""
+    rng = np.random.default_rng(28 + S)
+    w = tiny(dtype="bf16", hidden=4, n_q_heads=1, n_kv_heads=1, head_dim=2, ffn_dim=4)
+    L = rnd_layer(rng, w)
+    L["w_qkv"][0:2] = 0
+    L["w_o"] = np.eye(4, 2, dtype=np.float32)
+    L["w_down"][:] = 0
+    Lb = {n: (a if n.endswith("norm") else _bf16_bits(a)) for n, a in L.items()}
+    kvb = _bf16_bits(rnd_kv(rng, w, 1, 8))
+    cached_v = _bf16_val(kvb[1, 0, 0, :S]).copy()
+    x = rng.standard_normal((1, 4))
+    out = orc.decode_layer(orc.make_desc(w, 1, 8), Lb, kvb, [S], x)
+    u = rms(x[0], L["attn_norm"], 1e-5)
+    v = _bf16_val(Lb["w_qkv"][4:6]) @ u
+    v_rnd = np.array([orc.round_bf16(t) for t in v])
+    assert np.abs(v_rnd - v).max() > 1e-5            # rounding moves v by far more than the tolerance below
+    np.testing.assert_array_equal(_bf16_val(kvb[1, 0, 0, S]), v_rnd)
+    expect = (cached_v.sum(axis=0) + v_rnd) / (S + 1)
+    np.testing.assert_allclose(out[0, :2] - x[0, :2], expect, rtol=1e-12, atol=1e-14)
+
+
 def test_batch_requests_are_independent(orc):
     rng = np.random.default_rng(24)
     w = tiny()
