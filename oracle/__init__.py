@@ -75,6 +75,7 @@ def lib():
         L.orc_decode_layer.argtypes = [P, P, P, P, I, P]
         L.orc_decode_stack.argtypes = [P, P, P, P, I, P]
         L.orc_moe_layer.argtypes = [P, P, P, P, I, I, P, P, P, P, P, P, P, P]
+        L.orc_moe_layer_routed.argtypes = [P, P, P, P, I, P, P, P]
         _lib = L
     return _lib
 
@@ -231,3 +232,21 @@ def moe_layer(desc: Desc, layer: dict, kv_layer, seq_lens, hidden, bm):
     if rc:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return h, r
+
+
+def moe_layer_routed(desc: Desc, layer: dict, kv_layer, seq_lens, hidden, topk_idx):
+    """One MoE layer with each token's experts given (``topk_idx`` [T][k]):
+    gates are the softmax over the layer's own float32 logits at those experts.
+    Returns (hidden', gates [T][k])."""
+    s, keep = _layer_struct(layer)
+    h = np.array(hidden, dtype=np.float64, copy=True)
+    T = h.shape[0]
+    idx = _c(topk_idx, np.int32)
+    assert idx.shape == (T, desc.top_k)
+    sl = _c(seq_lens, np.int32)
+    w = np.empty((T, desc.top_k), np.float64)
+    rc = lib().orc_moe_layer_routed(ctypes.byref(desc), ctypes.byref(s), _ptr(kv_layer), _ptr(sl), T, _ptr(idx),
+                                    _ptr(h), _ptr(w))
+    if rc:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return h, w

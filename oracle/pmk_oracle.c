@@ -317,16 +317,28 @@ int orc_decode_stack(const orc_desc* D, const orc_layer* layers, void* kv, const
   return 0;
 }
 
+/* Gates for a given selection: the softmax over the selected logits, taken
+ * in selection order (the renormalised full softmax restricted to idx). */
+static void sel_gates(const float* z, const int32_t* idx, int k, double* w) {
+  double zmax = (double)z[idx[0]], sum = 0.0;
+  for (int j = 0; j < k; ++j) { w[j] = exp((double)z[idx[j]] - zmax); sum += w[j]; }
+  for (int j = 0; j < k; ++j) w[j] /= sum;
+}
+
 /* One MoE decoder layer over T tokens, each token its own request:
  *   h1 = attention half; u2 = RMSNorm(h1; ffn_norm);
  *   z = W_router u2 (rounded to float32: the decision precision);
  *   (idx, w) = top-k of z with renormalised softmax gates;
  *   x' = h1 + sum_j w_j * SwiGLU_{idx_j}(u2)      (summed in slot order j = 0..k-1);
  * and the grouping of all tokens' choices (orc_group). Each routing output is
- * optional (NULL skips it). */
-int orc_moe_layer(const orc_desc* D, const orc_layer* W, void* kv, const int32_t* seq_lens, int T, int bm,
-                  double* hidden, float* logits, int32_t* topk_idx, double* topk_w, int32_t* exp_indptr,
-                  int32_t* tile_indptr, int32_t* sorted_tok, int32_t* sorted_slot) {
+ * optional (NULL skips it). With force_idx (T x k), the selection is taken
+ * from there instead of from top-k (gates: the softmax over this layer's own
+ * logits at the given experts), for comparing a token that another
+ * implementation routed differently at a near tie. */
+static int moe_layer_impl(const orc_desc* D, const orc_layer* W, void* kv, const int32_t* seq_lens, int T, int bm,
+                          double* hidden, float* logits, int32_t* topk_idx, double* topk_w, int32_t* exp_indptr,
+                          int32_t* tile_indptr, int32_t* sorted_tok, int32_t* sorted_slot,
+                          const int32_t* force_idx) {
   if (check_desc(D) || T < 0 || T > D->max_batch || D->n_experts <= 0 || D->top_k <= 0 ||
       D->top_k > D->n_experts || D->expert_ffn_dim <= 0 || bm <= 0)
     return -1;
@@ -348,7 +360,15 @@ int orc_moe_layer(const orc_desc* D, const orc_layer* W, void* kv, const int32_t
     orc_matvec(W->w_router, dt, E, H, u2, zd);
     for (int e = 0; e < E; ++e) z[e] = (float)zd[e];
     int32_t* idx = all_idx + (size_t)t * k;
-    orc_topk(z, E, k, idx, w);
+    if (force_idx) {
+      for (int j = 0; j < k; ++j) {
+        idx[j] = force_idx[(size_t)t * k + j];
+        if (idx[j] < 0 || idx[j] >= E) { free(h1); free(u2); free(f); free(zd); free(z); free(all_idx); free(w); return -3; }
+      }
+      sel_gates(z, idx, k, w);
+    } else {
+      orc_topk(z, E, k, idx, w);
+    }
     for (int i = 0; i < H; ++i) x[i] = h1[i];
     for (int j = 0; j < k; ++j) {
       int e = idx[j];
@@ -366,4 +386,18 @@ int orc_moe_layer(const orc_desc* D, const orc_layer* W, void* kv, const int32_t
     orc_group(all_idx, T, k, E, bm, exp_indptr, tile_indptr, sorted_tok, sorted_slot);
   free(h1); free(u2); free(f); free(zd); free(z); free(all_idx); free(w);
   return 0;
+}
+
+int orc_moe_layer(const orc_desc* D, const orc_layer* W, void* kv, const int32_t* seq_lens, int T, int bm,
+                  double* hidden, float* logits, int32_t* topk_idx, double* topk_w, int32_t* exp_indptr,
+                  int32_t* tile_indptr, int32_t* sorted_tok, int32_t* sorted_slot) {
+  return moe_layer_impl(D, W, kv, seq_lens, T, bm, hidden, logits, topk_idx, topk_w, exp_indptr, tile_indptr,
+                        sorted_tok, sorted_slot, NULL);
+}
+
+/* The same layer with the experts of every token given (force_idx, T x k). */
+int orc_moe_layer_routed(const orc_desc* D, const orc_layer* W, void* kv, const int32_t* seq_lens, int T,
+                         const int32_t* force_idx, double* hidden, double* topk_w) {
+  if (!force_idx) return -1;
+  return moe_layer_impl(D, W, kv, seq_lens, T, 1, hidden, NULL, NULL, topk_w, NULL, NULL, NULL, NULL, force_idx);
 }

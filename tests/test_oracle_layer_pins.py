@@ -357,3 +357,48 @@ def test_bf16_storage_consistent_with_f32_storage(orc):
     # the appended entries are the float32 ones rounded to bfloat16
     for b, s in ((0, 5), (1, 11)):
         np.testing.assert_array_equal(kvb[:, b, :, s], tobf(kvf[:, b, :, s]))
+
+
+def test_moe_routed_with_own_topk_equals_moe_layer(orc):
+    """The layer with each token's experts given: handed the layer's own
+    top-k, it reproduces the routed layer exactly (outputs and gates)."""
+    rng = np.random.default_rng(35)
+    w = moe_cfg(8, 3)
+    L = rnd_layer(rng, w, moe=True)
+    T = 4
+    kv = rnd_kv(rng, w, T, 7)
+    x = rng.standard_normal((T, 8))
+    sl = [0, 2, 6, 3]
+    out, r = orc.moe_layer(orc.make_desc(w, T, 7), L, kv.copy(), sl, x, bm=2)
+    out2, g2 = orc.moe_layer_routed(orc.make_desc(w, T, 7), L, kv.copy(), sl, x, r["topk_idx"])
+    np.testing.assert_array_equal(out2, out)
+    np.testing.assert_array_equal(g2, r["topk_w"])
+
+
+def test_moe_routed_other_selection_is_gate_weighted_mixture(orc):
+    """Any given selection: the output is h1 plus the dense SwiGLU of each
+    given expert weighted by the softmax of the layer's logits over the
+    selection (brute force through the dense layer); a selection in another
+    order gives the same gates, permuted, and the same output up to the
+    order of the sum."""
+    rng = np.random.default_rng(36)
+    E, k = 8, 3
+    w = moe_cfg(E, k)
+    L = rnd_layer(rng, w, moe=True)
+    T = 3
+    kv = rnd_kv(rng, w, T, 6)
+    x = rng.standard_normal((T, 8))
+    sl = [1, 4, 0]
+    _, r = orc.moe_layer(orc.make_desc(w, T, 6), L, kv.copy(), sl, x, bm=1)
+    sel = np.array([[7, 0, 3], [2, 5, 1], [6, 4, 0]], np.int32)
+    out, g = orc.moe_layer_routed(orc.make_desc(w, T, 6), L, kv.copy(), sl, x, sel)
+    dw = tiny(ffn_dim=6)
+    dense = [orc.decode_layer(orc.make_desc(dw, T, 6), dense_from_expert(L, e), kv.copy(), sl, x) for e in range(E)]
+    for t in range(T):
+        zs = r["router_logits"][t, sel[t]].astype(np.float64)
+        np.testing.assert_allclose(g[t], sps.softmax(zs), rtol=1e-13)
+        ref = sum(g[t, j] * dense[sel[t, j]][t] for j in range(k))
+        np.testing.assert_allclose(out[t], ref, rtol=1e-11, atol=1e-12)
+    out_p, g_p = orc.moe_layer_routed(orc.make_desc(w, T, 6), L, kv.copy(), sl, x, sel[:, ::-1].copy())
+    np.testing.assert_allclose(g_p, g[:, ::-1], rtol=1e-13)
+    np.testing.assert_allclose(out_p, out, rtol=1e-12, atol=1e-13)
