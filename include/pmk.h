@@ -26,8 +26,13 @@
  *    time: calls on one handle must not overlap.
  *  - Return value: 0 (PMK_OK) or a PMK_ERR_* code; no exception crosses the ABI.
  *    Errors the device detects (a request length out of range, an event wait
- *    that exceeded the watchdog) are recorded in a device error word, returned
- *    by pmk_get_device_error() and by the next call on the handle.
+ *    that exceeded the watchdog) are recorded in a device error word. The
+ *    device also copies it into a pinned host mirror, so once the step that
+ *    hit the error has finished on the device, every later decode_step /
+ *    moe_layer_step on the handle returns that code without launching, until
+ *    pmk_get_device_error() has read and cleared it. A call made while that
+ *    step is still running cannot know yet: it returns PMK_OK, and the device
+ *    skips its step (the error word stays set).
  */
 #ifndef PMK_H
 #define PMK_H
@@ -126,12 +131,19 @@ typedef struct pmk_info {
 
 typedef struct pmk_handle pmk_handle;
 
-/* Create a handle: validates desc and every weight pointer, keeps the weight
- * pointers (no copy), builds the RoPE cos/sin table on the host in double and
- * uploads it as float32, allocates the workspace (activations, attention
- * partials, event counters, task queues, MoE routing arrays, error word) for
+/* Create a handle (Event Tensor summary, Core method, ETC compiler and
+ * scheduling: the megakernel is compiled ahead of time and its runtime needs
+ * only the counter tensors and the scheduler queue; the two kinds of dynamism
+ * are handled at run time from symbolic batch/length dimensions). Validates
+ * desc and every weight pointer, keeps the weight pointers (no copy), builds
+ * the RoPE cos/sin table on the host in double and uploads it as float32,
+ * allocates the workspace (activations, attention partials, event counters,
+ * task queues, MoE routing arrays, error word and its pinned host mirror) for
  * max_batch and max_seq, and sizes the persistent grid to the device's compute
- * units. Errors: PMK_ERR_ARG, PMK_ERR_UNSUPPORTED, PMK_ERR_OOM, PMK_ERR_DEVICE. */
+ * units (one workgroup per compute unit, as the per-SM queues of static
+ * scheduling assume). The handle is owned by the caller until
+ * decode_layer_destroy. Errors: PMK_ERR_ARG (null pointer, inconsistent
+ * dims), PMK_ERR_UNSUPPORTED, PMK_ERR_OOM, PMK_ERR_DEVICE. */
 int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* weights, pmk_handle** out);
 
 /* One decode step of the whole stack for `batch` requests (Event Tensor
@@ -150,7 +162,8 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* weights, pm
  * Two launches (a queue/event prologue and the persistent kernel). Dense
  * handles only; a MoE handle runs the same step with routed experts.
  * Errors: PMK_ERR_ARG (batch outside [1, max_batch], null pointer), a pending
- * device error from an earlier call, PMK_ERR_DEVICE. */
+ * device error from an earlier step that has reached the host mirror
+ * (PMK_ERR_SEQ, PMK_ERR_TIMEOUT; nothing is launched), PMK_ERR_DEVICE. */
 int decode_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq_lens, int32_t batch, void* stream);
 
 /* One step of a stack of MoE decoder layers for `tokens` tokens, each its own
@@ -164,17 +177,34 @@ int decode_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq
 int moe_layer_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq_lens, int32_t tokens,
                    const pmk_routing* routing, void* stream);
 
-/* Synchronise the device, free the workspace and the handle. NULL is a no-op. */
+/* Synchronise the device, free the workspace (counter tensors, queues,
+ * activations), the host error mirror and the handle (the runtime state that
+ * decode_layer_init created; Event Tensor summary, Core method, ETC compiler
+ * and scheduling). The caller's weights, caches and hidden states are not
+ * touched. NULL is a no-op. Returns PMK_ERR_DEVICE if the synchronisation
+ * failed (everything is freed anyway). */
 int decode_layer_destroy(pmk_handle* h);
 
 /* Static description of a status code. */
 const char* pmk_strerror(int status);
 
 /* Synchronise the handle's last stream and return the device error word
- * (PMK_OK, PMK_ERR_TIMEOUT or PMK_ERR_SEQ), then clear it. */
+ * (PMK_OK, PMK_ERR_TIMEOUT, PMK_ERR_SEQ, or PMK_ERR_ARG for a task queue
+ * that outgrew its capacity), then clear it and its host mirror, so later
+ * calls run again. The watchdog behind PMK_ERR_TIMEOUT answers the pages'
+ * open point on deadlocks inside a persistent megakernel (Event Tensor
+ * summary, Critical analysis, systemic gaps: observability and debugging):
+ * a wait that never ends becomes an error, and every workgroup leaves the
+ * step. Errors: PMK_ERR_ARG (null handle), PMK_ERR_DEVICE. */
 int pmk_get_device_error(pmk_handle* h);
 
-/* Launch configuration and sizes of a handle. */
+/* Launch configuration and sizes of a handle: the persistent grid (one
+ * workgroup per compute unit, each with its own static task queue; Event
+ * Tensor summary, Core method, ETC compiler and scheduling) and the row-tile
+ * size moe_bm of the grouped GEMM, which sets the granularity of tile_indptr
+ * (same page, Core method, two kinds of dynamism: the per-expert prefix sum
+ * over grouped-GEMM tiles decides which tiles an expert triggers).
+ * `out` is caller-owned. Errors: PMK_ERR_ARG (null pointer). */
 int pmk_query(const pmk_handle* h, pmk_info* out);
 
 /* Per-launch timing of the persistent kernel with HIP events recorded on the
@@ -273,6 +303,28 @@ int pmk_pack_weights(const void* src, void* dst, int64_t rows, int64_t cols, voi
  * entries_per_wg - 1 are dropped). Each call overwrites the buffer.
  * Errors: PMK_ERR_ARG (null handle, entries_per_wg < 2 with a buffer). */
 int pmk_trace_attach(pmk_handle* h, uint32_t* buf, int32_t entries_per_wg);
+
+/* Streaming-read probe: the HBM read bandwidth that a kernel doing nothing
+ * but reading reaches on this device, as the measured reference next to the
+ * nominal peak for the decode step's bandwidth roofline (the pages measure
+ * decode against the memory roofline: "Dataflow Is All You Need" summary
+ * page, Experiments and results, 45-78 % of roofline on SN40; Problem and
+ * motivation, ~21 % of HBM bandwidth used by GPU decode on H100). One
+ * workgroup per compute unit, 8 waves,
+ * 16 loads of 16 bytes per lane in flight (the decode GEMV engine's ring),
+ * each wave streaming 16 KiB blocks of `buf` round-robin:
+ *   pattern 0: contiguous 1 KiB per wave-wide load, non-temporal (the tile
+ *              weight layout);
+ *   pattern 1: 16 rows x 64 bytes per wave-wide load over rows of 8 KiB,
+ *              through the caches (row-major bfloat16 weights with 4096
+ *              columns).
+ * Runs `reps` launches on `stream`, each timed with HIP events, and writes the
+ * fastest in milliseconds to *ms_out (bandwidth = bytes / ms). `buf`: device,
+ * 256-byte aligned, `bytes` a positive multiple of 1 MiB, only read; `sink`:
+ * a device int that the probe may increment (it keeps the loads from being
+ * optimised away). Synchronises the stream. Errors: PMK_ERR_ARG, PMK_ERR_DEVICE. */
+int pmk_stream_probe(const void* buf, int64_t bytes, int32_t pattern, int32_t reps, int* sink, void* stream,
+                     double* ms_out);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,8 @@ MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC}
 
 EXPORTS = ("decode_layer_init", "decode_step", "moe_layer_step", "decode_layer_destroy", "pmk_strerror",
            "pmk_get_device_error", "pmk_query", "pmk_timing_enable", "pmk_timing_read", "pmk_trace_attach",
-           "pmk_set_schedule", "pmk_set_moe_scheduler", "pmk_set_watchdog_us", "pmk_pack_weights")
+           "pmk_set_schedule", "pmk_set_moe_scheduler", "pmk_set_watchdog_us", "pmk_pack_weights",
+           "pmk_stream_probe")
 
 i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -102,6 +103,8 @@ def load():
     L.pmk_set_watchdog_us.restype = i32
     L.pmk_pack_weights.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
     L.pmk_pack_weights.restype = i32
+    L.pmk_stream_probe.argtypes = [vp, ctypes.c_int64, i32, i32, vp, vp, P(ctypes.c_double)]
+    L.pmk_stream_probe.restype = i32
     _lib = L
     return L
 

@@ -30,6 +30,7 @@ struct pmk_handle {
   uint32_t* trace = nullptr;
   int trace_cap = 0;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> tev;
+  int* err_host = nullptr;   // pinned host-coherent mirror of the device error word
   size_t tused = 0;
   int sched = PMK_SCHED_FUSED;
   int moe_sched = PMK_MOE_STATIC;
@@ -166,16 +167,10 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
       delete h;
       return PMK_ERR_UNSUPPORTED;
     }
-    for (int nb = 2; nb <= std::min(dm.max_batch, kMaxNb); ++nb)
-      for (int avail : {G - G / 4, G}) {
-        const StageGeo g = stage_geo(K4[st], U4[st], R4[st], nb, avail, dm.kstep, dm.xpad);
-        // more than 16 rows: the same split for 16, one record per batch block
-        const size_t blocks = nb == kMaxNb ? (size_t)ceil_div(dm.max_batch, kMaxNb) : 1;
-        if (g.ks > 1) {
-          const size_t rec = ((size_t)ceil_div(U4[st], g.tiles) * R4[st] * nb + 16 + 3) & ~(size_t)3;
-          kpart_floats = std::max(kpart_floats, blocks * g.tiles * g.ks * rec);
-        }
-      }
+    // every batch and every grid share the prologue may choose (QKV and O
+    // give up to a quarter of the grid to attention tasks of their own)
+    kpart_floats = std::max(kpart_floats, (size_t)kpart_need(K4[st], U4[st], R4[st], dm.max_batch, G, st <= 1,
+                                                             dm.kstep, dm.xpad));
   }
   const long attn_max = (long)dm.max_batch * dm.Hkv * dm.max_chunks;
   // a workgroup's attention share may also hold one piece of every (request, KV head)
@@ -259,6 +254,14 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     return code;
   };
   if (hipMemset(base, 0, total) != hipSuccess) return fail(PMK_ERR_DEVICE);
+  // the device writes a detected error here as well, so that the next call
+  // can return it without waiting for the stream
+  if (hipHostMalloc((void**)&h->err_host, 64, hipHostMallocCoherent) != hipSuccess) {
+    h->err_host = nullptr;
+    return fail(PMK_ERR_OOM);
+  }
+  *(volatile int*)h->err_host = 0;
+  ws.err_host = h->err_host;
 
   // RoPE table: angle pos * theta^(-2i/d) in double, cos/sin rounded to float
   {
@@ -311,6 +314,10 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
                     const pmk_routing* rout, void* stream) {
   if (!h || !hidden || !kv || !seq_lens) return PMK_ERR_ARG;
   if (batch < 1 || batch > h->dm.max_batch) return PMK_ERR_ARG;
+  // a device error of an earlier step that has reached the host mirror: the
+  // step would be skipped on the device anyway
+  const int pending = *(volatile int*)h->err_host;
+  if (pending != 0) return pending;
   hipStream_t s = (hipStream_t)stream;
   StepArgs a{};
   a.dm = h->dm;
@@ -395,6 +402,7 @@ int decode_layer_destroy(pmk_handle* h) {
   }
   if (h->d_layers) (void)hipFree(h->d_layers);
   if (h->ws_base) (void)hipFree(h->ws_base);
+  if (h->err_host) (void)hipHostFree(h->err_host);
   delete h;
   return rc;
 }
@@ -423,6 +431,7 @@ int pmk_get_device_error(pmk_handle* h) {
   if (hipMemcpy(&e, h->ws.err, 4, hipMemcpyDeviceToHost) != hipSuccess) return PMK_ERR_DEVICE;
   if (e != 0 && hipMemset(h->ws.err, 0, 64 * 4) != hipSuccess) return PMK_ERR_DEVICE;
   if (hipDeviceSynchronize() != hipSuccess) return PMK_ERR_DEVICE;
+  *(volatile int*)h->err_host = 0;
   return e;
 }
 

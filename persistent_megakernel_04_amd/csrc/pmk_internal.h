@@ -68,6 +68,36 @@ __host__ __device__ inline StageGeo stage_geo(int K, int units, int urows, int n
   }
 }
 
+// Split-K record layout of a dense stage, as the persistent kernel addresses
+// it: task (row tile t, slice s, batch block k) stores its slice's partial sums
+// (the tile's rows x nb, then nb sums of squares) at record
+// ((k tiles + t) ks + s), records `stride` floats apart, a whole number of
+// 16-byte units sized for the stage's largest tile. nb: rows of the block (16
+// for every block of a batch beyond 16 rows).
+__host__ __device__ inline int kpart_stride(int units, int urows, int tiles, int nb) {
+  return ((units + tiles - 1) / tiles * urows * nb + 16 + 3) & ~3;
+}
+
+// Floats of split-K records a stage of depth K needs at most, over every
+// batch (nb = min(batch, 16) rows per block, ceil(max_batch / 16) blocks at 16)
+// and every grid share the prologue may give the stage (the whole grid, or the
+// grid less the workgroups of up to a quarter of it that take attention tasks
+// of their own: avail in [grid - grid / 4, grid] for QKV and O).
+__host__ __device__ inline long kpart_need(int K, int units, int urows, int max_batch, int grid, bool attn_share,
+                                           int kstep, int xpad) {
+  long need = 0;
+  const int lo = attn_share ? grid - grid / 4 : grid;
+  for (int nb = 2; nb <= (max_batch < kMaxNb ? max_batch : kMaxNb); ++nb)
+    for (int avail = lo; avail <= grid; ++avail) {
+      const StageGeo g = stage_geo(K, units, urows, nb, avail, kstep, xpad);
+      if (g.ks <= 1) continue;
+      const long blocks = nb == kMaxNb ? (max_batch + kMaxNb - 1) / kMaxNb : 1;
+      const long ext = blocks * g.tiles * g.ks * (long)kpart_stride(units, urows, g.tiles, nb);
+      if (ext > need) need = ext;
+    }
+  return need;
+}
+
 // Task types of the per-workgroup queue (one layer's worth; replayed per layer).
 enum TaskType : int {
   T_QKV = 1,      // y = tile: RMSNorm1 + QKV rows + RoPE + KV append
@@ -140,6 +170,7 @@ struct Workspace {
   int4* queue;         // [grid][max_queue]
   int* qlen;           // [grid]
   int* err;            // [0] error word, [16] abort flag
+  int* err_host;       // pinned, host-coherent mirror of the error word (written by the device when set)
   void* args;          // a copy of this step's StepArgs, written by the prologue
   float* kpart;        // split-K partial sums: [tile][slice][rows nb + 16] of the current stage
   int* tctr;           // [4][tctr_stride][kCtr] per (batch block, row tile): slices done (reset by the last one)

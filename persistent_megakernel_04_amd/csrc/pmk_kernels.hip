@@ -623,7 +623,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
     ps.b0 = b0;
     // one record stride for every block of the stage (the last may be short),
     // a whole number of 16-byte units
-    ps.rs = ((units + g.tiles - 1) / g.tiles * urows * (g.blk > 1 ? kMaxNb : ps.nb) + 16 + 3) & ~3;
+    ps.rs = kpart_stride(units, urows, g.tiles, g.blk > 1 ? kMaxNb : ps.nb);
     return true;
   };
   switch (task.x) {
@@ -1834,10 +1834,27 @@ __device__ __forceinline__ int stage_of(int type) {
 // kPart: a launch of an ablation schedule, which runs the layers and task
 // types `rs` names, with a grid-wide barrier after every stage if rs.barrier;
 // the fused launch (kPart false) runs everything, chained by events alone.
+// Copy a device error into the host mirror (system scope: the host reads it
+// without synchronising). Called by one thread.
+__device__ __forceinline__ void mirror_error(const StepArgs& a, int e) {
+  if (e != 0 && a.ws.err_host)
+    __hip_atomic_store(a.ws.err_host, e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+template <typename WT, bool kPart, int KP>
+__device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* lds_raw);
+
 template <typename WT, bool kPart, int KP>
 __global__ void __launch_bounds__(kBlock, 1) pmk_main(const StepArgs* __restrict__ pa, RunSpec rs) {
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-  const StepArgs& a = *pa;
+  main_body<WT, kPart, KP>(*pa, rs, lds_raw);
+  // every exit path ends here: a workgroup that leaves with the error word set
+  // (a watchdog expiry anywhere in the grid) copies it to the host mirror
+  if (threadIdx.x == 0) mirror_error(*pa, ldci(pa->ws.err));
+}
+
+template <typename WT, bool kPart, int KP>
+__device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* lds_raw) {
   const Dims& dm = a.dm;
   const int wg = blockIdx.x, wave = wave_id();
   const Lds s = lds_layout(lds_raw);
@@ -2073,10 +2090,12 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   }
   __syncthreads();
   if (bad) {
-    if ((bad & 2) && tid == 0) {
+    if (tid == 0) {
       int expected = 0;
-      __hip_atomic_compare_exchange_strong(a.ws.err, &expected, (int)PMK_ERR_SEQ, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+      if (bad & 2)
+        __hip_atomic_compare_exchange_strong(a.ws.err, &expected, (int)PMK_ERR_SEQ, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      mirror_error(a, ldci(a.ws.err));
     }
     for (int w = tid; w < G; w += blockDim.x) a.ws.qlen[w] = 0;
     return;
@@ -2276,6 +2295,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     int expected = 0;
     __hip_atomic_compare_exchange_strong(a.ws.err, &expected, (int)PMK_ERR_ARG, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
+    mirror_error(a, ldci(a.ws.err));
   }
 }
 

@@ -77,6 +77,19 @@ WORKLOADS = {
         name="c4_moe", dtype="bf16", n_layers=1, hidden=2048, n_q_heads=32, n_kv_heads=4, head_dim=128,
         ffn_dim=0, n_experts=128, top_k=8, expert_ffn_dim=768, batches=(1, 4, 16, 64, 128),
         seq_lo=2048, seq_hi=2048, notes="Qwen3-30B-A3B-shaped MoE decode layer"),
+    # one GPU's share of the Llama-70B shape under 8-way tensor parallelism: 8 query heads and 1 KV head
+    # (the heads split 8 ways), FFN 28672 / 8; all 80 layers, batch 8, ragged U{8192..16384}
+    "c5_tp8_share": Workload(
+        name="c5_tp8_share", dtype="bf16", n_layers=80, hidden=8192, n_q_heads=8, n_kv_heads=1, head_dim=128,
+        ffn_dim=3584, batches=(8,), seq_lo=8192, seq_hi=16384,
+        notes="per-GPU share of the 70B-shaped stack under 8-way tensor parallelism (no all-reduce)"),
+    # one GPU's share of the MoE layer under 8-way expert parallelism: the 16 local experts of 128; each
+    # token brings one routed row (top-1 over the local experts), so T tokens give T rows at T / 16 per
+    # expert, the density that an 8-way dispatch of T tokens' top-8 choices delivers to one GPU
+    "c4_ep8_share": Workload(
+        name="c4_ep8_share", dtype="bf16", n_layers=1, hidden=2048, n_q_heads=32, n_kv_heads=4, head_dim=128,
+        ffn_dim=0, n_experts=16, top_k=1, expert_ffn_dim=768, batches=(1, 16, 128), seq_lo=2048, seq_hi=2048,
+        notes="per-GPU share of the MoE layer under 8-way expert parallelism (no all-to-all)"),
     # Llama-70B-shaped 80-layer stack, bf16, batch 8, ragged U{8192..16384}
     "c5_70b": Workload(
         name="c5_70b", dtype="bf16", n_layers=80, hidden=8192, n_q_heads=64, n_kv_heads=8, head_dim=128,

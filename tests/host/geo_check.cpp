@@ -85,6 +85,50 @@ int main() {
           }
         }
     }
+  // Split-K record extent against the allocation. For every batch the
+  // prologue may see and every share it may give QKV and O (a quarter of the
+  // grid at most goes to attention workgroups of their own), the records the
+  // kernel writes -- task (tile t, slice s, block k) at record
+  // ((k tiles + t) ks + s), each `rs` floats holding the tile's rows x nb sums
+  // and nb sums of squares -- must lie inside the workspace's kpart region,
+  // sized by kpart_need. rs is written out here from the kernel's addressing.
+  struct KShape { int H, Hq, Hkv, d, F, kstep, xpad, max_batch; };
+  const KShape kshapes[] = {
+      {4096, 32, 8, 128, 14336, 32, 8, 128},   // 8B-shaped
+      {8192, 64, 8, 128, 28672, 32, 8, 16},    // 70B-shaped
+      {2048, 32, 4, 128, 0, 32, 8, 128},       // MoE layer's attention projections
+      {8192, 8, 1, 128, 3584, 32, 8, 16},      // a tensor-parallel share of the 70B shape
+      {4096, 4, 2, 64, 256, 16, 4, 16},        // float32, small QKV: the shares change the split's record size
+      {1024, 8, 2, 64, 4096, 16, 4, 16},
+      {256, 4, 2, 64, 688, 16, 4, 4}};
+  const int grids[] = {256, 304, 240, 80};
+  for (const KShape& sh : kshapes)
+    for (int G : grids)
+      for (int st = 0; st < 4; ++st) {
+        if (st >= 2 && sh.F == 0) continue;
+        const int K4[4] = {sh.H, sh.Hq * sh.d, sh.H, sh.F};
+        const int U4[4] = {(sh.Hq + 2 * sh.Hkv) * sh.d / 2, sh.H, sh.F, sh.H};
+        const int R4[4] = {2, 1, 2, 1};
+        const long alloc = kpart_need(K4[st], U4[st], R4[st], sh.max_batch, G, st <= 1, sh.kstep, sh.xpad);
+        for (int B = 1; B <= sh.max_batch; ++B)
+          for (int own = 0; own <= (st <= 1 ? G / 4 : 0); ++own) {
+            ++cases;
+            const int nb = B < kMaxNb ? B : kMaxNb;
+            StageGeo g = stage_geo(K4[st], U4[st], R4[st], nb, G - own, sh.kstep, sh.xpad);
+            if (g.ks <= 1) continue;   // no records (or passes over the batch)
+            const long blk = B > kMaxNb ? (B + kMaxNb - 1) / kMaxNb : 1;
+            const long rows = (long)(U4[st] + g.tiles - 1) / g.tiles * R4[st];
+            const long rs = (rows * (blk > 1 ? kMaxNb : nb) + 16 + 3) & ~3L;
+            const long used = rows * nb + nb;   // sums, then sums of squares
+            const long extent = (blk * g.tiles * g.ks - 1) * rs + used;
+            if (rs % 4 || used > rs || extent > alloc) {
+              std::printf("FAIL split-K records past the allocation: H %d Hq %d Hkv %d d %d F %d grid %d stage %d "
+                          "batch %d own %d: ks %d tiles %d rs %ld extent %ld alloc %ld\n",
+                          sh.H, sh.Hq, sh.Hkv, sh.d, sh.F, G, st, B, own, g.ks, g.tiles, rs, extent, alloc);
+              return 1;
+            }
+          }
+      }
   std::printf("ok %ld\n", cases);
   return 0;
 }

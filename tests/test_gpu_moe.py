@@ -5,10 +5,13 @@ Routing is checked three ways:
     logits (top-k by logit desc / index asc, gates = softmax of the selection,
     exp_indptr / tile_indptr / sorted_tok / sorted_slot from the definition);
   * against the oracle (which rounds its logits to float32 and takes the same
-    decision): every token routes identically except where the oracle's k-th /
-    (k+1)-th logit gap is below twice the measured logit difference (a near
-    tie, counted); outputs of identically routed tokens match to the tolerance,
-    and with no near ties the grouping arrays match bit for bit;
+    decision): the two sides' logits agree within ZERR_BOUND, and every token
+    routes identically except where the oracle's k-th / (k+1)-th logit gap is
+    below twice the measured logit difference (a near tie; none is allowed in
+    the seeded cases unless a test says so). Tokens routed alike match the
+    oracle element by element; a near-tie token is compared with the oracle
+    fed the GPU's selection. With no near tie the grouping arrays match bit
+    for bit;
   * an all-zero router makes every logit exactly 0, so routing is fixed by the
     tie rule alone and must match the oracle exactly.
 """
@@ -18,7 +21,7 @@ import torch
 
 import synth
 from synth.workloads import Workload
-from _cases import build_case, oracle_inputs, rel_l2, to_np
+from _cases import BF16_ULP_REL, build_case, check_rows, oracle_inputs, rel_l2, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +82,8 @@ def run_moe(orc, w, T, lens, tag, max_seq=None, zero_router=False, random_gains=
         model.set_moe_scheduler(moe_sched)
     bm = model.info()["moe_bm"]
     rb = routing_buffers(T, w.n_experts, w.top_k)
-    announce(f"moe_layer_step {w.name} T={T} lens={list(lens)[:6]} zero_router={zero_router}")
+    announce(f"moe_layer_step {w.name} T={T} lens={list(lens)[:6]} zero_router={zero_router} "
+             f"scheduler={moe_sched or 'static'} schedule={sched or 'fused'}")
     assert model.moe_layer_step(case.hidden, case.kv, case.seq_lens, rb) == 0
     torch.cuda.synchronize()
     assert model.device_error() == 0
@@ -88,31 +92,59 @@ def run_moe(orc, w, T, lens, tag, max_seq=None, zero_router=False, random_gains=
     desc = orc.make_desc(w, T, case.max_seq, n_layers=1)
     kv_ref = inp["kv"][0]
     ref, r_ref = orc.moe_layer(desc, inp["layers"][0], kv_ref, inp["seq_lens"], inp["hidden"], bm)
+    # the oracle fed a given selection (for tokens routed differently at a near tie)
+    r_ref["routed"] = lambda idx: orc.moe_layer_routed(desc, inp["layers"][0], kv_ref, inp["seq_lens"],
+                                                       inp["hidden"], idx)[0]
     model.close()
     return case, got, ref, r_gpu, r_ref, bm, kv_ref
 
 
-def compare_moe(w, T, got, ref, r_gpu, r_ref, bm):
+# Router logits (std ~0.9 for N(0, 0.02) routers) are float32 on both sides.
+# The GPU forms them from bfloat16 weights and inputs carried as bfloat16 hi +
+# lo pairs (2^-17 relative), summed in float32 over H terms, from an h1 that
+# carries the attention half's own error (a few 1e-6 relative): measured
+# differences are 3e-6 .. 3.4e-4 (the largest at 1024 tokens with 1..64
+# cached positions). Dropping the lo half alone would move logits by ~2e-3,
+# so the bound is 1e-3.
+ZERR_BOUND = 1e-3
+
+
+def near_tie_cap(T):
+    """Tokens allowed to route differently at a near tie. With 128 N(0, 0.9^2)
+    logits the gap between the k-th and (k+1)-th largest is about exponential
+    with mean ~0.06, and logit differences of ~1e-5 flip the order when the gap
+    is below ~2e-5: ~3.5e-4 per token. None up to 16 tokens; beyond, one per
+    256 tokens (at least one). Each such token is still compared, against the
+    oracle fed the GPU's selection."""
+    return 0 if T <= 16 else max(1, T // 256)
+
+
+def compare_moe(w, T, got, ref, r_gpu, r_ref, bm, max_near=None):
     E, k = w.n_experts, w.top_k
+    max_near = near_tie_cap(T) if max_near is None else max_near
     check_routing_self_consistent(r_gpu, T, E, k, bm)
     dz = np.abs(r_gpu["router_logits"].astype(np.float64) - r_ref["router_logits"].astype(np.float64))
     zerr = float(dz.max())
+    assert zerr <= ZERR_BOUND, f"router logits differ by {zerr}"
     same = np.all(r_gpu["topk_idx"] == r_ref["topk_idx"], axis=1)
-    near = 0
-    for t in np.nonzero(~same)[0]:
+    near = np.nonzero(~same)[0]
+    for t in near:
         zs = np.sort(r_ref["router_logits"][t].astype(np.float64))[::-1]
         gap = zs[k - 1] - zs[k]
         assert gap <= 2 * zerr, f"token {t} routed differently with a logit gap {gap} > 2 x {zerr}"
-        near += 1
-    err = rel_l2(got[same], ref[same]) if same.any() else 0.0
-    print(f"  logit max diff {zerr:.2e}, near-tie tokens {near}/{T}, rel_l2(hidden) = {err:.3e} (tol {w.tol})",
-          flush=True)
-    assert err <= w.tol
-    if near == 0:
+    print(f"  logit max diff {zerr:.2e}, near-tie tokens {len(near)}/{T}", flush=True)
+    assert len(near) <= max_near, f"{len(near)} near-tie tokens (at most {max_near} expected)"
+    assert same.any()
+    err = check_rows(got[same], ref[same], w, "hidden (tokens routed alike)")
+    if len(near):
+        # a near-tie token against the oracle fed the GPU's selection
+        alt = r_ref["routed"](r_gpu["topk_idx"])
+        check_rows(got[near], alt[near], w, "hidden (near-tie tokens, GPU selection)")
+    else:
         for key in ("exp_indptr", "tile_indptr", "sorted_tok", "sorted_slot", "topk_idx"):
             np.testing.assert_array_equal(r_gpu[key], r_ref[key], err_msg=key)
         np.testing.assert_allclose(r_gpu["topk_w"], r_ref["topk_w"], rtol=1e-3, atol=1e-5)
-    return near
+    return len(near)
 
 
 def test_moe_tiny_f32(orc):
@@ -131,17 +163,30 @@ def test_moe_small_bf16_two_router_blocks(orc):
     compare_moe(w, T, got, ref, rg, rr, bm)
 
 
-@pytest.mark.parametrize("T", [1, 4, 16])
+@pytest.mark.parametrize("T", [1, 4, 16, 64, 128])
 def test_moe_qwen3_30b_a3b_shape(orc, T):
     """The Qwen3-30B-A3B-shaped MoE layer (128 experts, top-8, expert FFN 768),
-    each token its own request with 2048 cached positions."""
+    each token its own request with 2048 cached positions, at the workload's
+    token counts (static expert scheduling)."""
     w = synth.get_workload("c4_moe")
     case, got, ref, rg, rr, bm, kv_ref = run_moe(orc, w, T, [2048] * T, f"m3_{T}", max_seq=2049)
     compare_moe(w, T, got, ref, rg, rr, bm)
-    # the appended K/V entries
-    a = case.kv[0, :, :, :, 2048].float().cpu().numpy()
-    b = (kv_ref[:, :T, :, 2048].astype(np.uint32) << 16).view(np.float32)
-    assert rel_l2(a, b) <= w.tol
+    # the appended K/V entries: rows (K/V, token) of Hkv d values
+    a = case.kv[0, :, :, :, 2048].float().cpu().numpy().reshape(2 * T, -1)
+    b = (kv_ref[:, :T, :, 2048].astype(np.uint32) << 16).view(np.float32).reshape(2 * T, -1)
+    check_rows(a, b, w, "appended K/V", ulp_rel=BF16_ULP_REL)
+
+
+@pytest.mark.parametrize("T", [16, 128])
+def test_moe_ep8_share_16_experts(orc, T):
+    """One GPU's share of the MoE layer under 8-way expert parallelism: the 16
+    local experts, each token one routed row (top-1 of 16), so the grouped
+    GEMM sees T rows at T / 16 per expert, as an 8-way dispatch of top-8 of
+    128 delivers them. Routing bit-exact, outputs per element."""
+    w = synth.get_workload("c4_ep8_share")
+    case, got, ref, rg, rr, bm, kv_ref = run_moe(orc, w, T, [2048] * T, f"m10_{T}", max_seq=2049)
+    np.testing.assert_array_equal(rg["topk_w"], 1.0)
+    compare_moe(w, T, got, ref, rg, rr, bm)
 
 
 @pytest.mark.parametrize("S", [1000, 1800])
@@ -204,7 +249,7 @@ def test_decode_step_on_moe_handle_matches_moe_layer_step(orc):
     bm = model.info()["moe_bm"]
     ref, _ = orc.moe_layer(orc.make_desc(w, T, 64, n_layers=1), inp["layers"][0], inp["kv"][0], inp["seq_lens"],
                            inp["hidden"], bm)
-    assert rel_l2(to_np(case.hidden), ref) <= w.tol
+    check_rows(to_np(case.hidden), ref, w)
     model.close()
 
 
