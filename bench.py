@@ -276,10 +276,11 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true", help="first run a plain 2 GiB device-to-device copy "
                     "(a kernel of known traffic, for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
-    ap.add_argument("--schedule", default="fused", choices=["fused", "layer", "stage", "barrier"],
+    ap.add_argument("--schedule", default="fused", choices=["fused", "layer", "stage", "barrier", "op"],
                     help="fused: the whole stack in one persistent launch per step (the default); layer / stage: "
                     "an ablation that puts a kernel boundary after every layer / every stage of a layer; barrier: "
-                    "one launch with a grid-wide barrier after every stage")
+                    "one launch with a grid-wide barrier after every stage; op: one launch per operator, ten per "
+                    "layer, with the norms, RoPE, KV append and attention merge as operators of their own")
     ap.add_argument("--moe-scheduler", default="static", choices=["static", "dynamic"],
                     help="MoE workloads: grouped expert tasks as fixed per-workgroup shares (static) or popped from "
                     "a per-layer queue (dynamic)")
@@ -385,7 +386,8 @@ def main():
     if w.n_experts:
         model.set_moe_scheduler(args.moe_scheduler)
     stages_per_layer = 8 if w.n_experts else 5
-    launches = {"fused": 2, "barrier": 2, "layer": 1 + L, "stage": 1 + L * stages_per_layer}[args.schedule]
+    launches = {"fused": 2, "barrier": 2, "layer": 1 + L, "stage": 1 + L * stages_per_layer,
+                "op": 1 + L * 10}[args.schedule]
     info = model.info()
     log(f"handle: grid={info['grid']} block={info['block']} lds={info['lds_bytes']} "
         f"workspace={info['workspace_bytes'] / 2**20:.1f} MiB")

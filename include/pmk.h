@@ -229,13 +229,27 @@ int pmk_timing_read(pmk_handle* h, double* total_ms, int32_t* launches);
  *                        of the next stage (nor its weight prefetch) before
  *                        every workgroup has finished the current one (the
  *                        pages' unfused megakernel).
- * The same task code and results in every mode (per-step prologue included);
+ *   PMK_SCHED_PER_OP     one launch per operator of each layer, ten per layer
+ *                        (320 per token for 32 layers, the unfused GPU
+ *                        picture of the "Dataflow Is All You Need" summary,
+ *                        Key observations, observation 1: K1-K10 per decoder
+ *                        layer): RMSNorm, QKV projection, RoPE, KV append,
+ *                        attention partials, partial merge, O projection +
+ *                        residual, RMSNorm, gate/up + SwiGLU, down +
+ *                        residual. The norms, RoPE, append and merge that the
+ *                        other modes fuse into the projections run as ops of
+ *                        their own (the projections then read the normalised
+ *                        rows from memory). Dense handles only.
+ * The same task code and results in every mode (per-step prologue included;
+ * the per-op mode adds the separate norm, RoPE, append and merge tasks);
  * timing (pmk_timing_*) covers all persistent launches of a step. Applies to
- * later calls. Errors: PMK_ERR_ARG (null handle, unknown mode). */
+ * later calls. Errors: PMK_ERR_ARG (null handle, unknown mode),
+ * PMK_ERR_UNSUPPORTED (PMK_SCHED_PER_OP on a MoE handle). */
 #define PMK_SCHED_FUSED 0
 #define PMK_SCHED_PER_LAYER 1
 #define PMK_SCHED_PER_STAGE 2
 #define PMK_SCHED_BARRIER 3
+#define PMK_SCHED_PER_OP 4
 int pmk_set_schedule(pmk_handle* h, int32_t mode);
 
 /* How the grouped expert GEMM tasks of a MoE layer reach workgroups (Event

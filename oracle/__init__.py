@@ -73,6 +73,7 @@ def lib():
         L.orc_topk.argtypes = [P, I, I, P, P]
         L.orc_group.argtypes = [P, I, I, I, I, P, P, P, P]
         L.orc_decode_layer.argtypes = [P, P, P, P, I, P]
+        L.orc_decode_layer_given_append.argtypes = [P, P, P, P, I, P]
         L.orc_decode_stack.argtypes = [P, P, P, P, I, P]
         L.orc_moe_layer.argtypes = [P, P, P, P, I, I, P, P, P, P, P, P, P, P]
         L.orc_moe_layer_routed.argtypes = [P, P, P, P, I, P, P, P]
@@ -193,24 +194,28 @@ def _layer_struct(layer: dict):
     return Layer(**vals), keep
 
 
-def decode_layer(desc: Desc, layer: dict, kv_layer, seq_lens, hidden):
+def decode_layer(desc: Desc, layer: dict, kv_layer, seq_lens, hidden, given_append: bool = False):
     """One dense layer. kv_layer [2][max_batch][Hkv][max_seq][d] is updated in
-    place (K/V appended); returns the new hidden [batch][H] (float64)."""
+    place (K/V appended); returns the new hidden [batch][H] (float64). With
+    given_append, each request's new K/V entry is read from slot seq_len as it
+    stands in kv_layer (another implementation's append) instead of written."""
     s, keep = _layer_struct(layer)
     h = np.array(hidden, dtype=np.float64, copy=True)
     sl = _c(seq_lens, np.int32)
     assert kv_layer.flags["C_CONTIGUOUS"]
-    rc = lib().orc_decode_layer(ctypes.byref(desc), ctypes.byref(s), _ptr(kv_layer), _ptr(sl), h.shape[0], _ptr(h))
+    fn = lib().orc_decode_layer_given_append if given_append else lib().orc_decode_layer
+    rc = fn(ctypes.byref(desc), ctypes.byref(s), _ptr(kv_layer), _ptr(sl), h.shape[0], _ptr(h))
     if rc:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return h
 
 
-def decode_stack(desc: Desc, layers: list, kv, seq_lens, hidden):
-    """The full stack; kv [L][2][max_batch][Hkv][max_seq][d] updated in place."""
+def decode_stack(desc: Desc, layers: list, kv, seq_lens, hidden, given_append: bool = False):
+    """The full stack; kv [L][2][max_batch][Hkv][max_seq][d] updated in place
+    (with given_append: read, see decode_layer)."""
     h = np.array(hidden, dtype=np.float64, copy=True)
     for l, layer in enumerate(layers):
-        h = decode_layer(desc, layer, kv[l], seq_lens, h)
+        h = decode_layer(desc, layer, kv[l], seq_lens, h, given_append)
     return h
 
 

@@ -233,8 +233,12 @@ static size_t kv_layer_elems(const orc_desc* D) {
  *   K[b][g][pos] <- rnd(k_g), V[b][g][pos] <- rnd(v_g)   (append, cache dtype);
  *   o = attention over the pos+1 cached entries (the new token attends to itself);
  *   h1 = x + W_o o.
- * kv points at this layer's [2][max_batch][Hkv][max_seq][d] block. */
-static void attn_half(const orc_desc* D, const orc_layer* W, void* kv, int b, int pos, const double* x, double* h1) {
+ * kv points at this layer's [2][max_batch][Hkv][max_seq][d] block. With
+ * given_append, the entry at slot pos is taken as it already stands in kv
+ * (another implementation's append, whose rounding to the cache dtype may fall
+ * on the other side of a rounding boundary) instead of being written. */
+static void attn_half(const orc_desc* D, const orc_layer* W, void* kv, int b, int pos, const double* x, double* h1,
+                      int given_append) {
   int H = D->hidden, Hq = D->n_q_heads, Hkv = D->n_kv_heads, d = D->head_dim, dt = D->dtype;
   int nq = Hq * d, nkv = Hkv * d;
   double* u = (double*)malloc(sizeof(double) * H);
@@ -249,7 +253,7 @@ static void attn_half(const orc_desc* D, const orc_layer* W, void* kv, int b, in
   size_t eb = dt == ORC_BF16 ? 2 : 4;
   void* K = base + eb * ((size_t)b * Hkv * (size_t)D->max_seq * d);
   void* V = base + eb * (half + (size_t)b * Hkv * (size_t)D->max_seq * d);
-  for (int g = 0; g < Hkv; ++g)
+  for (int g = 0; g < Hkv && !given_append; ++g)
     for (int t = 0; t < d; ++t) {
       size_t off = ((size_t)g * D->max_seq + (size_t)pos) * d + t;
       st(K, dt, off, qkv[nq + (size_t)g * d + t]);
@@ -286,7 +290,8 @@ static int check_desc(const orc_desc* D) {
 /* One dense decoder layer over a batch: for each request b (independently),
  * h1 = attention half; x' = h1 + FFN(RMSNorm(h1; ffn_norm)). hidden is
  * [batch][H] doubles, updated in place; kv is this layer's cache block. */
-int orc_decode_layer(const orc_desc* D, const orc_layer* W, void* kv, const int32_t* seq_lens, int batch, double* hidden) {
+static int decode_layer_impl(const orc_desc* D, const orc_layer* W, void* kv, const int32_t* seq_lens, int batch,
+                             double* hidden, int given_append) {
   if (check_desc(D) || batch < 0 || batch > D->max_batch || D->ffn_dim <= 0) return -1;
   for (int b = 0; b < batch; ++b)
     if (seq_lens[b] < 0 || seq_lens[b] >= D->max_seq) return -2;
@@ -296,7 +301,7 @@ int orc_decode_layer(const orc_desc* D, const orc_layer* W, void* kv, const int3
   double* f = (double*)malloc(sizeof(double) * H);
   for (int b = 0; b < batch; ++b) {
     double* x = hidden + (size_t)b * H;
-    attn_half(D, W, kv, b, seq_lens[b], x, h1);
+    attn_half(D, W, kv, b, seq_lens[b], x, h1, given_append);
     orc_rmsnorm(h1, W->ffn_norm, H, D->rms_eps, u2);
     swiglu_ffn(W->w_gate, W->w_up, W->w_down, D->dtype, H, D->ffn_dim, u2, f);
     for (int i = 0; i < H; ++i) x[i] = h1[i] + f[i];
@@ -305,6 +310,17 @@ int orc_decode_layer(const orc_desc* D, const orc_layer* W, void* kv, const int3
   free(u2);
   free(f);
   return 0;
+}
+
+int orc_decode_layer(const orc_desc* D, const orc_layer* W, void* kv, const int32_t* seq_lens, int batch, double* hidden) {
+  return decode_layer_impl(D, W, kv, seq_lens, batch, hidden, 0);
+}
+
+/* The same layer with each request's new K/V entry read from slot seq_len of
+ * kv as given, not appended (see attn_half). */
+int orc_decode_layer_given_append(const orc_desc* D, const orc_layer* W, void* kv, const int32_t* seq_lens, int batch,
+                                  double* hidden) {
+  return decode_layer_impl(D, W, kv, seq_lens, batch, hidden, 1);
 }
 
 /* The stack: layer l's output is layer l+1's input; no final norm. */
@@ -355,7 +371,7 @@ static int moe_layer_impl(const orc_desc* D, const orc_layer* W, void* kv, const
   double* w = (double*)malloc(sizeof(double) * k);
   for (int t = 0; t < T; ++t) {
     double* x = hidden + (size_t)t * H;
-    attn_half(D, W, kv, t, seq_lens[t], x, h1);
+    attn_half(D, W, kv, t, seq_lens[t], x, h1, 0);
     orc_rmsnorm(h1, W->ffn_norm, H, D->rms_eps, u2);
     orc_matvec(W->w_router, dt, E, H, u2, zd);
     for (int e = 0; e < E; ++e) z[e] = (float)zd[e];

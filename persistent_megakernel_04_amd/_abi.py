@@ -17,8 +17,9 @@ PMK_F32, PMK_BF16 = 0, 1
 PMK_ROWS, PMK_TILES = 0, 1
 
 # pmk_set_schedule modes (include/pmk.h)
-SCHED_FUSED, SCHED_PER_LAYER, SCHED_PER_STAGE, SCHED_BARRIER = 0, 1, 2, 3
-SCHEDULES = {"fused": SCHED_FUSED, "layer": SCHED_PER_LAYER, "stage": SCHED_PER_STAGE, "barrier": SCHED_BARRIER}
+SCHED_FUSED, SCHED_PER_LAYER, SCHED_PER_STAGE, SCHED_BARRIER, SCHED_PER_OP = 0, 1, 2, 3, 4
+SCHEDULES = {"fused": SCHED_FUSED, "layer": SCHED_PER_LAYER, "stage": SCHED_PER_STAGE, "barrier": SCHED_BARRIER,
+             "op": SCHED_PER_OP}
 # pmk_set_moe_scheduler modes
 MOE_STATIC, MOE_DYNAMIC = 0, 1
 MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC}

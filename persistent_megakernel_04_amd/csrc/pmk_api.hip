@@ -178,8 +178,9 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   // of a stage at most the grid, in groups of 8 per block
   const int nblk = ceil_div(dm.max_batch, kMaxNb);
   dm.tctr_stride = G * nblk;
+  // (+ 8: the per-op schedule's norm, RoPE, append and merge entries)
   dm.max_queue = ceil_div(dm.qkv_tiles, G) + ceil_div(dm.o_tiles, G) + ceil_div(attn_max, G) +
-                 dm.max_batch * dm.Hkv + 8 + 4 * (ceil_div((G + 8) * nblk, G) + 1);
+                 dm.max_batch * dm.Hkv + 16 + 4 * (ceil_div((G + 8) * nblk, G) + 1);
   if (moe)
     dm.max_queue += ceil_div((long)dm.router_tiles * ceil_div(dm.max_batch, kMaxNb), G) + 4;
   else
@@ -213,6 +214,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
       {(void**)&ws.kpart, kpart_floats * 4},
       {(void**)&ws.tctr, (size_t)4 * dm.tctr_stride * kCtr * 4},
       {(void**)&ws.bar, (size_t)dm.L * kMaxStages * kEvInts * 4},
+      {(void**)&ws.u, (size_t)dm.max_batch * dm.H * 4},
   };
   if (moe) {
     const std::vector<Part> mp = {
@@ -333,6 +335,7 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
   a.trace = h->trace;
   a.trace_cap = h->trace_cap;
   a.barrier = h->sched == PMK_SCHED_BARRIER;
+  a.per_op = h->sched == PMK_SCHED_PER_OP;
   a.moe_dyn = h->dm.moe && h->moe_sched == PMK_MOE_DYNAMIC;
   h->last_stream = s;
   if (launch_prologue(a, s) != hipSuccess) return PMK_ERR_DEVICE;
@@ -360,6 +363,9 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
     else
       for (int t : {T_GU, T_DOWN}) stages.push_back(bit(t));
     if (h->sched == PMK_SCHED_PER_LAYER) stages = {kAllTypes};
+    if (h->sched == PMK_SCHED_PER_OP)   // ten operators per layer, each a launch of its own
+      stages = {bit(T_NORM1), bit(T_QKV), bit(T_ROPE), bit(T_APPEND), bit(T_ATTN), bit(T_MERGE), bit(T_O),
+                bit(T_NORM2), bit(T_GU), bit(T_DOWN)};
     for (int l = 0; l < L; ++l)
       for (unsigned types : stages)
         if (launch_main(a, h->desc.dtype, s, RunSpec{l, l + 1, types, 0}) != hipSuccess) return PMK_ERR_DEVICE;
@@ -375,8 +381,9 @@ int pmk_set_moe_scheduler(pmk_handle* h, int32_t mode) {
 }
 
 int pmk_set_schedule(pmk_handle* h, int32_t mode) {
-  if (!h || mode < PMK_SCHED_FUSED || mode > PMK_SCHED_BARRIER)
+  if (!h || mode < PMK_SCHED_FUSED || mode > PMK_SCHED_PER_OP)
     return PMK_ERR_ARG;
+  if (mode == PMK_SCHED_PER_OP && h->dm.moe) return PMK_ERR_UNSUPPORTED;
   h->sched = mode;
   return PMK_OK;
 }

@@ -110,7 +110,13 @@ enum TaskType : int {
   T_MGU = 8,      // this workgroup's share of the grouped gate/up GEMM tasks
   T_MDOWN = 9,    // this workgroup's share of the grouped down GEMM tasks
   T_COMBINE = 10, // this workgroup's share of the per-token gated combine (MoE layer output)
-  T_ATTS = 11     // x >> 8: piece | pieces << 12, y = b | g << 16, z..w: positions: streamed attention piece
+  T_ATTS = 11,    // x >> 8: piece | pieces << 12, y = b | g << 16, z..w: positions: streamed attention piece
+  // the per-op schedule's separate operators (each a grid-stride share of its op per workgroup)
+  T_NORM1 = 12,   // u = RMSNorm(layer input; attn_norm)
+  T_NORM2 = 13,   // u = RMSNorm(h1; ffn_norm)
+  T_ROPE = 14,    // rotate q and k in place at each request's position
+  T_APPEND = 15,  // k, v rounded into the cache at each request's slot
+  T_MERGE = 16    // merge the attention chunks' partials of every (request, KV head) into o
 };
 
 // Events of one layer. Each event is a block of kEvInts ints: [0] is the
@@ -191,6 +197,7 @@ struct Workspace {
   int* mq;             // [L][2][kCtr]                  dynamic: pop counter, push counter
   float* mact;         // [L][max_batch k][Fe]          expert SwiGLU rows, grouped order (per layer)
   float* mout;         // [max_batch k][H]              expert down rows, grouped order
+  float* u;            // [max_batch][H]                per-op schedule: the RMSNorm output a projection reads
 };
 
 struct StepArgs {
@@ -211,6 +218,7 @@ struct StepArgs {
   int trace_cap;                       // entries per workgroup (entry 0 is the header)
   int barrier;                         // 1: the barrier schedule (the prologue arms ws.bar)
   int moe_dyn;                         // 1: grouped expert tasks popped from a per-layer queue
+  int per_op;                          // 1: the per-op schedule (norms, RoPE, append, merge as ops of their own)
 };
 
 // Which task paths an instantiation of the persistent kernel carries: all of

@@ -247,6 +247,8 @@ __device__ __forceinline__ void stage_rows(const GemvIn& in, int nb, int K, int 
     float ss = 0.f;
     for (int w = 0; w < kWaves; ++w) ss += s.ssp[threadIdx.x * kWaves + w];
     s.rstd[threadIdx.x] = in.norm == 2 ? ss : 1.0f / sqrtf(ss / (float)K + in.eps);
+  } else if (!in.norm && threadIdx.x < nb) {
+    s.rstd[threadIdx.x] = 1.0f;   // rows normalised by an op of their own (per-op schedule): no scale
   }
   __syncthreads();
 }
@@ -633,6 +635,8 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       ps.rw = GemvRows{ROWS_QKV, ldp(&Lp->w_qkv), nullptr, u.x, dm.d >> 1, dm.H, k0};
       ps.in = GemvIn{hid_in(a, c.l) + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->attn_norm) + k0,
                      ps.ks > 1 ? 2 : 1, dm.eps, -1};
+      if constexpr ((KP & 3) == KP_ALL)
+        if (a.per_op) ps.in = GemvIn{a.ws.u + (size_t)b0 * dm.H + k0, dm.H, nullptr, nullptr, 0, dm.eps, -1};
       ps.epi = E_QKV; ps.r0 = u.x; ps.n = u.y;
       break;
     }
@@ -651,6 +655,8 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       ps.rw = GemvRows{ROWS_PAIR, ldp(&Lp->w_gate), ldp(&Lp->w_up), u.x, u.y, dm.H, k0};
       ps.in = GemvIn{h1_of(a, c.l) + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->ffn_norm) + k0,
                      ps.ks > 1 ? 2 : 1, dm.eps, -1};
+      if constexpr ((KP & 3) == KP_ALL)
+        if (a.per_op) ps.in = GemvIn{a.ws.u + (size_t)b0 * dm.H + k0, dm.H, nullptr, nullptr, 0, dm.eps, -1};
       ps.epi = E_GU; ps.r0 = u.x; ps.n = u.y;
       break;
     }
@@ -856,6 +862,18 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
   switch (ps.epi) {
     case E_QKV: {   // RoPE at each request's position, then q/k/v out and the K/V append
       const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d, ni = ps.n * nb;
+      if constexpr ((KP & 3) == KP_ALL) {
+        if (a.per_op) {   // the projection alone: RoPE and the append are ops of their own
+          for (int idx = t0; idx < ni; idx += nt) {
+            const int m = idx / ps.n, ju = idx - m * ps.n;
+            const int unit = ps.r0 + ju, h = unit / half, i = unit - h * half;
+            float* dst = qkv_of(a, c.l) + (size_t)(b0 + m) * qkv_dim + h * dm.d + i;
+            stc(dst, ys[(2 * ju) * nb + m]);
+            stc(dst + half, ys[(2 * ju + 1) * nb + m]);
+          }
+          break;
+        }
+      }
       // lane m < nb holds request b0 + m's position; the rotation rows of
       // eight items per lane are loaded together (one latency per eight
       // items, not two dependent ones per item)
@@ -1018,7 +1036,7 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, int b, int g, int ci, 
       Ls += sp[D + 1] * f;
       A += *reinterpret_cast<const f4v*>(sp + e0) * f;
     }
-    if (nc == 1 && !a.attn_merge_o) {
+    if (nc == 1 && !a.attn_merge_o && !a.per_op) {
       stc4(orr, (h * D + e0) * 4, A / Ls);
     } else {
       stc4(prr, (h * DP + e0) * 4, A);
@@ -1026,7 +1044,7 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, int b, int g, int ci, 
     }
   }
   if (tid == 0) c.s.tclk[5] = (uint32_t)now_ticks();   // outputs issued
-  if (a.attn_merge_o) {   // the O-projection merges the partials as it stages its inputs
+  if (a.attn_merge_o || a.per_op) {   // the O-projection (or the per-op merge) merges the partials
     wg_notify(ev_ptr(a, c.l, EV_ATTN), tix & (kSubs - 1));
     return true;
   }
@@ -1810,6 +1828,108 @@ __device__ __forceinline__ bool task_combine(const Ctx& c, const int* wev) {
 }
 
 // ---------------------------------------------------------------------------
+// The per-op schedule's separate operators. Each runs in a launch of its own
+// (the kernel boundary orders it after the previous op), and every workgroup
+// takes a grid-stride share of the op's elements. They compute what the fused
+// tasks fold into the projections: the RMSNorms, RoPE, the K/V append and the
+// merge of the attention partials.
+// ---------------------------------------------------------------------------
+// u = x g / sqrt(mean(x^2) + eps) for every request row (x: the layer input,
+// or h1 for the second norm); one row per workgroup at a time.
+__device__ __forceinline__ bool task_norm(const Ctx& c, bool ffn) {
+  const StepArgs& a = c.a;
+  const Dims& dm = a.dm;
+  const float* x = ffn ? h1_of(a, c.l) : hid_in(a, c.l);
+  const float* g = ffn ? ldp(&a.layers[c.l].ffn_norm) : ldp(&a.layers[c.l].attn_norm);
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  __syncthreads();
+  for (int b = c.wg; b < a.batch; b += dm.grid) {
+    const float* xr = x + (size_t)b * dm.H;
+    float ss = 0.f;
+    for (int i = tid; i < dm.H; i += kBlock) {
+      const float v = ldc(xr + i);
+      ss += v * v;
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) c.s.red[wave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+    for (int w = 0; w < kWaves; ++w) tot += c.s.red[w];
+    const float r = 1.0f / sqrtf(tot / (float)dm.H + dm.eps);
+    for (int i = tid; i < dm.H; i += kBlock) stc(a.ws.u + (size_t)b * dm.H + i, ldc(xr + i) * r * g[i]);
+    __syncthreads();
+  }
+  return true;
+}
+
+// RoPE in place on the projected q and k heads: pair (i, i + d/2) of head h of
+// request b turned by the angle of position seq_lens[b] (the host-built table).
+__device__ __forceinline__ bool task_rope(const Ctx& c) {
+  const StepArgs& a = c.a;
+  const Dims& dm = a.dm;
+  const int half = dm.d >> 1, nh = dm.Hq + dm.Hkv, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
+  const long n = (long)a.batch * nh * half;
+  float* q = qkv_of(a, c.l);
+  for (long t = (long)c.wg * kBlock + threadIdx.x; t < n; t += (long)dm.grid * kBlock) {
+    const int b = (int)(t / (nh * half)), r = (int)(t - (long)b * nh * half), h = r / half, i = r - h * half;
+    const int pos = *gp(a.seq_lens + b);
+    const float2 cs = a.ws.rope[(size_t)pos * half + i];
+    float* z = q + (size_t)b * qkv_dim + h * dm.d + i;
+    const float y1 = ldc(z), y2 = ldc(z + half);
+    stc(z, y1 * cs.x - y2 * cs.y);
+    stc(z + half, y2 * cs.x + y1 * cs.y);
+  }
+  return true;
+}
+
+// The new K and V rows of every request into its cache slot seq_lens[b],
+// rounded to the cache dtype (nearest even).
+template <typename KT>
+__device__ __forceinline__ bool task_append(const Ctx& c) {
+  const StepArgs& a = c.a;
+  const Dims& dm = a.dm;
+  const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
+  const long n = (long)a.batch * 2 * dm.Hkv * dm.d;
+  const float* q = qkv_of(a, c.l);
+  for (long t = (long)c.wg * kBlock + threadIdx.x; t < n; t += (long)dm.grid * kBlock) {
+    const int b = (int)(t / (2 * dm.Hkv * dm.d)), r = (int)(t - (long)b * 2 * dm.Hkv * dm.d);
+    const int kvh = r / dm.d, e = r - kvh * dm.d, which = kvh / dm.Hkv, g = kvh - which * dm.Hkv;
+    const int pos = *gp(a.seq_lens + b);
+    const float v = ldc(q + (size_t)b * qkv_dim + (dm.Hq + kvh) * dm.d + e);
+    Elem<KT>::put(reinterpret_cast<KT*>(a.kv) + kv_off(dm, c.l, which, b, g, pos) + e, v);
+  }
+  return true;
+}
+
+// o of every (request, KV head): the log-sum-exp merge of the chunk partials
+// (acc, max, sum per query head, log2 units) the attention op left in part.
+__device__ __forceinline__ bool task_merge(const Ctx& c) {
+  const StepArgs& a = c.a;
+  const Dims& dm = a.dm;
+  const int D = dm.d, DP = D + 4, G = dm.Hq / dm.Hkv, ck = a.attn_chunk;
+  for (int bg = c.wg; bg < a.batch * dm.Hkv; bg += dm.grid) {
+    const int b = bg / dm.Hkv, g = bg - b * dm.Hkv;
+    const int nc = (*gp(a.seq_lens + b) + ck) / ck;
+    const float* part = a.ws.part + ((size_t)b * dm.Hkv + g) * dm.max_chunks * G * DP;
+    float* o = o_of(a, c.l) + (size_t)b * dm.Hq * D + (size_t)g * G * D;
+    for (int t = threadIdx.x; t < G * D; t += kBlock) {
+      const int h = t / D, e = t - h * D;
+      float M = -INFINITY;
+      for (int cc = 0; cc < nc; ++cc) M = fmaxf(M, ldc(part + (cc * G + h) * DP + D));
+      float L = 0.f, A = 0.f;
+      for (int cc = 0; cc < nc; ++cc) {
+        const float* p = part + (cc * G + h) * DP;
+        const float f = exp2f(ldc(p + D) - M);
+        L += ldc(p + D + 1) * f;
+        A += ldc(p + e) * f;
+      }
+      stc(o + t, A / L);
+    }
+  }
+  return true;
+}
+
+// ---------------------------------------------------------------------------
 // The persistent kernel
 // ---------------------------------------------------------------------------
 // Task types that run as GEMV passes.
@@ -1952,6 +2072,18 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
             if constexpr ((KP & 3) != KP_DENSE) {
               ok = task_combine(c, need(EV_MDOWN, l));
               if (ok) wg_notify(ev_ptr(a, l, EV_DOWN), wg & (kSubs - 1));
+            }
+            break;
+          case T_NORM1: case T_NORM2: case T_ROPE: case T_APPEND: case T_MERGE:
+            if constexpr (kPart && (KP & 3) == KP_ALL) {
+              switch (task.x) {
+                case T_NORM1: ok = task_norm(c, false); break;
+                case T_NORM2: ok = task_norm(c, true); break;
+                case T_ROPE: ok = task_rope(c); break;
+                case T_APPEND: ok = task_append<WT>(c); break;
+                default: ok = task_merge(c); break;
+              }
+              __syncthreads();
             }
             break;
           default: break;
@@ -2113,7 +2245,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       for (int b = 0; b < B; ++b) mx = max(mx, (sl[b] + c) / c);
       return mx;
     };
-    if (B <= dm.merge_b) {
+    if (B <= dm.merge_b && !a.per_op) {
       int c = kMinChunk;
       while (c < kMaxChunk && max_nc(c) > kMergeChunks) c <<= 1;
       if (max_nc(c) <= kMergeChunks) { ck = c; merge = 1; }
@@ -2133,7 +2265,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     // are cut into equal shares, one per workgroup (at least 64 positions),
     // and each piece of a range within a share is a task. cb then holds the
     // prefix sum of the requests' positions (S + 1), else of their chunks.
-    const int stream = !merge && dm.attn_mm;
+    const int stream = !merge && dm.attn_mm && !a.per_op;   // per-op: chunk partials, merged by an op
     stream_s = stream;
     int acc = 0;
     for (int b = 0; b < B; ++b) {
@@ -2155,7 +2287,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     // tile there would start only after attention and have its whole weight
     // tile still to load, which held the O event back by ~5 us at batch 1).
     // Otherwise the attention tasks follow the QKV tiles on every workgroup.
-    const int own = (merge && total_attn <= G / 4) ? total_attn : 0;
+    const int own = (merge && total_attn <= G / 4 && !a.per_op) ? total_attn : 0;
     attn_wg0_s = own ? G - own : G;
     // each dense stage's split (see stage_geo): up to 16 rows, one pass over
     // K slices that fit the LDS; beyond, the split of 16 rows for every block
@@ -2205,7 +2337,12 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
         if (ts < TS) push(make_int4(type, ts / g.ks, ts % g.ks, r >> 3));
       }
     };
+    if (a.per_op) push(make_int4(T_NORM1, 0, 0, 0));
     stage_tasks(T_QKV, 0);
+    if (a.per_op) {
+      push(make_int4(T_ROPE, 0, 0, 0));
+      push(make_int4(T_APPEND, 0, 0, 0));
+    }
     if (stream_s) {   // this workgroup's share of the laid-out ranges
       // range (b, g) spans [seg0, seg0 + kPieceCost + S_b + 1): its lead, then its positions
       auto start = [&](int b) { return (long)dm.Hkv * (cb[b] + (long)b * kPieceCost); };
@@ -2238,7 +2375,9 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       const int r = i - dm.Hkv * cb[lo], nc = cb[lo + 1] - cb[lo];
       push(make_int4(T_ATTN | (i << 8), lo, r / nc, r % nc));
     }
+    if (a.per_op) push(make_int4(T_MERGE, 0, 0, 0));
     stage_tasks(T_O, 1);
+    if (a.per_op) push(make_int4(T_NORM2, 0, 0, 0));
     if (!dm.moe) {
       stage_tasks(T_GU, 2);
       stage_tasks(T_DOWN, 3);
@@ -2260,7 +2399,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
       // dense stages: one notifier per row tile (and batch block), on sub-counter tile % kSubs
       case EV_QKV: arm_indexed(ev, geo_s[0].tiles, geo_s[0].blk); break;
       // one notifier per chunk task (partials merged by the O-projection), or per (request, KV head)
-      case EV_ATTN: arm_indexed(ev, merge_s ? total_attn : B * dm.Hkv); break;
+      case EV_ATTN: arm_indexed(ev, (merge_s || a.per_op) ? total_attn : B * dm.Hkv); break;
       case EV_O: arm_indexed(ev, geo_s[1].tiles, geo_s[1].blk); break;
       case EV_GU: arm_indexed(ev, dm.moe ? 0 : geo_s[2].tiles, geo_s[2].blk); break;
       case EV_DOWN:   // MoE: one combine slot per workgroup

@@ -15,7 +15,8 @@ import numpy as np
 
 TICK_US = 0.01     # 100 MHz
 TASK_NAMES = {1: "qkv", 2: "attn", 3: "o", 4: "gate_up", 5: "down", 6: "router", 7: "route", 8: "moe_gate_up",
-              9: "moe_down", 10: "combine", 11: "attn_s"}
+              9: "moe_down", 10: "combine", 11: "attn_s", 12: "norm1", 13: "norm2", 14: "rope", 15: "append",
+              16: "merge"}
 PHASES = ("t0", "ready", "staged", "streamed", "reduced", "stored", "t1")
 WORDS = 8
 

@@ -28,13 +28,24 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
-# Per-element bound, relative to the RMS of the reference row: |got - ref| <=
-# ELEM_TOL * rms(ref row). The workloads state a relative L2 bound over the
-# whole output (1e-5 float32, 1e-2 bfloat16); the kernels' measured errors are
-# far below it (rel-L2 of a few 1e-8 for float32, a few 1e-6 per bfloat16
-# layer, growing to ~1e-5 over the 32-layer stack), so a tighter element bound
-# catches a few wrong outputs that a whole-batch L2 would average away.
+# Per-element bounds, relative to the RMS of the reference row: |got - ref| <=
+# bound * rms(ref row). The workloads state a relative L2 bound over the whole
+# output (1e-5 float32, 1e-2 bfloat16), which every row must also meet.
+#
+# A bfloat16 cache makes each new K/V entry a rounding decision: where the
+# float32 (GPU) and double (oracle) values of an element straddle a rounding
+# boundary, the two stored entries differ by one bfloat16 ulp (2^-8 relative),
+# and with a short cache (weight ~1/S on the new entry) that moves a head's
+# attention output by up to ~2e-3 relative. So the outputs are compared twice:
+#  * against the oracle with its own appended entries: rel-L2 within the
+#    workload's bound and every element within ELEM_TOL_OWN of its row's RMS;
+#  * against the oracle fed the GPU's appended entries (the entries themselves
+#    checked to agree with the oracle's to one ulp): every element within
+#    ELEM_TOL, near the kernels' arithmetic error (a few 1e-6 relative per
+#    bfloat16 layer, ~1e-5 over a deep stack; a few 1e-8 for float32), which
+#    catches a handful of wrong outputs that a whole-batch L2 would average away.
 ELEM_TOL = {"f32": 1e-5, "bf16": 1e-3}
+ELEM_TOL_OWN = {"f32": 1e-5, "bf16": 1e-2}
 BF16_ULP_REL = 2.0 ** -7
 
 
@@ -115,8 +126,14 @@ def oracle_inputs(case: Case, requests=None):
     }
 
 
-def run_oracle_dense(orc, case: Case, inp) -> tuple[np.ndarray, np.ndarray]:
+def run_oracle_dense(orc, case: Case, inp, kv_given=None) -> tuple[np.ndarray, np.ndarray]:
+    """The oracle over the stack on `inp`. With kv_given (a host copy of the
+    GPU's cache after its step, over the same requests), each layer reads the
+    GPU's appended entries instead of appending its own."""
     desc = orc.make_desc(case.w, len(inp["requests"]), case.max_seq, n_layers=case.n_layers)
+    if kv_given is not None:
+        kv = np.ascontiguousarray(kv_given)
+        return orc.decode_stack(desc, inp["layers"], kv, inp["seq_lens"], inp["hidden"], given_append=True), kv
     kv = inp["kv"]
     out = orc.decode_stack(desc, inp["layers"], kv, inp["seq_lens"], inp["hidden"])
     return out, kv

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import synth
-from _cases import (BF16_ULP_REL, block_requests, build_case, check_rows, make_model, oracle_inputs,
+from _cases import (BF16_ULP_REL, ELEM_TOL_OWN, block_requests, build_case, check_rows, make_model, oracle_inputs,
                     run_oracle_dense, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -44,7 +44,26 @@ def check_appended(w, kv_gpu, kv_ref, lens, what="appended K/V"):
         got.append(kv_as_float(kv_gpu[:, :, i, :, int(s)]).reshape(-1, kv_gpu.shape[3] * kv_gpu.shape[5]))
         ref.append(kv_as_float(kv_ref[:, :, i, :, int(s)]).reshape(-1, kv_ref.shape[3] * kv_ref.shape[5]))
     ulp = BF16_ULP_REL if w.dtype == "bf16" else 0.0
-    check_rows(np.concatenate(got), np.concatenate(ref), w, what, ulp_rel=ulp)
+    # against the oracle's own chain: in a deep stack the entries of later
+    # layers also carry the drift of earlier layers' rounding decisions
+    check_rows(np.concatenate(got), np.concatenate(ref), w, what, ulp_rel=ulp, elem_tol=ELEM_TOL_OWN[w.dtype])
+
+
+def check_against_oracle(orc, case, inp, got, kv_gpu, what="hidden"):
+    """`got` (the GPU's outputs over inp's requests) against the oracle with
+    its own appended K/V entries (rel-L2 per row and overall within the
+    workload's bound, elements within ELEM_TOL_OWN), the GPU's appended
+    entries against the oracle's (one bfloat16 ulp at most per element), and
+    `got` against the oracle fed the GPU's appended entries (elements within
+    ELEM_TOL). kv_gpu: host copy of the GPU's cache after the step over the
+    same requests."""
+    w = case.w
+    ref, kv_ref = run_oracle_dense(orc, case, inp)
+    err = check_rows(got, ref, w, what + " vs oracle", elem_tol=ELEM_TOL_OWN[w.dtype])
+    check_appended(w, kv_gpu, kv_ref, inp["seq_lens"])
+    ref_g, _ = run_oracle_dense(orc, case, inp, kv_given=kv_gpu)
+    check_rows(got, ref_g, w, what + " vs oracle on the GPU's appended entries")
+    return err
 
 
 def check_dense(orc, case, requests="auto", sched=None):
@@ -63,13 +82,10 @@ def check_dense(orc, case, requests="auto", sched=None):
     model.step(case.hidden, case.kv, case.seq_lens)
     torch.cuda.synchronize()
     assert model.device_error() == 0
-    ref, kv_ref = run_oracle_dense(orc, case, inp)
-    got = to_np(case.hidden).astype(np.float64)[inp["requests"]]
-    err = check_rows(got, ref, case.w)
-    kv_gpu = to_np(case.kv[:, :, inp["requests"]] if requests is not None else case.kv)
-    check_appended(case.w, kv_gpu, kv_ref, inp["seq_lens"])
     model.close()
-    return err
+    got = to_np(case.hidden).astype(np.float64)[inp["requests"]]
+    kv_gpu = to_np(case.kv[:, :, inp["requests"]] if requests is not None else case.kv)
+    return check_against_oracle(orc, case, inp, got, kv_gpu)
 
 
 def test_c1_tiny_f32(orc):
@@ -182,8 +198,7 @@ def test_watchdog_abandons_step_then_handle_recovers(orc):
     model.step(case.hidden, case.kv, case.seq_lens)
     torch.cuda.synchronize()
     assert model.device_error() == 0
-    ref, _ = run_oracle_dense(orc, case, inp)
-    check_rows(to_np(case.hidden), ref, w, "hidden after recovery")
+    check_against_oracle(orc, case, inp, to_np(case.hidden), to_np(case.kv), "hidden after recovery")
     model.close()
 
 
@@ -198,16 +213,29 @@ def test_consecutive_steps_chain(orc):
     desc = orc.make_desc(w, 2, 260, n_layers=2)
     kv_ref, h_ref = inp["kv"], inp["hidden"]
     lens = np.array([40, 200], np.int32)
+    outs = []
     for step in range(3):
-        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
-        announce(f"chained step {step} lens={lens.tolist()}")
+        sl = torch.tensor(lens + step, dtype=torch.int32, device="cuda")
+        announce(f"chained step {step} lens={(lens + step).tolist()}")
         model.step(case.hidden, case.kv, sl)
         torch.cuda.synchronize()
         assert model.device_error() == 0
-        h_ref = orc.decode_stack(desc, inp["layers"], kv_ref, lens, h_ref)
-        check_rows(to_np(case.hidden), h_ref, w, f"hidden at step {step}")
-        lens = lens + 1
+        outs.append(to_np(case.hidden).astype(np.float64))
     model.close()
+    kv_gpu = to_np(case.kv)
+    h_given = inp["hidden"]
+    for step in range(3):
+        # the oracle chained on its own appends, and on the GPU's (the cache
+        # after the last step holds every step's entry; step i reads slots up
+        # to lens + i only)
+        h_ref = orc.decode_stack(desc, inp["layers"], kv_ref, lens + step, h_ref)
+        check_rows(outs[step], h_ref, w, f"hidden at step {step} vs oracle", elem_tol=ELEM_TOL_OWN[w.dtype])
+        h_given = orc.decode_stack(desc, inp["layers"], kv_gpu.copy(), lens + step, h_given, given_append=True)
+        check_rows(outs[step], h_given, w, f"hidden at step {step} vs oracle on the GPU's appended entries")
+    for b, s0 in enumerate(lens):   # rows (layer, K/V, Hkv, slot) of d values
+        check_rows(kv_as_float(kv_gpu[:, :, b, :, s0:s0 + 3]).reshape(-1, w.head_dim),
+                   kv_as_float(kv_ref[:, :, b, :, s0:s0 + 3]).reshape(-1, w.head_dim), w,
+                   f"appended K/V of request {b}", ulp_rel=BF16_ULP_REL, elem_tol=ELEM_TOL_OWN[w.dtype])
 
 
 def test_8b_full_stack_b1_bench_config(orc):
@@ -241,16 +269,20 @@ def test_c2_8b_full_stack_100_step_chain(orc):
     outs = [to_np(h).astype(np.float64) for h in hid]
     desc = orc.make_desc(w, 1, case.max_seq)
     kv_ref = inp["kv"]
+    kv_gpu = to_np(case.kv)
     worst = 0.0
     for i in range(n_steps):
-        ref = orc.decode_stack(desc, inp["layers"], kv_ref, np.array([S0 + i], np.int32), ins[i])
-        worst = max(worst, check_rows(outs[i], ref, w, f"hidden at step {i}"))
+        sl = np.array([S0 + i], np.int32)
+        ref = orc.decode_stack(desc, inp["layers"], kv_ref, sl, ins[i])
+        worst = max(worst, check_rows(outs[i], ref, w, f"hidden at step {i} vs oracle", elem_tol=ELEM_TOL_OWN[w.dtype]))
+        # the GPU's cache after the last step holds every step's entry; step i reads slots up to S0 + i only
+        ref_g = orc.decode_stack(desc, inp["layers"], kv_gpu.copy(), sl, ins[i], given_append=True)
+        check_rows(outs[i], ref_g, w, f"hidden at step {i} vs oracle on the GPU's appended entries")
         if i % 10 == 9:
             progress(f"c2 chain: oracle at step {i + 1}/{n_steps}, worst rel_l2 so far {worst:.3e}")
-    kv_gpu = to_np(case.kv)
     got = kv_as_float(kv_gpu[:, :, 0, :, S0:S0 + n_steps]).transpose(0, 1, 3, 2, 4).reshape(-1, w.n_kv_heads * 128)
     ref = kv_as_float(kv_ref[:, :, 0, :, S0:S0 + n_steps]).transpose(0, 1, 3, 2, 4).reshape(-1, w.n_kv_heads * 128)
-    check_rows(got, ref, w, "appended K/V of all 100 steps", ulp_rel=BF16_ULP_REL)
+    check_rows(got, ref, w, "appended K/V of all 100 steps", ulp_rel=BF16_ULP_REL, elem_tol=ELEM_TOL_OWN[w.dtype])
 
 
 def test_8b_full_stack_b16_ragged_every_request(orc):
@@ -275,23 +307,25 @@ def stream_oracle_stack(orc, w, case, lens, hidden_in, n_layers, label):
     """The oracle over a stack too large to copy at once: layer by layer, each
     layer's weights and cache block copied to the host after the GPU step.
     Slots 0..S-1 of the cache are untouched by the step; slot S holds the GPU's
-    appended entry, which is kept for the comparison and then overwritten by
-    the oracle's own append before its attention reads it. Returns (hidden,
-    GPU appended entries [L][B][2][Hkv][d], oracle appended entries)."""
+    appended entry. Each layer runs twice: reading the GPU's entry (the chain
+    on the GPU's appended entries), then appending its own over it (the
+    oracle's own chain). Returns (hidden, hidden on the GPU's entries, GPU
+    appended entries [L][B][2][Hkv][d], oracle appended entries)."""
     desc = orc.make_desc(w, len(lens), case.max_seq, n_layers=1)
-    h = hidden_in
+    h = h_g = hidden_in
     app_gpu, app_ref = [], []
     idx = np.arange(len(lens))
     for l in range(n_layers):
         layer = {k: to_np(v) for k, v in case.layers[l].items()}
         kv_l = np.ascontiguousarray(to_np(case.kv[l]))
         app_gpu.append(kv_l[:, idx, :, lens].copy())
+        h_g = orc.decode_layer(desc, layer, kv_l, lens, h_g, given_append=True)
         h = orc.decode_layer(desc, layer, kv_l, lens, h)
         app_ref.append(kv_l[:, idx, :, lens].copy())
         del layer, kv_l
         if l % 10 == 9:
             progress(f"{label}: oracle at layer {l + 1}/{n_layers}")
-    return h, np.stack(app_gpu), np.stack(app_ref)
+    return h, h_g, np.stack(app_gpu), np.stack(app_ref)
 
 
 def check_streamed(orc, w, B, lo, hi, key, tag):
@@ -308,12 +342,13 @@ def check_streamed(orc, w, B, lo, hi, key, tag):
     assert model.device_error() == 0
     model.close()
     got = to_np(case.hidden).astype(np.float64)
-    ref, app_gpu, app_ref = stream_oracle_stack(orc, w, case, lens, hidden0, w.n_layers, w.name)
-    check_rows(got, ref, w)
+    ref, ref_g, app_gpu, app_ref = stream_oracle_stack(orc, w, case, lens, hidden0, w.n_layers, w.name)
+    check_rows(got, ref, w, "hidden vs oracle", elem_tol=ELEM_TOL_OWN[w.dtype])
+    check_rows(got, ref_g, w, "hidden vs oracle on the GPU's appended entries")
     d = w.head_dim
     # rows (layer, request, K/V) of Hkv d values; app arrays are [L][B][2][Hkv][d]
     check_rows(kv_as_float(app_gpu).reshape(-1, w.n_kv_heads * d), kv_as_float(app_ref).reshape(-1, w.n_kv_heads * d),
-               w, "appended K/V", ulp_rel=BF16_ULP_REL)
+               w, "appended K/V", ulp_rel=BF16_ULP_REL, elem_tol=ELEM_TOL_OWN[w.dtype])
 
 
 def test_c5_70b_full_80_layers_b8(orc):
@@ -434,14 +469,15 @@ def test_f32_small_qkv_batch16_split_records(orc):
     check_dense(orc, case)
 
 
-@pytest.mark.parametrize("sched", ["layer", "stage", "barrier"])
+@pytest.mark.parametrize("sched", ["layer", "stage", "barrier", "op"])
 @pytest.mark.parametrize("B", [1, 4])
 def test_unfused_schedules_match_oracle(orc, sched, B):
-    """The ablation schedules (one launch of the persistent kernel per layer or
-    per stage of each layer, or one launch with a grid-wide barrier after every
-    stage) run the same tasks: the same results, at batch 1 (attention on
-    workgroups of its own, partials merged by the O-projection) and batch 4
-    (streamed attention, down projection split over K)."""
+    """The ablation schedules (one launch of the persistent kernel per layer,
+    per stage of each layer or per operator, or one launch with a grid-wide
+    barrier after every stage) run the same tasks: the same results, at batch
+    1 (attention on workgroups of its own, partials merged by the
+    O-projection; per-op: chunk partials merged by an op of their own) and
+    batch 4 (streamed attention, down projection split over K)."""
     w = synth.get_workload("c3_8b_sweep")
     lens = [512] if B == 1 else synth.ragged_lengths(B, 512, 2048, ("c3_8b_sweep", "sched", B))
     case = build_case(w, B, lens, n_layers=2, max_seq=int(max(lens)) + 2, tag=f"t13_{sched}_{B}")

@@ -243,6 +243,8 @@ def test_decode_step_on_moe_handle_matches_moe_layer_step(orc):
     from persistent_megakernel_04_amd import DecodeModel
     model = DecodeModel.from_workload(w, case.layers, case.max_batch, case.max_seq)
     announce("decode_step on a MoE handle")
+    from persistent_megakernel_04_amd import _abi
+    assert model.lib.pmk_set_schedule(model.handle, _abi.SCHED_PER_OP) == _abi.PMK_ERR_UNSUPPORTED
     assert model.decode_step(case.hidden, case.kv, case.seq_lens) == 0
     torch.cuda.synchronize()
     assert model.device_error() == 0

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import synth
-from _cases import block_requests, build_case, check_rows, make_model, oracle_inputs, run_oracle_dense, to_np
+from _cases import block_requests, build_case, make_model, oracle_inputs, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -85,10 +85,11 @@ def check_tiles_dense(orc, case, requests="auto", sched=None, oracle=True):
     assert torch.equal(h_rows.view(torch.int32), h_tiles.view(torch.int32)), "hidden differs between layouts"
     assert torch.equal(kv_rows.view(torch.int16), kv_tiles.view(torch.int16)), "KV cache differs between layouts"
     if oracle:
+        from test_gpu_dense import check_against_oracle
         inp = oracle_inputs(case, requests)
-        ref, _ = run_oracle_dense(orc, case, inp)
         print("  bit-identical between layouts", flush=True)
-        check_rows(to_np(h_tiles).astype(np.float64)[inp["requests"]], ref, case.w)
+        kv_gpu = to_np(kv_tiles[:, :, inp["requests"]] if requests is not None else kv_tiles)
+        check_against_oracle(orc, case, inp, to_np(h_tiles).astype(np.float64)[inp["requests"]], kv_gpu)
 
 
 def test_tiles_8b_full_stack_b1_bench_config(orc):

@@ -402,3 +402,43 @@ def test_moe_routed_other_selection_is_gate_weighted_mixture(orc):
     out_p, g_p = orc.moe_layer_routed(orc.make_desc(w, T, 6), L, kv.copy(), sl, x, sel[:, ::-1].copy())
     np.testing.assert_allclose(g_p, g[:, ::-1], rtol=1e-13)
     np.testing.assert_allclose(out_p, out, rtol=1e-12, atol=1e-13)
+
+
+def test_given_append_with_own_entries_equals_layer(orc):
+    """The layer that reads the new K/V entry from the cache as given: handed
+    a cache whose slot seq_len already holds the layer's own appended entries,
+    it reproduces the layer exactly (bf16 cache) and leaves the cache alone."""
+    rng = np.random.default_rng(37)
+    w = tiny(dtype="bf16", hidden=16, n_q_heads=4, n_kv_heads=2, head_dim=4, ffn_dim=24)
+    L = {n: (a if n.endswith("norm") else _bf16_bits(a)) for n, a in rnd_layer(rng, w).items()}
+    kv = _bf16_bits(rnd_kv(rng, w, 3, 9))
+    x = rng.standard_normal((3, 16))
+    sl = [0, 4, 8]
+    kv_own = kv.copy()
+    out = orc.decode_layer(orc.make_desc(w, 3, 9), L, kv_own, sl, x)
+    kv_given = kv_own.copy()
+    out2 = orc.decode_layer(orc.make_desc(w, 3, 9), L, kv_given, sl, x, given_append=True)
+    np.testing.assert_array_equal(out2, out)
+    np.testing.assert_array_equal(kv_given, kv_own)
+
+
+def test_given_append_reads_the_slot_as_stored(orc):
+    """d = 2, W_q = 0 (uniform attention), W_o selecting o, W_down = 0: with
+    an arbitrary entry planted at slot S the output is x + [mean of the S + 1
+    stored values, 0, 0], the planted value included; the layer that appends
+    overwrites the plant with its own entry instead."""
+    rng = np.random.default_rng(38)
+    w = tiny(hidden=4, n_q_heads=1, n_kv_heads=1, head_dim=2, ffn_dim=4)
+    L = rnd_layer(rng, w)
+    L["w_qkv"][0:2] = 0
+    L["w_o"] = np.eye(4, 2, dtype=np.float32)
+    L["w_down"][:] = 0
+    S = 4
+    kv = rnd_kv(rng, w, 1, 8)
+    kv[1, 0, 0, S] = [7.5, -3.25]
+    x = rng.standard_normal((1, 4))
+    expect = kv[1, 0, 0, :S + 1].astype(np.float64).mean(axis=0)
+    out = orc.decode_layer(orc.make_desc(w, 1, 8), L, kv.copy(), [S], x, given_append=True)
+    np.testing.assert_allclose(out[0, :2] - x[0, :2], expect, rtol=1e-12)
+    own = orc.decode_layer(orc.make_desc(w, 1, 8), L, kv.copy(), [S], x)
+    assert np.abs(own[0, :2] - out[0, :2]).max() > 0.1
