@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "pmk_internal.h"
+#include "pmk_sched.h"
 
 using namespace pmk;
 
@@ -125,30 +126,8 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   if (hipGetDeviceProperties(&prop, h->device) != hipSuccess) { delete h; return PMK_ERR_DEVICE; }
 
   Dims& dm = h->dm;
-  dm.L = desc->n_layers; dm.H = desc->hidden; dm.Hq = desc->n_q_heads; dm.Hkv = desc->n_kv_heads;
-  dm.d = desc->head_dim; dm.F = desc->ffn_dim; dm.E = desc->n_experts; dm.k = desc->top_k;
-  dm.Fe = desc->expert_ffn_dim; dm.max_batch = desc->max_batch; dm.max_seq = desc->max_seq;
-  // attention partial slots per (request, KV head): chunks of kMinChunk, or
-  // streamed pieces of at least that many positions, one more when a range
-  // starts inside a workgroup's share
-  dm.max_chunks = ceil_div(desc->max_seq, kMinChunk) + 1;
-  dm.eps = desc->rms_eps;
-  dm.grid = prop.multiProcessorCount;
-  dm.moe = moe ? 1 : 0;
-  dm.kstep = desc->dtype == PMK_BF16 ? 32 : 16;
-  dm.xpad = desc->dtype == PMK_BF16 ? 8 : 4;
-  dm.attn_mm = desc->dtype == PMK_BF16 && dm.d == 128 && dm.Hq / dm.Hkv <= 8;
-  dm.wtiles = desc->weight_layout == PMK_TILES ? 1 : 0;
-  dm.merge_b = std::min(dm.max_batch, kMergeFloats / (dm.Hq * dm.d));
+  dm = dims_from_desc(*desc, prop.multiProcessorCount);
   const int G = dm.grid;
-  dm.qkv_units = (dm.Hq + 2 * dm.Hkv) * dm.d / 2;
-  dm.qkv_tiles = std::min(G, dm.qkv_units);
-  dm.o_tiles = std::min(G, dm.H);
-  dm.gu_tiles = moe ? 0 : std::min(G, dm.F);
-  dm.down_tiles = moe ? 0 : std::min(G, dm.H);
-  dm.router_tiles = moe ? ceil_div(dm.E, 16) : 0;
-  dm.max_tiles = moe ? ceil_div((long)dm.max_batch * dm.k, kMoeBM) + dm.E : 0;
-  dm.max_down = dm.max_tiles * std::max(dm.H / 16, 1);
   // Dense stages: one input row of the whole depth and a tile's outputs must
   // fit the LDS (a step may put its few attention tasks on workgroups of their
   // own and the QKV and O tiles on the others, at least three quarters of the
@@ -172,20 +151,6 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     kpart_floats = std::max(kpart_floats, (size_t)kpart_need(K4[st], U4[st], R4[st], dm.max_batch, G, st <= 1,
                                                              dm.kstep, dm.xpad));
   }
-  const long attn_max = (long)dm.max_batch * dm.Hkv * dm.max_chunks;
-  // a workgroup's attention share may also hold one piece of every (request, KV head)
-  // batch blocks: a dense stage's (tile, slice, block) tasks, slices and tiles
-  // of a stage at most the grid, in groups of 8 per block
-  const int nblk = ceil_div(dm.max_batch, kMaxNb);
-  dm.tctr_stride = G * nblk;
-  // (+ 8: the per-op schedule's norm, RoPE, append and merge entries)
-  dm.max_queue = ceil_div(dm.qkv_tiles, G) + ceil_div(dm.o_tiles, G) + ceil_div(attn_max, G) +
-                 dm.max_batch * dm.Hkv + 16 + 4 * (ceil_div((G + 8) * nblk, G) + 1);
-  if (moe)
-    dm.max_queue += ceil_div((long)dm.router_tiles * ceil_div(dm.max_batch, kMaxNb), G) + 4;
-  else
-    dm.max_queue += ceil_div(dm.gu_tiles, G) + ceil_div(dm.down_tiles, G);
-
   // workspace carving
   const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
   const int Gq = dm.Hq / dm.Hkv;
@@ -204,7 +169,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
       {(void**)&ws.mpart, (size_t)dm.L * std::max(dm.merge_b, 1) * dm.Hkv * kMergeChunks * Gq * (dm.d + 4) * 4,
        (size_t)std::max(dm.merge_b, 1) * dm.Hkv * kMergeChunks * Gq * (dm.d + 4) * 4},
       {(void**)&ws.rope, (size_t)dm.max_seq * (dm.d / 2) * 8},
-      {(void**)&ws.ev, (size_t)dm.L * EV_COUNT * kEvInts * 4},
+      {(void**)&ws.ev, (size_t)dm.L * ev_layer_ints(dm) * 4},
       {(void**)&ws.mctr, (size_t)dm.L * dm.max_batch * dm.Hkv * kCtr * 4},
       {(void**)&ws.chunk_base, (size_t)(dm.max_batch + 1) * 4},
       {(void**)&ws.queue, (size_t)G * dm.max_queue * 16},
@@ -236,6 +201,8 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
     };
     parts.insert(parts.end(), mp.begin(), mp.end());
   }
+  // event offsets are 27-bit keys of the persistent kernel's seen-event cache
+  if ((long)dm.L * ev_layer_ints(dm) >= (1L << 27)) { delete h; return PMK_ERR_UNSUPPORTED; }
   // step intermediates are addressed with 32-bit byte offsets from one buffer
   // base, and stay below the kernels' out-of-range marker offset (1 GiB)
   for (auto& p : parts)

@@ -211,6 +211,7 @@ struct StepArgs {
   int attn_chunk;                      // KV positions per attention task this step (set by the prologue)
   int attn_merge_o;                    // 1: O-projection inputs merge the attention partials (set by the prologue)
   int qkv_tiles;                       // QKV tiles this step, on workgroups 0.. (set by the prologue)
+  int nblk;                            // event blocks of this step (set by the prologue; see pmk_sched.h)
   StageGeo geo[4];                     // QKV, O, gate/up, down split of this step (set by the prologue)
   unsigned long long watchdog_ticks;   // s_memrealtime ticks (100 MHz)
   pmk_routing rout;                    // optional routing outputs (device pointers)

@@ -31,6 +31,7 @@
 // wait is bounded by a watchdog; on expiry the step is abandoned (error word +
 // abort flag), so every wave exits.
 #include "pmk_device.h"
+#include "pmk_sched.h"
 
 namespace pmk {
 
@@ -45,6 +46,7 @@ struct Lds {
   float* ssp;      // [kMaxNb][kWaves] per-wave partial sums of squares
   int* flag;       // wait / last-arriver broadcast
   uint32_t* tclk;  // [8] phase clocks of the current task (trace): see the trace record layout
+  int* seen;       // [8] per wait kind, the event offset this workgroup last saw fired (+ 1; 0: none)
 };
 
 __device__ __forceinline__ Lds lds_layout(char* base) {
@@ -56,6 +58,7 @@ __device__ __forceinline__ Lds lds_layout(char* base) {
   s.ssp = reinterpret_cast<float*>(m + 64);               // 128 floats
   s.flag = reinterpret_cast<int*>(m + 64 + 512);          // 1 int
   s.tclk = reinterpret_cast<uint32_t*>(m + 64 + 512 + 16);   // 8 clocks
+  s.seen = reinterpret_cast<int*>(m + 64 + 512 + 16 + 32);   // 8 ints
   return s;
 }
 
@@ -95,9 +98,13 @@ __device__ __forceinline__ float* hid_out(const StepArgs& a, int l) {
   return l == a.dm.L - 1 ? a.hidden : a.ws.hid + (size_t)l * a.dm.max_batch * a.dm.H;
 }
 
-__device__ __forceinline__ int* ev_ptr(const StepArgs& a, int layer, int e) {
-  return a.ws.ev + ((size_t)layer * EV_COUNT + e) * kEvInts;
+// Event (kind, blk, g) of layer l in the event tensor (see pmk_sched.h).
+__device__ __forceinline__ int* ev_at(const StepArgs& a, int l, int kind, int blk = 0, int g = 0) {
+  return a.ws.ev + ev_off(a.dm, l, kind, blk, g);
 }
+// The event block of request b (batch blocks of 16 rows; one block unless
+// this step gives blocks events of their own).
+__device__ __forceinline__ int ev_blk_of(const StepArgs& a, int b) { return ev_blk(ldku(&a.nblk), b / kMaxNb); }
 
 __device__ __forceinline__ size_t kv_off(const Dims& dm, int l, int which, int b, int g, int pos) {
   return (((((size_t)l * 2 + which) * dm.max_batch + b) * dm.Hkv + g) * (size_t)dm.max_seq + pos) * dm.d;
@@ -143,7 +150,17 @@ struct GemvRows {
   int half;            // PAIR: rows taken from each matrix; QKV: head_dim / 2
   int ld;              // row stride of the matrix (elements)
   int k0;              // first column of the pass (a K slice)
+  int qg, qh;          // QKV: query heads per KV group, query heads
 };
+
+// The rotation unit at group-major position `up` (qkv_unit of pmk_sched.h,
+// from the fields a QKV pass carries).
+__device__ __forceinline__ int qkv_unit_r(const GemvRows& rw, int up) {
+  const int half = rw.half, G = rw.qg, per = (G + 2) * half, g = up / per, r = up - g * per;
+  if (r < G * half) return g * G * half + r;
+  if (r < (G + 1) * half) return rw.qh * half + g * half + (r - G * half);
+  return (rw.qh + rw.qh / G) * half + g * half + (r - (G + 1) * half);
+}
 
 // Where row `row` of a weight matrix with `ld` columns starts at column k0:
 // row-major, or (PK) in the tile layout: the matrix cut into 16-row x
@@ -161,8 +178,9 @@ __device__ __forceinline__ const WT* wrow(const void* base, size_t row, int ld, 
 template <typename WT, bool PK>
 __device__ __forceinline__ const WT* row_ptr(const GemvRows& rw, int j) {
   if (rw.mode == ROWS_QKV) {
-    // local row 2u is (head h, i), 2u + 1 is (h, i + d/2): the two rows of a rotation pair
-    const int unit = rw.r0 + (j >> 1), h = unit / rw.half, i = unit - h * rw.half;
+    // local row 2u is (head h, i), 2u + 1 is (h, i + d/2): the two rows of a
+    // rotation pair; units in KV-group-major order (qkv_unit)
+    const int unit = qkv_unit_r(rw, rw.r0 + (j >> 1)), h = unit / rw.half, i = unit - h * rw.half;
     return wrow<WT, PK>(rw.base, (size_t)(h * 2 * rw.half + i + (j & 1) * rw.half), rw.ld, rw.k0);
   }
   if (rw.mode == ROWS_PAIR && j >= rw.half) return wrow<WT, PK>(rw.base2, (size_t)(rw.r0 + j - rw.half), rw.ld, rw.k0);
@@ -561,11 +579,6 @@ struct Pass {
   float* ys;        // the pass's outputs [R][nb] in LDS, after its staged inputs
 };
 
-// Row tile `tile` of `units` units split in `tiles`: first unit and count.
-__device__ __forceinline__ int2 tile_units(int tile, int units, int tiles) {
-  const int u0 = (int)((long)tile * units / tiles);
-  return make_int2(u0, (int)((long)(tile + 1) * units / tiles) - u0);
-}
 
 // Pass p of a GEMV task; false once the task has no pass p. Dense stages take
 // their split from this step's geometry: task (tile, K slice) covers all
@@ -596,7 +609,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
     const int e = ldsu(a.ws.tile_info + 2 * t), row0 = ldsu(a.ws.tile_info + 2 * t + 1);
     const int h0 = (int)((long)sl * dm.H / sd), R = (int)((long)(sl + 1) * dm.H / sd) - h0;
     ps.rw = GemvRows{ROWS_CONTIG, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_down)) + (size_t)e * dm.H * dm.Fe,
-                     nullptr, h0, 0, dm.Fe, 0};
+                     nullptr, h0, 0, dm.Fe, 0, 0, 0};
     ps.in = GemvIn{mact_of(a, c.l) + (size_t)row0 * dm.Fe, dm.Fe, nullptr, nullptr, 0, 0.f, -1};
     ps.R = R; ps.K = dm.Fe; ps.kfull = dm.Fe; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
     ps.wev = a.ws.ectr + ((size_t)c.l * dm.E + e) * kCtr;
@@ -632,7 +645,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
     case T_QKV: {   // RMSNorm1 + QKV rotation pairs of the tile
       const int2 u = tile_units(tile, dm.qkv_units, ldku(&a.geo[0].tiles));
       if (!dense(0, dm.H, 2 * u.y, dm.qkv_units, 2)) return false;
-      ps.rw = GemvRows{ROWS_QKV, ldp(&Lp->w_qkv), nullptr, u.x, dm.d >> 1, dm.H, k0};
+      ps.rw = GemvRows{ROWS_QKV, ldp(&Lp->w_qkv), nullptr, u.x, dm.d >> 1, dm.H, k0, dm.Hq / dm.Hkv, dm.Hq};
       ps.in = GemvIn{hid_in(a, c.l) + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->attn_norm) + k0,
                      ps.ks > 1 ? 2 : 1, dm.eps, -1};
       if constexpr ((KP & 3) == KP_ALL)
@@ -644,7 +657,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int K = dm.Hq * dm.d;
       const int2 u = tile_units(tile, dm.H, ldku(&a.geo[1].tiles));
       if (!dense(1, K, u.y, dm.H, 1)) return false;
-      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_o), nullptr, u.x, 0, K, k0};
+      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_o), nullptr, u.x, 0, K, k0, 0, 0};
       ps.in = GemvIn{o_of(a, c.l) + (size_t)b0 * K + k0, K, nullptr, nullptr, 0, 0.f, a.attn_merge_o ? b0 : -1};
       ps.epi = E_O; ps.r0 = u.x; ps.n = u.y;
       break;
@@ -652,7 +665,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
     case T_GU: {    // RMSNorm2 + gate and up rows of the tile
       const int2 u = tile_units(tile, dm.F, ldku(&a.geo[2].tiles));
       if (!dense(2, dm.H, 2 * u.y, dm.F, 2)) return false;
-      ps.rw = GemvRows{ROWS_PAIR, ldp(&Lp->w_gate), ldp(&Lp->w_up), u.x, u.y, dm.H, k0};
+      ps.rw = GemvRows{ROWS_PAIR, ldp(&Lp->w_gate), ldp(&Lp->w_up), u.x, u.y, dm.H, k0, 0, 0};
       ps.in = GemvIn{h1_of(a, c.l) + (size_t)b0 * dm.H + k0, dm.H, nullptr, ldp(&Lp->ffn_norm) + k0,
                      ps.ks > 1 ? 2 : 1, dm.eps, -1};
       if constexpr ((KP & 3) == KP_ALL)
@@ -663,7 +676,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
     case T_DOWN: {  // down-projection rows of the tile
       const int2 u = tile_units(tile, dm.H, ldku(&a.geo[3].tiles));
       if (!dense(3, dm.F, u.y, dm.H, 1)) return false;
-      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_down), nullptr, u.x, 0, dm.F, k0};
+      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_down), nullptr, u.x, 0, dm.F, k0, 0, 0};
       ps.in = GemvIn{act_of(a, c.l) + (size_t)b0 * dm.F + k0, dm.F, nullptr, nullptr, 0, 0.f, -1};
       ps.epi = E_DOWN; ps.r0 = u.x; ps.n = u.y;
       break;
@@ -673,7 +686,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int nbr = pass_rows<WT>(dm.H, 16), br = task.z * kMaxNb + p * nbr;
       if (br >= bend) return false;
       const int r0 = tile * 16;
-      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_router), nullptr, r0, 0, dm.H, 0};
+      ps.rw = GemvRows{ROWS_CONTIG, ldp(&Lp->w_router), nullptr, r0, 0, dm.H, 0, 0, 0};
       ps.in = GemvIn{h1_of(a, c.l) + (size_t)br * dm.H, dm.H, nullptr, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
       ps.R = min(16, dm.E - r0); ps.K = dm.H; ps.kfull = dm.H; ps.nb = min(nbr, bend - br);
       ps.epi = E_ROUTER; ps.b0 = br; ps.r0 = r0; ps.n = ps.R;
@@ -712,7 +725,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       const int f0 = (int)((long)sl * dm.Fe / sg), Rh = (int)((long)(sl + 1) * dm.Fe / sg) - f0;
       const size_t eo = (size_t)e * dm.Fe * dm.H;
       ps.rw = GemvRows{ROWS_PAIR, reinterpret_cast<const WT*>(ldp(&Lp->w_exp_gate)) + eo,
-                       reinterpret_cast<const WT*>(ldp(&Lp->w_exp_up)) + eo, f0, Rh, dm.H, 0};
+                       reinterpret_cast<const WT*>(ldp(&Lp->w_exp_up)) + eo, f0, Rh, dm.H, 0, 0, 0};
       // the tile's rows: its routed tokens' FFN inputs (RMSNorm2 of h1), gathered
       ps.in = GemvIn{h1_of(a, c.l), dm.H, a.ws.sorted_tok + row0, ldp(&Lp->ffn_norm), 1, dm.eps, -1};
       ps.R = 2 * Rh; ps.K = dm.H; ps.kfull = dm.H; ps.nb = min(kMoeBM, ldsu(a.ws.exp_indptr + e + 1) - row0);
@@ -866,7 +879,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
         if (a.per_op) {   // the projection alone: RoPE and the append are ops of their own
           for (int idx = t0; idx < ni; idx += nt) {
             const int m = idx / ps.n, ju = idx - m * ps.n;
-            const int unit = ps.r0 + ju, h = unit / half, i = unit - h * half;
+            const int unit = qkv_unit(dm, ps.r0 + ju), h = unit / half, i = unit - h * half;
             float* dst = qkv_of(a, c.l) + (size_t)(b0 + m) * qkv_dim + h * dm.d + i;
             stc(dst, ys[(2 * ju) * nb + m]);
             stc(dst + half, ys[(2 * ju + 1) * nb + m]);
@@ -884,7 +897,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int idx = base + t0 + nt * u, m = idx / ps.n, ju = idx - m * ps.n;
-          const int unit = ps.r0 + ju, h = unit / half, i = unit - h * half;
+          const int unit = qkv_unit(dm, ps.r0 + ju), h = unit / half, i = unit - h * half;
           const int pos = __shfl(posl, m, 64);
           cs[u] = ldk2(rrs, idx < ni && h < dm.Hq + dm.Hkv ? (pos * half + i) * 8 : kNoRecord);
         }
@@ -893,7 +906,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
           const int idx = base + t0 + nt * u;
           if (idx >= ni) break;
           const int m = idx / ps.n, ju = idx - m * ps.n;
-          const int unit = ps.r0 + ju, h = unit / half, i = unit - h * half;
+          const int unit = qkv_unit(dm, ps.r0 + ju), h = unit / half, i = unit - h * half;
           const float r = c.s.rstd[m];
           float y1 = ys[(2 * ju) * nb + m] * r, y2 = ys[(2 * ju + 1) * nb + m] * r;
           const int bb = b0 + m, pos = __shfl(posl, m, 64);
@@ -1044,12 +1057,12 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, int b, int g, int ci, 
     }
   }
   if (tid == 0) c.s.tclk[5] = (uint32_t)now_ticks();   // outputs issued
-  if (a.attn_merge_o || a.per_op) {   // the O-projection (or the per-op merge) merges the partials
-    wg_notify(ev_ptr(a, c.l, EV_ATTN), tix & (kSubs - 1));
-    return true;
-  }
-  if (nc == 1) {
-    wg_notify(ev_ptr(a, c.l, EV_ATTN), (b * dm.Hkv + g) & (kSubs - 1));
+  // the event of (block of b, group g): flat, counts the chunk tasks that
+  // notify (the O-projection, or the per-op merge, merges the partials) or
+  // one notify per request
+  int* aev = ev_at(a, c.l, EV_ATTN, ev_blk_of(a, b), g);
+  if (a.attn_merge_o || a.per_op || nc == 1) {
+    wg_notify(aev, -1);
     return true;
   }
   // the last chunk task of (b, g) to finish merges the partials
@@ -1088,7 +1101,7 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, int b, int g, int ci, 
       }
       stc4(orr, (h * D + e0) * 4, A / Ls);
     }
-    wg_notify(ev_ptr(a, c.l, EV_ATTN), (b * dm.Hkv + g) & (kSubs - 1));
+    wg_notify(aev, -1);
   }
   __syncthreads();
   return true;
@@ -1119,7 +1132,7 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
     kr[it] = ldg16(Kb + (size_t)p * D);
     vr[it] = ldg16(Vb + (size_t)p * D);
   }
-  if (!ctx_wait(c, wev)) return false;
+  if (!ctx_wait(c, wev, 0)) return false;   // flat counter: QKV[block][group]
 
   float* sw = reinterpret_cast<float*>(c.s.xs);     // [kWaves][G][DP] per-wave partials
   float* qs = sw + kWaves * 8 * DP;                  // [G][D] this group's rotated queries
@@ -1237,7 +1250,7 @@ __device__ __forceinline__ bool task_attn_mm(const Ctx& c, int b, int g, int ci,
 #pragma unroll
     for (int i = 0; i < 16; ++i) vr[t][i] = ldg4_nt(Vb + (size_t)min(tb + i, pmax) * D + 2 * lane);
   }
-  if (!ctx_wait(c, wev)) return false;
+  if (!ctx_wait(c, wev, 0)) return false;   // flat counter: QKV[block][group]
 
   // A operand: query head j of the group (zero beyond G), q * log2(e) / sqrt(d) as hi + lo
   const auto qr = rsrc_n(qkv_of(a, c.l) + (size_t)b * qkv_dim, qkv_dim * 4);
@@ -1409,7 +1422,7 @@ __device__ __forceinline__ bool task_attn_stream(const Ctx& c, int b, int g, int
   AttnTile t0, t1;
   if (ntw > 0) load(t0, 0);
   if (ntw > 1) load(t1, 1);
-  if (!ctx_wait(c, wev)) return false;
+  if (!ctx_wait(c, wev, 0)) return false;   // flat counter: QKV[block][group]
 
   // A operand: query head j of the group (zero beyond G), q * log2(e) / sqrt(d) as hi + lo
   const auto qr = rsrc_n(qkv_of(a, c.l) + (size_t)b * qkv_dim, qkv_dim * 4);
@@ -1803,7 +1816,7 @@ __device__ __forceinline__ bool task_route(const Ctx& c, const int* wev) {
       if (a.rout.sorted_slot) *gp(a.rout.sorted_slot + i) = ldci(a.ws.sorted_slot + i);
     }
   }
-  wg_notify(ev_ptr(a, c.l, EV_ROUTE), -1);
+  wg_notify(ev_at(a, c.l, EV_ROUTE), -1);
   return true;
 }
 
@@ -1979,6 +1992,7 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
   const int wg = blockIdx.x, wave = wave_id();
   const Lds s = lds_layout(lds_raw);
   if (threadIdx.x == 0) *s.flag = (ldci(a.ws.err) == 0);
+  if (threadIdx.x < 8) s.seen[threadIdx.x] = 0;
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*s.flag)) return;
   const int n = ldku(a.ws.qlen + wg);
@@ -2000,23 +2014,47 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
   auto barrier_to = [&](int bi) -> bool {
     if (arrived >= bi) return true;
     for (; arrived < bi; ++arrived) wg_notify(a.ws.bar + (size_t)arrived * kEvInts, wg & (kSubs - 1));
-    return ctx_wait(Ctx{a, l, wg, s}, a.ws.bar + (size_t)(bi - 1) * kEvInts);
+    return ctx_wait(Ctx{a, l, wg, s}, a.ws.bar + (size_t)(bi - 1) * kEvInts, kSubs);
   };
-  unsigned passed = 0;   // events of layer l (bit e) and l - 1 (bit 16 + e) this workgroup has seen fired
-  // the event a task type waits on, or nullptr once this workgroup has seen it at zero
-  auto need = [&](int e, int el) -> const int* {
-    const unsigned bit = 1u << (e + (el != l ? 16 : 0));
-    if (passed & bit) return nullptr;
-    passed |= bit;
-    return ev_ptr(a, el, e);
+  // The events this workgroup has seen fired, one per wait kind (s.seen[k] =
+  // key of the last event waited on, key = offset + 1 + (counters - 1) << 27),
+  // so a later task that waits on the same event does not poll it again.
+  // Every wave records the key after its task's wait and reads it before the
+  // next task, so all waves agree.
+  enum : int { W_QKV = 0, W_ATTN, W_O, W_GU, W_DOWN, W_ROUTER, W_ROUTE, W_MDOWN };
+  auto key_of = [](long off, int subs) { return (int)off + 1 + (subs << 27); };
+  int pend_kind = -1, pend_key = 0;   // the wait the current task performs (recorded once it has)
+  // the event (offset `off`, counters off .. off + subs kCtr) a task waits on,
+  // or nullptr when this workgroup has already seen it fired
+  auto need = [&](int kind, long off, int subs) -> const int* {
+    const int key = key_of(off, subs);
+    if (s.seen[kind] == key) return nullptr;
+    pend_kind = kind;
+    pend_key = key;
+    return a.ws.ev + off;
   };
-  // whether an earlier task of this workgroup already waited on the event
-  auto seen = [&](int e, int el) -> bool { return (passed & (1u << (e + (el != l ? 16 : 0)))) != 0; };
+  auto seen_done = [&]() {
+    if (pend_kind >= 0) s.seen[pend_kind] = pend_key;
+    pend_kind = -1;
+  };
+  // whether this workgroup has seen event `off` fired
+  auto seen = [&](int kind, long off, int subs) -> bool { return s.seen[kind] == key_of(off, subs); };
+  // the wait of a task (pmk_sched.h: task_wait) as an event pointer and its
+  // extra counters, nullptr when already seen fired
+  auto wait_of = [&](int type, int y, int z, int w, int& subs) -> const int* {
+    const EvWait wt = task_wait(dm, ldku(&a.nblk), ldku(&a.geo[1].kr), type, y, z, w, l);
+    subs = kSubs;
+    if (wt.kind < 0) return nullptr;
+    if (ev_flat(wt.kind)) subs = wt.n - 1;
+    const int kind = wt.kind == EV_QKV ? W_QKV : wt.kind == EV_ATTN ? W_ATTN : wt.kind == EV_O ? W_O
+                   : wt.kind == EV_GU ? W_GU : wt.kind == EV_DOWN ? W_DOWN : wt.kind == EV_ROUTER ? W_ROUTER
+                   : wt.kind == EV_ROUTE ? W_ROUTE : W_MDOWN;
+    return need(kind, ev_off(dm, wt.layer, wt.kind, wt.blk, wt.g0), subs);
+  };
   auto advance = [&]() {
     if (++t == n) {
       t = 0;
       ++l;
-      passed = 0;
     }
   };
   auto record = [&](int type, uint32_t t_begin) {
@@ -2052,12 +2090,16 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
         const uint32_t t_begin = begin();
         bool ok = true;
         switch (task.x) {
-          case T_ATTN:
-            ok = attn_dispatch<WT>(c, task.y, task.z, task.w, tix, need(EV_QKV, l));
+          case T_ATTN: {   // (b, g): waits on the QKV tiles of its block and group alone
+            int subs;
+            const int* wev = wait_of(T_ATTN, task.y, task.z, task.w, subs);
+            ok = attn_dispatch<WT>(c, task.y, task.z, task.w, tix, wev);
             break;
+          }
           case T_ATTS: {   // x: piece << 8 | pieces << 20, y: b | g << 16, z/w: positions [z, w)
             const int b = task.y & 0xffff, g = task.y >> 16, piece = tix & 0xfff, np = tix >> 12;
-            const int* wev = need(EV_QKV, l);
+            int subs;
+            const int* wev = wait_of(T_ATTS, task.y, task.z, task.w, subs);
             if constexpr (sizeof(WT) == 2) {
               ok = dm.Hq / dm.Hkv <= 4 ? task_attn_stream<4>(c, b, g, task.z, task.w, piece, np, wev)
                                        : task_attn_stream<8>(c, b, g, task.z, task.w, piece, np, wev);
@@ -2065,13 +2107,17 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
             break;
           }
           case T_ROUTE:
-            if constexpr ((KP & 3) != KP_DENSE)
-              ok = dm.E <= 128 ? task_route<16>(c, need(EV_ROUTER, l)) : task_route<64>(c, need(EV_ROUTER, l));
+            if constexpr ((KP & 3) != KP_DENSE) {
+              int subs;
+              const int* wev = wait_of(T_ROUTE, 0, 0, 0, subs);
+              ok = dm.E <= 128 ? task_route<16>(c, wev) : task_route<64>(c, wev);
+            }
             break;
           case T_COMBINE:
             if constexpr ((KP & 3) != KP_DENSE) {
-              ok = task_combine(c, need(EV_MDOWN, l));
-              if (ok) wg_notify(ev_ptr(a, l, EV_DOWN), wg & (kSubs - 1));
+              int subs;
+              ok = task_combine(c, wait_of(T_COMBINE, 0, 0, 0, subs));
+              if (ok) wg_notify(ev_at(a, l, EV_DOWN), wg & (kSubs - 1));
             }
             break;
           case T_NORM1: case T_NORM2: case T_ROPE: case T_APPEND: case T_MERGE:
@@ -2089,6 +2135,7 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
           default: break;
         }
         if (!ok) return;
+        seen_done();
         record(task.x, t_begin);
         advance();
         continue;
@@ -2098,17 +2145,24 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
         const Ctx c{a, l, wg, s};
         const uint32_t t_begin = begin();
         bool ok = true;
-        int notify = -1;   // event this task notifies through sub-counter (wg % kSubs)
+        int notify = -1;   // event this task notifies
         const int* wev = nullptr;
+        int wsubs = kSubs;
+        // dense tasks: y = row tile, z = K slice, w = batch block; their block's events
+        const int eb = (task.x == T_QKV || task.x == T_O || task.x == T_GU || task.x == T_DOWN)
+                           ? (ldku(&a.nblk) > 1 ? task.w : 0) : 0;
+        // its wait (pmk_sched.h: task_wait) and the event it notifies
+        if (task.x == T_MGU) {   // the share's size is known once routing is done
+          ok = ctx_wait(c, wait_of(T_MGU, 0, 0, 0, wsubs), kSubs);
+        } else if (task.x != T_MDOWN) {
+          wev = wait_of(task.x, task.y, task.z, task.w, wsubs);
+        }
         switch (task.x) {
-          case T_QKV: wev = l > 0 ? need(EV_DOWN, l - 1) : nullptr; notify = EV_QKV; break;
-          case T_O: wev = need(EV_ATTN, l); notify = EV_O; break;
-          case T_GU: wev = need(EV_O, l); notify = EV_GU; break;
-          case T_DOWN: wev = need(EV_GU, l); notify = EV_DOWN; break;
-          case T_ROUTER: wev = need(EV_O, l); notify = EV_ROUTER; break;
-          case T_MGU:   // the share's size is known once routing is done
-            ok = ctx_wait(c, need(EV_ROUTE, l));
-            break;
+          case T_QKV: notify = EV_QKV; break;
+          case T_O: notify = EV_O; break;
+          case T_GU: notify = EV_GU; break;
+          case T_DOWN: notify = EV_DOWN; break;
+          case T_ROUTER: notify = EV_ROUTER; break;
           case T_MDOWN: notify = EV_MDOWN; break;
           default: break;
         }
@@ -2117,17 +2171,26 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
         for (int p = 0; ok; ++p) {
           Pass ps;
           if (!make_pass<WT, KP>(c, task, p, wev, ps)) break;
+          if (ps.wev == wev) ps.wsubs = wsubs;
           // the residual of O (the layer input) / down (h1) is final once this
           // workgroup has seen the event that produced it, or one that fires
           // only after it (every QKV tile waits for the previous layer's down
           // stage): load it before waiting
           float resid[kResid];
+          // (block eb of layer l's input: its down event of layer l - 1, or a QKV
+          // event of its block, whose tiles waited on that down event)
+          auto qkv_seen = [&]() {
+            const int k = s.seen[W_QKV] - 1;
+            return k >= ev_off(dm, l, EV_QKV, eb, 0) && k < ev_off(dm, l, EV_QKV, eb, dm.Hkv);
+          };
           const bool early = ps.R * ps.nb <= kYsFloats &&
-                             ((ps.epi == E_O && (l == 0 || seen(EV_DOWN, l - 1) || seen(EV_QKV, l))) ||
-                              (ps.epi == E_DOWN && seen(EV_O, l)));
+                             ((ps.epi == E_O && (l == 0 || seen(W_DOWN, ev_off(dm, l - 1, EV_DOWN, eb), kSubs) ||
+                                                 qkv_seen())) ||
+                              (ps.epi == E_DOWN && seen(W_O, ev_off(dm, l, EV_O, eb), kSubs)));
           if (early) load_resid(a, ps, resid);
           ok = gemv_any<WT, (KP & KP_TILES) != 0>(c, ps.rw, ps.R, ps.K, ps.in, ps.nb, ps.wev, ps.wsubs, ps.ys);
           if (!ok) break;
+          seen_done();
           if (ps.ks > 1 && !reduce_slices(c, ps)) {
             done = false;
             break;
@@ -2145,14 +2208,26 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
           if (threadIdx.x == 0) s.tclk[5] = (uint32_t)now_ticks();
         }
         if (!ok) return;
-        // dense stages notify per row tile (by the last slice of a split tile), the others per workgroup
+        // dense stages notify per row tile (by the last slice of a split tile),
+        // the others per workgroup; QKV tiles notify the flat counter of each
+        // KV group their units cover, in their block
         const bool dense = task.x == T_QKV || task.x == T_O || task.x == T_GU || task.x == T_DOWN;
         const int sub = (dense ? task.y : wg) & (kSubs - 1);
-        if (done && notify >= 0) {
-          if (split_last)
-            wg_notify(ev_ptr(a, l, notify), sub);
-          else if (wave == 0)
-            wave_notify(ev_ptr(a, l, notify), sub);
+        if (done && notify >= 0 && (split_last || wave == 0)) {
+          if (split_last) {
+            vm_drain();
+            __syncthreads();
+          } else {
+            vm_drain();
+          }
+          if ((threadIdx.x & (split_last ? kBlock - 1 : 63)) == 0) {
+            if (notify == EV_QKV) {
+              const int2 gr = qkv_tile_groups(dm, ldku(&a.geo[0].tiles), task.y);
+              for (int g = gr.x; g <= gr.y; ++g) (void)atomic_add_relaxed(ev_at(a, l, EV_QKV, eb, g), -1);
+            } else {
+              (void)atomic_add_relaxed(ev_slot(ev_at(a, l, notify, dense ? eb : 0), sub), -1);
+            }
+          }
         }
         record(task.x, t_begin);
         advance();
@@ -2171,40 +2246,11 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
 // ---------------------------------------------------------------------------
 // The per-step prologue: validate lengths, build queues, arm events.
 // ---------------------------------------------------------------------------
-// Number of the first `tiles` tasks of a stage (task t runs on workgroup
-// t % grid and notifies sub-counter (t % grid) & (kSubs - 1)) that notify
-// sub-counter x.
-__device__ __forceinline__ int sub_count(int tiles, int grid, int x) {
-  auto below = [x](int n) { return n > x ? (n - x + kSubs - 1) / kSubs : 0; };   // w < n with w % kSubs == x
-  return (tiles / grid) * below(grid) + below(tiles % grid);
-}
-
-// Arm an event whose `tiles` notifying tasks run on workgroups t % grid and
-// notify sub-counter (t % grid) % kSubs; [0] stays at zero.
-__device__ __forceinline__ void arm_tiles(int* ev, int tiles, int grid) {
-  ev[0] = 0;
-  for (int x = 0; x < kSubs; ++x) ev[(1 + x) * kCtr] = sub_count(tiles, grid, x);
-}
-
-// Arm an event with n notifiers indexed i that notify sub-counter i % kSubs,
-// each `mult` times.
-__device__ __forceinline__ void arm_indexed(int* ev, int n, int mult = 1) {
-  ev[0] = 0;
-  for (int x = 0; x < kSubs; ++x) ev[(1 + x) * kCtr] = (n > x ? (n - x + kSubs - 1) / kSubs : 0) * mult;
-}
-
-// Arm an event on counter [0] alone.
-__device__ __forceinline__ void arm_flat(int* ev, int n) {
-  ev[0] = n;
-  for (int x = 0; x < kSubs; ++x) ev[(1 + x) * kCtr] = 0;
-}
-
 __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   const Dims& dm = a.dm;
   const int tid = threadIdx.x, B = a.batch, G = dm.grid;
   __shared__ int bad;
-  __shared__ int total_attn, merge_s, qkv_tiles_s, attn_wg0_s, stream_s, share_s;
-  __shared__ StageGeo geo_s[4];
+  __shared__ Plan plan;
   __shared__ int cb[kMaxBatchAll + 1];
   __shared__ int sl[kMaxBatchAll];   // the requests' lengths, read once
   StepArgs* copy = reinterpret_cast<StepArgs*>(a.ws.args);
@@ -2234,200 +2280,67 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   }
   if (tid == 0) {
     a.ws.err[16] = 0;   // abort flag
-    // attention chunk. Small batches whose O-projection inputs fit one
-    // merging pass (see stage_attn_merge) take the smallest chunk that keeps
-    // every request within 8 chunks and let the O-projection merge the
-    // partials; otherwise the largest of 256/128/64 positions that still gives
-    // every workgroup a task, with the last chunk of a request merging.
-    int ck = kMaxChunk, merge = 0;
-    auto max_nc = [&](int c) {
-      int mx = 0;
-      for (int b = 0; b < B; ++b) mx = max(mx, (sl[b] + c) / c);
-      return mx;
-    };
-    if (B <= dm.merge_b && !a.per_op) {
-      int c = kMinChunk;
-      while (c < kMaxChunk && max_nc(c) > kMergeChunks) c <<= 1;
-      if (max_nc(c) <= kMergeChunks) { ck = c; merge = 1; }
-    }
-    if (!merge) {
-      while (ck > kMinChunk) {
-        long tasks = 0;
-        for (int b = 0; b < B; ++b) tasks += (sl[b] + ck) / ck;
-        if (tasks * dm.Hkv >= G) break;
-        ck >>= 1;
-      }
-    }
-    copy->attn_merge_o = merge;
-    merge_s = merge;
-    // Without the O-projection merge, the matrix-core attention streams its
-    // positions: all (request, KV head) position ranges, laid end to end,
-    // are cut into equal shares, one per workgroup (at least 64 positions),
-    // and each piece of a range within a share is a task. cb then holds the
-    // prefix sum of the requests' positions (S + 1), else of their chunks.
-    const int stream = !merge && dm.attn_mm && !a.per_op;   // per-op: chunk partials, merged by an op
-    stream_s = stream;
-    int acc = 0;
-    for (int b = 0; b < B; ++b) {
-      cb[b] = acc;
-      acc += stream ? sl[b] + 1 : (sl[b] + ck) / ck;   // ceil((S + 1) / ck)
-    }
-    cb[B] = acc;
-    total_attn = acc * dm.Hkv;
-    // streamed shares: every (request, KV head) range is laid out behind a
-    // lead of kPieceCost positions (what a piece costs beyond its positions),
-    // so that a share that starts a range holds fewer positions
-    const long P = stream ? (long)dm.Hkv * (acc + (long)B * kPieceCost) : (long)acc * dm.Hkv;
-    share_s = max(64, (int)((P + G - 1) / G + 15) / 16 * 16);
-    copy->attn_chunk = ck;
-    // A few attention tasks (at most a quarter of the grid) get workgroups of
-    // their own, the last ones, which hold no QKV or O tile: their task comes
-    // first in the layer, so its KV rows stream in while the QKV tiles run on
-    // the other workgroups, and they go on to gate/up when it is done (an O
-    // tile there would start only after attention and have its whole weight
-    // tile still to load, which held the O event back by ~5 us at batch 1).
-    // Otherwise the attention tasks follow the QKV tiles on every workgroup.
-    const int own = (merge && total_attn <= G / 4 && !a.per_op) ? total_attn : 0;
-    attn_wg0_s = own ? G - own : G;
-    // each dense stage's split (see stage_geo): up to 16 rows, one pass over
-    // K slices that fit the LDS; beyond, the split of 16 rows for every block
-    // of 16 (or, where no split fits, passes of rows over the whole depth)
-    const int K4[4] = {dm.H, dm.Hq * dm.d, dm.H, dm.F};
-    const int U4[4] = {dm.qkv_units, dm.H, dm.F, dm.H};
-    const int R4[4] = {2, 1, 2, 1};
-    for (int st = 0; st < 4; ++st) {
-      const int avail = st <= 1 ? G - own : G;
-      // more than 16 rows: the split of 16, and every 16-row block its own tasks
-      StageGeo g = stage_geo(K4[st], U4[st], R4[st], min(B, kMaxNb), avail, dm.kstep, dm.xpad);
-      if (B > kMaxNb && g.ks) g.blk = (B + kMaxNb - 1) / kMaxNb;
-      if (g.ks == 0) g = StageGeo{1, min(avail, U4[st]), K4[st], 1};
-      geo_s[st] = g;
-      copy->geo[st] = g;
-    }
-    qkv_tiles_s = geo_s[0].tiles;
-    copy->qkv_tiles = qkv_tiles_s;
+    plan = plan_step(dm, B, sl, cb, a.per_op);
+    copy->attn_merge_o = plan.merge;
+    copy->attn_chunk = plan.ck;
+    for (int st = 0; st < 4; ++st) copy->geo[st] = plan.geo[st];
+    copy->qkv_tiles = plan.geo[0].tiles;
+    copy->nblk = plan.nblk;
   }
   __syncthreads();
-  const int router_tasks = dm.moe ? dm.router_tiles * ((B + kMaxNb - 1) / kMaxNb) : 0;
-  // queues: stage order QKV, attention, O, then gate/up, down (dense) or
-  // router, route, grouped gate/up, grouped down, combine (MoE)
+  // every workgroup's queue (pmk_sched.h: build_queue)
   for (int w = tid; w < G; w += blockDim.x) {
     int4* q = a.ws.queue + (size_t)w * dm.max_queue;
     int n = 0;
-    auto push = [&](int4 v) {
+    build_queue(dm, plan, cb, w, [&](int4 v) {
       if (n < dm.max_queue) q[n] = v;
       ++n;
-    };
-    const int aw0 = attn_wg0_s;
-    // task i of a dense stage: row tile i / ks, K slice i % ks, on workgroup
-    // i % G. In batch blocks, the blocks of one (tile, slice) go to
-    // workgroups 8 apart, which share an L2 (one XCD), so that they stream the
-    // same weights together: groups of 8 (tile, slice) pairs, each group's
-    // blocks one after another.
-    auto stage_tasks = [&](int type, int st) {
-      const StageGeo g = geo_s[st];
-      const int TS = g.tiles * g.ks;
-      if (g.blk <= 1) {
-        for (int i = w; i < TS; i += G) push(make_int4(type, i / g.ks, i % g.ks, 0));
-        return;
-      }
-      const int per = 8 * g.blk;
-      for (int i = w; i < (TS + 7) / 8 * per; i += G) {
-        const int grp = i / per, r = i - grp * per, ts = grp * 8 + (r & 7);
-        if (ts < TS) push(make_int4(type, ts / g.ks, ts % g.ks, r >> 3));
-      }
-    };
-    if (a.per_op) push(make_int4(T_NORM1, 0, 0, 0));
-    stage_tasks(T_QKV, 0);
-    if (a.per_op) {
-      push(make_int4(T_ROPE, 0, 0, 0));
-      push(make_int4(T_APPEND, 0, 0, 0));
-    }
-    if (stream_s) {   // this workgroup's share of the laid-out ranges
-      // range (b, g) spans [seg0, seg0 + kPieceCost + S_b + 1): its lead, then its positions
-      auto start = [&](int b) { return (long)dm.Hkv * (cb[b] + (long)b * kPieceCost); };
-      const long share = share_s, hi = min((long)(w + 1) * share, start(B));
-      for (long pos = (long)w * share; pos < hi;) {
-        int lo = 0, up = B;   // request b: start(b) <= pos < start(b + 1)
-        while (up - lo > 1) {
-          const int mid = (lo + up) >> 1;
-          if (start(mid) <= pos) lo = mid; else up = mid;
-        }
-        const int len = cb[lo + 1] - cb[lo], span = len + kPieceCost;
-        const int g = (int)((pos - start(lo)) / span);
-        const long seg0 = start(lo) + (long)g * span, r0 = seg0 + kPieceCost, seg1 = seg0 + span;
-        const long e = min(hi, seg1), p0 = max(pos, r0);
-        if (e > p0) {
-          // pieces of a range are cut at multiples of the share: this is piece
-          // w - r0 / share of (seg1 - 1) / share - r0 / share + 1
-          const int piece = w - (int)(r0 / share), np = (int)((seg1 - 1) / share - r0 / share) + 1;
-          push(make_int4(T_ATTS | (piece << 8) | (np << 20), lo | (g << 16), (int)(p0 - r0), (int)(e - r0)));
-        }
-        pos = e;
-      }
-    }
-    for (int i = aw0 < G ? w - aw0 : w; !stream_s && i >= 0 && i < total_attn; i += (aw0 < G ? total_attn : G)) {
-      int lo = 0, hi = B;   // find b: Hkv*cb[b] <= i < Hkv*cb[b+1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (dm.Hkv * cb[mid] <= i) lo = mid; else hi = mid;
-      }
-      const int r = i - dm.Hkv * cb[lo], nc = cb[lo + 1] - cb[lo];
-      push(make_int4(T_ATTN | (i << 8), lo, r / nc, r % nc));
-    }
-    if (a.per_op) push(make_int4(T_MERGE, 0, 0, 0));
-    stage_tasks(T_O, 1);
-    if (a.per_op) push(make_int4(T_NORM2, 0, 0, 0));
-    if (!dm.moe) {
-      stage_tasks(T_GU, 2);
-      stage_tasks(T_DOWN, 3);
-    } else {
-      for (int i = w; i < router_tasks; i += G) push(make_int4(T_ROUTER, i % dm.router_tiles, i / dm.router_tiles, 0));
-      if (w == G - 1) push(make_int4(T_ROUTE, 0, 0, 0));
-      push(make_int4(T_MGU, 0, 0, 0));
-      push(make_int4(T_MDOWN, 0, 0, 0));
-      push(make_int4(T_COMBINE, 0, 0, 0));
-    }
+    });
     a.ws.qlen[w] = n <= dm.max_queue ? n : 0;
     if (n > dm.max_queue) atomicOr(&bad, 4);
   }
-  // events of every layer
-  for (int idx = tid; idx < dm.L * EV_COUNT; idx += blockDim.x) {
-    const int e = idx % EV_COUNT;
-    int* ev = a.ws.ev + (size_t)idx * kEvInts;
-    switch (e) {
-      // dense stages: one notifier per row tile (and batch block), on sub-counter tile % kSubs
-      case EV_QKV: arm_indexed(ev, geo_s[0].tiles, geo_s[0].blk); break;
-      // one notifier per chunk task (partials merged by the O-projection), or per (request, KV head)
-      case EV_ATTN: arm_indexed(ev, (merge_s || a.per_op) ? total_attn : B * dm.Hkv); break;
-      case EV_O: arm_indexed(ev, geo_s[1].tiles, geo_s[1].blk); break;
-      case EV_GU: arm_indexed(ev, dm.moe ? 0 : geo_s[2].tiles, geo_s[2].blk); break;
-      case EV_DOWN:   // MoE: one combine slot per workgroup
-        if (dm.moe) arm_tiles(ev, G, G); else arm_indexed(ev, geo_s[3].tiles, geo_s[3].blk);
-        break;
-      case EV_ROUTER: arm_tiles(ev, router_tasks, G); break;
-      case EV_ROUTE: arm_flat(ev, dm.moe ? 1 : 0); break;
-      case EV_MDOWN: arm_tiles(ev, dm.moe ? G : 0, G); break;
-      default: arm_flat(ev, 0); break;
+  // every counter of every layer armed with its count (pmk_sched.h: ev_count).
+  // Per layer: QKV and ATTN flat counters of the blocks in use, the O, GU and
+  // DOWN events of those blocks, and ROUTER, ROUTE, MDOWN.
+  const int nb = plan.nblk, H = dm.Hkv, per_layer = 2 * nb * H + (3 * nb + 3) * (1 + kSubs);
+  for (int idx = tid; idx < dm.L * per_layer; idx += blockDim.x) {
+    const int l = idx / per_layer;
+    int r = idx - l * per_layer;
+    int kind, blk = 0, g = 0, sub = 0;
+    if (r < 2 * nb * H) {
+      kind = r < nb * H ? EV_QKV : EV_ATTN;
+      r %= nb * H;
+      blk = r / H;
+      g = r - blk * H;
+    } else {
+      r -= 2 * nb * H;
+      const int e = r / (1 + kSubs);
+      sub = r - e * (1 + kSubs);
+      if (e < 3 * nb) {
+        kind = e < nb ? EV_O : e < 2 * nb ? EV_GU : EV_DOWN;
+        blk = e % nb;
+      } else {
+        kind = e == 3 * nb ? EV_ROUTER : e == 3 * nb + 1 ? EV_ROUTE : EV_MDOWN;
+      }
     }
+    a.ws.ev[ev_off(dm, l, kind, blk, g) + sub * kCtr] = ev_count(dm, plan, cb, kind, blk, g, sub);
   }
   for (int idx = tid; idx < 4 * G * ((B + kMaxNb - 1) / kMaxNb); idx += blockDim.x) {
     const int used = G * ((B + kMaxNb - 1) / kMaxNb), st = idx / used;   // (block, tile) records of each stage
     a.ws.tctr[((size_t)st * dm.tctr_stride + idx - st * used) * kCtr] = 0;
   }
   if (a.barrier)   // every workgroup arrives at every stage barrier
-    for (int idx = tid; idx < dm.L * kMaxStages; idx += blockDim.x) arm_tiles(a.ws.bar + (size_t)idx * kEvInts, G, G);
+    for (int idx = tid; idx < dm.L * kMaxStages; idx += blockDim.x) {
+      int* ev = a.ws.bar + (size_t)idx * kEvInts;
+      ev[0] = 0;
+      for (int x = 0; x < kSubs; ++x) ev[(1 + x) * kCtr] = sub_tiles(G, G, x);
+    }
   if (a.trace)
     for (int w = tid; w < G; w += blockDim.x) a.trace[(size_t)w * a.trace_cap * 8] = 0;
   // attention merge counters: the pieces (streamed) or chunks of each (request, KV head)
   for (int idx = tid; idx < dm.L * B * dm.Hkv; idx += blockDim.x) {
     const int l = idx / (B * dm.Hkv), rem = idx - l * B * dm.Hkv, b = rem / dm.Hkv, g = rem - b * dm.Hkv;
-    int n = cb[b + 1] - cb[b];
-    if (stream_s) {   // the workgroups whose shares meet the range's positions
-      const long r0 = (long)dm.Hkv * (cb[b] + (long)b * kPieceCost) + (long)g * (n + kPieceCost) + kPieceCost;
-      n = (int)((r0 + n - 1) / share_s - r0 / share_s) + 1;
-    }
-    a.ws.mctr[(((size_t)l * dm.max_batch + b) * dm.Hkv + g) * kCtr] = n;
+    a.ws.mctr[(((size_t)l * dm.max_batch + b) * dm.Hkv + g) * kCtr] = attn_pieces(dm, plan, cb, b, g);
   }
   __syncthreads();
   if (tid == 0 && (bad & 4)) {
