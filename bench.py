@@ -215,7 +215,7 @@ def run_timed(model, hid_in, kv, steps_lens, K, W, flush=None):
     return total_ms, step_ms, main_ms / timed_steps, host_us
 
 
-def batch_sweep(w, layers, batches, K, W, dev) -> list:
+def batch_sweep(w, layers, batches, K, W, dev, events="tile") -> list:
     """The 8B-shaped stack at each batch with ragged lengths uniform on
     [512, 8192] (seeded per batch), one handle and one cache for all batches
     (requests 0..B-1 of a max_batch cache; every request's slots are filled
@@ -232,6 +232,7 @@ def batch_sweep(w, layers, batches, K, W, dev) -> list:
     mb = max(batches)
     kv = synth.make_kv_cache(sw, mb, max_seq, device=dev, n_layers=w.n_layers)
     model = DecodeModel.from_workload(w, layers, mb, max_seq, weight_layout="tiles", pack=False)
+    model.set_event_granularity(events)
     rows = []
     for B in batches:
         hid = torch.stack([synth.make_hidden(sw, B, i, device=dev) for i in range(n)])
@@ -297,6 +298,9 @@ def main():
                     "non-temporally; auto: tiles for bfloat16 workloads")
     ap.add_argument("--trace", default=None, help="after the timed steps, run one traced step and write a "
                     "per-stage summary of the task trace to this file")
+    ap.add_argument("--events", default="tile", choices=["tile", "group", "stage"],
+                    help="granularity of the dense chain's events: per KV group and batch block (tile, the default), "
+                    "per KV group (group), or one per stage (stage: an ablation of the subset waits)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch sweep (4, 16, 64, 128) that the default "
                     "workload adds to its line")
     ap.add_argument("--sweep-steps", type=int, default=20, help="timed steps per sweep batch")
@@ -383,6 +387,7 @@ def main():
     model = DecodeModel.from_workload(w, layers, B, max_seq, weight_layout=layout, pack=False)
     log(f"weight layout: {layout}")
     model.set_schedule(args.schedule)
+    model.set_event_granularity(args.events)
     if w.n_experts:
         model.set_moe_scheduler(args.moe_scheduler)
     stages_per_layer = 8 if w.n_experts else 5
@@ -454,7 +459,7 @@ def main():
         del kv, hid, steps_lens
         gc.collect()
         torch.cuda.empty_cache()
-        sweep = batch_sweep(w, layers, (4, 16, 64, 128), args.sweep_steps, min(W, 3), dev)
+        sweep = batch_sweep(w, layers, (4, 16, 64, 128), args.sweep_steps, min(W, 3), dev, args.events)
 
     out = {"metric": METRIC, "value": round(B * K / (total_ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
            "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -469,7 +474,7 @@ def main():
                       **({"seq_range": list(args.seq_range)} if args.seq_range is not None else {}),
                       "weights": w.dtype, "kv_cache": w.dtype,
                       "accumulate": "f32", "parallelism": "single GPU", "schedule": args.schedule,
-                      "weight_layout": layout,
+                      "weight_layout": layout, "events": args.events,
                       "host_submit_us_per_step": round(host_us, 1), "cache_flushed": bool(args.flush_cache),
                       **({"moe_scheduler": args.moe_scheduler} if w.n_experts else {}),
                       "launches_per_step": launches},

@@ -278,6 +278,27 @@ int pmk_set_moe_scheduler(pmk_handle* h, int32_t mode);
  * Errors: PMK_ERR_ARG (null handle, negative limit). */
 int pmk_set_watchdog_us(pmk_handle* h, int32_t us);
 
+/* Granularity of the dense chain's events (Event Tensor summary, Core method:
+ * Event Tensor abstraction; Problem and motivation: a kernel boundary makes
+ * every consumer wait for the whole producer stage although it often needs
+ * only part of it):
+ *   PMK_EVENTS_TILE   per tile (the default): the QKV tiles of each KV group
+ *                     and batch block, the attention of each KV group and
+ *                     block, and the O, gate/up and down tiles of each
+ *                     16-row block (batches beyond 16 rows) each have an
+ *                     event; attention (b, g) waits on group g's QKV tiles
+ *                     only, an O task on the attention of the groups its K
+ *                     slice reads, a block's stages on that block's events;
+ *   PMK_EVENTS_GROUP  per KV group, one batch block;
+ *   PMK_EVENTS_STAGE  one event per stage: every attention task waits on all
+ *                     QKV tiles, every O task on all attention.
+ * Same results in every mode (an ablation of the subset waits). Applies to
+ * later calls. Errors: PMK_ERR_ARG (null handle, unknown mode). */
+#define PMK_EVENTS_TILE 0
+#define PMK_EVENTS_GROUP 1
+#define PMK_EVENTS_STAGE 2
+int pmk_set_event_granularity(pmk_handle* h, int32_t mode);
+
 /* Writes a copy of the bfloat16 matrix src [rows][cols] (row-major) into dst
  * in the tile layout that a handle with weight_layout = PMK_TILES reads. The
  * decode step reads each weight matrix once as a stream of 16-row groups

@@ -20,6 +20,9 @@ PMK_ROWS, PMK_TILES = 0, 1
 SCHED_FUSED, SCHED_PER_LAYER, SCHED_PER_STAGE, SCHED_BARRIER, SCHED_PER_OP = 0, 1, 2, 3, 4
 SCHEDULES = {"fused": SCHED_FUSED, "layer": SCHED_PER_LAYER, "stage": SCHED_PER_STAGE, "barrier": SCHED_BARRIER,
              "op": SCHED_PER_OP}
+# pmk_set_event_granularity modes
+EVENTS_TILE, EVENTS_GROUP, EVENTS_STAGE = 0, 1, 2
+EVENT_MODES = {"tile": EVENTS_TILE, "group": EVENTS_GROUP, "stage": EVENTS_STAGE}
 # pmk_set_moe_scheduler modes
 MOE_STATIC, MOE_DYNAMIC = 0, 1
 MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC}
@@ -27,7 +30,7 @@ MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC}
 EXPORTS = ("decode_layer_init", "decode_step", "moe_layer_step", "decode_layer_destroy", "pmk_strerror",
            "pmk_get_device_error", "pmk_query", "pmk_timing_enable", "pmk_timing_read", "pmk_trace_attach",
            "pmk_set_schedule", "pmk_set_moe_scheduler", "pmk_set_watchdog_us", "pmk_pack_weights",
-           "pmk_stream_probe")
+           "pmk_stream_probe", "pmk_set_event_granularity")
 
 i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -106,6 +109,8 @@ def load():
     L.pmk_pack_weights.restype = i32
     L.pmk_stream_probe.argtypes = [vp, ctypes.c_int64, i32, i32, vp, vp, P(ctypes.c_double)]
     L.pmk_stream_probe.restype = i32
+    L.pmk_set_event_granularity.argtypes = [vp, i32]
+    L.pmk_set_event_granularity.restype = i32
     _lib = L
     return L
 

@@ -34,6 +34,7 @@ struct pmk_handle {
   int* err_host = nullptr;   // pinned host-coherent mirror of the device error word
   size_t tused = 0;
   int sched = PMK_SCHED_FUSED;
+  int ev_mode = PMK_EVENTS_TILE;
   int moe_sched = PMK_MOE_STATIC;
 };
 
@@ -61,6 +62,7 @@ int check_desc(const pmk_model_desc* d) {
   if (d->head_dim * elem_bytes(d->dtype) != 256) return PMK_ERR_UNSUPPORTED;
   const int G = d->n_q_heads / d->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return PMK_ERR_UNSUPPORTED;
+  if (d->n_kv_heads > kMaxHkv) return PMK_ERR_UNSUPPORTED;
   if (d->max_batch > kMaxBatchAll) return PMK_ERR_UNSUPPORTED;
   if (d->weight_layout == PMK_TILES) {
     // bfloat16 only; every matrix in whole 16-row groups and 32-column steps
@@ -97,7 +99,7 @@ const char* pmk_strerror(int s) {
     case PMK_ERR_TIMEOUT: return "an event wait exceeded the watchdog; the step was abandoned";
     case PMK_ERR_SEQ: return "a request length is outside [0, max_seq); the step did not run";
     case PMK_ERR_UNSUPPORTED:
-      return "shape not implemented: needs head_dim*sizeof(dtype) == 256, Hq/Hkv in {1,2,4,8}, max_batch <= 1024, "
+      return "shape not implemented: needs head_dim*sizeof(dtype) == 256, Hq/Hkv in {1,2,4,8}, Hkv <= 128, max_batch <= 1024, "
              "GEMV depths that fit one LDS input row, and for MoE E <= 512, top_k <= 8, H and Fe small enough "
              "for 16 staged rows; the tile weight layout needs bfloat16, H, Hq d, F and Fe multiples of 32, "
              "(Hq + 2 Hkv) d and E multiples of 16";
@@ -132,24 +134,17 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
   // fit the LDS (a step may put its few attention tasks on workgroups of their
   // own and the QKV and O tiles on the others, at least three quarters of the
   // grid).
-  // Split-K partials: the largest need over batches of up to 16 rows (records
-  // of whole 16-byte units).
-  const int K4[4] = {dm.H, dm.Hq * dm.d, dm.H, dm.F};
-  const int U4[4] = {dm.qkv_units, dm.H, dm.F, dm.H};
-  const int R4[4] = {2, 1, 2, 1};
-  size_t kpart_floats = 16;
+  // (The split-K record regions are sized in dims_from_desc.)
   for (int st = 0; st < 4; ++st) {
     if (moe && st >= 2) continue;
-    const int tiles_min = std::min(st <= 1 ? G - G / 4 : G, U4[st]);
-    const long row_bytes = 4L * (ceil_div(K4[st], dm.kstep) * dm.kstep + dm.xpad);
-    if (row_bytes + 16 + 4L * ceil_div(U4[st], tiles_min) * R4[st] > kXyBytes) {
+    int K, U, R;
+    stage_dims(dm, st, K, U, R);
+    const int tiles_min = std::min(st <= 1 ? G - G / 4 : G, U);
+    const long row_bytes = 4L * (ceil_div(K, dm.kstep) * dm.kstep + dm.xpad);
+    if (row_bytes + 16 + 4L * ceil_div(U, tiles_min) * R > kXyBytes) {
       delete h;
       return PMK_ERR_UNSUPPORTED;
     }
-    // every batch and every grid share the prologue may choose (QKV and O
-    // give up to a quarter of the grid to attention tasks of their own)
-    kpart_floats = std::max(kpart_floats, (size_t)kpart_need(K4[st], U4[st], R4[st], dm.max_batch, G, st <= 1,
-                                                             dm.kstep, dm.xpad));
   }
   // workspace carving
   const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
@@ -176,7 +171,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
       {(void**)&ws.qlen, (size_t)G * 4},
       {(void**)&ws.err, 64 * 4},
       {(void**)&ws.args, sizeof(StepArgs)},
-      {(void**)&ws.kpart, kpart_floats * 4},
+      {(void**)&ws.kpart, (size_t)dm.kpart_off[4] * 4},
       {(void**)&ws.tctr, (size_t)4 * dm.tctr_stride * kCtr * 4},
       {(void**)&ws.bar, (size_t)dm.L * kMaxStages * kEvInts * 4},
       {(void**)&ws.u, (size_t)dm.max_batch * dm.H * 4},
@@ -303,6 +298,7 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
   a.trace_cap = h->trace_cap;
   a.barrier = h->sched == PMK_SCHED_BARRIER;
   a.per_op = h->sched == PMK_SCHED_PER_OP;
+  a.ev_mode = h->ev_mode;
   a.moe_dyn = h->dm.moe && h->moe_sched == PMK_MOE_DYNAMIC;
   h->last_stream = s;
   if (launch_prologue(a, s) != hipSuccess) return PMK_ERR_DEVICE;
@@ -344,6 +340,12 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
 int pmk_set_moe_scheduler(pmk_handle* h, int32_t mode) {
   if (!h || (mode != PMK_MOE_STATIC && mode != PMK_MOE_DYNAMIC)) return PMK_ERR_ARG;
   h->moe_sched = mode;
+  return PMK_OK;
+}
+
+int pmk_set_event_granularity(pmk_handle* h, int32_t mode) {
+  if (!h || mode < PMK_EVENTS_TILE || mode > PMK_EVENTS_STAGE) return PMK_ERR_ARG;
+  h->ev_mode = mode;
   return PMK_OK;
 }
 

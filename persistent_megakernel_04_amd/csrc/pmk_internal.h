@@ -23,6 +23,7 @@ constexpr int kMaxTopK = 8;
 constexpr int kMaxExperts = 512;
 constexpr int kMaxNb = 16;               // batch rows per GEMV pass (MFMA M)
 constexpr int kMaxBatchAll = 1024;       // largest max_batch (prologue LDS)
+constexpr int kMaxHkv = 128;             // KV heads at most (the prologue's per-group tile counts)
 constexpr int kMaxStages = 8;            // stages of a layer (MoE: QKV, attention, O, router, route, gate/up, down, combine)
 
 // LDS layout (bytes): [xy: a GEMV pass's staged inputs (xs), then its outputs
@@ -157,6 +158,7 @@ struct Dims {
   int tctr_stride;                   // split-K tile counters per stage: grid x batch blocks
   int max_down;                      // MoE: bound on grouped down tasks (row tiles x H slices)
   int wtiles;                        // 1: bfloat16 weights in the tile layout (pmk_pack_weights)
+  long kpart_off[5];                 // split-K records: first float of each dense stage's region; [4] = total
 };
 
 // Device workspace (one allocation, carved by the host).
@@ -178,7 +180,7 @@ struct Workspace {
   int* err;            // [0] error word, [16] abort flag
   int* err_host;       // pinned, host-coherent mirror of the error word (written by the device when set)
   void* args;          // a copy of this step's StepArgs, written by the prologue
-  float* kpart;        // split-K partial sums: [tile][slice][rows nb + 16] of the current stage
+  float* kpart;        // split-K partial sums: per dense stage, [block tiles + tile][slice][rows nb + 16]
   int* tctr;           // [4][tctr_stride][kCtr] per (batch block, row tile): slices done (reset by the last one)
   int* bar;            // [L][kMaxStages][kEvInts]     stage barriers (barrier schedule only)
   // MoE
@@ -220,6 +222,7 @@ struct StepArgs {
   int barrier;                         // 1: the barrier schedule (the prologue arms ws.bar)
   int moe_dyn;                         // 1: grouped expert tasks popped from a per-layer queue
   int per_op;                          // 1: the per-op schedule (norms, RoPE, append, merge as ops of their own)
+  int ev_mode;                         // granularity of the dense chain's events (pmk_sched.h: EvMode)
 };
 
 // Which task paths an instantiation of the persistent kernel carries: all of

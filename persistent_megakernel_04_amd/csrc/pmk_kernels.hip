@@ -793,7 +793,7 @@ __device__ __forceinline__ bool reduce_slices(const Ctx& c, const Pass& ps) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), n = ps.R * ps.nb, rs = ps.rs;
   const bool normed = ps.in.norm != 0;
   const int nrec = n + (normed ? ps.nb : 0), U = (nrec + 3) >> 2;
-  float* part = uptr(a.ws.kpart + (size_t)ps.tile * ps.ks * rs);
+  float* part = uptr(a.ws.kpart + kpart_rec(a.dm, ps.stage, ps.tile, ps.ks, 0, rs));
   const auto prs = rsrc_n(part, ps.ks * rs * 4);
   auto own = [&](int i) -> float { return i < n ? ps.ys[i] : (i < nrec ? c.s.rstd[i - n] : 0.f); };
   for (int u = tid; u < U; u += kBlock)
@@ -1108,7 +1108,7 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, int b, int g, int ci, 
 }
 
 template <typename KT, int HB, int ITS>
-__device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, int tix, const int* wev) {
+__device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, int tix, const int* wev, int wsubs) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   constexpr int EPL = 16 / (int)sizeof(KT);   // elements per lane (16 B)
@@ -1132,7 +1132,7 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
     kr[it] = ldg16(Kb + (size_t)p * D);
     vr[it] = ldg16(Vb + (size_t)p * D);
   }
-  if (!ctx_wait(c, wev, 0)) return false;   // flat counter: QKV[block][group]
+  if (!ctx_wait(c, wev, wsubs)) return false;   // flat counters: QKV[block][group] (all groups: per stage)
 
   float* sw = reinterpret_cast<float*>(c.s.xs);     // [kWaves][G][DP] per-wave partials
   float* qs = sw + kWaves * 8 * DP;                  // [G][D] this group's rotated queries
@@ -1222,7 +1222,7 @@ __device__ __forceinline__ bool task_attn(const Ctx& c, int b, int g, int ci, in
 // probabilities broadcast through LDS, so no cross-lane reduction is needed.
 // GP: query heads rounded up to 4 or 8.
 template <int TW, int GP>
-__device__ __forceinline__ bool task_attn_mm(const Ctx& c, int b, int g, int ci, int tix, const int* wev) {
+__device__ __forceinline__ bool task_attn_mm(const Ctx& c, int b, int g, int ci, int tix, const int* wev, int wsubs) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   typedef MM<uint16_t> T;
@@ -1250,7 +1250,7 @@ __device__ __forceinline__ bool task_attn_mm(const Ctx& c, int b, int g, int ci,
 #pragma unroll
     for (int i = 0; i < 16; ++i) vr[t][i] = ldg4_nt(Vb + (size_t)min(tb + i, pmax) * D + 2 * lane);
   }
-  if (!ctx_wait(c, wev, 0)) return false;   // flat counter: QKV[block][group]
+  if (!ctx_wait(c, wev, wsubs)) return false;   // flat counters: QKV[block][group] (all groups: per stage)
 
   // A operand: query head j of the group (zero beyond G), q * log2(e) / sqrt(d) as hi + lo
   const auto qr = rsrc_n(qkv_of(a, c.l) + (size_t)b * qkv_dim, qkv_dim * 4);
@@ -1397,7 +1397,7 @@ struct AttnTile {
 
 template <int GP>
 __device__ __forceinline__ bool task_attn_stream(const Ctx& c, int b, int g, int p0, int p1, int piece, int npieces,
-                                                 const int* wev) {
+                                                 const int* wev, int wsubs) {
   const StepArgs& a = c.a;
   const Dims& dm = a.dm;
   typedef MM<uint16_t> T;
@@ -1422,7 +1422,7 @@ __device__ __forceinline__ bool task_attn_stream(const Ctx& c, int b, int g, int
   AttnTile t0, t1;
   if (ntw > 0) load(t0, 0);
   if (ntw > 1) load(t1, 1);
-  if (!ctx_wait(c, wev, 0)) return false;   // flat counter: QKV[block][group]
+  if (!ctx_wait(c, wev, wsubs)) return false;   // flat counters: QKV[block][group] (all groups: per stage)
 
   // A operand: query head j of the group (zero beyond G), q * log2(e) / sqrt(d) as hi + lo
   const auto qr = rsrc_n(qkv_of(a, c.l) + (size_t)b * qkv_dim, qkv_dim * 4);
@@ -1563,25 +1563,26 @@ __device__ __forceinline__ bool task_attn_stream(const Ctx& c, int b, int g, int
 }
 
 template <typename KT, int HB>
-__device__ __forceinline__ bool attn_its(const Ctx& c, int b, int g, int ci, int tix, int ck, const int* wev) {
-  if (ck <= 64) return task_attn<KT, HB, 2>(c, b, g, ci, tix, wev);
-  if (ck <= 128) return task_attn<KT, HB, 4>(c, b, g, ci, tix, wev);
+__device__ __forceinline__ bool attn_its(const Ctx& c, int b, int g, int ci, int tix, int ck, const int* wev, int wsubs) {
+  if (ck <= 64) return task_attn<KT, HB, 2>(c, b, g, ci, tix, wev, wsubs);
+  if (ck <= 128) return task_attn<KT, HB, 4>(c, b, g, ci, tix, wev, wsubs);
   // 256-position chunks hold 16 KV rows per lane: two query heads at a time keep them in registers
-  return task_attn<KT, (HB > 2 ? 2 : HB), 8>(c, b, g, ci, tix, wev);
+  return task_attn<KT, (HB > 2 ? 2 : HB), 8>(c, b, g, ci, tix, wev, wsubs);
 }
 
 template <typename KT>
-__device__ __forceinline__ bool attn_dispatch(const Ctx& c, int b, int g, int ci, int tix, const int* wev) {
+__device__ __forceinline__ bool attn_dispatch(const Ctx& c, int b, int g, int ci, int tix, const int* wev, int wsubs) {
   const int G = c.a.dm.Hq / c.a.dm.Hkv, ck = c.a.attn_chunk;
   if constexpr (sizeof(KT) == 2) {
     // bfloat16 caches: decode_layer_init admits head_dim 128 with at most 8
     // query heads per KV head only, all on the matrix cores
-    if (G <= 4) return ck > 128 ? task_attn_mm<2, 4>(c, b, g, ci, tix, wev) : task_attn_mm<1, 4>(c, b, g, ci, tix, wev);
-    return ck > 128 ? task_attn_mm<2, 8>(c, b, g, ci, tix, wev) : task_attn_mm<1, 8>(c, b, g, ci, tix, wev);
+    if (G <= 4)
+      return ck > 128 ? task_attn_mm<2, 4>(c, b, g, ci, tix, wev, wsubs) : task_attn_mm<1, 4>(c, b, g, ci, tix, wev, wsubs);
+    return ck > 128 ? task_attn_mm<2, 8>(c, b, g, ci, tix, wev, wsubs) : task_attn_mm<1, 8>(c, b, g, ci, tix, wev, wsubs);
   } else {
-    if (G >= 4) return attn_its<KT, 4>(c, b, g, ci, tix, ck, wev);
-    if (G == 2) return attn_its<KT, 2>(c, b, g, ci, tix, ck, wev);
-    return attn_its<KT, 1>(c, b, g, ci, tix, ck, wev);
+    if (G >= 4) return attn_its<KT, 4>(c, b, g, ci, tix, ck, wev, wsubs);
+    if (G == 2) return attn_its<KT, 2>(c, b, g, ci, tix, ck, wev, wsubs);
+    return attn_its<KT, 1>(c, b, g, ci, tix, ck, wev, wsubs);
   }
 }
 
@@ -2017,12 +2018,14 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
     return ctx_wait(Ctx{a, l, wg, s}, a.ws.bar + (size_t)(bi - 1) * kEvInts, kSubs);
   };
   // The events this workgroup has seen fired, one per wait kind (s.seen[k] =
-  // key of the last event waited on, key = offset + 1 + (counters - 1) << 27),
+  // key of the last event waited on, key = offset / kCtr + 1 + (counters - 1)
+  // << 24: event offsets are multiples of kCtr below 2^27, waits span at most
+  // kMaxHkv counters),
   // so a later task that waits on the same event does not poll it again.
   // Every wave records the key after its task's wait and reads it before the
   // next task, so all waves agree.
   enum : int { W_QKV = 0, W_ATTN, W_O, W_GU, W_DOWN, W_ROUTER, W_ROUTE, W_MDOWN };
-  auto key_of = [](long off, int subs) { return (int)off + 1 + (subs << 27); };
+  auto key_of = [](long off, int subs) { return (int)(off / kCtr) + 1 + (subs << 24); };
   int pend_kind = -1, pend_key = 0;   // the wait the current task performs (recorded once it has)
   // the event (offset `off`, counters off .. off + subs kCtr) a task waits on,
   // or nullptr when this workgroup has already seen it fired
@@ -2042,7 +2045,7 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
   // the wait of a task (pmk_sched.h: task_wait) as an event pointer and its
   // extra counters, nullptr when already seen fired
   auto wait_of = [&](int type, int y, int z, int w, int& subs) -> const int* {
-    const EvWait wt = task_wait(dm, ldku(&a.nblk), ldku(&a.geo[1].kr), type, y, z, w, l);
+    const EvWait wt = task_wait(dm, ldku(&a.nblk), ldku(&a.geo[1].kr), type, y, z, w, l, ldku(&a.ev_mode));
     subs = kSubs;
     if (wt.kind < 0) return nullptr;
     if (ev_flat(wt.kind)) subs = wt.n - 1;
@@ -2093,7 +2096,7 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
           case T_ATTN: {   // (b, g): waits on the QKV tiles of its block and group alone
             int subs;
             const int* wev = wait_of(T_ATTN, task.y, task.z, task.w, subs);
-            ok = attn_dispatch<WT>(c, task.y, task.z, task.w, tix, wev);
+            ok = attn_dispatch<WT>(c, task.y, task.z, task.w, tix, wev, subs);
             break;
           }
           case T_ATTS: {   // x: piece << 8 | pieces << 20, y: b | g << 16, z/w: positions [z, w)
@@ -2101,8 +2104,8 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
             int subs;
             const int* wev = wait_of(T_ATTS, task.y, task.z, task.w, subs);
             if constexpr (sizeof(WT) == 2) {
-              ok = dm.Hq / dm.Hkv <= 4 ? task_attn_stream<4>(c, b, g, task.z, task.w, piece, np, wev)
-                                       : task_attn_stream<8>(c, b, g, task.z, task.w, piece, np, wev);
+              ok = dm.Hq / dm.Hkv <= 4 ? task_attn_stream<4>(c, b, g, task.z, task.w, piece, np, wev, subs)
+                                       : task_attn_stream<8>(c, b, g, task.z, task.w, piece, np, wev, subs);
             }
             break;
           }
@@ -2180,7 +2183,7 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
           // (block eb of layer l's input: its down event of layer l - 1, or a QKV
           // event of its block, whose tiles waited on that down event)
           auto qkv_seen = [&]() {
-            const int k = s.seen[W_QKV] - 1;
+            const long k = (long)(s.seen[W_QKV] - 1) * kCtr;
             return k >= ev_off(dm, l, EV_QKV, eb, 0) && k < ev_off(dm, l, EV_QKV, eb, dm.Hkv);
           };
           const bool early = ps.R * ps.nb <= kYsFloats &&
@@ -2251,6 +2254,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   const int tid = threadIdx.x, B = a.batch, G = dm.grid;
   __shared__ int bad;
   __shared__ Plan plan;
+  __shared__ int gtiles[kMaxHkv];   // QKV row tiles meeting each KV group
   __shared__ int cb[kMaxBatchAll + 1];
   __shared__ int sl[kMaxBatchAll];   // the requests' lengths, read once
   StepArgs* copy = reinterpret_cast<StepArgs*>(a.ws.args);
@@ -2280,14 +2284,19 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   }
   if (tid == 0) {
     a.ws.err[16] = 0;   // abort flag
-    plan = plan_step(dm, B, sl, cb, a.per_op);
+    plan = plan_step(dm, B, sl, cb, a.per_op, a.ev_mode);
     copy->attn_merge_o = plan.merge;
     copy->attn_chunk = plan.ck;
     for (int st = 0; st < 4; ++st) copy->geo[st] = plan.geo[st];
     copy->qkv_tiles = plan.geo[0].tiles;
     copy->nblk = plan.nblk;
   }
+  for (int g = tid; g < dm.Hkv; g += blockDim.x) gtiles[g] = 0;
   __syncthreads();
+  for (int t = tid; t < plan.geo[0].tiles; t += blockDim.x) {
+    const int2 gr = qkv_tile_groups(dm, plan.geo[0].tiles, t);
+    for (int g = gr.x; g <= gr.y; ++g) atomicAdd(&gtiles[g], 1);
+  }
   // every workgroup's queue (pmk_sched.h: build_queue)
   for (int w = tid; w < G; w += blockDim.x) {
     int4* q = a.ws.queue + (size_t)w * dm.max_queue;
@@ -2299,6 +2308,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     a.ws.qlen[w] = n <= dm.max_queue ? n : 0;
     if (n > dm.max_queue) atomicOr(&bad, 4);
   }
+  __syncthreads();
   // every counter of every layer armed with its count (pmk_sched.h: ev_count).
   // Per layer: QKV and ATTN flat counters of the blocks in use, the O, GU and
   // DOWN events of those blocks, and ROUTER, ROUTE, MDOWN.
@@ -2323,7 +2333,7 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
         kind = e == 3 * nb ? EV_ROUTER : e == 3 * nb + 1 ? EV_ROUTE : EV_MDOWN;
       }
     }
-    a.ws.ev[ev_off(dm, l, kind, blk, g) + sub * kCtr] = ev_count(dm, plan, cb, kind, blk, g, sub);
+    a.ws.ev[ev_off(dm, l, kind, blk, g) + sub * kCtr] = ev_count(dm, plan, cb, kind, blk, g, sub, gtiles);
   }
   for (int idx = tid; idx < 4 * G * ((B + kMaxNb - 1) / kMaxNb); idx += blockDim.x) {
     const int used = G * ((B + kMaxNb - 1) / kMaxNb), st = idx / used;   // (block, tile) records of each stage

@@ -33,6 +33,13 @@
 
 namespace pmk {
 
+// Depth, units and rows per unit of the four dense stages.
+__host__ __device__ inline void stage_dims(const Dims& dm, int st, int& K, int& U, int& R) {
+  K = st == 0 ? dm.H : st == 1 ? dm.Hq * dm.d : st == 2 ? dm.H : dm.F;
+  U = st == 0 ? dm.qkv_units : st == 1 ? dm.H : st == 2 ? dm.F : dm.H;
+  R = (st == 0 || st == 2) ? 2 : 1;
+}
+
 // The handle's fixed dimensions from the model description and the device's
 // compute-unit count (the persistent grid).
 __host__ inline Dims dims_from_desc(const pmk_model_desc& desc, int grid) {
@@ -77,7 +84,26 @@ __host__ inline Dims dims_from_desc(const pmk_model_desc& desc, int grid) {
     dm.max_queue += cdiv((long)dm.router_tiles * cdiv(dm.max_batch, kMaxNb), G) + 4;
   else
     dm.max_queue += cdiv(dm.gu_tiles, G) + cdiv(dm.down_tiles, G);
+  // split-K records: a region of its own for each dense stage, sized for
+  // every batch and grid share (with events per KV group or per batch block,
+  // one stage's tiles may still be reducing while a later stage's, or another
+  // block's, store their slices)
+  long off = 0;
+  for (int st = 0; st < 4; ++st) {
+    dm.kpart_off[st] = off;
+    if (moe && st >= 2) continue;   // no dense gate/up or down stage
+    int K, U, R;
+    stage_dims(dm, st, K, U, R);
+    off += (kpart_need(K, U, R, dm.max_batch, G, st <= 1, dm.kstep, dm.xpad) + 63) / 64 * 64;
+  }
+  dm.kpart_off[4] = off > 16 ? off : 16;
   return dm;
+}
+
+// First float of split-K record (stage st, tile index ti = block k x tiles +
+// row tile, slice s), records rs floats apart.
+__host__ __device__ inline long kpart_rec(const Dims& dm, int st, int ti, int ks, int s, int rs) {
+  return dm.kpart_off[st] + ((long)ti * ks + s) * rs;
 }
 
 // This step's split and event-block count (set by plan_step).
@@ -91,26 +117,29 @@ struct Plan {
   long share;        // streamed: positions (with each range's lead) per workgroup
   int nblk;          // event blocks (see above)
   int per_op;        // the per-op schedule
+  int ev_mode;       // EVM_TILE, EVM_GROUP or EVM_STAGE (pmk_set_event_granularity)
   StageGeo geo[4];   // QKV, O, gate/up, down
 };
 
+// Granularity of the dense chain's events: per tile (KV group and batch
+// block), per KV group only (one batch block), or one event per stage (every
+// attention task waits on every group's QKV tiles, every O task on every
+// group's attention: the stage-wide events of a plain megakernel).
+enum EvMode : int { EVM_TILE = 0, EVM_GROUP = 1, EVM_STAGE = 2 };
+
 __host__ __device__ inline int ceil_div_i(long a, long b) { return (int)((a + b - 1) / b); }
 
-// Depth, units and rows per unit of the four dense stages.
-__host__ __device__ inline void stage_dims(const Dims& dm, int st, int& K, int& U, int& R) {
-  K = st == 0 ? dm.H : st == 1 ? dm.Hq * dm.d : st == 2 ? dm.H : dm.F;
-  U = st == 0 ? dm.qkv_units : st == 1 ? dm.H : st == 2 ? dm.F : dm.H;
-  R = (st == 0 || st == 2) ? 2 : 1;
-}
 
 // The step's split from (B, sl): attention chunking, streaming and dedicated
 // attention workgroups, each dense stage's geometry, the event blocks. cb[0..B]
 // receives the prefix sum of the requests' positions (S + 1, streamed) or
 // chunks. Serial over the batch (the device prologue runs it on one thread).
-__host__ __device__ inline Plan plan_step(const Dims& dm, int B, const int* sl, int* cb, int per_op) {
+__host__ __device__ inline Plan plan_step(const Dims& dm, int B, const int* sl, int* cb, int per_op,
+                                          int ev_mode = EVM_TILE) {
   Plan p{};
   p.B = B;
   p.per_op = per_op;
+  p.ev_mode = ev_mode;
   const int G = dm.grid;
   // Small batches whose O-projection inputs fit one merging pass take the
   // smallest chunk that keeps every request within 8 chunks and let the
@@ -182,7 +211,7 @@ __host__ __device__ inline Plan plan_step(const Dims& dm, int B, const int* sl, 
   }
   // events per block when every dense stage splits by block (MoE layers keep
   // one block: their routed stages cover all tokens at once)
-  p.nblk = (all_blocked && !dm.moe) ? (B + kMaxNb - 1) / kMaxNb : 1;
+  p.nblk = (all_blocked && !dm.moe && ev_mode == EVM_TILE) ? (B + kMaxNb - 1) / kMaxNb : 1;
   return p;
 }
 
@@ -260,18 +289,24 @@ __host__ __device__ inline int2 block_requests(const Plan& p, int blk) {
 
 // The count counter `sub` (0 for [0], 1 + x for sub-counter x; flat events
 // have [0] only) of event (kind, blk, g) of a layer is armed with.
+// QKV row tiles whose units meet KV group g.
+__host__ __device__ inline int qkv_group_tiles(const Dims& dm, const Plan& p, int g) {
+  int n = 0;
+  for (int t = 0; t < p.geo[0].tiles; ++t) {
+    const int2 gr = qkv_tile_groups(dm, p.geo[0].tiles, t);
+    if (gr.x <= g && g <= gr.y) ++n;
+  }
+  return n;
+}
+// gtiles (nullable): qkv_group_tiles of every group, precomputed.
 __host__ __device__ inline int ev_count(const Dims& dm, const Plan& p, const int* cb, int kind, int blk, int g,
-                                        int sub) {
+                                        int sub, const int* gtiles = nullptr) {
   const int G = dm.grid;
   const int x = sub - 1;
   switch (kind) {
     case EV_QKV: {   // QKV row tiles covering group g, once per batch block they stand for
       if (sub != 0) return 0;
-      int n = 0;
-      for (int t = 0; t < p.geo[0].tiles; ++t) {
-        const int2 gr = qkv_tile_groups(dm, p.geo[0].tiles, t);
-        if (gr.x <= g && g <= gr.y) ++n;
-      }
+      const int n = gtiles ? gtiles[g] : qkv_group_tiles(dm, p, g);
       return n * (p.nblk > 1 ? 1 : p.geo[0].blk);
     }
     case EV_ATTN: {  // the attention tasks that finish (request, group g) of block blk
@@ -304,19 +339,21 @@ __host__ __device__ inline int ev_count(const Dims& dm, const Plan& p, const int
 // (n = 1); kind < 0: none. Task fields as queued: type, y, z, w; `nblk` event
 // blocks, `o_kr` the O-projection's K slice length this step.
 struct EvWait { int kind, layer, blk, g0, n; };
+// ev_mode EVM_STAGE: attention and O tasks wait on every group.
 __host__ __device__ inline EvWait task_wait(const Dims& dm, int nblk, int o_kr, int type, int y, int z, int w,
-                                            int l) {
+                                            int l, int ev_mode = EVM_TILE) {
+  const bool all = ev_mode == EVM_STAGE;
   switch (type) {
     case T_QKV:   // the previous layer's down stage of this block (MoE: its combine)
       if (l == 0) break;
       return EvWait{EV_DOWN, l - 1, dm.moe ? 0 : ev_blk(nblk, w), 0, 1};
     case T_ATTN:   // (request y, group z): the QKV tiles of its block and group
-      return EvWait{EV_QKV, l, ev_blk(nblk, y / kMaxNb), z, 1};
+      return EvWait{EV_QKV, l, ev_blk(nblk, y / kMaxNb), all ? 0 : z, all ? dm.Hkv : 1};
     case T_ATTS:   // a streamed piece of (request y & 0xffff, group y >> 16)
-      return EvWait{EV_QKV, l, ev_blk(nblk, (y & 0xffff) / kMaxNb), y >> 16, 1};
+      return EvWait{EV_QKV, l, ev_blk(nblk, (y & 0xffff) / kMaxNb), all ? 0 : y >> 16, all ? dm.Hkv : 1};
     case T_O: {    // the attention of its block for the groups whose heads its K slice z reads
       const int K = dm.Hq * dm.d, k0 = z * o_kr, kn = (K < k0 + o_kr ? K : k0 + o_kr) - k0;
-      const int2 gr = o_slice_groups(dm, k0, kn);
+      const int2 gr = all ? make_int2(0, dm.Hkv - 1) : o_slice_groups(dm, k0, kn);
       return EvWait{EV_ATTN, l, ev_blk(nblk, w), gr.x, gr.y - gr.x + 1};
     }
     case T_GU: return EvWait{EV_O, l, ev_blk(nblk, w), 0, 1};

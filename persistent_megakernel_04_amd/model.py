@@ -142,6 +142,12 @@ class DecodeModel:
         m = _abi.SCHEDULES[mode] if isinstance(mode, str) else int(mode)
         _abi.check(self.lib.pmk_set_schedule(self.handle, m), "pmk_set_schedule")
 
+    def set_event_granularity(self, mode):
+        """'tile' (the default: per KV group and batch block), 'group' (per KV group) or 'stage' (one event
+        per stage): how finely the dense chain's consumers wait on their producers."""
+        m = _abi.EVENT_MODES[mode] if isinstance(mode, str) else int(mode)
+        _abi.check(self.lib.pmk_set_event_granularity(self.handle, m), "pmk_set_event_granularity")
+
     def set_moe_scheduler(self, mode):
         """'static' (each workgroup a fixed share of the grouped expert tasks) or 'dynamic' (tasks popped from
         a per-layer queue, down tasks queued as their experts' gate/up tasks finish)."""

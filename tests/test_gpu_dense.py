@@ -496,3 +496,33 @@ def test_schedule_setters_reject_unknown_modes(orc):
     assert model.lib.pmk_set_moe_scheduler(model.handle, 2) == _abi.PMK_ERR_ARG
     model.close()
     check_dense(orc, case)
+
+
+@pytest.mark.parametrize("B,L,lo,hi", [(1, 2, 512, 512), (16, 2, 512, 4096), (40, 1, 256, 2048)])
+def test_event_granularities_give_identical_bits(orc, B, L, lo, hi):
+    """The dense chain's events per tile (per KV group, and per 16-row block
+    beyond 16 requests), per KV group only, or one per stage change only who
+    waits on what, not the arithmetic: the same hidden states and K/V entries,
+    bit for bit, and per tile against the oracle."""
+    w = synth.get_workload("c3_8b_sweep")
+    lens = [lo] * B if lo == hi else synth.ragged_lengths(B, lo, hi, ("c3_8b_sweep", "events", B))
+    case = build_case(w, B, lens, n_layers=L, max_seq=int(max(lens)) + 2, tag=f"t23_{B}")
+    inp = oracle_inputs(case, None if B <= 16 else block_requests(lens))
+    outs = {}
+    for mode in ("stage", "group", "tile"):
+        hidden, kv = case.hidden.clone(), case.kv.clone()
+        model = make_model(case)
+        model.set_event_granularity(mode)
+        announce(f"decode_step {w.name} L={L} B={B} events={mode}")
+        model.step(hidden, kv, case.seq_lens)
+        torch.cuda.synchronize()
+        assert model.device_error() == 0
+        model.close()
+        outs[mode] = (hidden, kv)
+    for mode in ("group", "tile"):
+        assert torch.equal(outs[mode][0].view(torch.int32), outs["stage"][0].view(torch.int32)), mode
+        assert torch.equal(outs[mode][1].view(torch.int16), outs["stage"][1].view(torch.int16)), mode
+    hidden, kv = outs["tile"]
+    rq = inp["requests"]
+    kv_gpu = to_np(kv[:, :, rq] if B > 16 else kv)
+    check_against_oracle(orc, case, inp, to_np(hidden).astype(np.float64)[rq], kv_gpu)

@@ -2,8 +2,10 @@
 built for the host with hipcc (no GPU), runs the queues and the event tensor
 that the device prologue builds (the same functions, pmk_sched.h) for the
 model shapes and batches 1..1024, and checks for deadlock, notify counts and
-producer-before-consumer order. Injected faults (a dropped notify, a counter
-armed one too high or too low) must each be reported."""
+producer-before-consumer order, and that no two row tiles' split-K records
+in use at once overlap. Injected faults (a dropped notify, a counter armed one
+too high or too low) must each be reported, and one split-K region shared by
+all stages must be reported where records of two stages meet."""
 import os
 import shutil
 import subprocess
@@ -30,7 +32,7 @@ def test_schedule_replays_without_deadlock_or_early_consumer(exe):
     assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
 
 
-@pytest.mark.parametrize("fault", ["drop", "plus", "minus"])
+@pytest.mark.parametrize("fault", ["drop", "plus", "minus", "kpart"])
 def test_replay_reports_injected_faults(exe, fault):
     r = subprocess.run([exe, "--fault", fault], capture_output=True, text=True, timeout=600)
     assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout + r.stderr
