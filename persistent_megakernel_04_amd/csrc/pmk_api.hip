@@ -168,6 +168,7 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
       {(void**)&ws.mctr, (size_t)dm.L * dm.max_batch * dm.Hkv * kCtr * 4},
       {(void**)&ws.chunk_base, (size_t)(dm.max_batch + 1) * 4},
       {(void**)&ws.queue, (size_t)G * dm.max_queue * 16},
+      {(void**)&ws.qev, (size_t)G * dm.max_queue * 16},
       {(void**)&ws.qlen, (size_t)G * 4},
       {(void**)&ws.err, 64 * 4},
       {(void**)&ws.args, sizeof(StepArgs)},

@@ -176,6 +176,7 @@ struct Workspace {
   int* mctr;           // [L][max_batch][Hkv][kCtr]     attention merge counters
   int* chunk_base;     // [max_batch + 1]               prefix sum of chunks per request
   int4* queue;         // [grid][max_queue]
+  int4* qev;           // [grid][max_queue]            each queued task's events (pmk_sched.h: task_events)
   int* qlen;           // [grid]
   int* err;            // [0] error word, [16] abort flag
   int* err_host;       // pinned, host-coherent mirror of the error word (written by the device when set)

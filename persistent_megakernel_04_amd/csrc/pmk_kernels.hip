@@ -66,6 +66,7 @@ struct Ctx {
   const StepArgs& a;
   int l, wg;
   Lds s;
+  int* nev = nullptr;   // the counter this task notifies (attention: the request's group), resolved for layer l
 };
 
 // Per-layer activations. Each buffer is written once per step, by the stage
@@ -98,13 +99,16 @@ __device__ __forceinline__ float* hid_out(const StepArgs& a, int l) {
   return l == a.dm.L - 1 ? a.hidden : a.ws.hid + (size_t)l * a.dm.max_batch * a.dm.H;
 }
 
-// Event (kind, blk, g) of layer l in the event tensor (see pmk_sched.h).
-__device__ __forceinline__ int* ev_at(const StepArgs& a, int l, int kind, int blk = 0, int g = 0) {
-  return a.ws.ev + ev_off(a.dm, l, kind, blk, g);
-}
-// The event block of request b (batch blocks of 16 rows; one block unless
-// this step gives blocks events of their own).
-__device__ __forceinline__ int ev_blk_of(const StepArgs& a, int b) { return ev_blk(ldku(&a.nblk), b / kMaxNb); }
+// x / d for a wave-uniform d > 0 and 0 <= x with x d < 2^32, by one
+// multiply-high: with m = floor(2^32 / d) + 1 = (2^32 + e) / d, 0 < e <= d,
+// x m / 2^32 = x / d + x e / (d 2^32), and the second term is below 1 / d,
+// too small to carry x / d past the next integer.
+struct UDiv {
+  uint32_t m;
+  int one;
+  __device__ __forceinline__ explicit UDiv(int d) : m(0xffffffffu / (uint32_t)d + 1u), one(d == 1) {}
+  __device__ __forceinline__ int div(int x) const { return one ? x : (int)__umulhi((uint32_t)x, m); }
+};
 
 __device__ __forceinline__ size_t kv_off(const Dims& dm, int l, int which, int b, int g, int pos) {
   return (((((size_t)l * 2 + which) * dm.max_batch + b) * dm.Hkv + g) * (size_t)dm.max_seq + pos) * dm.d;
@@ -874,12 +878,26 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
   }
   switch (ps.epi) {
     case E_QKV: {   // RoPE at each request's position, then q/k/v out and the K/V append
-      const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d, ni = ps.n * nb;
+      // element (request m, tile unit ju) at index ju << sh | m (2^sh >= nb):
+      // shifts instead of a division by nb, and the unit's (head, pair) from
+      // multiply-high dividers set up once (a runtime integer division is
+      // some forty vector instructions, and this loop ran 24 of them per lane)
+      const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d, G = dm.Hq / dm.Hkv;
+      const int sh = nb <= 1 ? 0 : 32 - __builtin_clz(nb - 1), ni = ps.n << sh;
+      const UDiv per_div((G + 2) * half), half_div(half);
+      auto unit_hi = [&](int ju, int& h, int& i) {
+        const int up = ps.r0 + ju, g = per_div.div(up), r = up - g * (G + 2) * half;
+        const int hg = half_div.div(r);   // head within the group's run: G query heads, its key, its value
+        i = r - hg * half;
+        h = hg < G ? g * G + hg : dm.Hq + (hg - G) * dm.Hkv + g;
+      };
       if constexpr ((KP & 3) == KP_ALL) {
         if (a.per_op) {   // the projection alone: RoPE and the append are ops of their own
           for (int idx = t0; idx < ni; idx += nt) {
-            const int m = idx / ps.n, ju = idx - m * ps.n;
-            const int unit = qkv_unit(dm, ps.r0 + ju), h = unit / half, i = unit - h * half;
+            const int m = idx & ((1 << sh) - 1), ju = idx >> sh;
+            if (m >= nb) continue;
+            int h, i;
+            unit_hi(ju, h, i);
             float* dst = qkv_of(a, c.l) + (size_t)(b0 + m) * qkv_dim + h * dm.d + i;
             stc(dst, ys[(2 * ju) * nb + m]);
             stc(dst + half, ys[(2 * ju + 1) * nb + m]);
@@ -894,19 +912,20 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
       const auto rrs = rsrc_n(a.ws.rope, dm.max_seq * half * 8);
       for (int base = 0; base < ni; base += nt * 8) {
         float2 cs[8];
+        int hs[8], is[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int idx = base + t0 + nt * u, m = idx / ps.n, ju = idx - m * ps.n;
-          const int unit = qkv_unit(dm, ps.r0 + ju), h = unit / half, i = unit - h * half;
+          const int idx = base + t0 + nt * u, m = idx & ((1 << sh) - 1);
+          unit_hi(min(idx >> sh, ps.n - 1), hs[u], is[u]);
           const int pos = __shfl(posl, m, 64);
-          cs[u] = ldk2(rrs, idx < ni && h < dm.Hq + dm.Hkv ? (pos * half + i) * 8 : kNoRecord);
+          cs[u] = ldk2(rrs, idx < ni && m < nb && hs[u] < dm.Hq + dm.Hkv ? (pos * half + is[u]) * 8 : kNoRecord);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int idx = base + t0 + nt * u;
           if (idx >= ni) break;
-          const int m = idx / ps.n, ju = idx - m * ps.n;
-          const int unit = qkv_unit(dm, ps.r0 + ju), h = unit / half, i = unit - h * half;
+          const int m = idx & ((1 << sh) - 1), ju = idx >> sh, h = hs[u], i = is[u];
+          if (m >= nb) continue;
           const float r = c.s.rstd[m];
           float y1 = ys[(2 * ju) * nb + m] * r, y2 = ys[(2 * ju + 1) * nb + m] * r;
           const int bb = b0 + m, pos = __shfl(posl, m, 64);
@@ -919,7 +938,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
           stc(dst, y1);
           stc(dst + half, y2);
           if (h >= dm.Hq) {
-            const int kvh = h - dm.Hq, which = kvh / dm.Hkv, g = kvh - which * dm.Hkv;
+            const int kvh = h - dm.Hq, which = kvh >= dm.Hkv ? 1 : 0, g = kvh - which * dm.Hkv;
             WT* cp = reinterpret_cast<WT*>(a.kv) + kv_off(dm, c.l, which, bb, g, pos);
             Elem<WT>::put(cp + i, y1);
             Elem<WT>::put(cp + i + half, y2);
@@ -1060,7 +1079,7 @@ __device__ __forceinline__ bool attn_finish(const Ctx& c, int b, int g, int ci, 
   // the event of (block of b, group g): flat, counts the chunk tasks that
   // notify (the O-projection, or the per-op merge, merges the partials) or
   // one notify per request
-  int* aev = ev_at(a, c.l, EV_ATTN, ev_blk_of(a, b), g);
+  int* aev = c.nev;
   if (a.attn_merge_o || a.per_op || nc == 1) {
     wg_notify(aev, -1);
     return true;
@@ -1817,7 +1836,7 @@ __device__ __forceinline__ bool task_route(const Ctx& c, const int* wev) {
       if (a.rout.sorted_slot) *gp(a.rout.sorted_slot + i) = ldci(a.ws.sorted_slot + i);
     }
   }
-  wg_notify(ev_at(a, c.l, EV_ROUTE), -1);
+  wg_notify(c.nev, -1);
   return true;
 }
 
@@ -1998,6 +2017,7 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
   if (!__builtin_amdgcn_readfirstlane(*s.flag)) return;
   const int n = ldku(a.ws.qlen + wg);
   const int4* q = a.ws.queue + (size_t)wg * dm.max_queue;
+  const int4* qe = a.ws.qev + (size_t)wg * dm.max_queue;
   uint32_t* tr = a.trace ? a.trace + (size_t)wg * a.trace_cap * 8 : nullptr;
   // records accumulate over the launches of a step (the prologue zeroes the counts)
   int tn = tr ? ldu(reinterpret_cast<const int*>(tr)) + 1 : 1;
@@ -2042,18 +2062,17 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
   };
   // whether this workgroup has seen event `off` fired
   auto seen = [&](int kind, long off, int subs) -> bool { return s.seen[kind] == key_of(off, subs); };
-  // the wait of a task (pmk_sched.h: task_wait) as an event pointer and its
-  // extra counters, nullptr when already seen fired
-  auto wait_of = [&](int type, int y, int z, int w, int& subs) -> const int* {
-    const EvWait wt = task_wait(dm, ldku(&a.nblk), ldku(&a.geo[1].kr), type, y, z, w, l, ldku(&a.ev_mode));
+  // the wait of a task as its queue entry gives it (pmk_sched.h:
+  // task_events): the event pointer of this layer and its extra counters,
+  // nullptr when there is none or this workgroup has already seen it fired
+  const long LI = ev_layer_ints(dm);
+  auto wait_of = [&](const int4& te, int type, int& subs) -> const int* {
     subs = kSubs;
-    if (wt.kind < 0) return nullptr;
-    if (ev_flat(wt.kind)) subs = wt.n - 1;
-    const int kind = wt.kind == EV_QKV ? W_QKV : wt.kind == EV_ATTN ? W_ATTN : wt.kind == EV_O ? W_O
-                   : wt.kind == EV_GU ? W_GU : wt.kind == EV_DOWN ? W_DOWN : wt.kind == EV_ROUTER ? W_ROUTER
-                   : wt.kind == EV_ROUTE ? W_ROUTE : W_MDOWN;
-    return need(kind, ev_off(dm, wt.layer, wt.kind, wt.blk, wt.g0), subs);
+    if (te.y < 0 || (l == 0 && type == T_QKV)) return nullptr;
+    subs = te.y & 0xffff;
+    return need(te.y >> 16, te.x + l * LI, subs);
   };
+  auto notify_ev = [&](const int4& te) -> int* { return te.z >= 0 ? a.ws.ev + te.z + l * LI : nullptr; };
   auto advance = [&]() {
     if (++t == n) {
       t = 0;
@@ -2081,6 +2100,7 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
   if (n > 0) {
     while (l < l_end) {
       int4 task = ldku4(q + t);
+      int4 te = ldku4(qe + t);
       const int tix = task.x >> 8;   // attention tasks: the task's index within the stage
       task.x &= 0xff;
       if (!mine(task.x)) {   // not this launch's (a per-stage schedule)
@@ -2089,20 +2109,20 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
       }
       if (bars && !barrier_to(l * ns + stage_of(task.x))) return;
       if (!gemv_task(task.x)) {
-        const Ctx c{a, l, wg, s};
+        const Ctx c{a, l, wg, s, notify_ev(te)};
         const uint32_t t_begin = begin();
         bool ok = true;
         switch (task.x) {
           case T_ATTN: {   // (b, g): waits on the QKV tiles of its block and group alone
             int subs;
-            const int* wev = wait_of(T_ATTN, task.y, task.z, task.w, subs);
+            const int* wev = wait_of(te, T_ATTN, subs);
             ok = attn_dispatch<WT>(c, task.y, task.z, task.w, tix, wev, subs);
             break;
           }
           case T_ATTS: {   // x: piece << 8 | pieces << 20, y: b | g << 16, z/w: positions [z, w)
             const int b = task.y & 0xffff, g = task.y >> 16, piece = tix & 0xfff, np = tix >> 12;
             int subs;
-            const int* wev = wait_of(T_ATTS, task.y, task.z, task.w, subs);
+            const int* wev = wait_of(te, T_ATTS, subs);
             if constexpr (sizeof(WT) == 2) {
               ok = dm.Hq / dm.Hkv <= 4 ? task_attn_stream<4>(c, b, g, task.z, task.w, piece, np, wev, subs)
                                        : task_attn_stream<8>(c, b, g, task.z, task.w, piece, np, wev, subs);
@@ -2112,15 +2132,15 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
           case T_ROUTE:
             if constexpr ((KP & 3) != KP_DENSE) {
               int subs;
-              const int* wev = wait_of(T_ROUTE, 0, 0, 0, subs);
+              const int* wev = wait_of(te, T_ROUTE, subs);
               ok = dm.E <= 128 ? task_route<16>(c, wev) : task_route<64>(c, wev);
             }
             break;
           case T_COMBINE:
             if constexpr ((KP & 3) != KP_DENSE) {
               int subs;
-              ok = task_combine(c, wait_of(T_COMBINE, 0, 0, 0, subs));
-              if (ok) wg_notify(ev_at(a, l, EV_DOWN), wg & (kSubs - 1));
+              ok = task_combine(c, wait_of(te, T_COMBINE, subs));
+              if (ok) wg_notify(c.nev, -1);
             }
             break;
           case T_NORM1: case T_NORM2: case T_ROPE: case T_APPEND: case T_MERGE:
@@ -2145,29 +2165,19 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
       }
       // a run of consecutive GEMV tasks (across layers too)
       for (;;) {
-        const Ctx c{a, l, wg, s};
+        const Ctx c{a, l, wg, s, notify_ev(te)};
         const uint32_t t_begin = begin();
         bool ok = true;
-        int notify = -1;   // event this task notifies
         const int* wev = nullptr;
         int wsubs = kSubs;
         // dense tasks: y = row tile, z = K slice, w = batch block; their block's events
         const int eb = (task.x == T_QKV || task.x == T_O || task.x == T_GU || task.x == T_DOWN)
                            ? (ldku(&a.nblk) > 1 ? task.w : 0) : 0;
-        // its wait (pmk_sched.h: task_wait) and the event it notifies
+        // its wait (the queue entry's: pmk_sched.h, task_events)
         if (task.x == T_MGU) {   // the share's size is known once routing is done
-          ok = ctx_wait(c, wait_of(T_MGU, 0, 0, 0, wsubs), kSubs);
+          ok = ctx_wait(c, wait_of(te, T_MGU, wsubs), kSubs);
         } else if (task.x != T_MDOWN) {
-          wev = wait_of(task.x, task.y, task.z, task.w, wsubs);
-        }
-        switch (task.x) {
-          case T_QKV: notify = EV_QKV; break;
-          case T_O: notify = EV_O; break;
-          case T_GU: notify = EV_GU; break;
-          case T_DOWN: notify = EV_DOWN; break;
-          case T_ROUTER: notify = EV_ROUTER; break;
-          case T_MDOWN: notify = EV_MDOWN; break;
-          default: break;
+          wev = wait_of(te, task.x, wsubs);
         }
         bool done = true;   // this task finished its row tile (not so for a split-K slice that was not the last)
         bool split_last = false;   // it finished a split tile as its last slice task (a split task has one pass)
@@ -2212,30 +2222,23 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
         }
         if (!ok) return;
         // dense stages notify per row tile (by the last slice of a split tile),
-        // the others per workgroup; QKV tiles notify the flat counter of each
-        // KV group their units cover, in their block
-        const bool dense = task.x == T_QKV || task.x == T_O || task.x == T_GU || task.x == T_DOWN;
-        const int sub = (dense ? task.y : wg) & (kSubs - 1);
-        if (done && notify >= 0 && (split_last || wave == 0)) {
+        // the others per workgroup: the counter(s) of the queue entry (a QKV
+        // tile, the flat counter of each KV group its units cover)
+        if (done && c.nev && (split_last || wave == 0)) {
           if (split_last) {
             vm_drain();
             __syncthreads();
           } else {
             vm_drain();
           }
-          if ((threadIdx.x & (split_last ? kBlock - 1 : 63)) == 0) {
-            if (notify == EV_QKV) {
-              const int2 gr = qkv_tile_groups(dm, ldku(&a.geo[0].tiles), task.y);
-              for (int g = gr.x; g <= gr.y; ++g) (void)atomic_add_relaxed(ev_at(a, l, EV_QKV, eb, g), -1);
-            } else {
-              (void)atomic_add_relaxed(ev_slot(ev_at(a, l, notify, dense ? eb : 0), sub), -1);
-            }
-          }
+          if ((threadIdx.x & (split_last ? kBlock - 1 : 63)) == 0)
+            for (int i = 0; i < te.w; ++i) (void)atomic_add_relaxed(c.nev + i * kCtr, -1);
         }
         record(task.x, t_begin);
         advance();
         if (l >= l_end || bars) break;
         task = ldku4(q + t);
+        te = ldku4(qe + t);
         task.x &= 0xff;
         if (!gemv_task(task.x) || !mine(task.x)) break;
       }
@@ -2300,9 +2303,13 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
   // every workgroup's queue (pmk_sched.h: build_queue)
   for (int w = tid; w < G; w += blockDim.x) {
     int4* q = a.ws.queue + (size_t)w * dm.max_queue;
+    int4* qe = a.ws.qev + (size_t)w * dm.max_queue;
     int n = 0;
     build_queue(dm, plan, cb, w, [&](int4 v) {
-      if (n < dm.max_queue) q[n] = v;
+      if (n < dm.max_queue) {
+        q[n] = v;
+        qe[n] = task_events(dm, plan, v, w);   // its wait and notify counters
+      }
       ++n;
     });
     a.ws.qlen[w] = n <= dm.max_queue ? n : 0;

@@ -255,6 +255,12 @@ __host__ __device__ inline int qkv_unit(const Dims& dm, int up) {
 }
 // Row tile `tile` of `units` units split in `tiles`: first unit and count.
 __host__ __device__ inline int2 tile_units(int tile, int units, int tiles) {
+  // 32-bit when the products fit (every model shape here: the 64-bit
+  // division is a long software sequence on the device)
+  if ((unsigned long)(tiles + 1) * (unsigned)units <= 0xffffffffUL) {
+    const unsigned u0 = (unsigned)tile * (unsigned)units / (unsigned)tiles;
+    return make_int2((int)u0, (int)((unsigned)(tile + 1) * (unsigned)units / (unsigned)tiles - u0));
+  }
   const int u0 = (int)((long)tile * units / tiles);
   return make_int2(u0, (int)((long)(tile + 1) * units / tiles) - u0);
 }
@@ -365,6 +371,59 @@ __host__ __device__ inline EvWait task_wait(const Dims& dm, int nblk, int o_kr, 
     default: break;
   }
   return EvWait{-1, 0, 0, 0, 0};
+}
+
+// A task's events as its queue entry carries them, so that the persistent
+// kernel does no event arithmetic of its own (offsets into the event memory
+// as if the task were in layer 0; layer l adds l ev_layer_ints):
+//   x  the first counter the task waits on (a QKV task waits on the previous
+//      layer's down event: x is layer -1's, and layer 0's QKV tasks wait on
+//      nothing);
+//   y  the counters past the first (a flat run) or kSubs (a hierarchical
+//      event), | the awaited event's kind << 16; -1: no wait;
+//   z  the counter the task notifies (of a hierarchical event, the
+//      sub-counter its tile or workgroup takes); -1: none. A split tile's
+//      slices notify only when they complete it;
+//   w  consecutive flat counters it notifies (a QKV tile: the KV groups its
+//      units cover).
+// Attention tasks notify from their own code (the chunk or piece that
+// finishes the request's group), at z.
+__host__ __device__ inline int4 task_events(const Dims& dm, const Plan& p, int4 t, int wg) {
+  const int type = t.x & 0xff;
+  const long LI = ev_layer_ints(dm);
+  int4 e = make_int4(0, -1, -1, 0);
+  // layer 1's wait, moved back one layer (so that QKV's is layer -1's)
+  const EvWait wt = task_wait(dm, p.nblk, p.geo[1].kr, type, t.y, t.z, t.w, 1, p.ev_mode);
+  if (wt.kind >= 0) {
+    e.x = (int)(ev_off(dm, wt.layer, wt.kind, wt.blk, wt.g0) - LI);
+    e.y = (ev_flat(wt.kind) ? wt.n - 1 : kSubs) | (wt.kind << 16);
+  }
+  auto sub_of = [](int i) { return (1 + (i & (kSubs - 1))) * kCtr; };
+  switch (type) {
+    case T_QKV: {
+      const int2 gr = qkv_tile_groups(dm, p.geo[0].tiles, t.y);
+      e.z = (int)ev_off(dm, 0, EV_QKV, ev_blk(p.nblk, t.w), gr.x);
+      e.w = gr.y - gr.x + 1;
+      break;
+    }
+    case T_O: case T_GU: case T_DOWN:
+      e.z = (int)ev_off(dm, 0, type == T_O ? EV_O : type == T_GU ? EV_GU : EV_DOWN, ev_blk(p.nblk, t.w)) +
+            sub_of(t.y);
+      e.w = 1;
+      break;
+    case T_ATTN: case T_ATTS: {
+      const int b = type == T_ATTN ? t.y : (t.y & 0xffff), g = type == T_ATTN ? t.z : (t.y >> 16);
+      e.z = (int)ev_off(dm, 0, EV_ATTN, ev_blk(p.nblk, b / kMaxNb), g);
+      e.w = 1;
+      break;
+    }
+    case T_ROUTER: e.z = (int)ev_off(dm, 0, EV_ROUTER) + sub_of(wg); e.w = 1; break;
+    case T_ROUTE: e.z = (int)ev_off(dm, 0, EV_ROUTE); e.w = 1; break;
+    case T_MDOWN: e.z = (int)ev_off(dm, 0, EV_MDOWN) + sub_of(wg); e.w = 1; break;
+    case T_COMBINE: e.z = (int)ev_off(dm, 0, EV_DOWN) + sub_of(wg); e.w = 1; break;
+    default: break;
+  }
+  return e;
 }
 
 // Pieces of (request b, KV head g) that streamed attention cuts its range into

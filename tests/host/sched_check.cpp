@@ -72,6 +72,7 @@ struct Replay {
   int L = 1;
   std::vector<int> sl, cb;
   std::vector<std::vector<int4>> q;
+  std::vector<std::vector<int4>> qe;   // each task's events (task_events), as the kernel reads them
   std::map<long, int> ctr;           // counter (int offset in the event memory) -> count
   std::map<long, int> mctr;          // attention merge counters (l, b, g)
   std::map<long, int> slices;        // (stage, l, tile, block) -> slices done
@@ -127,11 +128,16 @@ struct Replay {
     }
     return true;
   }
-  // the wait of a task, as (offset, counters); counters 0: none
-  std::pair<long, int> wait_of(int l, int4 t) const {
-    const EvWait wt = task_wait(dm, p.nblk, p.geo[1].kr, t.x & 0xff, t.y, t.z, t.w, l, p.ev_mode);
-    if (wt.kind < 0) return {0, 0};
-    return {ev_off(dm, wt.layer, wt.kind, wt.blk, wt.g0), ev_flat(wt.kind) ? wt.n : 1 + kSubs};
+  // the wait of a task, as (offset, counters); counters 0: none -- from its
+  // queue entry (task_events), as the kernel takes it
+  std::pair<long, int> wait_of(int l, const int4& t, const int4& e) const {
+    if (e.y < 0 || (l == 0 && (t.x & 0xff) == T_QKV)) return {0, 0};
+    return {e.x + l * ev_layer_ints(dm), (e.y & 0xffff) + 1};
+  }
+  // the entry's notifies: w consecutive counters from z
+  void notify_entry(int l, const int4& e) {
+    if (e.z < 0) fail("a task that notifies has no counter in its queue entry");
+    for (int i = 0; i < e.w; ++i) notify(e.z + l * ev_layer_ints(dm) + (long)i * kCtr);
   }
   static int wait_slot(int kind) {
     return kind == EV_QKV ? 0 : kind == EV_ATTN ? 1 : kind == EV_O ? 2 : kind == EV_GU ? 3 : kind == EV_DOWN ? 4 : 5;
@@ -223,7 +229,7 @@ struct Replay {
 
   // Task t of workgroup w at layer l: check what it reads, record what it
   // writes, notify its events. Called when its wait has fired.
-  void run(int w, int l, int4 t) {
+  void run(int w, int l, int4 t, const int4& e) {
     const int type = t.x & 0xff, Hkv = dm.Hkv, G = dm.Hq / Hkv, half = dm.d / 2;
     switch (type) {
       case T_QKV: {
@@ -237,7 +243,8 @@ struct Replay {
             qkv_have[l][(size_t)b * dm.qkv_units + unit] = 1;
           }
         const int2 gr = qkv_tile_groups(dm, p.geo[0].tiles, t.y);
-        for (int g = gr.x; g <= gr.y; ++g) notify(ev_off(dm, l, EV_QKV, ev_blk(p.nblk, t.w), g));
+        if (e.w != gr.y - gr.x + 1) fail("a QKV tile's entry notifies other than the groups its units cover");
+        notify_entry(l, e);
         return;
       }
       case T_ATTN: case T_ATTS: {
@@ -246,19 +253,18 @@ struct Replay {
         need_units(l, b, dm.Hq * half + g * half, dm.Hq * half + (g + 1) * half, "attention (its key head)");
         need_units(l, b, (dm.Hq + Hkv) * half + g * half, (dm.Hq + Hkv) * half + (g + 1) * half,
                    "attention (its value head)");
-        const long aev = ev_off(dm, l, EV_ATTN, ev_blk(p.nblk, b / kMaxNb), g);
         int& mc = mctr[((long)l * p.B + b) * Hkv + g];
         --mc;   // this chunk / piece of (b, g) is done
         if (p.merge || p.per_op) {   // every chunk notifies; the O-projection (or the merge op) merges
           if (mc == 0) o_have[l][(size_t)b * Hkv + g] = 1;
-          notify(aev);
+          notify_entry(l, e);
           return;
         }
         const int nc = type == T_ATTN ? cb[b + 1] - cb[b] : (t.x >> 20);
         if (nc == 1 || mc == 0) {   // the only, or the last, chunk / piece merges and notifies
           if (mc != 0) fail("a single-piece range whose merge counter was armed above one");
           o_have[l][(size_t)b * Hkv + g] = 1;
-          notify(aev);
+          notify_entry(l, e);
         }
         if (mc < 0) fail("attention merge counter below zero");
         return;
@@ -273,7 +279,7 @@ struct Replay {
         for (int b = r.x; b < r.y; ++b) need_x(l, b, u.x, u.x + u.y, "O-projection (its residual)");
         if (!stage_done(1, l, t.y, t.w)) return;
         for (int b = r.x; b < r.y; ++b) put_rows(h1_have, h1_cnt, l, b, u.x, u.x + u.y);
-        notify(ev_off(dm, l, EV_O, ev_blk(p.nblk, t.w)) + (1 + (t.y & (kSubs - 1))) * kCtr);
+        notify_entry(l, e);
         return;
       }
       case T_GU: {
@@ -281,7 +287,7 @@ struct Replay {
         for (int b = r.x; b < r.y; ++b) need_rows(h1_have, h1_cnt, l, b, 0, dm.H, "gate/up (its rows' RMSNorm)");
         if (!stage_done(2, l, t.y, t.w)) return;
         for (int b = r.x; b < r.y; ++b) act_have[l][(size_t)t.y * p.B + b] = 1;
-        notify(ev_off(dm, l, EV_GU, ev_blk(p.nblk, t.w)) + (1 + (t.y & (kSubs - 1))) * kCtr);
+        notify_entry(l, e);
         return;
       }
       case T_DOWN: {
@@ -297,7 +303,7 @@ struct Replay {
         for (int b = r.x; b < r.y; ++b) need_rows(h1_have, h1_cnt, l, b, u.x, u.x + u.y, "down (its residual)");
         if (!stage_done(3, l, t.y, t.w)) return;
         for (int b = r.x; b < r.y; ++b) put_rows(x_have, x_cnt, l, b, u.x, u.x + u.y);
-        notify(ev_off(dm, l, EV_DOWN, ev_blk(p.nblk, t.w)) + (1 + (t.y & (kSubs - 1))) * kCtr);
+        notify_entry(l, e);
         return;
       }
       // the MoE chain, per token (the grouped expert tasks' own per-expert
@@ -306,14 +312,14 @@ struct Replay {
         const int b0 = t.z * kMaxNb, b1 = b0 + kMaxNb < p.B ? b0 + kMaxNb : p.B;
         for (int b = b0; b < b1; ++b) need_rows(h1_have, h1_cnt, l, b, 0, dm.H, "router (its tokens' RMSNorm)");
         ++done_tasks[(long)l * 64 + T_ROUTER];
-        notify(ev_off(dm, l, EV_ROUTER) + (1 + (w & (kSubs - 1))) * kCtr);
+        notify_entry(l, e);
         return;
       }
       case T_ROUTE: {
         if (done_tasks[(long)l * 64 + T_ROUTER] != dm.router_tiles * ceil_div_i(p.B, kMaxNb))
           fail("routing ran before every router task");
         route_have[l] = 1;
-        notify(ev_off(dm, l, EV_ROUTE));
+        notify_entry(l, e);
         return;
       }
       case T_MGU:
@@ -323,12 +329,12 @@ struct Replay {
       case T_MDOWN:
         if (!route_have[l]) missing("grouped down (routing)", l, 0, 0);
         ++done_tasks[(long)l * 64 + T_MDOWN];
-        notify(ev_off(dm, l, EV_MDOWN) + (1 + (w & (kSubs - 1))) * kCtr);
+        notify_entry(l, e);
         return;
       case T_COMBINE: {
         if (done_tasks[(long)l * 64 + T_MDOWN] != dm.grid) fail("combine ran before every grouped down share");
         for (int b = w; b < p.B; b += dm.grid) put_rows(x_have, x_cnt, l, b, 0, dm.H);
-        notify(ev_off(dm, l, EV_DOWN) + (1 + (w & (kSubs - 1))) * kCtr);
+        notify_entry(l, e);
         return;
       }
       default: return;   // the per-op schedule's separate ops: ordered by their launches
@@ -392,7 +398,7 @@ struct Replay {
             int4* t = next(v);
             if (!t) continue;
             left = true;
-            const auto wt = wait_of(lay[v], *t);
+            const auto wt = wait_of(lay[v], *t, qe[v][t - q[v].data()]);
             if (wt.second == 0 || fired(wt.first, wt.second)) w = v;
           }
           if (!left) break;
@@ -405,14 +411,13 @@ struct Replay {
                 fail(buf);
               }
           }
-          int4 t = *next(w);
-          const auto wt = wait_of(lay[w], t);
+          const int4* tp = next(w);
+          const int4 t = *tp, e = qe[w][tp - q[w].data()];
+          const auto wt = wait_of(lay[w], t, e);
           early_residual(w, lay[w], t);
-          if (wt.second) {   // record the event as seen, per wait kind (the kernel's cache)
-            const EvWait e = task_wait(dm, p.nblk, p.geo[1].kr, t.x & 0xff, t.y, t.z, t.w, lay[w], p.ev_mode);
-            seen[w][wait_slot(e.kind)] = wt.first;
-          }
-          run(w, lay[w], t);
+          if (wt.second)   // record the event as seen, per wait kind (the kernel's cache)
+            seen[w][wait_slot(e.y >> 16)] = wt.first;
+          run(w, lay[w], t, e);
           ++pos[w];
         }
         if (fused) return;
@@ -452,8 +457,12 @@ std::string check(const Shape& sh, int grid, int B, int max_seq, int lo, int hi,
   r.cb.resize(B + 1);
   r.p = plan_step(r.dm, B, r.sl.data(), r.cb.data(), per_op ? 1 : 0, ev_mode);
   r.q.resize(grid);
+  r.qe.resize(grid);
   for (int w = 0; w < grid; ++w) {
-    build_queue(r.dm, r.p, r.cb.data(), w, [&](int4 v) { r.q[w].push_back(v); });
+    build_queue(r.dm, r.p, r.cb.data(), w, [&](int4 v) {
+      r.q[w].push_back(v);
+      r.qe[w].push_back(task_events(r.dm, r.p, v, w));
+    });
     if ((int)r.q[w].size() > r.dm.max_queue) return "queue of workgroup " + std::to_string(w) + " above capacity";
   }
   r.arm();
