@@ -86,6 +86,84 @@ int check_desc(const pmk_model_desc* d) {
   return PMK_OK;
 }
 
+
+// Stage shapes the LDS holds: one input row of the whole depth and a tile's
+// outputs (a step may put its few attention tasks on workgroups of their own
+// and the QKV and O tiles on the others, at least three quarters of the
+// grid); event offsets within the 27-bit keys of the persistent kernel's
+// seen-event cache. (The split-K record regions are sized in dims_from_desc.)
+int check_fit(const Dims& dm) {
+  const int G = dm.grid;
+  for (int st = 0; st < 4; ++st) {
+    if (dm.moe && st >= 2) continue;
+    int K, U, R;
+    stage_dims(dm, st, K, U, R);
+    const int tiles_min = std::min(st <= 1 ? G - G / 4 : G, U);
+    const long row_bytes = 4L * (ceil_div(K, dm.kstep) * dm.kstep + dm.xpad);
+    if (row_bytes + 16 + 4L * ceil_div(U, tiles_min) * R > kXyBytes) return PMK_ERR_UNSUPPORTED;
+  }
+  if ((long)dm.L * ev_layer_ints(dm) >= (1L << 27)) return PMK_ERR_UNSUPPORTED;
+  return PMK_OK;
+}
+
+// The workspace carved from `base` in 256-byte aligned parts (base nullptr:
+// sizes only). Returns the bytes it takes, or 0 when a part (a layer's slice
+// of a per-layer part) reaches 1 GiB: step intermediates are addressed with
+// 32-bit byte offsets from one buffer base and stay below the kernels'
+// out-of-range marker offset.
+size_t carve(const Dims& dm, Workspace& ws, char* base) {
+  struct Part { void** p; size_t bytes, per_layer; };
+  Part parts[48];
+  int n = 0;
+  auto add = [&](void* p, size_t bytes, size_t per_layer = 0) { parts[n++] = Part{(void**)p, bytes, per_layer}; };
+  const size_t B = (size_t)dm.max_batch, qkv_dim = (size_t)(dm.Hq + 2 * dm.Hkv) * dm.d, Gq = dm.Hq / dm.Hkv;
+  const size_t TK = B * std::max(dm.k, 1), F = std::max(dm.F, 1), mb = std::max(dm.merge_b, 1);
+  add(&ws.qkv, dm.L * B * qkv_dim * 4, B * qkv_dim * 4);
+  add(&ws.o, dm.L * B * dm.Hq * dm.d * 4, B * dm.Hq * dm.d * 4);
+  add(&ws.h1, dm.L * B * dm.H * 4, B * dm.H * 4);
+  add(&ws.act, dm.L * B * F * 4, B * F * 4);
+  add(&ws.hid, (size_t)std::max(dm.L - 1, 1) * B * dm.H * 4, B * dm.H * 4);
+  add(&ws.part, B * dm.Hkv * dm.max_chunks * Gq * (dm.d + 4) * 4);
+  add(&ws.mpart, dm.L * mb * dm.Hkv * kMergeChunks * Gq * (dm.d + 4) * 4, mb * dm.Hkv * kMergeChunks * Gq * (dm.d + 4) * 4);
+  add(&ws.rope, (size_t)dm.max_seq * (dm.d / 2) * 8);
+  add(&ws.ev, (size_t)dm.L * ev_layer_ints(dm) * 4);
+  add(&ws.mctr, dm.L * B * dm.Hkv * kCtr * 4);
+  add(&ws.chunk_base, (B + 1) * 4);
+  add(&ws.queue, (size_t)dm.grid * dm.max_queue * 16);
+  add(&ws.qev, (size_t)dm.grid * dm.max_queue * 16);
+  add(&ws.qlen, (size_t)dm.grid * 4);
+  add(&ws.err, 64 * 4);
+  add(&ws.args, sizeof(StepArgs));
+  add(&ws.kpart, (size_t)dm.kpart_off[4] * 4);
+  add(&ws.tctr, (size_t)4 * dm.tctr_stride * kCtr * 4);
+  add(&ws.bar, (size_t)dm.L * kMaxStages * kEvInts * 4);
+  add(&ws.u, B * dm.H * 4);
+  if (dm.moe) {
+    add(&ws.logits, B * dm.E * 4);
+    add(&ws.topk_idx, TK * 4);
+    add(&ws.topk_w, TK * 4);
+    add(&ws.exp_indptr, (size_t)(dm.E + 1) * 4);
+    add(&ws.sorted_tok, TK * 4);
+    add(&ws.sorted_slot, TK * 4);
+    add(&ws.pos_of, TK * 4);
+    add(&ws.tile_info, (size_t)dm.max_tiles * 2 * 4);
+    add(&ws.moe_info, 64 * 4);
+    add(&ws.ectr, (size_t)dm.L * dm.E * kCtr * 4);
+    add(&ws.tile_ptr, (size_t)(dm.E + 1) * 4);
+    add(&ws.rq, (size_t)dm.L * dm.max_down * 4);
+    add(&ws.mq, (size_t)dm.L * 2 * kCtr * 4);
+    add(&ws.mact, dm.L * TK * dm.Fe * 4, TK * dm.Fe * 4);
+    add(&ws.mout, TK * dm.H * 4);
+  }
+  size_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    if ((parts[i].per_layer ? parts[i].per_layer : parts[i].bytes) >= ((size_t)1 << 30)) return 0;
+    if (base) *parts[i].p = base + off;
+    off += align256(parts[i].bytes);
+  }
+  return off;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,91 +207,16 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* w, pmk_hand
 
   Dims& dm = h->dm;
   dm = dims_from_desc(*desc, prop.multiProcessorCount);
-  const int G = dm.grid;
-  // Dense stages: one input row of the whole depth and a tile's outputs must
-  // fit the LDS (a step may put its few attention tasks on workgroups of their
-  // own and the QKV and O tiles on the others, at least three quarters of the
-  // grid).
-  // (The split-K record regions are sized in dims_from_desc.)
-  for (int st = 0; st < 4; ++st) {
-    if (moe && st >= 2) continue;
-    int K, U, R;
-    stage_dims(dm, st, K, U, R);
-    const int tiles_min = std::min(st <= 1 ? G - G / 4 : G, U);
-    const long row_bytes = 4L * (ceil_div(K, dm.kstep) * dm.kstep + dm.xpad);
-    if (row_bytes + 16 + 4L * ceil_div(U, tiles_min) * R > kXyBytes) {
-      delete h;
-      return PMK_ERR_UNSUPPORTED;
-    }
-  }
-  // workspace carving
-  const int qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d;
-  const int Gq = dm.Hq / dm.Hkv;
-  // per_layer: the part holds one slice per layer (each addressed from its own base)
-  struct Part { void** p; size_t bytes; size_t per_layer = 0; };
+  rc = check_fit(dm);
+  if (rc) { delete h; return rc; }
   Workspace& ws = h->ws;
-  const size_t TK = (size_t)dm.max_batch * std::max(dm.k, 1);
-  std::vector<Part> parts = {
-      {(void**)&ws.qkv, (size_t)dm.L * dm.max_batch * qkv_dim * 4, (size_t)dm.max_batch * qkv_dim * 4},
-      {(void**)&ws.o, (size_t)dm.L * dm.max_batch * dm.Hq * dm.d * 4, (size_t)dm.max_batch * dm.Hq * dm.d * 4},
-      {(void**)&ws.h1, (size_t)dm.L * dm.max_batch * dm.H * 4, (size_t)dm.max_batch * dm.H * 4},
-      {(void**)&ws.act, (size_t)dm.L * dm.max_batch * std::max(dm.F, 1) * 4,
-       (size_t)dm.max_batch * std::max(dm.F, 1) * 4},
-      {(void**)&ws.hid, (size_t)std::max(dm.L - 1, 1) * dm.max_batch * dm.H * 4, (size_t)dm.max_batch * dm.H * 4},
-      {(void**)&ws.part, (size_t)dm.max_batch * dm.Hkv * dm.max_chunks * Gq * (dm.d + 4) * 4},
-      {(void**)&ws.mpart, (size_t)dm.L * std::max(dm.merge_b, 1) * dm.Hkv * kMergeChunks * Gq * (dm.d + 4) * 4,
-       (size_t)std::max(dm.merge_b, 1) * dm.Hkv * kMergeChunks * Gq * (dm.d + 4) * 4},
-      {(void**)&ws.rope, (size_t)dm.max_seq * (dm.d / 2) * 8},
-      {(void**)&ws.ev, (size_t)dm.L * ev_layer_ints(dm) * 4},
-      {(void**)&ws.mctr, (size_t)dm.L * dm.max_batch * dm.Hkv * kCtr * 4},
-      {(void**)&ws.chunk_base, (size_t)(dm.max_batch + 1) * 4},
-      {(void**)&ws.queue, (size_t)G * dm.max_queue * 16},
-      {(void**)&ws.qev, (size_t)G * dm.max_queue * 16},
-      {(void**)&ws.qlen, (size_t)G * 4},
-      {(void**)&ws.err, 64 * 4},
-      {(void**)&ws.args, sizeof(StepArgs)},
-      {(void**)&ws.kpart, (size_t)dm.kpart_off[4] * 4},
-      {(void**)&ws.tctr, (size_t)4 * dm.tctr_stride * kCtr * 4},
-      {(void**)&ws.bar, (size_t)dm.L * kMaxStages * kEvInts * 4},
-      {(void**)&ws.u, (size_t)dm.max_batch * dm.H * 4},
-  };
-  if (moe) {
-    const std::vector<Part> mp = {
-        {(void**)&ws.logits, (size_t)dm.max_batch * dm.E * 4},
-        {(void**)&ws.topk_idx, TK * 4},
-        {(void**)&ws.topk_w, TK * 4},
-        {(void**)&ws.exp_indptr, (size_t)(dm.E + 1) * 4},
-        {(void**)&ws.sorted_tok, TK * 4},
-        {(void**)&ws.sorted_slot, TK * 4},
-        {(void**)&ws.pos_of, TK * 4},
-        {(void**)&ws.tile_info, (size_t)dm.max_tiles * 2 * 4},
-        {(void**)&ws.moe_info, 64 * 4},
-        {(void**)&ws.ectr, (size_t)dm.L * dm.E * kCtr * 4},
-        {(void**)&ws.tile_ptr, (size_t)(dm.E + 1) * 4},
-        {(void**)&ws.rq, (size_t)dm.L * dm.max_down * 4},
-        {(void**)&ws.mq, (size_t)dm.L * 2 * kCtr * 4},
-        {(void**)&ws.mact, (size_t)dm.L * TK * dm.Fe * 4, TK * dm.Fe * 4},
-        {(void**)&ws.mout, TK * dm.H * 4},
-    };
-    parts.insert(parts.end(), mp.begin(), mp.end());
-  }
-  // event offsets are 27-bit keys of the persistent kernel's seen-event cache
-  if ((long)dm.L * ev_layer_ints(dm) >= (1L << 27)) { delete h; return PMK_ERR_UNSUPPORTED; }
-  // step intermediates are addressed with 32-bit byte offsets from one buffer
-  // base, and stay below the kernels' out-of-range marker offset (1 GiB)
-  for (auto& p : parts)
-    if ((p.per_layer ? p.per_layer : p.bytes) >= ((size_t)1 << 30)) { delete h; return PMK_ERR_ARG; }
-  size_t total = 0;
-  for (auto& p : parts) total += align256(p.bytes);
+  const size_t total = carve(dm, ws, nullptr);
+  if (total == 0) { delete h; return PMK_ERR_ARG; }
   void* base = nullptr;
   if (hipMalloc(&base, total) != hipSuccess) { delete h; return PMK_ERR_OOM; }
   h->ws_base = base;
   h->ws_bytes = total;
-  size_t off = 0;
-  for (auto& p : parts) {
-    *p.p = (char*)base + off;
-    off += align256(p.bytes);
-  }
+  (void)carve(dm, ws, (char*)base);
   auto fail = [&](int code) {
     decode_layer_destroy(h);
     return code;
