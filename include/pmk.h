@@ -52,7 +52,8 @@ enum pmk_status {
   PMK_ERR_DEVICE = 3,       /* a HIP call failed (launch, copy, event) */
   PMK_ERR_TIMEOUT = 4,      /* device: an event wait exceeded the watchdog; the step was abandoned */
   PMK_ERR_SEQ = 5,          /* device: seq_lens[b] < 0 or >= max_seq; the step did not run */
-  PMK_ERR_UNSUPPORTED = 6   /* a shape this build does not implement (see pmk_strerror) */
+  PMK_ERR_UNSUPPORTED = 6,  /* a shape this build does not implement (see pmk_strerror) */
+  PMK_ERR_SCRATCH = 7       /* decode_step_static: the model's workspace exceeds its 64 MiB static scratch */
 };
 
 enum pmk_dtype { PMK_F32 = 0, PMK_BF16 = 1 };
@@ -165,6 +166,31 @@ int decode_layer_init(const pmk_model_desc* desc, const pmk_weights* weights, pm
  * device error from an earlier step that has reached the host mirror
  * (PMK_ERR_SEQ, PMK_ERR_TIMEOUT; nothing is launched), PMK_ERR_DEVICE. */
 int decode_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq_lens, int32_t batch, void* stream);
+
+/* decode_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. One
+ * call does what decode_layer_init and decode_step do, with no handle: the
+ * workspace (counters, queues, activations, the RoPE table, the layer-pointer
+ * table) lives in a file-scope device array of 64 MiB that each GPU the
+ * library runs on holds until the process ends. The call makes no hipMalloc,
+ * hipFree or other allocation; it launches a clearing kernel, the RoPE-table
+ * kernel, a host-to-device copy of weights->layers, the prologue and the
+ * persistent kernel (fused schedule, per-tile events, the descriptor's
+ * watchdog), all on `stream`.
+ *   desc, weights  as for decode_layer_init; dense stacks only (n_experts = 0,
+ *                  else PMK_ERR_UNSUPPORTED). weights->layers must stay
+ *                  valid until the copy has run on the stream.
+ *   hidden, kv_cache, seq_lens, batch, stream  as for decode_step.
+ *   status   nullable device int32: set to 0 when the step starts and to the
+ *            device error code (PMK_ERR_SEQ, PMK_ERR_TIMEOUT) if the step hits
+ *            one; there is no handle to hold it for a later call.
+ * Every call on a GPU shares that GPU's scratch, which keeps the last call's
+ * contents (each call clears what must start at zero): calls that overlap on
+ * one GPU, on any streams, race. Errors: PMK_ERR_ARG, PMK_ERR_UNSUPPORTED,
+ * PMK_ERR_SCRATCH (the workspace for desc is larger than the scratch: fewer
+ * layers, a smaller max_batch or max_seq), PMK_ERR_DEVICE. */
+int decode_step_static(const pmk_model_desc* desc, const pmk_weights* weights, float* hidden, void* kv_cache,
+                       const int32_t* seq_lens, int32_t batch, int32_t* status, void* stream);
 
 /* One step of a stack of MoE decoder layers for `tokens` tokens, each its own
  * request (Event Tensor summary, Key observations, observation 2: attention,

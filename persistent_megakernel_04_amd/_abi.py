@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libpmk.so")
 
 PMK_ABI_VERSION = 1
-PMK_OK, PMK_ERR_ARG, PMK_ERR_OOM, PMK_ERR_DEVICE, PMK_ERR_TIMEOUT, PMK_ERR_SEQ, PMK_ERR_UNSUPPORTED = range(7)
+(PMK_OK, PMK_ERR_ARG, PMK_ERR_OOM, PMK_ERR_DEVICE, PMK_ERR_TIMEOUT, PMK_ERR_SEQ, PMK_ERR_UNSUPPORTED,
+ PMK_ERR_SCRATCH) = range(8)
 PMK_F32, PMK_BF16 = 0, 1
 PMK_ROWS, PMK_TILES = 0, 1
 
@@ -30,7 +31,7 @@ MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC}
 EXPORTS = ("decode_layer_init", "decode_step", "moe_layer_step", "decode_layer_destroy", "pmk_strerror",
            "pmk_get_device_error", "pmk_query", "pmk_timing_enable", "pmk_timing_read", "pmk_trace_attach",
            "pmk_set_schedule", "pmk_set_moe_scheduler", "pmk_set_watchdog_us", "pmk_pack_weights",
-           "pmk_stream_probe", "pmk_set_event_granularity")
+           "pmk_stream_probe", "pmk_set_event_granularity", "decode_step_static")
 
 i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -111,6 +112,8 @@ def load():
     L.pmk_stream_probe.restype = i32
     L.pmk_set_event_granularity.argtypes = [vp, i32]
     L.pmk_set_event_granularity.restype = i32
+    L.decode_step_static.argtypes = [P(ModelDesc), P(Weights), vp, vp, vp, i32, vp, vp]
+    L.decode_step_static.restype = i32
     _lib = L
     return L
 

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <utility>
 #include <vector>
@@ -164,6 +165,59 @@ size_t carve(const Dims& dm, Workspace& ws, char* base) {
   return off;
 }
 
+
+// ---------------------------------------------------------------------------
+// decode_step_static: the no-allocation entry point. Its workspace (the
+// handle's, plus the RoPE table and the layer-pointer table) is carved from
+// `scratch`, a file-scope device array each GPU holds for the life of the
+// process; host code reaches it only through the address that
+// hipGetSymbolAddress returns for the current device (the array's name in
+// host code is a host-side stand-in, not a device address).
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void* g_scratch[kMaxDevices];   // scratch's device address, per device
+int g_static_grid[kMaxDevices];
+
+// Set-up on the current device, once: scratch's address and the grid.
+int static_setup(int dev, char** ptr, int* grid) {
+  if (dev < 0 || dev >= kMaxDevices) return PMK_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PMK_ERR_DEVICE;
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1)
+      return PMK_ERR_DEVICE;
+    g_static_grid[dev] = cu;
+    g_scratch[dev] = p;
+  }
+  *ptr = (char*)g_scratch[dev];
+  *grid = g_static_grid[dev];
+  return PMK_OK;
+}
+
+// The error word and abort flag cleared, and the caller's status word.
+__global__ void static_clear(int* err, int32_t* status) {
+  err[threadIdx.x] = 0;
+  if (threadIdx.x == 0 && status) *status = 0;
+}
+
+// The RoPE table on the device, as decode_layer_init writes it on the host:
+// angle p theta^(-2i/d) in double, cos and sin rounded to float.
+__global__ void static_rope(float2* tab, int max_seq, int half, int d, double theta) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= max_seq * half) return;
+  const int p = idx / half, i = idx - p * half;
+  const double phi = (double)p * pow(theta, -2.0 * i / (double)d);
+  tab[idx] = make_float2((float)cos(phi), (float)sin(phi));
+}
+
+static_assert(sizeof(LayerPtrs) == sizeof(pmk_layer_weights), "the layer table is copied as the caller gives it");
+
 }  // namespace
 
 extern "C" {
@@ -176,6 +230,9 @@ const char* pmk_strerror(int s) {
     case PMK_ERR_DEVICE: return "HIP runtime call failed";
     case PMK_ERR_TIMEOUT: return "an event wait exceeded the watchdog; the step was abandoned";
     case PMK_ERR_SEQ: return "a request length is outside [0, max_seq); the step did not run";
+    case PMK_ERR_SCRATCH:
+      return "the model's workspace exceeds the 64 MiB static scratch of decode_step_static (fewer layers, a "
+             "smaller max_batch or max_seq)";
     case PMK_ERR_UNSUPPORTED:
       return "shape not implemented: needs head_dim*sizeof(dtype) == 256, Hq/Hkv in {1,2,4,8}, Hkv <= 128, max_batch <= 1024, "
              "GEMV depths that fit one LDS input row, and for MoE E <= 512, top_k <= 8, H and Fe small enough "
@@ -363,6 +420,58 @@ int pmk_set_schedule(pmk_handle* h, int32_t mode) {
 
 int decode_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq_lens, int32_t batch, void* stream) {
   return run_step(h, hidden, kv_cache, seq_lens, batch, nullptr, stream);
+}
+
+int decode_step_static(const pmk_model_desc* desc, const pmk_weights* w, float* hidden, void* kv_cache,
+                       const int32_t* seq_lens, int32_t batch, int32_t* status, void* stream) {
+  int rc = check_desc(desc);
+  if (rc) return rc;
+  if (desc->n_experts > 0) return PMK_ERR_UNSUPPORTED;   // dense stacks only
+  if (!w || w->n_layers != desc->n_layers || !w->layers || !hidden || !kv_cache || !seq_lens) return PMK_ERR_ARG;
+  if (batch < 1 || batch > desc->max_batch) return PMK_ERR_ARG;
+  for (int l = 0; l < desc->n_layers; ++l) {
+    const pmk_layer_weights& L = w->layers[l];
+    if (!L.attn_norm || !L.w_qkv || !L.w_o || !L.ffn_norm || !L.w_gate || !L.w_up || !L.w_down) return PMK_ERR_ARG;
+  }
+  int dev = 0, grid = 0;
+  char* base = nullptr;
+  if (hipGetDevice(&dev) != hipSuccess) return PMK_ERR_DEVICE;
+  rc = static_setup(dev, &base, &grid);
+  if (rc) return rc;
+  const Dims dm = dims_from_desc(*desc, grid);
+  rc = check_fit(dm);
+  if (rc) return rc;
+  Workspace ws{};
+  const size_t wbytes = carve(dm, ws, nullptr);
+  const size_t lbytes = align256(sizeof(LayerPtrs) * dm.L);
+  // (a part of 1 GiB or more, carve's 0, is far beyond the scratch as well)
+  if (wbytes == 0 || wbytes + lbytes > kStaticScratchBytes) return PMK_ERR_SCRATCH;
+  (void)carve(dm, ws, base);
+  LayerPtrs* layers = reinterpret_cast<LayerPtrs*>(base + wbytes);
+  ws.err_host = status;   // the kernels copy a device error here
+  hipStream_t s = (hipStream_t)stream;
+  if (prepare_main(desc->dtype, dm.wtiles) != hipSuccess) return PMK_ERR_DEVICE;
+  hipLaunchKernelGGL(static_clear, dim3(1), dim3(64), 0, s, ws.err, status);
+  const int half = dm.d / 2, nrope = dm.max_seq * half;
+  hipLaunchKernelGGL(static_rope, dim3((nrope + 255) / 256), dim3(256), 0, s, reinterpret_cast<float2*>(ws.rope),
+                     dm.max_seq, half, dm.d, (double)desc->rope_theta);
+  if (hipGetLastError() != hipSuccess) return PMK_ERR_DEVICE;
+  if (hipMemcpyAsync(layers, w->layers, sizeof(LayerPtrs) * dm.L, hipMemcpyHostToDevice, s) != hipSuccess)
+    return PMK_ERR_DEVICE;
+  StepArgs a{};
+  a.dm = dm;
+  a.ws = ws;
+  a.layers = layers;
+  a.hidden = hidden;
+  a.kv = kv_cache;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.qkv_tiles = dm.qkv_tiles;
+  a.watchdog_ticks = (unsigned long long)(desc->watchdog_ms > 0 ? desc->watchdog_ms : 2000) * 100000ull;
+  a.ev_mode = PMK_EVENTS_TILE;
+  if (launch_prologue(a, s) != hipSuccess) return PMK_ERR_DEVICE;
+  if (launch_main(a, desc->dtype, s, RunSpec{0, dm.L, kAllTypes, 0}) != hipSuccess) return PMK_ERR_DEVICE;
+  return PMK_OK;
 }
 
 int moe_layer_step(pmk_handle* h, float* hidden, void* kv_cache, const int32_t* seq_lens, int32_t tokens,

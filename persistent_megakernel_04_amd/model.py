@@ -106,6 +106,16 @@ class DecodeModel:
         return self.lib.moe_layer_step(self.handle, _ptr(hidden), _ptr(kv_cache), _ptr(seq_lens),
                                        int(hidden.shape[0]), None if r is None else ctypes.byref(r), _stream())
 
+    def decode_step_static(self, hidden: torch.Tensor, kv_cache: torch.Tensor, seq_lens: torch.Tensor,
+                           status: torch.Tensor | None = None) -> int:
+        """Raw status of decode_step_static with this model's descriptor and
+        weights: the same step without the handle's workspace (the library's
+        static scratch instead; nothing is allocated). `status`: an optional
+        one-element int32 device tensor for the step's device error code."""
+        w = _abi.Weights(self.desc.n_layers, self._arr)
+        return self.lib.decode_step_static(ctypes.byref(self.desc), ctypes.byref(w), _ptr(hidden), _ptr(kv_cache),
+                                           _ptr(seq_lens), int(hidden.shape[0]), _ptr(status), _stream())
+
     def step(self, hidden, kv_cache, seq_lens, routing=None):
         """Checked call: decode_step (dense) or moe_layer_step (MoE)."""
         if self.desc.n_experts:

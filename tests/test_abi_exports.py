@@ -54,6 +54,9 @@ def test_strerror_and_null_handle_errors_need_no_gpu():
     assert lib.pmk_timing_enable(None, 1) == _abi.PMK_ERR_ARG
     out = ctypes.c_void_p()
     assert lib.decode_layer_init(None, None, ctypes.byref(out)) == _abi.PMK_ERR_ARG
+    # the no-allocation step checks its descriptor and pointers before any HIP call
+    assert lib.decode_step_static(None, None, None, None, None, 1, None, None) == _abi.PMK_ERR_ARG
+    assert b"scratch" in lib.pmk_strerror(_abi.PMK_ERR_SCRATCH)
 
 
 def test_pack_weights_and_tile_layout_argument_checks_need_no_gpu():
