@@ -32,7 +32,8 @@ constexpr int kMaxStages = 8;            // stages of a layer (MoE: QKV, attenti
 constexpr int kXyBytes = 147968;
 constexpr int kRedBytes = 8192;
 constexpr int kMiscBytes = 2048;
-constexpr int kLdsBytes = kXyBytes + kRedBytes + kMiscBytes;
+constexpr int kRopeBytes = 4096;         // the QKV tile's rotation rows, kept across the layers of a launch
+constexpr int kLdsBytes = kXyBytes + kRedBytes + kMiscBytes + kRopeBytes;
 constexpr int kXsBytes = 131584;         // staged inputs of a pass at most (the rest of xy holds ys)
 constexpr int kYsFloats = 2048;          // outputs of a pass whose residual is loaded ahead (O, down)
 constexpr int kRingK = 16;               // weight loads in flight per wave

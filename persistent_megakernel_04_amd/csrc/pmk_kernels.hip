@@ -47,6 +47,9 @@ struct Lds {
   int* flag;       // wait / last-arriver broadcast
   uint32_t* tclk;  // [8] phase clocks of the current task (trace): see the trace record layout
   int* seen;       // [8] per wait kind, the event offset this workgroup last saw fired (+ 1; 0: none)
+  int* rope_key;   // [3] the QKV pass whose rotation rows rope holds: first unit + 1, first request, elements 32 + nb
+  int* rope_pos;   // [kMaxNb] its requests' positions
+  float2* rope;    // [kRopeBytes / 8] its (cos, sin) per element
 };
 
 __device__ __forceinline__ Lds lds_layout(char* base) {
@@ -59,6 +62,9 @@ __device__ __forceinline__ Lds lds_layout(char* base) {
   s.flag = reinterpret_cast<int*>(m + 64 + 512);          // 1 int
   s.tclk = reinterpret_cast<uint32_t*>(m + 64 + 512 + 16);   // 8 clocks
   s.seen = reinterpret_cast<int*>(m + 64 + 512 + 16 + 32);   // 8 ints
+  s.rope_key = reinterpret_cast<int*>(m + 64 + 512 + 16 + 32 + 32);   // 4 ints
+  s.rope_pos = reinterpret_cast<int*>(m + 64 + 512 + 16 + 32 + 48);   // 16 ints
+  s.rope = reinterpret_cast<float2*>(m + kMiscBytes);
   return s;
 }
 
@@ -907,18 +913,44 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
       }
       // lane m < nb holds request b0 + m's position; the rotation rows of
       // eight items per lane are loaded together (one latency per eight
-      // items, not two dependent ones per item)
-      const int posl = *gp(a.seq_lens + b0 + (lane < nb ? lane : 0));
+      // items, not two dependent ones per item). A workgroup takes the same
+      // QKV pass in every layer of a launch, at the same positions: the
+      // first layer's rows are kept in LDS (rope, keyed by the pass) and the
+      // later layers read them there instead of from memory.
+      // (a wave-uniform flag, so that a hit branches around the loads
+      // instead of issuing them and selecting)
+      const bool hit = __builtin_amdgcn_readfirstlane(c.s.rope_key[0] == ps.r0 + 1 && c.s.rope_key[1] == b0 &&
+                                                      c.s.rope_key[2] == ni * 32 + nb) != 0;
+      const bool keep = !hit && ni <= kRopeBytes / 8;
+      int posl;
+      if (hit)
+        posl = c.s.rope_pos[lane < nb ? lane : 0];
+      else
+        posl = *gp(a.seq_lens + b0 + (lane < nb ? lane : 0));
+      if (keep && t0 < 64 && lane < nb) c.s.rope_pos[lane] = posl;   // the first wave of the pass: one per request
       const auto rrs = rsrc_n(a.ws.rope, dm.max_seq * half * 8);
       for (int base = 0; base < ni; base += nt * 8) {
         float2 cs[8];
         int hs[8], is[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int idx = base + t0 + nt * u, m = idx & ((1 << sh) - 1);
-          unit_hi(min(idx >> sh, ps.n - 1), hs[u], is[u]);
-          const int pos = __shfl(posl, m, 64);
-          cs[u] = ldk2(rrs, idx < ni && m < nb && hs[u] < dm.Hq + dm.Hkv ? (pos * half + is[u]) * 8 : kNoRecord);
+        for (int u = 0; u < 8; ++u) unit_hi(min((base + t0 + nt * u) >> sh, ps.n - 1), hs[u], is[u]);
+        if (hit) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) cs[u] = c.s.rope[min(base + t0 + nt * u, ni - 1)];
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int idx = base + t0 + nt * u, m = idx & ((1 << sh) - 1);
+            const int pos = __shfl(posl, m, 64);
+            cs[u] = ldk2(rrs, idx < ni && m < nb && hs[u] < dm.Hq + dm.Hkv ? (pos * half + is[u]) * 8 : kNoRecord);
+          }
+        }
+        if (keep) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int idx = base + t0 + nt * u;
+            if (idx < ni) c.s.rope[idx] = cs[u];
+          }
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -944,6 +976,13 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
             Elem<WT>::put(cp + i + half, y2);
           }
         }
+      }
+      // the kept rows are read by this workgroup's next QKV pass, a later
+      // task: every task starts with a workgroup barrier
+      if (keep && t0 == 0) {
+        c.s.rope_key[0] = ps.r0 + 1;
+        c.s.rope_key[1] = b0;
+        c.s.rope_key[2] = ni * 32 + nb;
       }
       break;
     }
@@ -2013,6 +2052,8 @@ __device__ __forceinline__ void main_body(const StepArgs& a, RunSpec rs, char* l
   const Lds s = lds_layout(lds_raw);
   if (threadIdx.x == 0) *s.flag = (ldci(a.ws.err) == 0);
   if (threadIdx.x < 8) s.seen[threadIdx.x] = 0;
+  if (threadIdx.x < 3) s.rope_key[threadIdx.x] = 0;
+  if (threadIdx.x < kMaxNb) s.rope_pos[threadIdx.x] = 0;
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*s.flag)) return;
   const int n = ldku(a.ws.qlen + wg);
