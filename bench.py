@@ -282,9 +282,9 @@ def main():
                     "an ablation that puts a kernel boundary after every layer / every stage of a layer; barrier: "
                     "one launch with a grid-wide barrier after every stage; op: one launch per operator, ten per "
                     "layer, with the norms, RoPE, KV append and attention merge as operators of their own")
-    ap.add_argument("--moe-scheduler", default="static", choices=["static", "dynamic"],
-                    help="MoE workloads: grouped expert tasks as fixed per-workgroup shares (static) or popped from "
-                    "a per-layer queue (dynamic)")
+    ap.add_argument("--moe-scheduler", default="static", choices=["static", "dynamic", "xcd"],
+                    help="MoE workloads: grouped expert tasks as fixed per-workgroup shares (static), popped from "
+                    "a per-layer queue (dynamic) or from per-XCD queues with stealing (xcd)")
     ap.add_argument("--flush-cache", action="store_true",
                     help="between timed steps, write a 1 GiB buffer so that no weight stays in the 256 MB "
                     "memory-side cache (for working sets that fit it, e.g. the MoE layer at one token); the "

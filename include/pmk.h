@@ -288,10 +288,18 @@ int pmk_set_schedule(pmk_handle* h, int32_t mode);
  *                    queue that the last gate/up task of each expert fills
  *                    with that expert's down tasks when the expert's counter
  *                    reaches zero.
- * Same results either way. Ignored by dense handles; applies to later calls.
- * Errors: PMK_ERR_ARG (null handle, unknown mode). */
+ *   PMK_MOE_DYNAMIC_XCD  the same tasks and ready queue, popped hierarchically
+ *                    (the pages leave the GPU scheduler's hierarchy as future
+ *                    work; Event Tensor summary, Limitations and future
+ *                    work): one counter per XCD, each over the task indices
+ *                    congruent to that XCD's id mod 8, so a workgroup's pops
+ *                    stay on its own XCD's counter; a workgroup whose XCD
+ *                    counter has run out steals from the others.
+ * Same results in every mode. Ignored by dense handles; applies to later
+ * calls. Errors: PMK_ERR_ARG (null handle, unknown mode). */
 #define PMK_MOE_STATIC 0
 #define PMK_MOE_DYNAMIC 1
+#define PMK_MOE_DYNAMIC_XCD 2
 int pmk_set_moe_scheduler(pmk_handle* h, int32_t mode);
 
 /* The event-wait limit of later calls, in microseconds (100 ticks of the

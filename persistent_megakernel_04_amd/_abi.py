@@ -25,8 +25,8 @@ SCHEDULES = {"fused": SCHED_FUSED, "layer": SCHED_PER_LAYER, "stage": SCHED_PER_
 EVENTS_TILE, EVENTS_GROUP, EVENTS_STAGE = 0, 1, 2
 EVENT_MODES = {"tile": EVENTS_TILE, "group": EVENTS_GROUP, "stage": EVENTS_STAGE}
 # pmk_set_moe_scheduler modes
-MOE_STATIC, MOE_DYNAMIC = 0, 1
-MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC}
+MOE_STATIC, MOE_DYNAMIC, MOE_DYNAMIC_XCD = 0, 1, 2
+MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC, "xcd": MOE_DYNAMIC_XCD}
 
 EXPORTS = ("decode_layer_init", "decode_step", "moe_layer_step", "decode_layer_destroy", "pmk_strerror",
            "pmk_get_device_error", "pmk_query", "pmk_timing_enable", "pmk_timing_read", "pmk_trace_attach",

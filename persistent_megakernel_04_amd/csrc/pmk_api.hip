@@ -152,7 +152,7 @@ size_t carve(const Dims& dm, Workspace& ws, char* base) {
     add(&ws.ectr, (size_t)dm.L * dm.E * kCtr * 4);
     add(&ws.tile_ptr, (size_t)(dm.E + 1) * 4);
     add(&ws.rq, (size_t)dm.L * dm.max_down * 4);
-    add(&ws.mq, (size_t)dm.L * 2 * kCtr * 4);
+    add(&ws.mq, (size_t)dm.L * kMq * kCtr * 4);
     add(&ws.mact, dm.L * TK * dm.Fe * 4, TK * dm.Fe * 4);
     add(&ws.mout, TK * dm.H * 4);
   }
@@ -360,7 +360,7 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
   a.barrier = h->sched == PMK_SCHED_BARRIER;
   a.per_op = h->sched == PMK_SCHED_PER_OP;
   a.ev_mode = h->ev_mode;
-  a.moe_dyn = h->dm.moe && h->moe_sched == PMK_MOE_DYNAMIC;
+  a.moe_dyn = !h->dm.moe ? 0 : h->moe_sched == PMK_MOE_DYNAMIC ? 1 : h->moe_sched == PMK_MOE_DYNAMIC_XCD ? 2 : 0;
   h->last_stream = s;
   if (launch_prologue(a, s) != hipSuccess) return PMK_ERR_DEVICE;
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -399,7 +399,7 @@ static int run_step(pmk_handle* h, float* hidden, void* kv, const int32_t* seq_l
 }
 
 int pmk_set_moe_scheduler(pmk_handle* h, int32_t mode) {
-  if (!h || (mode != PMK_MOE_STATIC && mode != PMK_MOE_DYNAMIC)) return PMK_ERR_ARG;
+  if (!h || mode < PMK_MOE_STATIC || mode > PMK_MOE_DYNAMIC_XCD) return PMK_ERR_ARG;
   h->moe_sched = mode;
   return PMK_OK;
 }

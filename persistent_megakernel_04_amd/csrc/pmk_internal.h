@@ -12,6 +12,8 @@ constexpr int kBlock = 512;              // threads per persistent workgroup: 8 
 constexpr int kWaves = kBlock / 64;
 constexpr int kSubs = 8;                 // sub-counters of a hierarchical event
 constexpr int kCtr = 16;                 // ints between two counters (64 bytes)
+constexpr int kXcd = 8;                  // XCDs of the device (the per-XCD task queues of the dynamic MoE scheduler)
+constexpr int kMq = 2 + kXcd;            // per layer: the central pop counter, the push counter, a pop counter per XCD
 constexpr int kEvInts = (1 + kSubs) * kCtr;
 constexpr int kMinChunk = 64;            // smallest attention chunk (KV positions per tile task)
 constexpr int kPieceCost = 320;          // streamed attention: a piece's fixed cost in KV positions
@@ -198,7 +200,7 @@ struct Workspace {
   int* ectr;           // [L][E][kCtr]                  per-expert counters (gate/up -> down)
   int* tile_ptr;       // [E + 1]                       first row tile of each expert (tile_indptr)
   int* rq;             // [L][max_down]                 dynamic: ready down tasks, index + 1 (0: not yet pushed)
-  int* mq;             // [L][2][kCtr]                  dynamic: pop counter, push counter
+  int* mq;             // [L][kMq][kCtr]                dynamic: pop counter, push counter, per-XCD pop counters
   float* mact;         // [L][max_batch k][Fe]          expert SwiGLU rows, grouped order (per layer)
   float* mout;         // [max_batch k][H]              expert down rows, grouped order
   float* u;            // [max_batch][H]                per-op schedule: the RMSNorm output a projection reads
@@ -222,7 +224,7 @@ struct StepArgs {
   uint32_t* trace;                     // optional task trace [grid][trace_cap][8], caller-owned
   int trace_cap;                       // entries per workgroup (entry 0 is the header)
   int barrier;                         // 1: the barrier schedule (the prologue arms ws.bar)
-  int moe_dyn;                         // 1: grouped expert tasks popped from a per-layer queue
+  int moe_dyn;                         // 1: grouped expert tasks popped from a per-layer queue; 2: per-XCD queues
   int per_op;                          // 1: the per-op schedule (norms, RoPE, append, merge as ops of their own)
   int ev_mode;                         // granularity of the dense chain's events (pmk_sched.h: EvMode)
 };

@@ -594,6 +594,32 @@ struct Pass {
 // their split from this step's geometry: task (tile, K slice) covers all
 // batch rows in one pass when the depth is split, else passes of what the LDS
 // holds (a task whose stage is not split has slice 0).
+// The XCD this workgroup runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ int xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kXcd - 1); }
+
+// One thread: the next grouped expert task index of layer l's dynamic queue,
+// or n (the count of tasks) when none is left. Central: one counter for every
+// workgroup. Per XCD: counter x hands out the indices x, x + 8, x + 16, ...;
+// a workgroup takes its own XCD's next index, else steals the next index of
+// another XCD's counter (reading each first, to skip exhausted ones without an
+// atomic). Each counter hands out its gate/up indices (below the count of
+// gate/up tasks) before its down indices, so a workgroup that waits on a down
+// task's ready-queue slot implies that every gate/up task is held by a
+// workgroup that runs it: the queue cannot deadlock.
+__device__ __forceinline__ int moe_pop(const StepArgs& a, int l, int n) {
+  int* mq = a.ws.mq + (size_t)l * kMq * kCtr;
+  if (a.moe_dyn != 2) return min(atomic_add_relaxed(mq, 1), n);
+  const int x = xcd_id();
+  for (int s = 0; s < kXcd; ++s) {
+    const int y = (x + s) & (kXcd - 1);
+    int* cy = mq + (2 + y) * kCtr;
+    if (s > 0 && y + kXcd * ldci(cy) >= n) continue;   // exhausted already
+    const int i = y + kXcd * atomic_add_relaxed(cy, 1);
+    if (i < n) return i;
+  }
+  return n;
+}
+
 template <typename WT, int KP>
 __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, const int* wev, Pass& ps) {
   const StepArgs& a = c.a;
@@ -708,7 +734,7 @@ __device__ __forceinline__ bool make_pass(const Ctx& c, const int4 task, int p, 
       if (a.moe_dyn) {
         // dynamic: the next index of the layer's queue, gate/up tasks [0, nmgu),
         // then down tasks in the order their experts became ready
-        if (threadIdx.x == 0) *c.s.flag = atomic_add_relaxed(a.ws.mq + (size_t)c.l * 2 * kCtr, 1);
+        if (threadIdx.x == 0) *c.s.flag = moe_pop(a, c.l, nmgu + ldsu(a.ws.moe_info + 1));
         __syncthreads();
         i = __builtin_amdgcn_readfirstlane(*c.s.flag);
         __syncthreads();
@@ -1019,7 +1045,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
           if (left == 1) {
             const int t0 = ldci(a.ws.tile_ptr + ps.e), t1 = ldci(a.ws.tile_ptr + ps.e + 1);
             const int sd = ldci(a.ws.moe_info + 3), n = (t1 - t0) * sd;
-            const int slot = __shfl(lane == 0 ? atomic_add_relaxed(a.ws.mq + ((size_t)c.l * 2 + 1) * kCtr, n) : 0, 0, 64);
+            const int slot = __shfl(lane == 0 ? atomic_add_relaxed(a.ws.mq + ((size_t)c.l * kMq + 1) * kCtr, n) : 0, 0, 64);
             int* rq = a.ws.rq + (size_t)c.l * dm.max_down + slot;
             for (int i = lane; i < n; i += 64) stci(rq + i, t0 * sd + i + 1);
           }
@@ -1840,7 +1866,7 @@ __device__ __forceinline__ bool task_route(const Ctx& c, const int* wev) {
   }
   if (a.moe_dyn) {   // this layer's task queue: empty, nothing popped or pushed yet
     for (int i = tid; i < ntiles * sd; i += kBlock) stci(a.ws.rq + (size_t)c.l * dm.max_down + i, 0);
-    if (tid < 2) stci(a.ws.mq + ((size_t)c.l * 2 + tid) * kCtr, 0);
+    if (tid < kMq) stci(a.ws.mq + ((size_t)c.l * kMq + tid) * kCtr, 0);
   }
   for (int i = tid; i < Tk; i += kBlock) stci(a.ws.topk_idx + i, sidx[i]);
   if (tid == 0) {

@@ -159,8 +159,9 @@ class DecodeModel:
         _abi.check(self.lib.pmk_set_event_granularity(self.handle, m), "pmk_set_event_granularity")
 
     def set_moe_scheduler(self, mode):
-        """'static' (each workgroup a fixed share of the grouped expert tasks) or 'dynamic' (tasks popped from
-        a per-layer queue, down tasks queued as their experts' gate/up tasks finish)."""
+        """'static' (each workgroup a fixed share of the grouped expert tasks), 'dynamic' (tasks popped from
+        a per-layer queue, down tasks queued as their experts' gate/up tasks finish) or 'xcd' (the same tasks
+        popped from a counter per XCD, with stealing)."""
         m = _abi.MOE_SCHEDULERS[mode] if isinstance(mode, str) else int(mode)
         _abi.check(self.lib.pmk_set_moe_scheduler(self.handle, m), "pmk_set_moe_scheduler")
 

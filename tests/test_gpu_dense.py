@@ -493,7 +493,7 @@ def test_schedule_setters_reject_unknown_modes(orc):
     model = make_model(case)
     assert model.lib.pmk_set_schedule(model.handle, 9) == _abi.PMK_ERR_ARG
     assert model.lib.pmk_set_schedule(model.handle, -1) == _abi.PMK_ERR_ARG
-    assert model.lib.pmk_set_moe_scheduler(model.handle, 2) == _abi.PMK_ERR_ARG
+    assert model.lib.pmk_set_moe_scheduler(model.handle, 3) == _abi.PMK_ERR_ARG
     model.close()
     check_dense(orc, case)
 
