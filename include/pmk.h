@@ -395,6 +395,28 @@ int pmk_trace_attach(pmk_handle* h, uint32_t* buf, int32_t entries_per_wg);
 int pmk_stream_probe(const void* buf, int64_t bytes, int32_t pattern, int32_t reps, int* sink, void* stream,
                      double* ms_out);
 
+/* Cross-XCD message-passing litmus of the persistent kernel's synchronisation
+ * scheme (the pages leave the deadlock and race debugging of event-driven
+ * kernels open; Event Tensor summary, Critical analysis), made from the same
+ * device primitives: a writer's device-coherent stores, a drain of its stores
+ * and a relaxed agent-scope atomic decrement; readers on the eight XCDs that
+ * spin on the counter (watchdog-bounded) and then read a block written once
+ * through the caches, as the kernels stage activations, and a block rewritten
+ * every round device-coherently, as they read split-K records. `rounds`
+ * rounds, one writer each (workgroup round mod grid), eight readers each.
+ *   work    device buffer, 256-byte aligned, of at least
+ *           rounds * 4224 + 4352 bytes (blocks, counters, error word);
+ *   result  device int32[8]: [0] the first round a reader saw a stale value
+ *           (-1: none; the run stops there), [1] its element, [2] the value
+ *           read, [3] the value written, [4] 0: the written-once block read
+ *           through the caches, 1: the rewritten block read coherently;
+ *           [5] 1 if a wait timed out (2 s); [6] rounds x readers checked;
+ *           [7] stale values of the rewritten block read through the caches
+ *           (counted, not a failure: the access the kernels avoid).
+ * Asynchronous on `stream` (a cooperative launch of one workgroup per compute
+ * unit). Errors: PMK_ERR_ARG, PMK_ERR_DEVICE. */
+int pmk_event_litmus(void* work, int64_t bytes, int32_t rounds, int32_t* result, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

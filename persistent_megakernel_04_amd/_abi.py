@@ -31,7 +31,8 @@ MOE_SCHEDULERS = {"static": MOE_STATIC, "dynamic": MOE_DYNAMIC, "xcd": MOE_DYNAM
 EXPORTS = ("decode_layer_init", "decode_step", "moe_layer_step", "decode_layer_destroy", "pmk_strerror",
            "pmk_get_device_error", "pmk_query", "pmk_timing_enable", "pmk_timing_read", "pmk_trace_attach",
            "pmk_set_schedule", "pmk_set_moe_scheduler", "pmk_set_watchdog_us", "pmk_pack_weights",
-           "pmk_stream_probe", "pmk_set_event_granularity", "decode_step_static")
+           "pmk_stream_probe", "pmk_set_event_granularity", "decode_step_static",
+           "pmk_event_litmus")
 
 i32, f32, vp = ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -114,6 +115,8 @@ def load():
     L.pmk_set_event_granularity.restype = i32
     L.decode_step_static.argtypes = [P(ModelDesc), P(Weights), vp, vp, vp, i32, vp, vp]
     L.decode_step_static.restype = i32
+    L.pmk_event_litmus.argtypes = [vp, ctypes.c_int64, i32, vp, vp]
+    L.pmk_event_litmus.restype = i32
     _lib = L
     return L
 
