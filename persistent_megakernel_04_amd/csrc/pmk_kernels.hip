@@ -109,11 +109,14 @@ __device__ __forceinline__ float* hid_out(const StepArgs& a, int l) {
 // multiply-high: with m = floor(2^32 / d) + 1 = (2^32 + e) / d, 0 < e <= d,
 // x m / 2^32 = x / d + x e / (d 2^32), and the second term is below 1 / d,
 // too small to carry x / d past the next integer.
+// (d = 1: m wraps to 0 and `keep` adds x back, without a branch)
 struct UDiv {
-  uint32_t m;
-  int one;
-  __device__ __forceinline__ explicit UDiv(int d) : m(0xffffffffu / (uint32_t)d + 1u), one(d == 1) {}
-  __device__ __forceinline__ int div(int x) const { return one ? x : (int)__umulhi((uint32_t)x, m); }
+  uint32_t m, keep;
+  __device__ __forceinline__ explicit UDiv(int d)
+      : m(0xffffffffu / (uint32_t)d + 1u), keep(d == 1 ? 0xffffffffu : 0u) {}
+  __device__ __forceinline__ int div(int x) const {
+    return (int)(__umulhi((uint32_t)x, m) + ((uint32_t)x & keep));
+  }
 };
 
 __device__ __forceinline__ size_t kv_off(const Dims& dm, int l, int which, int b, int g, int pos) {
@@ -910,18 +913,23 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
   }
   switch (ps.epi) {
     case E_QKV: {   // RoPE at each request's position, then q/k/v out and the K/V append
-      // element (request m, tile unit ju) at index ju << sh | m (2^sh >= nb):
-      // shifts instead of a division by nb, and the unit's (head, pair) from
-      // multiply-high dividers set up once (a runtime integer division is
-      // some forty vector instructions, and this loop ran 24 of them per lane)
-      const int half = dm.d >> 1, qkv_dim = (dm.Hq + 2 * dm.Hkv) * dm.d, G = dm.Hq / dm.Hkv;
+      // The model's dimensions are held in registers for the whole epilogue
+      // (read through `a`, they are reloaded after every store, which might
+      // alias the argument block), and the index math is branch-free: element
+      // (request m, tile unit ju) at index ju << sh | m (2^sh >= nb), the
+      // unit's (head, pair) from multiply-high dividers set up once.
+      const int Hq = dm.Hq, Hkv = dm.Hkv, d = dm.d, half = d >> 1, G = Hq / Hkv, per = (G + 2) * half;
+      const int qkv_dim = (Hq + 2 * Hkv) * d, max_seq = dm.max_seq, mb = dm.max_batch, r0 = ps.r0;
       const int sh = nb <= 1 ? 0 : 32 - __builtin_clz(nb - 1), ni = ps.n << sh;
-      const UDiv per_div((G + 2) * half), half_div(half);
+      float* const qkv = qkv_of(a, c.l);
+      WT* const kvb = reinterpret_cast<WT*>(a.kv);
+      const UDiv per_div(per), half_div(half);
       auto unit_hi = [&](int ju, int& h, int& i) {
-        const int up = ps.r0 + ju, g = per_div.div(up), r = up - g * (G + 2) * half;
+        const int up = r0 + ju, g = per_div.div(up), r = up - g * per;
         const int hg = half_div.div(r);   // head within the group's run: G query heads, its key, its value
         i = r - hg * half;
-        h = hg < G ? g * G + hg : dm.Hq + (hg - G) * dm.Hkv + g;
+        const int hq = g * G + hg, hkv = Hq + (hg - G) * Hkv + g;
+        h = hg < G ? hq : hkv;
       };
       if constexpr ((KP & 3) == KP_ALL) {
         if (a.per_op) {   // the projection alone: RoPE and the append are ops of their own
@@ -930,7 +938,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
             if (m >= nb) continue;
             int h, i;
             unit_hi(ju, h, i);
-            float* dst = qkv_of(a, c.l) + (size_t)(b0 + m) * qkv_dim + h * dm.d + i;
+            float* dst = qkv + (size_t)(b0 + m) * qkv_dim + h * d + i;
             stc(dst, ys[(2 * ju) * nb + m]);
             stc(dst + half, ys[(2 * ju + 1) * nb + m]);
           }
@@ -945,7 +953,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
       // later layers read them there instead of from memory.
       // (a wave-uniform flag, so that a hit branches around the loads
       // instead of issuing them and selecting)
-      const bool hit = __builtin_amdgcn_readfirstlane(c.s.rope_key[0] == ps.r0 + 1 && c.s.rope_key[1] == b0 &&
+      const bool hit = __builtin_amdgcn_readfirstlane(c.s.rope_key[0] == r0 + 1 && c.s.rope_key[1] == b0 &&
                                                       c.s.rope_key[2] == ni * 32 + nb) != 0;
       const bool keep = !hit && ni <= kRopeBytes / 8;
       int posl;
@@ -954,7 +962,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
       else
         posl = *gp(a.seq_lens + b0 + (lane < nb ? lane : 0));
       if (keep && t0 < 64 && lane < nb) c.s.rope_pos[lane] = posl;   // the first wave of the pass: one per request
-      const auto rrs = rsrc_n(a.ws.rope, dm.max_seq * half * 8);
+      const auto rrs = rsrc_n(a.ws.rope, max_seq * half * 8);
       for (int base = 0; base < ni; base += nt * 8) {
         float2 cs[8];
         int hs[8], is[8];
@@ -968,7 +976,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
           for (int u = 0; u < 8; ++u) {
             const int idx = base + t0 + nt * u, m = idx & ((1 << sh) - 1);
             const int pos = __shfl(posl, m, 64);
-            cs[u] = ldk2(rrs, idx < ni && m < nb && hs[u] < dm.Hq + dm.Hkv ? (pos * half + is[u]) * 8 : kNoRecord);
+            cs[u] = ldk2(rrs, idx < ni && m < nb && hs[u] < Hq + Hkv ? (pos * half + is[u]) * 8 : kNoRecord);
           }
         }
         if (keep) {
@@ -987,17 +995,17 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
           const float r = c.s.rstd[m];
           float y1 = ys[(2 * ju) * nb + m] * r, y2 = ys[(2 * ju + 1) * nb + m] * r;
           const int bb = b0 + m, pos = __shfl(posl, m, 64);
-          if (h < dm.Hq + dm.Hkv) {
+          if (h < Hq + Hkv) {
             const float t1 = y1 * cs[u].x - y2 * cs[u].y, t2 = y2 * cs[u].x + y1 * cs[u].y;
             y1 = t1;
             y2 = t2;
           }
-          float* dst = qkv_of(a, c.l) + (size_t)bb * qkv_dim + h * dm.d + i;
+          float* dst = qkv + (size_t)bb * qkv_dim + h * d + i;
           stc(dst, y1);
           stc(dst + half, y2);
-          if (h >= dm.Hq) {
-            const int kvh = h - dm.Hq, which = kvh >= dm.Hkv ? 1 : 0, g = kvh - which * dm.Hkv;
-            WT* cp = reinterpret_cast<WT*>(a.kv) + kv_off(dm, c.l, which, bb, g, pos);
+          if (h >= Hq) {   // the append: kv_off of (layer, K or V, request, KV head, pos)
+            const int kvh = h - Hq, which = kvh >= Hkv ? 1 : 0, g = kvh - which * Hkv;
+            WT* cp = kvb + ((((size_t)(c.l * 2 + which) * mb + bb) * Hkv + g) * (size_t)max_seq + pos) * d;
             Elem<WT>::put(cp + i, y1);
             Elem<WT>::put(cp + i + half, y2);
           }
@@ -1006,7 +1014,7 @@ __device__ __forceinline__ void epilogue(const Ctx& c, const Pass& ps, bool have
       // the kept rows are read by this workgroup's next QKV pass, a later
       // task: every task starts with a workgroup barrier
       if (keep && t0 == 0) {
-        c.s.rope_key[0] = ps.r0 + 1;
+        c.s.rope_key[0] = r0 + 1;
         c.s.rope_key[1] = b0;
         c.s.rope_key[2] = ni * 32 + nb;
       }
