@@ -215,7 +215,7 @@ def run_timed(model, hid_in, kv, steps_lens, K, W, flush=None):
     return total_ms, step_ms, main_ms / timed_steps, host_us
 
 
-def batch_sweep(w, layers, batches, K, W, dev, events="tile") -> list:
+def batch_sweep(w, layers, batches, K, W, dev, events="group") -> list:
     """The 8B-shaped stack at each batch with ragged lengths uniform on
     [512, 8192] (seeded per batch), one handle and one cache for all batches
     (requests 0..B-1 of a max_batch cache; every request's slots are filled
@@ -298,9 +298,9 @@ def main():
                     "non-temporally; auto: tiles for bfloat16 workloads")
     ap.add_argument("--trace", default=None, help="after the timed steps, run one traced step and write a "
                     "per-stage summary of the task trace to this file")
-    ap.add_argument("--events", default="tile", choices=["tile", "group", "stage"],
-                    help="granularity of the dense chain's events: per KV group and batch block (tile, the default), "
-                    "per KV group (group), or one per stage (stage: an ablation of the subset waits)")
+    ap.add_argument("--events", default="group", choices=["tile", "group", "stage"],
+                    help="granularity of the dense chain's events: per KV group (group, the default), per KV group "
+                    "and 16-row batch block beyond 16 rows (tile), or one event per stage (stage)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch sweep (4, 16, 64, 128) that the default "
                     "workload adds to its line")
     ap.add_argument("--sweep-steps", type=int, default=20, help="timed steps per sweep batch")

@@ -316,14 +316,17 @@ int pmk_set_watchdog_us(pmk_handle* h, int32_t us);
  * Event Tensor abstraction; Problem and motivation: a kernel boundary makes
  * every consumer wait for the whole producer stage although it often needs
  * only part of it):
- *   PMK_EVENTS_TILE   per tile (the default): the QKV tiles of each KV group
- *                     and batch block, the attention of each KV group and
- *                     block, and the O, gate/up and down tiles of each
- *                     16-row block (batches beyond 16 rows) each have an
- *                     event; attention (b, g) waits on group g's QKV tiles
- *                     only, an O task on the attention of the groups its K
- *                     slice reads, a block's stages on that block's events;
- *   PMK_EVENTS_GROUP  per KV group, one batch block;
+ *   PMK_EVENTS_TILE   per tile: the QKV tiles of each KV group and batch
+ *                     block, the attention of each KV group and block, and
+ *                     the O, gate/up and down tiles of each 16-row block
+ *                     (batches beyond 16 rows) each have an event; attention
+ *                     (b, g) waits on group g's QKV tiles only, an O task on
+ *                     the attention of the groups its K slice reads, a
+ *                     block's stages on that block's events;
+ *   PMK_EVENTS_GROUP  (the default) the same up to 16 rows; beyond, one batch
+ *                     block (per-block events measured 1.6 % slower at 64
+ *                     rows: the queues are static, so a block's tasks cannot
+ *                     overtake another's anyway);
  *   PMK_EVENTS_STAGE  one event per stage: every attention task waits on all
  *                     QKV tiles, every O task on all attention.
  * Same results in every mode (an ablation of the subset waits). Applies to

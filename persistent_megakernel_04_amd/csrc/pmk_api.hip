@@ -35,7 +35,7 @@ struct pmk_handle {
   int* err_host = nullptr;   // pinned host-coherent mirror of the device error word
   size_t tused = 0;
   int sched = PMK_SCHED_FUSED;
-  int ev_mode = PMK_EVENTS_TILE;
+  int ev_mode = PMK_EVENTS_GROUP;
   int moe_sched = PMK_MOE_STATIC;
 };
 
@@ -468,7 +468,7 @@ int decode_step_static(const pmk_model_desc* desc, const pmk_weights* w, float* 
   a.batch = batch;
   a.qkv_tiles = dm.qkv_tiles;
   a.watchdog_ticks = (unsigned long long)(desc->watchdog_ms > 0 ? desc->watchdog_ms : 2000) * 100000ull;
-  a.ev_mode = PMK_EVENTS_TILE;
+  a.ev_mode = PMK_EVENTS_GROUP;
   if (launch_prologue(a, s) != hipSuccess) return PMK_ERR_DEVICE;
   if (launch_main(a, desc->dtype, s, RunSpec{0, dm.L, kAllTypes, 0}) != hipSuccess) return PMK_ERR_DEVICE;
   return PMK_OK;

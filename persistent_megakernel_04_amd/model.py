@@ -153,7 +153,7 @@ class DecodeModel:
         _abi.check(self.lib.pmk_set_schedule(self.handle, m), "pmk_set_schedule")
 
     def set_event_granularity(self, mode):
-        """'tile' (the default: per KV group and batch block), 'group' (per KV group) or 'stage' (one event
+        """'group' (the default: per KV group), 'tile' (per KV group and, beyond 16 rows, batch block) or 'stage' (one event
         per stage): how finely the dense chain's consumers wait on their producers."""
         m = _abi.EVENT_MODES[mode] if isinstance(mode, str) else int(mode)
         _abi.check(self.lib.pmk_set_event_granularity(self.handle, m), "pmk_set_event_granularity")
