@@ -373,12 +373,18 @@ __device__ __forceinline__ WaveItems wave_items(int RG, int NKS, int nb, int wav
   WaveItems it;
   const int ks = k_split(RG, nb);
   // slices of whole ring lengths, so that no wave pads its range with
-  // dummy steps (the last slice ends at NKS)
+  // dummy steps (the last slice ends at NKS). Where they cannot be equal, the
+  // first slices take one ring length more: they go to waves 0-3, the first
+  // wave on each SIMD, which win the issue arbitration over the second ones
+  // (traced: the last wave of a task to finish its share is always one of
+  // waves 4-7, and with the extra lengths on odd waves the down projection's
+  // tasks ended ~4 us after their first wave at batch 1).
   const int NB = (NKS + kRing - 1) / kRing;
   auto slice = [&](int sl) {
     it.sl = sl;
-    it.ks_lo = min(sl * NB / ks * kRing, NKS);
-    it.nks = min((sl + 1) * NB / ks * kRing, NKS) - it.ks_lo;
+    const int q = NB / ks, r = NB - q * ks, b0 = sl * q + min(sl, r), b1 = b0 + q + (sl < r ? 1 : 0);
+    it.ks_lo = min(b0 * kRing, NKS);
+    it.nks = min(b1 * kRing, NKS) - it.ks_lo;
   };
   if (ks == 1) {
     it.n = wave < RG ? (RG - wave + kWaves - 1) / kWaves : 0;
