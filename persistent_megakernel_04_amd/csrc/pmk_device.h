@@ -120,6 +120,9 @@ __device__ __forceinline__ float2 ldc2(__amdgpu_buffer_rsrc_t r, int off) {
   const u2v v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16);
   return make_float2(__uint_as_float(v.x), __uint_as_float(v.y));
 }
+__device__ __forceinline__ float ldc1(__amdgpu_buffer_rsrc_t r, int off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 16));
+}
 __device__ __forceinline__ void stc4(__amdgpu_buffer_rsrc_t r, int off, f4v v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4v, v), r, off, 0, 16);
 }
