@@ -196,10 +196,39 @@ __device__ __forceinline__ void wave_notify(int* ev, int sub) {
 }
 
 // Wave 0 only: spin until the event's counters are all zero (`subs` = number
-// of sub-counters to read besides [0]; 0 for a bare counter). Returns false on
-// abort or watchdog expiry (then the error word holds PMK_ERR_TIMEOUT and the
-// abort flag is set, so every other waiting workgroup also leaves its loop).
+// of sub-counters to read besides [0]; 0 for a bare counter; a run of flat
+// counters may hold up to kMaxHkv). Returns false on abort or watchdog expiry
+// (then the error word holds PMK_ERR_TIMEOUT and the abort flag is set, so
+// every other waiting workgroup also leaves its loop).
+__device__ __forceinline__ bool spin_fail(int* err) {
+  if ((threadIdx.x & 63) == 0) {
+    int expected = 0;
+    __hip_atomic_compare_exchange_strong(gp(err), &expected, (int)PMK_ERR_TIMEOUT, __ATOMIC_RELAXED,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stci(err + 16, 1);
+  }
+  return false;
+}
+// More than 64 counters (a wait on the flat counters of more than 64 KV
+// groups): two reads per lane.
+__device__ __forceinline__ bool spin_zero_wide(const int* ev, int subs, int* err, unsigned long long ticks) {
+  const int lane = threadIdx.x & 63;
+  const int* m0 = ev + (lane <= subs ? lane : 0) * kCtr;
+  const int* m1 = ev + (lane + 64 <= subs ? lane + 64 : 0) * kCtr;
+  const unsigned long long t0 = now_ticks();
+  for (int it = 0;; ++it) {
+    const int x0 = ldci(m0), x1 = ldci(m1);
+    if (__all(x0 == 0 && x1 == 0)) return true;
+    __builtin_amdgcn_s_sleep(1);
+    if ((it & 15) == 15) {
+      if (ldci(err + 16) != 0) return false;
+      if (now_ticks() - t0 > ticks) return spin_fail(err);
+    }
+  }
+}
+// Up to 64 counters: one read per lane.
 __device__ __forceinline__ bool spin_zero(const int* ev, int subs, int* err, unsigned long long ticks) {
+  if (subs >= 64) return spin_zero_wide(ev, subs, err, ticks);
   const int lane = threadIdx.x & 63;
   const int* mine = ev + (lane <= subs ? lane : 0) * kCtr;
   if (__all(ldci(mine) == 0)) return true;
@@ -209,15 +238,7 @@ __device__ __forceinline__ bool spin_zero(const int* ev, int subs, int* err, uns
     if (__all(ldci(mine) == 0)) return true;
     if ((it & 15) == 15) {
       if (ldci(err + 16) != 0) return false;
-      if (now_ticks() - t0 > ticks) {
-        if (lane == 0) {
-          int expected = 0;
-          __hip_atomic_compare_exchange_strong(gp(err), &expected, (int)PMK_ERR_TIMEOUT, __ATOMIC_RELAXED,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          stci(err + 16, 1);
-        }
-        return false;
-      }
+      if (now_ticks() - t0 > ticks) return spin_fail(err);
     }
   }
 }

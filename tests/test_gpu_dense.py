@@ -108,6 +108,26 @@ def test_c1_shapes_two_layers_random_gains(orc):
     check_dense(orc, case)
 
 
+@pytest.mark.parametrize("events", ["group", "stage"])
+def test_more_than_64_kv_heads(orc, events):
+    """72 KV heads (fp32, one query head each): an O-projection tile reads the
+    attention of all 72 groups, so its wait spans 72 flat counters (per stage:
+    attention waits on the QKV counters of all 72 groups too), more than the 64
+    lanes of the waiting wave read at once."""
+    import dataclasses
+    w = dataclasses.replace(synth.get_workload("c1_tiny_f32"), name="c1_wide_kv", n_q_heads=72, n_kv_heads=72)
+    case = build_case(w, 2, [40, 130], max_seq=160, tag="t21")
+    inp = oracle_inputs(case)
+    model = make_model(case)
+    model.set_event_granularity(events)
+    announce(f"decode_step {w.name} Hkv=72 B=2 events={events}")
+    model.step(case.hidden, case.kv, case.seq_lens)
+    torch.cuda.synchronize()
+    assert model.device_error() == 0
+    model.close()
+    check_against_oracle(orc, case, inp, to_np(case.hidden).astype(np.float64), to_np(case.kv))
+
+
 def test_8b_shape_two_layers_b1(orc):
     w = synth.get_workload("c2_8b_b1")
     case = build_case(w, 1, [512], n_layers=2, max_seq=640, tag="t4")
