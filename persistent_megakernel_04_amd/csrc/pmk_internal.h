@@ -72,6 +72,46 @@ __host__ __device__ inline StageGeo stage_geo(int K, int units, int urows, int n
   }
 }
 
+// The split of a dense stage for a batch of B rows on `avail` workgroups. Up
+// to 16 rows: stage_geo for those rows. Beyond, the batch runs in blocks of
+// 16 rows, each (row tile, K slice, block) a task of its own (blk > 1), with
+// row tiles sized for about `mult` tasks per workgroup over all the blocks
+// (tiles x slices ~ avail mult / blocks): the smallest mult of 1, 2, 4, ...
+// whose tile outputs and 16-row input slices fit the LDS. Each tile's weights
+// are still read once per block (by workgroups of one XCD, through its L2),
+// but each block's inputs are staged by that many times fewer tiles, and a
+// workgroup runs that many times fewer tasks, each with its own wait,
+// staging, stores and notify. Where no K split fits: passes of rows over the
+// whole depth (slice 1, one block).
+// Whether a pass of split g (nb staged rows of its K slice, then its tile's
+// outputs for them) fits the LDS region that holds it.
+__host__ __device__ inline bool stage_fits(const StageGeo& g, int units, int urows, int nb, int kstep, int xpad) {
+  const long xs = (long)nb * ((g.kr + kstep - 1) / kstep * kstep + xpad) * 4;
+  const long rows = (long)(units + g.tiles - 1) / g.tiles * urows;
+  return (xs + 15) / 16 * 16 + rows * nb * 4 <= kXyBytes;
+}
+__host__ __device__ inline StageGeo stage_split(int K, int units, int urows, int B, int avail, int kstep, int xpad) {
+  StageGeo g{0, 0, 0, 1};
+  if (B <= kMaxNb) {
+    g = stage_geo(K, units, urows, B, avail, kstep, xpad);
+  } else {
+    const int nbk = (B + kMaxNb - 1) / kMaxNb;
+    for (int mult = 1;; mult *= 2) {
+      if (mult >= nbk) {   // one tile set per block: the split of 16 rows on the whole share
+        g = stage_geo(K, units, urows, kMaxNb, avail, kstep, xpad);
+        break;
+      }
+      const long av = (long)avail * mult / nbk;
+      g = stage_geo(K, units, urows, kMaxNb, av > 1 ? (int)av : 1, kstep, xpad);
+      // (stage_geo stops at its shortest slice whether or not the tile fits)
+      if (g.ks && stage_fits(g, units, urows, kMaxNb, kstep, xpad)) break;
+    }
+    if (g.ks) g.blk = nbk;
+  }
+  if (g.ks == 0) g = StageGeo{1, avail < units ? avail : units, K, 1};
+  return g;
+}
+
 // Split-K record layout of a dense stage, as the persistent kernel addresses
 // it: task (row tile t, slice s, batch block k) stores its slice's partial sums
 // (the tile's rows x nb, then nb sums of squares) at record
@@ -83,22 +123,26 @@ __host__ __device__ inline int kpart_stride(int units, int urows, int tiles, int
 }
 
 // Floats of split-K records a stage of depth K needs at most, over every
-// batch (nb = min(batch, 16) rows per block, ceil(max_batch / 16) blocks at 16)
-// and every grid share the prologue may give the stage (the whole grid, or the
+// batch (stage_split: nb = min(batch, 16) rows per block, its blocks) and
+// every grid share the prologue may give the stage (the whole grid, or the
 // grid less the workgroups of up to a quarter of it that take attention tasks
 // of their own: avail in [grid - grid / 4, grid] for QKV and O).
 __host__ __device__ inline long kpart_need(int K, int units, int urows, int max_batch, int grid, bool attn_share,
                                            int kstep, int xpad) {
   long need = 0;
   const int lo = attn_share ? grid - grid / 4 : grid;
-  for (int nb = 2; nb <= (max_batch < kMaxNb ? max_batch : kMaxNb); ++nb)
+  // every batch up to 16, then one batch per count of 16-row blocks (the split
+  // depends on the block count alone)
+  for (int B = 1;; B = B < kMaxNb ? B + 1 : B + kMaxNb) {
+    const int Bc = B < max_batch ? B : max_batch;
     for (int avail = lo; avail <= grid; ++avail) {
-      const StageGeo g = stage_geo(K, units, urows, nb, avail, kstep, xpad);
+      const StageGeo g = stage_split(K, units, urows, Bc, avail, kstep, xpad);
       if (g.ks <= 1) continue;
-      const long blocks = nb == kMaxNb ? (max_batch + kMaxNb - 1) / kMaxNb : 1;
-      const long ext = blocks * g.tiles * g.ks * (long)kpart_stride(units, urows, g.tiles, nb);
+      const long ext = (long)g.blk * g.tiles * g.ks * kpart_stride(units, urows, g.tiles, Bc < kMaxNb ? Bc : kMaxNb);
       if (ext > need) need = ext;
     }
+    if (Bc >= max_batch) break;
+  }
   return need;
 }
 

@@ -191,9 +191,9 @@ __host__ __device__ inline Plan plan_step(const Dims& dm, int B, const int* sl, 
   // first in the layer, so its KV rows stream in while the QKV tiles run on
   // the other workgroups.
   p.own = (merge && p.total_attn <= G / 4 && !per_op) ? p.total_attn : 0;
-  // each dense stage's split (stage_geo): up to 16 rows, one pass over K
-  // slices that fit the LDS; beyond, the split of 16 rows for every block of
-  // 16 (or, where no split fits, passes of rows over the whole depth)
+  // each dense stage's split (stage_split): up to 16 rows, one pass over K
+  // slices that fit the LDS; beyond, blocks of 16 rows over larger row tiles
+  // (or, where no split fits, passes of rows over the whole depth)
   bool all_blocked = B > kMaxNb;
   for (int st = 0; st < 4; ++st) {
     if (dm.moe && st >= 2) {   // MoE layers have no dense gate/up or down stage
@@ -203,9 +203,7 @@ __host__ __device__ inline Plan plan_step(const Dims& dm, int B, const int* sl, 
     int K, U, R;
     stage_dims(dm, st, K, U, R);
     const int avail = st <= 1 ? G - p.own : G;
-    StageGeo g = stage_geo(K, U, R, B < kMaxNb ? B : kMaxNb, avail, dm.kstep, dm.xpad);
-    if (B > kMaxNb && g.ks) g.blk = (B + kMaxNb - 1) / kMaxNb;
-    if (g.ks == 0) g = StageGeo{1, avail < U ? avail : U, K, 1};
+    const StageGeo g = stage_split(K, U, R, B, avail, dm.kstep, dm.xpad);
     if (g.blk <= 1) all_blocked = false;
     p.geo[st] = g;
   }

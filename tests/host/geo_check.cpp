@@ -56,6 +56,50 @@ int main() {
                 if (rs % 4 != 0 || 4 * units4 > rs) return fail("record stride");
               }
             }
+  // Batches beyond 16 (stage_split): blocks of 16 rows over row tiles sized
+  // for fewer tasks than one set per block. Every split with more than one
+  // tile set per workgroup's share must fit the LDS outright; the whole-share
+  // split keeps stage_geo's rule; slices cover K; blocks match the batch.
+  {
+    struct BShape { int H, Hq, Hkv, d, F, kstep, xpad; };
+    const BShape bshapes[] = {{4096, 32, 8, 128, 14336, 32, 8}, {2048, 32, 4, 128, 0, 32, 8},
+                              {8192, 64, 8, 128, 28672, 32, 8}, {256, 4, 2, 64, 688, 16, 4},
+                              {4096, 4, 2, 64, 256, 16, 4}};
+    const int bavails[] = {192, 240, 256, 304, 80};
+    for (const BShape& sh : bshapes)
+      for (int st = 0; st < 4; ++st) {
+        if (st >= 2 && sh.F == 0) continue;
+        const int K4[4] = {sh.H, sh.Hq * sh.d, sh.H, sh.F};
+        const int U4[4] = {(sh.Hq + 2 * sh.Hkv) * sh.d / 2, sh.H, sh.F, sh.H};
+        const int R4[4] = {2, 1, 2, 1};
+        const int grain = kRingK * sh.kstep;
+        for (int B = 17; B <= 1024; B += (B < 64 ? 1 : 16))
+          for (int avail : bavails) {
+            ++cases;
+            const StageGeo g = stage_split(K4[st], U4[st], R4[st], B, avail, sh.kstep, sh.xpad);
+            const StageGeo whole = stage_geo(K4[st], U4[st], R4[st], kMaxNb, avail, sh.kstep, sh.xpad);
+            auto fail = [&](const char* why) {
+              std::printf("FAIL %s: H %d stage %d B %d avail %d -> ks %d tiles %d kr %d blk %d\n", why, sh.H, st, B,
+                          avail, g.ks, g.tiles, g.kr, g.blk);
+              return 1;
+            };
+            if (whole.ks == 0) {   // passes over the batch, as before
+              if (g.blk != 1 || g.ks != 1) return fail("no split fits, yet blocks");
+              continue;
+            }
+            if (g.blk != (B + kMaxNb - 1) / kMaxNb) return fail("block count");
+            if (g.ks < 1 || g.ks > kMaxKs) return fail("slice count");
+            if ((long)(g.ks - 1) * g.kr >= K4[st] || (long)g.ks * g.kr < K4[st]) return fail("slices do not cover K");
+            if (g.tiles < 1 || g.tiles > U4[st] || g.tiles > whole.tiles) return fail("tile count");
+            const bool is_whole = g.tiles == whole.tiles && g.ks == whole.ks && g.kr == whole.kr;
+            if (!is_whole && !stage_fits(g, U4[st], R4[st], kMaxNb, sh.kstep, sh.xpad)) return fail("does not fit the LDS");
+            if (is_whole && !stage_fits(g, U4[st], R4[st], kMaxNb, sh.kstep, sh.xpad) && g.kr > grain)
+              return fail("whole-share split does not fit the LDS");
+            // fewer tasks per workgroup than one set of tiles per block, where the blocks outnumber one
+            if ((long)g.tiles * g.ks * g.blk > (long)whole.tiles * whole.ks * g.blk) return fail("more tasks");
+          }
+      }
+  }
   // The decode workloads' own splits pull the other slices' records into LDS
   // in one round trip (the kernel falls back to register loads otherwise,
   // e.g. for the 70B-shaped gate/up tiles at 10 to 16 rows).
@@ -114,9 +158,9 @@ int main() {
           for (int own = 0; own <= (st <= 1 ? G / 4 : 0); ++own) {
             ++cases;
             const int nb = B < kMaxNb ? B : kMaxNb;
-            StageGeo g = stage_geo(K4[st], U4[st], R4[st], nb, G - own, sh.kstep, sh.xpad);
+            StageGeo g = stage_split(K4[st], U4[st], R4[st], B, G - own, sh.kstep, sh.xpad);
             if (g.ks <= 1) continue;   // no records (or passes over the batch)
-            const long blk = B > kMaxNb ? (B + kMaxNb - 1) / kMaxNb : 1;
+            const long blk = g.blk;
             const long rows = (long)(U4[st] + g.tiles - 1) / g.tiles * R4[st];
             const long rs = (rows * (blk > 1 ? kMaxNb : nb) + 16 + 3) & ~3L;
             const long used = rows * nb + nb;   // sums, then sums of squares
