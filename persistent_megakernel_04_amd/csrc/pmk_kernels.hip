@@ -2371,9 +2371,68 @@ __global__ void __launch_bounds__(1024) pmk_prologue(StepArgs a) {
     for (int w = tid; w < G; w += blockDim.x) a.ws.qlen[w] = 0;
     return;
   }
+  // The step's split: pmk_sched.h's plan_step. Up to 32 requests, on one
+  // thread. Beyond, its parts in parallel (one thread over every request took
+  // up to ~190 us at 1024 requests): the lengths' aggregates by wave
+  // reductions, the attention plan on one thread, cb as a prefix sum over the
+  // workgroup (a request per thread), and each dense stage's split on a
+  // thread of its own (at one request the reductions and barriers cost more
+  // than they save).
+  __shared__ unsigned long long agg_sum[kChunkSizes + 1];   // tasks per chunk size, then positions
+  __shared__ int agg_max[kChunkSizes];
+  __shared__ int wave_tot[32];
+  if (B <= 32) {
+    if (tid == 0) {
+      a.ws.err[16] = 0;   // abort flag
+      plan = plan_step(dm, B, sl, cb, a.per_op, a.ev_mode);
+    }
+  } else {
+    if (tid < kChunkSizes + 1) agg_sum[tid] = 0;
+    if (tid < kChunkSizes) agg_max[tid] = 0;
+    __syncthreads();
+    {
+      PlanAgg g{};
+      for (int b = tid; b < B; b += blockDim.x) plan_agg_add(g, sl[b]);
+      for (int i = 0; i <= kChunkSizes; ++i) {
+        long long t = i < kChunkSizes ? g.tasks[i] : g.positions;
+        int m = i < kChunkSizes ? g.max_nc[i] : 0;
+        for (int o = 32; o > 0; o >>= 1) {
+          t += __shfl_xor(t, o, 64);
+          m = max(m, __shfl_xor(m, o, 64));
+        }
+        if ((tid & 63) == 0) {
+          atomicAdd(&agg_sum[i], (unsigned long long)t);
+          if (i < kChunkSizes) atomicMax(&agg_max[i], m);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      a.ws.err[16] = 0;   // abort flag
+      PlanAgg g{};
+      for (int i = 0; i < kChunkSizes; ++i) {
+        g.tasks[i] = (long)agg_sum[i];
+        g.max_nc[i] = agg_max[i];
+      }
+      g.positions = (long)agg_sum[kChunkSizes];
+      plan = plan_attention(dm, B, g, a.per_op, a.ev_mode);
+    }
+    __syncthreads();
+    {
+      static_assert(kMaxBatchAll <= 1024, "one request per prologue thread");
+      const int v = tid < B ? plan_cb_term(plan, sl[tid]) : 0, inc = wave_scan(v), wv = tid >> 6;
+      if ((tid & 63) == 63) wave_tot[wv] = inc;
+      __syncthreads();
+      int off = 0;
+      for (int i = 0; i < wv; ++i) off += wave_tot[i];
+      if (tid < B) cb[tid] = off + inc - v;
+      if (tid == B - 1) cb[B] = off + inc;
+    }
+    if (tid < 4) plan.geo[tid] = plan_geo(dm, plan, tid);
+    __syncthreads();
+    if (tid == 0) plan.nblk = plan_nblk(dm, plan);
+  }
   if (tid == 0) {
-    a.ws.err[16] = 0;   // abort flag
-    plan = plan_step(dm, B, sl, cb, a.per_op, a.ev_mode);
     copy->attn_merge_o = plan.merge;
     copy->attn_chunk = plan.ck;
     for (int st = 0; st < 4; ++st) copy->geo[st] = plan.geo[st];

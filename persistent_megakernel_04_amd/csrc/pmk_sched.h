@@ -130,12 +130,28 @@ enum EvMode : int { EVM_TILE = 0, EVM_GROUP = 1, EVM_STAGE = 2 };
 __host__ __device__ inline int ceil_div_i(long a, long b) { return (int)((a + b - 1) / b); }
 
 
-// The step's split from (B, sl): attention chunking, streaming and dedicated
-// attention workgroups, each dense stage's geometry, the event blocks. cb[0..B]
-// receives the prefix sum of the requests' positions (S + 1, streamed) or
-// chunks. Serial over the batch (the device prologue runs it on one thread).
-__host__ __device__ inline Plan plan_step(const Dims& dm, int B, const int* sl, int* cb, int per_op,
-                                          int ev_mode = EVM_TILE) {
+// What the step's split needs of the requests' lengths: for each chunk size
+// kMinChunk << i (i < kChunkSizes), the chunks of all requests together and
+// the most chunks of one request ((S + c) / c for a request with S cached
+// positions: its new entry included), and the positions of all requests.
+constexpr int kChunkSizes = 3;   // 64, 128, 256 = kMaxChunk
+struct PlanAgg {
+  long tasks[kChunkSizes];
+  int max_nc[kChunkSizes];
+  long positions;                // sum of S
+};
+__host__ __device__ inline void plan_agg_add(PlanAgg& g, int S) {
+  for (int i = 0; i < kChunkSizes; ++i) {
+    const int nc = (S >> (6 + i)) + 1;   // (S + c) / c, c = kMinChunk << i = 2^(6 + i)
+    g.tasks[i] += nc;
+    g.max_nc[i] = g.max_nc[i] > nc ? g.max_nc[i] : nc;
+  }
+  g.positions += S;
+}
+// The step's split from the lengths' aggregates: attention chunking,
+// streaming and dedicated attention workgroups (every field but geo and nblk).
+__host__ __device__ inline Plan plan_attention(const Dims& dm, int B, const PlanAgg& g, int per_op, int ev_mode) {
+  static_assert(kMinChunk == 64 && kMaxChunk == kMinChunk << (kChunkSizes - 1), "chunk sizes");
   Plan p{};
   p.B = B;
   p.per_op = per_op;
@@ -146,26 +162,15 @@ __host__ __device__ inline Plan plan_step(const Dims& dm, int B, const int* sl, 
   // O-projection merge the partials; otherwise the largest of 256/128/64
   // positions that still gives every workgroup a task, with the last chunk
   // of a request merging.
-  int ck = kMaxChunk, merge = 0;
-  auto max_nc = [&](int c) {
-    int mx = 0;
-    for (int b = 0; b < B; ++b) mx = mx > (sl[b] + c) / c ? mx : (sl[b] + c) / c;
-    return mx;
-  };
+  int ci = kChunkSizes - 1, merge = 0;
   if (B <= dm.merge_b && !per_op) {
-    int c = kMinChunk;
-    while (c < kMaxChunk && max_nc(c) > kMergeChunks) c <<= 1;
-    if (max_nc(c) <= kMergeChunks) { ck = c; merge = 1; }
+    int c = 0;
+    while (c < kChunkSizes - 1 && g.max_nc[c] > kMergeChunks) ++c;
+    if (g.max_nc[c] <= kMergeChunks) { ci = c; merge = 1; }
   }
-  if (!merge) {
-    while (ck > kMinChunk) {
-      long tasks = 0;
-      for (int b = 0; b < B; ++b) tasks += (sl[b] + ck) / ck;
-      if (tasks * dm.Hkv >= G) break;
-      ck >>= 1;
-    }
-  }
-  p.ck = ck;
+  if (!merge)
+    while (ci > 0 && g.tasks[ci] * dm.Hkv < G) --ci;
+  p.ck = kMinChunk << ci;
   p.merge = merge;
   // Without the O-projection merge, the matrix-core attention streams its
   // positions: all (request, KV head) position ranges, laid end to end, are
@@ -173,17 +178,13 @@ __host__ __device__ inline Plan plan_step(const Dims& dm, int B, const int* sl, 
   // piece of a range within a share is a task. The per-op schedule keeps chunk
   // partials, merged by an op of their own.
   p.stream = !merge && dm.attn_mm && !per_op;
-  int acc = 0;
-  for (int b = 0; b < B; ++b) {
-    cb[b] = acc;
-    acc += p.stream ? sl[b] + 1 : (sl[b] + ck) / ck;   // positions, or ceil((S + 1) / ck) chunks
-  }
-  cb[B] = acc;
-  p.total_attn = acc * dm.Hkv;
+  // cb[B]: positions (S + 1 each, streamed) or chunks
+  const long acc = p.stream ? g.positions + B : g.tasks[ci];
+  p.total_attn = (int)(acc * dm.Hkv);
   // streamed shares: every (request, KV head) range is laid out behind a lead
   // of kPieceCost positions (what a piece costs beyond its positions), so that
   // a share that starts a range holds fewer positions
-  const long P = p.stream ? (long)dm.Hkv * (acc + (long)B * kPieceCost) : (long)acc * dm.Hkv;
+  const long P = p.stream ? (long)dm.Hkv * (acc + (long)B * kPieceCost) : acc * dm.Hkv;
   const long sh = (P + G - 1) / G;
   p.share = ((sh + 15) / 16 * 16) < 64 ? 64 : (sh + 15) / 16 * 16;
   // A few attention tasks (at most a quarter of the grid) get workgroups of
@@ -191,25 +192,47 @@ __host__ __device__ inline Plan plan_step(const Dims& dm, int B, const int* sl, 
   // first in the layer, so its KV rows stream in while the QKV tiles run on
   // the other workgroups.
   p.own = (merge && p.total_attn <= G / 4 && !per_op) ? p.total_attn : 0;
-  // each dense stage's split (stage_split): up to 16 rows, one pass over K
-  // slices that fit the LDS; beyond, blocks of 16 rows over larger row tiles
-  // (or, where no split fits, passes of rows over the whole depth)
-  bool all_blocked = B > kMaxNb;
-  for (int st = 0; st < 4; ++st) {
-    if (dm.moe && st >= 2) {   // MoE layers have no dense gate/up or down stage
-      p.geo[st] = StageGeo{1, 1, 1, 1};
-      continue;
-    }
-    int K, U, R;
-    stage_dims(dm, st, K, U, R);
-    const int avail = st <= 1 ? G - p.own : G;
-    const StageGeo g = stage_split(K, U, R, B, avail, dm.kstep, dm.xpad);
-    if (g.blk <= 1) all_blocked = false;
-    p.geo[st] = g;
+  return p;
+}
+// One request's entry of cb (the prefix sum of positions S + 1, streamed, or
+// of chunks ceil((S + 1) / ck)).
+__host__ __device__ inline int plan_cb_term(const Plan& p, int S) { return p.stream ? S + 1 : (S + p.ck) / p.ck; }
+// Dense stage st's split (stage_split): up to 16 rows, one pass over K
+// slices that fit the LDS; beyond, blocks of 16 rows over larger row tiles
+// (or, where no split fits, passes of rows over the whole depth).
+__host__ __device__ inline StageGeo plan_geo(const Dims& dm, const Plan& p, int st) {
+  if (dm.moe && st >= 2) return StageGeo{1, 1, 1, 1};   // MoE layers have no dense gate/up or down stage
+  int K, U, R;
+  stage_dims(dm, st, K, U, R);
+  const int avail = st <= 1 ? dm.grid - p.own : dm.grid;
+  return stage_split(K, U, R, p.B, avail, dm.kstep, dm.xpad);
+}
+// Events per block when every dense stage splits by block (MoE layers keep
+// one block: their routed stages cover all tokens at once).
+__host__ __device__ inline int plan_nblk(const Dims& dm, const Plan& p) {
+  bool all_blocked = p.B > kMaxNb;
+  for (int st = 0; st < 4; ++st)
+    if (!(dm.moe && st >= 2) && p.geo[st].blk <= 1) all_blocked = false;
+  return (all_blocked && !dm.moe && p.ev_mode == EVM_TILE) ? (p.B + kMaxNb - 1) / kMaxNb : 1;
+}
+
+// The step's split from (B, sl), serially: the composition of the parts above
+// (the device prologue computes the same parts in parallel). cb[0..B]
+// receives the prefix sum of the requests' positions (S + 1, streamed) or
+// chunks.
+__host__ __device__ inline Plan plan_step(const Dims& dm, int B, const int* sl, int* cb, int per_op,
+                                          int ev_mode = EVM_TILE) {
+  PlanAgg g{};
+  for (int b = 0; b < B; ++b) plan_agg_add(g, sl[b]);
+  Plan p = plan_attention(dm, B, g, per_op, ev_mode);
+  int acc = 0;
+  for (int b = 0; b < B; ++b) {
+    cb[b] = acc;
+    acc += plan_cb_term(p, sl[b]);
   }
-  // events per block when every dense stage splits by block (MoE layers keep
-  // one block: their routed stages cover all tokens at once)
-  p.nblk = (all_blocked && !dm.moe && ev_mode == EVM_TILE) ? (B + kMaxNb - 1) / kMaxNb : 1;
+  cb[B] = acc;
+  for (int st = 0; st < 4; ++st) p.geo[st] = plan_geo(dm, p, st);
+  p.nblk = plan_nblk(dm, p);
   return p;
 }
 
