@@ -491,10 +491,53 @@ std::string check(const Shape& sh, int grid, int B, int max_seq, int lo, int hi,
 
 }  // namespace
 
+// The plan's length aggregates (PlanAgg: the shift for a request's chunks)
+// against their definitions: chunks of S cached positions plus the new entry
+// at chunk size c are (S + c) / c, summed over the batch and maximised.
+static bool check_aggregates() {
+  for (int S = 0; S <= (1 << 20); ++S) {
+    PlanAgg g{};
+    plan_agg_add(g, S);
+    for (int i = 0; i < kChunkSizes; ++i) {
+      const int c = kMinChunk << i;
+      if (g.tasks[i] != (S + c) / c || g.max_nc[i] != (S + c) / c) {
+        std::printf("FAIL chunk count of %d positions at chunk %d\n", S, c);
+        return false;
+      }
+    }
+  }
+  std::mt19937 rng(12345);
+  for (int rep = 0; rep < 200; ++rep) {
+    const int B = 1 + (int)(rng() % 1024);
+    std::vector<int> sl(B);
+    PlanAgg g{};
+    long pos = 0, t[kChunkSizes] = {0, 0, 0};
+    int mx[kChunkSizes] = {0, 0, 0};
+    for (int b = 0; b < B; ++b) {
+      sl[b] = (int)(rng() % 200000);
+      plan_agg_add(g, sl[b]);
+      pos += sl[b];
+      for (int i = 0; i < kChunkSizes; ++i) {
+        const int c = kMinChunk << i, nc = (sl[b] + c) / c;
+        t[i] += nc;
+        mx[i] = mx[i] > nc ? mx[i] : nc;
+      }
+    }
+    bool ok = g.positions == pos;
+    for (int i = 0; i < kChunkSizes; ++i) ok = ok && g.tasks[i] == t[i] && g.max_nc[i] == mx[i];
+    if (!ok) {
+      std::printf("FAIL aggregates of a batch of %d\n", B);
+      return false;
+    }
+  }
+  return true;
+}
+
 int main(int argc, char** argv) {
   std::string fault;
   for (int i = 1; i + 1 < argc; ++i)
     if (!std::strcmp(argv[i], "--fault")) fault = argv[i + 1];
+  if (fault.empty() && !check_aggregates()) return 1;
   const Shape s8b{"8B", PMK_BF16, 4096, 32, 8, 128, 14336, 0, 0, 0};
   const Shape s70{"70B", PMK_BF16, 8192, 64, 8, 128, 28672, 0, 0, 0};
   const Shape stp{"70B TP share", PMK_BF16, 8192, 8, 1, 128, 3584, 0, 0, 0};
