@@ -439,6 +439,17 @@ def test_8b_shape_largest_batch_short_caches(orc):
     check_dense(orc, case, requests=sorted(set(block_requests(lens)) | {full}))
 
 
+@pytest.mark.parametrize("B", [17, 33])
+def test_8b_shape_odd_block_counts(orc, B):
+    """Batches just past one and two 16-row blocks (the last block holding a
+    single request): the blocked split sizes its row tiles for the block count
+    (two and three blocks); one layer, every request compared."""
+    w = synth.get_workload("c3_8b_sweep")
+    lens = synth.ragged_lengths(B, 16, 700, ("c3_8b_sweep", "lens_odd_blocks", B))
+    case = build_case(w, B, lens, n_layers=1, max_seq=int(lens.max()) + 2, tag=f"t22_{B}")
+    check_dense(orc, case, requests=list(range(B)))
+
+
 @pytest.mark.parametrize("B", [256, 512])
 def test_8b_shape_batch_beyond_128_every_block(orc, B):
     """Decode batches beyond the sweep's largest point (16 to 32 blocks of 16
